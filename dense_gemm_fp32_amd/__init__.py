@@ -1,0 +1,20 @@
+"""MI355X (gfx950) GEMM library: row-major C := alpha*A*B + beta*C in fp32 and
+in fp16 with fp32 accumulation, hand-written HIP kernels behind a C ABI
+(include/gemm.h, libgemm.so).
+
+The binding is loaded on first use of one of its names, so that host-only
+helpers of this package (the build script, the measurement model) import
+without the library; using the GEMM entry points without a built library
+raises ImportError.
+"""
+_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe",
+                  "gemm_set_load_mode", "gemm", "GemmError", "LIB_PATH", "EXPORTS")
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,122 @@
+"""ctypes binding of libgemm.so: the C entry points of include/gemm.h under
+the same names, plus a torch-tensor convenience wrapper.
+
+Only argument marshalling happens here; every step of the GEMM runs in the
+HIP kernels of libgemm.so.  There is no fallback: if the library is missing
+the import fails with an error that says how to build it.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads torch's HIP runtime first, so libgemm.so binds to the same one)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgemm.so is not built (%s); run `python -m dense_gemm_fp32_amd.build`"
+                      % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_I = ctypes.c_int
+_F = ctypes.c_float
+_P = ctypes.c_void_p
+
+_lib.gemm_f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
+_lib.gemm_f32.restype = _I
+_lib.gemm_f16.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
+_lib.gemm_f16.restype = _I
+_lib.gemm_status_string.argtypes = [_I]
+_lib.gemm_status_string.restype = ctypes.c_char_p
+_lib.gemm_describe.argtypes = [_I, _I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, ctypes.c_char_p, _I]
+_lib.gemm_describe.restype = _I
+_lib.gemm_set_load_mode.argtypes = [_I]
+_lib.gemm_set_load_mode.restype = _I
+
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status):
+        super().__init__("gemm status %d: %s" % (status, gemm_status_string(status)))
+        self.status = status
+
+
+def _addr(x):
+    """Device address of a torch tensor, or an integer address as given."""
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C := alpha*A*B + beta*C in fp32 (see include/gemm.h).  A, B, C are
+    device addresses or torch tensors; stream is a hipStream_t handle, a
+    torch.cuda.Stream or None (the null stream).  Returns the status code."""
+    return _lib.gemm_f32(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                         _stream(stream))
+
+
+def gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """fp16-in / fp16-out GEMM with fp32 accumulation (see include/gemm.h)."""
+    return _lib.gemm_f16(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                         _stream(stream))
+
+
+def gemm_status_string(status):
+    return _lib.gemm_status_string(int(status)).decode()
+
+
+def gemm_describe(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+    """(status, text) describing the variant chosen for these arguments."""
+    buf = ctypes.create_string_buffer(256)
+    dt = {"f32": 0, "f16": 1}.get(dtype, dtype)
+    rc = _lib.gemm_describe(dt, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                            buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def gemm_set_load_mode(mode):
+    """0 = vector/scalar loads by alignment (default), 1 = force scalar."""
+    return _lib.gemm_set_load_mode(int(mode))
+
+
+def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C := alpha*A@B + beta*C for 2-D torch tensors on the GPU (in place).
+
+    Rows may be padded (stride(0) >= number of columns) but each row must be
+    contiguous (stride(1) == 1).  float32 tensors go to gemm_f32, float16 to
+    gemm_f16.  Uses the current torch stream unless one is given."""
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("%s must be 2-D with stride(1) == 1" % name)
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                             tuple(C.shape)))
+    if not (A.dtype == B.dtype == C.dtype):
+        raise ValueError("A, B and C must share a dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(C.stride(0), 1)
+    if A.dtype == torch.float32:
+        rc = gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    elif A.dtype == torch.float16:
+        rc = gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    else:
+        raise ValueError("unsupported dtype %s" % A.dtype)
+    if rc != 0:
+        raise GemmError(rc)
+    return C

@@ -1,0 +1,164 @@
+// api.hip -- the extern "C" entry points declared in include/gemm.h:
+// argument checks, quick returns, variant choice and launch.
+//
+// Argument checks follow the BLAS convention (return -i for the first invalid
+// argument i) and run before any HIP call.  The operation is
+// C := alpha*A*B + beta*C on row-major matrices with leading dimensions (the
+// SGEMM summary: definition and memory-layout section).
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/gemm.h"
+#include "internal.hpp"
+
+namespace {
+
+std::atomic<int> g_load_mode{0};
+
+// Shared argument checks.  `elem_bytes` only matters for descriptions.
+int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+               float beta, const void *C, int ldc) {
+  if (M < 0) return -1;
+  if (N < 0) return -2;
+  if (K < 0) return -3;
+  if (lda < (K > 1 ? K : 1)) return -6;
+  if (ldb < (N > 1 ? N : 1)) return -8;
+  if (ldc < (N > 1 ? N : 1)) return -11;
+  const bool empty = (M == 0 || N == 0);
+  const bool reads_ab = !empty && K > 0 && alpha != 0.0f;
+  if (reads_ab && A == nullptr) return -5;
+  if (reads_ab && B == nullptr) return -7;
+  const bool touches_c = !empty && !((alpha == 0.0f || K == 0) && beta == 1.0f);
+  if (touches_c && C == nullptr) return -10;
+  return 0;
+}
+
+enum class Route { kNothing, kScale, kGemm };
+
+Route route(int M, int N, int K, float alpha, float beta) {
+  if (M == 0 || N == 0) return Route::kNothing;
+  if (alpha == 0.0f || K == 0) return beta == 1.0f ? Route::kNothing : Route::kScale;
+  return Route::kGemm;
+}
+
+dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
+                      int ldb, float beta, void *C, int ldc, void *stream) {
+  dgemm::Call c;
+  c.M = M;
+  c.N = N;
+  c.K = K;
+  c.alpha = alpha;
+  c.beta = beta;
+  c.A = A;
+  c.lda = lda;
+  c.B = B;
+  c.ldb = ldb;
+  c.C = C;
+  c.ldc = ldc;
+  c.force_scalar = g_load_mode.load(std::memory_order_relaxed) == 1;
+  c.stream = static_cast<hipStream_t>(stream);
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
+      break;
+    case Route::kGemm:
+      e = dgemm::launch_f32(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream));
+      break;
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
+int gemm_f16(int M, int N, int K, float alpha, const gemm_half_t *A, int lda, const gemm_half_t *B,
+             int ldb, float beta, gemm_half_t *C, int ldc, void *stream) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = dgemm::launch_scale_f16(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
+      break;
+    case Route::kGemm:
+      e = dgemm::launch_f16(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream));
+      break;
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
+const char *gemm_status_string(int status) {
+  switch (status) {
+    case 0: return "success";
+    case -1: return "invalid argument 1: M < 0";
+    case -2: return "invalid argument 2: N < 0";
+    case -3: return "invalid argument 3: K < 0";
+    case -5: return "invalid argument 5: A is NULL";
+    case -6: return "invalid argument 6: lda < max(1, K)";
+    case -7: return "invalid argument 7: B is NULL";
+    case -8: return "invalid argument 8: ldb < max(1, N)";
+    case -10: return "invalid argument 10: C is NULL";
+    case -11: return "invalid argument 11: ldc < max(1, N)";
+    default: break;
+  }
+  if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+  return "unknown status";
+}
+
+int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, int lda,
+                  const void *B, int ldb, float beta, const void *C, int ldc, char *buf, int len) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  char text[256];
+  if (rc != 0) {
+    snprintf(text, sizeof text, "invalid: %s", gemm_status_string(rc));
+  } else if (dtype != 0 && dtype != 1) {
+    snprintf(text, sizeof text, "invalid: unknown dtype %d", dtype);
+  } else {
+    switch (route(M, N, K, alpha, beta)) {
+      case Route::kNothing:
+        snprintf(text, sizeof text, "%s no-op", dtype ? "f16" : "f32");
+        break;
+      case Route::kScale:
+        snprintf(text, sizeof text, "%s scale C := beta*C%s", dtype ? "f16" : "f32",
+                 beta == 0.0f ? " (zero fill, C not read)" : "");
+        break;
+      case Route::kGemm: {
+        dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, const_cast<void *>(C), ldc,
+                                  nullptr);
+        dgemm::Plan p = dtype ? dgemm::plan_f16(c) : dgemm::plan_f32(c);
+        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s",
+                 p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",
+                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads,
+                 beta == 0.0f ? " beta0 (C not read)" : "");
+        break;
+      }
+    }
+  }
+  if (buf && len > 0) {
+    strncpy(buf, text, (size_t)len - 1);
+    buf[len - 1] = '\0';
+  }
+  return rc;
+}
+
+int gemm_set_load_mode(int mode) {
+  if (mode != 0 && mode != 1) return -1;
+  return g_load_mode.exchange(mode);
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// internal.hpp -- host-side interface between the C ABI (api.hip) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgemm {
+
+// One validated GEMM call, after quick returns have been taken: M, N, K > 0
+// and alpha != 0.
+struct Call {
+  int M, N, K;
+  float alpha, beta;
+  const void *A;
+  int lda;
+  const void *B;
+  int ldb;
+  void *C;
+  int ldc;
+  bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
+  hipStream_t stream;
+};
+
+// Chosen kernel variant (for launching and for gemm_describe).
+struct Plan {
+  const char *name;      // tile configuration, e.g. "f32 mfma32x32x2 128x128x32 w2x2"
+  int bm, bn, bk;
+  int threads;
+  int vec_a, vec_b, vec_c;   // elements per global access (1 = scalar)
+  long long blocks;
+};
+
+Plan plan_f32(const Call &c);
+Plan plan_f16(const Call &c);
+hipError_t launch_f32(const Call &c);
+hipError_t launch_f16(const Call &c);
+
+// C := beta * C over an M x N matrix (beta == 0 writes zeros without reading).
+hipError_t launch_scale_f32(int M, int N, float beta, float *C, int ldc, hipStream_t s);
+hipError_t launch_scale_f16(int M, int N, float beta, uint16_t *C, int ldc, hipStream_t s);
+
+inline bool aligned_to(const void *p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+}  // namespace dgemm

@@ -1,0 +1,132 @@
+/*
+ * gemm.h -- C ABI of the MI355X (gfx950) dense GEMM library, libgemm.so.
+ *
+ * Operation (both entry points):
+ *
+ *     C := alpha * A * B + beta * C
+ *
+ * with A an M x K matrix, B a K x N matrix and C an M x N matrix, all
+ * row-major with leading dimensions: element (i, j) of X is X[i*ldX + j].
+ * This is the SGEMM definition and layout of the "Advanced Matrix
+ * Multiplication on NVIDIA GPUs" summary (opening paragraphs and the section
+ * on memory layout: row-major storage, lda = k and ldb = ldc = n for dense
+ * matrices, larger leading dimensions for sub-matrices or padded rows).
+ * gemm_f16 is the fp16-in / fp16-out variant with fp32 accumulation that the
+ * "LeetGPU GEMM T4" page solves: products are summed in fp32, alpha*sum +
+ * beta*C is formed in fp32 and rounded once to half, round-to-nearest-even.
+ *
+ * Semantics:
+ *   - beta == 0: C is write-only; its previous contents (NaN included) are
+ *     never read (the tiling section of the SGEMM summary reads C only when
+ *     beta != 0).
+ *   - alpha == 0 or K == 0: A and B are not read; C := beta * C (beta == 0
+ *     writes zeros without reading C; beta == 1 returns without launching).
+ *   - M == 0 or N == 0: nothing to do; returns 0 without launching.
+ *   - The summation order over K is fixed for a given shape, leading
+ *     dimensions and alignment, so repeated calls give bitwise-identical
+ *     results (no atomics, no split-K).
+ *   - Accuracy: |C_gpu - C_exact| <= 4*K*u*(|alpha|*(|A||B|)_ij + |beta|*|C_ij|)
+ *     plus one rounding to the output type, u = 2^-24 (fp32 accumulation).
+ *
+ * Memory and ownership:
+ *   - A, B and C are DEVICE pointers owned by the caller.  The library keeps
+ *     no pointer after it returns, allocates nothing and frees nothing.
+ *   - C must not overlap A or B.
+ *   - The pad elements of each row (columns K..lda-1 of A, N..ldb-1 of B,
+ *     N..ldc-1 of C) are never read or written.
+ *
+ * Streams and synchronisation:
+ *   - `stream` is a hipStream_t (NULL = the default stream).  The call only
+ *     enqueues work on it and returns; it does not synchronise.  The caller
+ *     keeps A, B and C alive until that work has completed.
+ *   - The library holds no state, so calls are thread-safe and reentrant.
+ *
+ * Return value:
+ *   0                 success (work enqueued, or nothing to do)
+ *   -i (i = 1..12)    argument i (1-based, in signature order) is invalid.
+ *                     Checks run in this order and the first failure wins:
+ *                       M < 0 -> -1, N < 0 -> -2, K < 0 -> -3,
+ *                       lda < max(1, K) -> -6, ldb < max(1, N) -> -8,
+ *                       ldc < max(1, N) -> -11,
+ *                       A == NULL -> -5, B == NULL -> -7 (only when A and B
+ *                       would be read: M, N > 0, K > 0, alpha != 0),
+ *                       C == NULL -> -10 (only when M, N > 0 and C would be
+ *                       touched).
+ *                     Argument checks make no HIP call, so they work without
+ *                     a GPU.
+ *   > 0               a hipError_t from the kernel launch.
+ */
+#ifndef DENSE_GEMM_GEMM_H
+#define DENSE_GEMM_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE-754 binary16 bit pattern (1 sign, 5 exponent, 10 fraction bits). */
+typedef uint16_t gemm_half_t;
+
+#define GEMM_SUCCESS 0
+
+/*
+ * fp32 GEMM: A, B, C hold binary32 values; products are accumulated in fp32
+ * on the matrix cores (v_mfma_f32_32x32x2_f32), then alpha*acc + beta*C is
+ * formed in fp32 and stored.
+ *   M, N, K        problem size (>= 0)
+ *   alpha, beta    scalars (binary32)
+ *   A, lda         device pointer to A (M x K), lda >= max(1, K)
+ *   B, ldb         device pointer to B (K x N), ldb >= max(1, N)
+ *   C, ldc         device pointer to C (M x N), ldc >= max(1, N); in/out
+ *   stream         hipStream_t to enqueue on (NULL = default stream)
+ */
+int gemm_f32(int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream);
+
+/*
+ * fp16 GEMM with fp32 accumulation: A, B, C hold binary16 bit patterns;
+ * products are exact in fp32 and accumulated in fp32 on the matrix cores
+ * (v_mfma_f32_32x32x16_f16); alpha*acc + beta*C is formed in fp32 (C widened
+ * exactly) and rounded once to binary16, round-to-nearest-even, overflowing
+ * to +-infinity.  Arguments as for gemm_f32; alpha and beta are binary32.
+ */
+int gemm_f16(int M, int N, int K, float alpha,
+             const gemm_half_t *A, int lda,
+             const gemm_half_t *B, int ldb,
+             float beta, gemm_half_t *C, int ldc,
+             void *stream);
+
+/* Static, human-readable text for a status code returned above (never NULL). */
+const char *gemm_status_string(int status);
+
+/*
+ * Describe, without launching anything, the kernel variant the library picks
+ * for a call with these arguments: writes a NUL-terminated text such as
+ * "f32 mfma 128x128x32 loads A:vec4 B:vec4 C:vec2" into buf (at most len
+ * bytes, truncated if needed).  dtype: 0 = fp32, 1 = fp16.  Pointers are only
+ * inspected for alignment.  Returns the status gemm_f32 / gemm_f16 would
+ * return for the argument checks (0 or -i); no HIP call is made.
+ */
+int gemm_describe(int dtype, int M, int N, int K, float alpha,
+                  const void *A, int lda, const void *B, int ldb,
+                  float beta, const void *C, int ldc,
+                  char *buf, int len);
+
+/*
+ * Diagnostic switch for tests: 0 = choose vector or scalar loads per operand
+ * from alignment (the default); 1 = force scalar (element-wise) global loads
+ * and stores for every operand.  Applies process-wide to later calls; not
+ * meant for concurrent use with other threads issuing GEMMs.  Returns the
+ * previous setting, or -1 for an unknown mode.
+ */
+int gemm_set_load_mode(int mode);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_GEMM_H */

@@ -1,0 +1,128 @@
+"""Shared helpers of the GPU parity tests: upload host buffers, call the
+library through its C ABI (ctypes binding), read back, compare with the
+oracle element by element."""
+import sys
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+GUARD = 512          # elements after C that must survive every call
+
+
+def note(msg):
+    """Name the case before a GPU step (flushed, so it survives a crash)."""
+    print("[gpu-case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np_t(dtype):
+    return np.float32 if dtype == "f32" else np.float16
+
+
+def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
+    """Call gemm_f32 / gemm_f16 on device copies of the host buffers.
+
+    Returns (status, C buffer after the call as a host array).  C's buffer
+    is followed by a guard region of sentinels that must be left intact."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    note("%s %s M=%d N=%d K=%d lda=%d ldb=%d ldc=%d alpha=%r beta=%r" %
+         (tag, dtype, M, N, K, lda, ldb, ldc, alpha, beta))
+    t = _np_t(dtype)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        if x is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    dA, dB = up(A), up(B)
+    cbuf = np.concatenate([np.asarray(C, t).reshape(-1), np.full(GUARD, wl.C_PAD_SENTINEL, t)])
+    dC = up(cbuf)
+    fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_f16
+    stream = torch.cuda.current_stream(dev)
+    rc = fn(M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc, stream)
+    torch.cuda.synchronize(dev)
+    out = dC.cpu().numpy()
+    guard = out[-GUARD:]
+    assert np.array_equal(guard.view(np.uint16 if dtype == "f16" else np.uint32),
+                          np.full(GUARD, wl.C_PAD_SENTINEL, t).view(np.uint16 if dtype == "f16" else np.uint32)), \
+        "write past the end of C"
+    return rc, out[:-GUARD]
+
+
+def check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out, label=""):
+    """Elementwise parity of `out` (the C buffer after the call) with the
+    oracle, plus: pad columns of C unchanged bit for bit.  Returns the worst
+    |err|/tol."""
+    R, G = oracle.gemm(M, N, K, alpha, A, lda, B, ldb, beta, C if beta != 0 else None, ldc, dtype)
+    Cv = wl.view(np.asarray(C), M, N, ldc).astype(np.float64) if (beta != 0 and M and N) else 0.0
+    tol = oracle.tolerance(G, np.abs(Cv), alpha, beta, K, R, dtype)
+    gpu = wl.view(out, M, N, ldc)
+    ok, worst, idx = oracle.compare(gpu, R, tol)
+    if not ok:
+        i, j = idx
+        g = gpu[i, j]
+        raise AssertionError("%s: worst |err|/tol = %.3g at (%d, %d): gpu %r oracle %r tol %.3g" %
+                             (label, worst, i, j, g, R[i, j], tol[i, j]))
+    assert_pads_unchanged(out, C, M, N, ldc, dtype)
+    return worst
+
+
+def assert_pads_unchanged(out, C, M, N, ldc, dtype):
+    if ldc == N or M == 0:
+        return
+    u = np.uint16 if dtype == "f16" else np.uint32
+    o = np.asarray(out).view(u).reshape(-1)
+    c = np.asarray(C).view(u).reshape(-1)
+    full = (M * ldc)
+    o2 = o[:full].reshape(M, ldc)[:, N:]
+    c2 = c[:full].reshape(M, ldc)[:, N:]
+    assert np.array_equal(o2, c2), "pad columns of C were modified"
+
+
+def exact_expected(dtype, R):
+    """The correctly rounded result, for cases where every partial sum is exact."""
+    if dtype == "f32":
+        return oracle.round_f32(R)
+    return oracle.round_f16(R).view(np.float16)
+
+
+def bits(x, dtype):
+    return np.asarray(x).view(np.uint16 if dtype == "f16" else np.uint32)
+
+
+def check_sampled(dtype, w, A, B, C, out, nrows=48, seed=0):
+    """Full-size parity on sampled rows (oracle on those rows only), the
+    whole-matrix checksum and Freivalds' product check."""
+    M, N, K = w.M, w.N, w.K
+    rows = wl.sample_rows(M, nrows, seed)
+    t = _np_t(dtype)
+    Av = wl.view(np.asarray(A), M, K, w.lda)[rows]
+    Cv_full = wl.view(np.asarray(C), M, N, w.ldc)
+    Csub = np.ascontiguousarray(Cv_full[rows])
+    Asub = np.ascontiguousarray(Av)
+    R, G = oracle.gemm(len(rows), N, K, w.alpha, Asub.reshape(-1), K, B, w.ldb, w.beta,
+                       Csub.reshape(-1) if w.beta != 0 else None, N, dtype)
+    tol = oracle.tolerance(G, np.abs(Csub.astype(np.float64)) if w.beta != 0 else 0.0,
+                           w.alpha, w.beta, K, R, dtype)
+    gpu_full = wl.view(out, M, N, w.ldc)
+    ok, worst, idx = oracle.compare(np.ascontiguousarray(gpu_full[rows]), R, tol)
+    assert ok, "%s sampled rows: worst %.3g at %s" % (w.name, worst, idx)
+    # whole-matrix checks
+    g64 = oracle.half_to_double(np.ascontiguousarray(gpu_full)) if dtype == "f16" else gpu_full.astype(np.float64)
+    assert np.all(np.isfinite(g64))
+    u_out = oracle.U32 if dtype == "f32" else oracle.U16
+    eta = oracle.ETA32 if dtype == "f32" else oracle.ETA16
+    exp, mag = oracle.checksum(M, N, K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, dtype)
+    s = g64.sum()
+    bound = (1 + u_out) * 4 * K * oracle.U32 * mag + u_out * np.abs(g64).sum() + M * N * eta
+    assert abs(s - exp) <= bound, "checksum %r vs %r (bound %r)" % (s, exp, bound)
+    x = np.random.default_rng(seed + 1).choice([-1.0, 1.0], size=N)
+    y, ymag = oracle.freivalds(M, N, K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, x, dtype)
+    yg = g64 @ x
+    fb = (1 + u_out) * 4 * K * oracle.U32 * ymag + u_out * np.abs(g64).sum(axis=1) + N * eta
+    assert np.all(np.abs(yg - y) <= fb), "Freivalds check failed"
+    return worst

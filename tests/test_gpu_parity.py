@@ -1,0 +1,283 @@
+"""GPU parity of gemm_f32 / gemm_f16 against the CPU oracle, called through
+the C ABI.  Tolerance: |err| <= (1+u_out)*4*max(K,1)*2^-24*(|alpha|G + |beta||C|)
++ u_out*|R| + eta_out (oracle.tolerance), elementwise; bitwise equality where
+every partial sum is exact."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gemm_harness import bits, check, check_sampled, exact_expected, run
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16"]
+
+
+def _t(dtype):
+    return np.float32 if dtype == "f32" else np.float16
+
+
+def _w_run_check(w, label=None):
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    return check(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, out,
+                 label or w.name)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_f32_256():
+    _w_run_check(wl.F32_256)
+
+
+@pytest.mark.parametrize("n", [256, 512, 1024, 2048])
+def test_f32_square_full_oracle(n):
+    _w_run_check(wl.square(n, seeds=(2, 3, 4)))
+
+
+@pytest.mark.parametrize("w", [wl.RAGGED_F32, wl.RAGGED_F16], ids=lambda w: w.name)
+def test_ragged_padded_unaligned(w):
+    """1000 x 3000 x 517, lda=530, ldb=3005, ldc=3003: unaligned leading
+    dimensions (scalar loads), all three tails, NaN in the pads of A and B,
+    sentinels in the pad of C."""
+    _w_run_check(w)
+
+
+def test_f32_4096_sampled():
+    w = wl.F32_4096
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out)
+
+
+def test_f16_4096_beta_half_sampled():
+    w = wl.F16_4096
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out)
+
+
+def test_f32_sweep_endpoints_sampled():
+    """The size sweep's first size with beta = 1 (accumulating into C)."""
+    w = wl.sweep(1024)
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out, nrows=32)
+
+
+# ---------------------------------------------------------------- tails
+
+TAIL_DIMS = [1, 2, 7, 31, 33, 64, 127, 129, 255, 257]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_tails_brute_force(dtype):
+    """Every combination of small and tile-crossing M, N, K (aligned and
+    unaligned leading dimensions) against the full oracle."""
+    rng = np.random.default_rng(17)
+    t = _t(dtype)
+    combos = list(itertools.product(TAIL_DIMS, repeat=3))
+    rng.shuffle(combos)
+    for idx, (M, N, K) in enumerate(combos[:120]):
+        pad = int(rng.integers(0, 9))
+        lda, ldb, ldc = K + pad, N + (pad + 3) % 9, N + (2 * pad) % 9
+        alpha = float(t(rng.uniform(0.5, 2)))
+        beta = [0.0, 1.0, -0.5][idx % 3]
+        A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
+        B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
+        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+        rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, "tail")
+        assert rc == 0
+        check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out,
+              "tail M=%d N=%d K=%d ld=%d,%d,%d" % (M, N, K, lda, ldb, ldc))
+
+
+# ---------------------------------------------------------------- exactness
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (-1.0, 1.0), (2.0, -2.0), (1.0, 0.5)])
+def test_f32_small_integers_exact(alpha, beta):
+    """A, B, C in {-8..8}, K = 1000: every partial sum is an integer below
+    2^24, so the result must equal the correctly rounded value bit for bit."""
+    M, N, K = 300, 260, 1000
+    A = wl.small_ints(M, K, -8, 8, 1, "f32")
+    B = wl.small_ints(K, N, -8, 8, 2, "f32")
+    C = wl.small_ints(M, N, -8, 8, 3, "f32")
+    A, B, C = A.reshape(-1), B.reshape(-1), C.reshape(-1)
+    rc, out = run("f32", M, N, K, alpha, A, K, B, N, beta, C, N, "ints")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, alpha, A, K, B, N, beta, C, N)
+    assert np.array_equal(bits(out.reshape(M, N), "f32"), bits(exact_expected("f32", R), "f32"))
+
+
+def test_f32_full_precision_operands_exact():
+    """A = odd integers up to 4095 (12 significant bits), B in {-1, 0, 1}:
+    exact in fp32 for K = 4096, but any rounding of the operands below 12
+    significant bits (tf32 / bf16-style) breaks equality.  Both operand roles."""
+    M, N, K = 256, 192, 4096
+    A = wl.odd_ints(M, K, 4095, 5).reshape(-1)
+    B = wl.small_ints(K, N, -1, 1, 6, "f32").reshape(-1)
+    rc, out = run("f32", M, N, K, 1.0, A, K, B, N, 0.0, np.zeros(M * N, np.float32), N, "odd")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, 1.0, A, K, B, N, 0.0, None, N)
+    assert np.all(np.abs(R) < 2 ** 24)
+    assert np.array_equal(bits(out.reshape(M, N), "f32"), bits(exact_expected("f32", R), "f32"))
+    # transposed roles: B holds the 12-bit values
+    A2 = wl.small_ints(M, K, -1, 1, 7, "f32").reshape(-1)
+    B2 = wl.odd_ints(K, N, 4095, 8).reshape(-1)
+    rc, out = run("f32", M, N, K, 1.0, A2, K, B2, N, 0.0, np.zeros(M * N, np.float32), N, "odd2")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, 1.0, A2, K, B2, N, 0.0, None, N)
+    assert np.array_equal(bits(out.reshape(M, N), "f32"), bits(exact_expected("f32", R), "f32"))
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0, -1.0, 2.0])
+def test_f16_small_integers_exact(beta):
+    """A, B in {-3..3}, K = 200, C in {-8..8}: |R| <= 1816 + 16 is an integer,
+    exact in fp16, so the output must equal it bit for bit."""
+    M, N, K = 200, 280, 200
+    A = wl.small_ints(M, K, -3, 3, 11, "f16").reshape(-1)
+    B = wl.small_ints(K, N, -3, 3, 12, "f16").reshape(-1)
+    C = wl.small_ints(M, N, -8, 8, 13, "f16").reshape(-1)
+    rc, out = run("f16", M, N, K, 1.0, A, K, B, N, beta, C, N, "f16ints")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, 1.0, A, K, B, N, beta, C, N, "f16")
+    assert np.all(np.abs(R) <= 2048)
+    assert np.array_equal(bits(out, "f16"), oracle.round_f16(R).reshape(-1))
+
+
+def test_f16_output_rounding_is_nearest_even():
+    """K = 2, A = [1, 3*2^-11], B = [1, 1]^T: the fp32 accumulator is exactly
+    1 + 3*2^-11, halfway between halves 1+2^-10 and 1+2^-9; ties-to-even gives
+    1 + 2^-9 (round-toward-zero would give 1 + 2^-10).  1 + 0.75*2^-10 is
+    not a tie and goes to 1 + 2^-10."""
+    A = np.array([1.0, 3 * 2.0 ** -11, 1.0, 0.75 * 2.0 ** -10], np.float16)
+    B = np.array([1.0, 1.0], np.float16)
+    C = np.zeros(2, np.float16)
+    rc, out = run("f16", 2, 1, 2, 1.0, A, 2, B, 1, 0.0, C, 1, "rne")
+    assert rc == 0
+    got = bits(out, "f16")
+    assert int(got[0]) == 0x3C02, hex(got[0])
+    assert int(got[1]) == 0x3C01, hex(got[1])
+    # overflow: 2 * 65504 rounds to +inf; -65520 ties to -inf
+    A = np.array([65504.0, 65504.0, -32752.0, -32768.0], np.float16)
+    B = np.array([1.0, 1.0], np.float16)
+    rc, out = run("f16", 2, 1, 2, 1.0, A, 2, B, 1, 0.0, C, 1, "ovf")
+    assert rc == 0
+    got = bits(out, "f16")
+    assert int(got[0]) == 0x7C00 and int(got[1]) == 0xFC00, [hex(g) for g in got]
+
+
+# ---------------------------------------------------------------- special matrices
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_identity_and_permutation_bitwise(dtype):
+    t = _t(dtype)
+    rng = np.random.default_rng(31)
+    M, N = 300, 200
+    B = rng.uniform(-1, 1, (M, N)).astype(t)
+    eye = np.eye(M, dtype=t)
+    C0 = np.zeros(M * N, t)
+    rc, out = run(dtype, M, N, M, 1.0, eye.reshape(-1), M, B.reshape(-1), N, 0.0, C0, N, "A=I")
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B.reshape(-1), dtype))
+    A = rng.uniform(-1, 1, (M, N)).astype(t)
+    eyeN = np.eye(N, dtype=t)
+    rc, out = run(dtype, M, N, N, 1.0, A.reshape(-1), N, eyeN.reshape(-1), N, 0.0, C0, N, "B=I")
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(A.reshape(-1), dtype))
+    p = rng.permutation(M)
+    P = np.zeros((M, M), t)
+    P[np.arange(M), p] = 1
+    rc, out = run(dtype, M, N, M, 1.0, P.reshape(-1), M, B.reshape(-1), N, 0.0, C0, N, "A=P")
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B[p].reshape(-1), dtype))
+
+
+# ---------------------------------------------------------------- alpha / beta
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_alpha_zero_ignores_A_and_B(dtype):
+    t = _t(dtype)
+    M, N, K = 130, 70, 90
+    A = np.full(M * K, np.nan, t)
+    B = np.full(K * N, np.inf, t)
+    C = np.random.default_rng(1).uniform(-1, 1, M * N).astype(t)
+    rc, out = run(dtype, M, N, K, 0.0, A, K, B, N, -0.5, C, N, "alpha0")
+    assert rc == 0
+    expect = (np.float32(-0.5) * C.astype(np.float32)).astype(t)
+    assert np.array_equal(bits(out, dtype), bits(expect, dtype))
+    # alpha = 0 and beta = 0: exact zeros, C (NaN here) not read
+    Cn = np.full(M * N, np.nan, t)
+    rc, out = run(dtype, M, N, K, 0.0, A, K, B, N, 0.0, Cn, N, "alpha0beta0")
+    assert rc == 0 and np.all(out == 0)
+    # alpha = 0, beta = 1: C unchanged bit for bit (nothing launched)
+    rc, out = run(dtype, M, N, K, 0.0, None, K, None, N, 1.0, C, N, "alpha0beta1")
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(C, dtype))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_beta_zero_ignores_C(dtype):
+    t = _t(dtype)
+    M, N, K = 257, 129, 65
+    rng = np.random.default_rng(2)
+    A = rng.uniform(-1, 1, M * K).astype(t)
+    B = rng.uniform(-1, 1, K * N).astype(t)
+    Cn = np.full(M * N, np.nan, t)
+    rc, out = run(dtype, M, N, K, 1.0, A, K, B, N, 0.0, Cn, N, "beta0")
+    assert rc == 0 and np.all(np.isfinite(out.astype(np.float64)))
+    check(dtype, M, N, K, 1.0, A, K, B, N, 0.0, Cn, N, out, "beta0")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_k_zero_scales_C(dtype):
+    t = _t(dtype)
+    M, N = 100, 300
+    C = np.random.default_rng(3).uniform(-1, 1, M * (N + 4)).astype(t)
+    rc, out = run(dtype, M, N, 0, 1.0, None, 1, None, N, 2.0, C, N + 4, "k0")
+    assert rc == 0
+    check(dtype, M, N, 0, 1.0, None, 1, None, N, 2.0, C, N + 4, out, "k0")
+
+
+# ---------------------------------------------------------------- determinism, paths
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bitwise_deterministic_and_scalar_path_agrees(dtype):
+    """Two identical calls give identical bits; forcing element-wise loads
+    changes only how data moves, not the summation order, so the forced-scalar
+    result is bitwise equal too."""
+    import dense_gemm_fp32_amd as dg
+    t = _t(dtype)
+    M, N, K = 700, 900, 600
+    rng = np.random.default_rng(4)
+    A = rng.standard_normal(M * K).astype(t)
+    B = rng.standard_normal(K * N).astype(t)
+    C = rng.standard_normal(M * N).astype(t)
+    rc1, o1 = run(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, "det1")
+    rc2, o2 = run(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, "det2")
+    assert rc1 == rc2 == 0 and np.array_equal(bits(o1, dtype), bits(o2, dtype))
+    prev = dg.gemm_set_load_mode(1)
+    try:
+        rc3, o3 = run(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, "scalar")
+    finally:
+        dg.gemm_set_load_mode(prev)
+    assert rc3 == 0 and np.array_equal(bits(o1, dtype), bits(o3, dtype))
+    check(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, o1, "det")
+
+
+def test_torch_wrapper_matches_raw_call():
+    import torch
+    import dense_gemm_fp32_amd as dg
+    g = torch.Generator().manual_seed(0)
+    A = torch.rand(333, 444, generator=g).cuda()
+    B = torch.rand(444, 555, generator=g).cuda()
+    C = torch.zeros(333, 555).cuda()
+    dg.gemm(A, B, C, 1.0, 0.0)
+    torch.cuda.synchronize()
+    R, G = oracle.gemm(333, 555, 444, 1.0, A.cpu().numpy().reshape(-1), 444,
+                       B.cpu().numpy().reshape(-1), 555, 0.0, None, 555)
+    tol = oracle.tolerance(G, 0.0, 1.0, 0.0, 444, R)
+    assert oracle.compare(C.cpu().numpy(), R, tol)[0]
