@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the hot path: gemm_f32 on the fp32 4096^3 row-major
+product (A, B ~ U[-1, 1] from fixed seeds, alpha = 1, beta = 0), inputs
+resident in device memory.  W untimed steps, then exactly K timed steps
+between two synchronisations; the JSON line reports TFLOP/s = 2MNK / t.
+
+Also reported on the same line:
+  * roofline: the GEMM kernel's achieved TFLOP/s from HIP events around each
+    launch in the timed region, against the fp32 matrix peak (157.3 TFLOP/s),
+    and HBM traffic per launch from the committed rocprofv3 counter summary
+    when it was taken on the current kernel sources (else null);
+  * p4_protocol: the replay schedule of the SGEMM summary's benchmarking
+    section -- floor(1000*exp((1024-n)/3100)) replays, cache flushed before
+    each (outside the timed interval), mean of the second half;
+  * fp16: the same for gemm_f16 on the fp16 4096^3 GEMM with beta = 0.5;
+  * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
+    the same workload (a subset of output rows).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
+PEAK_F16 = 2516.6     # TFLOP/s, MI355X dense fp16 matrix
+PEAK_HBM = 8000.0     # GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+from dense_gemm_fp32_amd.model import replay_count  # noqa: E402
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_fp32_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(key):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != kernel_source_hash():
+        return None
+    ent = data.get("kernels", {}).get(key)
+    if not ent:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16", action="store_true")
+    ap.add_argument("--no-p4", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["f32", "f16", "copy"], default=None,
+                    help="run only one kernel (profiling runs); 'copy' runs a plain "
+                         "device copy of known size to calibrate HBM counters")
+    return ap.parse_args()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import dense_gemm_fp32_amd as dg
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.only == "copy":
+        run_copy_calibration(torch, dev)
+        return
+
+    def upload(w):
+        A, B, C = wl.make(w)
+        return tuple(torch.from_numpy(x).to(dev) for x in (A, B, C)), (A, B, C)
+
+    def timed_steps(fn, w, dA, dB, dC, steps, warmup):
+        for _ in range(warmup):
+            rc = fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream)
+            if rc != 0:
+                raise RuntimeError("gemm returned %d: %s" % (rc, dg.gemm_status_string(rc)))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        launch_ms = [a.elapsed_time(b) for a, b in ev]
+        return wall, launch_ms
+
+    def p4_protocol(fn, w, dA, dB, dC):
+        n = round((w.M * w.N * w.K) ** (1.0 / 3.0))
+        reps = replay_count(n)
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
+        times = []
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            flush.zero_()
+            s.record(stream)
+            fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream)
+            e.record(stream)
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        del flush
+        last = times[len(times) - len(times) // 2:]
+        mean = sum(last) / len(last)
+        return {"replays": reps, "averaged": len(last), "flush_bytes": 512 * 1024 * 1024,
+                "mean_ms": round(mean, 5), "median_ms": round(sorted(last)[len(last) // 2], 5),
+                "min_ms": round(min(times), 5), "tflops": round(w.flops / (mean * 1e-3) / 1e12, 2)}
+
+    def measure(fn, w, peak, key, steps, warmup, p4):
+        (dA, dB, dC), host = upload(w)
+        wall, launch_ms = timed_steps(fn, w, dA, dB, dC, steps, warmup)
+        ms_per_step = wall * 1e3 / steps
+        avg_launch = sum(launch_ms) / len(launch_ms)
+        achieved = w.flops / (avg_launch * 1e-3) / 1e12
+        traffic = load_traffic(key)
+        res = {
+            "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "ms_per_step": round(ms_per_step, 5),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                         "traffic": traffic,
+                         "avg_launch_ms": round(avg_launch, 5),
+                         "algorithmic_flops_per_launch": w.flops},
+        }
+        if p4:
+            res["p4_protocol"] = p4_protocol(fn, w, dA, dB, dC)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        return res, host
+
+    if args.only == "f16":
+        f16_res, _ = measure(dg.gemm_f16, wl.F16_4096, PEAK_F16, "f16", args.steps, args.warmup,
+                             False)
+        print(json.dumps({"only": "f16", **f16_res}), flush=True)
+        return
+    w32 = wl.F32_4096
+    main_res, host32 = measure(dg.gemm_f32, w32, PEAK_F32, "f32", args.steps, args.warmup,
+                               not args.no_p4 and args.only is None)
+    if args.only == "f32":
+        print(json.dumps({"only": "f32", **main_res}), flush=True)
+        return
+
+    f16_res = None
+    if not args.no_fp16:
+        w16 = wl.F16_4096
+        f16_res, _ = measure(dg.gemm_f16, w16, PEAK_F16, "f16", args.steps, args.warmup,
+                             not args.no_p4)
+        f16_res = {"workload": "fp16 in/out, fp32 accumulation, M=N=K=4096, A,B,C ~ U[-1,1], "
+                               "alpha=1, beta=0.5", "unit": "TFLOP/s", **f16_res}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w32, host32, args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": "GEMM TFLOP/s (2MNK/t) fp32 at 4096^3; % of MI355X fp32 matrix peak",
+        "value": main_res["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fp32 SGEMM row-major M=N=K=4096, lda=ldb=ldc=4096, "
+                               "A,B ~ U[-1,1] (seeds 2,3), alpha=1, beta=0",
+                   "M": w32.M, "N": w32.N, "K": w32.K},
+        "pct_of_peak": round(100.0 * main_res["value"] / PEAK_F32, 2),
+        "roofline": main_res["roofline"],
+        "p4_protocol": main_res.get("p4_protocol"),
+        "fp16": f16_res,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "torch": torch.__version__,
+                   "hip": torch.version.hip},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_copy_calibration(torch, dev):
+    """A plain device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB) for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1024 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"only": "copy", "bytes_read": n * 4, "bytes_written": n * 4}), flush=True)
+
+
+def cpu_baseline(w, host, target_s):
+    """Oracle (as it stands) on a bounded sample of the workload: full output
+    rows of the same product, timed on this host's cores."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    A, B, C = host
+    Av = wl.view(A, w.M, w.K, w.lda)
+    threads = oracle.threads()
+
+    def run_rows(nrows):
+        sub = np.ascontiguousarray(Av[:nrows]).reshape(-1)
+        t0 = time.perf_counter()
+        oracle.gemm(nrows, w.N, w.K, w.alpha, sub, w.K, B, w.ldb, w.beta, None, w.N, w.dtype)
+        return time.perf_counter() - t0
+
+    probe_rows = max(threads, 4)
+    t = run_rows(probe_rows)
+    rows = int(max(probe_rows, min(w.M, probe_rows * target_s / max(t, 1e-6))))
+    rows = max(threads, rows - rows % threads) if rows >= threads else rows
+    t = run_rows(rows)
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": "%d of the %d output rows of the fp32 4096^3 GEMM (%d x %d x %d), "
+                      "double-precision oracle with |A||B| bound terms" % (rows, w.M, rows, w.N, w.K)}
+
+
+if __name__ == "__main__":
+    main()

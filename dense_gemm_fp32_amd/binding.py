@@ -108,15 +108,17 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
                                                              tuple(C.shape)))
     if not (A.dtype == B.dtype == C.dtype):
         raise ValueError("A, B and C must share a dtype")
+    if A.dtype not in (torch.float32, torch.float16):
+        raise ValueError("unsupported dtype %s" % A.dtype)
+    if not (A.is_cuda and B.is_cuda and C.is_cuda):
+        raise ValueError("A, B and C must be GPU tensors")
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(C.stride(0), 1)
     if A.dtype == torch.float32:
         rc = gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
-    elif A.dtype == torch.float16:
-        rc = gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     else:
-        raise ValueError("unsupported dtype %s" % A.dtype)
+        rc = gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     if rc != 0:
         raise GemmError(rc)
     return C

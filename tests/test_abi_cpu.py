@@ -1,0 +1,147 @@
+"""The C ABI without a GPU: libgemm.so loads, exports every function that
+include/gemm.h declares, validates arguments before any HIP call, takes the
+quick returns, and reports the chosen variant.  No test here launches work."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+
+FAKE = 0x10000        # a non-null, 64 KiB-aligned address; never dereferenced here
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import dense_gemm_fp32_amd as dg
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for n in _declared():
+        assert n in exported, n
+        from dense_gemm_fp32_amd import binding
+        assert hasattr(binding._lib, n)
+    assert set(dg.EXPORTS) <= exported
+
+
+def test_single_hip_runtime_loaded():
+    import dense_gemm_fp32_amd as dg  # noqa: F401  (loads torch, then libgemm.so)
+    dg.gemm_status_string(0)
+    maps = open("/proc/self/maps").read()
+    libs = set(re.findall(r"(\S*libamdhip64\S*)", maps))
+    assert len(libs) == 1, libs
+
+
+CASES = [
+    # (expected, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+    (-1, -1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-2, 4, -1, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-3, 4, 4, -1, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-6, 4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4),
+    (-6, 4, 4, 0, 1.0, FAKE, 0, FAKE, 4, 0.0, FAKE, 4),
+    (-8, 4, 9, 4, 1.0, FAKE, 4, FAKE, 8, 0.0, FAKE, 9),
+    (-11, 4, 9, 4, 1.0, FAKE, 4, FAKE, 9, 0.0, FAKE, 8),
+    (-5, 4, 4, 4, 1.0, None, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-7, 4, 4, 4, 1.0, FAKE, 4, None, 4, 0.0, FAKE, 4),
+    (-10, 4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, None, 4),
+    (-10, 4, 4, 4, 0.0, None, 4, None, 4, 0.5, None, 4),   # scale path needs C
+    (-1, -1, -1, -1, 1.0, None, 0, None, 0, 0.0, None, 0),  # first failure wins
+    (-6, 4, 4, 8, 1.0, None, 7, None, 3, 0.0, None, 3),
+    # quick returns: nothing touched, no launch, null pointers allowed
+    (0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4),
+    (0, 4, 0, 4, 1.0, None, 4, None, 1, 0.0, None, 1),
+    (0, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, None, 4),
+    (0, 4, 4, 0, 1.0, None, 1, None, 4, 1.0, None, 4),
+]
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16"])
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_argument_checks_and_quick_returns(fn, case):
+    import dense_gemm_fp32_amd as dg
+    expected, *args = case
+    assert getattr(dg, fn)(*args, None) == expected
+    # gemm_describe applies the same checks
+    rc, text = dg.gemm_describe("f32" if fn == "gemm_f32" else "f16", *args)
+    assert rc == expected
+    if expected < 0:
+        assert text.startswith("invalid")
+
+
+def test_status_strings():
+    import dense_gemm_fp32_amd as dg
+    assert dg.gemm_status_string(0) == "success"
+    for code in (-1, -2, -3, -5, -6, -7, -8, -10, -11):
+        s = dg.gemm_status_string(code)
+        assert s.startswith("invalid argument %d" % -code), s
+    assert dg.gemm_status_string(-99) == "unknown status"
+    assert len(dg.gemm_status_string(1)) > 0
+
+
+def test_describe_picks_vector_or_scalar_loads():
+    import dense_gemm_fp32_amd as dg
+    rc, t = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
+    assert rc == 0 and "A:vec4" in t and "B:vec4" in t and "C:vec" in t and "beta0" in t
+    # ragged, unaligned leading dimensions (K+13, N+5, N+3): element-wise everywhere
+    rc, t = dg.gemm_describe("f32", 1000, 3000, 517, 1.5, FAKE, 530, FAKE, 3005, -0.75, FAKE, 3003)
+    assert rc == 0 and "A:scalar1" in t and "B:scalar1" in t and "C:scalar1" in t
+    rc, t = dg.gemm_describe("f16", 1000, 3000, 517, 1.5, FAKE, 530, FAKE, 3005, -0.75, FAKE, 3003)
+    assert rc == 0 and "A:scalar1" in t and "B:scalar1" in t and "C:scalar1" in t
+    rc, t = dg.gemm_describe("f16", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.5, FAKE, 4096)
+    assert rc == 0 and "A:vec8" in t and "B:vec8" in t and "beta0" not in t
+    # misaligned base pointer: scalar for that operand only
+    rc, t = dg.gemm_describe("f32", 256, 256, 256, 1.0, FAKE + 4, 256, FAKE, 256, 0.0, FAKE, 256)
+    assert "A:scalar1" in t and "B:vec4" in t
+    # degenerate routes
+    assert "scale" in dg.gemm_describe("f32", 8, 8, 0, 1.0, None, 1, None, 8, 2.0, FAKE, 8)[1]
+    assert "zero fill" in dg.gemm_describe("f32", 8, 8, 8, 0.0, None, 8, None, 8, 0.0, FAKE, 8)[1]
+    assert "no-op" in dg.gemm_describe("f16", 8, 8, 8, 0.0, None, 8, None, 8, 1.0, None, 8)[1]
+
+
+def test_force_scalar_mode_switch():
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_load_mode(1)
+    try:
+        rc, t = dg.gemm_describe("f32", 512, 512, 512, 1.0, FAKE, 512, FAKE, 512, 0.0, FAKE, 512)
+        assert "A:scalar1" in t and "B:scalar1" in t and "C:scalar1" in t
+    finally:
+        assert dg.gemm_set_load_mode(prev) == 1
+    assert dg.gemm_set_load_mode(7) == -1
+
+
+def test_torch_wrapper_rejects_bad_layouts():
+    import torch
+    import dense_gemm_fp32_amd as dg
+    A = torch.zeros(4, 6)
+    with pytest.raises(ValueError):
+        dg.gemm(A.t(), torch.zeros(4, 5), torch.zeros(6, 5))      # stride(1) != 1
+    with pytest.raises(ValueError):
+        dg.gemm(A, torch.zeros(5, 5), torch.zeros(4, 5))           # K mismatch
+    with pytest.raises(ValueError):
+        dg.gemm(A.double(), torch.zeros(6, 5).double(), torch.zeros(4, 5).double())
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libgemm.so the binding raises instead of falling back."""
+    import shutil
+    import sys
+    pkg = tmp_path / "dense_gemm_fp32_amd"
+    shutil.copytree(os.path.join(ROOT, "dense_gemm_fp32_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = ("import sys; sys.path.insert(0, %r); import dense_gemm_fp32_amd as d; d.gemm_f32" %
+            str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr
