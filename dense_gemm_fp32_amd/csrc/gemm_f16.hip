@@ -6,58 +6,227 @@
 // fp32 and rounded once to half, round-to-nearest-even (the fp16 GEMM of the
 // "LeetGPU GEMM T4" page: fp32 accumulators, one conversion at the end).
 //
-// Structure: the same double-buffered LDS K loop as the fp32 kernel (one
-// barrier per K step, next tiles' global loads in flight during the MFMAs).
+// Pipeline.  Each workgroup owns a BM x BN tile of C and walks K in steps of
+// BK through STAGES LDS slots (the double buffering of the SGEMM summary's
+// tiling section, deepened: the loads of step kt+STAGES-1 are in flight while
+// step kt is multiplied).  Global tiles move with direct global->LDS loads
+// (global_load_lds_dwordx4: each wave instruction writes 1 KB of LDS without
+// passing through registers); a wave waits for its own loads with an explicit
+// vmcnt and a raw barrier publishes the slot, so younger loads stay in flight
+// across the barrier.  The barrier for step kt+1 sits before the last k
+// sub-step of step kt, so the first fragments of kt+1 are read while the last
+// MFMAs of kt run.
 //
-// Operand layout.  For v_mfma_f32_32x32x16_f16 lane l supplies 8 halves of
-// A row l%32 and 8 halves of B column l%32 for the same k-slot group l/32, so
-// both operands must be k-contiguous per lane:
-//   * A tile in LDS: [BM rows][BK k] (+8 halves of row padding), copied
-//     straight from memory with 128-bit loads.
-//   * B tile in LDS: transposed to [BN columns][BK k].  Each thread loads a
-//     4 (k) x 8 (n) block of B with four 128-bit loads, transposes it in
-//     registers, and writes eight 4-half (64-bit) runs along k.
-//   * Output columns are interleaved inside a wave tile (block bj, lane
-//     column j holds wave column FN*j + bj), so each lane stores FN adjacent
-//     halves of a C row and 32 lanes cover a contiguous run.  The transposed
-//     B store places column FN*j + bj at LDS row 32*bj + j, so the MFMA reads
-//     stay on consecutive LDS rows.
+// LDS layout (per slot, no padding, 16-byte chunks XOR-swizzled by row):
+//   * A [BM rows][BK k]: row r's logical chunk c sits at chunk c ^ swz_a(r),
+//     which spreads 8 consecutive rows over distinct bank groups for the
+//     128-bit MFMA operand reads.
+//   * B [BK rows][BN n] as in memory: k-row kr's chunk c sits at c ^ 2*(kr%4),
+//     so the four k-rows read together by a transpose read use distinct banks.
+// The swizzle is applied on the global side: lane L of a direct load writes
+// LDS bytes 16L..16L+15 of its 1 KB, so it fetches the global chunk that
+// belongs there.
 //
-// Edges and alignment as in the fp32 kernel: masked loads that substitute 0
-// outside the matrix on the edge tiles and the last K step, 128-bit loads only
-// when the leading dimension is a multiple of 8 halves and the base 16-byte
-// aligned, element-wise loads otherwise.
+// Operands.  v_mfma_f32_32x32x16_f16: lane l supplies A(row l%32, k 8h..8h+7)
+// and B(k 8h..8h+7, col l%32) for h = l/32 (any k order shared by A and B gives
+// the same sum).  A: one ds_read_b128 of the lane's row.  B: two
+// ds_read_b64_tr_b16, each returning 4 consecutive k of the lane's column from
+// a 4 (k) x 16 (n) block that 16 lanes address (within each 16-lane group,
+// lane i receives element i%4 of the 8-byte rows read by lanes i/4, 4+i/4,
+// 8+i/4, 12+i/4).
+//
+// Epilogue.  Accumulators leave the MFMA layout (one column per lane) through
+// a per-wave LDS staging area, 32 rows at a time; each lane then owns 4
+// adjacent columns of a row, reads C there when beta != 0 (8-byte accesses),
+// forms alpha*acc + beta*C in fp32, rounds to half and stores 8 bytes, so 32
+// lanes write 256 contiguous bytes of a row (the coalesced, LDS-staged
+// epilogue of the SGEMM summary).
+//
+// Edges.  Direct loads cannot substitute zeros, so they are used only where
+// every chunk they read lies inside the matrix: A rows beyond M are clamped to
+// row M-1 (those rows only feed C rows that are never stored), B column chunks
+// beyond N are clamped to the last chunk when N % 8 == 0.  The partial K step
+// (K % BK != 0) is done first, through registers with per-element masks.  A
+// workgroup whose columns cross an N that is not a multiple of 8, and every
+// workgroup of a call whose A or B is not 16-byte aligned (base or leading
+// dimension), uses the register-staged path instead: masked loads (0 outside
+// the matrix; pad elements are never read) written to the same LDS layout.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace dgemm {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
-struct F16Tile {
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); counters not waited on are set to their maxima.
+constexpr int wait_vmcnt(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
+}
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+constexpr int kWaitAll = 0;
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_>
+struct H16Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int STAGES = STAGES_;
   static constexpr int GROUP_M = GROUP_M_;
-  static constexpr int NT = WAVES_M * WAVES_N * kWave;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * kWave;
   static constexpr int WTM = BM / WAVES_M;
   static constexpr int WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32;
   static constexpr int FN = WTN / 32;
-  static constexpr int SA = BK + 8;            // LDS row stride of A (halves)
-  static constexpr int SB = BK + 8;            // LDS row stride of B^T (halves)
-  static constexpr int A_ELEMS = BM * SA;
-  static constexpr int B_ELEMS = BN * SB;
-  static constexpr int A_CHUNKS = BM * BK / 8 / NT;        // 8-half chunks per thread
-  static constexpr int B_BLOCKS = (BK / 4) * (BN / 8) / NT;  // 4x8 blocks per thread
-  static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * 2;
+  static constexpr int SUB = BK / 16;                   // MFMA k sub-steps per K step
+  static constexpr int RA = 2 * BK;                     // bytes per A row in LDS
+  static constexpr int CA = BK / 8;                     // 16-byte chunks per A row
+  static constexpr int RPW = RA >= 256 ? 1 : 256 / RA;  // A rows per 256-byte bank window
+  static constexpr int RB = 2 * BN;                     // bytes per B row in LDS
+  static constexpr int A_BYTES = BM * RA;
+  static constexpr int B_BYTES = BK * RB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int QA = A_BYTES / 1024;             // 1 KB wave loads per A tile
+  static constexpr int QB = B_BYTES / 1024;
+  static constexpr int QA_W = QA / NWAVES;              // ... per wave
+  static constexpr int QB_W = QB / NWAVES;
+  static constexpr int LOADS = QA_W + QB_W;             // direct loads per wave per K step
+  static constexpr int EP_STRIDE = WTN + 4;             // epilogue staging row stride (floats)
+  static constexpr int EP_BYTES = 32 * EP_STRIDE * 4;   // per wave
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(BM % (WAVES_M * 32) == 0 && BN % (WAVES_N * 32) == 0, "wave tiling");
-  static_assert(BK % 16 == 0, "BK multiple of 16");
-  static_assert((BM * BK / 8) % NT == 0, "A load split");
-  static_assert(((BK / 4) * (BN / 8)) % NT == 0, "B load split");
-  static_assert(FN == 1 || FN == 2 || FN == 4, "FN");
+  static_assert(BK % 32 == 0 && SUB % 2 == 0, "BK multiple of 32");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
+  static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
+  static_assert(RB % 256 == 0, "B rows span whole bank windows");
+  static_assert(WTN % 64 == 0, "wave column origin multiple of 64");
+  static_assert(FM % 2 == 0, "the last sub-step splits the block rows in halves");
+  static_assert(STAGES >= 3, "the early barrier needs three or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NWAVES * EP_BYTES <= LDS_BYTES, "epilogue staging fits in the pipeline LDS");
+  static_assert(3 * LOADS <= 63, "vmcnt range");
 };
 
-// 8 halves from global memory, element-wise or as one 128-bit load.
+// Swizzles, chosen from measured gfx950 LDS behaviour: 64 banks of 4 bytes,
+// a 128-bit read served 16 lanes (256 bytes) per pass, a 64-bit transpose
+// read 32 lanes per pass.
+//   A: the 16 rows one pass reads must land on 16 distinct 16-byte bank
+//      groups of the 256-byte window: row r's chunks are XORed with
+//      (r / (256/RA)) % CA.
+//   B: a transpose-read pass covers four k rows x 64 bytes; XORing chunk
+//      bits 2-3 with kr % 4 puts the four rows' 64-byte pieces in the four
+//      quarters of the window.
+__device__ __forceinline__ int swz_b(int kr) { return 4 * (kr & 3); }
+
+template <class T>
+__device__ __forceinline__ int swz_a(int r) {
+  return (r / T::RPW) % T::CA;
+}
+
+// Tile-relative (row, column) of the global data behind 16-byte LDS chunk
+// (q, lane) of a slot's A region (row r, k column kc) or B region (k row kr,
+// column nc).
+template <class T>
+__device__ __forceinline__ void a_chunk(int q, int lane, int &r, int &kc) {
+  const int o = q * 1024 + 16 * lane;
+  r = o / T::RA;
+  const int p = (o % T::RA) / 16;
+  kc = 8 * (p ^ swz_a<T>(r));
+}
+
+template <class T>
+__device__ __forceinline__ void b_chunk(int q, int lane, int &kr, int &nc) {
+  const int o = q * 1024 + 16 * lane;
+  kr = o / T::RB;
+  const int p = (o % T::RB) / 16;
+  nc = 8 * (p ^ swz_b(kr));
+}
+
+// ---------------------------------------------------------------- direct loads
+
+// This lane's global source addresses for K step origin 0.
+template <class T>
+struct DirectAddr {
+  const uint16_t *a[T::QA_W];
+  const uint16_t *b[T::QB_W];
+};
+
+template <class T>
+__device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0,
+                                             DirectAddr<T> &d) {
+  const uint16_t *A = static_cast<const uint16_t *>(p.A);
+  const uint16_t *B = static_cast<const uint16_t *>(p.B);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int j = 0; j < T::QA_W; ++j) {
+    int r, kc;
+    a_chunk<T>(wave * T::QA_W + j, lane, r, kc);
+    int gr = m0 + r;
+    gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
+    d.a[j] = A + (size_t)gr * (size_t)p.lda + kc;
+  }
+#pragma unroll
+  for (int j = 0; j < T::QB_W; ++j) {
+    int kr, nc;
+    b_chunk<T>(wave * T::QB_W + j, lane, kr, nc);
+    int gn = n0 + nc;
+    gn = gn + 8 <= p.N ? gn : p.N - 8;     // N % 8 == 0 here: the last whole chunk
+    d.b[j] = B + (size_t)kr * (size_t)p.ldb + gn;
+  }
+}
+
+// One 16-byte direct global->LDS load per lane: lane L's 16 bytes land at LDS
+// byte address m0 + 16*L (m0 is wave-uniform).  The load is written as inline
+// assembly on purpose: the compiler's wait-count tracking then does not see
+// it, and does not drain every outstanding direct load before each LDS read.
+// Completion is ensured explicitly instead: each wave waits on vmcnt for its
+// own loads of a slot before the barrier that publishes the slot (the
+// kernel's only other vector-memory loads come before the direct loads or
+// after a full wait).  The build checks that no compiler-generated
+// instruction uses m0.
+__device__ __forceinline__ void direct_load16(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a pointer into the kernel's shared array.
+__device__ __forceinline__ uint32_t lds_address(const char *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+template <class T>
+__device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAddr<T> &d, int k0,
+                                             uint32_t slot_addr) {
+  const int wave = wave_id();
+  const size_t boff = (size_t)k0 * (size_t)p.ldb;
+#pragma unroll
+  for (int j = 0; j < T::QA_W; ++j)
+    direct_load16(d.a[j] + k0, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+#pragma unroll
+  for (int j = 0; j < T::QB_W; ++j)
+    direct_load16(d.b[j] + boff,
+                  slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+}
+
+// Barrier that does not wait for outstanding loads; the asm statement keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------- register-staged loads
+
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8(const uint16_t *src) {
   if (VEC) return *reinterpret_cast<const u32x4 *>(src);
@@ -67,7 +236,6 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *src) {
   return v;
 }
 
-// 8 halves with per-element predicate ok(e); 0 where it fails.
 template <class Ok>
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t *src, Ok ok) {
   u32x4 v;
@@ -80,248 +248,393 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *src, Ok ok) {
   return v;
 }
 
-template <class T, bool VEC, bool CHECK_M, bool CHECK_K>
-__device__ __forceinline__ void load_a(const GemmParams &p, int m0, int k0,
-                                       u32x4 (&ra)[T::A_CHUNKS]) {
+template <class T>
+struct RegTile {
+  u32x4 a[T::QA_W];
+  u32x4 b[T::QB_W];
+};
+
+// The chunks a direct load would fetch, through registers, with 0 for every
+// element outside the matrix (rows >= M, columns >= N, k >= K).
+template <class T, bool VA, bool VB>
+__device__ __forceinline__ void reg_load(const GemmParams &p, int m0, int n0, int k0,
+                                         RegTile<T> &t) {
   const uint16_t *A = static_cast<const uint16_t *>(p.A);
-  constexpr int CPR = T::BK / 8;
+  const uint16_t *B = static_cast<const uint16_t *>(p.B);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int i = 0; i < T::A_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    const int row = c / CPR;
-    const int kc = c % CPR;
-    const int gr = m0 + row;
-    const int gk = k0 + 8 * kc;
+  for (int j = 0; j < T::QA_W; ++j) {
+    int r, kc;
+    a_chunk<T>(wave * T::QA_W + j, lane, r, kc);
+    const int gr = m0 + r, gk = k0 + kc;
     const uint16_t *src = A + (size_t)gr * (size_t)p.lda + gk;
-    const bool row_ok = !CHECK_M || gr < p.M;
-    if (row_ok && (!CHECK_K || gk + 7 < p.K)) {
-      ra[i] = load8<VEC>(src);
+    const bool row_ok = gr < p.M;
+    if (row_ok && gk + 7 < p.K) {
+      t.a[j] = load8<VA>(src);
     } else {
       const int K = p.K;
-      ra[i] = load8_masked(src, [&](int e) { return row_ok && gk + e < K; });
+      t.a[j] = load8_masked(src, [&](int e) { return row_ok && gk + e < K; });
     }
   }
-}
-
-// B block b of this thread: k rows 4*kg..4*kg+3 of the tile, columns 8*ng..8*ng+7.
-template <class T>
-__device__ __forceinline__ void b_block_coords(int i, int &kg, int &ng) {
-  constexpr int KG = T::BK / 4;
-  const int blk = threadIdx.x + i * T::NT;
-  kg = blk % KG;
-  ng = blk / KG;
-}
-
-template <class T, bool VEC, bool CHECK_N, bool CHECK_K>
-__device__ __forceinline__ void load_b(const GemmParams &p, int n0, int k0,
-                                       u32x4 (&rb)[T::B_BLOCKS][4]) {
-  const uint16_t *B = static_cast<const uint16_t *>(p.B);
 #pragma unroll
-  for (int i = 0; i < T::B_BLOCKS; ++i) {
-    int kg, ng;
-    b_block_coords<T>(i, kg, ng);
-    const int gn = n0 + 8 * ng;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int gk = k0 + 4 * kg + r;
-      const uint16_t *src = B + (size_t)gk * (size_t)p.ldb + gn;
-      const bool k_ok = !CHECK_K || gk < p.K;
-      if (k_ok && (!CHECK_N || gn + 7 < p.N)) {
-        rb[i][r] = load8<VEC>(src);
-      } else {
-        const int N = p.N;
-        rb[i][r] = load8_masked(src, [&](int e) { return k_ok && gn + e < N; });
-      }
-    }
-  }
-}
-
-// LDS row of B^T that holds tile column n (see the interleaving note above).
-template <class T>
-__device__ __forceinline__ int bt_row(int n) {
-  const int w = n / T::WTN;
-  const int c = n % T::WTN;
-  return w * T::WTN + 32 * (c % T::FN) + c / T::FN;
-}
-
-template <class T>
-__device__ __forceinline__ void store_lds(uint16_t *As, uint16_t *Bs, const u32x4 (&ra)[T::A_CHUNKS],
-                                          const u32x4 (&rb)[T::B_BLOCKS][4]) {
-  constexpr int CPR = T::BK / 8;
-#pragma unroll
-  for (int i = 0; i < T::A_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    *reinterpret_cast<u32x4 *>(&As[(c / CPR) * T::SA + 8 * (c % CPR)]) = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < T::B_BLOCKS; ++i) {
-    int kg, ng;
-    b_block_coords<T>(i, kg, ng);
-    // Transpose the 4 x 8 block: column c8 becomes the 4-half run
-    // (B[k+0][c8], B[k+1][c8], B[k+2][c8], B[k+3][c8]).
-#pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
-      const int sh = 16 * (c8 % 2);
-      const uint32_t h0 = (rb[i][0][c8 / 2] >> sh) & 0xffffu;
-      const uint32_t h1 = (rb[i][1][c8 / 2] >> sh) & 0xffffu;
-      const uint32_t h2 = (rb[i][2][c8 / 2] >> sh) & 0xffffu;
-      const uint32_t h3 = (rb[i][3][c8 / 2] >> sh) & 0xffffu;
-      u32x2 run;
-      run[0] = h0 | (h1 << 16);
-      run[1] = h2 | (h3 << 16);
-      *reinterpret_cast<u32x2 *>(&Bs[bt_row<T>(8 * ng + c8) * T::SB + 4 * kg]) = run;
+  for (int j = 0; j < T::QB_W; ++j) {
+    int kr, nc;
+    b_chunk<T>(wave * T::QB_W + j, lane, kr, nc);
+    const int gk = k0 + kr, gn = n0 + nc;
+    const uint16_t *src = B + (size_t)gk * (size_t)p.ldb + gn;
+    const bool k_ok = gk < p.K;
+    if (k_ok && gn + 7 < p.N) {
+      t.b[j] = load8<VB>(src);
+    } else {
+      const int N = p.N;
+      t.b[j] = load8_masked(src, [&](int e) { return k_ok && gn + e < N; });
     }
   }
 }
 
 template <class T>
-__device__ __forceinline__ void compute_tile(const uint16_t *As, const uint16_t *Bs, int wm0,
-                                             int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+__device__ __forceinline__ void reg_store(const RegTile<T> &t, char *slot) {
+  const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32;
-  const int lh = lane / 32;
 #pragma unroll
-  for (int kk = 0; kk < T::BK; kk += 16) {
-    f16x8 a[T::FM], b[T::FN];
+  for (int j = 0; j < T::QA_W; ++j)
+    *reinterpret_cast<u32x4 *>(slot + (wave * T::QA_W + j) * 1024 + 16 * lane) = t.a[j];
 #pragma unroll
-    for (int bi = 0; bi < T::FM; ++bi)
-      a[bi] = *reinterpret_cast<const f16x8 *>(&As[(wm0 + 32 * bi + li) * T::SA + kk + 8 * lh]);
+  for (int j = 0; j < T::QB_W; ++j)
+    *reinterpret_cast<u32x4 *>(slot + T::A_BYTES + (wave * T::QB_W + j) * 1024 + 16 * lane) =
+        t.b[j];
+}
+
+// ---------------------------------------------------------------- fragments and MFMA
+
+template <class T>
+struct Frag {
+  f16x8 a[T::FM];
+  f16x8 b[T::FN];
+};
+
+// Per-lane LDS byte offsets of the fragments, relative to a slot.
+template <class T>
+struct FragAddr {
+  int a[T::SUB];   // A block 0 at sub-step s; block bi adds 32*bi*RA
+  int b[T::FN];    // B block bj at sub-step 0, first transpose read
+};
+
+template <class T>
+__device__ __forceinline__ void frag_setup(int wm0, int wn0, FragAddr<T> &f) {
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 32, lh = lane / 32;
+  const int r = wm0 + li;
+  const int sa = swz_a<T>(r);
+#pragma unroll
+  for (int s = 0; s < T::SUB; ++s) f.a[s] = r * T::RA + 16 * ((2 * s + lh) ^ sa);
+  // B: 16-lane group g reads k rows 8*(g/2) + 4*rd + i/4 and columns
+  // wn0 + 32*bj + 16*(g%2) + 4*(i%4) .. +3 (i = lane % 16).
+  const int g = lane / 16, i = lane % 16;
+  const int kr = 8 * (g / 2) + i / 4;
+  const int t = 2 * (g % 2) + (i % 4) / 2;
+  const int sb = swz_b(kr);
+#pragma unroll
+  for (int bj = 0; bj < T::FN; ++bj)
+    f.b[bj] = T::A_BYTES + kr * T::RB + 16 * ((wn0 / 8 + 4 * bj + t) ^ sb) + 8 * (i % 2);
+}
+
+// Fragment reads in the order the MFMAs consume them (A block 0, all B
+// blocks, then A blocks 1..), so the waits before early MFMAs stay short.
+template <class T>
+__device__ __forceinline__ void frag_read(const char *slot, const FragAddr<T> &f, int s,
+                                          Frag<T> &fr) {
+  fr.a[0] = *reinterpret_cast<const f16x8 *>(slot + f.a[s]);
+#pragma unroll
+  for (int bj = 0; bj < T::FN; ++bj) {
+    const char *base = slot + f.b[bj] + 16 * s * T::RB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 4 * T::RB));
+    fr.b[bj] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+#pragma unroll
+  for (int bi = 1; bi < T::FM; ++bi)
+    fr.a[bi] = *reinterpret_cast<const f16x8 *>(slot + f.a[s] + 32 * bi * T::RA);
+}
+
+// MFMAs for block rows [BI0, BI1) of one sub-step.
+template <class T, int BI0, int BI1>
+__device__ __forceinline__ void mfma_rows(const Frag<T> &fr, f32x16 (&acc)[T::FM][T::FN]) {
+#pragma unroll
+  for (int bi = BI0; bi < BI1; ++bi)
 #pragma unroll
     for (int bj = 0; bj < T::FN; ++bj)
-      b[bj] = *reinterpret_cast<const f16x8 *>(&Bs[(wn0 + 32 * bj + li) * T::SB + kk + 8 * lh]);
-#pragma unroll
-    for (int bi = 0; bi < T::FM; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < T::FN; ++bj)
-        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+      acc[bi][bj] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+}
+
+// Scheduling pattern for a region holding NM MFMAs and NR LDS reads: the
+// reads are spread evenly behind the first NM - TAIL MFMAs, so they trickle
+// into the LDS queue behind MFMAs instead of stalling the wave in front of
+// them, and the last of them is issued TAIL MFMAs before the region ends.
+template <int I, int NM, int NR, int TAIL>
+__device__ __forceinline__ void interleave_slot() {
+  if constexpr (I < NM) {
+    constexpr int SLOTS = NM - TAIL > 0 ? NM - TAIL : 1;
+    constexpr int PER = (NR + SLOTS - 1) / SLOTS;
+    constexpr int LEFT = NR - I * PER;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+    if constexpr (I < SLOTS && LEFT > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, LEFT < PER ? LEFT : PER, 0);  // DS reads
+    interleave_slot<I + 1, NM, NR, TAIL>();
   }
 }
 
+template <int NM, int NR, int TAIL>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  interleave_slot<0, NM, NR, TAIL>();
+}
+
+// ---------------------------------------------------------------- epilogue
+
 template <class T, bool VEC_C, bool CHECK>
-__device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0,
+__device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, char *lds,
                                          const f32x16 (&acc)[T::FM][T::FN]) {
   uint16_t *C = static_cast<uint16_t *>(p.C);
+  const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32;
-  const int lh = lane / 32;
-  const int col = c0 + T::FN * li;
+  const int li = lane % 32, lh = lane / 32;
+  float *stage = reinterpret_cast<float *>(lds + wave * T::EP_BYTES);
   const float alpha = p.alpha, beta = p.beta;
-  const bool cols_ok = !CHECK || col + T::FN - 1 < p.N;
+  constexpr int LPR = T::WTN / 4;                 // lanes per staged row
+  constexpr int ROWS_PER_PASS = kWave / LPR;
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + 32 * bi + 8 * (r / 4) + 4 * lh + (r % 4);
+    for (int bj = 0; bj < T::FN; ++bj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[bi][bj][r];
+#pragma unroll
+    for (int pass = 0; pass < 32 / ROWS_PER_PASS; ++pass) {
+      const int rl = pass * ROWS_PER_PASS + lane / LPR;
+      const int cl = 4 * (lane % LPR);
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(&stage[rl * T::EP_STRIDE + cl]);
+      const int row = r0 + 32 * bi + rl;
+      const int col = c0 + cl;
       if (CHECK && row >= p.M) continue;
       uint16_t *dst = C + (size_t)row * (size_t)p.ldc + col;
-      if (VEC_C && cols_ok) {
-        // FN adjacent halves: one 2*FN-byte access.
-        uint16_t cin[T::FN];
+      if (VEC_C && (!CHECK || col + 3 < p.N)) {
+        float o[4];
         if (beta != 0.0f) {
-          if constexpr (T::FN == 4) {
-            const u32x2 w = *reinterpret_cast<const u32x2 *>(dst);
-            cin[0] = w[0] & 0xffff; cin[1] = w[0] >> 16; cin[2] = w[1] & 0xffff; cin[3] = w[1] >> 16;
-          } else if constexpr (T::FN == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(dst);
-            cin[0] = w & 0xffff; cin[1] = w >> 16;
-          } else {
-            cin[0] = dst[0];
-          }
-        }
-        uint16_t out[T::FN];
-#pragma unroll
-        for (int bj = 0; bj < T::FN; ++bj) {
-          float v = alpha * acc[bi][bj][r];
-          if (beta != 0.0f) v = __builtin_fmaf(beta, f16_bits_to_f32(cin[bj]), v);
-          out[bj] = f32_to_f16_bits(v);
-        }
-        if constexpr (T::FN == 4) {
-          u32x2 w;
-          w[0] = (uint32_t)out[0] | ((uint32_t)out[1] << 16);
-          w[1] = (uint32_t)out[2] | ((uint32_t)out[3] << 16);
-          *reinterpret_cast<u32x2 *>(dst) = w;
-        } else if constexpr (T::FN == 2) {
-          *reinterpret_cast<uint32_t *>(dst) = (uint32_t)out[0] | ((uint32_t)out[1] << 16);
+          const u32x2 w = *reinterpret_cast<const u32x2 *>(dst);
+          o[0] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] & 0xffff)), alpha * v[0]);
+          o[1] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] >> 16)), alpha * v[1]);
+          o[2] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[1] & 0xffff)), alpha * v[2]);
+          o[3] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[1] >> 16)), alpha * v[3]);
         } else {
-          dst[0] = out[0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
         }
+        u32x2 w;
+        w[0] = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
+        w[1] = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
+        *reinterpret_cast<u32x2 *>(dst) = w;
       } else {
 #pragma unroll
-        for (int bj = 0; bj < T::FN; ++bj) {
-          if (CHECK && col + bj >= p.N) continue;
-          float v = alpha * acc[bi][bj][r];
-          if (beta != 0.0f) v = __builtin_fmaf(beta, f16_bits_to_f32(dst[bj]), v);
-          dst[bj] = f32_to_f16_bits(v);
+        for (int e = 0; e < 4; ++e) {
+          if (CHECK && col + e >= p.N) continue;
+          float o = alpha * v[e];
+          if (beta != 0.0f) o = __builtin_fmaf(beta, f16_bits_to_f32(dst[e]), o);
+          dst[e] = f32_to_f16_bits(o);
         }
       }
     }
   }
 }
 
-template <class T, bool VA, bool VB, bool EDGE, bool CHECK_K>
-__device__ __forceinline__ void load_tiles(const GemmParams &p, int m0, int n0, int k0,
-                                           u32x4 (&ra)[T::A_CHUNKS], u32x4 (&rb)[T::B_BLOCKS][4]) {
-  load_a<T, VA, EDGE, CHECK_K>(p, m0, k0, ra);
-  load_b<T, VB, EDGE, CHECK_K>(p, n0, k0, rb);
+// ---------------------------------------------------------------- main loops
+
+// K step kt covers [k0(kt), k0(kt) + BK); when K % BK != 0 the partial step
+// comes first, then the full steps from k = 0.
+struct KSteps {
+  int nk, nfull, tail, bk;
+  __device__ __forceinline__ int k0(int kt) const {
+    return tail ? (kt == 0 ? nfull * bk : (kt - 1) * bk) : kt * bk;
+  }
+};
+
+template <class T>
+__device__ __forceinline__ KSteps make_steps(int K) {
+  KSteps s;
+  s.bk = T::BK;
+  s.nfull = K / T::BK;
+  s.tail = K % T::BK;
+  s.nk = s.nfull + (s.tail ? 1 : 0);
+  return s;
 }
 
-template <class T, bool VA, bool VB, bool VC, bool EDGE>
-__device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, uint16_t *lds) {
-  uint16_t *As = lds;
-  uint16_t *Bs = lds + 2 * T::A_ELEMS;
-  const int wave = threadIdx.x / kWave;
-  const int wm0 = (wave / T::WAVES_N) * T::WTM;
-  const int wn0 = (wave % T::WAVES_N) * T::WTN;
-
-  f32x16 acc[T::FM][T::FN];
+template <class T>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi)
 #pragma unroll
     for (int bj = 0; bj < T::FN; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+}
 
-  const int nk = (p.K + T::BK - 1) / T::BK;
-  const int nfull = p.K / T::BK;
-  u32x4 ra[T::A_CHUNKS];
-  u32x4 rb[T::B_BLOCKS][4];
-
-  if (nfull > 0) load_tiles<T, VA, VB, EDGE, false>(p, m0, n0, 0, ra, rb);
-  else load_tiles<T, VA, VB, EDGE, true>(p, m0, n0, 0, ra, rb);
-  store_lds<T>(As, Bs, ra, rb);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k1 = (kt + 1) * T::BK;
-      if (kt + 1 < nfull) load_tiles<T, VA, VB, EDGE, false>(p, m0, n0, k1, ra, rb);
-      else load_tiles<T, VA, VB, EDGE, true>(p, m0, n0, k1, ra, rb);
+// All sub-steps of one K step from LDS slot `slot`.  On entry fr[0] holds
+// sub-step 0.  Each sub-step's MFMAs run interleaved with the reads of the
+// next sub-step's fragments.  In the last sub-step the first half of the MFMAs
+// is issued, then `next()` publishes the following slot (its barrier wait
+// overlaps those MFMAs) and may issue loads, then sub-step 0 of the following
+// K step is read from `next_slot` into fr[0] between the remaining MFMAs.  On
+// the last K step this reads a stale slot whose values are never used:
+// keeping the reads unconditional keeps the LDS wait counts exact.
+template <class T, class Next>
+__device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
+                                      const FragAddr<T> &fa, Frag<T> (&fr)[2],
+                                      f32x16 (&acc)[T::FM][T::FN], Next next) {
+  constexpr int NREAD = T::FM + 2 * T::FN;     // LDS instructions per sub-step
+  constexpr int HALF = T::FM / 2;
+#pragma unroll
+  for (int s = 0; s < T::SUB; ++s) {
+    if (s + 1 < T::SUB) {
+      frag_read<T>(slot, fa, s + 1, fr[(s + 1) & 1]);
+      mfma_rows<T, 0, T::FM>(fr[s & 1], acc);
+      interleave_mfma_reads<T::FM * T::FN, NREAD, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      mfma_rows<T, 0, HALF>(fr[s & 1], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      next();
+      frag_read<T>(next_slot, fa, 0, fr[0]);
+      mfma_rows<T, HALF, T::FM>(fr[s & 1], acc);
+      interleave_mfma_reads<(T::FM - HALF) * T::FN, NREAD, 2>();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    compute_tile<T>(As + cur * T::A_ELEMS, Bs + cur * T::B_ELEMS, wm0, wn0, acc);
-    if (more) store_lds<T>(As + (cur ^ 1) * T::A_ELEMS, Bs + (cur ^ 1) * T::B_ELEMS, ra, rb);
-    __syncthreads();
   }
+}
 
-  epilogue<T, VC, EDGE>(p, m0 + wm0, n0 + wn0, acc);
+// Direct-load pipeline over STAGES slots.
+template <class T>
+__device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
+                                                uint32_t lds_u32, int wm0, int wn0,
+                                                f32x16 (&acc)[T::FM][T::FN]) {
+  const KSteps ks = make_steps<T>(p.K);
+  DirectAddr<T> da;
+  direct_setup<T>(p, m0, n0, da);
+  FragAddr<T> fa;
+  frag_setup<T>(wm0, wn0, fa);
+
+  // Prologue: step 0 (masked, through registers, when it is the partial
+  // step), then direct loads of steps 1 .. STAGES-2.
+  if (ks.tail) {
+    RegTile<T> t;
+    reg_load<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_store<T>(t, lds);
+  } else {
+    direct_issue<T>(p, da, ks.k0(0), lds_u32);
+  }
+  int issued = 1;
+#pragma unroll
+  for (int j = 1; j < T::STAGES - 1; ++j) {
+    if (j < ks.nk) {
+      direct_issue<T>(p, da, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      ++issued;
+    }
+  }
+  // Publish step 0; the loads of steps 1.. may stay in flight.
+  switch (issued - 1) {
+    case 0: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0); break;
+  }
+  lds_barrier();
+
+  Frag<T> fr[2];
+  frag_read<T>(lds, fa, 0, fr[0]);
+
+  for (int kt = 0; kt < ks.nk; ++kt) {
+    const char *slot = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+    kstep<T>(slot, next_slot, fa, fr, acc, [&]() {
+      // Step kt+1 must have landed; steps issued after it may stay in flight.
+      // (After the last step nothing is in flight and this is a full wait.)
+      const int after = (issued - 1) - (kt + 1);
+      if (after <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
+      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS));
+      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS));
+      lds_barrier();
+      // Every wave has consumed step kt-1: its slot takes step kt+STAGES-1.
+      const int nx = kt + T::STAGES - 1;
+      if (nx < ks.nk) {
+        direct_issue<T>(p, da, ks.k0(nx), lds_u32 + (uint32_t)((nx % T::STAGES) * T::STAGE_BYTES));
+        ++issued;
+      }
+    });
+  }
+}
+
+// Register-staged double-buffered pipeline (unaligned operands, ragged N).
+template <class T, bool VA, bool VB>
+__device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int n0, char *lds,
+                                                int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+  const KSteps ks = make_steps<T>(p.K);
+  FragAddr<T> fa;
+  frag_setup<T>(wm0, wn0, fa);
+  RegTile<T> t;
+  reg_load<T, VA, VB>(p, m0, n0, ks.k0(0), t);
+  reg_store<T>(t, lds);
+  __syncthreads();
+  Frag<T> fr[2];
+  frag_read<T>(lds, fa, 0, fr[0]);
+  for (int kt = 0; kt < ks.nk; ++kt) {
+    const char *slot = lds + (kt % 2) * T::STAGE_BYTES;
+    char *nslot = lds + ((kt + 1) % 2) * T::STAGE_BYTES;
+    if (kt + 1 < ks.nk) reg_load<T, VA, VB>(p, m0, n0, ks.k0(kt + 1), t);
+    // nslot was last read in step kt-1, before that step's barrier.  On the
+    // last step the store repeats old data into a slot nobody reads again.
+    kstep<T>(slot, nslot, fa, fr, acc, [&]() {
+      reg_store<T>(t, nslot);
+      __syncthreads();
+    });
+  }
 }
 
 template <class T, bool VA, bool VB, bool VC>
 __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (T::A_ELEMS + T::B_ELEMS)];
+  __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   int tm, tn;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
-  const bool edge = (m0 + T::BM > p.M) || (n0 + T::BN > p.N);
-  if (edge) mainloop<T, VA, VB, VC, true>(p, m0, n0, lds);
-  else mainloop<T, VA, VB, VC, false>(p, m0, n0, lds);
+  const int wave = threadIdx.x / kWave;
+  const int wm0 = (wave / T::WAVES_N) * T::WTM;
+  const int wn0 = (wave % T::WAVES_N) * T::WTN;
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+
+  const bool n_edge = n0 + T::BN > p.N;
+  const bool direct = VA && VB && (!n_edge || (p.N % 8) == 0);
+  if (direct) mainloop_direct<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+  else mainloop_staged<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();   // every wave is done with the pipeline slots
+  const bool edge = n_edge || (m0 + T::BM > p.M);
+  if (edge) epilogue<T, VC, true>(p, m0 + wm0, n0 + wn0, lds, acc);
+  else epilogue<T, VC, false>(p, m0 + wm0, n0 + wn0, lds, acc);
 }
 
 // ---------------------------------------------------------------- host side
 
-typedef F16Tile<256, 256, 32, 2, 2, 4> F16Main;
+// Tile configuration: BM, BN, BK, waves along M, waves along N, LDS slots,
+// L2 group rows.
+#ifndef DGEMM_F16_TILE
+#define DGEMM_F16_TILE 256, 256, 32, 2, 4, 4, 4
+#endif
+typedef H16Tile<DGEMM_F16_TILE> F16Main;
+#define DGEMM_STR2(...) #__VA_ARGS__
+#define DGEMM_STR(...) DGEMM_STR2(__VA_ARGS__)
 
 static bool vec_ok(const void *p, int ld, int elems) {
   return (ld % elems) == 0 && aligned_to(p, (uintptr_t)elems * 2);
@@ -337,10 +650,10 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.threads = T::NT;
   const bool va = !c.force_scalar && vec_ok(c.A, c.lda, 8);
   const bool vb = !c.force_scalar && vec_ok(c.B, c.ldb, 8);
-  const bool vc = !c.force_scalar && T::FN > 1 && vec_ok(c.C, c.ldc, T::FN);
+  const bool vc = !c.force_scalar && vec_ok(c.C, c.ldc, 4);
   pl.vec_a = va ? 8 : 1;
   pl.vec_b = vb ? 8 : 1;
-  pl.vec_c = vc ? T::FN : 1;
+  pl.vec_c = vc ? 4 : 1;
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
   pl.blocks = tm * tn;
@@ -387,7 +700,7 @@ static hipError_t dispatch(const Call &c) {
 }
 
 Plan plan_f16(const Call &c) {
-  return make_plan<F16Main>(c, "f16 mfma32x32x16 256x256x32 waves2x2");
+  return make_plan<F16Main>(c, "f16 mfma32x32x16 tile " DGEMM_STR(DGEMM_F16_TILE));
 }
 
 hipError_t launch_f16(const Call &c) { return dispatch<F16Main>(c); }

@@ -289,7 +289,13 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 
 // ---------------------------------------------------------------- host side
 
-typedef F32Tile<128, 128, 32, 2, 2, 8> F32Main;
+// Tile configuration: BM, BN, BK, waves along M, waves along N, L2 group rows.
+#ifndef DGEMM_F32_TILE
+#define DGEMM_F32_TILE 128, 128, 32, 2, 2, 8
+#endif
+typedef F32Tile<DGEMM_F32_TILE> F32Main;
+#define DGEMM_STR2(...) #__VA_ARGS__
+#define DGEMM_STR(...) DGEMM_STR2(__VA_ARGS__)
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
   return (ld % elems) == 0 && aligned_to(p, (uintptr_t)elems * bytes_per_elem);
@@ -355,7 +361,7 @@ static hipError_t dispatch(const Call &c) {
 }
 
 Plan plan_f32(const Call &c) {
-  return make_plan<F32Main>(c, "f32 mfma32x32x2 128x128x32 waves2x2");
+  return make_plan<F32Main>(c, "f32 mfma32x32x2 tile " DGEMM_STR(DGEMM_F32_TILE));
 }
 
 hipError_t launch_f32(const Call &c) { return dispatch<F32Main>(c); }
