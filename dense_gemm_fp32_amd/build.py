@@ -7,6 +7,7 @@ dense_gemm_fp32_amd/libgemm.so next to this file.
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -40,9 +41,45 @@ def _compile(src, verbose=False):
     return obj
 
 
+# Sources that set m0 in inline assembly (the fp16 kernel's direct
+# global->LDS loads).  m0 is a register the compiler reserves for itself, so the
+# build verifies that no compiler-generated instruction in these sources
+# touches it: the asm's m0 writes then cannot disturb compiled code.
+M0_ASM_SOURCES = ["gemm_f16.hip"]
+
+
+def check_m0_only_in_asm(src):
+    """Compile `src` to gfx950 assembly and verify that every instruction
+    mentioning m0 lies inside an inline-asm block.  Raises RuntimeError."""
+    cmd = [HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed on %s:\n%s" % (src, r.stderr))
+    inside = False
+    bad = []
+    for n, line in enumerate(r.stdout.splitlines(), 1):
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not t or t.startswith((";", ".")):
+            continue
+        code = t.split(";", 1)[0]
+        if not inside and re.search(r"\bm0\b", code):
+            bad.append("%d: %s" % (n, t))
+    if bad:
+        raise RuntimeError("compiler-generated code uses m0 in %s (inline asm clobbers it):\n%s"
+                           % (src, "\n".join(bad[:20])))
+
+
 def build(verbose=False):
     """Compile all sources and link libgemm.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    for src in M0_ASM_SOURCES:
+        check_m0_only_in_asm(src)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()

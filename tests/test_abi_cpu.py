@@ -145,3 +145,12 @@ def test_missing_library_fails_loudly(tmp_path):
             str(tmp_path))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_only_inline_asm_touches_m0():
+    """The fp16 kernel sets m0 in inline assembly; no compiler-generated
+    instruction of that translation unit may use m0 (checked on the gfx950
+    assembly of the current source)."""
+    from dense_gemm_fp32_amd import build as b
+    for src in b.M0_ASM_SOURCES:
+        b.check_m0_only_in_asm(src)

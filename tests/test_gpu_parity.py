@@ -281,3 +281,57 @@ def test_torch_wrapper_matches_raw_call():
                        B.cpu().numpy().reshape(-1), 555, 0.0, None, 555)
     tol = oracle.tolerance(G, 0.0, 1.0, 0.0, 444, R)
     assert oracle.compare(C.cpu().numpy(), R, tol)[0]
+
+
+# ---------------------------------------------------------------- fp16 load paths
+
+# Leading dimensions that are multiples of 8 halves (16-byte rows) send the
+# fp16 kernel's interior tiles through direct global->LDS loads; these shapes
+# put every edge case of that path in play: rows past M (clamped reads), a
+# column edge with N % 8 == 0 (clamped chunks) and != 0 (that tile column
+# takes the masked register path while the others stay direct), a partial K
+# step (done first, masked), K shorter than one step, and exact multiples.
+F16_PATH_SHAPES = [
+    # M,    N,   K,  lda, ldb, ldc
+    (300, 264, 100, 104, 264, 264),
+    (257, 512, 64, 64, 512, 520),
+    (600, 530, 96, 96, 536, 536),
+    (256, 256, 17, 24, 256, 256),
+    (513, 776, 1000, 1000, 776, 784),
+    (64, 1024, 544, 552, 1024, 1024),
+]
+
+
+@pytest.mark.parametrize("shape", F16_PATH_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_direct_path_edges_match_oracle_and_staged_path(shape):
+    import dense_gemm_fp32_amd as dg
+    M, N, K, lda, ldb, ldc = shape
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(np.float16), lda, np.nan)
+    B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(np.float16), ldb, np.nan)
+    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(np.float16), ldc, wl.C_PAD_SENTINEL)
+    rc, out_direct = run("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 direct")
+    assert rc == 0
+    check("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, out_direct, "direct %s" % (shape,))
+    prev = dg.gemm_set_load_mode(1)
+    try:
+        rc, out_staged = run("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 staged")
+    finally:
+        dg.gemm_set_load_mode(prev)
+    assert rc == 0
+    # same LDS layout and summation order on both paths: identical bits
+    assert np.array_equal(bits(out_direct, "f16"), bits(out_staged, "f16"))
+
+
+def test_f16_nan_in_a_row_past_m_is_not_read():
+    """Rows past M are clamped to row M-1 on the direct path: a NaN placed in
+    the memory right after A's last row must not reach C."""
+    M, N, K = 200, 256, 64
+    rng = np.random.default_rng(5)
+    A = np.concatenate([rng.uniform(-1, 1, M * K).astype(np.float16),
+                        np.full(64 * K, np.nan, np.float16)])
+    B = rng.uniform(-1, 1, K * N).astype(np.float16)
+    C = np.zeros(M * N, np.float16)
+    rc, out = run("f16", M, N, K, 1.0, A, K, B, N, 0.0, C, N, "rows past M")
+    assert rc == 0
+    check("f16", M, N, K, 1.0, A, K, B, N, 0.0, C, N, out, "rows past M")
