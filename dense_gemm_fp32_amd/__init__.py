@@ -8,7 +8,8 @@ without the library; using the GEMM entry points without a built library
 raises ImportError.
 """
 _BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe",
-                  "gemm_set_load_mode", "gemm", "GemmError", "LIB_PATH", "EXPORTS")
+                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm", "GemmError", "LIB_PATH",
+                  "EXPORTS")
 
 __all__ = list(_BINDING_NAMES)
 

@@ -33,8 +33,11 @@ _lib.gemm_describe.argtypes = [_I, _I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, c
 _lib.gemm_describe.restype = _I
 _lib.gemm_set_load_mode.argtypes = [_I]
 _lib.gemm_set_load_mode.restype = _I
+_lib.gemm_set_tile_config.argtypes = [_I]
+_lib.gemm_set_tile_config.restype = _I
 
-EXPORTS = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode")
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
+           "gemm_set_tile_config")
 
 
 class GemmError(RuntimeError):
@@ -90,6 +93,12 @@ def gemm_describe(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
 def gemm_set_load_mode(mode):
     """0 = vector/scalar loads by alignment (default), 1 = force scalar."""
     return _lib.gemm_set_load_mode(int(mode))
+
+
+def gemm_set_tile_config(config):
+    """0 = tile configuration by problem size (default); 1/2/3 = force the
+    large/medium/small configuration."""
+    return _lib.gemm_set_tile_config(int(config))
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):

@@ -41,11 +41,11 @@ def _compile(src, verbose=False):
     return obj
 
 
-# Sources that set m0 in inline assembly (the fp16 kernel's direct
+# Sources that set m0 in inline assembly (the kernels' direct
 # global->LDS loads).  m0 is a register the compiler reserves for itself, so the
 # build verifies that no compiler-generated instruction in these sources
 # touches it: the asm's m0 writes then cannot disturb compiled code.
-M0_ASM_SOURCES = ["gemm_f16.hip"]
+M0_ASM_SOURCES = ["gemm_f16.hip", "gemm_f32.hip"]
 
 
 def check_m0_only_in_asm(src):

@@ -16,6 +16,7 @@
 namespace {
 
 std::atomic<int> g_load_mode{0};
+std::atomic<int> g_tile_config{0};
 
 // Shared argument checks.  `elem_bytes` only matters for descriptions.
 int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
@@ -58,6 +59,7 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.C = C;
   c.ldc = ldc;
   c.force_scalar = g_load_mode.load(std::memory_order_relaxed) == 1;
+  c.tile_config = g_tile_config.load(std::memory_order_relaxed);
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -159,6 +161,11 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
 int gemm_set_load_mode(int mode) {
   if (mode != 0 && mode != 1) return -1;
   return g_load_mode.exchange(mode);
+}
+
+int gemm_set_tile_config(int config) {
+  if (config < 0 || config > 3) return -1;
+  return g_tile_config.exchange(config);
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kCUs = 256;       // MI355X compute units (tile-size choice)
 
 // Kernel arguments (passed by value; lives in the kernarg segment).
 struct GemmParams {
@@ -70,6 +71,69 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
+}
+
+
+// ---------------------------------------------------------------- pipeline helpers
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); counters not waited on are set to their maxima.
+constexpr int wait_vmcnt(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
+}
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+constexpr int kWaitAll = 0;
+
+// One 16-byte direct global->LDS load per lane: lane L's 16 bytes land at LDS
+// byte address m0 + 16*L (m0 is wave-uniform).  The load is written as inline
+// assembly on purpose: the compiler's wait-count tracking then does not see
+// it, and does not drain every outstanding direct load before each LDS read.
+// Completion is ensured explicitly instead: each wave waits on vmcnt for its
+// own loads of a slot before the barrier that publishes the slot (the
+// kernel's only other vector-memory loads come before the direct loads or
+// after a full wait).  The build checks that no compiler-generated
+// instruction uses m0.
+__device__ __forceinline__ void direct_load16(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a pointer into the kernel's shared array.
+__device__ __forceinline__ uint32_t lds_address(const char *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// Barrier that does not wait for outstanding loads; the asm statement keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// K step kt covers [k0(kt), k0(kt) + BK); when K % BK != 0 the partial step
+// comes first, then the full steps from k = 0.
+struct KSteps {
+  int nk, nfull, tail, bk;
+  __device__ __forceinline__ int k0(int kt) const {
+    return tail ? (kt == 0 ? nfull * bk : (kt - 1) * bk) : kt * bk;
+  }
+};
+
+__device__ __forceinline__ KSteps make_steps(int K, int BK) {
+  KSteps s;
+  s.bk = BK;
+  s.nfull = K / BK;
+  s.tail = K % BK;
+  s.nk = s.nfull + (s.tail ? 1 : 0);
+  return s;
 }
 
 }  // namespace dgemm

@@ -59,14 +59,6 @@ namespace dgemm {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
-// [6:4], lgkmcnt [11:8]); counters not waited on are set to their maxima.
-constexpr int wait_vmcnt(int n) {
-  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
-}
-constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
-constexpr int kWaitAll = 0;
-
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_>
 struct H16Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -177,32 +169,6 @@ __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0
   }
 }
 
-// One 16-byte direct global->LDS load per lane: lane L's 16 bytes land at LDS
-// byte address m0 + 16*L (m0 is wave-uniform).  The load is written as inline
-// assembly on purpose: the compiler's wait-count tracking then does not see
-// it, and does not drain every outstanding direct load before each LDS read.
-// Completion is ensured explicitly instead: each wave waits on vmcnt for its
-// own loads of a slot before the barrier that publishes the slot (the
-// kernel's only other vector-memory loads come before the direct loads or
-// after a full wait).  The build checks that no compiler-generated
-// instruction uses m0.
-__device__ __forceinline__ void direct_load16(const void *gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-// LDS byte address of a pointer into the kernel's shared array.
-__device__ __forceinline__ uint32_t lds_address(const char *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-}
-
-// Wave index as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-}
-
 template <class T>
 __device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAddr<T> &d, int k0,
                                              uint32_t slot_addr) {
@@ -215,14 +181,6 @@ __device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAd
   for (int j = 0; j < T::QB_W; ++j)
     direct_load16(d.b[j] + boff,
                   slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
-}
-
-// Barrier that does not wait for outstanding loads; the asm statement keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------- register-staged loads
@@ -451,25 +409,6 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
 
 // ---------------------------------------------------------------- main loops
 
-// K step kt covers [k0(kt), k0(kt) + BK); when K % BK != 0 the partial step
-// comes first, then the full steps from k = 0.
-struct KSteps {
-  int nk, nfull, tail, bk;
-  __device__ __forceinline__ int k0(int kt) const {
-    return tail ? (kt == 0 ? nfull * bk : (kt - 1) * bk) : kt * bk;
-  }
-};
-
-template <class T>
-__device__ __forceinline__ KSteps make_steps(int K) {
-  KSteps s;
-  s.bk = T::BK;
-  s.nfull = K / T::BK;
-  s.tail = K % T::BK;
-  s.nk = s.nfull + (s.tail ? 1 : 0);
-  return s;
-}
-
 template <class T>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
 #pragma unroll
@@ -518,7 +457,7 @@ template <class T>
 __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
                                                 uint32_t lds_u32, int wm0, int wn0,
                                                 f32x16 (&acc)[T::FM][T::FN]) {
-  const KSteps ks = make_steps<T>(p.K);
+  const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr<T> da;
   direct_setup<T>(p, m0, n0, da);
   FragAddr<T> fa;
@@ -578,7 +517,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
 template <class T, bool VA, bool VB>
 __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int n0, char *lds,
                                                 int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
-  const KSteps ks = make_steps<T>(p.K);
+  const KSteps ks = make_steps(p.K, T::BK);
   FragAddr<T> fa;
   frag_setup<T>(wm0, wn0, fa);
   RegTile<T> t;
@@ -627,14 +566,12 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 
 // ---------------------------------------------------------------- host side
 
-// Tile configuration: BM, BN, BK, waves along M, waves along N, LDS slots,
-// L2 group rows.
-#ifndef DGEMM_F16_TILE
-#define DGEMM_F16_TILE 256, 256, 32, 2, 4, 4, 4
-#endif
-typedef H16Tile<DGEMM_F16_TILE> F16Main;
-#define DGEMM_STR2(...) #__VA_ARGS__
-#define DGEMM_STR(...) DGEMM_STR2(__VA_ARGS__)
+// Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
+// L2 group rows), largest first; a call takes the largest tile that still
+// gives every CU a workgroup.
+typedef H16Tile<256, 256, 32, 2, 4, 4, 4> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU
+typedef H16Tile<128, 128, 32, 2, 2, 4, 8> F16Mid;     // 4 waves,  64 KB LDS, 2 WG/CU
+typedef H16Tile<64, 128, 32, 1, 2, 4, 8> F16Small;    // 2 waves,  48 KB LDS, 3 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems) {
   return (ld % elems) == 0 && aligned_to(p, (uintptr_t)elems * 2);
@@ -699,10 +636,36 @@ static hipError_t dispatch(const Call &c) {
   }
 }
 
-Plan plan_f16(const Call &c) {
-  return make_plan<F16Main>(c, "f16 mfma32x32x16 tile " DGEMM_STR(DGEMM_F16_TILE));
+template <class T>
+static long long tiles_of(const Call &c) {
+  return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-hipError_t launch_f16(const Call &c) { return dispatch<F16Main>(c); }
+enum class F16Cfg { kBig, kMid, kSmall };
+
+static F16Cfg choose_f16(const Call &c) {
+  if (c.tile_config == 1) return F16Cfg::kBig;
+  if (c.tile_config == 2) return F16Cfg::kMid;
+  if (c.tile_config == 3) return F16Cfg::kSmall;
+  if (tiles_of<F16Big>(c) >= kCUs) return F16Cfg::kBig;
+  if (tiles_of<F16Mid>(c) >= kCUs) return F16Cfg::kMid;
+  return F16Cfg::kSmall;
+}
+
+Plan plan_f16(const Call &c) {
+  switch (choose_f16(c)) {
+    case F16Cfg::kBig: return make_plan<F16Big>(c, "f16 mfma32x32x16 tile 256x256x32 8 waves 4 slots");
+    case F16Cfg::kMid: return make_plan<F16Mid>(c, "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
+    default: return make_plan<F16Small>(c, "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
+  }
+}
+
+hipError_t launch_f16(const Call &c) {
+  switch (choose_f16(c)) {
+    case F16Cfg::kBig: return dispatch<F16Big>(c);
+    case F16Cfg::kMid: return dispatch<F16Mid>(c);
+    default: return dispatch<F16Small>(c);
+  }
+}
 
 }  // namespace dgemm

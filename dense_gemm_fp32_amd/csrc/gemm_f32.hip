@@ -3,63 +3,84 @@
 // C := alpha*A*B + beta*C, row-major, fp32 in/out, fp32 accumulation with
 // v_mfma_f32_32x32x2_f32.
 //
-// Structure (the tiling of the SGEMM summary's tiling section, mapped onto
-// CDNA): each workgroup owns one BM x BN tile of C and walks K in steps of
-// BK, staging the A (BM x BK) and B (BK x BN) tiles through double-buffered
-// LDS; the next tiles' global loads are issued before the current tiles'
-// MFMAs so their latency is hidden, with one barrier per K step.  Each wave
-// owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in registers as FM x FN
-// blocks of 32x32 accumulators.
+// Pipeline.  Each workgroup owns a BM x BN tile of C and walks K in steps of
+// BK (the tiling of the SGEMM summary's tiling section) through STAGES LDS
+// slots filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KB of
+// LDS per wave instruction, no registers in between).  Each wave waits on
+// vmcnt for its own loads of a slot and a raw barrier publishes it, so the
+// loads of later steps stay in flight while this step is multiplied (the
+// summary's shared-memory double buffering, one slot deeper).  The barrier
+// for step kt+1 sits inside the last k group of step kt, after half of its
+// MFMAs, so the barrier wait overlaps them.  Each wave owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in AGPRs as FM x FN blocks of
+// 32x32 accumulators.
 //
 // Operand layout.  For v_mfma_f32_32x32x2_f32 lane l supplies A(row l%32,
 // k-slot l/32) and B(k-slot l/32, col l%32) and receives C(row
 // 8*(r/4) + 4*(l/32) + r%4, col l%32) in accumulator register r.  Any
 // permutation of k that A and B share leaves the sum unchanged, so:
-//   * A is stored in LDS k-contiguous per row (padded by 4 floats so that 8
-//     consecutive rows fall in distinct bank groups); one ds_read_b128 gives a
-//     lane 4 consecutive k of its row, used by 4 successive MFMAs: lanes 0-31
-//     take k = kk..kk+3, lanes 32-63 take k = kk+4..kk+7.
-//   * B is stored as in memory (k rows, n contiguous).  Output columns are
-//     interleaved inside a wave tile: MFMA block bj, lane column j holds
-//     global column wn0 + FN*j + bj.  A lane therefore reads FN consecutive
-//     floats of one B row with one LDS read, and in the epilogue writes FN
-//     consecutive floats of each C row: 32 lanes cover 32*FN contiguous
-//     floats, so stores are coalesced without a trip through LDS.
+//   * A sits in LDS k-contiguous per row, 16-byte chunks XOR-swizzled by row
+//     ((r/2)%8 for 128-byte rows: the 16 rows one 128-bit read pass touches
+//     fall in 16 distinct bank groups of gfx950's 64 banks).  One
+//     ds_read_b128 gives a lane 4 consecutive k of its row, used by 4
+//     successive MFMAs: lanes 0-31 take k = 8g..8g+3, lanes 32-63
+//     k = 8g+4..8g+7.
+//   * B sits as in memory (k rows, n contiguous).  Output columns are
+//     interleaved inside a wave tile (block bj, lane column j holds wave
+//     column FN*j + bj), so a lane reads FN adjacent floats of one B row per
+//     k, and in the epilogue writes FN adjacent floats of each C row: 32
+//     lanes cover 32*FN contiguous floats, coalesced straight from registers.
 //
-// Edges: tiles that cross M or N and the last, partial K step take masked
-// loads that substitute 0 for every element outside the matrix (never a read
-// of a pad element), and masked stores.  Interior tiles and full K steps run
-// unmasked.  Alignment: A and B chunks are read with 128-bit loads when the
-// leading dimension is a multiple of 4 and the base 16-byte aligned, else with
-// 32-bit loads (the alignment gate of the SGEMM summary's texture-load
-// variant).
+// Edges.  Direct loads cannot substitute zeros, so they only read chunks that
+// lie inside the matrix: A rows past M are clamped to row M-1 (they only feed
+// C rows that are never stored), B column chunks past N are clamped to the
+// last chunk when N % 4 == 0.  The partial K step (K % BK != 0) runs first
+// through registers with per-element masks.  A workgroup whose columns cross
+// an N that is not a multiple of 4, and every workgroup of a call whose A or B
+// is not 16-byte aligned (base or leading dimension; the alignment gate of the
+// SGEMM summary's texture-load variant), uses a register-staged path with
+// masked loads (0 outside the matrix; pad elements are never read) into the
+// same LDS layout.  Stores are masked on edge tiles.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace dgemm {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
-struct F32Tile {
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_>
+struct S32Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int STAGES = STAGES_;
   static constexpr int GROUP_M = GROUP_M_;
-  static constexpr int NT = WAVES_M * WAVES_N * kWave;
-  static constexpr int WTM = BM / WAVES_M;   // wave tile rows
-  static constexpr int WTN = BN / WAVES_N;   // wave tile columns
-  static constexpr int FM = WTM / 32;        // 32x32 blocks per wave (rows)
-  static constexpr int FN = WTN / 32;        // 32x32 blocks per wave (cols) = C columns per lane
-  static constexpr int SA = BK + 4;          // LDS row stride of the A tile (floats)
-  static constexpr int SB = BN;              // LDS row stride of the B tile (floats)
-  static constexpr int A_ELEMS = BM * SA;
-  static constexpr int B_ELEMS = BK * SB;
-  static constexpr int A_CHUNKS = BM * BK / 4 / NT;   // 4-float chunks per thread per K step
-  static constexpr int B_CHUNKS = BK * BN / 4 / NT;
-  static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * 4;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * kWave;
+  static constexpr int WTM = BM / WAVES_M;              // wave tile rows
+  static constexpr int WTN = BN / WAVES_N;              // wave tile columns
+  static constexpr int FM = WTM / 32;                   // 32x32 blocks per wave (rows)
+  static constexpr int FN = WTN / 32;                   // ... (cols) = C columns per lane
+  static constexpr int KG = BK / 8;                     // 8-k groups per K step
+  static constexpr int RA = 4 * BK;                     // bytes per A row in LDS
+  static constexpr int CA = BK / 4;                     // 16-byte chunks per A row
+  static constexpr int RPW = RA >= 256 ? 1 : 256 / RA;  // A rows per 256-byte bank window
+  static constexpr int RB = 4 * BN;                     // bytes per B row in LDS
+  static constexpr int A_BYTES = BM * RA;
+  static constexpr int B_BYTES = BK * RB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int QA = A_BYTES / 1024;             // 1 KB wave loads per A tile
+  static constexpr int QB = B_BYTES / 1024;
+  static constexpr int QA_W = QA / NWAVES;              // ... per wave
+  static constexpr int QB_W = QB / NWAVES;
+  static constexpr int LOADS = QA_W + QB_W;             // direct loads per wave per K step
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(BM % (WAVES_M * 32) == 0 && BN % (WAVES_N * 32) == 0, "wave tiling");
-  static_assert(BK % 8 == 0, "BK multiple of 8");
-  static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "load split");
+  static_assert(BK % 8 == 0 && KG >= 1, "BK multiple of 8");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
+  static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
   static_assert(FN == 1 || FN == 2 || FN == 4, "FN");
+  static_assert(FM % 2 == 0, "the last k group splits the block rows in halves");
+  static_assert(STAGES >= 3, "the early barrier needs three or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(3 * LOADS <= 63, "vmcnt range");
 };
 
 template <int N> struct FVec;
@@ -67,118 +88,329 @@ template <> struct FVec<1> { typedef float type; };
 template <> struct FVec<2> { typedef f32x2 type; };
 template <> struct FVec<4> { typedef f32x4 type; };
 
-// Global -> registers: the A tile rows m0.., columns k0..k0+BK-1.
-template <class T, bool VEC, bool CHECK_M, bool CHECK_K>
-__device__ __forceinline__ void load_a(const GemmParams &p, int m0, int k0,
-                                       f32x4 (&ra)[T::A_CHUNKS]) {
+template <class T>
+__device__ __forceinline__ int swz_a32(int r) {
+  return (r / T::RPW) % T::CA;
+}
+
+// Tile-relative origin of the global data behind 16-byte LDS chunk (q, lane)
+// of a slot's A region (row r, k column kc) or B region (k row kr, column nc).
+template <class T>
+__device__ __forceinline__ void a_chunk32(int q, int lane, int &r, int &kc) {
+  const int o = q * 1024 + 16 * lane;
+  r = o / T::RA;
+  kc = 4 * (((o % T::RA) / 16) ^ swz_a32<T>(r));
+}
+
+template <class T>
+__device__ __forceinline__ void b_chunk32(int q, int lane, int &kr, int &nc) {
+  const int o = q * 1024 + 16 * lane;
+  kr = o / T::RB;
+  nc = 4 * ((o % T::RB) / 16);
+}
+
+// ---------------------------------------------------------------- direct loads
+
+template <class T>
+struct DirectAddr32 {
+  const float *a[T::QA_W];
+  const float *b[T::QB_W];
+};
+
+template <class T>
+__device__ __forceinline__ void direct_setup32(const GemmParams &p, int m0, int n0,
+                                               DirectAddr32<T> &d) {
   const float *A = static_cast<const float *>(p.A);
-  constexpr int CPR = T::BK / 4;
-#pragma unroll
-  for (int i = 0; i < T::A_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    const int row = c / CPR;
-    const int kc = c % CPR;
-    const int gr = m0 + row;
-    const int gk = k0 + 4 * kc;
-    const float *src = A + (size_t)gr * (size_t)p.lda + gk;
-    const bool row_ok = !CHECK_M || gr < p.M;
-    if (row_ok && (!CHECK_K || gk + 3 < p.K)) {
-      if (VEC) {
-        ra[i] = *reinterpret_cast<const f32x4 *>(src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ra[i][e] = src[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ra[i][e] = (row_ok && gk + e < p.K) ? src[e] : 0.0f;
-    }
-  }
-}
-
-// Global -> registers: the B tile rows k0..k0+BK-1, columns n0...
-template <class T, bool VEC, bool CHECK_N, bool CHECK_K>
-__device__ __forceinline__ void load_b(const GemmParams &p, int n0, int k0,
-                                       f32x4 (&rb)[T::B_CHUNKS]) {
   const float *B = static_cast<const float *>(p.B);
-  constexpr int CPR = T::BN / 4;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int i = 0; i < T::B_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    const int kr = c / CPR;
-    const int nc = c % CPR;
-    const int gk = k0 + kr;
-    const int gn = n0 + 4 * nc;
-    const float *src = B + (size_t)gk * (size_t)p.ldb + gn;
-    const bool k_ok = !CHECK_K || gk < p.K;
-    if (k_ok && (!CHECK_N || gn + 3 < p.N)) {
-      if (VEC) {
-        rb[i] = *reinterpret_cast<const f32x4 *>(src);
-      } else {
+  for (int j = 0; j < T::QA_W; ++j) {
+    int r, kc;
+    a_chunk32<T>(wave * T::QA_W + j, lane, r, kc);
+    int gr = m0 + r;
+    gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
+    d.a[j] = A + (size_t)gr * (size_t)p.lda + kc;
+  }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rb[i][e] = src[e];
-      }
+  for (int j = 0; j < T::QB_W; ++j) {
+    int kr, nc;
+    b_chunk32<T>(wave * T::QB_W + j, lane, kr, nc);
+    int gn = n0 + nc;
+    gn = gn + 4 <= p.N ? gn : p.N - 4;     // N % 4 == 0 here: the last whole chunk
+    d.b[j] = B + (size_t)kr * (size_t)p.ldb + gn;
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void direct_issue32(const GemmParams &p, const DirectAddr32<T> &d,
+                                               int k0, uint32_t slot_addr) {
+  const int wave = wave_id();
+  const size_t boff = (size_t)k0 * (size_t)p.ldb;
+#pragma unroll
+  for (int j = 0; j < T::QA_W; ++j)
+    direct_load16(d.a[j] + k0, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+#pragma unroll
+  for (int j = 0; j < T::QB_W; ++j)
+    direct_load16(d.b[j] + boff,
+                  slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+}
+
+// ---------------------------------------------------------------- register-staged loads
+
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4(const float *src) {
+  if (VEC) return *reinterpret_cast<const f32x4 *>(src);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = src[e];
+  return v;
+}
+
+template <class T>
+struct RegTile32 {
+  f32x4 a[T::QA_W];
+  f32x4 b[T::QB_W];
+};
+
+// The chunks the direct loads would fetch, through registers, with 0 for every
+// element outside the matrix (rows >= M, columns >= N, k >= K).
+template <class T, bool VA, bool VB>
+__device__ __forceinline__ void reg_load32(const GemmParams &p, int m0, int n0, int k0,
+                                           RegTile32<T> &t) {
+  const float *A = static_cast<const float *>(p.A);
+  const float *B = static_cast<const float *>(p.B);
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int j = 0; j < T::QA_W; ++j) {
+    int r, kc;
+    a_chunk32<T>(wave * T::QA_W + j, lane, r, kc);
+    const int gr = m0 + r, gk = k0 + kc;
+    const float *src = A + (size_t)gr * (size_t)p.lda + gk;
+    const bool row_ok = gr < p.M;
+    if (row_ok && gk + 3 < p.K) {
+      t.a[j] = load4<VA>(src);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rb[i][e] = (k_ok && gn + e < p.N) ? src[e] : 0.0f;
+      for (int e = 0; e < 4; ++e) t.a[j][e] = (row_ok && gk + e < p.K) ? src[e] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < T::QB_W; ++j) {
+    int kr, nc;
+    b_chunk32<T>(wave * T::QB_W + j, lane, kr, nc);
+    const int gk = k0 + kr, gn = n0 + nc;
+    const float *src = B + (size_t)gk * (size_t)p.ldb + gn;
+    const bool k_ok = gk < p.K;
+    if (k_ok && gn + 3 < p.N) {
+      t.b[j] = load4<VB>(src);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.b[j][e] = (k_ok && gn + e < p.N) ? src[e] : 0.0f;
     }
   }
 }
 
 template <class T>
-__device__ __forceinline__ void store_lds(float *As, float *Bs, const f32x4 (&ra)[T::A_CHUNKS],
-                                          const f32x4 (&rb)[T::B_CHUNKS]) {
-  constexpr int CPRA = T::BK / 4;
-  constexpr int CPRB = T::BN / 4;
+__device__ __forceinline__ void reg_store32(const RegTile32<T> &t, char *slot) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int i = 0; i < T::A_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    *reinterpret_cast<f32x4 *>(&As[(c / CPRA) * T::SA + 4 * (c % CPRA)]) = ra[i];
-  }
+  for (int j = 0; j < T::QA_W; ++j)
+    *reinterpret_cast<f32x4 *>(slot + (wave * T::QA_W + j) * 1024 + 16 * lane) = t.a[j];
 #pragma unroll
-  for (int i = 0; i < T::B_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * T::NT;
-    *reinterpret_cast<f32x4 *>(&Bs[(c / CPRB) * T::SB + 4 * (c % CPRB)]) = rb[i];
-  }
+  for (int j = 0; j < T::QB_W; ++j)
+    *reinterpret_cast<f32x4 *>(slot + T::A_BYTES + (wave * T::QB_W + j) * 1024 + 16 * lane) =
+        t.b[j];
 }
 
-// acc += A_tile(wave rows) * B_tile(wave cols) over the BK columns in LDS.
+// ---------------------------------------------------------------- fragments and MFMA
+
 template <class T>
-__device__ __forceinline__ void compute_tile(const float *As, const float *Bs, int wm0, int wn0,
-                                             f32x16 (&acc)[T::FM][T::FN]) {
-  typedef typename FVec<T::FN>::type BVec;
+struct Frag32 {
+  f32x4 a[T::FM];                       // 4 k of the lane's row in each block row
+  typename FVec<T::FN>::type b[4];      // FN columns at each of the 4 k
+};
+
+// Per-lane LDS byte offsets of the fragments, relative to a slot.
+template <class T>
+struct FragAddr32 {
+  int a[T::KG];   // A block row 0 at k group g; block row bi adds 32*bi*RA
+  int b;          // B at k group 0, first k; k group g adds 8*g*RB, k s adds s*RB
+};
+
+template <class T>
+__device__ __forceinline__ void frag_setup32(int wm0, int wn0, FragAddr32<T> &f) {
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32;
-  const int lh = lane / 32;
+  const int li = lane % 32, lh = lane / 32;
+  const int r = wm0 + li;
+  const int sa = swz_a32<T>(r);
 #pragma unroll
-  for (int kk = 0; kk < T::BK; kk += 8) {
-    f32x4 a[T::FM];
+  for (int g = 0; g < T::KG; ++g) f.a[g] = r * T::RA + 16 * ((2 * g + lh) ^ sa);
+  f.b = T::A_BYTES + 4 * lh * T::RB + 4 * (wn0 + T::FN * li);
+}
+
+template <class T>
+__device__ __forceinline__ void frag_read32(const char *slot, const FragAddr32<T> &f, int g,
+                                            Frag32<T> &fr) {
+  typedef typename FVec<T::FN>::type BVec;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    fr.b[s] = *reinterpret_cast<const BVec *>(slot + f.b + (8 * g + s) * T::RB);
+#pragma unroll
+  for (int bi = 0; bi < T::FM; ++bi)
+    fr.a[bi] = *reinterpret_cast<const f32x4 *>(slot + f.a[g] + 32 * bi * T::RA);
+}
+
+// MFMAs of k slots [S0, S1) of one k group.
+template <class T, int S0, int S1>
+__device__ __forceinline__ void mfma_slots(const Frag32<T> &fr, f32x16 (&acc)[T::FM][T::FN]) {
+#pragma unroll
+  for (int s = S0; s < S1; ++s)
 #pragma unroll
     for (int bi = 0; bi < T::FM; ++bi)
-      a[bi] = *reinterpret_cast<const f32x4 *>(&As[(wm0 + 32 * bi + li) * T::SA + kk + 4 * lh]);
-    BVec b[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      b[s] = *reinterpret_cast<const BVec *>(&Bs[(kk + 4 * lh + s) * T::SB + wn0 + T::FN * li]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int bi = 0; bi < T::FM; ++bi) {
-#pragma unroll
-        for (int bj = 0; bj < T::FN; ++bj) {
-          float bv;
-          if constexpr (T::FN == 1) bv = b[s]; else bv = b[s][bj];
-          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[bi][s], bv, acc[bi][bj], 0, 0, 0);
-        }
+      for (int bj = 0; bj < T::FN; ++bj) {
+        float bv;
+        if constexpr (T::FN == 1) bv = fr.b[s]; else bv = fr.b[s][bj];
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.a[bi][s], bv, acc[bi][bj], 0, 0, 0);
       }
+}
+
+// Interleave pattern: one LDS read behind each of the first NR MFMAs.
+template <int I, int NM, int NR>
+__device__ __forceinline__ void interleave32_slot() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+    if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+    interleave32_slot<I + 1, NM, NR>();
+  }
+}
+
+// All k groups of one K step from `slot`; fr[0] holds group 0 on entry.  The
+// next group's fragments are read while the current group's MFMAs run.  In
+// the last group, half of the MFMAs are issued, then `next()` publishes the
+// following slot (its barrier wait overlaps those MFMAs), then group 0 of the
+// following step is read from `next_slot` (a stale slot on the last step,
+// never used) between the remaining MFMAs.
+template <class T, class Next>
+__device__ __forceinline__ void kstep32(const char *slot, const char *next_slot,
+                                        const FragAddr32<T> &fa, Frag32<T> (&fr)[2],
+                                        f32x16 (&acc)[T::FM][T::FN], Next next) {
+  constexpr int NREAD = T::FM + 4;
+  constexpr int NMF = 4 * T::FM * T::FN;
+#pragma unroll
+  for (int g = 0; g < T::KG; ++g) {
+    if (g + 1 < T::KG) {
+      frag_read32<T>(slot, fa, g + 1, fr[(g + 1) & 1]);
+      mfma_slots<T, 0, 4>(fr[g & 1], acc);
+      interleave32_slot<0, NMF, NREAD>();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      mfma_slots<T, 0, 2>(fr[g & 1], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      next();
+      frag_read32<T>(next_slot, fa, 0, fr[0]);
+      mfma_slots<T, 2, 4>(fr[g & 1], acc);
+      interleave32_slot<0, NMF / 2, NREAD>();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
+
+// ---------------------------------------------------------------- main loops
+
+template <class T>
+__device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, int n0, char *lds,
+                                                  uint32_t lds_u32, int wm0, int wn0,
+                                                  f32x16 (&acc)[T::FM][T::FN]) {
+  const KSteps ks = make_steps(p.K, T::BK);
+  DirectAddr32<T> da;
+  direct_setup32<T>(p, m0, n0, da);
+  FragAddr32<T> fa;
+  frag_setup32<T>(wm0, wn0, fa);
+
+  // Prologue: step 0 (masked, through registers, when it is the partial
+  // step), then direct loads of steps 1 .. STAGES-2.
+  if (ks.tail) {
+    RegTile32<T> t;
+    reg_load32<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_store32<T>(t, lds);
+  } else {
+    direct_issue32<T>(p, da, ks.k0(0), lds_u32);
+  }
+  int issued = 1;
+#pragma unroll
+  for (int j = 1; j < T::STAGES - 1; ++j) {
+    if (j < ks.nk) {
+      direct_issue32<T>(p, da, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      ++issued;
+    }
+  }
+  switch (issued - 1) {
+    case 0: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0); break;
+  }
+  lds_barrier();
+
+  Frag32<T> fr[2];
+  frag_read32<T>(lds, fa, 0, fr[0]);
+
+  for (int kt = 0; kt < ks.nk; ++kt) {
+    const char *slot = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+    kstep32<T>(slot, next_slot, fa, fr, acc, [&]() {
+      // Step kt+1 must have landed; steps issued after it may stay in flight.
+      const int after = (issued - 1) - (kt + 1);
+      if (after <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
+      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS));
+      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS));
+      lds_barrier();
+      // Every wave has consumed step kt-1: its slot takes step kt+STAGES-1.
+      const int nx = kt + T::STAGES - 1;
+      if (nx < ks.nk) {
+        direct_issue32<T>(p, da, ks.k0(nx),
+                          lds_u32 + (uint32_t)((nx % T::STAGES) * T::STAGE_BYTES));
+        ++issued;
+      }
+    });
+  }
+}
+
+template <class T, bool VA, bool VB>
+__device__ __forceinline__ void mainloop_staged32(const GemmParams &p, int m0, int n0, char *lds,
+                                                  int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+  const KSteps ks = make_steps(p.K, T::BK);
+  FragAddr32<T> fa;
+  frag_setup32<T>(wm0, wn0, fa);
+  RegTile32<T> t;
+  reg_load32<T, VA, VB>(p, m0, n0, ks.k0(0), t);
+  reg_store32<T>(t, lds);
+  __syncthreads();
+  Frag32<T> fr[2];
+  frag_read32<T>(lds, fa, 0, fr[0]);
+  for (int kt = 0; kt < ks.nk; ++kt) {
+    const char *slot = lds + (kt % 2) * T::STAGE_BYTES;
+    char *nslot = lds + ((kt + 1) % 2) * T::STAGE_BYTES;
+    if (kt + 1 < ks.nk) reg_load32<T, VA, VB>(p, m0, n0, ks.k0(kt + 1), t);
+    // nslot was last read in step kt-1, before that step's barrier.  On the
+    // last step the store repeats old data into a slot nobody reads again.
+    kstep32<T>(slot, nslot, fa, fr, acc, [&]() {
+      reg_store32<T>(t, nslot);
+      __syncthreads();
+    });
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
 
 // alpha*acc + beta*C -> C for one wave tile whose origin is (r0, c0).
 template <class T, bool VEC_C, bool CHECK>
-__device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0,
-                                         const f32x16 (&acc)[T::FM][T::FN]) {
+__device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
+                                           const f32x16 (&acc)[T::FM][T::FN]) {
   typedef typename FVec<T::FN>::type CVec;
   float *C = static_cast<float *>(p.C);
   const int lane = threadIdx.x % kWave;
@@ -227,21 +459,16 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0,
   }
 }
 
-template <class T, bool VA, bool VB, bool EDGE, bool CHECK_K>
-__device__ __forceinline__ void load_tiles(const GemmParams &p, int m0, int n0, int k0,
-                                           f32x4 (&ra)[T::A_CHUNKS], f32x4 (&rb)[T::B_CHUNKS]) {
-  load_a<T, VA, EDGE, CHECK_K>(p, m0, k0, ra);
-  load_b<T, VB, EDGE, CHECK_K>(p, n0, k0, rb);
-}
-
-template <class T, bool VA, bool VB, bool VC, bool EDGE>
-__device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, float *lds) {
-  float *As = lds;                   // [2][A_ELEMS]
-  float *Bs = lds + 2 * T::A_ELEMS;  // [2][B_ELEMS]
-  const int wave = threadIdx.x / kWave;
+template <class T, bool VA, bool VB, bool VC>
+__global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  int tm, tn;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * T::BM;
+  const int n0 = tn * T::BN;
+  const int wave = wave_id();
   const int wm0 = (wave / T::WAVES_N) * T::WTM;
   const int wn0 = (wave % T::WAVES_N) * T::WTN;
-
   f32x16 acc[T::FM][T::FN];
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi)
@@ -250,52 +477,27 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, fl
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
 
-  const int nk = (p.K + T::BK - 1) / T::BK;   // K >= 1 here
-  const int nfull = p.K / T::BK;
-  f32x4 ra[T::A_CHUNKS], rb[T::B_CHUNKS];
+  const bool n_edge = n0 + T::BN > p.N;
+  const bool direct = VA && VB && (!n_edge || (p.N % 4) == 0);
+  if (direct) mainloop_direct32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+  else mainloop_staged32<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-  if (nfull > 0) load_tiles<T, VA, VB, EDGE, false>(p, m0, n0, 0, ra, rb);
-  else load_tiles<T, VA, VB, EDGE, true>(p, m0, n0, 0, ra, rb);
-  store_lds<T>(As, Bs, ra, rb);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k1 = (kt + 1) * T::BK;
-      if (kt + 1 < nfull) load_tiles<T, VA, VB, EDGE, false>(p, m0, n0, k1, ra, rb);
-      else load_tiles<T, VA, VB, EDGE, true>(p, m0, n0, k1, ra, rb);
-    }
-    compute_tile<T>(As + cur * T::A_ELEMS, Bs + cur * T::B_ELEMS, wm0, wn0, acc);
-    if (more) store_lds<T>(As + (cur ^ 1) * T::A_ELEMS, Bs + (cur ^ 1) * T::B_ELEMS, ra, rb);
-    __syncthreads();
-  }
-
-  epilogue<T, VC, EDGE>(p, m0 + wm0, n0 + wn0, acc);
-}
-
-template <class T, bool VA, bool VB, bool VC>
-__global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) float lds[2 * (T::A_ELEMS + T::B_ELEMS)];
-  int tm, tn;
-  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * T::BM;
-  const int n0 = tn * T::BN;
-  const bool edge = (m0 + T::BM > p.M) || (n0 + T::BN > p.N);
-  if (edge) mainloop<T, VA, VB, VC, true>(p, m0, n0, lds);
-  else mainloop<T, VA, VB, VC, false>(p, m0, n0, lds);
+  const bool edge = n_edge || (m0 + T::BM > p.M);
+  if (edge) epilogue32<T, VC, true>(p, m0 + wm0, n0 + wn0, acc);
+  else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
 }
 
 // ---------------------------------------------------------------- host side
 
-// Tile configuration: BM, BN, BK, waves along M, waves along N, L2 group rows.
-#ifndef DGEMM_F32_TILE
-#define DGEMM_F32_TILE 128, 128, 32, 2, 2, 8
-#endif
-typedef F32Tile<DGEMM_F32_TILE> F32Main;
-#define DGEMM_STR2(...) #__VA_ARGS__
-#define DGEMM_STR(...) DGEMM_STR2(__VA_ARGS__)
+// Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
+// L2 group rows), largest first.  A call takes the largest tile that still
+// gives every CU a workgroup; small problems fall through to smaller tiles
+// (the size-based kernel choice of the SGEMM summary's results section,
+// retuned for 256 CUs).
+typedef S32Tile<256, 128, 32, 4, 2, 3, 8> F32Big;     // 8 waves, 144 KB LDS, 1 WG/CU
+typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32Mid;     // 4 waves,  48 KB LDS, 3 WG/CU
+typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
   return (ld % elems) == 0 && aligned_to(p, (uintptr_t)elems * bytes_per_elem);
@@ -360,10 +562,36 @@ static hipError_t dispatch(const Call &c) {
   }
 }
 
-Plan plan_f32(const Call &c) {
-  return make_plan<F32Main>(c, "f32 mfma32x32x2 tile " DGEMM_STR(DGEMM_F32_TILE));
+template <class T>
+static long long tiles_of(const Call &c) {
+  return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-hipError_t launch_f32(const Call &c) { return dispatch<F32Main>(c); }
+enum class F32Cfg { kBig, kMid, kSmall };
+
+static F32Cfg choose_f32(const Call &c) {
+  if (c.tile_config == 1) return F32Cfg::kBig;
+  if (c.tile_config == 2) return F32Cfg::kMid;
+  if (c.tile_config == 3) return F32Cfg::kSmall;
+  if (tiles_of<F32Big>(c) >= kCUs) return F32Cfg::kBig;
+  if (tiles_of<F32Mid>(c) >= kCUs) return F32Cfg::kMid;
+  return F32Cfg::kSmall;
+}
+
+Plan plan_f32(const Call &c) {
+  switch (choose_f32(c)) {
+    case F32Cfg::kBig: return make_plan<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots");
+    case F32Cfg::kMid: return make_plan<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
+    default: return make_plan<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
+  }
+}
+
+hipError_t launch_f32(const Call &c) {
+  switch (choose_f32(c)) {
+    case F32Cfg::kBig: return dispatch<F32Big>(c);
+    case F32Cfg::kMid: return dispatch<F32Mid>(c);
+    default: return dispatch<F32Small>(c);
+  }
+}
 
 }  // namespace dgemm

@@ -39,7 +39,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  The call only
  *     enqueues work on it and returns; it does not synchronise.  The caller
  *     keeps A, B and C alive until that work has completed.
- *   - The library holds no state, so calls are thread-safe and reentrant.
+ *   - The library keeps no per-call state, so calls are thread-safe and
+ *     reentrant; the only process-wide state is the two diagnostic switches
+ *     at the end of this header (default off).
  *
  * Return value:
  *   0                 success (work enqueued, or nothing to do)
@@ -124,6 +126,14 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha,
  * previous setting, or -1 for an unknown mode.
  */
 int gemm_set_load_mode(int mode);
+
+/*
+ * Diagnostic switch for tests: 0 = choose the tile configuration from the
+ * problem size (the default); 1, 2, 3 = force the large, medium or small
+ * configuration.  Process-wide, like gemm_set_load_mode.  Returns the
+ * previous setting, or -1 for an unknown value.
+ */
+int gemm_set_tile_config(int config);
 
 #ifdef __cplusplus
 }

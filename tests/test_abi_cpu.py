@@ -21,7 +21,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode"):
+    for n in ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
+              "gemm_set_tile_config"):
         assert n in names
 
 
@@ -154,3 +155,21 @@ def test_only_inline_asm_touches_m0():
     from dense_gemm_fp32_amd import build as b
     for src in b.M0_ASM_SOURCES:
         b.check_m0_only_in_asm(src)
+
+
+def test_tile_table_choice_and_override():
+    import dense_gemm_fp32_amd as dg
+    def name(dt, n):
+        return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
+    assert "256x128x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
+    assert "64x64x32" in name("f32", 1024) and "64x64x32" in name("f32", 256)
+    assert "256x256x32" in name("f16", 4096) and "128x128x32" in name("f16", 2048)
+    assert "64x128x32" in name("f16", 512)
+    prev = dg.gemm_set_tile_config(1)
+    try:
+        assert "256x128x32" in name("f32", 256) and "256x256x32" in name("f16", 256)
+        dg.gemm_set_tile_config(3)
+        assert "64x64x32" in name("f32", 4096)
+    finally:
+        dg.gemm_set_tile_config(prev)
+    assert dg.gemm_set_tile_config(9) == -1

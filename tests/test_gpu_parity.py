@@ -335,3 +335,56 @@ def test_f16_nan_in_a_row_past_m_is_not_read():
     rc, out = run("f16", M, N, K, 1.0, A, K, B, N, 0.0, C, N, "rows past M")
     assert rc == 0
     check("f16", M, N, K, 1.0, A, K, B, N, 0.0, C, N, out, "rows past M")
+
+
+# ---------------------------------------------------------------- tile table
+
+from contextlib import contextmanager
+
+
+@contextmanager
+def tile_config(cfg):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_tile_config(cfg)
+    try:
+        yield
+    finally:
+        dg.gemm_set_tile_config(prev)
+
+
+TABLE_SHAPES = [
+    # M,    N,   K,  lda, ldb, ldc   (aligned: direct loads with every edge)
+    (300, 264, 100, 104, 264, 264),
+    (600, 640, 96, 96, 648, 640),
+    # unaligned leading dimensions: register-staged path
+    (257, 530, 77, 77, 533, 531),
+]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3], ids=["large", "medium", "small"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_every_tile_configuration_matches_oracle(dtype, cfg):
+    t = _t(dtype)
+    for shape in TABLE_SHAPES:
+        M, N, K, lda, ldb, ldc = shape
+        rng = np.random.default_rng(M + 3 * N + 7 * K + cfg)
+        A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
+        B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
+        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+        with tile_config(cfg):
+            rc, out = run(dtype, M, N, K, 0.75, A, lda, B, ldb, 1.5, C, ldc, "cfg%d" % cfg)
+        assert rc == 0
+        check(dtype, M, N, K, 0.75, A, lda, B, ldb, 1.5, C, ldc, out, "cfg %d %s" % (cfg, shape))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_large_tiles_with_edges_sampled(dtype):
+    """Large-tile configuration picked by size, with all three edges and
+    aligned leading dimensions (direct loads with clamping), checked on
+    sampled rows, the checksum and Freivalds' product check."""
+    w = wl.Workload("edges_large_" + dtype, dtype, 4100, 4104, 1000, 1000, 4104, 4112, 1.25, -0.5,
+                    "uniform", "uniform", (21, 22, 23))
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out, nrows=24)
