@@ -75,6 +75,11 @@ def parse_args():
     ap.add_argument("--no-p4", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="fp32 size sweep M=N=K=1024..12800 step 128, beta=1, replay protocol "
+                         "with cache flush; one JSON row per size")
+    ap.add_argument("--sweep-sizes", default=None,
+                    help="comma-separated sizes for --sweep (default 1024..12800 step 128)")
     ap.add_argument("--only", choices=["f32", "f16", "copy"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
                          "device copy of known size to calibrate HBM counters")
@@ -99,6 +104,9 @@ def main():
 
     if args.only == "copy":
         run_copy_calibration(torch, dev)
+        return
+    if args.sweep:
+        run_sweep(args, torch, dev, stream)
         return
 
     def upload(w):
@@ -216,6 +224,47 @@ def main():
                    "hip": torch.version.hip},
     }
     print(json.dumps(line), flush=True)
+
+
+def run_sweep(args, torch, dev, stream):
+    """The square fp32 sweep of the SGEMM summary's benchmarking section:
+    M = N = K = n, A, B, C ~ U[-1, 1], alpha = beta = 1, floor(1000 *
+    exp((1024 - n)/3100)) replays with a 512 MiB flush before each (outside
+    the timed interval), mean of the second half.  Inputs of size n are the
+    leading n x n blocks of seeded 12800 x 12800 matrices."""
+    import dense_gemm_fp32_amd as dg
+    import workloads as wl
+    sizes = ([int(x) for x in args.sweep_sizes.split(",")] if args.sweep_sizes
+             else wl.sweep_sizes())
+    nmax = max(sizes)
+    w = wl.sweep(nmax)
+    big = [torch.from_numpy(wl.draw(nmax, nmax, "uniform", seed, "f32")).to(dev)
+           for seed in w.seeds]
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for n in sizes:
+        A, B, C = (x[:n, :n].contiguous() for x in big)
+        reps = replay_count(n)
+        rc = dg.gemm_f32(n, n, n, 1.0, A, n, B, n, 1.0, C, n, stream)   # warm-up
+        if rc != 0:
+            raise RuntimeError("gemm_f32 returned %d" % rc)
+        times = []
+        for _ in range(reps):
+            flush.zero_()
+            s_ev.record(stream)
+            dg.gemm_f32(n, n, n, 1.0, A, n, B, n, 1.0, C, n, stream)
+            e_ev.record(stream)
+            e_ev.synchronize()
+            times.append(s_ev.elapsed_time(e_ev))
+        last = times[len(times) - len(times) // 2:]
+        mean = sum(last) / len(last)
+        rc, plan = dg.gemm_describe("f32", n, n, n, 1.0, A, n, B, n, 1.0, C, n)
+        print(json.dumps({"n": n, "replays": reps, "averaged": len(last),
+                          "mean_ms": round(mean, 5), "min_ms": round(min(times), 5),
+                          "tflops": round(2.0 * n ** 3 / (mean * 1e-3) / 1e12, 2),
+                          "pct_of_peak": round(100 * 2.0 * n ** 3 / (mean * 1e-3) / 1e12 / PEAK_F32, 2),
+                          "plan": plan}), flush=True)
+        del A, B, C
 
 
 def run_copy_calibration(torch, dev):

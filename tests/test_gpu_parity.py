@@ -388,3 +388,14 @@ def test_large_tiles_with_edges_sampled(dtype):
     rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
     assert rc == 0
     check_sampled(w.dtype, w, A, B, C, out, nrows=24)
+
+
+def test_f32_sweep_largest_size_sampled():
+    """The size sweep's largest size, 12800^3 with beta = 1 (large-tile
+    configuration, direct loads), on sampled rows, the checksum and
+    Freivalds' check."""
+    w = wl.sweep(12800)
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out, nrows=16)
