@@ -568,7 +568,7 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 
 // Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
 // L2 group rows), largest first; a call takes the largest tile that still
-// gives every CU a workgroup.
+// gives at least half of the CUs a workgroup.
 typedef H16Tile<256, 256, 32, 2, 4, 4, 4> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU
 typedef H16Tile<128, 128, 32, 2, 2, 4, 8> F16Mid;     // 4 waves,  64 KB LDS, 2 WG/CU
 typedef H16Tile<64, 128, 32, 1, 2, 4, 8> F16Small;    // 2 waves,  48 KB LDS, 3 WG/CU
@@ -647,8 +647,11 @@ static F16Cfg choose_f16(const Call &c) {
   if (c.tile_config == 1) return F16Cfg::kBig;
   if (c.tile_config == 2) return F16Cfg::kMid;
   if (c.tile_config == 3) return F16Cfg::kSmall;
-  if (tiles_of<F16Big>(c) >= kCUs) return F16Cfg::kBig;
-  if (tiles_of<F16Mid>(c) >= kCUs) return F16Cfg::kMid;
+  // Measured: the large tile stays ahead down to about half a round of
+  // tiles (fewer busy CUs draw less power and clock higher), the medium one
+  // down to half a round as well.
+  if (tiles_of<F16Big>(c) >= kCUs / 2) return F16Cfg::kBig;
+  if (tiles_of<F16Mid>(c) >= kCUs / 2) return F16Cfg::kMid;
   return F16Cfg::kSmall;
 }
 

@@ -491,10 +491,9 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 // ---------------------------------------------------------------- host side
 
 // Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
-// L2 group rows), largest first.  A call takes the largest tile that still
-// gives every CU a workgroup; small problems fall through to smaller tiles
-// (the size-based kernel choice of the SGEMM summary's results section,
-// retuned for 256 CUs).
+// L2 group rows), largest first.  A call takes the configuration with the
+// best estimated throughput for its tile count (the size-based kernel choice
+// of the SGEMM summary's results section, retuned for 256 CUs).
 typedef S32Tile<256, 128, 32, 4, 2, 3, 8> F32Big;     // 8 waves, 144 KB LDS, 1 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32Mid;     // 4 waves,  48 KB LDS, 3 WG/CU
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
@@ -569,13 +568,26 @@ static long long tiles_of(const Call &c) {
 
 enum class F32Cfg { kBig, kMid, kSmall };
 
+// Share of the machine a configuration keeps busy: with T tiles spread over
+// the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
+// T/CUs (several workgroups per CU share it, so only whole tiles per CU
+// count).  Scores multiply it by the configuration's measured throughput at
+// full occupancy (fraction of the fp32 peak at 4096^3: 0.89, 0.87, 0.60).
+static double busy_share(long long tiles) {
+  const double per_cu = (double)tiles / kCUs;
+  const double rounds = (double)((tiles + kCUs - 1) / kCUs);
+  return per_cu / rounds;
+}
+
 static F32Cfg choose_f32(const Call &c) {
   if (c.tile_config == 1) return F32Cfg::kBig;
   if (c.tile_config == 2) return F32Cfg::kMid;
   if (c.tile_config == 3) return F32Cfg::kSmall;
-  if (tiles_of<F32Big>(c) >= kCUs) return F32Cfg::kBig;
-  if (tiles_of<F32Mid>(c) >= kCUs) return F32Cfg::kMid;
-  return F32Cfg::kSmall;
+  const double big = 0.89 * busy_share(tiles_of<F32Big>(c));
+  const double mid = 0.87 * busy_share(tiles_of<F32Mid>(c));
+  const double small = 0.60 * busy_share(tiles_of<F32Small>(c));
+  if (big >= mid && big >= small) return F32Cfg::kBig;
+  return mid >= small ? F32Cfg::kMid : F32Cfg::kSmall;
 }
 
 Plan plan_f32(const Call &c) {
