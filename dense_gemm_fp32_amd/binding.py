@@ -96,8 +96,8 @@ def gemm_set_load_mode(mode):
 
 
 def gemm_set_tile_config(config):
-    """0 = tile configuration by problem size (default); 1/2/3 = force the
-    large/medium/small configuration."""
+    """0 = tile configuration by problem size (default); 1/2/3/4 = force the
+    large/medium/small/tiny configuration (fp16 maps 4 to small)."""
     return _lib.gemm_set_tile_config(int(config))
 
 

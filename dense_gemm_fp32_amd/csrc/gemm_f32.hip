@@ -77,7 +77,6 @@ struct S32Tile {
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
   static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
   static_assert(FN == 1 || FN == 2 || FN == 4, "FN");
-  static_assert(FM % 2 == 0, "the last k group splits the block rows in halves");
   static_assert(STAGES >= 3, "the early barrier needs three or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(3 * LOADS <= 63, "vmcnt range");
@@ -497,6 +496,7 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 typedef S32Tile<256, 128, 32, 4, 2, 3, 8> F32Big;     // 8 waves, 144 KB LDS, 1 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32Mid;     // 4 waves,  48 KB LDS, 3 WG/CU
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
+typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
   return (ld % elems) == 0 && aligned_to(p, (uintptr_t)elems * bytes_per_elem);
@@ -566,13 +566,14 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kBig, kMid, kSmall };
+enum class F32Cfg { kBig, kMid, kSmall, kTiny };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
 // T/CUs (several workgroups per CU share it, so only whole tiles per CU
 // count).  Scores multiply it by the configuration's measured throughput at
-// full occupancy (fraction of the fp32 peak at 4096^3: 0.89, 0.87, 0.60).
+// full occupancy (fraction of the fp32 peak at 4096^3: 0.89, 0.87, 0.60;
+// 0.30 assumed for the 32x32 tile, which only small problems take).
 static double busy_share(long long tiles) {
   const double per_cu = (double)tiles / kCUs;
   const double rounds = (double)((tiles + kCUs - 1) / kCUs);
@@ -583,18 +584,22 @@ static F32Cfg choose_f32(const Call &c) {
   if (c.tile_config == 1) return F32Cfg::kBig;
   if (c.tile_config == 2) return F32Cfg::kMid;
   if (c.tile_config == 3) return F32Cfg::kSmall;
+  if (c.tile_config == 4) return F32Cfg::kTiny;
   const double big = 0.89 * busy_share(tiles_of<F32Big>(c));
   const double mid = 0.87 * busy_share(tiles_of<F32Mid>(c));
   const double small = 0.60 * busy_share(tiles_of<F32Small>(c));
-  if (big >= mid && big >= small) return F32Cfg::kBig;
-  return mid >= small ? F32Cfg::kMid : F32Cfg::kSmall;
+  const double tiny = 0.30 * busy_share(tiles_of<F32Tiny>(c));
+  if (big >= mid && big >= small && big >= tiny) return F32Cfg::kBig;
+  if (mid >= small && mid >= tiny) return F32Cfg::kMid;
+  return small >= tiny ? F32Cfg::kSmall : F32Cfg::kTiny;
 }
 
 Plan plan_f32(const Call &c) {
   switch (choose_f32(c)) {
     case F32Cfg::kBig: return make_plan<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots");
     case F32Cfg::kMid: return make_plan<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
-    default: return make_plan<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
+    case F32Cfg::kSmall: return make_plan<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
+    default: return make_plan<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots");
   }
 }
 
@@ -602,7 +607,8 @@ hipError_t launch_f32(const Call &c) {
   switch (choose_f32(c)) {
     case F32Cfg::kBig: return dispatch<F32Big>(c);
     case F32Cfg::kMid: return dispatch<F32Mid>(c);
-    default: return dispatch<F32Small>(c);
+    case F32Cfg::kSmall: return dispatch<F32Small>(c);
+    default: return dispatch<F32Tiny>(c);
   }
 }
 

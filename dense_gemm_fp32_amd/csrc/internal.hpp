@@ -19,7 +19,7 @@ struct Call {
   void *C;
   int ldc;
   bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
-  int tile_config;       // diagnostic: 0 = by size, 1/2/3 = large/medium/small
+  int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny
   hipStream_t stream;
 };
 

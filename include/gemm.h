@@ -129,9 +129,10 @@ int gemm_set_load_mode(int mode);
 
 /*
  * Diagnostic switch for tests: 0 = choose the tile configuration from the
- * problem size (the default); 1, 2, 3 = force the large, medium or small
- * configuration.  Process-wide, like gemm_set_load_mode.  Returns the
- * previous setting, or -1 for an unknown value.
+ * problem size (the default); 1, 2, 3, 4 = force the large, medium, small or
+ * (fp32 only; fp16 uses its small one) tiny configuration.  Process-wide,
+ * like gemm_set_load_mode.  Returns the previous setting, or -1 for an
+ * unknown value.
  */
 int gemm_set_tile_config(int config);
 

@@ -361,7 +361,7 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3], ids=["large", "medium", "small"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4], ids=["large", "medium", "small", "tiny"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
