@@ -399,3 +399,34 @@ def test_f32_sweep_largest_size_sampled():
     rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
     assert rc == 0
     check_sampled(w.dtype, w, A, B, C, out, nrows=16)
+
+
+# ---------------------------------------------------------------- randomized shapes
+
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+
+@settings(max_examples=60, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(dtype=st.sampled_from(DTYPES),
+       M=st.integers(1, 300), N=st.integers(1, 300), K=st.integers(1, 300),
+       pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
+       alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
+       beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4]),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed):
+    """Random small shapes (every tail residue of every tile size is
+    reachable), random row padding (aligned and unaligned leading
+    dimensions), alpha/beta and forced tile configurations."""
+    t = _t(dtype)
+    rng = np.random.default_rng(seed)
+    lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
+    A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
+    B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
+    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+    with tile_config(cfg):
+        rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, "hyp cfg%d" % cfg)
+    assert rc == 0
+    check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out,
+          "random %s M=%d N=%d K=%d ld=%d,%d,%d cfg=%d" % (dtype, M, N, K, lda, ldb, ldc, cfg))
