@@ -8,14 +8,16 @@
 //
 // Pipeline.  Each workgroup owns a BM x BN tile of C and walks K in steps of
 // BK through STAGES LDS slots (the double buffering of the SGEMM summary's
-// tiling section, deepened: the loads of step kt+STAGES-1 are in flight while
-// step kt is multiplied).  Global tiles move with direct global->LDS loads
+// tiling section, deepened).  Global tiles move with direct global->LDS loads
 // (global_load_lds_dwordx4: each wave instruction writes 1 KB of LDS without
 // passing through registers); a wave waits for its own loads with an explicit
 // vmcnt and a raw barrier publishes the slot, so younger loads stay in flight
-// across the barrier.  The barrier for step kt+1 sits before the last k
-// sub-step of step kt, so the first fragments of kt+1 are read while the last
-// MFMAs of kt run.
+// across the barrier.  One barrier per K step, placed before the second half
+// of the MFMAs of step kt's last k sub-step, does three things: step kt+1 has
+// landed (so its first fragments are read while the last MFMAs of kt run),
+// and every wave has read all of step kt's fragments, so step kt's slot is
+// refilled at once with step kt+STAGES.  A load thus has STAGES-1 steps of
+// compute to arrive, and two slots are enough to run the pipeline.
 //
 // LDS layout (per slot, no padding, 16-byte chunks XOR-swizzled by row):
 //   * A [BM rows][BK k]: row r's logical chunk c sits at chunk c ^ swz_a(r),
@@ -94,7 +96,7 @@ struct H16Tile {
   static_assert(RB % 256 == 0, "B rows span whole bank windows");
   static_assert(WTN % 64 == 0, "wave column origin multiple of 64");
   static_assert(FM % 2 == 0, "the last sub-step splits the block rows in halves");
-  static_assert(STAGES >= 3, "the early barrier needs three or more slots");
+  static_assert(STAGES >= 2, "the pipeline needs two or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(NWAVES * EP_BYTES <= LDS_BYTES, "epilogue staging fits in the pipeline LDS");
   static_assert(3 * LOADS <= 63, "vmcnt range");
@@ -452,7 +454,18 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
   }
 }
 
-// Direct-load pipeline over STAGES slots.
+// Wait until at most `steps` K steps of this wave's direct loads are still in
+// flight (LOADS instructions per step; steps <= 0 waits for all of them), and
+// for every LDS access.  More than three steps wait as for three.
+template <class T>
+__device__ __forceinline__ void wait_direct(int steps) {
+  if (steps <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
+  else if (steps == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0);
+  else if (steps == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0);
+  else __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0);
+}
+
+// Direct-load pipeline over STAGES slots: slot j % STAGES holds step j.
 template <class T>
 __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
                                                 uint32_t lds_u32, int wm0, int wn0,
@@ -464,7 +477,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
   frag_setup<T>(wm0, wn0, fa);
 
   // Prologue: step 0 (masked, through registers, when it is the partial
-  // step), then direct loads of steps 1 .. STAGES-2.
+  // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile<T> t;
     reg_load<T, true, true>(p, m0, n0, ks.k0(0), t);
@@ -474,39 +487,33 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
   }
   int issued = 1;
 #pragma unroll
-  for (int j = 1; j < T::STAGES - 1; ++j) {
+  for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
       direct_issue<T>(p, da, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++issued;
     }
   }
   // Publish step 0; the loads of steps 1.. may stay in flight.
-  switch (issued - 1) {
-    case 0: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
-    case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0); break;
-    case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0); break;
-  }
+  wait_direct<T>(issued - 1);
   lds_barrier();
 
   Frag<T> fr[2];
   frag_read<T>(lds, fa, 0, fr[0]);
 
   for (int kt = 0; kt < ks.nk; ++kt) {
-    const char *slot = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    const int slot_no = kt % T::STAGES;
+    const char *slot = lds + slot_no * T::STAGE_BYTES;
     const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
     kstep<T>(slot, next_slot, fa, fr, acc, [&]() {
-      // Step kt+1 must have landed; steps issued after it may stay in flight.
-      // (After the last step nothing is in flight and this is a full wait.)
-      const int after = (issued - 1) - (kt + 1);
-      if (after <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
-      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS));
-      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS));
+      // Step kt+1 must have landed (steps issued after it may stay in
+      // flight), and this wave's reads of step kt must be complete.  After
+      // the last step nothing is in flight and this is a full wait.
+      wait_direct<T>((issued - 1) - (kt + 1));
       lds_barrier();
-      // Every wave has consumed step kt-1: its slot takes step kt+STAGES-1.
-      const int nx = kt + T::STAGES - 1;
+      // Every wave has read all of step kt: its slot takes step kt+STAGES.
+      const int nx = kt + T::STAGES;
       if (nx < ks.nk) {
-        direct_issue<T>(p, da, ks.k0(nx), lds_u32 + (uint32_t)((nx % T::STAGES) * T::STAGE_BYTES));
+        direct_issue<T>(p, da, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         ++issued;
       }
     });
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 // Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
 // L2 group rows), largest first; a call takes the largest tile that still
 // gives at least half of the CUs a workgroup.
-typedef H16Tile<256, 256, 32, 2, 4, 4, 4> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU
+typedef H16Tile<256, 256, 64, 2, 4, 2, 4> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU
 typedef H16Tile<128, 128, 32, 2, 2, 4, 8> F16Mid;     // 4 waves,  64 KB LDS, 2 WG/CU
 typedef H16Tile<64, 128, 32, 1, 2, 4, 8> F16Small;    // 2 waves,  48 KB LDS, 3 WG/CU
 
@@ -657,7 +664,7 @@ static F16Cfg choose_f16(const Call &c) {
 
 Plan plan_f16(const Call &c) {
   switch (choose_f16(c)) {
-    case F16Cfg::kBig: return make_plan<F16Big>(c, "f16 mfma32x32x16 tile 256x256x32 8 waves 4 slots");
+    case F16Cfg::kBig: return make_plan<F16Big>(c, "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
     case F16Cfg::kMid: return make_plan<F16Mid>(c, "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
     default: return make_plan<F16Small>(c, "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
   }

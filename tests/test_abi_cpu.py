@@ -165,11 +165,11 @@ def test_tile_table_choice_and_override():
     assert "64x64x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
     assert "256x128x32" in name("f32", 8192)
-    assert "256x256x32" in name("f16", 4096) and "256x256x32" in name("f16", 3072)
+    assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
     assert "128x128x32" in name("f16", 2048) and "64x128x32" in name("f16", 512)
     prev = dg.gemm_set_tile_config(1)
     try:
-        assert "256x128x32" in name("f32", 256) and "256x256x32" in name("f16", 256)
+        assert "256x128x32" in name("f32", 256) and "256x256x64" in name("f16", 256)
         dg.gemm_set_tile_config(3)
         assert "64x64x32" in name("f32", 4096)
         dg.gemm_set_tile_config(4)
