@@ -84,20 +84,50 @@ constexpr int wait_vmcnt(int n) {
 constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 constexpr int kWaitAll = 0;
 
-// One 16-byte direct global->LDS load per lane: lane L's 16 bytes land at LDS
-// byte address m0 + 16*L (m0 is wave-uniform).  The load is written as inline
-// assembly on purpose: the compiler's wait-count tracking then does not see
-// it, and does not drain every outstanding direct load before each LDS read.
-// Completion is ensured explicitly instead: each wave waits on vmcnt for its
-// own loads of a slot before the barrier that publishes the slot (the
-// kernel's only other vector-memory loads come before the direct loads or
-// after a full wait).  The build checks that no compiler-generated
-// instruction uses m0.
-__device__ __forceinline__ void direct_load16(const void *gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// Buffer resource (V#) for raw byte-addressed loads from `base`: no stride,
+// no swizzle, 32-bit data format, and the largest record count, so the
+// hardware range check never clips (callers keep every access inside the
+// matrix themselves).
+typedef int BufRsrc __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ BufRsrc buffer_rsrc(const void *base) {
+  const unsigned long long b = (unsigned long long)(uintptr_t)base;
+  BufRsrc r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((b >> 32) & 0xffffu));
+  r[2] = -1;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 16-byte direct global->LDS load per lane: lane L loads the 16 bytes at
+// byte offset `voff` from the resource's base and writes them to LDS bytes
+// m0 + 16*L (m0 is wave-uniform).  Each lane sends a 32-bit offset rather
+// than a 64-bit address, which measurably lowers the cost of the loads next
+// to the MFMA work.  The load is written as inline assembly on purpose: the
+// compiler's wait-count tracking then does not see it, and does not drain
+// every outstanding direct load before each LDS read.  Completion is ensured
+// explicitly instead: each wave waits on vmcnt for its own loads of a slot
+// before the barrier that publishes the slot (the kernel's only other
+// vector-memory loads come before the direct loads or after a full wait).
+// The build checks that no compiler-generated instruction uses m0.
+__device__ __forceinline__ void buffer_load16(uint32_t voff, BufRsrc rsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
                : "memory", "m0");
+}
+
+// Wait until at most `steps` K steps of this wave's direct loads are still in
+// flight (LOADS load instructions per step; steps <= 0 waits for all of
+// them), and for every LDS access.  More than three steps wait as for three.
+template <int LOADS>
+__device__ __forceinline__ void wait_direct(int steps) {
+  static_assert(3 * LOADS <= 63, "vmcnt range");
+  if (steps <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
+  else if (steps == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS) & kWaitLgkm0);
+  else if (steps == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LOADS) & kWaitLgkm0);
+  else __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * LOADS) & kWaitLgkm0);
 }
 
 // LDS byte address of a pointer into the kernel's shared array.

@@ -9,8 +9,9 @@
 // Pipeline.  Each workgroup owns a BM x BN tile of C and walks K in steps of
 // BK through STAGES LDS slots (the double buffering of the SGEMM summary's
 // tiling section, deepened).  Global tiles move with direct global->LDS loads
-// (global_load_lds_dwordx4: each wave instruction writes 1 KB of LDS without
-// passing through registers); a wave waits for its own loads with an explicit
+// (buffer_load_dwordx4 ... lds: each wave instruction writes 1 KB of LDS
+// without passing through registers, from 32-bit per-lane offsets against a
+// per-step buffer base); a wave waits for its own loads with an explicit
 // vmcnt and a raw barrier publishes the slot, so younger loads stay in flight
 // across the barrier.  One barrier per K step, placed before the second half
 // of the MFMAs of step kt's last k sub-step, does three things: step kt+1 has
@@ -51,7 +52,8 @@
 // (K % BK != 0) is done first, through registers with per-element masks.  A
 // workgroup whose columns cross an N that is not a multiple of 8, and every
 // workgroup of a call whose A or B is not 16-byte aligned (base or leading
-// dimension), uses the register-staged path instead: masked loads (0 outside
+// dimension) or whose BM*lda or BK*ldb reaches 2^31 elements (32-bit load
+// offsets), uses the register-staged path instead: masked loads (0 outside
 // the matrix; pad elements are never read) written to the same LDS layout.
 #include "common.hpp"
 #include "internal.hpp"
@@ -139,18 +141,20 @@ __device__ __forceinline__ void b_chunk(int q, int lane, int &kr, int &nc) {
 
 // ---------------------------------------------------------------- direct loads
 
-// This lane's global source addresses for K step origin 0.
+// This lane's byte offsets, relative to the tile origin of a K step (A: row
+// m0, column k0; B: row k0, column n0), of the 16-byte chunks it loads.  The
+// offsets do not change from step to step; each step only moves the buffer
+// base.  They fit in 32 bits when BM*lda and BK*ldb are below 2^31, which the
+// kernel checks before taking this path.
 template <class T>
 struct DirectAddr {
-  const uint16_t *a[T::QA_W];
-  const uint16_t *b[T::QB_W];
+  uint32_t a[T::QA_W];
+  uint32_t b[T::QB_W];
 };
 
 template <class T>
 __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0,
                                              DirectAddr<T> &d) {
-  const uint16_t *A = static_cast<const uint16_t *>(p.A);
-  const uint16_t *B = static_cast<const uint16_t *>(p.B);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
@@ -159,7 +163,7 @@ __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0
     a_chunk<T>(wave * T::QA_W + j, lane, r, kc);
     int gr = m0 + r;
     gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
-    d.a[j] = A + (size_t)gr * (size_t)p.lda + kc;
+    d.a[j] = 2u * (uint32_t)((gr - m0) * p.lda + kc);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
@@ -167,22 +171,24 @@ __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0
     b_chunk<T>(wave * T::QB_W + j, lane, kr, nc);
     int gn = n0 + nc;
     gn = gn + 8 <= p.N ? gn : p.N - 8;     // N % 8 == 0 here: the last whole chunk
-    d.b[j] = B + (size_t)kr * (size_t)p.ldb + gn;
+    d.b[j] = 2u * (uint32_t)(kr * p.ldb + (gn - n0));
   }
 }
 
 template <class T>
-__device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAddr<T> &d, int k0,
-                                             uint32_t slot_addr) {
+__device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAddr<T> &d, int m0,
+                                             int n0, int k0, uint32_t slot_addr) {
   const int wave = wave_id();
-  const size_t boff = (size_t)k0 * (size_t)p.ldb;
+  const BufRsrc ra =
+      buffer_rsrc(static_cast<const uint16_t *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
+  const BufRsrc rb =
+      buffer_rsrc(static_cast<const uint16_t *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j)
-    direct_load16(d.a[j] + k0, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+    buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j)
-    direct_load16(d.b[j] + boff,
-                  slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+    buffer_load16(d.b[j], rb, slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
 }
 
 // ---------------------------------------------------------------- register-staged loads
@@ -364,6 +370,25 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
   const float alpha = p.alpha, beta = p.beta;
   constexpr int LPR = T::WTN / 4;                 // lanes per staged row
   constexpr int ROWS_PER_PASS = kWave / LPR;
+  constexpr int PASSES = 32 / ROWS_PER_PASS;
+  const int cl = 4 * (lane % LPR);
+  const int col = c0 + cl;
+  const bool cols_ok = !CHECK || col + 3 < p.N;
+  // Every C value this lane combines (vector path, beta != 0) is loaded
+  // before the first is used, so the latencies of the loads overlap instead
+  // of adding up block row by block row.
+  u32x2 cpre[T::FM][PASSES];
+  if (VEC_C && beta != 0.0f) {
+#pragma unroll
+    for (int bi = 0; bi < T::FM; ++bi)
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
+        cpre[bi][pass] = u32x2{0u, 0u};
+        if (!CHECK || (row < p.M && cols_ok))
+          cpre[bi][pass] = *reinterpret_cast<const u32x2 *>(C + (size_t)row * (size_t)p.ldc + col);
+      }
+  }
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi) {
 #pragma unroll
@@ -372,18 +397,16 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
       for (int r = 0; r < 16; ++r)
         stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[bi][bj][r];
 #pragma unroll
-    for (int pass = 0; pass < 32 / ROWS_PER_PASS; ++pass) {
+    for (int pass = 0; pass < PASSES; ++pass) {
       const int rl = pass * ROWS_PER_PASS + lane / LPR;
-      const int cl = 4 * (lane % LPR);
       const f32x4 v = *reinterpret_cast<const f32x4 *>(&stage[rl * T::EP_STRIDE + cl]);
       const int row = r0 + 32 * bi + rl;
-      const int col = c0 + cl;
       if (CHECK && row >= p.M) continue;
       uint16_t *dst = C + (size_t)row * (size_t)p.ldc + col;
-      if (VEC_C && (!CHECK || col + 3 < p.N)) {
+      if (VEC_C && cols_ok) {
         float o[4];
         if (beta != 0.0f) {
-          const u32x2 w = *reinterpret_cast<const u32x2 *>(dst);
+          const u32x2 w = cpre[bi][pass];
           o[0] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] & 0xffff)), alpha * v[0]);
           o[1] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] >> 16)), alpha * v[1]);
           o[2] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[1] & 0xffff)), alpha * v[2]);
@@ -454,17 +477,6 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
   }
 }
 
-// Wait until at most `steps` K steps of this wave's direct loads are still in
-// flight (LOADS instructions per step; steps <= 0 waits for all of them), and
-// for every LDS access.  More than three steps wait as for three.
-template <class T>
-__device__ __forceinline__ void wait_direct(int steps) {
-  if (steps <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
-  else if (steps == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0);
-  else if (steps == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0);
-  else __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0);
-}
-
 // Direct-load pipeline over STAGES slots: slot j % STAGES holds step j.
 template <class T>
 __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
@@ -483,18 +495,18 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
     reg_load<T, true, true>(p, m0, n0, ks.k0(0), t);
     reg_store<T>(t, lds);
   } else {
-    direct_issue<T>(p, da, ks.k0(0), lds_u32);
+    direct_issue<T>(p, da, m0, n0, ks.k0(0), lds_u32);
   }
   int issued = 1;
 #pragma unroll
   for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
-      direct_issue<T>(p, da, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      direct_issue<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++issued;
     }
   }
   // Publish step 0; the loads of steps 1.. may stay in flight.
-  wait_direct<T>(issued - 1);
+  wait_direct<T::LOADS>(issued - 1);
   lds_barrier();
 
   Frag<T> fr[2];
@@ -508,12 +520,12 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
       // Step kt+1 must have landed (steps issued after it may stay in
       // flight), and this wave's reads of step kt must be complete.  After
       // the last step nothing is in flight and this is a full wait.
-      wait_direct<T>((issued - 1) - (kt + 1));
+      wait_direct<T::LOADS>((issued - 1) - (kt + 1));
       lds_barrier();
       // Every wave has read all of step kt: its slot takes step kt+STAGES.
       const int nx = kt + T::STAGES;
       if (nx < ks.nk) {
-        direct_issue<T>(p, da, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
+        direct_issue<T>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         ++issued;
       }
     });
@@ -560,7 +572,8 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   zero_acc<T>(acc);
 
   const bool n_edge = n0 + T::BN > p.N;
-  const bool direct = VA && VB && (!n_edge || (p.N % 8) == 0);
+  const bool direct = VA && VB && (!n_edge || (p.N % 8) == 0) &&
+                      (long long)T::BM * p.lda < (1LL << 31) && (long long)T::BK * p.ldb < (1LL << 31);
   if (direct) mainloop_direct<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
   else mainloop_staged<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
 

@@ -5,13 +5,15 @@
 //
 // Pipeline.  Each workgroup owns a BM x BN tile of C and walks K in steps of
 // BK (the tiling of the SGEMM summary's tiling section) through STAGES LDS
-// slots filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KB of
-// LDS per wave instruction, no registers in between).  Each wave waits on
-// vmcnt for its own loads of a slot and a raw barrier publishes it, so the
-// loads of later steps stay in flight while this step is multiplied (the
-// summary's shared-memory double buffering, one slot deeper).  The barrier
-// for step kt+1 sits inside the last k group of step kt, after half of its
-// MFMAs, so the barrier wait overlaps them.  Each wave owns a
+// slots filled by direct global->LDS loads (buffer_load_dwordx4 ... lds, 1 KB
+// of LDS per wave instruction, no registers in between, 32-bit per-lane
+// offsets against a per-step buffer base).  Each wave waits on vmcnt for its
+// own loads of a slot and a raw barrier publishes it, so the loads of later
+// steps stay in flight while this step is multiplied (the summary's
+// shared-memory double buffering, deepened).  The barrier for step kt+1 sits
+// inside the last k group of step kt, after half of its MFMAs, so the barrier
+// wait overlaps them; by then every wave has read all of step kt, so step
+// kt's slot is refilled at once with step kt+STAGES.  Each wave owns a
 // (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in AGPRs as FM x FN blocks of
 // 32x32 accumulators.
 //
@@ -38,7 +40,8 @@
 // through registers with per-element masks.  A workgroup whose columns cross
 // an N that is not a multiple of 4, and every workgroup of a call whose A or B
 // is not 16-byte aligned (base or leading dimension; the alignment gate of the
-// SGEMM summary's texture-load variant), uses a register-staged path with
+// SGEMM summary's texture-load variant) or whose BM*lda or BK*ldb reaches
+// 2^30 elements (32-bit load offsets), uses a register-staged path with
 // masked loads (0 outside the matrix; pad elements are never read) into the
 // same LDS layout.  Stores are masked on edge tiles.
 #include "common.hpp"
@@ -77,7 +80,7 @@ struct S32Tile {
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
   static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
   static_assert(FN == 1 || FN == 2 || FN == 4, "FN");
-  static_assert(STAGES >= 3, "the early barrier needs three or more slots");
+  static_assert(STAGES >= 2, "the pipeline needs two or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(3 * LOADS <= 63, "vmcnt range");
 };
@@ -112,15 +115,16 @@ __device__ __forceinline__ void b_chunk32(int q, int lane, int &kr, int &nc) {
 
 template <class T>
 struct DirectAddr32 {
-  const float *a[T::QA_W];
-  const float *b[T::QB_W];
+  uint32_t a[T::QA_W];   // byte offsets from the A tile origin (row m0, column k0)
+  uint32_t b[T::QB_W];   // byte offsets from the B tile origin (row k0, column n0)
 };
 
+// The offsets do not change from step to step; each step only moves the
+// buffer base.  They fit in 32 bits when BM*lda and BK*ldb are below 2^30,
+// which the kernel checks before taking this path.
 template <class T>
 __device__ __forceinline__ void direct_setup32(const GemmParams &p, int m0, int n0,
                                                DirectAddr32<T> &d) {
-  const float *A = static_cast<const float *>(p.A);
-  const float *B = static_cast<const float *>(p.B);
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
 #pragma unroll
@@ -129,7 +133,7 @@ __device__ __forceinline__ void direct_setup32(const GemmParams &p, int m0, int 
     a_chunk32<T>(wave * T::QA_W + j, lane, r, kc);
     int gr = m0 + r;
     gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
-    d.a[j] = A + (size_t)gr * (size_t)p.lda + kc;
+    d.a[j] = 4u * (uint32_t)((gr - m0) * p.lda + kc);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
@@ -137,22 +141,24 @@ __device__ __forceinline__ void direct_setup32(const GemmParams &p, int m0, int 
     b_chunk32<T>(wave * T::QB_W + j, lane, kr, nc);
     int gn = n0 + nc;
     gn = gn + 4 <= p.N ? gn : p.N - 4;     // N % 4 == 0 here: the last whole chunk
-    d.b[j] = B + (size_t)kr * (size_t)p.ldb + gn;
+    d.b[j] = 4u * (uint32_t)(kr * p.ldb + (gn - n0));
   }
 }
 
 template <class T>
 __device__ __forceinline__ void direct_issue32(const GemmParams &p, const DirectAddr32<T> &d,
-                                               int k0, uint32_t slot_addr) {
+                                               int m0, int n0, int k0, uint32_t slot_addr) {
   const int wave = wave_id();
-  const size_t boff = (size_t)k0 * (size_t)p.ldb;
+  const BufRsrc ra =
+      buffer_rsrc(static_cast<const float *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
+  const BufRsrc rb =
+      buffer_rsrc(static_cast<const float *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j)
-    direct_load16(d.a[j] + k0, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+    buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j)
-    direct_load16(d.b[j] + boff,
-                  slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+    buffer_load16(d.b[j], rb, slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
 }
 
 // ---------------------------------------------------------------- register-staged loads
@@ -331,48 +337,41 @@ __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, i
   frag_setup32<T>(wm0, wn0, fa);
 
   // Prologue: step 0 (masked, through registers, when it is the partial
-  // step), then direct loads of steps 1 .. STAGES-2.
+  // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile32<T> t;
     reg_load32<T, true, true>(p, m0, n0, ks.k0(0), t);
     reg_store32<T>(t, lds);
   } else {
-    direct_issue32<T>(p, da, ks.k0(0), lds_u32);
+    direct_issue32<T>(p, da, m0, n0, ks.k0(0), lds_u32);
   }
   int issued = 1;
 #pragma unroll
-  for (int j = 1; j < T::STAGES - 1; ++j) {
+  for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
-      direct_issue32<T>(p, da, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      direct_issue32<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++issued;
     }
   }
-  switch (issued - 1) {
-    case 0: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
-    case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS) & kWaitLgkm0); break;
-    case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS) & kWaitLgkm0); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * T::LOADS) & kWaitLgkm0); break;
-  }
+  wait_direct<T::LOADS>(issued - 1);
   lds_barrier();
 
   Frag32<T> fr[2];
   frag_read32<T>(lds, fa, 0, fr[0]);
 
   for (int kt = 0; kt < ks.nk; ++kt) {
-    const char *slot = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    const int slot_no = kt % T::STAGES;
+    const char *slot = lds + slot_no * T::STAGE_BYTES;
     const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
     kstep32<T>(slot, next_slot, fa, fr, acc, [&]() {
-      // Step kt+1 must have landed; steps issued after it may stay in flight.
-      const int after = (issued - 1) - (kt + 1);
-      if (after <= 0) __builtin_amdgcn_s_waitcnt(kWaitAll);
-      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(T::LOADS));
-      else __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * T::LOADS));
+      // Step kt+1 must have landed (steps issued after it may stay in
+      // flight), and this wave's reads of step kt must be complete.
+      wait_direct<T::LOADS>((issued - 1) - (kt + 1));
       lds_barrier();
-      // Every wave has consumed step kt-1: its slot takes step kt+STAGES-1.
-      const int nx = kt + T::STAGES - 1;
+      // Every wave has read all of step kt: its slot takes step kt+STAGES.
+      const int nx = kt + T::STAGES;
       if (nx < ks.nk) {
-        direct_issue32<T>(p, da, ks.k0(nx),
-                          lds_u32 + (uint32_t)((nx % T::STAGES) * T::STAGE_BYTES));
+        direct_issue32<T>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         ++issued;
       }
     });
@@ -477,7 +476,8 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
 
   const bool n_edge = n0 + T::BN > p.N;
-  const bool direct = VA && VB && (!n_edge || (p.N % 4) == 0);
+  const bool direct = VA && VB && (!n_edge || (p.N % 4) == 0) &&
+                      (long long)T::BM * p.lda < (1LL << 30) && (long long)T::BK * p.ldb < (1LL << 30);
   if (direct) mainloop_direct32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
   else mainloop_staged32<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
