@@ -17,6 +17,10 @@ Also reported on the same line:
     section -- floor(1000*exp((1024-n)/3100)) replays, cache flushed before
     each (outside the timed interval), mean of the second half;
   * fp16: the same for gemm_f16 on the fp16 4096^3 GEMM with beta = 0.5;
+  * power (per precision): average socket power and graphics clock over a
+    few seconds of back-to-back calls, read from the SMU through amdsmi, the
+    energy per GEMM and GFLOP/J, and the matrix peak scaled to the measured
+    clock (peak x clock / 2400 MHz); null where amdsmi is unavailable;
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same workload (a subset of output rows).
 """
@@ -65,6 +69,88 @@ def load_traffic(key):
     return ent.get("hbm_bytes_per_launch")
 
 
+NOMINAL_SCLK_MHZ = 2400.0
+
+
+def smi_handle(torch, dev):
+    """amdsmi handle of `dev` (matched by PCI bus), or None without amdsmi."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+    except Exception:
+        return None, None
+    if not handles:
+        return None, None
+    props = torch.cuda.get_device_properties(dev)
+    for h in handles:
+        try:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+            if int(bdf.split(":")[1], 16) == props.pci_bus_id:
+                return amdsmi, h
+        except Exception:
+            continue
+    return amdsmi, handles[0]
+
+
+def power_window(torch, dev, call, flops, peak, seconds, warm=1.5):
+    """Back-to-back calls for `warm` + `seconds` seconds.  Power is the SMU
+    energy accumulator's increase over its own timestamps between two reads
+    taken under load (the SMU refreshes it about once a second, so both
+    snapshots fall inside the loaded interval); clocks are the per-XCD
+    graphics clocks sampled in between.  Returns None without amdsmi."""
+    smi, h = smi_handle(torch, dev)
+    if h is None:
+        return None
+
+    def energy():
+        e = smi.amdsmi_get_energy_count(h)
+        return e["energy_accumulator"] * e["counter_resolution"] * 1e-6, e["timestamp"] * 1e-9
+
+    def run_for(sec, samples=None):
+        calls, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < sec:
+            for _ in range(16):
+                call()
+            calls += 16
+            torch.cuda.synchronize(dev)
+            if samples is not None:
+                try:
+                    m = smi.amdsmi_get_gpu_metrics_info(h)
+                    clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int) and c < 0xFFFF]
+                    samples.append((sum(clks) / len(clks) if clks else None,
+                                    m.get("current_socket_power")))
+                except Exception:
+                    pass
+        return calls, time.perf_counter() - t0
+
+    try:
+        run_for(warm)
+        e0, ts0 = energy()
+        samples = []
+        calls, wall = run_for(seconds, samples)
+        e1, ts1 = energy()
+    except Exception:
+        return None
+    if ts1 <= ts0:
+        return None
+    watts = (e1 - e0) / (ts1 - ts0)
+    clks = [c for c, _ in samples if c]
+    clk = sum(clks) / len(clks) if clks else None
+    per_call_s = wall / calls
+    joules = watts * per_call_s
+    res = {"avg_socket_power_w": round(watts, 1),
+           "window_s": round(wall, 2), "calls": calls,
+           "ms_per_call": round(per_call_s * 1e3, 5),
+           "energy_per_gemm_j": round(joules, 6),
+           "gflop_per_j": round(flops / joules / 1e9, 1),
+           "avg_gfxclk_mhz": round(clk, 1) if clk else None,
+           "clock_adjusted_peak": round(peak * clk / NOMINAL_SCLK_MHZ, 1) if clk else None}
+    if clk:
+        res["frac_of_clock_adjusted_peak"] = round(flops / per_call_s / 1e12 / res["clock_adjusted_peak"], 4)
+    return res
+
+
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,6 +159,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--no-p4", action="store_true")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power / energy windows")
+    ap.add_argument("--power-seconds", type=float, default=3.0,
+                    help="length of each measured power window")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--sweep", action="store_true",
@@ -151,7 +241,7 @@ def main():
                 "mean_ms": round(mean, 5), "median_ms": round(sorted(last)[len(last) // 2], 5),
                 "min_ms": round(min(times), 5), "tflops": round(w.flops / (mean * 1e-3) / 1e12, 2)}
 
-    def measure(fn, w, peak, key, steps, warmup, p4):
+    def measure(fn, w, peak, key, steps, warmup, p4, power=False):
         (dA, dB, dC), host = upload(w)
         wall, launch_ms = timed_steps(fn, w, dA, dB, dC, steps, warmup)
         ms_per_step = wall * 1e3 / steps
@@ -169,6 +259,11 @@ def main():
         }
         if p4:
             res["p4_protocol"] = p4_protocol(fn, w, dA, dB, dC)
+        if power:
+            res["power"] = power_window(
+                torch, dev,
+                lambda: fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream),
+                w.flops, peak, args.power_seconds)
         del dA, dB, dC
         torch.cuda.empty_cache()
         return res, host
@@ -180,7 +275,8 @@ def main():
         return
     w32 = wl.F32_4096
     main_res, host32 = measure(dg.gemm_f32, w32, PEAK_F32, "f32", args.steps, args.warmup,
-                               not args.no_p4 and args.only is None)
+                               not args.no_p4 and args.only is None,
+                               not args.no_power and args.only is None)
     if args.only == "f32":
         print(json.dumps({"only": "f32", **main_res}), flush=True)
         return
@@ -189,7 +285,7 @@ def main():
     if not args.no_fp16:
         w16 = wl.F16_4096
         f16_res, _ = measure(dg.gemm_f16, w16, PEAK_F16, "f16", args.steps, args.warmup,
-                             not args.no_p4)
+                             not args.no_p4, not args.no_power)
         f16_res = {"workload": "fp16 in/out, fp32 accumulation, M=N=K=4096, A,B,C ~ U[-1,1], "
                                "alpha=1, beta=0.5", "unit": "TFLOP/s", **f16_res}
 
@@ -217,6 +313,7 @@ def main():
         "pct_of_peak": round(100.0 * main_res["value"] / PEAK_F32, 2),
         "roofline": main_res["roofline"],
         "p4_protocol": main_res.get("p4_protocol"),
+        "power": main_res.get("power"),
         "fp16": f16_res,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
