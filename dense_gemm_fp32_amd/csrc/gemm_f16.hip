@@ -665,7 +665,7 @@ enum class F16Cfg { kBig, kMid, kSmall };
 
 static F16Cfg choose_f16(const Call &c) {
   if (c.tile_config == 1) return F16Cfg::kBig;
-  if (c.tile_config == 2) return F16Cfg::kMid;
+  if (c.tile_config == 2 || c.tile_config == 5) return F16Cfg::kMid;
   if (c.tile_config >= 3) return F16Cfg::kSmall;
   // Measured: the large tile stays ahead down to about half a round of
   // tiles (fewer busy CUs draw less power and clock higher), the medium one

@@ -13,9 +13,13 @@
 // shared-memory double buffering, deepened).  The barrier for step kt+1 sits
 // inside the last k group of step kt, after half of its MFMAs, so the barrier
 // wait overlaps them; by then every wave has read all of step kt, so step
-// kt's slot is refilled at once with step kt+STAGES.  Each wave owns a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in AGPRs as FM x FN blocks of
-// 32x32 accumulators.
+// kt's slot can take step kt+STAGES.  The multi-wave tiles spread that step's
+// loads over the following k slots, one between each group of MFMAs
+// (mainloop_spread32): issued all at once they fill the load queue, and the
+// wave that blocks on a full queue also stops issuing MFMAs.  The one-wave
+// tiles, which share a CU with other workgroups, issue them together
+// (mainloop_direct32).  Each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile
+// held as FM x FN blocks of 32x32 accumulators.
 //
 // Operand layout.  For v_mfma_f32_32x32x2_f32 lane l supplies A(row l%32,
 // k-slot l/32) and B(k-slot l/32, col l%32) and receives C(row
@@ -49,9 +53,11 @@
 
 namespace dgemm {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_,
+          bool SPREAD_ = false>
 struct S32Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr bool SPREAD = SPREAD_;               // direct path: loads spread over the step
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
   static constexpr int GROUP_M = GROUP_M_;
@@ -378,6 +384,147 @@ __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, i
   }
 }
 
+// One direct load (number j of this wave's LOADS per step) of the step whose
+// buffer resources are (ra, rb) into the slot at `slot_addr`.
+template <class T>
+__device__ __forceinline__ void direct_one32(const DirectAddr32<T> &d, int j, BufRsrc ra,
+                                             BufRsrc rb, uint32_t slot_addr, int wave) {
+  if (j < T::QA_W)
+    buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+  else
+    buffer_load16(d.b[j - T::QA_W], rb,
+                  slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j - T::QA_W) * 1024));
+}
+
+// The step whose loads are in progress: its buffer resources and LDS slot.
+struct Fill {
+  BufRsrc ra, rb;
+  uint32_t slot_addr;
+  bool live;           // the step exists (index < nk)
+};
+
+template <class T>
+__device__ __forceinline__ Fill make_fill(const GemmParams &p, const KSteps &ks, int step, int m0,
+                                          int n0, uint32_t slot_addr) {
+  Fill f;
+  f.live = step < ks.nk;
+  f.slot_addr = slot_addr;
+  const int k0 = f.live ? ks.k0(step) : 0;
+  f.ra = buffer_rsrc(static_cast<const float *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
+  f.rb = buffer_rsrc(static_cast<const float *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
+  return f;
+}
+
+// Direct-load pipeline with the loads spread out.  A step has NS = 4*KG k
+// slots of FM*FN MFMAs each.  The barrier that publishes step kt+1 sits after
+// k slot NS-3 of step kt (half of the last k group); once past it, every wave
+// has read all of step kt, so step kt's slot takes step kt+STAGES.  Instead of
+// issuing that step's LOADS loads at once -- which fills the load queue and
+// holds up the issuing wave, and with it the MFMAs of its SIMD -- one load (or
+// a few, evenly) follows each of the next NS k slots: slots NS-2 and NS-1 of
+// step kt and slots 0 .. NS-3 of step kt+1.  A step's last load is thus issued
+// just before the barrier of the step that follows the one that started it,
+// and is needed STAGES-2 barriers later.
+template <class T>
+__device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, int n0, char *lds,
+                                                  uint32_t lds_u32, int wm0, int wn0,
+                                                  f32x16 (&acc)[T::FM][T::FN]) {
+  static_assert(T::STAGES >= 3, "a load needs a step of lead");
+  static_assert(T::STAGES - 2 <= 3, "vmcnt steps");
+  static_assert(T::KG % 2 == 0, "the last k group reads the next step's group 0 into fr[0]");
+  constexpr int NS = 4 * T::KG;            // k slots per step
+  constexpr int L = T::LOADS;
+  constexpr int NREAD = T::FM + 4;         // LDS reads per k group
+  constexpr int RPS = (NREAD + 3) / 4;     // reads placed after each k slot
+  const KSteps ks = make_steps(p.K, T::BK);
+  DirectAddr32<T> da;
+  direct_setup32<T>(p, m0, n0, da);
+  FragAddr32<T> fa;
+  frag_setup32<T>(wm0, wn0, fa);
+  const int wave = wave_id();
+
+  if (ks.tail) {
+    RegTile32<T> t;
+    reg_load32<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_store32<T>(t, lds);
+  } else {
+    direct_issue32<T>(p, da, m0, n0, ks.k0(0), lds_u32);
+  }
+  int pro = 0;
+#pragma unroll
+  for (int j = 1; j < T::STAGES; ++j) {
+    if (j < ks.nk) {
+      direct_issue32<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      ++pro;
+    }
+  }
+  wait_direct<L>(pro);
+  lds_barrier();
+
+  Frag32<T> fr[2];
+  frag_read32<T>(lds, fa, 0, fr[0]);
+  // Before the first barrier nothing is being refilled.
+  Fill fill = make_fill<T>(p, ks, ks.nk, m0, n0, 0);
+
+  for (int kt = 0; kt < ks.nk; ++kt) {
+    const int slot_no = kt % T::STAGES;
+    const char *slot = lds + slot_no * T::STAGE_BYTES;
+    const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+#pragma unroll
+    for (int g = 0; g < T::KG; ++g) {
+      Frag32<T> &cur = fr[g & 1];
+      Frag32<T> &nxt = fr[(g + 1) & 1];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int kslot = 4 * g + sl;
+        if (kslot == NS - 2) {
+          // Publish step kt+1: steps up to kt+STAGES-1 are fully issued.
+          const int steps_after = (ks.nk < kt + T::STAGES ? ks.nk : kt + T::STAGES) - kt - 2;
+          wait_direct<L>(steps_after);
+          lds_barrier();
+          fill = make_fill<T>(p, ks, kt + T::STAGES, m0, n0,
+                              lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
+        }
+        // LDS reads for the next k group (or the next step's group 0), a
+        // few after each k slot's MFMAs.
+        const bool last = g + 1 == T::KG;
+        if (!last || sl >= 2) {
+          const int first = last ? 2 * RPS * (sl - 2) : RPS * sl;
+          const int cnt = last ? 2 * RPS : RPS;
+          const char *rs = last ? next_slot : slot;
+          const int rg = last ? 0 : g + 1;
+          // Reads in frag_read32's order: B for k 0..3, then A blocks.
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int r = first + q;
+            if (q < cnt && r < NREAD) {
+              typedef typename FVec<T::FN>::type BVec;
+              if (r < 4) nxt.b[r] = *reinterpret_cast<const BVec *>(rs + fa.b + (8 * rg + r) * T::RB);
+              else nxt.a[r - 4] = *reinterpret_cast<const f32x4 *>(rs + fa.a[rg] + 32 * (r - 4) * T::RA);
+            }
+          }
+        }
+#pragma unroll
+        for (int bi = 0; bi < T::FM; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < T::FN; ++bj) {
+            float bv;
+            if constexpr (T::FN == 1) bv = cur.b[sl]; else bv = cur.b[sl][bj];
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[bi][sl], bv, acc[bi][bj], 0, 0, 0);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+        // Loads of the step being filled: gap number `gap` of NS since the
+        // barrier that freed its slot.
+        const int gap = kslot >= NS - 2 ? kslot - (NS - 2) : kslot + 2;
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+          if ((j * NS) / L == gap && fill.live) direct_one32<T>(da, j, fill.ra, fill.rb, fill.slot_addr, wave);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
 template <class T, bool VA, bool VB>
 __device__ __forceinline__ void mainloop_staged32(const GemmParams &p, int m0, int n0, char *lds,
                                                   int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
@@ -478,8 +625,12 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   const bool n_edge = n0 + T::BN > p.N;
   const bool direct = VA && VB && (!n_edge || (p.N % 4) == 0) &&
                       (long long)T::BM * p.lda < (1LL << 30) && (long long)T::BK * p.ldb < (1LL << 30);
-  if (direct) mainloop_direct32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
-  else mainloop_staged32<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+  if (direct) {
+    if constexpr (T::SPREAD) mainloop_spread32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+    else mainloop_direct32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+  } else {
+    mainloop_staged32<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
 
   const bool edge = n_edge || (m0 + T::BM > p.M);
@@ -493,8 +644,9 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 // L2 group rows), largest first.  A call takes the configuration with the
 // best estimated throughput for its tile count (the size-based kernel choice
 // of the SGEMM summary's results section, retuned for 256 CUs).
-typedef S32Tile<256, 128, 32, 4, 2, 3, 8> F32Big;     // 8 waves, 144 KB LDS, 1 WG/CU
-typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32Mid;     // 4 waves,  48 KB LDS, 3 WG/CU
+typedef S32Tile<256, 128, 32, 4, 2, 3, 8, true> F32Big;  // 8 waves, 144 KB LDS, 1 WG/CU
+typedef S32Tile<128, 128, 16, 2, 2, 3, 8, true> F32Mid;  // 4 waves,  48 KB LDS, 3 WG/CU
+typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issued together
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
 typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
@@ -566,38 +718,58 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kBig, kMid, kSmall, kTiny };
+enum class F32Cfg { kBig, kMid, kMidB, kSmall, kTiny };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
 // T/CUs (several workgroups per CU share it, so only whole tiles per CU
-// count).  Scores multiply it by the configuration's measured throughput at
-// full occupancy (fraction of the fp32 peak at 4096^3: 0.89, 0.87, 0.60;
-// 0.30 assumed for the 32x32 tile, which only small problems take).
+// count).
 static double busy_share(long long tiles) {
   const double per_cu = (double)tiles / kCUs;
   const double rounds = (double)((tiles + kCUs - 1) / kCUs);
   return per_cu / rounds;
 }
 
+// Share of a busy CU's four SIMDs that hold a wave: the workgroups resident
+// on it at once (at most `per_cu`, the LDS limit) times the waves of each.
+template <class T>
+static double simd_share(long long tiles, int per_cu) {
+  long long resident = (tiles + kCUs - 1) / kCUs;
+  if (resident > per_cu) resident = per_cu;
+  const double waves = (double)(resident * T::NWAVES);
+  return waves >= 4.0 ? 1.0 : waves / 4.0;
+}
+
+// Otherwise score = measured throughput at full occupancy (fraction of the fp32 peak at
+// 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57, 0.63) x the two
+// shares above; the largest score wins.
 static F32Cfg choose_f32(const Call &c) {
   if (c.tile_config == 1) return F32Cfg::kBig;
   if (c.tile_config == 2) return F32Cfg::kMid;
   if (c.tile_config == 3) return F32Cfg::kSmall;
   if (c.tile_config == 4) return F32Cfg::kTiny;
-  const double big = 0.89 * busy_share(tiles_of<F32Big>(c));
-  const double mid = 0.87 * busy_share(tiles_of<F32Mid>(c));
-  const double small = 0.60 * busy_share(tiles_of<F32Small>(c));
-  const double tiny = 0.30 * busy_share(tiles_of<F32Tiny>(c));
+  if (c.tile_config == 5) return F32Cfg::kMidB;
+  const long long tb = tiles_of<F32Big>(c), tm = tiles_of<F32Mid>(c);
+  const long long ts = tiles_of<F32Small>(c), tt = tiles_of<F32Tiny>(c);
+  // Problems too small to give every CU even a 32x32 tile are latency-bound:
+  // the most workgroups and the shortest prologue win.
+  if (tt <= kCUs) return F32Cfg::kTiny;
+  const double big = 0.92 * busy_share(tb) * simd_share<F32Big>(tb, 1);
+  const double mid = 0.91 * busy_share(tm) * simd_share<F32Mid>(tm, 3);
+  const double small = 0.57 * busy_share(ts) * simd_share<F32Small>(ts, 3);
+  const double tiny = 0.63 * busy_share(tt) * simd_share<F32Tiny>(tt, 6);
   if (big >= mid && big >= small && big >= tiny) return F32Cfg::kBig;
-  if (mid >= small && mid >= tiny) return F32Cfg::kMid;
+  // Spread loads pay while a CU holds one workgroup; with several resident
+  // the others hide the load bursts and issuing them together is cheaper.
+  if (mid >= small && mid >= tiny) return tm <= kCUs ? F32Cfg::kMid : F32Cfg::kMidB;
   return small >= tiny ? F32Cfg::kSmall : F32Cfg::kTiny;
 }
 
 Plan plan_f32(const Call &c) {
   switch (choose_f32(c)) {
-    case F32Cfg::kBig: return make_plan<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots");
-    case F32Cfg::kMid: return make_plan<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
+    case F32Cfg::kBig: return make_plan<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads");
+    case F32Cfg::kMid: return make_plan<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads");
+    case F32Cfg::kMidB: return make_plan<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
     case F32Cfg::kSmall: return make_plan<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
     default: return make_plan<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots");
   }
@@ -607,6 +779,7 @@ hipError_t launch_f32(const Call &c) {
   switch (choose_f32(c)) {
     case F32Cfg::kBig: return dispatch<F32Big>(c);
     case F32Cfg::kMid: return dispatch<F32Mid>(c);
+    case F32Cfg::kMidB: return dispatch<F32MidB>(c);
     case F32Cfg::kSmall: return dispatch<F32Small>(c);
     default: return dispatch<F32Tiny>(c);
   }

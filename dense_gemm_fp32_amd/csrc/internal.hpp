@@ -19,7 +19,8 @@ struct Call {
   void *C;
   int ldc;
   bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
-  int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny
+  int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
+                         // 5 = medium with the loads of a step issued together
   hipStream_t stream;
 };
 

@@ -130,7 +130,9 @@ int gemm_set_load_mode(int mode);
 /*
  * Diagnostic switch for tests: 0 = choose the tile configuration from the
  * problem size (the default); 1, 2, 3, 4 = force the large, medium, small or
- * (fp32 only; fp16 uses its small one) tiny configuration.  Process-wide,
+ * (fp32 only; fp16 uses its small one) tiny configuration; 5 = the medium
+ * configuration with each K step's loads issued together rather than spread
+ * (fp32 only; fp16 uses its medium one).  Process-wide,
  * like gemm_set_load_mode.  Returns the previous setting, or -1 for an
  * unknown value.
  */

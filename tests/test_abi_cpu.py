@@ -162,7 +162,8 @@ def test_tile_table_choice_and_override():
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
     assert "256x128x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
-    assert "64x64x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
+    assert "32x32x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
+    assert "32x32x32" in name("f32", 64) and "32x32x32" in name("f32", 1536)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
     assert "256x128x32" in name("f32", 8192)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)

@@ -361,7 +361,7 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4], ids=["large", "medium", "small", "tiny"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5], ids=["large", "medium", "small", "tiny", "medium-bunched"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -413,7 +413,7 @@ from hypothesis import HealthCheck, given, settings, strategies as st
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
        beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 5]),
        seed=st.integers(0, 2 ** 31 - 1))
 def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed):
     """Random small shapes (every tail residue of every tile size is
