@@ -1,5 +1,5 @@
-"""CPU oracle for row-major C := alpha*A*B + beta*C (fp32, and fp16 with fp32
-accumulation), evaluated in double precision.
+"""CPU oracle for row-major C := alpha*A*B + beta*C (fp32; fp16 with fp32
+accumulation; fp16 inputs with an fp32 C), evaluated in double precision.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
@@ -58,6 +58,10 @@ def _load():
     lib.oracle_gemm_f32_elems.restype = None
     lib.oracle_gemm_f16_elems.argtypes = [I, D, lp, L, lp, L, D, lp, L, L, lp, lp, lp, lp]
     lib.oracle_gemm_f16_elems.restype = None
+    lib.oracle_gemm_f16f32.argtypes = [I, I, I, D, lp, L, lp, L, D, lp, L, lp, lp]
+    lib.oracle_gemm_f16f32.restype = I
+    lib.oracle_gemm_f16f32_elems.argtypes = [I, D, lp, L, lp, L, D, lp, L, L, lp, lp, lp, lp]
+    lib.oracle_gemm_f16f32_elems.restype = None
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = D
     lib.oracle_double_to_half.argtypes = [D]
@@ -93,37 +97,51 @@ def _flat(buf, dtype):
     return a
 
 
+# Storage type of (A and B, C) per call type: "f32" all binary32, "f16" all
+# binary16, "f16f32" binary16 inputs with a binary32 C (the output type).
+OPERANDS = {"f32": ("f32", "f32"), "f16": ("f16", "f16"), "f16f32": ("f16", "f32")}
+
+
+def out_type(dtype):
+    """Storage type of C and of the result for a call type."""
+    return OPERANDS[dtype][1]
+
+
+def _prep(x, t):
+    """Host buffer as a flat array of the storage type t ("f32" / "f16")."""
+    if x is None:
+        return None
+    x = np.asarray(x)
+    if t == "f16":
+        if x.dtype == np.float16:
+            x = x.view(np.uint16)
+        return _flat(x, np.uint16)
+    return _flat(x, np.float32)
+
+
 def gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype="f32"):
     """R = alpha*A*B + beta*C in double, and G = |A||B| (both dense M x N).
 
     A, B, C are host buffers in the library's layout: element (i, j) of a
     matrix with leading dimension ld is buf[i*ld + j].  dtype "f32" takes
     float32 buffers; "f16" takes float16 (or uint16 bit-pattern) buffers.
-    A and B are not read when alpha == 0 or K == 0; C is not read when
-    beta == 0 (either may then be None).
+    "f16f32" takes float16 A and B with a float32 C.  A and B are not read
+    when alpha == 0 or K == 0; C is not read when beta == 0 (either may then
+    be None).
     """
     lib = _load()
-    if dtype == "f32":
-        conv = np.float32
-        fn = lib.oracle_gemm_f32
-    elif dtype == "f16":
-        conv = np.uint16
-        fn = lib.oracle_gemm_f16
-    else:
+    fns = {"f32": lib.oracle_gemm_f32, "f16": lib.oracle_gemm_f16, "f16f32": lib.oracle_gemm_f16f32}
+    if dtype not in fns:
         raise ValueError(dtype)
-
-    def prep(x):
-        if x is None:
-            return None
-        x = np.asarray(x)
-        if dtype == "f16" and x.dtype == np.float16:
-            x = x.view(np.uint16)
-        return _flat(x, conv)
+    fn = fns[dtype]
+    tin, tc = OPERANDS[dtype]
+    prep = lambda x: _prep(x, tin)
+    prep_c = lambda x: _prep(x, tc)
 
     use_ab = alpha != 0.0 and K > 0
     a = prep(A) if use_ab else None
     b = prep(B) if use_ab else None
-    c = prep(C) if beta != 0.0 else None
+    c = prep_c(C) if beta != 0.0 else None
     if use_ab and M > 0 and N > 0:
         _check_span(a, M, K, lda, "A")
         _check_span(b, K, N, ldb, "B")
@@ -146,25 +164,17 @@ def gemm_elems(rows, cols, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype="f32"):
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     if rows.shape != cols.shape or rows.ndim != 1:
         raise ValueError("rows and cols must be equal-length 1-D arrays")
-    if dtype == "f32":
-        conv, fn = np.float32, lib.oracle_gemm_f32_elems
-    elif dtype == "f16":
-        conv, fn = np.uint16, lib.oracle_gemm_f16_elems
-    else:
+    fns = {"f32": lib.oracle_gemm_f32_elems, "f16": lib.oracle_gemm_f16_elems,
+           "f16f32": lib.oracle_gemm_f16f32_elems}
+    if dtype not in fns:
         raise ValueError(dtype)
-
-    def prep(x):
-        if x is None:
-            return None
-        x = np.asarray(x)
-        if dtype == "f16" and x.dtype == np.float16:
-            x = x.view(np.uint16)
-        return _flat(x, conv)
+    fn = fns[dtype]
+    tin, tc = OPERANDS[dtype]
 
     use_ab = alpha != 0.0 and K > 0
-    a = prep(A) if use_ab else None
-    b = prep(B) if use_ab else None
-    c = prep(C) if beta != 0.0 else None
+    a = _prep(A, tin) if use_ab else None
+    b = _prep(B, tin) if use_ab else None
+    c = _prep(C, tc) if beta != 0.0 else None
     n = rows.shape[0]
     R = np.empty(n, np.float64)
     G = np.empty(n, np.float64)
@@ -278,9 +288,10 @@ def checksum(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype="f32"):
     magnitude = |alpha| sum_k colsum|A|_k rowsum|B|_k + |beta| sum|C| bounds the
     sum of the terms of G that enter the bound.
     """
-    A2 = _view2(A, M, K, lda, dtype) if (alpha != 0 and K > 0) else None
-    B2 = _view2(B, K, N, ldb, dtype) if (alpha != 0 and K > 0) else None
-    C2 = _view2(C, M, N, ldc, dtype) if beta != 0 else None
+    tin, tc = OPERANDS[dtype]
+    A2 = _view2(A, M, K, lda, tin) if (alpha != 0 and K > 0) else None
+    B2 = _view2(B, K, N, ldb, tin) if (alpha != 0 and K > 0) else None
+    C2 = _view2(C, M, N, ldc, tc) if beta != 0 else None
     exp = 0.0
     mag = 0.0
     if A2 is not None:
@@ -302,13 +313,14 @@ def freivalds(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, x, dtype="f32"):
     x = np.asarray(x, np.float64)
     y = np.zeros(M, np.float64)
     mag = np.zeros(M, np.float64)
+    tin, tc = OPERANDS[dtype]
     if alpha != 0 and K > 0:
-        A2 = _view2(A, M, K, lda, dtype)
-        B2 = _view2(B, K, N, ldb, dtype)
+        A2 = _view2(A, M, K, lda, tin)
+        B2 = _view2(B, K, N, ldb, tin)
         y += float(alpha) * (A2 @ (B2 @ x))
         mag += abs(float(alpha)) * (np.abs(A2) @ (np.abs(B2) @ np.abs(x)))
     if beta != 0:
-        C2 = _view2(C, M, N, ldc, dtype)
+        C2 = _view2(C, M, N, ldc, tc)
         y += float(beta) * (C2 @ x)
         mag += abs(float(beta)) * (np.abs(C2) @ np.abs(x))
     return y, mag

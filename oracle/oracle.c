@@ -237,6 +237,49 @@ int oracle_gemm_f16(int M, int N, int K, double alpha,
     return err;
 }
 
+/* Mixed precision: binary16 A and B, binary32 C (and output).  The page on
+ * tensor-core WMMA versus fp32 cores accumulates half products into float
+ * accumulators and writes the float result; here, as everywhere in this
+ * file, the sum is formed in double (every half product is exact), and C is
+ * read as float only when beta != 0. */
+int oracle_gemm_f16f32(int M, int N, int K, double alpha,
+                       const uint16_t *A, long lda, const uint16_t *B, long ldb,
+                       double beta, const float *C, long ldc,
+                       double *R, double *G)
+{
+    int use_ab = (alpha != 0.0) && (K > 0);
+    int err = 0;
+#pragma omp parallel
+    {
+        size_t n1 = (size_t)(N > 0 ? N : 1);
+        double *s = (double *)malloc(sizeof(double) * n1 * 3);
+        if (!s) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+            double *g = s + n1;
+            double *bdec = s + 2 * n1;
+#pragma omp for schedule(static)
+            for (int i = 0; i < M; ++i) {
+                if (use_ab) {
+                    row_f16(N, K, A + (size_t)i * (size_t)lda, B, ldb, s, g, bdec);
+                } else {
+                    for (int j = 0; j < N; ++j) { s[j] = 0.0; g[j] = 0.0; }
+                }
+                for (int j = 0; j < N; ++j) {
+                    double r = use_ab ? alpha * s[j] : 0.0;
+                    if (beta != 0.0)
+                        r += beta * (double)C[(size_t)i * (size_t)ldc + j];
+                    R[(size_t)i * N + j] = r;
+                    G[(size_t)i * N + j] = g[j];
+                }
+            }
+            free(s);
+        }
+    }
+    return err;
+}
+
 /* Selected elements only: R[t], G[t] for (rows[t], cols[t]), t < count.  Same
  * arithmetic as the full version (k ascending), for sizes where the full
  * product would take too long on the host. */
@@ -289,6 +332,33 @@ void oracle_gemm_f16_elems(int K, double alpha,
         double r = use_ab ? alpha * s : 0.0;
         if (beta != 0.0)
             r += beta * oracle_half_to_double(C[i * (size_t)ldc + j]);
+        R[t] = r;
+        G[t] = g;
+    }
+}
+
+void oracle_gemm_f16f32_elems(int K, double alpha,
+                              const uint16_t *A, long lda, const uint16_t *B, long ldb,
+                              double beta, const float *C, long ldc,
+                              long count, const long *rows, const long *cols,
+                              double *R, double *G)
+{
+    int use_ab = (alpha != 0.0) && (K > 0);
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < count; ++t) {
+        size_t i = (size_t)rows[t], j = (size_t)cols[t];
+        double s = 0.0, g = 0.0;
+        if (use_ab) {
+            for (int k = 0; k < K; ++k) {
+                double a = oracle_half_to_double(A[i * (size_t)lda + k]);
+                double b = oracle_half_to_double(B[(size_t)k * (size_t)ldb + j]);
+                s += a * b;
+                g += fabs(a) * fabs(b);
+            }
+        }
+        double r = use_ab ? alpha * s : 0.0;
+        if (beta != 0.0)
+            r += beta * (double)C[i * (size_t)ldc + j];
         R[t] = r;
         G[t] = g;
     }

@@ -38,6 +38,13 @@ MUTANTS = [
     ("f16_no_overflow_check", "if (v > 65504.0)", "if (v > 65504.0 && 0)", 1),
     ("f16_elems_A_stride", "double a = oracle_half_to_double(A[i * (size_t)lda + k]);",
      "double a = oracle_half_to_double(A[i * (size_t)K + k]);", 1),
+    ("mixed_beta_dropped", "r += beta * (double)C[(size_t)i * (size_t)ldc + j];", "r += 0.0;", 2),
+    ("mixed_C_as_half", "r += beta * (double)C[(size_t)i * (size_t)ldc + j];",
+     "r += beta * oracle_half_to_double(((const uint16_t *)C)[(size_t)i * (size_t)ldc + j]);", 2),
+    ("mixed_C_rounded_to_half", "r += beta * (double)C[(size_t)i * (size_t)ldc + j];",
+     "r += beta * oracle_half_to_double(oracle_double_to_half((double)C[(size_t)i * (size_t)ldc + j]));", 2),
+    ("mixed_elems_beta_sign", "r += beta * (double)C[i * (size_t)ldc + j];",
+     "r -= beta * (double)C[i * (size_t)ldc + j];", 2),
 ]
 
 

@@ -46,18 +46,24 @@ def _exact(M, N, K, alpha, A, B, beta, C):
 
 # ---------------------------------------------------------------- brute force
 
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+_NP = {"f32": np.float32, "f16": np.float16}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "f16f32"])
 def test_exact_rational_dyadic_all_small_shapes(dtype):
     """Small dyadic inputs (multiples of 1/8 in [-2, 2]): every product and
     partial sum is exact in double, so the oracle must equal the rational
     value exactly, for every M, N, K in 0..4 and several alpha/beta."""
-    t = np.float32 if dtype == "f32" else np.float16
+    tin, tc = (_NP[x] for x in wl.operand_types(dtype))
     rng = np.random.default_rng(7)
     for M, N, K in itertools.product(range(0, 5), repeat=3):
         for alpha, beta in [(1.0, 0.0), (-1.5, 0.5), (0.25, -2.0), (0.0, 1.0), (2.0, 1.0)]:
-            A = (rng.integers(-16, 17, size=(M, K)) / 8.0).astype(t)
-            B = (rng.integers(-16, 17, size=(K, N)) / 8.0).astype(t)
-            C = (rng.integers(-16, 17, size=(M, N)) / 8.0).astype(t)
+            A = (rng.integers(-16, 17, size=(M, K)) / 8.0).astype(tin)
+            B = (rng.integers(-16, 17, size=(K, N)) / 8.0).astype(tin)
+            # C carries a 1/4096 part in the mixed case: exact in fp32, not in
+            # fp16, so C read through the wrong type cannot pass.
+            cfine = (rng.integers(-8, 9, size=(M, N)) / 4096.0) if dtype == "f16f32" else 0.0
+            C = (rng.integers(-16, 17, size=(M, N)) / 8.0 + cfine).astype(tc)
             lda, ldb, ldc = K + 1, N + 2, N + 3
             R, G = oracle.gemm(M, N, K, alpha, _buf(A, lda), lda, _buf(B, ldb), ldb,
                                beta, _buf(C, ldc, 7.0), ldc, dtype)
@@ -207,7 +213,8 @@ def test_nan_propagates_when_read():
 
 # ---------------------------------------------------------------- library routine
 
-@pytest.mark.parametrize("w", [wl.F32_SQUARE[0], wl.RAGGED_F32, wl.RAGGED_F16], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.F32_SQUARE[0], wl.RAGGED_F32, wl.RAGGED_F16, wl.RAGGED_F16F32],
+                         ids=lambda w: w.name)
 def test_against_numpy_float64_matmul(w):
     """numpy's float64 matmul (dgemm) agrees with the oracle within the double
     summation error of either side."""
@@ -220,6 +227,25 @@ def test_against_numpy_float64_matmul(w):
     mag = abs(w.alpha) * (np.abs(a) @ np.abs(b)) + abs(w.beta) * np.abs(c)
     assert np.all(np.abs(R - ref) <= 2 * (w.K + 3) * EPS53 * mag)
     np.testing.assert_allclose(G, np.abs(a) @ np.abs(b), rtol=2 * w.K * EPS53, atol=0)
+
+
+def test_mixed_path_reads_fp32_C_and_half_inputs():
+    """fp16 inputs with an fp32 C: the result is the fp32 oracle on the
+    inputs widened to fp32 (exact) with the same fp32 C, bit for bit; C values
+    below fp16's resolution change it."""
+    rng = np.random.default_rng(19)
+    M, N, K = 17, 23, 31
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float16)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float16)
+    C = (rng.uniform(-1, 1, (M, N)) + 2.0 ** -20).astype(np.float32)
+    Rm, Gm = oracle.gemm(M, N, K, -0.5, _buf(A, K), K, _buf(B, N), N, 1.25, _buf(C, N), N, "f16f32")
+    R32, G32 = oracle.gemm(M, N, K, -0.5, _buf(A.astype(np.float32), K), K,
+                           _buf(B.astype(np.float32), N), N, 1.25, _buf(C, N), N, "f32")
+    np.testing.assert_array_equal(Rm, R32)
+    np.testing.assert_array_equal(Gm, G32)
+    Rh, _ = oracle.gemm(M, N, K, -0.5, _buf(A, K), K, _buf(B, N), N, 1.25,
+                        _buf(C.astype(np.float16), N), N, "f16")
+    assert not np.array_equal(Rm, Rh)
 
 
 def test_f16_path_equals_f32_path_on_same_values():
@@ -238,14 +264,14 @@ def test_f16_path_equals_f32_path_on_same_values():
     np.testing.assert_array_equal(G16, G32)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "f16f32"])
 def test_sampled_elements_small(dtype):
     rng = np.random.default_rng(4)
     M, N, K, lda, ldb, ldc = 23, 31, 45, 47, 36, 33
-    t = np.float32 if dtype == "f32" else np.float16
-    A = _buf(rng.standard_normal((M, K)).astype(t), lda)
-    B = _buf(rng.standard_normal((K, N)).astype(t), ldb)
-    C = _buf(rng.standard_normal((M, N)).astype(t), ldc, 5.0)
+    tin, tc = (_NP[x] for x in wl.operand_types(dtype))
+    A = _buf(rng.standard_normal((M, K)).astype(tin), lda)
+    B = _buf(rng.standard_normal((K, N)).astype(tin), ldb)
+    C = _buf(rng.standard_normal((M, N)).astype(tc), ldc, 5.0)
     for alpha, beta in [(1.5, -0.75), (0.0, 2.0), (-1.0, 0.0)]:
         R, G = oracle.gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype)
         rows, cols = wl.sample_positions(M, N, 200, 3)

@@ -9,8 +9,9 @@ Workloads follow the shapes the pages time: square N x N fp32 products from
 seeded random matrices with C zeroed before each run ("From 306 ms to 86 ms",
 section on how each kernel was timed), the square fp32 size sweep
 1024..12800 in steps of 128 ("Advanced Matrix Multiplication on NVIDIA GPUs"
-summary, benchmarking section), and an fp16-in / fp16-out GEMM standing in
-for the LeetGPU problem whose shape the "LeetGPU GEMM T4" page does not give.
+summary, benchmarking section), an fp16-in / fp16-out GEMM standing in for
+the LeetGPU problem whose shape the "LeetGPU GEMM T4" page does not give, and
+fp16 inputs with an fp32 C (the tensor-core WMMA page's output type).
 A ragged case with padded, unaligned leading dimensions exercises the scalar
 load path and all three tails (the same summary's layout section: leading
 dimensions may exceed the column count, and 128-bit loads need ld % 4 == 0).
@@ -31,7 +32,7 @@ C_PAD_SENTINEL = 1234.0   # exactly representable in fp16 and fp32
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str              # "f32" or "f16" (inputs and output)
+    dtype: str              # "f32" or "f16" (inputs and output), "f16f32" (fp16 in, fp32 C)
     M: int
     N: int
     K: int
@@ -66,6 +67,12 @@ RAGGED_F32 = Workload("ragged_f32", "f32", 1000, 3000, 517, 530, 3005, 3003, 1.5
                       "normal", "normal", (4, 5, 6), "lda=K+13, ldb=N+5, ldc=N+3")
 RAGGED_F16 = Workload("ragged_f16", "f16", 1000, 3000, 517, 530, 3005, 3003, 1.5, -0.75,
                       "normal", "normal", (4, 5, 6), "lda=K+13, ldb=N+5, ldc=N+3")
+# fp16 inputs with an fp32 C and result (the tensor-core WMMA page writes float
+# accumulators from half inputs): the ragged case and the 4096^3 square.
+RAGGED_F16F32 = Workload("ragged_f16f32", "f16f32", 1000, 3000, 517, 530, 3005, 3003, 1.5, -0.75,
+                         "normal", "normal", (4, 5, 6), "fp16 A, B; fp32 C; lda=K+13, ldb=N+5, ldc=N+3")
+F16F32_4096 = Workload("f16f32_4096_beta0.5", "f16f32", 4096, 4096, 4096, 4096, 4096, 4096, 1.0, 0.5,
+                       "uniform", "uniform", (3, 4, 5), "fp16 A, B; fp32 C and result")
 
 
 def sweep_sizes():
@@ -78,7 +85,12 @@ def sweep(n):
                   name="f32_sweep_%d" % n)
 
 
-ALL = [F32_256] + F32_SQUARE + [F16_4096, RAGGED_F32, RAGGED_F16]
+ALL = [F32_256] + F32_SQUARE + [F16_4096, RAGGED_F32, RAGGED_F16, RAGGED_F16F32, F16F32_4096]
+
+
+def operand_types(dtype):
+    """Storage types (A and B, C) of a workload type."""
+    return {"f32": ("f32", "f32"), "f16": ("f16", "f16"), "f16f32": ("f16", "f32")}[dtype]
 
 
 def _np_dtype(dtype):
@@ -114,9 +126,10 @@ def pad(mat, ld, fill):
 def make(w, pad_ab=float("nan"), pad_c=C_PAD_SENTINEL):
     """Host buffers (A, B, C) for workload w, each 1-D and padded to its ld."""
     sa, sb, sc = w.seeds
-    A = pad(draw(w.M, w.K, w.dist_ab, sa, w.dtype), w.lda, pad_ab)
-    B = pad(draw(w.K, w.N, w.dist_ab, sb, w.dtype), w.ldb, pad_ab)
-    C = pad(draw(w.M, w.N, w.dist_c, sc, w.dtype), w.ldc, pad_c)
+    tin, tc = operand_types(w.dtype)
+    A = pad(draw(w.M, w.K, w.dist_ab, sa, tin), w.lda, pad_ab)
+    B = pad(draw(w.K, w.N, w.dist_ab, sb, tin), w.ldb, pad_ab)
+    C = pad(draw(w.M, w.N, w.dist_c, sc, tc), w.ldc, pad_c)
     return A, B, C
 
 
