@@ -17,6 +17,8 @@ Also reported on the same line:
     section -- floor(1000*exp((1024-n)/3100)) replays, cache flushed before
     each (outside the timed interval), mean of the second half;
   * fp16: the same for gemm_f16 on the fp16 4096^3 GEMM with beta = 0.5;
+  * fp16_out_fp32: gemm_f16f32 (fp16 A and B, fp32 C and result) on the same
+    shape with beta = 0.5 (launch timing only);
   * power (per precision): average socket power and graphics clock over a
     few seconds of back-to-back calls, read from the SMU through amdsmi, the
     energy per GEMM and GFLOP/J, and the matrix peak scaled to the measured
@@ -158,6 +160,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
+    ap.add_argument("--no-f16f32", action="store_true")
     ap.add_argument("--no-p4", action="store_true")
     ap.add_argument("--no-power", action="store_true",
                     help="skip the power / energy windows")
@@ -170,7 +173,7 @@ def parse_args():
                          "with cache flush; one JSON row per size")
     ap.add_argument("--sweep-sizes", default=None,
                     help="comma-separated sizes for --sweep (default 1024..12800 step 128)")
-    ap.add_argument("--only", choices=["f32", "f16", "copy"], default=None,
+    ap.add_argument("--only", choices=["f32", "f16", "f16f32", "copy"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
                          "device copy of known size to calibrate HBM counters")
     return ap.parse_args()
@@ -273,6 +276,11 @@ def main():
                              False)
         print(json.dumps({"only": "f16", **f16_res}), flush=True)
         return
+    if args.only == "f16f32":
+        res, _ = measure(dg.gemm_f16f32, wl.F16F32_4096, PEAK_F16, "f16f32", args.steps,
+                         args.warmup, False)
+        print(json.dumps({"only": "f16f32", **res}), flush=True)
+        return
     w32 = wl.F32_4096
     main_res, host32 = measure(dg.gemm_f32, w32, PEAK_F32, "f32", args.steps, args.warmup,
                                not args.no_p4 and args.only is None,
@@ -288,6 +296,14 @@ def main():
                              not args.no_p4, not args.no_power)
         f16_res = {"workload": "fp16 in/out, fp32 accumulation, M=N=K=4096, A,B,C ~ U[-1,1], "
                                "alpha=1, beta=0.5", "unit": "TFLOP/s", **f16_res}
+
+    mixed_res = None
+    if not args.no_f16f32:
+        mixed_res, _ = measure(dg.gemm_f16f32, wl.F16F32_4096, PEAK_F16, "f16f32", args.steps,
+                               args.warmup, False)
+        mixed_res = {"workload": "fp16 A and B, fp32 C and result, fp32 accumulation, "
+                                 "M=N=K=4096, A,B,C ~ U[-1,1], alpha=1, beta=0.5",
+                     "unit": "TFLOP/s", **mixed_res}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -315,6 +331,7 @@ def main():
         "p4_protocol": main_res.get("p4_protocol"),
         "power": main_res.get("power"),
         "fp16": f16_res,
+        "fp16_out_fp32": mixed_res,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -1,5 +1,6 @@
-"""MI355X (gfx950) GEMM library: row-major C := alpha*A*B + beta*C in fp32 and
-in fp16 with fp32 accumulation, hand-written HIP kernels behind a C ABI
+"""MI355X (gfx950) GEMM library: row-major C := alpha*A*B + beta*C in fp32, in
+fp16 with fp32 accumulation, and with fp16 inputs and an fp32 C; hand-written
+HIP kernels behind a C ABI
 (include/gemm.h, libgemm.so).
 
 The binding is loaded on first use of one of its names, so that host-only
@@ -7,7 +8,7 @@ helpers of this package (the build script, the measurement model) import
 without the library; using the GEMM entry points without a built library
 raises ImportError.
 """
-_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe",
+_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_status_string", "gemm_describe",
                   "gemm_set_load_mode", "gemm_set_tile_config", "gemm", "GemmError", "LIB_PATH",
                   "EXPORTS")
 

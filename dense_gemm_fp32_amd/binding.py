@@ -27,6 +27,8 @@ _lib.gemm_f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f32.restype = _I
 _lib.gemm_f16.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16.restype = _I
+_lib.gemm_f16f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
+_lib.gemm_f16f32.restype = _I
 _lib.gemm_status_string.argtypes = [_I]
 _lib.gemm_status_string.restype = ctypes.c_char_p
 _lib.gemm_describe.argtypes = [_I, _I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, ctypes.c_char_p, _I]
@@ -36,7 +38,7 @@ _lib.gemm_set_load_mode.restype = _I
 _lib.gemm_set_tile_config.argtypes = [_I]
 _lib.gemm_set_tile_config.restype = _I
 
-EXPORTS = ("gemm_f32", "gemm_f16", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
            "gemm_set_tile_config")
 
 
@@ -77,6 +79,12 @@ def gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
                          _stream(stream))
 
 
+def gemm_f16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """fp16 A and B, fp32 C and result, fp32 accumulation (see include/gemm.h)."""
+    return _lib.gemm_f16f32(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                            _stream(stream))
+
+
 def gemm_status_string(status):
     return _lib.gemm_status_string(int(status)).decode()
 
@@ -84,7 +92,7 @@ def gemm_status_string(status):
 def gemm_describe(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
     """(status, text) describing the variant chosen for these arguments."""
     buf = ctypes.create_string_buffer(256)
-    dt = {"f32": 0, "f16": 1}.get(dtype, dtype)
+    dt = {"f32": 0, "f16": 1, "f16f32": 2}.get(dtype, dtype)
     rc = _lib.gemm_describe(dt, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                             buf, len(buf))
     return rc, buf.value.decode()
@@ -106,7 +114,8 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
 
     Rows may be padded (stride(0) >= number of columns) but each row must be
     contiguous (stride(1) == 1).  float32 tensors go to gemm_f32, float16 to
-    gemm_f16.  Uses the current torch stream unless one is given."""
+    gemm_f16, float16 A and B with a float32 C to gemm_f16f32.  Uses the
+    current torch stream unless one is given."""
     for name, t in (("A", A), ("B", B), ("C", C)):
         if t.dim() != 2 or t.stride(1) != 1:
             raise ValueError("%s must be 2-D with stride(1) == 1" % name)
@@ -115,10 +124,13 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
                                                              tuple(C.shape)))
-    if not (A.dtype == B.dtype == C.dtype):
-        raise ValueError("A, B and C must share a dtype")
+    if A.dtype != B.dtype:
+        raise ValueError("A and B must share a dtype")
     if A.dtype not in (torch.float32, torch.float16):
         raise ValueError("unsupported dtype %s" % A.dtype)
+    mixed = A.dtype == torch.float16 and C.dtype == torch.float32
+    if C.dtype != A.dtype and not mixed:
+        raise ValueError("C must have A's dtype, or float32 with float16 A and B")
     if not (A.is_cuda and B.is_cuda and C.is_cuda):
         raise ValueError("A, B and C must be GPU tensors")
     if stream is None:
@@ -126,6 +138,8 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
     lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(C.stride(0), 1)
     if A.dtype == torch.float32:
         rc = gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    elif mixed:
+        rc = gemm_f16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     else:
         rc = gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     if rc != 0:

@@ -45,8 +45,9 @@ Route route(int M, int N, int K, float alpha, float beta) {
 }
 
 dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
-                      int ldb, float beta, void *C, int ldc, void *stream) {
+                      int ldb, float beta, void *C, int ldc, void *stream, bool out32 = false) {
   dgemm::Call c;
+  c.out32 = out32;
   c.M = M;
   c.N = N;
   c.K = K;
@@ -104,6 +105,24 @@ int gemm_f16(int M, int N, int K, float alpha, const gemm_half_t *A, int lda, co
   return e == hipSuccess ? GEMM_SUCCESS : (int)e;
 }
 
+int gemm_f16f32(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
+      break;
+    case Route::kGemm:
+      e = dgemm::launch_f16(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, true));
+      break;
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
 const char *gemm_status_string(int status) {
   switch (status) {
     case 0: return "success";
@@ -128,20 +147,22 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
   char text[256];
   if (rc != 0) {
     snprintf(text, sizeof text, "invalid: %s", gemm_status_string(rc));
-  } else if (dtype != 0 && dtype != 1) {
+  } else if (dtype < 0 || dtype > 2) {
     snprintf(text, sizeof text, "invalid: unknown dtype %d", dtype);
   } else {
+    static const char *const kNames[3] = {"f32", "f16", "f16f32"};
+    const char *dn = kNames[dtype];
     switch (route(M, N, K, alpha, beta)) {
       case Route::kNothing:
-        snprintf(text, sizeof text, "%s no-op", dtype ? "f16" : "f32");
+        snprintf(text, sizeof text, "%s no-op", dn);
         break;
       case Route::kScale:
-        snprintf(text, sizeof text, "%s scale C := beta*C%s", dtype ? "f16" : "f32",
+        snprintf(text, sizeof text, "%s scale C := beta*C%s", dn,
                  beta == 0.0f ? " (zero fill, C not read)" : "");
         break;
       case Route::kGemm: {
         dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, const_cast<void *>(C), ldc,
-                                  nullptr);
+                                  nullptr, dtype == 2);
         dgemm::Plan p = dtype ? dgemm::plan_f16(c) : dgemm::plan_f32(c);
         snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s",
                  p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",

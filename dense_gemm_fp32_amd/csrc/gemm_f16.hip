@@ -432,6 +432,73 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
   }
 }
 
+// The same epilogue for an fp32 C and result: alpha*acc + beta*C in fp32,
+// written as 16-byte stores (4 adjacent floats per lane, 512 contiguous
+// bytes per 32 lanes).  C is loaded one block row at a time, before that
+// row's accumulators are staged, so the load latency overlaps the staging
+// without holding every row's C in registers at once.
+template <class T, bool VEC_C, bool CHECK>
+__device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int c0, char *lds,
+                                               const f32x16 (&acc)[T::FM][T::FN]) {
+  float *C = static_cast<float *>(p.C);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 32, lh = lane / 32;
+  float *stage = reinterpret_cast<float *>(lds + wave * T::EP_BYTES);
+  const float alpha = p.alpha, beta = p.beta;
+  constexpr int LPR = T::WTN / 4;
+  constexpr int ROWS_PER_PASS = kWave / LPR;
+  constexpr int PASSES = 32 / ROWS_PER_PASS;
+  const int cl = 4 * (lane % LPR);
+  const int col = c0 + cl;
+  const bool cols_ok = !CHECK || col + 3 < p.N;
+#pragma unroll
+  for (int bi = 0; bi < T::FM; ++bi) {
+    f32x4 cpre[PASSES];
+    if (VEC_C && beta != 0.0f) {
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
+        cpre[pass] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!CHECK || (row < p.M && cols_ok))
+          cpre[pass] = *reinterpret_cast<const f32x4 *>(C + (size_t)row * (size_t)p.ldc + col);
+      }
+    }
+#pragma unroll
+    for (int bj = 0; bj < T::FN; ++bj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[bi][bj][r];
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int rl = pass * ROWS_PER_PASS + lane / LPR;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(&stage[rl * T::EP_STRIDE + cl]);
+      const int row = r0 + 32 * bi + rl;
+      if (CHECK && row >= p.M) continue;
+      float *dst = C + (size_t)row * (size_t)p.ldc + col;
+      if (VEC_C && cols_ok) {
+        f32x4 o;
+        if (beta != 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(beta, cpre[pass][e], alpha * v[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
+        }
+        *reinterpret_cast<f32x4 *>(dst) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (CHECK && col + e >= p.N) continue;
+          float o = alpha * v[e];
+          if (beta != 0.0f) o = __builtin_fmaf(beta, dst[e], o);
+          dst[e] = o;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- main loops
 
 template <class T>
@@ -558,7 +625,8 @@ __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int
   }
 }
 
-template <class T, bool VA, bool VB, bool VC>
+// OUT32: C and the result are fp32 (fp16 inputs); otherwise fp16.
+template <class T, bool VA, bool VB, bool VC, bool OUT32>
 __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   int tm, tn;
@@ -580,8 +648,13 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();   // every wave is done with the pipeline slots
   const bool edge = n_edge || (m0 + T::BM > p.M);
-  if (edge) epilogue<T, VC, true>(p, m0 + wm0, n0 + wn0, lds, acc);
-  else epilogue<T, VC, false>(p, m0 + wm0, n0 + wn0, lds, acc);
+  if constexpr (OUT32) {
+    if (edge) epilogue_out32<T, VC, true>(p, m0 + wm0, n0 + wn0, lds, acc);
+    else epilogue_out32<T, VC, false>(p, m0 + wm0, n0 + wn0, lds, acc);
+  } else {
+    if (edge) epilogue<T, VC, true>(p, m0 + wm0, n0 + wn0, lds, acc);
+    else epilogue<T, VC, false>(p, m0 + wm0, n0 + wn0, lds, acc);
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -607,7 +680,9 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.threads = T::NT;
   const bool va = !c.force_scalar && vec_ok(c.A, c.lda, 8);
   const bool vb = !c.force_scalar && vec_ok(c.B, c.ldb, 8);
-  const bool vc = !c.force_scalar && vec_ok(c.C, c.ldc, 4);
+  // C: 4 adjacent elements per access (8 bytes of fp16 or 16 of fp32).
+  const bool vc = !c.force_scalar && (c.ldc % 4) == 0 &&
+                  aligned_to(c.C, (uintptr_t)(c.out32 ? 16 : 8));
   pl.vec_a = va ? 8 : 1;
   pl.vec_b = vb ? 8 : 1;
   pl.vec_c = vc ? 4 : 1;
@@ -617,7 +692,7 @@ static Plan make_plan(const Call &c, const char *name) {
   return pl;
 }
 
-template <class T, bool VA, bool VB, bool VC>
+template <class T, bool VA, bool VB, bool VC, bool OUT32>
 static hipError_t launch_variant(const Call &c, const Plan &pl) {
   GemmParams p;
   p.A = c.A;
@@ -634,26 +709,31 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = T::GROUP_M;
-  hipLaunchKernelGGL((hgemm_mfma<T, VA, VB, VC>), dim3((unsigned)pl.blocks), dim3(T::NT), 0,
+  hipLaunchKernelGGL((hgemm_mfma<T, VA, VB, VC, OUT32>), dim3((unsigned)pl.blocks), dim3(T::NT), 0,
                      c.stream, p);
   return hipGetLastError();
+}
+
+template <class T, bool OUT32>
+static hipError_t dispatch_out(const Call &c, const Plan &pl) {
+  const int key = (pl.vec_a > 1 ? 4 : 0) | (pl.vec_b > 1 ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
+  switch (key) {
+    case 0: return launch_variant<T, false, false, false, OUT32>(c, pl);
+    case 1: return launch_variant<T, false, false, true, OUT32>(c, pl);
+    case 2: return launch_variant<T, false, true, false, OUT32>(c, pl);
+    case 3: return launch_variant<T, false, true, true, OUT32>(c, pl);
+    case 4: return launch_variant<T, true, false, false, OUT32>(c, pl);
+    case 5: return launch_variant<T, true, false, true, OUT32>(c, pl);
+    case 6: return launch_variant<T, true, true, false, OUT32>(c, pl);
+    default: return launch_variant<T, true, true, true, OUT32>(c, pl);
+  }
 }
 
 template <class T>
 static hipError_t dispatch(const Call &c) {
   const Plan pl = make_plan<T>(c, "");
   if (pl.blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int key = (pl.vec_a > 1 ? 4 : 0) | (pl.vec_b > 1 ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
-  switch (key) {
-    case 0: return launch_variant<T, false, false, false>(c, pl);
-    case 1: return launch_variant<T, false, false, true>(c, pl);
-    case 2: return launch_variant<T, false, true, false>(c, pl);
-    case 3: return launch_variant<T, false, true, true>(c, pl);
-    case 4: return launch_variant<T, true, false, false>(c, pl);
-    case 5: return launch_variant<T, true, false, true>(c, pl);
-    case 6: return launch_variant<T, true, true, false>(c, pl);
-    default: return launch_variant<T, true, true, true>(c, pl);
-  }
+  return c.out32 ? dispatch_out<T, true>(c, pl) : dispatch_out<T, false>(c, pl);
 }
 
 template <class T>
@@ -677,9 +757,15 @@ static F16Cfg choose_f16(const Call &c) {
 
 Plan plan_f16(const Call &c) {
   switch (choose_f16(c)) {
-    case F16Cfg::kBig: return make_plan<F16Big>(c, "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
-    case F16Cfg::kMid: return make_plan<F16Mid>(c, "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
-    default: return make_plan<F16Small>(c, "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
+    case F16Cfg::kBig:
+      return make_plan<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
+                                          : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
+    case F16Cfg::kMid:
+      return make_plan<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
+                                          : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
+    default:
+      return make_plan<F16Small>(c, c.out32 ? "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots out f32"
+                                            : "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
   }
 }
 

@@ -18,6 +18,7 @@ struct Call {
   int ldb;
   void *C;
   int ldc;
+  bool out32;            // fp16 inputs: C and the result are fp32 (else fp16)
   bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
   int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
                          // 5 = medium with the loads of a step issued together

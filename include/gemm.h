@@ -1,7 +1,7 @@
 /*
  * gemm.h -- C ABI of the MI355X (gfx950) dense GEMM library, libgemm.so.
  *
- * Operation (both entry points):
+ * Operation (every entry point):
  *
  *     C := alpha * A * B + beta * C
  *
@@ -14,6 +14,9 @@
  * gemm_f16 is the fp16-in / fp16-out variant with fp32 accumulation that the
  * "LeetGPU GEMM T4" page solves: products are summed in fp32, alpha*sum +
  * beta*C is formed in fp32 and rounded once to half, round-to-nearest-even.
+ * gemm_f16f32 takes fp16 A and B with an fp32 C and result: the float
+ * accumulators of the "Tensorcore_wmma_vs_fp32 test code" page, whose WMMA
+ * kernel multiplies half fragments into float accumulators and stores those.
  *
  * Semantics:
  *   - beta == 0: C is write-only; its previous contents (NaN included) are
@@ -102,6 +105,20 @@ int gemm_f16(int M, int N, int K, float alpha,
              float beta, gemm_half_t *C, int ldc,
              void *stream);
 
+/*
+ * fp16 inputs, fp32 C and result: A and B hold binary16 values (as for
+ * gemm_f16), C holds binary32.  Products are accumulated in fp32 on the
+ * matrix cores (v_mfma_f32_32x32x16_f16); alpha*acc + beta*C is formed in fp32
+ * and stored as binary32 (no rounding to half).  Arguments and return values
+ * as for gemm_f32, with ldc counting floats.  The degenerate paths (alpha == 0
+ * or K == 0) scale the fp32 C as gemm_f32 does.
+ */
+int gemm_f16f32(int M, int N, int K, float alpha,
+                const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb,
+                float beta, float *C, int ldc,
+                void *stream);
+
 /* Static, human-readable text for a status code returned above (never NULL). */
 const char *gemm_status_string(int status);
 
@@ -109,7 +126,8 @@ const char *gemm_status_string(int status);
  * Describe, without launching anything, the kernel variant the library picks
  * for a call with these arguments: writes a NUL-terminated text such as
  * "f32 mfma 128x128x32 loads A:vec4 B:vec4 C:vec2" into buf (at most len
- * bytes, truncated if needed).  dtype: 0 = fp32, 1 = fp16.  Pointers are only
+ * bytes, truncated if needed).  dtype: 0 = fp32, 1 = fp16, 2 = fp16 inputs
+ * with an fp32 C (gemm_f16f32).  Pointers are only
  * inspected for alignment.  Returns the status gemm_f32 / gemm_f16 would
  * return for the argument checks (0 or -i); no HIP call is made.
  */

@@ -18,11 +18,21 @@ def note(msg):
 
 
 def _np_t(dtype):
+    """numpy storage type of C and of the result ("f16f32": fp32 C)."""
+    return np.float16 if dtype == "f16" else np.float32
+
+
+def np_in(dtype):
+    """numpy storage type of A and B."""
     return np.float32 if dtype == "f32" else np.float16
 
 
+def np_out(dtype):
+    return _np_t(dtype)
+
+
 def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
-    """Call gemm_f32 / gemm_f16 on device copies of the host buffers.
+    """Call gemm_f32 / gemm_f16 / gemm_f16f32 on device copies of the host buffers.
 
     Returns (status, C buffer after the call as a host array).  C's buffer
     is followed by a guard region of sentinels that must be left intact."""
@@ -41,7 +51,7 @@ def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
     dA, dB = up(A), up(B)
     cbuf = np.concatenate([np.asarray(C, t).reshape(-1), np.full(GUARD, wl.C_PAD_SENTINEL, t)])
     dC = up(cbuf)
-    fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_f16
+    fn = {"f32": dg.gemm_f32, "f16": dg.gemm_f16, "f16f32": dg.gemm_f16f32}[dtype]
     stream = torch.cuda.current_stream(dev)
     rc = fn(M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc, stream)
     torch.cuda.synchronize(dev)
@@ -59,7 +69,7 @@ def check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out, label=""):
     |err|/tol."""
     R, G = oracle.gemm(M, N, K, alpha, A, lda, B, ldb, beta, C if beta != 0 else None, ldc, dtype)
     Cv = wl.view(np.asarray(C), M, N, ldc).astype(np.float64) if (beta != 0 and M and N) else 0.0
-    tol = oracle.tolerance(G, np.abs(Cv), alpha, beta, K, R, dtype)
+    tol = oracle.tolerance(G, np.abs(Cv), alpha, beta, K, R, oracle.out_type(dtype))
     gpu = wl.view(out, M, N, ldc)
     ok, worst, idx = oracle.compare(gpu, R, tol)
     if not ok:
@@ -85,7 +95,7 @@ def assert_pads_unchanged(out, C, M, N, ldc, dtype):
 
 def exact_expected(dtype, R):
     """The correctly rounded result, for cases where every partial sum is exact."""
-    if dtype == "f32":
+    if dtype != "f16":
         return oracle.round_f32(R)
     return oracle.round_f16(R).view(np.float16)
 
@@ -107,15 +117,15 @@ def check_sampled(dtype, w, A, B, C, out, nrows=48, seed=0):
     R, G = oracle.gemm(len(rows), N, K, w.alpha, Asub.reshape(-1), K, B, w.ldb, w.beta,
                        Csub.reshape(-1) if w.beta != 0 else None, N, dtype)
     tol = oracle.tolerance(G, np.abs(Csub.astype(np.float64)) if w.beta != 0 else 0.0,
-                           w.alpha, w.beta, K, R, dtype)
+                           w.alpha, w.beta, K, R, oracle.out_type(dtype))
     gpu_full = wl.view(out, M, N, w.ldc)
     ok, worst, idx = oracle.compare(np.ascontiguousarray(gpu_full[rows]), R, tol)
     assert ok, "%s sampled rows: worst %.3g at %s" % (w.name, worst, idx)
     # whole-matrix checks
     g64 = oracle.half_to_double(np.ascontiguousarray(gpu_full)) if dtype == "f16" else gpu_full.astype(np.float64)
     assert np.all(np.isfinite(g64))
-    u_out = oracle.U32 if dtype == "f32" else oracle.U16
-    eta = oracle.ETA32 if dtype == "f32" else oracle.ETA16
+    u_out = oracle.U16 if dtype == "f16" else oracle.U32
+    eta = oracle.ETA16 if dtype == "f16" else oracle.ETA32
     exp, mag = oracle.checksum(M, N, K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, dtype)
     s = g64.sum()
     bound = (1 + u_out) * 4 * K * oracle.U32 * mag + u_out * np.abs(g64).sum() + M * N * eta

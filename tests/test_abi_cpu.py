@@ -69,14 +69,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_f16f32"])
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_argument_checks_and_quick_returns(fn, case):
     import dense_gemm_fp32_amd as dg
     expected, *args = case
     assert getattr(dg, fn)(*args, None) == expected
     # gemm_describe applies the same checks
-    rc, text = dg.gemm_describe("f32" if fn == "gemm_f32" else "f16", *args)
+    rc, text = dg.gemm_describe({"gemm_f32": "f32", "gemm_f16": "f16", "gemm_f16f32": "f16f32"}[fn],
+                                *args)
     assert rc == expected
     if expected < 0:
         assert text.startswith("invalid")
@@ -106,6 +107,12 @@ def test_describe_picks_vector_or_scalar_loads():
     # misaligned base pointer: scalar for that operand only
     rc, t = dg.gemm_describe("f32", 256, 256, 256, 1.0, FAKE + 4, 256, FAKE, 256, 0.0, FAKE, 256)
     assert "A:scalar1" in t and "B:vec4" in t
+    # fp16 inputs with an fp32 C: 16-byte C accesses need a 16-byte aligned base
+    rc, t = dg.gemm_describe("f16f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.5, FAKE, 4096)
+    assert rc == 0 and "out f32" in t and "C:vec4" in t
+    rc, t = dg.gemm_describe("f16f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.5, FAKE + 8, 4096)
+    assert "C:scalar1" in t
+    assert dg.gemm_describe(3, 8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8)[1].startswith("invalid")
     # degenerate routes
     assert "scale" in dg.gemm_describe("f32", 8, 8, 0, 1.0, None, 1, None, 8, 2.0, FAKE, 8)[1]
     assert "zero fill" in dg.gemm_describe("f32", 8, 8, 8, 0.0, None, 8, None, 8, 0.0, FAKE, 8)[1]

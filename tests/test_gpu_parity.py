@@ -9,15 +9,22 @@ import pytest
 
 import oracle
 import workloads as wl
-from gemm_harness import bits, check, check_sampled, exact_expected, run
+from gemm_harness import bits, check, check_sampled, exact_expected, np_in, np_out, run
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = ["f32", "f16"]
+# "f16f32": fp16 A and B with an fp32 C and result (gemm_f16f32).
+DTYPES = ["f32", "f16", "f16f32"]
 
 
 def _t(dtype):
-    return np.float32 if dtype == "f32" else np.float16
+    """Storage type of A and B."""
+    return np_in(dtype)
+
+
+def _tc(dtype):
+    """Storage type of C and of the result."""
+    return np_out(dtype)
 
 
 def _w_run_check(w, label=None):
@@ -39,7 +46,7 @@ def test_f32_square_full_oracle(n):
     _w_run_check(wl.square(n, seeds=(2, 3, 4)))
 
 
-@pytest.mark.parametrize("w", [wl.RAGGED_F32, wl.RAGGED_F16], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.RAGGED_F32, wl.RAGGED_F16, wl.RAGGED_F16F32], ids=lambda w: w.name)
 def test_ragged_padded_unaligned(w):
     """1000 x 3000 x 517, lda=530, ldb=3005, ldc=3003: unaligned leading
     dimensions (scalar loads), all three tails, NaN in the pads of A and B,
@@ -57,6 +64,14 @@ def test_f32_4096_sampled():
 
 def test_f16_4096_beta_half_sampled():
     w = wl.F16_4096
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out)
+
+
+def test_f16f32_4096_beta_half_sampled():
+    w = wl.F16F32_4096
     A, B, C = wl.make(w)
     rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
     assert rc == 0
@@ -92,7 +107,7 @@ def test_tails_brute_force(dtype):
         beta = [0.0, 1.0, -0.5][idx % 3]
         A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
         B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
-        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
         rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, "tail")
         assert rc == 0
         check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out,
@@ -152,6 +167,23 @@ def test_f16_small_integers_exact(beta):
     assert np.array_equal(bits(out, "f16"), oracle.round_f16(R).reshape(-1))
 
 
+@pytest.mark.parametrize("beta", [0.0, 1.0, -0.75])
+def test_f16f32_small_integers_and_fine_C_exact(beta):
+    """fp16 A, B in {-8..8}, K = 1000, fp32 C = integers plus multiples of
+    2^-10: every partial sum and the result are exact in fp32 (not in fp16), so
+    the output must equal the correctly rounded value bit for bit -- an output
+    rounded through half, or a C read as half, cannot."""
+    M, N, K = 260, 300, 1000
+    A = wl.small_ints(M, K, -8, 8, 21, "f16").reshape(-1)
+    B = wl.small_ints(K, N, -8, 8, 22, "f16").reshape(-1)
+    C = (wl.small_ints(M, N, -64, 64, 23, "f32")
+         + wl.small_ints(M, N, -512, 512, 24, "f32") / 1024.0).astype(np.float32).reshape(-1)
+    rc, out = run("f16f32", M, N, K, 1.0, A, K, B, N, beta, C, N, "f16f32ints")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, 1.0, A, K, B, N, beta, C, N, "f16f32")
+    assert np.array_equal(bits(out, "f16f32"), bits(exact_expected("f16f32", R).reshape(-1), "f16f32"))
+
+
 def test_f16_output_rounding_is_nearest_even():
     """K = 2, A = [1, 3*2^-11], B = [1, 1]^T: the fp32 accumulator is exactly
     1 + 3*2^-11, halfway between halves 1+2^-10 and 1+2^-9; ties-to-even gives
@@ -178,40 +210,40 @@ def test_f16_output_rounding_is_nearest_even():
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_identity_and_permutation_bitwise(dtype):
-    t = _t(dtype)
+    t, tc = _t(dtype), _tc(dtype)
     rng = np.random.default_rng(31)
     M, N = 300, 200
     B = rng.uniform(-1, 1, (M, N)).astype(t)
     eye = np.eye(M, dtype=t)
-    C0 = np.zeros(M * N, t)
+    C0 = np.zeros(M * N, tc)
     rc, out = run(dtype, M, N, M, 1.0, eye.reshape(-1), M, B.reshape(-1), N, 0.0, C0, N, "A=I")
-    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B.reshape(-1), dtype))
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B.reshape(-1).astype(tc), dtype))
     A = rng.uniform(-1, 1, (M, N)).astype(t)
     eyeN = np.eye(N, dtype=t)
     rc, out = run(dtype, M, N, N, 1.0, A.reshape(-1), N, eyeN.reshape(-1), N, 0.0, C0, N, "B=I")
-    assert rc == 0 and np.array_equal(bits(out, dtype), bits(A.reshape(-1), dtype))
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(A.reshape(-1).astype(tc), dtype))
     p = rng.permutation(M)
     P = np.zeros((M, M), t)
     P[np.arange(M), p] = 1
     rc, out = run(dtype, M, N, M, 1.0, P.reshape(-1), M, B.reshape(-1), N, 0.0, C0, N, "A=P")
-    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B[p].reshape(-1), dtype))
+    assert rc == 0 and np.array_equal(bits(out, dtype), bits(B[p].reshape(-1).astype(tc), dtype))
 
 
 # ---------------------------------------------------------------- alpha / beta
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_alpha_zero_ignores_A_and_B(dtype):
-    t = _t(dtype)
+    t, tc = _t(dtype), _tc(dtype)
     M, N, K = 130, 70, 90
     A = np.full(M * K, np.nan, t)
     B = np.full(K * N, np.inf, t)
-    C = np.random.default_rng(1).uniform(-1, 1, M * N).astype(t)
+    C = np.random.default_rng(1).uniform(-1, 1, M * N).astype(tc)
     rc, out = run(dtype, M, N, K, 0.0, A, K, B, N, -0.5, C, N, "alpha0")
     assert rc == 0
-    expect = (np.float32(-0.5) * C.astype(np.float32)).astype(t)
+    expect = (np.float32(-0.5) * C.astype(np.float32)).astype(tc)
     assert np.array_equal(bits(out, dtype), bits(expect, dtype))
     # alpha = 0 and beta = 0: exact zeros, C (NaN here) not read
-    Cn = np.full(M * N, np.nan, t)
+    Cn = np.full(M * N, np.nan, tc)
     rc, out = run(dtype, M, N, K, 0.0, A, K, B, N, 0.0, Cn, N, "alpha0beta0")
     assert rc == 0 and np.all(out == 0)
     # alpha = 0, beta = 1: C unchanged bit for bit (nothing launched)
@@ -226,7 +258,7 @@ def test_beta_zero_ignores_C(dtype):
     rng = np.random.default_rng(2)
     A = rng.uniform(-1, 1, M * K).astype(t)
     B = rng.uniform(-1, 1, K * N).astype(t)
-    Cn = np.full(M * N, np.nan, t)
+    Cn = np.full(M * N, np.nan, _tc(dtype))
     rc, out = run(dtype, M, N, K, 1.0, A, K, B, N, 0.0, Cn, N, "beta0")
     assert rc == 0 and np.all(np.isfinite(out.astype(np.float64)))
     check(dtype, M, N, K, 1.0, A, K, B, N, 0.0, Cn, N, out, "beta0")
@@ -236,7 +268,7 @@ def test_beta_zero_ignores_C(dtype):
 def test_k_zero_scales_C(dtype):
     t = _t(dtype)
     M, N = 100, 300
-    C = np.random.default_rng(3).uniform(-1, 1, M * (N + 4)).astype(t)
+    C = np.random.default_rng(3).uniform(-1, 1, M * (N + 4)).astype(_tc(dtype))
     rc, out = run(dtype, M, N, 0, 1.0, None, 1, None, N, 2.0, C, N + 4, "k0")
     assert rc == 0
     check(dtype, M, N, 0, 1.0, None, 1, None, N, 2.0, C, N + 4, out, "k0")
@@ -255,7 +287,7 @@ def test_bitwise_deterministic_and_scalar_path_agrees(dtype):
     rng = np.random.default_rng(4)
     A = rng.standard_normal(M * K).astype(t)
     B = rng.standard_normal(K * N).astype(t)
-    C = rng.standard_normal(M * N).astype(t)
+    C = rng.standard_normal(M * N).astype(_tc(dtype))
     rc1, o1 = run(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, "det1")
     rc2, o2 = run(dtype, M, N, K, 1.5, A, K, B, N, -0.75, C, N, "det2")
     assert rc1 == rc2 == 0 and np.array_equal(bits(o1, dtype), bits(o2, dtype))
@@ -302,25 +334,26 @@ F16_PATH_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f16f32"])
 @pytest.mark.parametrize("shape", F16_PATH_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_f16_direct_path_edges_match_oracle_and_staged_path(shape):
+def test_f16_direct_path_edges_match_oracle_and_staged_path(shape, dtype):
     import dense_gemm_fp32_amd as dg
     M, N, K, lda, ldb, ldc = shape
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(np.float16), lda, np.nan)
     B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(np.float16), ldb, np.nan)
-    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(np.float16), ldc, wl.C_PAD_SENTINEL)
-    rc, out_direct = run("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 direct")
+    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
+    rc, out_direct = run(dtype, M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 direct")
     assert rc == 0
-    check("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, out_direct, "direct %s" % (shape,))
+    check(dtype, M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, out_direct, "direct %s" % (shape,))
     prev = dg.gemm_set_load_mode(1)
     try:
-        rc, out_staged = run("f16", M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 staged")
+        rc, out_staged = run(dtype, M, N, K, 1.25, A, lda, B, ldb, -0.5, C, ldc, "f16 staged")
     finally:
         dg.gemm_set_load_mode(prev)
     assert rc == 0
     # same LDS layout and summation order on both paths: identical bits
-    assert np.array_equal(bits(out_direct, "f16"), bits(out_staged, "f16"))
+    assert np.array_equal(bits(out_direct, dtype), bits(out_staged, dtype))
 
 
 def test_f16_nan_in_a_row_past_m_is_not_read():
@@ -370,7 +403,7 @@ def test_every_tile_configuration_matches_oracle(dtype, cfg):
         rng = np.random.default_rng(M + 3 * N + 7 * K + cfg)
         A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
         B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
-        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
         with tile_config(cfg):
             rc, out = run(dtype, M, N, K, 0.75, A, lda, B, ldb, 1.5, C, ldc, "cfg%d" % cfg)
         assert rc == 0
@@ -424,7 +457,7 @@ def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed
     lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
     A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
     B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
-    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(t), ldc, wl.C_PAD_SENTINEL)
+    C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
     with tile_config(cfg):
         rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, "hyp cfg%d" % cfg)
     assert rc == 0
