@@ -9,7 +9,7 @@ without the library; using the GEMM entry points without a built library
 raises ImportError.
 """
 _BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_status_string", "gemm_describe",
-                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm", "GemmError", "LIB_PATH",
+                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm", "GemmError", "LIB_PATH",
                   "EXPORTS")
 
 __all__ = list(_BINDING_NAMES)

@@ -37,9 +37,11 @@ _lib.gemm_set_load_mode.argtypes = [_I]
 _lib.gemm_set_load_mode.restype = _I
 _lib.gemm_set_tile_config.argtypes = [_I]
 _lib.gemm_set_tile_config.restype = _I
+_lib.gemm_set_split.argtypes = [_I]
+_lib.gemm_set_split.restype = _I
 
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
-           "gemm_set_tile_config")
+           "gemm_set_tile_config", "gemm_set_split")
 
 
 class GemmError(RuntimeError):
@@ -107,6 +109,12 @@ def gemm_set_tile_config(config):
     """0 = tile configuration by problem size (default); 1/2/3/4 = force the
     large/medium/small/tiny configuration (fp16 maps 4 to small)."""
     return _lib.gemm_set_tile_config(int(config))
+
+
+def gemm_set_split(mode):
+    """0 = split K by problem size (default), 1 = never, 2..64 = force that
+    many K chunks."""
+    return _lib.gemm_set_split(int(mode))
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):

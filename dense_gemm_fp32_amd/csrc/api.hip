@@ -17,6 +17,7 @@ namespace {
 
 std::atomic<int> g_load_mode{0};
 std::atomic<int> g_tile_config{0};
+std::atomic<int> g_split_mode{0};
 
 // Shared argument checks.  `elem_bytes` only matters for descriptions.
 int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
@@ -61,6 +62,10 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.ldc = ldc;
   c.force_scalar = g_load_mode.load(std::memory_order_relaxed) == 1;
   c.tile_config = g_tile_config.load(std::memory_order_relaxed);
+  c.split_mode = g_split_mode.load(std::memory_order_relaxed);
+  c.splits = 1;
+  c.k_chunk = 0;
+  c.split_stride = 0;
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -164,9 +169,11 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
         dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, const_cast<void *>(C), ldc,
                                   nullptr, dtype == 2);
         dgemm::Plan p = dtype ? dgemm::plan_f16(c) : dgemm::plan_f32(c);
-        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s",
+        char split[48] = "";
+        if (p.splits > 1) snprintf(split, sizeof split, " split-K %d", p.splits);
+        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s",
                  p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",
-                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads,
+                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split,
                  beta == 0.0f ? " beta0 (C not read)" : "");
         break;
       }
@@ -182,6 +189,11 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
 int gemm_set_load_mode(int mode) {
   if (mode != 0 && mode != 1) return -1;
   return g_load_mode.exchange(mode);
+}
+
+int gemm_set_split(int mode) {
+  if (mode < 0 || mode > 64) return -1;
+  return g_split_mode.exchange(mode);
 }
 
 int gemm_set_tile_config(int config) {

@@ -32,7 +32,28 @@ struct GemmParams {
   float alpha, beta;
   int tiles_m, tiles_n;   // ceil(M/BM), ceil(N/BN)
   int group_m;            // tile rows per L2 group
+  // Split K: `splits` > 1 divides K into chunks of k_chunk (a multiple of
+  // the tile's K step; the last chunk takes the rest).  Workgroup (tile,
+  // split s) multiplies A(:, chunk s) by B(chunk s, :) and writes the raw fp32
+  // sums to C + s*split_stride (a workspace, ldc its row pitch); the caller
+  // sets alpha = 1, beta = 0 for that pass and reduces the slabs afterwards.
+  int splits;
+  int k_chunk;
+  long long split_stride;  // elements between the slabs of consecutive splits
 };
+
+// Restrict the kernel arguments to split `s` of a split-K launch: K range
+// [s*k_chunk, min(K, (s+1)*k_chunk)) and that split's output slab.
+template <typename TIn, typename TOut>
+__device__ __forceinline__ void select_split(GemmParams &p, int s) {
+  if (p.splits <= 1) return;
+  const int kb = s * p.k_chunk;
+  const int left = p.K - kb;
+  p.K = left < p.k_chunk ? left : p.k_chunk;
+  p.A = static_cast<const TIn *>(p.A) + kb;
+  p.B = static_cast<const TIn *>(p.B) + (size_t)kb * (size_t)p.ldb;
+  p.C = static_cast<TOut *>(p.C) + (size_t)s * (size_t)p.split_stride;
+}
 
 // Map a linear workgroup id to a C tile (tm, tn).
 //
@@ -44,13 +65,21 @@ struct GemmParams {
 //    `group_m` tile rows before moving one tile column right, so the
 //    workgroups resident on one XCD at a time share A row panels and B column
 //    panels in that XCD's L2.
+//
+// With a split-K launch the grid holds `splits` copies of the tile order, one
+// per K chunk, after one another: the renumbered id gives the split (b / T for
+// T tiles) and the tile within it, so an XCD's range covers tiles of the same
+// K chunk, which share A and B panels.
 __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
-                                              int group_m, int &tm, int &tn) {
+                                              int group_m, int &tm, int &tn, int &split) {
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
   const int q = nblocks / kXcds;
   const int r = nblocks % kXcds;
-  const int b = xcd * q + (xcd < r ? xcd : r) + local;
+  int b = xcd * q + (xcd < r ? xcd : r) + local;
+  const int tiles = tiles_m * tiles_n;
+  split = b / tiles;
+  b -= split * tiles;
   const int per_group = group_m * tiles_n;
   const int g = b / per_group;
   const int first_m = g * group_m;

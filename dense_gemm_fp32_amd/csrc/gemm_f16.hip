@@ -629,8 +629,9 @@ __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int
 template <class T, bool VA, bool VB, bool VC, bool OUT32>
 __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
-  int tm, tn;
-  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  int tm, tn, split;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+  select_split<uint16_t, float>(p, split);   // split-K passes always write fp32 slabs
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
   const int wave = threadIdx.x / kWave;
@@ -689,6 +690,7 @@ static Plan make_plan(const Call &c, const char *name) {
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
   pl.blocks = tm * tn;
+  pl.splits = 1;
   return pl;
 }
 
@@ -709,8 +711,11 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = T::GROUP_M;
-  hipLaunchKernelGGL((hgemm_mfma<T, VA, VB, VC, OUT32>), dim3((unsigned)pl.blocks), dim3(T::NT), 0,
-                     c.stream, p);
+  p.splits = c.splits;
+  p.k_chunk = c.k_chunk;
+  p.split_stride = c.split_stride;
+  hipLaunchKernelGGL((hgemm_mfma<T, VA, VB, VC, OUT32>), dim3((unsigned)(pl.blocks * c.splits)),
+                     dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
 }
 
@@ -732,7 +737,7 @@ static hipError_t dispatch_out(const Call &c, const Plan &pl) {
 template <class T>
 static hipError_t dispatch(const Call &c) {
   const Plan pl = make_plan<T>(c, "");
-  if (pl.blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (pl.blocks * c.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   return c.out32 ? dispatch_out<T, true>(c, pl) : dispatch_out<T, false>(c, pl);
 }
 
@@ -755,25 +760,86 @@ static F16Cfg choose_f16(const Call &c) {
   return F16Cfg::kSmall;
 }
 
+// Splits of K for a call on configuration T: none unless forced (the size
+// rule that enables split K is chosen from measurements, below).
+template <class T>
+static int want_splits(const Call &c) {
+  (void)c;
+  return 1;
+}
+
+// Run configuration T, splitting K when the split count says so: the tiles
+// of every K chunk write raw fp32 sums (the fp32-output kernel) to a pooled
+// workspace, then one pass sums the chunks in order, applies alpha and beta
+// and rounds to C's type.  If the workspace cannot be had the call runs
+// unsplit.
+template <class T>
+static hipError_t launch_cfg(const Call &c) {
+  int kc = 0;
+  const int S = clamp_splits(c, want_splits<T>(c), T::BK, tiles_of<T>(c), &kc);
+  if (S <= 1) return dispatch<T>(c);
+  const int ldw = (c.N + 3) / 4 * 4;
+  const long long stride = (long long)c.M * ldw;
+  void *ws = nullptr;
+  if (workspace_alloc(c.stream, (size_t)S * (size_t)stride * sizeof(float), &ws) != hipSuccess)
+    return dispatch<T>(c);
+  Call pc = c;
+  pc.C = ws;
+  pc.ldc = ldw;
+  pc.alpha = 1.0f;
+  pc.beta = 0.0f;
+  pc.out32 = true;
+  pc.splits = S;
+  pc.k_chunk = kc;
+  pc.split_stride = stride;
+  hipError_t e = dispatch<T>(pc);
+  if (e == hipSuccess) {
+    SplitReduce r;
+    r.W = static_cast<const float *>(ws);
+    r.stride = stride;
+    r.ldw = ldw;
+    r.S = S;
+    r.M = c.M;
+    r.N = c.N;
+    r.alpha = c.alpha;
+    r.beta = c.beta;
+    r.C = c.C;
+    r.ldc = c.ldc;
+    r.half_out = !c.out32;
+    r.force_scalar = c.force_scalar;
+    e = launch_splitk_reduce(r, c.stream);
+  }
+  const hipError_t f = workspace_free(c.stream, ws);
+  return e != hipSuccess ? e : f;
+}
+
+template <class T>
+static Plan plan_cfg(const Call &c, const char *name) {
+  Plan pl = make_plan<T>(c, name);
+  int kc = 0;
+  pl.splits = clamp_splits(c, want_splits<T>(c), T::BK, pl.blocks, &kc);
+  return pl;
+}
+
 Plan plan_f16(const Call &c) {
   switch (choose_f16(c)) {
     case F16Cfg::kBig:
-      return make_plan<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
-                                          : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
+      return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
+                                         : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
     case F16Cfg::kMid:
-      return make_plan<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
-                                          : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
+      return plan_cfg<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
+                                         : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
     default:
-      return make_plan<F16Small>(c, c.out32 ? "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots out f32"
-                                            : "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
+      return plan_cfg<F16Small>(c, c.out32 ? "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots out f32"
+                                           : "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
   }
 }
 
 hipError_t launch_f16(const Call &c) {
   switch (choose_f16(c)) {
-    case F16Cfg::kBig: return dispatch<F16Big>(c);
-    case F16Cfg::kMid: return dispatch<F16Mid>(c);
-    default: return dispatch<F16Small>(c);
+    case F16Cfg::kBig: return launch_cfg<F16Big>(c);
+    case F16Cfg::kMid: return launch_cfg<F16Mid>(c);
+    default: return launch_cfg<F16Small>(c);
   }
 }
 

@@ -607,8 +607,9 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
 template <class T, bool VA, bool VB, bool VC>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
-  int tm, tn;
-  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  int tm, tn, split;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+  select_split<float, float>(p, split);
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
   const int wave = wave_id();
@@ -671,6 +672,7 @@ static Plan make_plan(const Call &c, const char *name) {
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
   pl.blocks = tm * tn;
+  pl.splits = 1;
   return pl;
 }
 
@@ -691,15 +693,18 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = T::GROUP_M;
-  hipLaunchKernelGGL((sgemm_mfma<T, VA, VB, VC>), dim3((unsigned)pl.blocks), dim3(T::NT), 0,
-                     c.stream, p);
+  p.splits = c.splits;
+  p.k_chunk = c.k_chunk;
+  p.split_stride = c.split_stride;
+  hipLaunchKernelGGL((sgemm_mfma<T, VA, VB, VC>), dim3((unsigned)(pl.blocks * c.splits)),
+                     dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
 }
 
 template <class T>
 static hipError_t dispatch(const Call &c) {
   const Plan pl = make_plan<T>(c, "");
-  if (pl.blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (pl.blocks * c.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int key = (pl.vec_a > 1 ? 4 : 0) | (pl.vec_b > 1 ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
   switch (key) {
     case 0: return launch_variant<T, false, false, false>(c, pl);
@@ -765,23 +770,82 @@ static F32Cfg choose_f32(const Call &c) {
   return small >= tiny ? F32Cfg::kSmall : F32Cfg::kTiny;
 }
 
+// Splits of K for a call on configuration T: none unless forced (the size
+// rule that enables split K is chosen from measurements, below).
+template <class T>
+static int want_splits(const Call &c) {
+  (void)c;
+  return 1;
+}
+
+// Run configuration T, splitting K when the split count says so: the tiles
+// of every K chunk write raw fp32 sums to a pooled workspace, then one pass
+// sums the chunks in order and applies alpha and beta.  If the workspace
+// cannot be had the call runs unsplit.
+template <class T>
+static hipError_t launch_cfg(const Call &c) {
+  int kc = 0;
+  const int S = clamp_splits(c, want_splits<T>(c), T::BK, tiles_of<T>(c), &kc);
+  if (S <= 1) return dispatch<T>(c);
+  const int ldw = (c.N + 3) / 4 * 4;
+  const long long stride = (long long)c.M * ldw;
+  void *ws = nullptr;
+  if (workspace_alloc(c.stream, (size_t)S * (size_t)stride * sizeof(float), &ws) != hipSuccess)
+    return dispatch<T>(c);
+  Call pc = c;
+  pc.C = ws;
+  pc.ldc = ldw;
+  pc.alpha = 1.0f;
+  pc.beta = 0.0f;
+  pc.splits = S;
+  pc.k_chunk = kc;
+  pc.split_stride = stride;
+  hipError_t e = dispatch<T>(pc);
+  if (e == hipSuccess) {
+    SplitReduce r;
+    r.W = static_cast<const float *>(ws);
+    r.stride = stride;
+    r.ldw = ldw;
+    r.S = S;
+    r.M = c.M;
+    r.N = c.N;
+    r.alpha = c.alpha;
+    r.beta = c.beta;
+    r.C = c.C;
+    r.ldc = c.ldc;
+    r.half_out = false;
+    r.force_scalar = c.force_scalar;
+    e = launch_splitk_reduce(r, c.stream);
+  }
+  const hipError_t f = workspace_free(c.stream, ws);
+  return e != hipSuccess ? e : f;
+}
+
+template <class T>
+static Plan plan_cfg(const Call &c, const char *name) {
+  Plan pl = make_plan<T>(c, name);
+  int kc = 0;
+  pl.splits = clamp_splits(c, want_splits<T>(c), T::BK, pl.blocks, &kc);
+  return pl;
+}
+
 Plan plan_f32(const Call &c) {
   switch (choose_f32(c)) {
-    case F32Cfg::kBig: return make_plan<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads");
-    case F32Cfg::kMid: return make_plan<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads");
-    case F32Cfg::kMidB: return make_plan<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
-    case F32Cfg::kSmall: return make_plan<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
-    default: return make_plan<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots");
+    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads");
+    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads");
+    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
+    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
+    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots");
   }
 }
 
 hipError_t launch_f32(const Call &c) {
   switch (choose_f32(c)) {
-    case F32Cfg::kBig: return dispatch<F32Big>(c);
-    case F32Cfg::kMid: return dispatch<F32Mid>(c);
-    case F32Cfg::kMidB: return dispatch<F32MidB>(c);
-    case F32Cfg::kSmall: return dispatch<F32Small>(c);
-    default: return dispatch<F32Tiny>(c);
+    case F32Cfg::kBig: return launch_cfg<F32Big>(c);
+    case F32Cfg::kMid: return launch_cfg<F32Mid>(c);
+    case F32Cfg::kMidB: return launch_cfg<F32MidB>(c);
+    case F32Cfg::kSmall: return launch_cfg<F32Small>(c);
+    default: return launch_cfg<F32Tiny>(c);
   }
 }
 

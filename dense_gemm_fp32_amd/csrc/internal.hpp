@@ -20,6 +20,11 @@ struct Call {
   int ldc;
   bool out32;            // fp16 inputs: C and the result are fp32 (else fp16)
   bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
+  int split_mode;        // 0 = split K by size, 1 = never, >= 2 = that many splits (diagnostic)
+  // Set by the launcher for the partial pass of a split-K call (else 1, 0, 0).
+  int splits;
+  int k_chunk;
+  long long split_stride;
   int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
                          // 5 = medium with the loads of a step issued together
   hipStream_t stream;
@@ -31,8 +36,34 @@ struct Plan {
   int bm, bn, bk;
   int threads;
   int vec_a, vec_b, vec_c;   // elements per global access (1 = scalar)
-  long long blocks;
+  long long blocks;          // tiles
+  int splits;                // K chunks (1 = no split)
 };
+
+// The reduction pass of a split-K call: C := alpha * sum_s W_s + beta * C over
+// an M x N matrix, the S slabs of W (fp32, row pitch ldw, `stride` floats
+// apart) summed in order s = 0..S-1.
+struct SplitReduce {
+  const float *W;
+  long long stride;
+  int ldw, S, M, N;
+  float alpha, beta;
+  void *C;
+  int ldc;
+  bool half_out;       // C is fp16 (else fp32)
+  bool force_scalar;
+};
+
+// Workspace from the library's per-device memory pool, ordered on stream s.
+hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr);
+hipError_t workspace_free(hipStream_t s, void *ptr);
+hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s);
+
+// Split count for a problem with `tiles` tiles of K step `bk`, given the
+// call's split mode and the heuristic's choice `want` (1 = no split): clamped
+// so every split has at least one K step, the grid stays within range and the
+// workspace under its cap.  Also returns the chunk length.
+int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk);
 
 Plan plan_f32(const Call &c);
 Plan plan_f16(const Call &c);

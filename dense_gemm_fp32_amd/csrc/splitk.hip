@@ -1,0 +1,197 @@
+// splitk.hip -- the second half of a split-K GEMM and its workspace.
+//
+// When a problem's tile grid leaves CUs idle, the GEMM kernels can divide K
+// into S chunks (the independent, tile-sized units of the SGEMM summary's
+// tiling section, multiplied by S along K) and write each chunk's raw fp32
+// sums to its own slab of a workspace.  splitk_reduce then forms, for every
+// element,
+//
+//     C := alpha * (W_0 + W_1 + ... + W_{S-1}) + beta * C
+//
+// summing the slabs in that fixed order in fp32, so the result is the same
+// bits on every call with the same shape and split count (no atomics, no
+// arrival-order dependence).  alpha*sum + beta*C is formed in fp32 and, for an
+// fp16 C, rounded once to half with round-to-nearest-even, exactly as the
+// single-pass epilogues do.  C is read only when beta != 0.
+//
+// The workspace comes from a memory pool the library owns, one per device,
+// with stream-ordered allocation on the call's stream: it is taken before
+// the GEMM pass and given back after the reduction, in stream order, so
+// concurrent calls on different streams never share it and nothing is
+// synchronised.  Freed blocks stay in the pool for later calls.
+#include <mutex>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dgemm {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices];
+bool g_pool_made[kMaxDevices];
+
+hipError_t pool_for(int dev, hipMemPool_t *out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool_made[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipError_t e = hipMemPoolCreate(&g_pool[dev], &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;   // keep freed blocks for the next call
+    e = hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    g_pool_made[dev] = true;
+  }
+  *out = g_pool[dev];
+  return hipSuccess;
+}
+
+int stream_device(hipStream_t s) {
+  int dev = -1;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) == hipSuccess) return dev;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return dev;
+}
+
+constexpr int kReduceThreads = 256;
+constexpr unsigned kReduceMaxBlocks = 8192;
+
+template <bool HALF_OUT, bool VEC_C, bool READ_C>
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce(const float *__restrict__ W,
+                                                                long long stride, int ldw, int S,
+                                                                int M, int N, float alpha,
+                                                                float beta, void *Cv, int ldc) {
+  const long long groups = (long long)((N + 3) / 4);   // 4 adjacent columns per thread
+  const long long total = (long long)M * groups;
+  for (long long t = (long long)blockIdx.x * kReduceThreads + threadIdx.x; t < total;
+       t += (long long)gridDim.x * kReduceThreads) {
+    const int i = (int)(t / groups);
+    const int j = 4 * (int)(t - (long long)i * groups);
+    // ldw is a multiple of 4 and covers N, so the 16-byte loads stay inside
+    // the slab; lanes past N carry values that are never stored.
+    const float *w = W + (size_t)i * (size_t)ldw + j;
+    f32x4 sum = *reinterpret_cast<const f32x4 *>(w);
+    for (int s = 1; s < S; ++s) sum += *reinterpret_cast<const f32x4 *>(w + (size_t)s * stride);
+    if constexpr (HALF_OUT) {
+      uint16_t *c = static_cast<uint16_t *>(Cv) + (size_t)i * (size_t)ldc + j;
+      if (VEC_C && j + 3 < N) {
+        u32x2 cw = u32x2{0u, 0u};
+        if (READ_C) cw = *reinterpret_cast<const u32x2 *>(c);
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o = alpha * sum[e];
+          if (READ_C) {
+            const uint16_t ce = (uint16_t)((e < 2 ? cw[0] : cw[1]) >> (16 * (e & 1)));
+            o = __builtin_fmaf(beta, f16_bits_to_f32(ce), o);
+          }
+          h[e] = f32_to_f16_bits(o);
+        }
+        u32x2 ow;
+        ow[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        ow[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<u32x2 *>(c) = ow;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (j + e >= N) continue;
+          float o = alpha * sum[e];
+          if (READ_C) o = __builtin_fmaf(beta, f16_bits_to_f32(c[e]), o);
+          c[e] = f32_to_f16_bits(o);
+        }
+      }
+    } else {
+      float *c = static_cast<float *>(Cv) + (size_t)i * (size_t)ldc + j;
+      if (VEC_C && j + 3 < N) {
+        f32x4 o;
+        if (READ_C) {
+          const f32x4 cv = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(beta, cv[e], alpha * sum[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = alpha * sum[e];
+        }
+        *reinterpret_cast<f32x4 *>(c) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (j + e >= N) continue;
+          float o = alpha * sum[e];
+          if (READ_C) o = __builtin_fmaf(beta, c[e], o);
+          c[e] = o;
+        }
+      }
+    }
+  }
+}
+
+template <bool HALF_OUT, bool VEC_C>
+hipError_t reduce_launch(const SplitReduce &r, hipStream_t s) {
+  const long long total = (long long)r.M * (long long)((r.N + 3) / 4);
+  long long blocks = (total + kReduceThreads - 1) / kReduceThreads;
+  if (blocks > kReduceMaxBlocks) blocks = kReduceMaxBlocks;
+  if (blocks < 1) blocks = 1;
+  if (r.beta != 0.0f)
+    hipLaunchKernelGGL((splitk_reduce<HALF_OUT, VEC_C, true>), dim3((unsigned)blocks),
+                       dim3(kReduceThreads), 0, s, r.W, r.stride, r.ldw, r.S, r.M, r.N, r.alpha,
+                       r.beta, r.C, r.ldc);
+  else
+    hipLaunchKernelGGL((splitk_reduce<HALF_OUT, VEC_C, false>), dim3((unsigned)blocks),
+                       dim3(kReduceThreads), 0, s, r.W, r.stride, r.ldw, r.S, r.M, r.N, r.alpha,
+                       r.beta, r.C, r.ldc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Largest workspace a split-K call takes; beyond it the call runs unsplit.
+constexpr long long kWorkspaceCap = 1LL << 30;
+
+int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk) {
+  *k_chunk = 0;
+  int S = c.split_mode == 1 ? 1 : (c.split_mode >= 2 ? c.split_mode : want);
+  const int steps = (c.K + bk - 1) / bk;
+  if (S > steps) S = steps;
+  if (S < 2) return 1;
+  const int kc = ((c.K + S - 1) / S + bk - 1) / bk * bk;   // whole K steps per chunk
+  S = (c.K + kc - 1) / kc;                                   // chunks actually needed
+  if (S < 2) return 1;
+  if (tiles * (long long)S > 0x7fffffffLL) return 1;
+  const long long ldw = ((long long)c.N + 3) / 4 * 4;
+  if ((long long)S * (long long)c.M * ldw * (long long)sizeof(float) > kWorkspaceCap) return 1;
+  *k_chunk = kc;
+  return S;
+}
+
+hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr) {
+  *ptr = nullptr;
+  hipMemPool_t pool;
+  hipError_t e = pool_for(stream_device(s), &pool);
+  if (e != hipSuccess) return e;
+  e = hipMallocFromPoolAsync(ptr, bytes, pool, s);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    (void)hipGetLastError();   // a failed allocation is not the caller's error
+  }
+  return e;
+}
+
+hipError_t workspace_free(hipStream_t s, void *ptr) {
+  return ptr ? hipFreeAsync(ptr, s) : hipSuccess;
+}
+
+hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s) {
+  const uintptr_t need = r.half_out ? 8 : 16;
+  const bool vec = !r.force_scalar && (r.ldc % 4) == 0 && aligned_to(r.C, need);
+  if (r.half_out) return vec ? reduce_launch<true, true>(r, s) : reduce_launch<true, false>(r, s);
+  return vec ? reduce_launch<false, true>(r, s) : reduce_launch<false, false>(r, s);
+}
+
+}  // namespace dgemm

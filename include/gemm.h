@@ -27,13 +27,25 @@
  *   - M == 0 or N == 0: nothing to do; returns 0 without launching.
  *   - The summation order over K is fixed for a given shape, leading
  *     dimensions and alignment, so repeated calls give bitwise-identical
- *     results (no atomics, no split-K).
+ *     results: no atomics, and a call that splits K (below) sums its chunks
+ *     in a fixed order.
+ *   - Split K: when a problem's tile grid would leave CUs idle, a call may
+ *     divide K into S chunks, multiply each chunk into its own fp32 slab of a
+ *     workspace, and then form alpha * (slab_0 + ... + slab_{S-1}) + beta * C
+ *     in one more pass (same bound; one rounding to the output type).
  *   - Accuracy: |C_gpu - C_exact| <= 4*K*u*(|alpha|*(|A||B|)_ij + |beta|*|C_ij|)
  *     plus one rounding to the output type, u = 2^-24 (fp32 accumulation).
  *
  * Memory and ownership:
  *   - A, B and C are DEVICE pointers owned by the caller.  The library keeps
- *     no pointer after it returns, allocates nothing and frees nothing.
+ *     no pointer to them after it returns and never allocates or frees the
+ *     caller's memory.
+ *   - A split-K call takes S*M*ceil(N/4)*16 bytes of workspace (at most
+ *     1 GiB) from a memory pool the library creates per device, with
+ *     stream-ordered allocation on the call's stream, and returns it to the
+ *     pool, in stream order, after its last kernel; freed blocks stay in the
+ *     pool until the process ends.  If the workspace cannot be had the call
+ *     runs without splitting.
  *   - C must not overlap A or B.
  *   - The pad elements of each row (columns K..lda-1 of A, N..ldb-1 of B,
  *     N..ldc-1 of C) are never read or written.
@@ -43,8 +55,8 @@
  *     enqueues work on it and returns; it does not synchronise.  The caller
  *     keeps A, B and C alive until that work has completed.
  *   - The library keeps no per-call state, so calls are thread-safe and
- *     reentrant; the only process-wide state is the two diagnostic switches
- *     at the end of this header (default off).
+ *     reentrant; the only process-wide state is the workspace pools and the
+ *     diagnostic switches at the end of this header (default off).
  *
  * Return value:
  *   0                 success (work enqueued, or nothing to do)
@@ -155,6 +167,15 @@ int gemm_set_load_mode(int mode);
  * unknown value.
  */
 int gemm_set_tile_config(int config);
+
+/*
+ * Diagnostic switch for tests: 0 = split K by problem size (the default);
+ * 1 = never split; 2..64 = split K into that many chunks whenever K has that
+ * many tile K steps (fewer otherwise).  Process-wide, like
+ * gemm_set_load_mode.  Returns the previous setting, or -1 for an unknown
+ * value.
+ */
+int gemm_set_split(int mode);
 
 #ifdef __cplusplus
 }

@@ -463,3 +463,109 @@ def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed
     assert rc == 0
     check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out,
           "random %s M=%d N=%d K=%d ld=%d,%d,%d cfg=%d" % (dtype, M, N, K, lda, ldb, ldc, cfg))
+
+
+# ---------------------------------------------------------------- split K
+
+@contextmanager
+def split_mode(mode):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_split(mode)
+    try:
+        yield
+    finally:
+        dg.gemm_set_split(prev)
+
+
+SPLIT_SHAPES = [
+    # M,    N,    K,  lda,  ldb,  ldc    (aligned: direct loads; K tail)
+    (300, 264, 1000, 1000, 264, 264),
+    # unaligned leading dimensions (register-staged loads), all three tails
+    (257, 530, 777, 781, 533, 531),
+    # deep K, little M x N
+    (64, 72, 4096, 4096, 72, 80),
+]
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_k_matches_oracle(dtype, splits):
+    """Forced split K (each chunk's fp32 sums to a pooled workspace, then one
+    ordered reduction with alpha, beta and the output rounding) against the
+    full oracle; beta = 0 with a NaN-filled C checks that C stays write-only."""
+    t, tc = _t(dtype), _tc(dtype)
+    for idx, shape in enumerate(SPLIT_SHAPES):
+        M, N, K, lda, ldb, ldc = shape
+        rng = np.random.default_rng(M + 5 * N + 11 * K + splits)
+        A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
+        B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
+        beta = [-0.5, 0.0, 1.0][idx % 3]
+        cvals = rng.uniform(-1, 1, (M, N)).astype(tc) if beta != 0 else np.full((M, N), np.nan, tc)
+        C = wl.pad(cvals, ldc, wl.C_PAD_SENTINEL)
+        with split_mode(splits):
+            rc, out = run(dtype, M, N, K, 1.25, A, lda, B, ldb, beta, C, ldc, "split%d" % splits)
+        assert rc == 0
+        check(dtype, M, N, K, 1.25, A, lda, B, ldb, beta, C, ldc, out,
+              "split %d %s %s" % (splits, dtype, shape))
+
+
+@pytest.mark.parametrize("w", [wl.RAGGED_F32, wl.RAGGED_F16, wl.RAGGED_F16F32], ids=lambda w: w.name)
+def test_split_k_ragged_workload(w):
+    """The ragged 1000 x 3000 x 517 workload (unaligned, NaN pads, C-pad
+    sentinel) with K split in 4."""
+    A, B, C = wl.make(w)
+    with split_mode(4):
+        rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                      w.name + " split4")
+    assert rc == 0
+    check(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, out,
+          w.name + " split4")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_k_deterministic_and_paths_agree(dtype):
+    """A split call gives the same bits twice, with element-wise loads forced
+    (same chunking and summation order), and on every tile configuration the
+    chunks are reduced in order; its result is within the bound of the
+    unsplit one."""
+    import dense_gemm_fp32_amd as dg
+    t, tc = _t(dtype), _tc(dtype)
+    M, N, K = 333, 456, 1500
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal(M * K).astype(t)
+    B = rng.standard_normal(K * N).astype(t)
+    C = rng.standard_normal(M * N).astype(tc)
+    with split_mode(5):
+        rc1, o1 = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split det1")
+        rc2, o2 = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split det2")
+        prev = dg.gemm_set_load_mode(1)
+        try:
+            rc3, o3 = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split scalar")
+        finally:
+            dg.gemm_set_load_mode(prev)
+    assert rc1 == rc2 == rc3 == 0
+    assert np.array_equal(bits(o1, dtype), bits(o2, dtype))
+    assert np.array_equal(bits(o1, dtype), bits(o3, dtype))
+    check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o1, "split det")
+    for cfg in (1, 2, 3, 4):
+        with split_mode(3), tile_config(cfg):
+            rc, o = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split cfg%d" % cfg)
+        assert rc == 0
+        check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o, "split 3 cfg %d" % cfg)
+
+
+def test_split_k_more_chunks_than_k_steps():
+    """K = 40 has two 32-wide K steps: a forced split of 7 runs as 2 chunks
+    (fp32 tiny tile, K step 32), still matching the oracle."""
+    import dense_gemm_fp32_amd as dg
+    M, N, K = 96, 80, 40
+    rng = np.random.default_rng(9)
+    A = rng.uniform(-1, 1, M * K).astype(np.float32)
+    B = rng.uniform(-1, 1, K * N).astype(np.float32)
+    C = rng.uniform(-1, 1, M * N).astype(np.float32)
+    with split_mode(7), tile_config(4):
+        assert "split-K 2" in dg.gemm_describe("f32", M, N, K, 1.0, A.ctypes.data, K, B.ctypes.data, N,
+                                              1.0, C.ctypes.data, N)[1]
+        rc, out = run("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, "split7 K40")
+    assert rc == 0
+    check("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, out, "split7 K40")
