@@ -748,24 +748,82 @@ static long long tiles_of(const Call &c) {
 
 enum class F16Cfg { kBig, kMid, kSmall };
 
-static F16Cfg choose_f16(const Call &c) {
-  if (c.tile_config == 1) return F16Cfg::kBig;
-  if (c.tile_config == 2 || c.tile_config == 5) return F16Cfg::kMid;
-  if (c.tile_config >= 3) return F16Cfg::kSmall;
-  // Measured: the large tile stays ahead down to about half a round of
-  // tiles (fewer busy CUs draw less power and clock higher), the medium one
-  // down to half a round as well.
-  if (tiles_of<F16Big>(c) >= kCUs / 2) return F16Cfg::kBig;
-  if (tiles_of<F16Mid>(c) >= kCUs / 2) return F16Cfg::kMid;
-  return F16Cfg::kSmall;
+// Share of the CUs kept busy by `tiles` workgroups (whole tiles per CU) and
+// share of the two-waves-per-SIMD occupancy a busy CU reaches with its
+// resident workgroups (one wave per SIMD leaves the matrix pipe idle while
+// the wave waits: measured, the 128x128 tile runs 2x faster per CU with two
+// workgroups resident than with one).
+static double busy_share16(long long tiles) {
+  const double per_cu = (double)tiles / kCUs;
+  const double rounds = (double)((tiles + kCUs - 1) / kCUs);
+  return per_cu / rounds;
 }
 
-// Splits of K for a call on configuration T: none unless forced (the size
-// rule that enables split K is chosen from measurements, below).
 template <class T>
-static int want_splits(const Call &c) {
-  (void)c;
-  return 1;
+static double score16(const Call &c, double eff, int per_cu, int splits) {
+  const long long t = tiles_of<T>(c) * splits;
+  long long resident = (t + kCUs - 1) / kCUs;
+  if (resident > per_cu) resident = per_cu;
+  const double waves = (double)(resident * T::NWAVES);
+  return eff * busy_share16(t) * (waves >= 8.0 ? 1.0 : waves / 8.0);
+}
+
+struct F16Choice {
+  F16Cfg cfg;
+  int splits;
+  double time;   // estimated seconds
+};
+
+// Estimated time: the product at `score` of the fp16 peak, plus, when K is
+// split S ways, the extra pass (launch, and S fp32 slabs of M x N written and
+// read back at ~6 TB/s; the writes overlap the product).
+static double est_time16(const Call &c, double score, int splits) {
+  const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
+  double t = flops / (score * 2516.6e12);
+  if (splits > 1) t += 4e-6 + 8.0 * splits * (double)c.M * (double)c.N / 6e12;
+  return t;
+}
+
+template <class T>
+static void try_splits16(const Call &c, F16Cfg cfg, double eff, int per_cu, F16Choice &best) {
+  for (int S = 2; S <= 8; ++S) {
+    const int kc = ((c.K + S - 1) / S + T::BK - 1) / T::BK * T::BK;
+    if (kc < 1024) break;
+    const int used = (c.K + kc - 1) / kc;
+    const double t = est_time16(c, score16<T>(c, eff, per_cu, used), used);
+    if (t < best.time * 0.98) best = F16Choice{cfg, used, t};
+  }
+}
+
+// Unsplit: measured, the large tile stays ahead down to about half a round
+// of tiles (fewer busy CUs draw less power and clock higher), the medium one
+// down to half a round as well.  K is split only when it is at least twice
+// max(M, N): the fp16 product is fast enough that the extra pass over the
+// fp32 slabs pays only for deep K (512 x 512 x 8192 and 1024 x 1024 x 8192:
+// 2-3x with 8 chunks of the 128x128 tile; no square size gains).  Scores use
+// the tiles' throughput at two waves per SIMD as a fraction of the fp16 peak
+// (0.47, 0.47, 0.42); split candidates' chunks are at least 1024 deep and
+// the fastest estimate (est_time16) wins.
+static F16Choice choose_f16(const Call &c) {
+  const int forced = c.split_mode >= 2 ? c.split_mode : 1;
+  if (c.tile_config == 1) return F16Choice{F16Cfg::kBig, forced, 0.0};
+  if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
+  if (c.tile_config >= 3) return F16Choice{F16Cfg::kSmall, forced, 0.0};
+  F16Choice best;
+  if (tiles_of<F16Big>(c) >= kCUs / 2)
+    best = F16Choice{F16Cfg::kBig, 1, est_time16(c, score16<F16Big>(c, 0.47, 1, 1), 1)};
+  else if (tiles_of<F16Mid>(c) >= kCUs / 2)
+    best = F16Choice{F16Cfg::kMid, 1, est_time16(c, score16<F16Mid>(c, 0.47, 2, 1), 1)};
+  else
+    best = F16Choice{F16Cfg::kSmall, 1, est_time16(c, score16<F16Small>(c, 0.42, 3, 1), 1)};
+  if (c.split_mode == 0 && c.K >= 2 * (c.M > c.N ? c.M : c.N)) {
+    try_splits16<F16Big>(c, F16Cfg::kBig, 0.47, 1, best);
+    try_splits16<F16Mid>(c, F16Cfg::kMid, 0.47, 2, best);
+    try_splits16<F16Small>(c, F16Cfg::kSmall, 0.42, 3, best);
+  } else if (c.split_mode >= 2) {
+    best.splits = forced;
+  }
+  return best;
 }
 
 // Run configuration T, splitting K when the split count says so: the tiles
@@ -774,9 +832,9 @@ static int want_splits(const Call &c) {
 // and rounds to C's type.  If the workspace cannot be had the call runs
 // unsplit.
 template <class T>
-static hipError_t launch_cfg(const Call &c) {
+static hipError_t launch_cfg(const Call &c, int want) {
   int kc = 0;
-  const int S = clamp_splits(c, want_splits<T>(c), T::BK, tiles_of<T>(c), &kc);
+  const int S = clamp_splits(c, want, T::BK, tiles_of<T>(c), &kc);
   if (S <= 1) return dispatch<T>(c);
   const int ldw = (c.N + 3) / 4 * 4;
   const long long stride = (long long)c.M * ldw;
@@ -814,32 +872,34 @@ static hipError_t launch_cfg(const Call &c) {
 }
 
 template <class T>
-static Plan plan_cfg(const Call &c, const char *name) {
+static Plan plan_cfg(const Call &c, const char *name, int want) {
   Plan pl = make_plan<T>(c, name);
   int kc = 0;
-  pl.splits = clamp_splits(c, want_splits<T>(c), T::BK, pl.blocks, &kc);
+  pl.splits = clamp_splits(c, want, T::BK, pl.blocks, &kc);
   return pl;
 }
 
 Plan plan_f16(const Call &c) {
-  switch (choose_f16(c)) {
+  const F16Choice ch = choose_f16(c);
+  switch (ch.cfg) {
     case F16Cfg::kBig:
       return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
-                                         : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots");
+                                         : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots", ch.splits);
     case F16Cfg::kMid:
       return plan_cfg<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
-                                         : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots");
+                                         : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots", ch.splits);
     default:
       return plan_cfg<F16Small>(c, c.out32 ? "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots out f32"
-                                           : "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots");
+                                           : "f16 mfma32x32x16 tile 64x128x32 2 waves 4 slots", ch.splits);
   }
 }
 
 hipError_t launch_f16(const Call &c) {
-  switch (choose_f16(c)) {
-    case F16Cfg::kBig: return launch_cfg<F16Big>(c);
-    case F16Cfg::kMid: return launch_cfg<F16Mid>(c);
-    default: return launch_cfg<F16Small>(c);
+  const F16Choice ch = choose_f16(c);
+  switch (ch.cfg) {
+    case F16Cfg::kBig: return launch_cfg<F16Big>(c, ch.splits);
+    case F16Cfg::kMid: return launch_cfg<F16Mid>(c, ch.splits);
+    default: return launch_cfg<F16Small>(c, ch.splits);
   }
 }
 

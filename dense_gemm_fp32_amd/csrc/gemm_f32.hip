@@ -745,37 +745,103 @@ static double simd_share(long long tiles, int per_cu) {
   return waves >= 4.0 ? 1.0 : waves / 4.0;
 }
 
-// Otherwise score = measured throughput at full occupancy (fraction of the fp32 peak at
-// 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57, 0.63) x the two
-// shares above; the largest score wins.
-static F32Cfg choose_f32(const Call &c) {
-  if (c.tile_config == 1) return F32Cfg::kBig;
-  if (c.tile_config == 2) return F32Cfg::kMid;
-  if (c.tile_config == 3) return F32Cfg::kSmall;
-  if (c.tile_config == 4) return F32Cfg::kTiny;
-  if (c.tile_config == 5) return F32Cfg::kMidB;
-  const long long tb = tiles_of<F32Big>(c), tm = tiles_of<F32Mid>(c);
-  const long long ts = tiles_of<F32Small>(c), tt = tiles_of<F32Tiny>(c);
-  // Problems too small to give every CU even a 32x32 tile are latency-bound:
-  // the most workgroups and the shortest prologue win.
-  if (tt <= kCUs) return F32Cfg::kTiny;
-  const double big = 0.92 * busy_share(tb) * simd_share<F32Big>(tb, 1);
-  const double mid = 0.91 * busy_share(tm) * simd_share<F32Mid>(tm, 3);
-  const double small = 0.57 * busy_share(ts) * simd_share<F32Small>(ts, 3);
-  const double tiny = 0.63 * busy_share(tt) * simd_share<F32Tiny>(tt, 6);
-  if (big >= mid && big >= small && big >= tiny) return F32Cfg::kBig;
-  // Spread loads pay while a CU holds one workgroup; with several resident
-  // the others hide the load bursts and issuing them together is cheaper.
-  if (mid >= small && mid >= tiny) return tm <= kCUs ? F32Cfg::kMid : F32Cfg::kMidB;
-  return small >= tiny ? F32Cfg::kSmall : F32Cfg::kTiny;
+// Throughput score of configuration T when its tiles are run `splits` times
+// (one per K chunk): measured throughput at full occupancy x the two shares.
+template <class T>
+static double score_of(const Call &c, double eff, int per_cu, int splits) {
+  const long long t = tiles_of<T>(c) * splits;
+  return eff * busy_share(t) * simd_share<T>(t, per_cu);
 }
 
-// Splits of K for a call on configuration T: none unless forced (the size
-// rule that enables split K is chosen from measurements, below).
+// K chunk of configuration T when K is split `splits` ways: whole K steps.
 template <class T>
-static int want_splits(const Call &c) {
-  (void)c;
-  return 1;
+static int chunk_of(const Call &c, int splits) {
+  return ((c.K + splits - 1) / splits + T::BK - 1) / T::BK * T::BK;
+}
+
+// The 32x32 tile's throughput depends on the K each workgroup runs: one wave
+// per workgroup, so its prologue and epilogue weigh like ~700 k of work
+// (measured 0.435 of the peak at K = 1024, 0.41 at 1536, 0.63 at 4096).
+static double tiny_eff(int kc) { return 0.74 * (double)kc / ((double)kc + 700.0); }
+
+struct F32Choice {
+  F32Cfg cfg;
+  int splits;   // wanted K chunks (1 = none); clamp_splits has the last word
+  double time;  // estimated seconds
+};
+
+// Estimated time of a choice: the product at `score` of the fp32 peak, plus,
+// when K is split S ways, the extra pass: a few microseconds to launch and S
+// fp32 slabs of M x N written and read back at ~6 TB/s (the writes overlap the product).
+static double est_time(const Call &c, double score, int splits) {
+  const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
+  double t = flops / (score * 157.3e12);
+  if (splits > 1) t += 4e-6 + 8.0 * splits * (double)c.M * (double)c.N / 6e12;
+  return t;
+}
+
+// Best split of K for configuration T, if one is estimated faster than
+// `best`: chunks of at least `kmin` (so each workgroup still runs enough K
+// steps to hide its prologue and epilogue), at most 8.
+template <class T>
+static void try_splits(const Call &c, F32Cfg cfg, double eff, int per_cu, int kmin,
+                       F32Choice &best) {
+  for (int S = 2; S <= 8; ++S) {
+    const int kc = chunk_of<T>(c, S);
+    if (kc < kmin) break;
+    const int used = (c.K + kc - 1) / kc;
+    const double e = cfg == F32Cfg::kTiny ? tiny_eff(kc) : eff;
+    const double t = est_time(c, score_of<T>(c, e, per_cu, used), used);
+    if (t < best.time * 0.98) best = F32Choice{cfg, used, t};
+  }
+}
+
+// Otherwise score = measured throughput at full occupancy (fraction of the
+// fp32 peak at 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57,
+// and tiny_eff for the 32x32 tile) x the two shares above; the largest score
+// wins.  When K is at least max(M, N) and 1024, K splits of every
+// configuration are estimated too (est_time; measured
+// winners: 1536^3, 2560^3, 3072^3 and deep-K shapes such as 1024 x 1024 x
+// 8192 take 3-8 chunks of the 128x128 tile; square problems up to 1024 and
+// those whose tiles already fill the CUs stay unsplit).
+static F32Choice choose_f32(const Call &c) {
+  const int forced = c.split_mode >= 2 ? c.split_mode : 1;
+  if (c.tile_config == 1) return F32Choice{F32Cfg::kBig, forced, 0.0};
+  if (c.tile_config == 2) return F32Choice{F32Cfg::kMid, forced, 0.0};
+  if (c.tile_config == 3) return F32Choice{F32Cfg::kSmall, forced, 0.0};
+  if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0};
+  if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0};
+  const double big = score_of<F32Big>(c, 0.92, 1, 1);
+  const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
+  const double small = score_of<F32Small>(c, 0.57, 3, 1);
+  const double tiny = score_of<F32Tiny>(c, tiny_eff(c.K), 6, 1);
+  F32Choice best;
+  if (tiles_of<F32Tiny>(c) <= kCUs) {
+    // Problems too small to give every CU even a 32x32 tile are
+    // latency-bound: the most workgroups and the shortest prologue win.
+    best = F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1)};
+  } else if (big >= mid && big >= small && big >= tiny) {
+    best = F32Choice{F32Cfg::kBig, 1, est_time(c, big, 1)};
+  } else if (mid >= small && mid >= tiny) {
+    best = F32Choice{F32Cfg::kMid, 1, est_time(c, mid, 1)};
+  } else {
+    best = small >= tiny ? F32Choice{F32Cfg::kSmall, 1, est_time(c, small, 1)}
+                         : F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1)};
+  }
+  if (c.split_mode == 0 && c.K >= 1024 && c.K >= (c.M > c.N ? c.M : c.N)) {
+    // The large tile runs one workgroup per CU, so nothing overlaps its
+    // prologue and epilogue: it needs longer chunks than the others.
+    try_splits<F32Big>(c, F32Cfg::kBig, 0.92, 1, 1024, best);
+    try_splits<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 384, best);
+    try_splits<F32Small>(c, F32Cfg::kSmall, 0.57, 3, 1024, best);
+    try_splits<F32Tiny>(c, F32Cfg::kTiny, 0.63, 6, 1024, best);
+  } else if (c.split_mode >= 2) {
+    best.splits = forced;
+  }
+  // Spread loads pay while a CU holds one workgroup; with several resident
+  // the others hide the load bursts and issuing them together is cheaper.
+  if (best.cfg == F32Cfg::kMid && tiles_of<F32Mid>(c) * best.splits > kCUs) best.cfg = F32Cfg::kMidB;
+  return best;
 }
 
 // Run configuration T, splitting K when the split count says so: the tiles
@@ -783,9 +849,9 @@ static int want_splits(const Call &c) {
 // sums the chunks in order and applies alpha and beta.  If the workspace
 // cannot be had the call runs unsplit.
 template <class T>
-static hipError_t launch_cfg(const Call &c) {
+static hipError_t launch_cfg(const Call &c, int want) {
   int kc = 0;
-  const int S = clamp_splits(c, want_splits<T>(c), T::BK, tiles_of<T>(c), &kc);
+  const int S = clamp_splits(c, want, T::BK, tiles_of<T>(c), &kc);
   if (S <= 1) return dispatch<T>(c);
   const int ldw = (c.N + 3) / 4 * 4;
   const long long stride = (long long)c.M * ldw;
@@ -822,30 +888,32 @@ static hipError_t launch_cfg(const Call &c) {
 }
 
 template <class T>
-static Plan plan_cfg(const Call &c, const char *name) {
+static Plan plan_cfg(const Call &c, const char *name, int want) {
   Plan pl = make_plan<T>(c, name);
   int kc = 0;
-  pl.splits = clamp_splits(c, want_splits<T>(c), T::BK, pl.blocks, &kc);
+  pl.splits = clamp_splits(c, want, T::BK, pl.blocks, &kc);
   return pl;
 }
 
 Plan plan_f32(const Call &c) {
-  switch (choose_f32(c)) {
-    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads");
-    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads");
-    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots");
-    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots");
-    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots");
+  const F32Choice ch = choose_f32(c);
+  switch (ch.cfg) {
+    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits);
+    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits);
+    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits);
+    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits);
+    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits);
   }
 }
 
 hipError_t launch_f32(const Call &c) {
-  switch (choose_f32(c)) {
-    case F32Cfg::kBig: return launch_cfg<F32Big>(c);
-    case F32Cfg::kMid: return launch_cfg<F32Mid>(c);
-    case F32Cfg::kMidB: return launch_cfg<F32MidB>(c);
-    case F32Cfg::kSmall: return launch_cfg<F32Small>(c);
-    default: return launch_cfg<F32Tiny>(c);
+  const F32Choice ch = choose_f32(c);
+  switch (ch.cfg) {
+    case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits);
+    case F32Cfg::kMid: return launch_cfg<F32Mid>(c, ch.splits);
+    case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits);
+    case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits);
+    default: return launch_cfg<F32Tiny>(c, ch.splits);
   }
 }
 

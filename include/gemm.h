@@ -40,10 +40,12 @@
  *   - A, B and C are DEVICE pointers owned by the caller.  The library keeps
  *     no pointer to them after it returns and never allocates or frees the
  *     caller's memory.
- *   - A split-K call takes S*M*ceil(N/4)*16 bytes of workspace (at most
- *     1 GiB) from a memory pool the library creates per device, with
- *     stream-ordered allocation on the call's stream, and returns it to the
- *     pool, in stream order, after its last kernel; freed blocks stay in the
+ *   - A split-K call needs S*M*ceil(N/4)*16 bytes of workspace (at most
+ *     1 GiB; larger splits are not taken) and takes it from a memory pool the
+ *     library creates per device, with stream-ordered allocation on the
+ *     call's stream, returning it to the pool, in stream order, after its
+ *     last kernel.  Requests are made at the largest size used so far on the
+ *     device (2 MiB steps) so that freed blocks are reused; they stay in the
  *     pool until the process ends.  If the workspace cannot be had the call
  *     runs without splitting.
  *   - C must not overlap A or B.

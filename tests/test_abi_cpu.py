@@ -170,8 +170,13 @@ def test_tile_table_choice_and_override():
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
     assert "256x128x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
     assert "32x32x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
-    assert "32x32x32" in name("f32", 64) and "32x32x32" in name("f32", 1536)
+    assert "32x32x32" in name("f32", 64) and "split" not in name("f32", 1024)
+    # K split where the grid leaves CUs idle and K is long enough
+    assert "128x128x16" in name("f32", 1536) and "split-K 3" in name("f32", 1536)
+    assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
+    assert "split" not in name("f16", 1536)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
+    assert "split-K 2" in name("f32", 5120) and "split" not in name("f32", 8192)
     assert "256x128x32" in name("f32", 8192)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
     assert "128x128x32" in name("f16", 2048) and "64x128x32" in name("f16", 512)
@@ -185,3 +190,21 @@ def test_tile_table_choice_and_override():
     finally:
         dg.gemm_set_tile_config(prev)
     assert dg.gemm_set_tile_config(9) == -1
+
+
+def test_split_choice_and_override():
+    import dense_gemm_fp32_amd as dg
+    def d(dt, M, N, K):
+        return dg.gemm_describe(dt, M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
+    assert "split-K 8" in d("f16", 1024, 1024, 8192) and "split-K 4" in d("f32", 512, 512, 8192)
+    assert "split" not in d("f32", 1000, 3000, 517)
+    prev = dg.gemm_set_split(1)
+    try:
+        assert "split" not in d("f16", 1024, 1024, 8192)
+        dg.gemm_set_split(5)
+        assert "split-K 5" in d("f32", 4096, 4096, 4096)
+        assert "split-K 2" in d("f32", 64, 64, 40)       # only two 32-deep K steps
+        assert "split" not in d("f32", 64, 64, 16)       # one K step: nothing to split
+    finally:
+        dg.gemm_set_split(prev)
+    assert dg.gemm_set_split(65) == -1 and dg.gemm_set_split(-1) == -1

@@ -554,6 +554,22 @@ def test_split_k_deterministic_and_paths_agree(dtype):
         check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o, "split 3 cfg %d" % cfg)
 
 
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 1536, 1536, 1536), ("f16", 1024, 1024, 8192),
+                                          ("f16f32", 512, 512, 8192), ("f32", 512, 512, 8192)])
+def test_split_k_chosen_by_size_sampled(dtype, M, N, K):
+    """Shapes whose tile grid leaves CUs idle take split K by themselves;
+    checked on sampled rows, the checksum and Freivalds' product check."""
+    import dense_gemm_fp32_amd as dg
+    w = wl.Workload("auto_split_%s_%dx%dx%d" % (dtype, M, N, K), dtype, M, N, K, K, N, N, 1.5, -0.5,
+                    "uniform", "uniform", (31, 32, 33))
+    A, B, C = wl.make(w)
+    assert "split-K" in dg.gemm_describe(dtype, M, N, K, w.alpha, A.ctypes.data, K, B.ctypes.data, N,
+                                         w.beta, C.ctypes.data, N)[1]
+    rc, out = run(dtype, M, N, K, w.alpha, A, K, B, N, w.beta, C, N, w.name)
+    assert rc == 0
+    check_sampled(dtype, w, A, B, C, out, nrows=32)
+
+
 def test_split_k_more_chunks_than_k_steps():
     """K = 40 has two 32-wide K steps: a forced split of 7 runs as 2 chunks
     (fp32 tiny tile, K step 32), still matching the oracle."""
