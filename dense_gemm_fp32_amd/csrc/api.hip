@@ -37,6 +37,25 @@ int check_args(int M, int N, int K, float alpha, const void *A, int lda, const v
   return 0;
 }
 
+// The same checks for column-major operands (BLAS layout: X(i, j) at
+// X[i + j*ldX]), with the argument indices of the column-major entry points.
+int check_args_colmajor(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
+                        int ldb, float beta, const void *C, int ldc) {
+  if (M < 0) return -1;
+  if (N < 0) return -2;
+  if (K < 0) return -3;
+  if (lda < (M > 1 ? M : 1)) return -6;
+  if (ldb < (K > 1 ? K : 1)) return -8;
+  if (ldc < (M > 1 ? M : 1)) return -11;
+  const bool empty = (M == 0 || N == 0);
+  const bool reads_ab = !empty && K > 0 && alpha != 0.0f;
+  if (reads_ab && A == nullptr) return -5;
+  if (reads_ab && B == nullptr) return -7;
+  const bool touches_c = !empty && !((alpha == 0.0f || K == 0) && beta == 1.0f);
+  if (touches_c && C == nullptr) return -10;
+  return 0;
+}
+
 enum class Route { kNothing, kScale, kGemm };
 
 Route route(int M, int N, int K, float alpha, float beta) {
@@ -128,6 +147,36 @@ int gemm_f16f32(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
   return e == hipSuccess ? GEMM_SUCCESS : (int)e;
 }
 
+// Column-major calls.  A column-major M x N matrix with leading dimension ld
+// is, byte for byte, the row-major N x M matrix of its transpose with the same
+// ld.  So C = A*B (all column-major) is the row-major product
+// C^T = B^T * A^T: the row-major entry point with M and N exchanged and A and
+// B exchanged, on the same buffers (the SGEMM summary's layout section:
+// column-major use swaps A and B).  Arguments are checked first with the
+// column-major rules and indices.
+int gemm_f32_colmajor(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                      int ldb, float beta, float *C, int ldc, void *stream) {
+  const int rc = check_args_colmajor(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  return gemm_f32(N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream);
+}
+
+int gemm_f16_colmajor(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                      const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc,
+                      void *stream) {
+  const int rc = check_args_colmajor(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  return gemm_f16(N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream);
+}
+
+int gemm_f16f32_colmajor(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                         const gemm_half_t *B, int ldb, float beta, float *C, int ldc,
+                         void *stream) {
+  const int rc = check_args_colmajor(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  return gemm_f16f32(N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream);
+}
+
 const char *gemm_status_string(int status) {
   switch (status) {
     case 0: return "success";
@@ -135,11 +184,11 @@ const char *gemm_status_string(int status) {
     case -2: return "invalid argument 2: N < 0";
     case -3: return "invalid argument 3: K < 0";
     case -5: return "invalid argument 5: A is NULL";
-    case -6: return "invalid argument 6: lda < max(1, K)";
+    case -6: return "invalid argument 6: lda < max(1, K) (row-major) or max(1, M) (column-major)";
     case -7: return "invalid argument 7: B is NULL";
-    case -8: return "invalid argument 8: ldb < max(1, N)";
+    case -8: return "invalid argument 8: ldb < max(1, N) (row-major) or max(1, K) (column-major)";
     case -10: return "invalid argument 10: C is NULL";
-    case -11: return "invalid argument 11: ldc < max(1, N)";
+    case -11: return "invalid argument 11: ldc < max(1, N) (row-major) or max(1, M) (column-major)";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

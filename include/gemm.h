@@ -63,7 +63,9 @@
  * Return value:
  *   0                 success (work enqueued, or nothing to do)
  *   -i (i = 1..12)    argument i (1-based, in signature order) is invalid.
- *                     Checks run in this order and the first failure wins:
+ *                     Checks run in this order and the first failure wins
+ *                     (row-major entry points; see the column-major ones
+ *                     below for their leading-dimension rules):
  *                       M < 0 -> -1, N < 0 -> -2, K < 0 -> -3,
  *                       lda < max(1, K) -> -6, ldb < max(1, N) -> -8,
  *                       ldc < max(1, N) -> -11,
@@ -132,6 +134,34 @@ int gemm_f16f32(int M, int N, int K, float alpha,
                 const gemm_half_t *B, int ldb,
                 float beta, float *C, int ldc,
                 void *stream);
+
+/*
+ * Column-major variants (BLAS layout): element (i, j) of X is X[i + j*ldX],
+ * with lda >= max(1, M), ldb >= max(1, K), ldc >= max(1, M).  Same operation,
+ * semantics, precisions, ownership, streams and return values as the
+ * row-major entry points above; the argument checks use these column-major
+ * rules (-6 for lda < max(1, M), -8 for ldb < max(1, K), -11 for
+ * ldc < max(1, M), the rest as above).  A column-major matrix is the
+ * row-major matrix of its transpose on the same bytes, so each call runs the
+ * row-major product C^T = B^T * A^T: the "Advanced Matrix Multiplication on
+ * NVIDIA GPUs" summary's layout section handles column-major use by swapping
+ * A and B in the same way.
+ */
+int gemm_f32_colmajor(int M, int N, int K, float alpha,
+                      const float *A, int lda,
+                      const float *B, int ldb,
+                      float beta, float *C, int ldc,
+                      void *stream);
+int gemm_f16_colmajor(int M, int N, int K, float alpha,
+                      const gemm_half_t *A, int lda,
+                      const gemm_half_t *B, int ldb,
+                      float beta, gemm_half_t *C, int ldc,
+                      void *stream);
+int gemm_f16f32_colmajor(int M, int N, int K, float alpha,
+                         const gemm_half_t *A, int lda,
+                         const gemm_half_t *B, int ldb,
+                         float beta, float *C, int ldc,
+                         void *stream);
 
 /* Static, human-readable text for a status code returned above (never NULL). */
 const char *gemm_status_string(int status);

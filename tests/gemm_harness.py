@@ -63,6 +63,42 @@ def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
     return rc, out[:-GUARD]
 
 
+def colmajor_buf(mat, ld, fill):
+    """Column-major buffer of a rows x cols matrix: element (i, j) at
+    buf[i + j*ld], pad rows i >= rows of every column filled with `fill`."""
+    rows, cols = mat.shape
+    buf = np.full((cols, ld), fill, dtype=mat.dtype)
+    buf[:, :rows] = mat.T
+    return buf.reshape(-1)
+
+
+def colmajor_view(buf, rows, cols, ld):
+    """rows x cols logical matrix of a column-major buffer (a copy)."""
+    return np.asarray(buf).reshape(-1)[:cols * ld].reshape(cols, ld)[:, :rows].T.copy()
+
+
+def run_colmajor(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
+    """Call a column-major entry point on device copies; returns (status, C
+    buffer after the call).  C's buffer is followed by guard sentinels."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    note("%s colmajor %s M=%d N=%d K=%d lda=%d ldb=%d ldc=%d" % (tag, dtype, M, N, K, lda, ldb, ldc))
+    t = _np_t(dtype)
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    cbuf = np.concatenate([np.asarray(C, t).reshape(-1), np.full(GUARD, wl.C_PAD_SENTINEL, t)])
+    dA, dB, dC = up(A), up(B), up(cbuf)
+    fn = {"f32": dg.gemm_f32_colmajor, "f16": dg.gemm_f16_colmajor,
+          "f16f32": dg.gemm_f16f32_colmajor}[dtype]
+    rc = fn(M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    out = dC.cpu().numpy()
+    u = np.uint16 if dtype == "f16" else np.uint32
+    assert np.array_equal(out[-GUARD:].view(u), np.full(GUARD, wl.C_PAD_SENTINEL, t).view(u)), \
+        "write past the end of C"
+    return rc, out[:-GUARD]
+
+
 def check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out, label=""):
     """Elementwise parity of `out` (the C buffer after the call) with the
     oracle, plus: pad columns of C unchanged bit for bit.  Returns the worst

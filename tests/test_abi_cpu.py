@@ -83,6 +83,30 @@ def test_argument_checks_and_quick_returns(fn, case):
         assert text.startswith("invalid")
 
 
+COLMAJOR_CASES = [
+    # (expected, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc): lda >= M, ldb >= K, ldc >= M
+    (-1, -1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-6, 5, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 5),
+    (-8, 4, 4, 9, 1.0, FAKE, 4, FAKE, 8, 0.0, FAKE, 4),
+    (-11, 9, 4, 4, 1.0, FAKE, 9, FAKE, 4, 0.0, FAKE, 8),
+    (-5, 4, 4, 4, 1.0, None, 4, FAKE, 4, 0.0, FAKE, 4),
+    (-7, 4, 4, 4, 1.0, FAKE, 4, None, 4, 0.0, FAKE, 4),
+    (-10, 4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, None, 4),
+    # a row-major-valid call that is invalid column-major (lda = K < M)
+    (-6, 8, 2, 3, 1.0, FAKE, 3, FAKE, 2, 0.0, FAKE, 8),
+    (0, 0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 1),
+    (0, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, None, 4),
+]
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor"])
+@pytest.mark.parametrize("case", COLMAJOR_CASES, ids=[str(i) for i in range(len(COLMAJOR_CASES))])
+def test_colmajor_argument_checks(fn, case):
+    import dense_gemm_fp32_amd as dg
+    expected, *args = case
+    assert getattr(dg, fn)(*args, None) == expected
+
+
 def test_status_strings():
     import dense_gemm_fp32_amd as dg
     assert dg.gemm_status_string(0) == "success"

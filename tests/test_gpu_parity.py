@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gemm_harness import bits, check, check_sampled, exact_expected, np_in, np_out, run
+from gemm_harness import (bits, check, check_sampled, colmajor_buf, colmajor_view, exact_expected,
+                          np_in, np_out, run, run_colmajor)
 
 pytestmark = pytest.mark.gpu
 
@@ -585,3 +586,43 @@ def test_split_k_more_chunks_than_k_steps():
         rc, out = run("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, "split7 K40")
     assert rc == 0
     check("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, out, "split7 K40")
+
+
+# ---------------------------------------------------------------- column-major calls
+
+COLMAJOR_SHAPES = [
+    # M,   N,   K,  lda, ldb, ldc   (lda >= M, ldb >= K, ldc >= M)
+    (300, 200, 100, 300, 100, 300),
+    (257, 530, 77, 261, 80, 259),
+    (1000, 64, 1500, 1000, 1504, 1008),   # deep K: takes split K in fp32
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_colmajor_matches_oracle(dtype):
+    """Column-major operands laid out explicitly (element (i, j) at
+    X[i + j*ld]), checked against the oracle on row-major copies of the same
+    logical matrices; the pad rows of C's columns must be left unchanged."""
+    t, tc = _t(dtype), _tc(dtype)
+    for idx, (M, N, K, lda, ldb, ldc) in enumerate(COLMAJOR_SHAPES):
+        rng = np.random.default_rng(M + 7 * N + 3 * K)
+        A = rng.uniform(-1, 1, (M, K)).astype(t)
+        B = rng.uniform(-1, 1, (K, N)).astype(t)
+        C = rng.uniform(-1, 1, (M, N)).astype(tc)
+        beta = [0.5, 0.0, -1.0][idx % 3]
+        Cbuf = colmajor_buf(C, ldc, wl.C_PAD_SENTINEL)
+        rc, out = run_colmajor(dtype, M, N, K, 1.5, colmajor_buf(A, lda, np.nan), lda,
+                               colmajor_buf(B, ldb, np.nan), ldb, beta, Cbuf, ldc, "colmajor")
+        assert rc == 0
+        got = colmajor_view(out, M, N, ldc)
+        R, G = oracle.gemm(M, N, K, 1.5, np.ascontiguousarray(A).reshape(-1), K,
+                           np.ascontiguousarray(B).reshape(-1), N, beta,
+                           np.ascontiguousarray(C).reshape(-1) if beta != 0 else None, N, dtype)
+        tol = oracle.tolerance(G, np.abs(C.astype(np.float64)) if beta != 0 else 0.0, 1.5, beta, K, R,
+                               oracle.out_type(dtype))
+        ok, worst, where = oracle.compare(got, R, tol)
+        assert ok, "colmajor %s %s: worst %.3g at %s" % (dtype, (M, N, K), worst, where)
+        u = np.uint16 if dtype == "f16" else np.uint32
+        pads_in = Cbuf.reshape(N, ldc)[:, M:].view(u)
+        pads_out = np.asarray(out).reshape(N, ldc)[:, M:].view(u)
+        assert np.array_equal(pads_in, pads_out), "pad rows of C were modified"
