@@ -19,6 +19,9 @@ Also reported on the same line:
   * fp16: the same for gemm_f16 on the fp16 4096^3 GEMM with beta = 0.5;
   * fp16_out_fp32: gemm_f16f32 (fp16 A and B, fp32 C and result) on the same
     shape with beta = 0.5 (launch timing only);
+  * valu_ablation: gemm_f32_valu (the pages' SIMT register-blocked design on
+    the vector ALUs) on the fp32 4096^3 workload, against the fp32 vector
+    peak (157.3 TFLOP/s), next to the matrix-core result;
   * power (per precision): average socket power and graphics clock over a
     few seconds of back-to-back calls, read from the SMU through amdsmi, the
     energy per GEMM and GFLOP/J, and the matrix peak scaled to the measured
@@ -37,6 +40,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
+# MI355X's published fp32 vector peak: 256 CUs x 4 SIMDs x 64 flops per clock x
+# 2.4 GHz.  (A 16-lane-per-clock count would give 78.6; the vector-ALU kernel,
+# non-packed v_fmac_f32 only, measures ~82 TFLOP/s, so that count is too low.)
+PEAK_F32_VALU = 157.3
 PEAK_F16 = 2516.6     # TFLOP/s, MI355X dense fp16 matrix
 PEAK_HBM = 8000.0     # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -161,6 +168,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--no-f16f32", action="store_true")
+    ap.add_argument("--no-valu", action="store_true")
     ap.add_argument("--no-p4", action="store_true")
     ap.add_argument("--no-power", action="store_true",
                     help="skip the power / energy windows")
@@ -173,7 +181,7 @@ def parse_args():
                          "with cache flush; one JSON row per size")
     ap.add_argument("--sweep-sizes", default=None,
                     help="comma-separated sizes for --sweep (default 1024..12800 step 128)")
-    ap.add_argument("--only", choices=["f32", "f16", "f16f32", "copy"], default=None,
+    ap.add_argument("--only", choices=["f32", "f16", "f16f32", "valu", "copy"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
                          "device copy of known size to calibrate HBM counters")
     return ap.parse_args()
@@ -276,6 +284,12 @@ def main():
                              False)
         print(json.dumps({"only": "f16", **f16_res}), flush=True)
         return
+    if args.only == "valu":
+        res, _ = measure(dg.gemm_f32_valu, wl.F32_4096, PEAK_F32_VALU, "valu", args.steps,
+                         args.warmup, False)
+        res["roofline"]["bound"] = "alu"
+        print(json.dumps({"only": "valu", **res}), flush=True)
+        return
     if args.only == "f16f32":
         res, _ = measure(dg.gemm_f16f32, wl.F16F32_4096, PEAK_F16, "f16f32", args.steps,
                          args.warmup, False)
@@ -305,6 +319,16 @@ def main():
                                  "M=N=K=4096, A,B,C ~ U[-1,1], alpha=1, beta=0.5",
                      "unit": "TFLOP/s", **mixed_res}
 
+    valu_res = None
+    if not args.no_valu:
+        valu_res, _ = measure(dg.gemm_f32_valu, w32, PEAK_F32_VALU, "valu", args.steps,
+                              args.warmup, False)
+        valu_res["roofline"]["bound"] = "alu"
+        valu_res = {"workload": "the fp32 4096^3 workload on gemm_f32_valu (vector ALUs, "
+                                "128x128 tiles, 8x8 outputs per thread)", "unit": "TFLOP/s",
+                    **valu_res,
+                    "matrix_core_speedup": round(main_res["value"] / valu_res["value"], 2)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w32, host32, args.cpu_seconds)
@@ -332,6 +356,7 @@ def main():
         "power": main_res.get("power"),
         "fp16": f16_res,
         "fp16_out_fp32": mixed_res,
+        "valu_ablation": valu_res,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -8,7 +8,8 @@ helpers of this package (the build script, the measurement model) import
 without the library; using the GEMM entry points without a built library
 raises ImportError.
 """
-_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_colmajor", "gemm_f16_colmajor",
+_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
+                  "gemm_f16_colmajor",
                   "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe",
                   "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm", "GemmError", "LIB_PATH",
                   "EXPORTS")

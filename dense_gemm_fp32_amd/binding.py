@@ -29,7 +29,7 @@ _lib.gemm_f16.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16.restype = _I
 _lib.gemm_f16f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16f32.restype = _I
-for _n in ("gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor"):
+for _n in ("gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_f32_valu"):
     getattr(_lib, _n).argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
     getattr(_lib, _n).restype = _I
 _lib.gemm_status_string.argtypes = [_I]
@@ -43,8 +43,8 @@ _lib.gemm_set_tile_config.restype = _I
 _lib.gemm_set_split.argtypes = [_I]
 _lib.gemm_set_split.restype = _I
 
-EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_colmajor", "gemm_f16_colmajor",
-           "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
+           "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
            "gemm_set_tile_config", "gemm_set_split")
 
 
@@ -89,6 +89,13 @@ def gemm_f16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
     """fp16 A and B, fp32 C and result, fp32 accumulation (see include/gemm.h)."""
     return _lib.gemm_f16f32(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                             _stream(stream))
+
+
+def gemm_f32_valu(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """fp32 GEMM on the vector ALUs (ablation of the matrix-core path; see
+    include/gemm.h)."""
+    return _lib.gemm_f32_valu(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                              _stream(stream))
 
 
 def gemm_f32_colmajor(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):

@@ -147,6 +147,24 @@ int gemm_f16f32(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
   return e == hipSuccess ? GEMM_SUCCESS : (int)e;
 }
 
+int gemm_f32_valu(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                  int ldb, float beta, float *C, int ldc, void *stream) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
+      break;
+    case Route::kGemm:
+      e = dgemm::launch_f32_valu(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream));
+      break;
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
 // Column-major calls.  A column-major M x N matrix with leading dimension ld
 // is, byte for byte, the row-major N x M matrix of its transpose with the same
 // ld.  So C = A*B (all column-major) is the row-major product

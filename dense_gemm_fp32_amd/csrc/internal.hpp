@@ -68,6 +68,8 @@ int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk)
 Plan plan_f32(const Call &c);
 Plan plan_f16(const Call &c);
 hipError_t launch_f32(const Call &c);
+// fp32 on the vector ALUs (the SIMT register-blocked design; ablation).
+hipError_t launch_f32_valu(const Call &c);
 hipError_t launch_f16(const Call &c);
 
 // C := beta * C over an M x N matrix (beta == 0 writes zeros without reading).

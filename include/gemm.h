@@ -136,6 +136,21 @@ int gemm_f16f32(int M, int N, int K, float alpha,
                 void *stream);
 
 /*
+ * fp32 GEMM on the vector ALUs instead of the matrix cores: the SIMT design of
+ * the pages' SGEMM kernels (shared-memory tiles, 8 x 8 outputs per thread in
+ * registers: "From 306 ms to 86 ms", register blocking, and the SGEMM
+ * summary's tiling section), kept as the ablation against gemm_f32.  Same
+ * arguments, semantics and return values as gemm_f32; fp32 FMAs (no packed
+ * form) against the 157.3 TFLOP/s fp32 vector peak.  Never splits K and
+ * takes no workspace.
+ */
+int gemm_f32_valu(int M, int N, int K, float alpha,
+                  const float *A, int lda,
+                  const float *B, int ldb,
+                  float beta, float *C, int ldc,
+                  void *stream);
+
+/*
  * Column-major variants (BLAS layout): element (i, j) of X is X[i + j*ldX],
  * with lda >= max(1, M), ldb >= max(1, K), ldc >= max(1, M).  Same operation,
  * semantics, precisions, ownership, streams and return values as the

@@ -31,7 +31,7 @@ def np_out(dtype):
     return _np_t(dtype)
 
 
-def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
+def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag="", entry=None):
     """Call gemm_f32 / gemm_f16 / gemm_f16f32 on device copies of the host buffers.
 
     Returns (status, C buffer after the call as a host array).  C's buffer
@@ -52,6 +52,8 @@ def run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
     cbuf = np.concatenate([np.asarray(C, t).reshape(-1), np.full(GUARD, wl.C_PAD_SENTINEL, t)])
     dC = up(cbuf)
     fn = {"f32": dg.gemm_f32, "f16": dg.gemm_f16, "f16f32": dg.gemm_f16f32}[dtype]
+    if entry is not None:
+        fn = getattr(dg, entry)
     stream = torch.cuda.current_stream(dev)
     rc = fn(M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc, stream)
     torch.cuda.synchronize(dev)

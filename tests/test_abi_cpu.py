@@ -69,15 +69,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_f16f32"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu"])
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_argument_checks_and_quick_returns(fn, case):
     import dense_gemm_fp32_amd as dg
     expected, *args = case
     assert getattr(dg, fn)(*args, None) == expected
     # gemm_describe applies the same checks
-    rc, text = dg.gemm_describe({"gemm_f32": "f32", "gemm_f16": "f16", "gemm_f16f32": "f16f32"}[fn],
-                                *args)
+    rc, text = dg.gemm_describe({"gemm_f32": "f32", "gemm_f16": "f16", "gemm_f16f32": "f16f32",
+                                 "gemm_f32_valu": "f32"}[fn], *args)
     assert rc == expected
     if expected < 0:
         assert text.startswith("invalid")

@@ -626,3 +626,64 @@ def test_colmajor_matches_oracle(dtype):
         pads_in = Cbuf.reshape(N, ldc)[:, M:].view(u)
         pads_out = np.asarray(out).reshape(N, ldc)[:, M:].view(u)
         assert np.array_equal(pads_in, pads_out), "pad rows of C were modified"
+
+
+# ---------------------------------------------------------------- vector-ALU fp32 (ablation)
+
+def test_valu_tails_and_ragged_match_oracle():
+    """gemm_f32_valu (the SIMT register-blocked design on the vector ALUs):
+    tile-crossing shapes with aligned and unaligned leading dimensions, and
+    the ragged workload with NaN pads and a C-pad sentinel."""
+    rng = np.random.default_rng(41)
+    for idx, (M, N, K) in enumerate([(1, 1, 1), (7, 130, 33), (129, 127, 17), (255, 257, 100),
+                                     (300, 200, 1000), (64, 64, 16)]):
+        pad = idx % 3
+        lda, ldb, ldc = K + 4 * pad, N + pad, N + 2 * pad
+        beta = [0.0, 1.0, -0.5][idx % 3]
+        A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(np.float32), lda, np.nan)
+        B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(np.float32), ldb, np.nan)
+        C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(np.float32), ldc, wl.C_PAD_SENTINEL)
+        rc, out = run("f32", M, N, K, 1.25, A, lda, B, ldb, beta, C, ldc, "valu", entry="gemm_f32_valu")
+        assert rc == 0
+        check("f32", M, N, K, 1.25, A, lda, B, ldb, beta, C, ldc, out, "valu %s" % ((M, N, K),))
+    w = wl.RAGGED_F32
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, "valu ragged",
+                  entry="gemm_f32_valu")
+    assert rc == 0
+    check(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, out, "valu ragged")
+
+
+def test_valu_exact_specials_and_deterministic():
+    """Small integers (exact in fp32: bitwise equal to the rounded oracle),
+    beta = 0 with NaN C, alpha = 0 with NaN A and B, and two identical calls
+    giving identical bits."""
+    M, N, K = 300, 260, 1000
+    A = wl.small_ints(M, K, -8, 8, 1, "f32").reshape(-1)
+    B = wl.small_ints(K, N, -8, 8, 2, "f32").reshape(-1)
+    C = wl.small_ints(M, N, -8, 8, 3, "f32").reshape(-1)
+    rc, out = run("f32", M, N, K, -1.0, A, K, B, N, 2.0, C, N, "valu ints", entry="gemm_f32_valu")
+    assert rc == 0
+    R, _ = oracle.gemm(M, N, K, -1.0, A, K, B, N, 2.0, C, N)
+    assert np.array_equal(bits(out, "f32"), bits(exact_expected("f32", R).reshape(-1), "f32"))
+    Cn = np.full(M * N, np.nan, np.float32)
+    rc, out = run("f32", M, N, K, 1.0, A, K, B, N, 0.0, Cn, N, "valu beta0", entry="gemm_f32_valu")
+    assert rc == 0 and np.all(np.isfinite(out))
+    An = np.full(M * K, np.nan, np.float32)
+    rc, out = run("f32", M, N, K, 0.0, An, K, An[:K * N], N, 0.5, C, N, "valu alpha0",
+                  entry="gemm_f32_valu")
+    assert rc == 0 and np.array_equal(out, (np.float32(0.5) * C).astype(np.float32))
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal(M * K).astype(np.float32)
+    rc1, o1 = run("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, "valu det1", entry="gemm_f32_valu")
+    rc2, o2 = run("f32", M, N, K, 1.0, A, K, B, N, 1.0, C, N, "valu det2", entry="gemm_f32_valu")
+    assert rc1 == rc2 == 0 and np.array_equal(bits(o1, "f32"), bits(o2, "f32"))
+
+
+def test_valu_4096_sampled():
+    w = wl.F32_4096
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, "valu 4096",
+                  entry="gemm_f32_valu")
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out, nrows=24)
