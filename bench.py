@@ -26,6 +26,11 @@ Also reported on the same line:
     few seconds of back-to-back calls, read from the SMU through amdsmi, the
     energy per GEMM and GFLOP/J, and the matrix peak scaled to the measured
     clock (peak x clock / 2400 MHz); null where amdsmi is unavailable;
+  * mfma_ceiling (per precision): the matrix-core ceiling probe of the
+    library (gemm_probe_mfma: the GEMM's MFMA instruction on register operands
+    drawn like the GEMM inputs, no memory traffic) timed with HIP events and
+    under the same power window: the rate the part sustains at the clock it
+    holds under matrix-core load, and each GEMM's fraction of it;
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same workload (a subset of output rows).
 """
@@ -160,6 +165,49 @@ def power_window(torch, dev, call, flops, peak, seconds, warm=1.5):
     return res
 
 
+def mfma_ceiling(torch, dev, stream, dg, wl, dtype, peak, seconds):
+    """The library's matrix-core ceiling probe on operands drawn like the
+    GEMM inputs (U[-1, 1], rounded to the operand type): launches of ~20 ms,
+    TFLOP/s from HIP events over 10 launches, then a power window."""
+    tname = "f16" if dtype == 1 else "f32"
+    vals = wl.draw(1, 65536 // (2 if dtype == 1 else 4), "uniform", 17, tname).reshape(-1)
+    ops = torch.from_numpy(vals).to(dev)
+    out = torch.empty(512 * 512, dtype=torch.float32, device=dev)
+
+    def launch(iters):
+        rc, fl = dg.gemm_probe_mfma(dtype, iters, ops, out, stream)
+        if rc != 0:
+            raise RuntimeError("gemm_probe_mfma returned %d: %s" % (rc, dg.gemm_status_string(rc)))
+        return fl
+
+    def timed(iters, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fl = launch(iters)
+        b.record(stream)
+        b.synchronize()
+        return fl, a.elapsed_time(b) / n
+
+    iters = 256
+    timed(iters, 1)
+    _, ms = timed(iters, 2)
+    iters = max(1, int(iters * 20.0 / max(ms, 1e-3)))
+    timed(iters, 5)                       # bring the clock to its loaded level
+    fl, ms = timed(iters, 10)
+    res = {"instruction": "v_mfma_f32_32x32x16_f16" if dtype == 1 else "v_mfma_f32_32x32x2_f32",
+           "iters": iters, "ms_per_launch": round(ms, 4),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / peak, 4)}
+    pw = power_window(torch, dev, lambda: launch(iters), fl, peak, seconds)
+    if pw:
+        res.update({k: pw[k] for k in ("avg_socket_power_w", "avg_gfxclk_mhz",
+                                        "clock_adjusted_peak", "frac_of_clock_adjusted_peak")
+                    if k in pw})
+    del ops, out
+    return res
+
+
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +220,8 @@ def parse_args():
     ap.add_argument("--no-p4", action="store_true")
     ap.add_argument("--no-power", action="store_true",
                     help="skip the power / energy windows")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the matrix-core ceiling probe")
     ap.add_argument("--power-seconds", type=float, default=3.0,
                     help="length of each measured power window")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -329,6 +379,17 @@ def main():
                     **valu_res,
                     "matrix_core_speedup": round(main_res["value"] / valu_res["value"], 2)}
 
+    ceiling = None
+    if not args.no_ceiling and not args.no_power:
+        ceiling = {"f32": mfma_ceiling(torch, dev, stream, dg, wl, 0, PEAK_F32, args.power_seconds),
+                   "f16": mfma_ceiling(torch, dev, stream, dg, wl, 1, PEAK_F16, args.power_seconds)}
+        if ceiling["f32"]:
+            main_res["roofline"]["frac_of_mfma_ceiling"] = round(
+                main_res["roofline"]["achieved"] / ceiling["f32"]["tflops"], 4)
+        if ceiling["f16"] and f16_res:
+            f16_res["roofline"]["frac_of_mfma_ceiling"] = round(
+                f16_res["roofline"]["achieved"] / ceiling["f16"]["tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w32, host32, args.cpu_seconds)
@@ -357,6 +418,7 @@ def main():
         "fp16": f16_res,
         "fp16_out_fp32": mixed_res,
         "valu_ablation": valu_res,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -11,7 +11,8 @@ raises ImportError.
 _BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
                   "gemm_f16_colmajor",
                   "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe",
-                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm", "GemmError", "LIB_PATH",
+                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma", "gemm", "GemmError",
+                  "LIB_PATH",
                   "EXPORTS")
 
 __all__ = list(_BINDING_NAMES)

@@ -42,10 +42,13 @@ _lib.gemm_set_tile_config.argtypes = [_I]
 _lib.gemm_set_tile_config.restype = _I
 _lib.gemm_set_split.argtypes = [_I]
 _lib.gemm_set_split.restype = _I
+_lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
+                                 ctypes.POINTER(ctypes.c_double), _P]
+_lib.gemm_probe_mfma.restype = _I
 
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
            "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
-           "gemm_set_tile_config", "gemm_set_split")
+           "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma")
 
 
 class GemmError(RuntimeError):
@@ -138,6 +141,18 @@ def gemm_set_tile_config(config):
     """0 = tile configuration by problem size (default); 1/2/3/4 = force the
     large/medium/small/tiny configuration (fp16 maps 4 to small)."""
     return _lib.gemm_set_tile_config(int(config))
+
+
+def gemm_probe_mfma(dtype, iters, operands, out, stream=None):
+    """Matrix-core ceiling probe (see include/gemm.h): `operands` and `out`
+    are device torch tensors (at least 64 KiB and 1 MiB).  Returns (status,
+    flops of the launch)."""
+    flops = ctypes.c_double(0.0)
+    rc = _lib.gemm_probe_mfma(int(dtype), int(iters), _addr(operands),
+                              operands.numel() * operands.element_size(), _addr(out),
+                              out.numel() * out.element_size(), ctypes.byref(flops),
+                              _stream(stream))
+    return rc, flops.value
 
 
 def gemm_set_split(mode):

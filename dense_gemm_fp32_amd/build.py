@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_valu.hip", "scale.hip", "splitk.hip"]
+SOURCES = ["api.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_valu.hip", "scale.hip", "splitk.hip",
+           "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -207,6 +207,13 @@ const char *gemm_status_string(int status) {
     case -8: return "invalid argument 8: ldb < max(1, N) (row-major) or max(1, K) (column-major)";
     case -10: return "invalid argument 10: C is NULL";
     case -11: return "invalid argument 11: ldc < max(1, N) (row-major) or max(1, M) (column-major)";
+    case -101: return "invalid probe argument 1: dtype is not 0 (fp32) or 1 (fp16)";
+    case -102: return "invalid probe argument 2: iters < 1";
+    case -103: return "invalid probe argument 3: operands is NULL";
+    case -104: return "invalid probe argument 4: operand buffer smaller than 65536 bytes";
+    case -105: return "invalid probe argument 5: out is NULL";
+    case -106: return "invalid probe argument 6: out buffer smaller than 1 MiB";
+    case -107: return "invalid probe argument 7: flops is NULL";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
@@ -251,6 +258,20 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
     buf[len - 1] = '\0';
   }
   return rc;
+}
+
+int gemm_probe_mfma(int dtype, int iters, const void *operands, size_t operand_bytes, float *out,
+                    size_t out_bytes, double *flops, void *stream) {
+  if (dtype != 0 && dtype != 1) return -101;
+  if (iters < 1) return -102;
+  if (operands == nullptr) return -103;
+  if (operand_bytes < dgemm::probe_operand_bytes()) return -104;
+  if (out == nullptr) return -105;
+  if (out_bytes < dgemm::probe_out_bytes()) return -106;
+  if (flops == nullptr) return -107;
+  *flops = dgemm::probe_flops(dtype, iters);
+  const hipError_t e = dgemm::launch_probe(dtype, iters, operands, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
 }
 
 int gemm_set_load_mode(int mode) {

@@ -70,6 +70,13 @@ Plan plan_f16(const Call &c);
 hipError_t launch_f32(const Call &c);
 // fp32 on the vector ALUs (the SIMT register-blocked design; ablation).
 hipError_t launch_f32_valu(const Call &c);
+
+// Matrix-core ceiling probe (probe.hip): buffer sizes it needs, its flop
+// count per launch, and the launch (dtype 0 = fp32, 1 = fp16).
+size_t probe_operand_bytes();
+size_t probe_out_bytes();
+double probe_flops(int dtype, int iters);
+hipError_t launch_probe(int dtype, int iters, const void *operands, float *out, hipStream_t s);
 hipError_t launch_f16(const Call &c);
 
 // C := beta * C over an M x N matrix (beta == 0 writes zeros without reading).

@@ -81,6 +81,7 @@
 #define DENSE_GEMM_GEMM_H
 
 #include <stdint.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -223,6 +224,29 @@ int gemm_set_tile_config(int config);
  * value.
  */
 int gemm_set_split(int mode);
+
+/*
+ * Matrix-core ceiling probe: a measurement aid, not a GEMM.  It bounds what
+ * any GEMM kernel can reach on this part at the clock the part sustains
+ * under matrix-core load (the power-aware comparison of the SGEMM summary's
+ * discussion of tuning and power): one launch of 512 workgroups x 8 waves,
+ * each wave running `iters` rounds of 8 independent MFMAs on operand
+ * registers loaded once (dtype 1: v_mfma_f32_32x32x16_f16, fp16 operands;
+ * dtype 0: v_mfma_f32_32x32x2_f32, fp32 operands), with no memory traffic
+ * inside the loop.
+ *   operands: DEVICE buffer of at least 65536 bytes holding fp16 (dtype 1)
+ *             or fp32 (dtype 0) values; give it the distribution of the GEMM
+ *             inputs being compared, since the MFMA power depends on the bits.
+ *   out:      DEVICE buffer of at least 1 MiB; receives one float per thread
+ *             (the sum of its accumulators), so that no MFMA is dead.
+ *   flops:    HOST pointer; receives the launch's flop count
+ *             (waves x iters x 8 x 2*32*32*k).
+ * Enqueues one kernel on `stream` and returns 0, a positive hipError_t if the
+ * launch fails, or -101 .. -107 for an invalid argument 1 .. 7 (checked in
+ * order, before any HIP call).
+ */
+int gemm_probe_mfma(int dtype, int iters, const void *operands, size_t operand_bytes,
+                    float *out, size_t out_bytes, double *flops, void *stream);
 
 #ifdef __cplusplus
 }

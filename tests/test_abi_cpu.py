@@ -232,3 +232,27 @@ def test_split_choice_and_override():
     finally:
         dg.gemm_set_split(prev)
     assert dg.gemm_set_split(65) == -1 and dg.gemm_set_split(-1) == -1
+
+
+def test_probe_argument_checks():
+    """gemm_probe_mfma validates its arguments in order before any HIP call."""
+    import ctypes
+    from dense_gemm_fp32_amd import binding
+    lib = binding._lib
+    fl = ctypes.c_double(-1.0)
+    ok_ops, ok_out = 65536, 1 << 20
+    cases = [
+        (-101, (2, 1, FAKE, ok_ops, FAKE, ok_out, ctypes.byref(fl))),
+        (-101, (-1, 1, FAKE, ok_ops, FAKE, ok_out, ctypes.byref(fl))),
+        (-102, (1, 0, FAKE, ok_ops, FAKE, ok_out, ctypes.byref(fl))),
+        (-103, (1, 1, None, ok_ops, FAKE, ok_out, ctypes.byref(fl))),
+        (-104, (0, 1, FAKE, ok_ops - 1, FAKE, ok_out, ctypes.byref(fl))),
+        (-105, (1, 1, FAKE, ok_ops, None, ok_out, ctypes.byref(fl))),
+        (-106, (1, 1, FAKE, ok_ops, FAKE, ok_out - 4, ctypes.byref(fl))),
+        (-107, (1, 1, FAKE, ok_ops, FAKE, ok_out, None)),
+        (-101, (7, 0, None, 0, None, 0, None)),            # first failure wins
+    ]
+    for expected, args in cases:
+        assert lib.gemm_probe_mfma(*args, None) == expected, (expected, args)
+        assert "probe" in binding.gemm_status_string(expected)
+    assert fl.value == -1.0        # no flop count written on a rejected call

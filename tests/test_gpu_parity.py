@@ -687,3 +687,34 @@ def test_valu_4096_sampled():
                   entry="gemm_f32_valu")
     assert rc == 0
     check_sampled(w.dtype, w, A, B, C, out, nrows=24)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_mfma_probe_runs_and_counts(dtype):
+    """The matrix-core ceiling probe: its flop count follows its definition
+    (512 workgroups x 8 waves x iters x 8 MFMAs of 2*32*32*k flops) and every
+    thread's accumulator sum equals iters times the sum after one round (the
+    rounds repeat the same products; small integer operands keep every sum
+    exact)."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import note
+    note("mfma probe dtype=%d" % dtype)
+    dev = torch.device("cuda:0")
+    tdt = torch.float16 if dtype == 1 else torch.float32
+    nvals = 65536 // (2 if dtype == 1 else 4)
+    g = torch.Generator().manual_seed(11)
+    ops = torch.randint(-2, 3, (nvals,), generator=g).to(tdt).to(dev)
+    out1 = torch.empty(512 * 512, dtype=torch.float32, device=dev)
+    out3 = torch.empty_like(out1)
+    rc, f1 = dg.gemm_probe_mfma(dtype, 1, ops, out1)
+    assert rc == 0, dg.gemm_status_string(rc)
+    rc, f3 = dg.gemm_probe_mfma(dtype, 3, ops, out3)
+    assert rc == 0, dg.gemm_status_string(rc)
+    torch.cuda.synchronize(dev)
+    k = 16 if dtype == 1 else 2
+    assert f1 == 512 * 8 * 1 * 8 * 2 * 32 * 32 * k and f3 == 3 * f1
+    a1, a3 = out1.cpu().double(), out3.cpu().double()
+    assert torch.isfinite(a1).all() and torch.isfinite(a3).all()
+    assert torch.equal(a3, 3 * a1)
