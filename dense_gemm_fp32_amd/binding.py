@@ -29,7 +29,9 @@ _lib.gemm_f16.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16.restype = _I
 _lib.gemm_f16f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16f32.restype = _I
-for _n in ("gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_f32_valu"):
+LAYOUT_NAMES = tuple("gemm_%s_%s" % (t, l) for t in ("f32", "f16", "f16f32") for l in ("nt", "tn", "tt"))
+for _n in ("gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor",
+           "gemm_f32_valu") + LAYOUT_NAMES:
     getattr(_lib, _n).argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
     getattr(_lib, _n).restype = _I
 _lib.gemm_status_string.argtypes = [_I]
@@ -48,7 +50,7 @@ _lib.gemm_probe_mfma.restype = _I
 
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
            "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
-           "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma")
+           "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma") + LAYOUT_NAMES
 
 
 class GemmError(RuntimeError):
@@ -143,6 +145,22 @@ def gemm_set_tile_config(config):
     return _lib.gemm_set_tile_config(int(config))
 
 
+def _layout_entry(name):
+    fn = getattr(_lib, name)
+
+    def call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+        return fn(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                  _stream(stream))
+    call.__name__ = name
+    call.__doc__ = ("%s: C := alpha*op(A)*op(B) + beta*C with the operand layouts its suffix "
+                    "names (see include/gemm.h).  Returns the status code." % name)
+    return call
+
+
+for _n in LAYOUT_NAMES:
+    globals()[_n] = _layout_entry(_n)
+
+
 def gemm_probe_mfma(dtype, iters, operands, out, stream=None):
     """Matrix-core ceiling probe (see include/gemm.h): `operands` and `out`
     are device torch tensors (at least 64 KiB and 1 MiB).  Returns (status,
@@ -161,16 +179,35 @@ def gemm_set_split(mode):
     return _lib.gemm_set_split(int(mode))
 
 
+def _operand(name, t):
+    """(transposed, ld) of a 2-D operand: rows contiguous (stride(1) == 1) as
+    stored, or columns contiguous (stride(0) == 1: the transpose of a
+    row-major tensor, e.g. X.t())."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    rows, cols = t.shape
+    if t.stride(1) == 1 and (t.stride(0) >= cols or rows <= 1):
+        return False, max(t.stride(0), cols, 1)
+    if t.stride(0) == 1 and (t.stride(1) >= rows or cols <= 1):
+        return True, max(t.stride(1), rows, 1)
+    raise ValueError("%s must have contiguous rows (stride(1) == 1) or contiguous columns "
+                     "(stride(0) == 1)" % name)
+
+
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C := alpha*A@B + beta*C for 2-D torch tensors on the GPU (in place).
 
-    Rows may be padded (stride(0) >= number of columns) but each row must be
-    contiguous (stride(1) == 1).  float32 tensors go to gemm_f32, float16 to
-    gemm_f16, float16 A and B with a float32 C to gemm_f16f32.  Uses the
-    current torch stream unless one is given."""
-    for name, t in (("A", A), ("B", B), ("C", C)):
-        if t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError("%s must be 2-D with stride(1) == 1" % name)
+    A and B may be row-major (stride(1) == 1, rows possibly padded) or
+    transposed views of row-major tensors (stride(0) == 1, e.g. X.t()); the
+    latter run the _nt / _tn / _tt entry points, which read the operand in
+    its stored orientation.  C must have stride(1) == 1.  float32 tensors go
+    to the fp32 entry points, float16 to the fp16 ones, float16 A and B with a
+    float32 C to the fp16-in / fp32-out ones.  Uses the current torch stream
+    unless one is given."""
+    ta, lda = _operand("A", A)
+    tb, ldb = _operand("B", B)
+    if C.dim() != 2 or C.stride(1) != 1 or (C.shape[0] > 1 and C.stride(0) < C.shape[1]):
+        raise ValueError("C must be 2-D with stride(1) == 1 and stride(0) >= its column count")
     M, K = A.shape
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N):
@@ -187,13 +224,10 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
         raise ValueError("A, B and C must be GPU tensors")
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
-    lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(C.stride(0), 1)
-    if A.dtype == torch.float32:
-        rc = gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
-    elif mixed:
-        rc = gemm_f16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
-    else:
-        rc = gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    ldc = max(C.stride(0), N, 1)
+    kind = "f32" if A.dtype == torch.float32 else ("f16f32" if mixed else "f16")
+    name = "gemm_" + kind + ("" if not (ta or tb) else "_" + ("t" if ta else "n") + ("t" if tb else "n"))
+    rc = globals()[name](M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     if rc != 0:
         raise GemmError(rc)
     return C

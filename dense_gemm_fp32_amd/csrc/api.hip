@@ -19,14 +19,17 @@ std::atomic<int> g_load_mode{0};
 std::atomic<int> g_tile_config{0};
 std::atomic<int> g_split_mode{0};
 
-// Shared argument checks.  `elem_bytes` only matters for descriptions.
-int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
-               float beta, const void *C, int ldc) {
+// Shared argument checks.  ta / tb: A is stored transposed (K x M, so its
+// rows hold M elements) / B is (N x K, rows of K); otherwise A is M x K and B
+// K x N.  Every matrix is row-major.
+int check_args_t(bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
+                 const void *B, int ldb, float beta, const void *C, int ldc) {
   if (M < 0) return -1;
   if (N < 0) return -2;
   if (K < 0) return -3;
-  if (lda < (K > 1 ? K : 1)) return -6;
-  if (ldb < (N > 1 ? N : 1)) return -8;
+  const int row_a = ta ? M : K, row_b = tb ? K : N;
+  if (lda < (row_a > 1 ? row_a : 1)) return -6;
+  if (ldb < (row_b > 1 ? row_b : 1)) return -8;
   if (ldc < (N > 1 ? N : 1)) return -11;
   const bool empty = (M == 0 || N == 0);
   const bool reads_ab = !empty && K > 0 && alpha != 0.0f;
@@ -35,6 +38,11 @@ int check_args(int M, int N, int K, float alpha, const void *A, int lda, const v
   const bool touches_c = !empty && !((alpha == 0.0f || K == 0) && beta == 1.0f);
   if (touches_c && C == nullptr) return -10;
   return 0;
+}
+
+int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+               float beta, const void *C, int ldc) {
+  return check_args_t(false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
 }
 
 // The same checks for column-major operands (BLAS layout: X(i, j) at
@@ -65,9 +73,12 @@ Route route(int M, int N, int K, float alpha, float beta) {
 }
 
 dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
-                      int ldb, float beta, void *C, int ldc, void *stream, bool out32 = false) {
+                      int ldb, float beta, void *C, int ldc, void *stream, bool out32 = false,
+                      bool ta = false, bool tb = false) {
   dgemm::Call c;
   c.out32 = out32;
+  c.ta = ta;
+  c.tb = tb;
   c.M = M;
   c.N = N;
   c.K = K;
@@ -89,62 +100,96 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   return c;
 }
 
+// One call of any type and layout: checks, quick returns, launch.
+// kind: 0 = fp32, 1 = fp16 in and out, 2 = fp16 in, fp32 C.
+int run_gemm(int kind, bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
+             const void *B, int ldb, float beta, void *C, int ldc, void *stream) {
+  const int rc = check_args_t(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = kind == 1 ? dgemm::launch_scale_f16(M, N, beta, static_cast<uint16_t *>(C), ldc, s)
+                    : dgemm::launch_scale_f32(M, N, beta, static_cast<float *>(C), ldc, s);
+      break;
+    case Route::kGemm: {
+      const dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                      kind == 2, ta, tb);
+      e = kind == 0 ? dgemm::launch_f32(c) : dgemm::launch_f16(c);
+      break;
+    }
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
 }  // namespace
 
 extern "C" {
 
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream) {
-  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc != 0) return rc;
-  hipError_t e = hipSuccess;
-  switch (route(M, N, K, alpha, beta)) {
-    case Route::kNothing:
-      return GEMM_SUCCESS;
-    case Route::kScale:
-      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
-      break;
-    case Route::kGemm:
-      e = dgemm::launch_f32(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream));
-      break;
-  }
-  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+  return run_gemm(0, false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_f16(int M, int N, int K, float alpha, const gemm_half_t *A, int lda, const gemm_half_t *B,
              int ldb, float beta, gemm_half_t *C, int ldc, void *stream) {
-  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc != 0) return rc;
-  hipError_t e = hipSuccess;
-  switch (route(M, N, K, alpha, beta)) {
-    case Route::kNothing:
-      return GEMM_SUCCESS;
-    case Route::kScale:
-      e = dgemm::launch_scale_f16(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
-      break;
-    case Route::kGemm:
-      e = dgemm::launch_f16(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream));
-      break;
-  }
-  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+  return run_gemm(1, false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_f16f32(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
                 const gemm_half_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
-  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc != 0) return rc;
-  hipError_t e = hipSuccess;
-  switch (route(M, N, K, alpha, beta)) {
-    case Route::kNothing:
-      return GEMM_SUCCESS;
-    case Route::kScale:
-      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, static_cast<hipStream_t>(stream));
-      break;
-    case Route::kGemm:
-      e = dgemm::launch_f16(make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, true));
-      break;
-  }
-  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+  return run_gemm(2, false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+// Transposed operands (row-major storage): the first letter gives A's
+// operation, the second B's; "t": the operand is stored transposed (A as
+// K x M, B as N x K) and multiplied as its transpose.
+int gemm_f32_nt(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(0, false, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f32_tn(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(0, true, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f32_tt(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(0, true, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16_nt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc, void *stream) {
+  return run_gemm(1, false, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16_tn(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc, void *stream) {
+  return run_gemm(1, true, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc, void *stream) {
+  return run_gemm(1, true, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16f32_nt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(2, false, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16f32_tn(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(2, true, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16f32_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+  return run_gemm(2, true, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_f32_valu(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -202,9 +247,9 @@ const char *gemm_status_string(int status) {
     case -2: return "invalid argument 2: N < 0";
     case -3: return "invalid argument 3: K < 0";
     case -5: return "invalid argument 5: A is NULL";
-    case -6: return "invalid argument 6: lda < max(1, K) (row-major) or max(1, M) (column-major)";
+    case -6: return "invalid argument 6: lda < max(1, row length of A as stored: K, or M when A is stored transposed or column-major)";
     case -7: return "invalid argument 7: B is NULL";
-    case -8: return "invalid argument 8: ldb < max(1, N) (row-major) or max(1, K) (column-major)";
+    case -8: return "invalid argument 8: ldb < max(1, row length of B as stored: N, or K when B is stored transposed or column-major)";
     case -10: return "invalid argument 10: C is NULL";
     case -11: return "invalid argument 11: ldc < max(1, N) (row-major) or max(1, M) (column-major)";
     case -101: return "invalid probe argument 1: dtype is not 0 (fp32) or 1 (fp16)";

@@ -40,18 +40,21 @@ struct GemmParams {
   int splits;
   int k_chunk;
   long long split_stride;  // elements between the slabs of consecutive splits
+  // Bit 0: every row of A starts 16-byte aligned (vector loads); bit 1: of B.
+  int vec_ab;
 };
 
 // Restrict the kernel arguments to split `s` of a split-K launch: K range
-// [s*k_chunk, min(K, (s+1)*k_chunk)) and that split's output slab.
-template <typename TIn, typename TOut>
+// [s*k_chunk, min(K, (s+1)*k_chunk)) and that split's output slab.  TA / TB:
+// A is stored K x M / B is stored N x K (k runs along the rows).
+template <typename TIn, typename TOut, bool TA = false, bool TB = false>
 __device__ __forceinline__ void select_split(GemmParams &p, int s) {
   if (p.splits <= 1) return;
   const int kb = s * p.k_chunk;
   const int left = p.K - kb;
   p.K = left < p.k_chunk ? left : p.k_chunk;
-  p.A = static_cast<const TIn *>(p.A) + kb;
-  p.B = static_cast<const TIn *>(p.B) + (size_t)kb * (size_t)p.ldb;
+  p.A = static_cast<const TIn *>(p.A) + (TA ? (size_t)kb * (size_t)p.lda : (size_t)kb);
+  p.B = static_cast<const TIn *>(p.B) + (TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb);
   p.C = static_cast<TOut *>(p.C) + (size_t)s * (size_t)p.split_stride;
 }
 

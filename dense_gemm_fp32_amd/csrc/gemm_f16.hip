@@ -20,23 +20,27 @@
 // refilled at once with step kt+STAGES.  A load thus has STAGES-1 steps of
 // compute to arrive, and two slots are enough to run the pipeline.
 //
-// LDS layout (per slot, no padding, 16-byte chunks XOR-swizzled by row):
-//   * A [BM rows][BK k]: row r's logical chunk c sits at chunk c ^ swz_a(r),
-//     which spreads 8 consecutive rows over distinct bank groups for the
-//     128-bit MFMA operand reads.
-//   * B [BK rows][BN n] as in memory: k-row kr's chunk c sits at c ^ 2*(kr%4),
-//     so the four k-rows read together by a transpose read use distinct banks.
+// LDS layout (per slot, no padding, 16-byte chunks XOR-swizzled by row).
+// Each operand keeps its stored orientation (HRegion):
+//   * k-major (A as stored, M x K; B stored transposed, N x K): [EXT rows][BK
+//     k], row r's logical chunk c at chunk c ^ swz(r), which spreads 8
+//     consecutive rows over distinct bank groups for the 128-bit reads.
+//   * index-major (B as stored, K x N; A stored transposed, K x M): [BK rows]
+//     [EXT], k-row kr's chunk c at c ^ 4*(kr%4), so the four k-rows read
+//     together by a transpose read use distinct banks.
 // The swizzle is applied on the global side: lane L of a direct load writes
 // LDS bytes 16L..16L+15 of its 1 KB, so it fetches the global chunk that
 // belongs there.
 //
 // Operands.  v_mfma_f32_32x32x16_f16: lane l supplies A(row l%32, k 8h..8h+7)
 // and B(k 8h..8h+7, col l%32) for h = l/32 (any k order shared by A and B gives
-// the same sum).  A: one ds_read_b128 of the lane's row.  B: two
-// ds_read_b64_tr_b16, each returning 4 consecutive k of the lane's column from
-// a 4 (k) x 16 (n) block that 16 lanes address (within each 16-lane group,
-// lane i receives element i%4 of the 8-byte rows read by lanes i/4, 4+i/4,
-// 8+i/4, 12+i/4).
+// the same sum).  From a k-major region: one ds_read_b128 of the lane's row.
+// From an index-major region: two ds_read_b64_tr_b16, each returning 4
+// consecutive k of the lane's index from a 4 (k) x 16 (index) block that 16
+// lanes address (within each 16-lane group, lane i receives element i%4 of the
+// 8-byte rows read by lanes i/4, 4+i/4, 8+i/4, 12+i/4).  The row-major
+// product reads A k-major and B index-major; the transposed-operand entry
+// points flip either.
 //
 // Epilogue.  Accumulators leave the MFMA layout (one column per lane) through
 // a per-wave LDS staging area, 32 rows at a time; each lane then owns 4
@@ -46,13 +50,15 @@
 // epilogue of the SGEMM summary).
 //
 // Edges.  Direct loads cannot substitute zeros, so they are used only where
-// every chunk they read lies inside the matrix: A rows beyond M are clamped to
-// row M-1 (those rows only feed C rows that are never stored), B column chunks
-// beyond N are clamped to the last chunk when N % 8 == 0.  The partial K step
-// (K % BK != 0) is done first, through registers with per-element masks.  A
-// workgroup whose columns cross an N that is not a multiple of 8, and every
+// every chunk they read lies inside the matrix: rows of a k-major operand
+// beyond its extent (M for A, N for B) are clamped to the last row (they only
+// feed rows or columns of C that are never stored), chunks of an index-major
+// operand beyond its extent are clamped to the last chunk when the extent is
+// a multiple of 8.  The partial K step (K % BK != 0) is done first, through
+// registers with per-element masks.  A workgroup whose tile crosses the
+// extent of an index-major operand that is not a multiple of 8, and every
 // workgroup of a call whose A or B is not 16-byte aligned (base or leading
-// dimension) or whose BM*lda or BK*ldb reaches 2^31 elements (32-bit load
+// dimension) or whose offsets would reach 2^31 elements (32-bit load
 // offsets), uses the register-staged path instead: masked loads (0 outside
 // the matrix; pad elements are never read) written to the same LDS layout.
 #include "common.hpp"
@@ -76,12 +82,8 @@ struct H16Tile {
   static constexpr int FM = WTM / 32;
   static constexpr int FN = WTN / 32;
   static constexpr int SUB = BK / 16;                   // MFMA k sub-steps per K step
-  static constexpr int RA = 2 * BK;                     // bytes per A row in LDS
-  static constexpr int CA = BK / 8;                     // 16-byte chunks per A row
-  static constexpr int RPW = RA >= 256 ? 1 : 256 / RA;  // A rows per 256-byte bank window
-  static constexpr int RB = 2 * BN;                     // bytes per B row in LDS
-  static constexpr int A_BYTES = BM * RA;
-  static constexpr int B_BYTES = BK * RB;
+  static constexpr int A_BYTES = BM * BK * 2;           // a slot's A region
+  static constexpr int B_BYTES = BK * BN * 2;           // ... and B region
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int QA = A_BYTES / 1024;             // 1 KB wave loads per A tile
   static constexpr int QB = B_BYTES / 1024;
@@ -95,8 +97,7 @@ struct H16Tile {
   static_assert(BK % 32 == 0 && SUB % 2 == 0, "BK multiple of 32");
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
   static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
-  static_assert(RB % 256 == 0, "B rows span whole bank windows");
-  static_assert(WTN % 64 == 0, "wave column origin multiple of 64");
+  static_assert(WTM % 64 == 0 && WTN % 64 == 0, "wave origins multiples of 64");
   static_assert(FM % 2 == 0, "the last sub-step splits the block rows in halves");
   static_assert(STAGES >= 2, "the pipeline needs two or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -104,85 +105,140 @@ struct H16Tile {
   static_assert(3 * LOADS <= 63, "vmcnt range");
 };
 
+// Operand regions.  A slot holds an A region (BM indices m by BK k) and a B
+// region (BN indices n by BK k).  An operand whose memory is k-contiguous (A
+// as stored, or B stored transposed, N x K) sits k-contiguous in LDS too:
+// rows of 2*BK bytes, one per index ("k-major").  An operand whose memory is
+// index-contiguous (B as stored, or A stored transposed, K x M) sits as in
+// memory: rows of 2*EXT bytes, one per k ("index-major").  Direct loads copy
+// 16-byte chunks, so the LDS orientation follows the memory layout.
+//
 // Swizzles, chosen from measured gfx950 LDS behaviour: 64 banks of 4 bytes,
 // a 128-bit read served 16 lanes (256 bytes) per pass, a 64-bit transpose
 // read 32 lanes per pass.
-//   A: the 16 rows one pass reads must land on 16 distinct 16-byte bank
-//      groups of the 256-byte window: row r's chunks are XORed with
-//      (r / (256/RA)) % CA.
-//   B: a transpose-read pass covers four k rows x 64 bytes; XORing chunk
-//      bits 2-3 with kr % 4 puts the four rows' 64-byte pieces in the four
-//      quarters of the window.
-__device__ __forceinline__ int swz_b(int kr) { return 4 * (kr & 3); }
+//   k-major: the 16 rows one pass reads must land on 16 distinct 16-byte
+//      bank groups of the 256-byte window: row r's chunks are XORed with
+//      (r / (256/ROW)) % (ROW/16).
+//   index-major: a transpose-read pass covers four k rows x 64 bytes; XORing
+//      chunk bits 2-3 with kr % 4 puts the four rows' 64-byte pieces in the
+//      four quarters of the window (rows of 128 bytes, two to a window: bit 2
+//      with (kr/2) % 2).
+template <int EXT, int BK, bool KMAJ>
+struct HRegion {
+  static constexpr bool K_MAJOR = KMAJ;
+  static constexpr int EXTENT = EXT;
+  static constexpr int ROW = KMAJ ? 2 * BK : 2 * EXT;      // bytes per LDS row
+  static constexpr int CH = ROW / 16;                       // 16-byte chunks per row
+  static constexpr int RPW = ROW >= 256 ? 1 : 256 / ROW;    // rows per 256-byte window
+  static constexpr int READS = KMAJ ? 1 : 2;                // LDS reads per fragment
+  static_assert(KMAJ || ROW >= 128, "index-major rows of at least 128 bytes");
+  static_assert(!KMAJ || (32 % RPW == 0 && (32 / RPW) % CH == 0),
+                "the swizzle repeats every 32 rows");
 
-template <class T>
-__device__ __forceinline__ int swz_a(int r) {
-  return (r / T::RPW) % T::CA;
-}
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (KMAJ) return (row / RPW) % CH;
+    else if constexpr (ROW >= 256) return 4 * (row & 3);
+    else return 4 * ((row >> 1) & 1);
+  }
 
-// Tile-relative (row, column) of the global data behind 16-byte LDS chunk
-// (q, lane) of a slot's A region (row r, k column kc) or B region (k row kr,
-// column nc).
-template <class T>
-__device__ __forceinline__ void a_chunk(int q, int lane, int &r, int &kc) {
-  const int o = q * 1024 + 16 * lane;
-  r = o / T::RA;
-  const int p = (o % T::RA) / 16;
-  kc = 8 * (p ^ swz_a<T>(r));
-}
+  // Tile-relative index and k of the 8 elements behind 16-byte chunk
+  // (q, lane) of the region (lane L of a 1 KB direct load writes bytes
+  // q*1024 + 16L .. +15).
+  __device__ static __forceinline__ void chunk(int q, int lane, int &idx, int &kk) {
+    const int o = q * 1024 + 16 * lane;
+    const int row = o / ROW;
+    const int c = ((o % ROW) / 16) ^ swz(row);
+    if constexpr (KMAJ) {
+      idx = row;
+      kk = 8 * c;
+    } else {
+      kk = row;
+      idx = 8 * c;
+    }
+  }
+};
 
-template <class T>
-__device__ __forceinline__ void b_chunk(int q, int lane, int &kr, int &nc) {
-  const int o = q * 1024 + 16 * lane;
-  kr = o / T::RB;
-  const int p = (o % T::RB) / 16;
-  nc = 8 * (p ^ swz_b(kr));
-}
+// The two regions of tile T when A is stored transposed (TA) and/or B is
+// (TB), and the LDS reads per k sub-step of one wave.
+template <class T, bool TA_, bool TB_>
+struct HLayout {
+  static constexpr bool TA = TA_, TB = TB_;
+  typedef HRegion<T::BM, T::BK, !TA_> RA;
+  typedef HRegion<T::BN, T::BK, TB_> RB;
+  static constexpr int NREAD = T::FM * RA::READS + T::FN * RB::READS;
+};
 
 // ---------------------------------------------------------------- direct loads
 
-// This lane's byte offsets, relative to the tile origin of a K step (A: row
-// m0, column k0; B: row k0, column n0), of the 16-byte chunks it loads.  The
-// offsets do not change from step to step; each step only moves the buffer
-// base.  They fit in 32 bits when BM*lda and BK*ldb are below 2^31, which the
-// kernel checks before taking this path.
+// This lane's byte offsets, relative to the origin of a K step's tile of the
+// operand (the element at index idx0, k k0), of the 16-byte chunks it loads.
+// The offsets do not change from step to step; each step only moves the
+// buffer base.  They fit in 32 bits when EXT*ld (k-major) or BK*ld
+// (index-major) is below 2^31 elements, which the kernel checks before
+// taking this path.
 template <class T>
 struct DirectAddr {
   uint32_t a[T::QA_W];
   uint32_t b[T::QB_W];
 };
 
-template <class T>
+// Offset of the chunk at tile-relative (idx, kk).  Indices past the edge:
+// k-major rows are clamped to the last row (they only feed rows or columns of
+// C that are never stored); index-major chunks to the last whole chunk
+// (ext % 8 == 0 on this path), which also lies inside the matrix.
+template <class R>
+__device__ __forceinline__ uint32_t direct_offset(int idx, int kk, int idx0, int ext, int ld) {
+  int g = idx0 + idx;
+  if constexpr (R::K_MAJOR) {
+    g = g < ext ? g : ext - 1;
+    return 2u * (uint32_t)((g - idx0) * ld + kk);
+  } else {
+    g = g + 8 <= ext ? g : ext - 8;
+    return 2u * (uint32_t)(kk * ld + (g - idx0));
+  }
+}
+
+// First element of a K step's tile of an operand stored with leading
+// dimension ld.
+template <class R>
+__device__ __forceinline__ const uint16_t *tile_base(const void *X, int idx0, int k0, int ld) {
+  const uint16_t *x = static_cast<const uint16_t *>(X);
+  return R::K_MAJOR ? x + (size_t)idx0 * (size_t)ld + k0 : x + (size_t)k0 * (size_t)ld + idx0;
+}
+
+// The direct path's conditions for one operand: 32-bit offsets, and for an
+// index-major operand whose tile crosses the edge, whole chunks up to it.
+template <class R, int BK>
+__device__ __forceinline__ bool direct_ok(bool edge, int ext, int ld) {
+  if constexpr (R::K_MAJOR) return (long long)R::EXTENT * ld < (1LL << 31);
+  else return (!edge || (ext % 8) == 0) && (long long)BK * ld < (1LL << 31);
+}
+
+template <class T, class L>
 __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0,
                                              DirectAddr<T> &d) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j) {
-    int r, kc;
-    a_chunk<T>(wave * T::QA_W + j, lane, r, kc);
-    int gr = m0 + r;
-    gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
-    d.a[j] = 2u * (uint32_t)((gr - m0) * p.lda + kc);
+    int idx, kk;
+    L::RA::chunk(wave * T::QA_W + j, lane, idx, kk);
+    d.a[j] = direct_offset<typename L::RA>(idx, kk, m0, p.M, p.lda);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
-    int kr, nc;
-    b_chunk<T>(wave * T::QB_W + j, lane, kr, nc);
-    int gn = n0 + nc;
-    gn = gn + 8 <= p.N ? gn : p.N - 8;     // N % 8 == 0 here: the last whole chunk
-    d.b[j] = 2u * (uint32_t)(kr * p.ldb + (gn - n0));
+    int idx, kk;
+    L::RB::chunk(wave * T::QB_W + j, lane, idx, kk);
+    d.b[j] = direct_offset<typename L::RB>(idx, kk, n0, p.N, p.ldb);
   }
 }
 
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAddr<T> &d, int m0,
                                              int n0, int k0, uint32_t slot_addr) {
   const int wave = wave_id();
-  const BufRsrc ra =
-      buffer_rsrc(static_cast<const uint16_t *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
-  const BufRsrc rb =
-      buffer_rsrc(static_cast<const uint16_t *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
+  const BufRsrc ra = buffer_rsrc(tile_base<typename L::RA>(p.A, m0, k0, p.lda));
+  const BufRsrc rb = buffer_rsrc(tile_base<typename L::RB>(p.B, n0, k0, p.ldb));
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j)
     buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
@@ -220,42 +276,44 @@ struct RegTile {
   u32x4 b[T::QB_W];
 };
 
+// One chunk of an operand (tile origin idx0, k0) through registers, with 0
+// for every element outside the matrix (index >= ext, k >= K).  `vec`: the
+// operand's rows start 16-byte aligned, so a whole chunk is one load.
+template <class R>
+__device__ __forceinline__ u32x4 staged_chunk(const void *X, int ld, int idx0, int ext, int k0,
+                                              int K, int idx, int kk, bool vec) {
+  const int g = idx0 + idx, gk = k0 + kk;
+  if constexpr (R::K_MAJOR) {
+    const uint16_t *src = static_cast<const uint16_t *>(X) + (size_t)g * (size_t)ld + gk;
+    const bool ok = g < ext;
+    if (ok && gk + 7 < K) return vec ? load8<true>(src) : load8<false>(src);
+    return load8_masked(src, [&](int e) { return ok && gk + e < K; });
+  } else {
+    const uint16_t *src = static_cast<const uint16_t *>(X) + (size_t)gk * (size_t)ld + g;
+    const bool ok = gk < K;
+    if (ok && g + 7 < ext) return vec ? load8<true>(src) : load8<false>(src);
+    return load8_masked(src, [&](int e) { return ok && g + e < ext; });
+  }
+}
+
 // The chunks a direct load would fetch, through registers, with 0 for every
 // element outside the matrix (rows >= M, columns >= N, k >= K).
-template <class T, bool VA, bool VB>
-__device__ __forceinline__ void reg_load(const GemmParams &p, int m0, int n0, int k0,
-                                         RegTile<T> &t) {
-  const uint16_t *A = static_cast<const uint16_t *>(p.A);
-  const uint16_t *B = static_cast<const uint16_t *>(p.B);
+template <class T, class L>
+__device__ __forceinline__ void reg_load(const GemmParams &p, int m0, int n0, int k0, bool va,
+                                         bool vb, RegTile<T> &t) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j) {
-    int r, kc;
-    a_chunk<T>(wave * T::QA_W + j, lane, r, kc);
-    const int gr = m0 + r, gk = k0 + kc;
-    const uint16_t *src = A + (size_t)gr * (size_t)p.lda + gk;
-    const bool row_ok = gr < p.M;
-    if (row_ok && gk + 7 < p.K) {
-      t.a[j] = load8<VA>(src);
-    } else {
-      const int K = p.K;
-      t.a[j] = load8_masked(src, [&](int e) { return row_ok && gk + e < K; });
-    }
+    int idx, kk;
+    L::RA::chunk(wave * T::QA_W + j, lane, idx, kk);
+    t.a[j] = staged_chunk<typename L::RA>(p.A, p.lda, m0, p.M, k0, p.K, idx, kk, va);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
-    int kr, nc;
-    b_chunk<T>(wave * T::QB_W + j, lane, kr, nc);
-    const int gk = k0 + kr, gn = n0 + nc;
-    const uint16_t *src = B + (size_t)gk * (size_t)p.ldb + gn;
-    const bool k_ok = gk < p.K;
-    if (k_ok && gn + 7 < p.N) {
-      t.b[j] = load8<VB>(src);
-    } else {
-      const int N = p.N;
-      t.b[j] = load8_masked(src, [&](int e) { return k_ok && gn + e < N; });
-    }
+    int idx, kk;
+    L::RB::chunk(wave * T::QB_W + j, lane, idx, kk);
+    t.b[j] = staged_chunk<typename L::RB>(p.B, p.ldb, n0, p.N, k0, p.K, idx, kk, vb);
   }
 }
 
@@ -280,48 +338,76 @@ struct Frag {
   f16x8 b[T::FN];
 };
 
-// Per-lane LDS byte offsets of the fragments, relative to a slot.
-template <class T>
-struct FragAddr {
-  int a[T::SUB];   // A block 0 at sub-step s; block bi adds 32*bi*RA
-  int b[T::FN];    // B block bj at sub-step 0, first transpose read
+// Per-lane LDS byte offsets of one operand's fragments, relative to its
+// region.  k-major: one per k sub-step (block 0; block b adds 32*b rows).
+// Index-major: one per block (sub-step 0, first transpose read; sub-step s
+// adds 16*s rows).
+template <class R, int SUB, int NB>
+struct OpAddr {
+  int o[R::K_MAJOR ? SUB : NB];
 };
 
-template <class T>
-__device__ __forceinline__ void frag_setup(int wm0, int wn0, FragAddr<T> &f) {
+template <class T, class L>
+struct FragAddr {
+  OpAddr<typename L::RA, T::SUB, T::FM> a;
+  OpAddr<typename L::RB, T::SUB, T::FN> b;
+};
+
+// v_mfma_f32_32x32x16_f16 takes, in lane l, 8 consecutive k (8h..8h+7,
+// h = l/32) of index l%32 of the block -- the same shape for A (rows) and B
+// (columns).  k-major: one ds_read_b128 of the lane's row.  Index-major: two
+// ds_read_b64_tr_b16, each returning 4 consecutive k of the lane's index from
+// a 4 (k) x 16 (index) block that 16 lanes address: 16-lane group g reads k
+// rows 8*(g/2) + i/4 (+4 for the second read) at indices
+// w0 + 32*b + 16*(g%2) + 4*(i%4) .. +3 (i = lane % 16).
+template <class R, int SUB, int NB>
+__device__ __forceinline__ void op_setup(int w0, OpAddr<R, SUB, NB> &f) {
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32, lh = lane / 32;
-  const int r = wm0 + li;
-  const int sa = swz_a<T>(r);
+  if constexpr (R::K_MAJOR) {
+    const int row = w0 + lane % 32, lh = lane / 32;
+    const int sw = R::swz(row);
 #pragma unroll
-  for (int s = 0; s < T::SUB; ++s) f.a[s] = r * T::RA + 16 * ((2 * s + lh) ^ sa);
-  // B: 16-lane group g reads k rows 8*(g/2) + 4*rd + i/4 and columns
-  // wn0 + 32*bj + 16*(g%2) + 4*(i%4) .. +3 (i = lane % 16).
-  const int g = lane / 16, i = lane % 16;
-  const int kr = 8 * (g / 2) + i / 4;
-  const int t = 2 * (g % 2) + (i % 4) / 2;
-  const int sb = swz_b(kr);
+    for (int s = 0; s < SUB; ++s) f.o[s] = row * R::ROW + 16 * ((2 * s + lh) ^ sw);
+  } else {
+    const int g = lane / 16, i = lane % 16;
+    const int kr = 8 * (g / 2) + i / 4;
+    const int t = 2 * (g % 2) + (i % 4) / 2;
+    const int sw = R::swz(kr);
 #pragma unroll
-  for (int bj = 0; bj < T::FN; ++bj)
-    f.b[bj] = T::A_BYTES + kr * T::RB + 16 * ((wn0 / 8 + 4 * bj + t) ^ sb) + 8 * (i % 2);
+    for (int b = 0; b < NB; ++b) f.o[b] = kr * R::ROW + 16 * ((w0 / 8 + 4 * b + t) ^ sw) + 8 * (i % 2);
+  }
+}
+
+template <class T, class L>
+__device__ __forceinline__ void frag_setup(int wm0, int wn0, FragAddr<T, L> &f) {
+  op_setup(wm0, f.a);
+  op_setup(wn0, f.b);
+}
+
+// Fragment of block b at k sub-step s from an operand region.
+template <class R, int SUB, int NB>
+__device__ __forceinline__ f16x8 op_read(const char *region, const OpAddr<R, SUB, NB> &f, int s,
+                                         int b) {
+  if constexpr (R::K_MAJOR) {
+    return *reinterpret_cast<const f16x8 *>(region + f.o[s] + 32 * b * R::ROW);
+  } else {
+    const char *base = region + f.o[b] + 16 * s * R::ROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 4 * R::ROW));
+    return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 // Fragment reads in the order the MFMAs consume them (A block 0, all B
 // blocks, then A blocks 1..), so the waits before early MFMAs stay short.
-template <class T>
-__device__ __forceinline__ void frag_read(const char *slot, const FragAddr<T> &f, int s,
+template <class T, class L>
+__device__ __forceinline__ void frag_read(const char *slot, const FragAddr<T, L> &f, int s,
                                           Frag<T> &fr) {
-  fr.a[0] = *reinterpret_cast<const f16x8 *>(slot + f.a[s]);
+  fr.a[0] = op_read(slot, f.a, s, 0);
 #pragma unroll
-  for (int bj = 0; bj < T::FN; ++bj) {
-    const char *base = slot + f.b[bj] + 16 * s * T::RB;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 4 * T::RB));
-    fr.b[bj] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
+  for (int bj = 0; bj < T::FN; ++bj) fr.b[bj] = op_read(slot + T::A_BYTES, f.b, s, bj);
 #pragma unroll
-  for (int bi = 1; bi < T::FM; ++bi)
-    fr.a[bi] = *reinterpret_cast<const f16x8 *>(slot + f.a[s] + 32 * bi * T::RA);
+  for (int bi = 1; bi < T::FM; ++bi) fr.a[bi] = op_read(slot, f.a, s, bi);
 }
 
 // MFMAs for block rows [BI0, BI1) of one sub-step.
@@ -519,16 +605,16 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
 // K step is read from `next_slot` into fr[0] between the remaining MFMAs.  On
 // the last K step this reads a stale slot whose values are never used:
 // keeping the reads unconditional keeps the LDS wait counts exact.
-template <class T, class Next>
+template <class T, class L, class Next>
 __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
-                                      const FragAddr<T> &fa, Frag<T> (&fr)[2],
+                                      const FragAddr<T, L> &fa, Frag<T> (&fr)[2],
                                       f32x16 (&acc)[T::FM][T::FN], Next next) {
-  constexpr int NREAD = T::FM + 2 * T::FN;     // LDS instructions per sub-step
+  constexpr int NREAD = L::NREAD;     // LDS instructions per sub-step
   constexpr int HALF = T::FM / 2;
 #pragma unroll
   for (int s = 0; s < T::SUB; ++s) {
     if (s + 1 < T::SUB) {
-      frag_read<T>(slot, fa, s + 1, fr[(s + 1) & 1]);
+      frag_read<T, L>(slot, fa, s + 1, fr[(s + 1) & 1]);
       mfma_rows<T, 0, T::FM>(fr[s & 1], acc);
       interleave_mfma_reads<T::FM * T::FN, NREAD, 4>();
       __builtin_amdgcn_sched_barrier(0);
@@ -536,7 +622,7 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
       mfma_rows<T, 0, HALF>(fr[s & 1], acc);
       __builtin_amdgcn_sched_barrier(0);
       next();
-      frag_read<T>(next_slot, fa, 0, fr[0]);
+      frag_read<T, L>(next_slot, fa, 0, fr[0]);
       mfma_rows<T, HALF, T::FM>(fr[s & 1], acc);
       interleave_mfma_reads<(T::FM - HALF) * T::FN, NREAD, 2>();
       __builtin_amdgcn_sched_barrier(0);
@@ -545,30 +631,30 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
 }
 
 // Direct-load pipeline over STAGES slots: slot j % STAGES holds step j.
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
                                                 uint32_t lds_u32, int wm0, int wn0,
                                                 f32x16 (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr<T> da;
-  direct_setup<T>(p, m0, n0, da);
-  FragAddr<T> fa;
-  frag_setup<T>(wm0, wn0, fa);
+  direct_setup<T, L>(p, m0, n0, da);
+  FragAddr<T, L> fa;
+  frag_setup<T, L>(wm0, wn0, fa);
 
   // Prologue: step 0 (masked, through registers, when it is the partial
   // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile<T> t;
-    reg_load<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_load<T, L>(p, m0, n0, ks.k0(0), true, true, t);
     reg_store<T>(t, lds);
   } else {
-    direct_issue<T>(p, da, m0, n0, ks.k0(0), lds_u32);
+    direct_issue<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
   }
   int issued = 1;
 #pragma unroll
   for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
-      direct_issue<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      direct_issue<T, L>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++issued;
     }
   }
@@ -577,13 +663,13 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
   lds_barrier();
 
   Frag<T> fr[2];
-  frag_read<T>(lds, fa, 0, fr[0]);
+  frag_read<T, L>(lds, fa, 0, fr[0]);
 
   for (int kt = 0; kt < ks.nk; ++kt) {
     const int slot_no = kt % T::STAGES;
     const char *slot = lds + slot_no * T::STAGE_BYTES;
     const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
-    kstep<T>(slot, next_slot, fa, fr, acc, [&]() {
+    kstep<T, L>(slot, next_slot, fa, fr, acc, [&]() {
       // Step kt+1 must have landed (steps issued after it may stay in
       // flight), and this wave's reads of step kt must be complete.  After
       // the last step nothing is in flight and this is a full wait.
@@ -592,46 +678,50 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
       // Every wave has read all of step kt: its slot takes step kt+STAGES.
       const int nx = kt + T::STAGES;
       if (nx < ks.nk) {
-        direct_issue<T>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
+        direct_issue<T, L>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         ++issued;
       }
     });
   }
 }
 
-// Register-staged double-buffered pipeline (unaligned operands, ragged N).
-template <class T, bool VA, bool VB>
+// Register-staged double-buffered pipeline (unaligned operands, ragged
+// edges of index-major operands).
+template <class T, class L>
 __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int n0, char *lds,
-                                                int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+                                                int wm0, int wn0, bool va, bool vb,
+                                                f32x16 (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
-  FragAddr<T> fa;
-  frag_setup<T>(wm0, wn0, fa);
+  FragAddr<T, L> fa;
+  frag_setup<T, L>(wm0, wn0, fa);
   RegTile<T> t;
-  reg_load<T, VA, VB>(p, m0, n0, ks.k0(0), t);
+  reg_load<T, L>(p, m0, n0, ks.k0(0), va, vb, t);
   reg_store<T>(t, lds);
   __syncthreads();
   Frag<T> fr[2];
-  frag_read<T>(lds, fa, 0, fr[0]);
+  frag_read<T, L>(lds, fa, 0, fr[0]);
   for (int kt = 0; kt < ks.nk; ++kt) {
     const char *slot = lds + (kt % 2) * T::STAGE_BYTES;
     char *nslot = lds + ((kt + 1) % 2) * T::STAGE_BYTES;
-    if (kt + 1 < ks.nk) reg_load<T, VA, VB>(p, m0, n0, ks.k0(kt + 1), t);
+    if (kt + 1 < ks.nk) reg_load<T, L>(p, m0, n0, ks.k0(kt + 1), va, vb, t);
     // nslot was last read in step kt-1, before that step's barrier.  On the
     // last step the store repeats old data into a slot nobody reads again.
-    kstep<T>(slot, nslot, fa, fr, acc, [&]() {
+    kstep<T, L>(slot, nslot, fa, fr, acc, [&]() {
       reg_store<T>(t, nslot);
       __syncthreads();
     });
   }
 }
 
+// TA / TB: A is stored transposed (K x M, lda >= M) / B is (N x K, ldb >= K).
 // OUT32: C and the result are fp32 (fp16 inputs); otherwise fp16.
-template <class T, bool VA, bool VB, bool VC, bool OUT32>
+template <class T, bool TA, bool TB, bool VC, bool OUT32>
 __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
+  typedef HLayout<T, TA, TB> L;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   int tm, tn, split;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
-  select_split<uint16_t, float>(p, split);   // split-K passes always write fp32 slabs
+  select_split<uint16_t, float, TA, TB>(p, split);   // split-K passes always write fp32 slabs
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
   const int wave = threadIdx.x / kWave;
@@ -640,15 +730,17 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   f32x16 acc[T::FM][T::FN];
   zero_acc<T>(acc);
 
+  const bool m_edge = m0 + T::BM > p.M;
   const bool n_edge = n0 + T::BN > p.N;
-  const bool direct = VA && VB && (!n_edge || (p.N % 8) == 0) &&
-                      (long long)T::BM * p.lda < (1LL << 31) && (long long)T::BK * p.ldb < (1LL << 31);
-  if (direct) mainloop_direct<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
-  else mainloop_staged<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+  const bool va = (p.vec_ab & 1) != 0, vb = (p.vec_ab & 2) != 0;
+  const bool direct = va && vb && direct_ok<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
+                      direct_ok<typename L::RB, T::BK>(n_edge, p.N, p.ldb);
+  if (direct) mainloop_direct<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+  else mainloop_staged<T, L>(p, m0, n0, lds, wm0, wn0, va, vb, acc);
 
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();   // every wave is done with the pipeline slots
-  const bool edge = n_edge || (m0 + T::BM > p.M);
+  const bool edge = n_edge || m_edge;
   if constexpr (OUT32) {
     if (edge) epilogue_out32<T, VC, true>(p, m0 + wm0, n0 + wn0, lds, acc);
     else epilogue_out32<T, VC, false>(p, m0 + wm0, n0 + wn0, lds, acc);
@@ -694,7 +786,7 @@ static Plan make_plan(const Call &c, const char *name) {
   return pl;
 }
 
-template <class T, bool VA, bool VB, bool VC, bool OUT32>
+template <class T, bool TA, bool TB, bool VC, bool OUT32>
 static hipError_t launch_variant(const Call &c, const Plan &pl) {
   GemmParams p;
   p.A = c.A;
@@ -714,14 +806,15 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.splits = c.splits;
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
-  hipLaunchKernelGGL((hgemm_mfma<T, VA, VB, VC, OUT32>), dim3((unsigned)(pl.blocks * c.splits)),
+  p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  hipLaunchKernelGGL((hgemm_mfma<T, TA, TB, VC, OUT32>), dim3((unsigned)(pl.blocks * c.splits)),
                      dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
 }
 
 template <class T, bool OUT32>
 static hipError_t dispatch_out(const Call &c, const Plan &pl) {
-  const int key = (pl.vec_a > 1 ? 4 : 0) | (pl.vec_b > 1 ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
+  const int key = (c.ta ? 4 : 0) | (c.tb ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
   switch (key) {
     case 0: return launch_variant<T, false, false, false, OUT32>(c, pl);
     case 1: return launch_variant<T, false, false, true, OUT32>(c, pl);

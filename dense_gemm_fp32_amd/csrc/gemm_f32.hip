@@ -36,18 +36,24 @@
 //     column FN*j + bj), so a lane reads FN adjacent floats of one B row per
 //     k, and in the epilogue writes FN adjacent floats of each C row: 32
 //     lanes cover 32*FN contiguous floats, coalesced straight from registers.
+//   * Stored transposed, an operand keeps its stored orientation in LDS
+//     (FRegion): A as K x M is read one float per lane per k slot, B as
+//     N x K with one ds_read_b128 of 4 k per block column (its LDS rows in
+//     the interleaved column order).
 //
 // Edges.  Direct loads cannot substitute zeros, so they only read chunks that
-// lie inside the matrix: A rows past M are clamped to row M-1 (they only feed
-// C rows that are never stored), B column chunks past N are clamped to the
-// last chunk when N % 4 == 0.  The partial K step (K % BK != 0) runs first
-// through registers with per-element masks.  A workgroup whose columns cross
-// an N that is not a multiple of 4, and every workgroup of a call whose A or B
-// is not 16-byte aligned (base or leading dimension; the alignment gate of the
-// SGEMM summary's texture-load variant) or whose BM*lda or BK*ldb reaches
-// 2^30 elements (32-bit load offsets), uses a register-staged path with
-// masked loads (0 outside the matrix; pad elements are never read) into the
-// same LDS layout.  Stores are masked on edge tiles.
+// lie inside the matrix: rows of a k-major operand past its extent (M for A,
+// N for B) are clamped to the last row (they only feed C rows or columns that
+// are never stored); chunks of an index-major operand past its extent are
+// clamped to the last chunk when the extent is a multiple of 4.  The partial K
+// step (K % BK != 0) runs first through registers with per-element masks.  A
+// workgroup whose tile crosses the extent of an index-major operand that is
+// not a multiple of 4, and every workgroup of a call whose A or B is not
+// 16-byte aligned (base or leading dimension; the alignment gate of the SGEMM
+// summary's texture-load variant) or whose offsets would reach 2^30 elements
+// (32-bit load offsets), uses a register-staged path with masked loads (0
+// outside the matrix; pad elements are never read) into the same LDS layout.
+// Stores are masked on edge tiles.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -68,12 +74,8 @@ struct S32Tile {
   static constexpr int FM = WTM / 32;                   // 32x32 blocks per wave (rows)
   static constexpr int FN = WTN / 32;                   // ... (cols) = C columns per lane
   static constexpr int KG = BK / 8;                     // 8-k groups per K step
-  static constexpr int RA = 4 * BK;                     // bytes per A row in LDS
-  static constexpr int CA = BK / 4;                     // 16-byte chunks per A row
-  static constexpr int RPW = RA >= 256 ? 1 : 256 / RA;  // A rows per 256-byte bank window
-  static constexpr int RB = 4 * BN;                     // bytes per B row in LDS
-  static constexpr int A_BYTES = BM * RA;
-  static constexpr int B_BYTES = BK * RB;
+  static constexpr int A_BYTES = BM * BK * 4;           // a slot's A region
+  static constexpr int B_BYTES = BK * BN * 4;           // ... and B region
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int QA = A_BYTES / 1024;             // 1 KB wave loads per A tile
   static constexpr int QB = B_BYTES / 1024;
@@ -96,69 +98,151 @@ template <> struct FVec<1> { typedef float type; };
 template <> struct FVec<2> { typedef f32x2 type; };
 template <> struct FVec<4> { typedef f32x4 type; };
 
-template <class T>
-__device__ __forceinline__ int swz_a32(int r) {
-  return (r / T::RPW) % T::CA;
-}
+// Operand regions.  A slot holds an A region (BM indices m by BK k) and a B
+// region (BN indices n by BK k).  An operand whose memory is k-contiguous (A
+// as stored, or B stored transposed, N x K) sits k-contiguous in LDS too
+// ("k-major": rows of 4*BK bytes, one per index, chunks XOR-swizzled by
+// (r / (256/ROW)) % (ROW/16) so that the 16 rows one 128-bit read pass
+// touches fall in 16 distinct bank groups).  An operand whose memory is
+// index-contiguous (B as stored, or A stored transposed, K x M) sits as in
+// memory ("index-major": rows of 4*EXT bytes, one per k).  Direct loads copy
+// 16-byte chunks, so the LDS orientation follows the memory layout.
+//   * An index-major A is read one float per lane per k: lanes 0-31 read 32
+//     consecutive m of k row kr, lanes 32-63 of row kr+4.  With rows of 256
+//     bytes or more, chunk bit 3 is XORed with bit 2 of the row so that the
+//     two rows' 128-byte pieces fall in different halves of the bank window.
+//   * A k-major B is read in the wave tiles' interleaved column order (lane
+//     column j of block bj is wave column FN*j + bj, so that the epilogue
+//     writes FN adjacent floats per lane).  Its LDS rows therefore hold each
+//     wave tile's columns in that order -- row 32*bj + j of a wave's WT rows
+//     is column FN*j + bj -- so a 16-lane read pass touches 16 consecutive
+//     rows.
+template <int EXT, int BK, bool KMAJ, bool IDX_SWZ, int FN, int WT>
+struct FRegion {
+  static constexpr bool K_MAJOR = KMAJ;
+  static constexpr int EXTENT = EXT;
+  static constexpr int ROW = KMAJ ? 4 * BK : 4 * EXT;      // bytes per LDS row
+  static constexpr int CH = ROW / 16;                       // 16-byte chunks per row
+  static constexpr int RPW = ROW >= 256 ? 1 : 256 / ROW;    // rows per 256-byte window
+  static_assert(!KMAJ || (32 % RPW == 0 && (32 / RPW) % CH == 0),
+                "the swizzle repeats every 32 rows");
+  static_assert(!KMAJ || FN == 1 || WT % (32 * FN) == 0, "wave tiles of whole blocks");
 
-// Tile-relative origin of the global data behind 16-byte LDS chunk (q, lane)
-// of a slot's A region (row r, k column kc) or B region (k row kr, column nc).
-template <class T>
-__device__ __forceinline__ void a_chunk32(int q, int lane, int &r, int &kc) {
-  const int o = q * 1024 + 16 * lane;
-  r = o / T::RA;
-  kc = 4 * (((o % T::RA) / 16) ^ swz_a32<T>(r));
-}
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (KMAJ) return (row / RPW) % CH;
+    else if constexpr (IDX_SWZ && CH >= 16) return 8 * ((row >> 2) & 1);
+    else return 0;
+  }
 
-template <class T>
-__device__ __forceinline__ void b_chunk32(int q, int lane, int &kr, int &nc) {
-  const int o = q * 1024 + 16 * lane;
-  kr = o / T::RB;
-  nc = 4 * ((o % T::RB) / 16);
-}
+  // Index held by LDS row r of a k-major region.
+  __device__ static __forceinline__ int index_of_row(int r) {
+    if constexpr (KMAJ && FN > 1) {
+      const int base = r / WT * WT, rin = r % WT;
+      return base + FN * (rin % 32) + rin / 32;
+    } else {
+      return r;
+    }
+  }
+
+  // Tile-relative index and k of the 4 elements behind 16-byte chunk
+  // (q, lane) of the region (lane L of a 1 KB direct load writes bytes
+  // q*1024 + 16L .. +15).
+  __device__ static __forceinline__ void chunk(int q, int lane, int &idx, int &kk) {
+    const int o = q * 1024 + 16 * lane;
+    const int row = o / ROW;
+    const int c = ((o % ROW) / 16) ^ swz(row);
+    if constexpr (KMAJ) {
+      idx = index_of_row(row);
+      kk = 4 * c;
+    } else {
+      kk = row;
+      idx = 4 * c;
+    }
+  }
+};
+
+// The two regions of tile T when A is stored transposed (TA) and/or B is
+// (TB), and the LDS reads of one wave per 8-k group: k-major A one 128-bit
+// read per block row, index-major A one float per block row and k; B as
+// stored FN adjacent floats per k, k-major B one 128-bit read per block.
+template <class T, bool TA_, bool TB_>
+struct FLayout {
+  static constexpr bool TA = TA_, TB = TB_;
+  typedef FRegion<T::BM, T::BK, !TA_, true, 1, T::WTM> RA;
+  typedef FRegion<T::BN, T::BK, TB_, false, T::FN, T::WTN> RB;
+  static constexpr int NRA = TA_ ? 4 * T::FM : T::FM;
+  static constexpr int NRB = TB_ ? T::FN : 4;
+  static constexpr int NREAD = NRA + NRB;
+};
 
 // ---------------------------------------------------------------- direct loads
 
 template <class T>
 struct DirectAddr32 {
-  uint32_t a[T::QA_W];   // byte offsets from the A tile origin (row m0, column k0)
-  uint32_t b[T::QB_W];   // byte offsets from the B tile origin (row k0, column n0)
+  uint32_t a[T::QA_W];   // byte offsets from the A tile origin of a K step
+  uint32_t b[T::QB_W];   // ... and from the B tile origin
 };
 
+// Offset of the chunk at tile-relative (idx, kk) from the tile origin (index
+// idx0, k k0).  Indices past the edge: k-major rows are clamped to the last
+// row (they only feed rows or columns of C that are never stored);
+// index-major chunks to the last whole chunk (ext % 4 == 0 on this path).
 // The offsets do not change from step to step; each step only moves the
-// buffer base.  They fit in 32 bits when BM*lda and BK*ldb are below 2^30,
-// which the kernel checks before taking this path.
-template <class T>
+// buffer base.  They fit in 32 bits when EXT*ld (k-major) or BK*ld
+// (index-major) is below 2^30 elements, which the kernel checks before
+// taking this path.
+template <class R>
+__device__ __forceinline__ uint32_t direct_offset32(int idx, int kk, int idx0, int ext, int ld) {
+  int g = idx0 + idx;
+  if constexpr (R::K_MAJOR) {
+    g = g < ext ? g : ext - 1;
+    return 4u * (uint32_t)((g - idx0) * ld + kk);
+  } else {
+    g = g + 4 <= ext ? g : ext - 4;
+    return 4u * (uint32_t)(kk * ld + (g - idx0));
+  }
+}
+
+// First element of a K step's tile of an operand with leading dimension ld.
+template <class R>
+__device__ __forceinline__ const float *tile_base32(const void *X, int idx0, int k0, int ld) {
+  const float *x = static_cast<const float *>(X);
+  return R::K_MAJOR ? x + (size_t)idx0 * (size_t)ld + k0 : x + (size_t)k0 * (size_t)ld + idx0;
+}
+
+// The direct path's conditions for one operand: 32-bit offsets, and for an
+// index-major operand whose tile crosses the edge, whole chunks up to it.
+template <class R, int BK>
+__device__ __forceinline__ bool direct_ok32(bool edge, int ext, int ld) {
+  if constexpr (R::K_MAJOR) return (long long)R::EXTENT * ld < (1LL << 30);
+  else return (!edge || (ext % 4) == 0) && (long long)BK * ld < (1LL << 30);
+}
+
+template <class T, class L>
 __device__ __forceinline__ void direct_setup32(const GemmParams &p, int m0, int n0,
                                                DirectAddr32<T> &d) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j) {
-    int r, kc;
-    a_chunk32<T>(wave * T::QA_W + j, lane, r, kc);
-    int gr = m0 + r;
-    gr = gr < p.M ? gr : p.M - 1;          // rows past M only feed unstored rows of C
-    d.a[j] = 4u * (uint32_t)((gr - m0) * p.lda + kc);
+    int idx, kk;
+    L::RA::chunk(wave * T::QA_W + j, lane, idx, kk);
+    d.a[j] = direct_offset32<typename L::RA>(idx, kk, m0, p.M, p.lda);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
-    int kr, nc;
-    b_chunk32<T>(wave * T::QB_W + j, lane, kr, nc);
-    int gn = n0 + nc;
-    gn = gn + 4 <= p.N ? gn : p.N - 4;     // N % 4 == 0 here: the last whole chunk
-    d.b[j] = 4u * (uint32_t)(kr * p.ldb + (gn - n0));
+    int idx, kk;
+    L::RB::chunk(wave * T::QB_W + j, lane, idx, kk);
+    d.b[j] = direct_offset32<typename L::RB>(idx, kk, n0, p.N, p.ldb);
   }
 }
 
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ void direct_issue32(const GemmParams &p, const DirectAddr32<T> &d,
                                                int m0, int n0, int k0, uint32_t slot_addr) {
   const int wave = wave_id();
-  const BufRsrc ra =
-      buffer_rsrc(static_cast<const float *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
-  const BufRsrc rb =
-      buffer_rsrc(static_cast<const float *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
+  const BufRsrc ra = buffer_rsrc(tile_base32<typename L::RA>(p.A, m0, k0, p.lda));
+  const BufRsrc rb = buffer_rsrc(tile_base32<typename L::RB>(p.B, n0, k0, p.ldb));
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j)
     buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
@@ -184,42 +268,48 @@ struct RegTile32 {
   f32x4 b[T::QB_W];
 };
 
+// One chunk of an operand (tile origin idx0, k0) through registers, with 0
+// for every element outside the matrix (index >= ext, k >= K).  `vec`: the
+// operand's rows start 16-byte aligned, so a whole chunk is one load.
+template <class R>
+__device__ __forceinline__ f32x4 staged_chunk32(const void *X, int ld, int idx0, int ext, int k0,
+                                                int K, int idx, int kk, bool vec) {
+  const int g = idx0 + idx, gk = k0 + kk;
+  f32x4 v;
+  if constexpr (R::K_MAJOR) {
+    const float *src = static_cast<const float *>(X) + (size_t)g * (size_t)ld + gk;
+    const bool ok = g < ext;
+    if (ok && gk + 3 < K) return vec ? load4<true>(src) : load4<false>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (ok && gk + e < K) ? src[e] : 0.0f;
+  } else {
+    const float *src = static_cast<const float *>(X) + (size_t)gk * (size_t)ld + g;
+    const bool ok = gk < K;
+    if (ok && g + 3 < ext) return vec ? load4<true>(src) : load4<false>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (ok && g + e < ext) ? src[e] : 0.0f;
+  }
+  return v;
+}
+
 // The chunks the direct loads would fetch, through registers, with 0 for every
 // element outside the matrix (rows >= M, columns >= N, k >= K).
-template <class T, bool VA, bool VB>
-__device__ __forceinline__ void reg_load32(const GemmParams &p, int m0, int n0, int k0,
-                                           RegTile32<T> &t) {
-  const float *A = static_cast<const float *>(p.A);
-  const float *B = static_cast<const float *>(p.B);
+template <class T, class L>
+__device__ __forceinline__ void reg_load32(const GemmParams &p, int m0, int n0, int k0, bool va,
+                                           bool vb, RegTile32<T> &t) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int j = 0; j < T::QA_W; ++j) {
-    int r, kc;
-    a_chunk32<T>(wave * T::QA_W + j, lane, r, kc);
-    const int gr = m0 + r, gk = k0 + kc;
-    const float *src = A + (size_t)gr * (size_t)p.lda + gk;
-    const bool row_ok = gr < p.M;
-    if (row_ok && gk + 3 < p.K) {
-      t.a[j] = load4<VA>(src);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t.a[j][e] = (row_ok && gk + e < p.K) ? src[e] : 0.0f;
-    }
+    int idx, kk;
+    L::RA::chunk(wave * T::QA_W + j, lane, idx, kk);
+    t.a[j] = staged_chunk32<typename L::RA>(p.A, p.lda, m0, p.M, k0, p.K, idx, kk, va);
   }
 #pragma unroll
   for (int j = 0; j < T::QB_W; ++j) {
-    int kr, nc;
-    b_chunk32<T>(wave * T::QB_W + j, lane, kr, nc);
-    const int gk = k0 + kr, gn = n0 + nc;
-    const float *src = B + (size_t)gk * (size_t)p.ldb + gn;
-    const bool k_ok = gk < p.K;
-    if (k_ok && gn + 3 < p.N) {
-      t.b[j] = load4<VB>(src);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t.b[j][e] = (k_ok && gn + e < p.N) ? src[e] : 0.0f;
-    }
+    int idx, kk;
+    L::RB::chunk(wave * T::QB_W + j, lane, idx, kk);
+    t.b[j] = staged_chunk32<typename L::RB>(p.B, p.ldb, n0, p.N, k0, p.K, idx, kk, vb);
   }
 }
 
@@ -244,34 +334,83 @@ struct Frag32 {
   typename FVec<T::FN>::type b[4];      // FN columns at each of the 4 k
 };
 
-// Per-lane LDS byte offsets of the fragments, relative to a slot.
-template <class T>
+// Per-lane LDS byte offsets of the fragments, relative to their region.
+//   A k-major: block row 0 at k group g (block row bi adds 32*bi rows).
+//   A index-major: block row bi at k 0 of the lane's half (k group g adds 8g
+//     rows, k slot s adds s rows).
+//   B as stored: k group 0, k slot 0 (k group g adds 8g rows, slot s adds s).
+//   B k-major: block 0 at k group g (block bj adds 32*bj rows).
+template <class T, class L>
 struct FragAddr32 {
-  int a[T::KG];   // A block row 0 at k group g; block row bi adds 32*bi*RA
-  int b;          // B at k group 0, first k; k group g adds 8*g*RB, k s adds s*RB
+  int a[L::RA::K_MAJOR ? T::KG : T::FM];
+  int b[L::RB::K_MAJOR ? T::KG : 1];
 };
 
-template <class T>
-__device__ __forceinline__ void frag_setup32(int wm0, int wn0, FragAddr32<T> &f) {
+template <class T, class L>
+__device__ __forceinline__ void frag_setup32(int wm0, int wn0, FragAddr32<T, L> &f) {
+  typedef typename L::RA RA;
+  typedef typename L::RB RB;
   const int lane = threadIdx.x % kWave;
   const int li = lane % 32, lh = lane / 32;
-  const int r = wm0 + li;
-  const int sa = swz_a32<T>(r);
+  if constexpr (RA::K_MAJOR) {
+    const int r = wm0 + li;
+    const int sa = RA::swz(r);
 #pragma unroll
-  for (int g = 0; g < T::KG; ++g) f.a[g] = r * T::RA + 16 * ((2 * g + lh) ^ sa);
-  f.b = T::A_BYTES + 4 * lh * T::RB + 4 * (wn0 + T::FN * li);
+    for (int g = 0; g < T::KG; ++g) f.a[g] = r * RA::ROW + 16 * ((2 * g + lh) ^ sa);
+  } else {
+    // rows 8g + 4*lh + s all have the swizzle of row 4*lh
+    const int sa = RA::swz(4 * lh);
+#pragma unroll
+    for (int bi = 0; bi < T::FM; ++bi) {
+      const int m = wm0 + 32 * bi + li;
+      f.a[bi] = 4 * lh * RA::ROW + 16 * ((m / 4) ^ sa) + 4 * (m % 4);
+    }
+  }
+  if constexpr (RB::K_MAJOR) {
+    const int r = wn0 + li;   // LDS row of lane column li of block 0
+    const int sb = RB::swz(r);
+#pragma unroll
+    for (int g = 0; g < T::KG; ++g) f.b[g] = r * RB::ROW + 16 * ((2 * g + lh) ^ sb);
+  } else {
+    f.b[0] = 4 * lh * RB::ROW + 4 * (wn0 + T::FN * li);
+  }
 }
 
-template <class T>
-__device__ __forceinline__ void frag_read32(const char *slot, const FragAddr32<T> &f, int g,
-                                            Frag32<T> &fr) {
+// LDS read number r (0 .. NREAD-1) of k group g: the B reads first (k order
+// for B as stored, block order for a k-major B), then the A reads (block
+// rows; for an index-major A, block row r/4 at k slot r%4).
+template <class T, class L>
+__device__ __forceinline__ void read_item32(int r, const char *slot, const FragAddr32<T, L> &f,
+                                            int g, Frag32<T> &fr) {
+  typedef typename L::RA RA;
+  typedef typename L::RB RB;
   typedef typename FVec<T::FN>::type BVec;
+  const char *rb = slot + T::A_BYTES;
+  if (r < L::NRB) {
+    if constexpr (RB::K_MAJOR) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(rb + f.b[g] + 32 * r * RB::ROW);
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    fr.b[s] = *reinterpret_cast<const BVec *>(slot + f.b + (8 * g + s) * T::RB);
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (T::FN == 1) fr.b[s] = v[s];
+        else fr.b[s][r] = v[s];
+      }
+    } else {
+      fr.b[r] = *reinterpret_cast<const BVec *>(rb + f.b[0] + (8 * g + r) * RB::ROW);
+    }
+  } else {
+    const int q = r - L::NRB;
+    if constexpr (RA::K_MAJOR)
+      fr.a[q] = *reinterpret_cast<const f32x4 *>(slot + f.a[g] + 32 * q * RA::ROW);
+    else
+      fr.a[q / 4][q % 4] = *reinterpret_cast<const float *>(slot + f.a[q / 4] + (8 * g + q % 4) * RA::ROW);
+  }
+}
+
+template <class T, class L>
+__device__ __forceinline__ void frag_read32(const char *slot, const FragAddr32<T, L> &f, int g,
+                                            Frag32<T> &fr) {
 #pragma unroll
-  for (int bi = 0; bi < T::FM; ++bi)
-    fr.a[bi] = *reinterpret_cast<const f32x4 *>(slot + f.a[g] + 32 * bi * T::RA);
+  for (int r = 0; r < L::NREAD; ++r) read_item32<T, L>(r, slot, f, g, fr);
 }
 
 // MFMAs of k slots [S0, S1) of one k group.
@@ -305,16 +444,16 @@ __device__ __forceinline__ void interleave32_slot() {
 // following slot (its barrier wait overlaps those MFMAs), then group 0 of the
 // following step is read from `next_slot` (a stale slot on the last step,
 // never used) between the remaining MFMAs.
-template <class T, class Next>
+template <class T, class L, class Next>
 __device__ __forceinline__ void kstep32(const char *slot, const char *next_slot,
-                                        const FragAddr32<T> &fa, Frag32<T> (&fr)[2],
+                                        const FragAddr32<T, L> &fa, Frag32<T> (&fr)[2],
                                         f32x16 (&acc)[T::FM][T::FN], Next next) {
-  constexpr int NREAD = T::FM + 4;
+  constexpr int NREAD = L::NREAD;
   constexpr int NMF = 4 * T::FM * T::FN;
 #pragma unroll
   for (int g = 0; g < T::KG; ++g) {
     if (g + 1 < T::KG) {
-      frag_read32<T>(slot, fa, g + 1, fr[(g + 1) & 1]);
+      frag_read32<T, L>(slot, fa, g + 1, fr[(g + 1) & 1]);
       mfma_slots<T, 0, 4>(fr[g & 1], acc);
       interleave32_slot<0, NMF, NREAD>();
       __builtin_amdgcn_sched_barrier(0);
@@ -322,7 +461,7 @@ __device__ __forceinline__ void kstep32(const char *slot, const char *next_slot,
       mfma_slots<T, 0, 2>(fr[g & 1], acc);
       __builtin_amdgcn_sched_barrier(0);
       next();
-      frag_read32<T>(next_slot, fa, 0, fr[0]);
+      frag_read32<T, L>(next_slot, fa, 0, fr[0]);
       mfma_slots<T, 2, 4>(fr[g & 1], acc);
       interleave32_slot<0, NMF / 2, NREAD>();
       __builtin_amdgcn_sched_barrier(0);
@@ -332,30 +471,30 @@ __device__ __forceinline__ void kstep32(const char *slot, const char *next_slot,
 
 // ---------------------------------------------------------------- main loops
 
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, int n0, char *lds,
                                                   uint32_t lds_u32, int wm0, int wn0,
                                                   f32x16 (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr32<T> da;
-  direct_setup32<T>(p, m0, n0, da);
-  FragAddr32<T> fa;
-  frag_setup32<T>(wm0, wn0, fa);
+  direct_setup32<T, L>(p, m0, n0, da);
+  FragAddr32<T, L> fa;
+  frag_setup32<T, L>(wm0, wn0, fa);
 
   // Prologue: step 0 (masked, through registers, when it is the partial
   // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile32<T> t;
-    reg_load32<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_load32<T, L>(p, m0, n0, ks.k0(0), true, true, t);
     reg_store32<T>(t, lds);
   } else {
-    direct_issue32<T>(p, da, m0, n0, ks.k0(0), lds_u32);
+    direct_issue32<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
   }
   int issued = 1;
 #pragma unroll
   for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
-      direct_issue32<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      direct_issue32<T, L>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++issued;
     }
   }
@@ -363,13 +502,13 @@ __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, i
   lds_barrier();
 
   Frag32<T> fr[2];
-  frag_read32<T>(lds, fa, 0, fr[0]);
+  frag_read32<T, L>(lds, fa, 0, fr[0]);
 
   for (int kt = 0; kt < ks.nk; ++kt) {
     const int slot_no = kt % T::STAGES;
     const char *slot = lds + slot_no * T::STAGE_BYTES;
     const char *next_slot = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
-    kstep32<T>(slot, next_slot, fa, fr, acc, [&]() {
+    kstep32<T, L>(slot, next_slot, fa, fr, acc, [&]() {
       // Step kt+1 must have landed (steps issued after it may stay in
       // flight), and this wave's reads of step kt must be complete.
       wait_direct<T::LOADS>((issued - 1) - (kt + 1));
@@ -377,7 +516,7 @@ __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, i
       // Every wave has read all of step kt: its slot takes step kt+STAGES.
       const int nx = kt + T::STAGES;
       if (nx < ks.nk) {
-        direct_issue32<T>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
+        direct_issue32<T, L>(p, da, m0, n0, ks.k0(nx), lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         ++issued;
       }
     });
@@ -403,15 +542,15 @@ struct Fill {
   bool live;           // the step exists (index < nk)
 };
 
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ Fill make_fill(const GemmParams &p, const KSteps &ks, int step, int m0,
                                           int n0, uint32_t slot_addr) {
   Fill f;
   f.live = step < ks.nk;
   f.slot_addr = slot_addr;
   const int k0 = f.live ? ks.k0(step) : 0;
-  f.ra = buffer_rsrc(static_cast<const float *>(p.A) + (size_t)m0 * (size_t)p.lda + k0);
-  f.rb = buffer_rsrc(static_cast<const float *>(p.B) + (size_t)k0 * (size_t)p.ldb + n0);
+  f.ra = buffer_rsrc(tile_base32<typename L::RA>(p.A, m0, k0, p.lda));
+  f.rb = buffer_rsrc(tile_base32<typename L::RB>(p.B, n0, k0, p.ldb));
   return f;
 }
 
@@ -425,7 +564,7 @@ __device__ __forceinline__ Fill make_fill(const GemmParams &p, const KSteps &ks,
 // step kt and slots 0 .. NS-3 of step kt+1.  A step's last load is thus issued
 // just before the barrier of the step that follows the one that started it,
 // and is needed STAGES-2 barriers later.
-template <class T>
+template <class T, class L>
 __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, int n0, char *lds,
                                                   uint32_t lds_u32, int wm0, int wn0,
                                                   f32x16 (&acc)[T::FM][T::FN]) {
@@ -433,38 +572,39 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
   static_assert(T::STAGES - 2 <= 3, "vmcnt steps");
   static_assert(T::KG % 2 == 0, "the last k group reads the next step's group 0 into fr[0]");
   constexpr int NS = 4 * T::KG;            // k slots per step
-  constexpr int L = T::LOADS;
-  constexpr int NREAD = T::FM + 4;         // LDS reads per k group
+  constexpr int NL = T::LOADS;
+  constexpr int NREAD = L::NREAD;          // LDS reads per k group
   constexpr int RPS = (NREAD + 3) / 4;     // reads placed after each k slot
+  static_assert(2 * RPS <= 8, "reads per k slot");
   const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr32<T> da;
-  direct_setup32<T>(p, m0, n0, da);
-  FragAddr32<T> fa;
-  frag_setup32<T>(wm0, wn0, fa);
+  direct_setup32<T, L>(p, m0, n0, da);
+  FragAddr32<T, L> fa;
+  frag_setup32<T, L>(wm0, wn0, fa);
   const int wave = wave_id();
 
   if (ks.tail) {
     RegTile32<T> t;
-    reg_load32<T, true, true>(p, m0, n0, ks.k0(0), t);
+    reg_load32<T, L>(p, m0, n0, ks.k0(0), true, true, t);
     reg_store32<T>(t, lds);
   } else {
-    direct_issue32<T>(p, da, m0, n0, ks.k0(0), lds_u32);
+    direct_issue32<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
   }
   int pro = 0;
 #pragma unroll
   for (int j = 1; j < T::STAGES; ++j) {
     if (j < ks.nk) {
-      direct_issue32<T>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
+      direct_issue32<T, L>(p, da, m0, n0, ks.k0(j), lds_u32 + (uint32_t)(j * T::STAGE_BYTES));
       ++pro;
     }
   }
-  wait_direct<L>(pro);
+  wait_direct<NL>(pro);
   lds_barrier();
 
   Frag32<T> fr[2];
-  frag_read32<T>(lds, fa, 0, fr[0]);
+  frag_read32<T, L>(lds, fa, 0, fr[0]);
   // Before the first barrier nothing is being refilled.
-  Fill fill = make_fill<T>(p, ks, ks.nk, m0, n0, 0);
+  Fill fill = make_fill<T, L>(p, ks, ks.nk, m0, n0, 0);
 
   for (int kt = 0; kt < ks.nk; ++kt) {
     const int slot_no = kt % T::STAGES;
@@ -480,10 +620,10 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
         if (kslot == NS - 2) {
           // Publish step kt+1: steps up to kt+STAGES-1 are fully issued.
           const int steps_after = (ks.nk < kt + T::STAGES ? ks.nk : kt + T::STAGES) - kt - 2;
-          wait_direct<L>(steps_after);
+          wait_direct<NL>(steps_after);
           lds_barrier();
-          fill = make_fill<T>(p, ks, kt + T::STAGES, m0, n0,
-                              lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
+          fill = make_fill<T, L>(p, ks, kt + T::STAGES, m0, n0,
+                                 lds_u32 + (uint32_t)(slot_no * T::STAGE_BYTES));
         }
         // LDS reads for the next k group (or the next step's group 0), a
         // few after each k slot's MFMAs.
@@ -493,15 +633,11 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
           const int cnt = last ? 2 * RPS : RPS;
           const char *rs = last ? next_slot : slot;
           const int rg = last ? 0 : g + 1;
-          // Reads in frag_read32's order: B for k 0..3, then A blocks.
+          // Reads in frag_read32's order (read_item32).
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const int r = first + q;
-            if (q < cnt && r < NREAD) {
-              typedef typename FVec<T::FN>::type BVec;
-              if (r < 4) nxt.b[r] = *reinterpret_cast<const BVec *>(rs + fa.b + (8 * rg + r) * T::RB);
-              else nxt.a[r - 4] = *reinterpret_cast<const f32x4 *>(rs + fa.a[rg] + 32 * (r - 4) * T::RA);
-            }
+            if (q < cnt && r < NREAD) read_item32<T, L>(r, rs, fa, rg, nxt);
           }
         }
 #pragma unroll
@@ -517,33 +653,34 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
         // barrier that freed its slot.
         const int gap = kslot >= NS - 2 ? kslot - (NS - 2) : kslot + 2;
 #pragma unroll
-        for (int j = 0; j < L; ++j)
-          if ((j * NS) / L == gap && fill.live) direct_one32<T>(da, j, fill.ra, fill.rb, fill.slot_addr, wave);
+        for (int j = 0; j < NL; ++j)
+          if ((j * NS) / NL == gap && fill.live) direct_one32<T>(da, j, fill.ra, fill.rb, fill.slot_addr, wave);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 }
 
-template <class T, bool VA, bool VB>
+template <class T, class L>
 __device__ __forceinline__ void mainloop_staged32(const GemmParams &p, int m0, int n0, char *lds,
-                                                  int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+                                                  int wm0, int wn0, bool va, bool vb,
+                                                  f32x16 (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
-  FragAddr32<T> fa;
-  frag_setup32<T>(wm0, wn0, fa);
+  FragAddr32<T, L> fa;
+  frag_setup32<T, L>(wm0, wn0, fa);
   RegTile32<T> t;
-  reg_load32<T, VA, VB>(p, m0, n0, ks.k0(0), t);
+  reg_load32<T, L>(p, m0, n0, ks.k0(0), va, vb, t);
   reg_store32<T>(t, lds);
   __syncthreads();
   Frag32<T> fr[2];
-  frag_read32<T>(lds, fa, 0, fr[0]);
+  frag_read32<T, L>(lds, fa, 0, fr[0]);
   for (int kt = 0; kt < ks.nk; ++kt) {
     const char *slot = lds + (kt % 2) * T::STAGE_BYTES;
     char *nslot = lds + ((kt + 1) % 2) * T::STAGE_BYTES;
-    if (kt + 1 < ks.nk) reg_load32<T, VA, VB>(p, m0, n0, ks.k0(kt + 1), t);
+    if (kt + 1 < ks.nk) reg_load32<T, L>(p, m0, n0, ks.k0(kt + 1), va, vb, t);
     // nslot was last read in step kt-1, before that step's barrier.  On the
     // last step the store repeats old data into a slot nobody reads again.
-    kstep32<T>(slot, nslot, fa, fr, acc, [&]() {
+    kstep32<T, L>(slot, nslot, fa, fr, acc, [&]() {
       reg_store32<T>(t, nslot);
       __syncthreads();
     });
@@ -604,12 +741,14 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
   }
 }
 
-template <class T, bool VA, bool VB, bool VC>
+// TA / TB: A is stored transposed (K x M, lda >= M) / B is (N x K, ldb >= K).
+template <class T, bool TA, bool TB, bool VC>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
+  typedef FLayout<T, TA, TB> L;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   int tm, tn, split;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
-  select_split<float, float>(p, split);
+  select_split<float, float, TA, TB>(p, split);
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
   const int wave = wave_id();
@@ -623,18 +762,20 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
 
+  const bool m_edge = m0 + T::BM > p.M;
   const bool n_edge = n0 + T::BN > p.N;
-  const bool direct = VA && VB && (!n_edge || (p.N % 4) == 0) &&
-                      (long long)T::BM * p.lda < (1LL << 30) && (long long)T::BK * p.ldb < (1LL << 30);
+  const bool va = (p.vec_ab & 1) != 0, vb = (p.vec_ab & 2) != 0;
+  const bool direct = va && vb && direct_ok32<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
+                      direct_ok32<typename L::RB, T::BK>(n_edge, p.N, p.ldb);
   if (direct) {
-    if constexpr (T::SPREAD) mainloop_spread32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
-    else mainloop_direct32<T>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+    if constexpr (T::SPREAD) mainloop_spread32<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+    else mainloop_direct32<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
   } else {
-    mainloop_staged32<T, VA, VB>(p, m0, n0, lds, wm0, wn0, acc);
+    mainloop_staged32<T, L>(p, m0, n0, lds, wm0, wn0, va, vb, acc);
   }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-  const bool edge = n_edge || (m0 + T::BM > p.M);
+  const bool edge = n_edge || m_edge;
   if (edge) epilogue32<T, VC, true>(p, m0 + wm0, n0 + wn0, acc);
   else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
 }
@@ -676,7 +817,7 @@ static Plan make_plan(const Call &c, const char *name) {
   return pl;
 }
 
-template <class T, bool VA, bool VB, bool VC>
+template <class T, bool TA, bool TB, bool VC>
 static hipError_t launch_variant(const Call &c, const Plan &pl) {
   GemmParams p;
   p.A = c.A;
@@ -696,7 +837,8 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.splits = c.splits;
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
-  hipLaunchKernelGGL((sgemm_mfma<T, VA, VB, VC>), dim3((unsigned)(pl.blocks * c.splits)),
+  p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  hipLaunchKernelGGL((sgemm_mfma<T, TA, TB, VC>), dim3((unsigned)(pl.blocks * c.splits)),
                      dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
 }
@@ -705,7 +847,7 @@ template <class T>
 static hipError_t dispatch(const Call &c) {
   const Plan pl = make_plan<T>(c, "");
   if (pl.blocks * c.splits > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int key = (pl.vec_a > 1 ? 4 : 0) | (pl.vec_b > 1 ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
+  const int key = (c.ta ? 4 : 0) | (c.tb ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
   switch (key) {
     case 0: return launch_variant<T, false, false, false>(c, pl);
     case 1: return launch_variant<T, false, false, true>(c, pl);

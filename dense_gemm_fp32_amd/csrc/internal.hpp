@@ -19,6 +19,7 @@ struct Call {
   void *C;
   int ldc;
   bool out32;            // fp16 inputs: C and the result are fp32 (else fp16)
+  bool ta, tb;           // A stored transposed (K x M, lda >= M) / B (N x K, ldb >= K)
   bool force_scalar;     // diagnostic: element-wise loads/stores everywhere
   int split_mode;        // 0 = split K by size, 1 = never, >= 2 = that many splits (diagnostic)
   // Set by the launcher for the partial pass of a split-K call (else 1, 0, 0).

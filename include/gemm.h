@@ -179,6 +179,50 @@ int gemm_f16f32_colmajor(int M, int N, int K, float alpha,
                          float beta, float *C, int ldc,
                          void *stream);
 
+/*
+ * Transposed operands, row-major storage: C := alpha * op(A) * op(B) + beta*C
+ * with op(A) M x K and op(B) K x N.  The suffix gives the operations, A's
+ * first: "n" = the operand as stored, "t" = its transpose.
+ *   _nt: A is M x K (lda >= max(1, K)); B is stored N x K (ldb >= max(1, K)),
+ *        op(B) = B^T (element (k, n) of op(B) is B[n*ldb + k]);
+ *   _tn: A is stored K x M (lda >= max(1, M)), op(A) = A^T (element (m, k)
+ *        of op(A) is A[k*lda + m]); B is K x N (ldb >= max(1, N));
+ *   _tt: both stored transposed (lda >= max(1, M), ldb >= max(1, K)).
+ * C is M x N, ldc >= max(1, N).  The SGEMM summary's layout section covers
+ * row-major storage and column-major use (by swapping A and B); these are
+ * BLAS's other operand forms, the transposes, on row-major storage, done
+ * natively: each operand sits in LDS in its stored orientation and the
+ * matrix-core fragments are read from it (no transposed copy is made).  Same
+ * semantics, precisions, accuracy bound, ownership, streams and split-K
+ * behaviour as the plain entry points; the argument checks use the row
+ * lengths above (-6 for lda, -8 for ldb, -11 for ldc, the rest as for
+ * gemm_f32).
+ */
+int gemm_f32_nt(int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+int gemm_f32_tn(int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+int gemm_f32_tt(int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+int gemm_f16_nt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc,
+                void *stream);
+int gemm_f16_tn(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc,
+                void *stream);
+int gemm_f16_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                const gemm_half_t *B, int ldb, float beta, gemm_half_t *C, int ldc,
+                void *stream);
+int gemm_f16f32_nt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc,
+                   void *stream);
+int gemm_f16f32_tn(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc,
+                   void *stream);
+int gemm_f16f32_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int lda,
+                   const gemm_half_t *B, int ldb, float beta, float *C, int ldc,
+                   void *stream);
+
 /* Static, human-readable text for a status code returned above (never NULL). */
 const char *gemm_status_string(int status);
 

@@ -174,3 +174,50 @@ def check_sampled(dtype, w, A, B, C, out, nrows=48, seed=0):
     fb = (1 + u_out) * 4 * K * oracle.U32 * ymag + u_out * np.abs(g64).sum(axis=1) + N * eta
     assert np.all(np.abs(yg - y) <= fb), "Freivalds check failed"
     return worst
+
+
+def layout_case(dtype, M, N, K, ta, tb, lda, ldb, ldc, seed, dist="uniform"):
+    """Stored operands of a transposed-layout call and the logical matrices.
+
+    A is stored K x M (lda >= M) when ta, else M x K; B is stored N x K
+    (ldb >= K) when tb, else K x N.  Pad elements of A and B are NaN (never
+    read), C's pad columns hold the sentinel.  Returns (Abuf, Bbuf, Cbuf,
+    A, B, C) with A (M x K), B (K x N), C (M x N) the logical matrices."""
+    t = "f32" if dtype == "f32" else "f16"
+    tc = "f16" if dtype == "f16" else "f32"
+    sa, sb, sc = seed, seed + 1, seed + 2
+    As = wl.draw(K, M, dist, sa, t) if ta else wl.draw(M, K, dist, sa, t)
+    Bs = wl.draw(N, K, dist, sb, t) if tb else wl.draw(K, N, dist, sb, t)
+    C = wl.draw(M, N, dist, sc, tc)
+    Abuf = wl.pad(As, lda, np.nan)
+    Bbuf = wl.pad(Bs, ldb, np.nan)
+    Cbuf = wl.pad(C, ldc, wl.C_PAD_SENTINEL)
+    A = np.ascontiguousarray(As.T if ta else As)
+    B = np.ascontiguousarray(Bs.T if tb else Bs)
+    return Abuf, Bbuf, Cbuf, A, B, C
+
+
+def run_layout(dtype, layout, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=""):
+    """Call gemm_<dtype>_<layout> (layout "nt", "tn" or "tt") on device
+    copies; returns (status, C buffer after the call).  C's buffer is followed
+    by guard sentinels that must be left intact."""
+    return run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tag=tag + " " + layout,
+               entry="gemm_%s_%s" % (dtype, layout))
+
+
+def check_layout(dtype, M, N, K, alpha, A, B, beta, C, Cbuf, ldc, out, label=""):
+    """Parity of a transposed-layout call's output with the oracle on the
+    logical matrices (row-major copies, lda = K, ldb = N); pad columns of C
+    unchanged.  Returns the worst |err|/tol."""
+    R, G = oracle.gemm(M, N, K, alpha, A.reshape(-1), max(K, 1), B.reshape(-1), max(N, 1), beta,
+                       np.ascontiguousarray(C).reshape(-1) if beta != 0 else None, max(N, 1), dtype)
+    Cv = C.astype(np.float64) if beta != 0 else 0.0
+    tol = oracle.tolerance(G, np.abs(Cv), alpha, beta, K, R, oracle.out_type(dtype))
+    gpu = wl.view(out, M, N, ldc)
+    ok, worst, idx = oracle.compare(gpu, R, tol)
+    if not ok:
+        i, j = idx
+        raise AssertionError("%s: worst |err|/tol = %.3g at (%d, %d): gpu %r oracle %r tol %.3g" %
+                             (label, worst, i, j, gpu[i, j], R[i, j], tol[i, j]))
+    assert_pads_unchanged(out, Cbuf, M, N, ldc, dtype)
+    return worst

@@ -256,3 +256,34 @@ def test_probe_argument_checks():
         assert lib.gemm_probe_mfma(*args, None) == expected, (expected, args)
         assert "probe" in binding.gemm_status_string(expected)
     assert fl.value == -1.0        # no flop count written on a rejected call
+
+
+LAYOUT_CASES = [
+    # (layout, expected, M, N, K, lda, ldb, ldc): the stored row lengths
+    # decide the leading-dimension checks
+    ("nt", 0, 4, 9, 8, 8, 8, 9),        # A M x K (lda >= K), B N x K (ldb >= K)
+    ("nt", -8, 4, 9, 8, 8, 7, 9),
+    ("nt", -6, 4, 9, 8, 7, 8, 9),
+    ("tn", 0, 6, 9, 8, 6, 9, 9),        # A K x M (lda >= M), B K x N (ldb >= N)
+    ("tn", -6, 6, 9, 8, 5, 9, 9),
+    ("tn", -8, 6, 9, 8, 6, 8, 9),
+    ("tt", 0, 6, 9, 8, 6, 8, 9),        # both transposed
+    ("tt", -6, 6, 9, 8, 5, 8, 9),
+    ("tt", -8, 6, 9, 8, 6, 7, 9),
+    ("tt", -11, 6, 9, 8, 6, 8, 8),
+    ("tn", -1, -1, 9, 8, 6, 9, 9),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "f16f32"])
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=[str(i) for i in range(len(LAYOUT_CASES))])
+def test_layout_argument_checks(dt, case):
+    """The transposed-operand entry points check lda and ldb against the
+    row lengths of A and B as stored, before any HIP call.  Successful cases
+    use quick returns (alpha = 0, beta = 1) so nothing is launched."""
+    import dense_gemm_fp32_amd as dg
+    layout, expected, M, N, K, lda, ldb, ldc = case
+    fn = getattr(dg, "gemm_%s_%s" % (dt, layout))
+    assert fn(M, N, K, 0.0, FAKE, lda, FAKE, ldb, 1.0, FAKE, ldc, None) == expected
+    if expected in (-6, -8):
+        assert "stored transposed" in dg.gemm_status_string(expected)

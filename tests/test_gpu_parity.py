@@ -718,3 +718,114 @@ def test_mfma_probe_runs_and_counts(dtype):
     a1, a3 = out1.cpu().double(), out3.cpu().double()
     assert torch.isfinite(a1).all() and torch.isfinite(a3).all()
     assert torch.equal(a3, 3 * a1)
+
+
+# ---------------------------------------------------------------- transposed operands
+
+LAYOUTS = ["nt", "tn", "tt"]
+
+# (M, N, K, pad_a, pad_b, pad_c): row lengths as stored plus the pads.  Pads
+# of 0 or multiples of 8 keep every row 16-byte aligned (direct loads); odd
+# pads force the register-staged path.
+LAYOUT_SHAPES = [
+    (1000, 3000, 517, 13, 5, 3),       # the ragged workload's sizes, unaligned
+    (515, 263, 300, 0, 0, 0),          # tails in M, N and K, aligned
+    (296, 200, 160, 8, 16, 4),         # M, N multiples of 8, padded rows
+    (256, 512, 384, 0, 0, 0),          # whole tiles
+    (33, 17, 1, 0, 0, 0),              # K = 1
+    (7, 130, 45, 1, 0, 2),
+]
+
+
+def _layout_run_check(dtype, layout, M, N, K, pads, seed, alpha=1.5, beta=-0.75, label=""):
+    from gemm_harness import check_layout, layout_case, run_layout
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    lda = (M if ta else K) + pads[0]
+    ldb = (K if tb else N) + pads[1]
+    ldc = N + pads[2]
+    Abuf, Bbuf, Cbuf, A, B, C = layout_case(dtype, M, N, K, ta, tb, lda, ldb, ldc, seed)
+    rc, out = run_layout(dtype, layout, M, N, K, alpha, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc,
+                         label)
+    assert rc == 0, rc
+    return check_layout(dtype, M, N, K, alpha, A, B, beta, C, Cbuf, ldc, out,
+                        "%s %s %s %s" % (label, dtype, layout, (M, N, K)))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_layouts_match_oracle(dtype, layout):
+    """gemm_*_nt / _tn / _tt: operands stored transposed (NaN pads, never
+    read), every tail and both the direct and the register-staged paths,
+    against the oracle on the logical matrices."""
+    for idx, (M, N, K, *pads) in enumerate(LAYOUT_SHAPES):
+        beta = [-0.75, 0.0, 1.0, 0.5][idx % 4]
+        _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_layouts_every_tile(dtype, layout, cfg):
+    """Each tile configuration with transposed operands, on a shape with
+    edge tiles in M and N (multiples of 8: direct loads up to the edge) and
+    one with odd edges (staged loads at the edge)."""
+    with tile_config(cfg):
+        _layout_run_check(dtype, layout, 296, 200, 160, (0, 0, 0), 200 + cfg, label="cfg%d" % cfg)
+        _layout_run_check(dtype, layout, 301, 203, 97, (0, 0, 0), 300 + cfg, beta=0.0,
+                          label="cfg%d" % cfg)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_layouts_split_k(dtype, layout):
+    """Split K with transposed operands: each chunk's operand offsets follow
+    the stored orientation."""
+    with split_mode(3):
+        _layout_run_check(dtype, layout, 200, 136, 1000, (0, 0, 0), 400, label="split3")
+        _layout_run_check(dtype, layout, 129, 77, 515, (3, 1, 2), 401, label="split3 ragged")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_layouts_large_sampled(dtype, layout):
+    """2048^3 with transposed operands on the large tiles (direct loads),
+    checked on sampled rows against the oracle."""
+    from gemm_harness import layout_case, run_layout
+    n = 2048
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    Abuf, Bbuf, Cbuf, A, B, C = layout_case(dtype, n, n, n, ta, tb, n, n, n, 500)
+    rc, out = run_layout(dtype, layout, n, n, n, 1.0, Abuf, n, Bbuf, n, 0.5, Cbuf, n, "large")
+    assert rc == 0
+    rows = wl.sample_rows(n, 32, 7)
+    R, G = oracle.gemm(len(rows), n, n, 1.0, np.ascontiguousarray(A[rows]).reshape(-1), n,
+                       B.reshape(-1), n, 0.5, np.ascontiguousarray(C[rows]).reshape(-1), n, dtype)
+    tol = oracle.tolerance(G, np.abs(C[rows].astype(np.float64)), 1.0, 0.5, n, R,
+                           oracle.out_type(dtype))
+    got = wl.view(out, n, n, n)[rows]
+    ok, worst, where = oracle.compare(np.ascontiguousarray(got), R, tol)
+    assert ok, "%s %s 2048^3 sampled: worst %.3g at %s" % (dtype, layout, worst, where)
+
+
+def test_tensor_wrapper_takes_transposed_views():
+    """dense_gemm_fp32_amd.gemm on X.t() views runs the transposed entry
+    points; the result is within the fp32 accumulation bound of the float64
+    product of the same logical matrices.  A view with neither rows nor
+    columns contiguous is refused."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import note
+    note("tensor wrapper transposed views")
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(5)
+    At = (torch.rand(96, 130, generator=g) * 2 - 1).to(dev)      # stored K x M
+    Bt = (torch.rand(70, 96, generator=g) * 2 - 1).to(dev)       # stored N x K
+    C = torch.zeros(130, 70, device=dev)
+    dg.gemm(At.t(), Bt.t(), C, 1.0, 0.0)
+    torch.cuda.synchronize()
+    A = At.t().contiguous().cpu().double().numpy()
+    B = Bt.t().contiguous().cpu().double().numpy()
+    R = A @ B
+    bound = 4 * 96 * 2.0 ** -24 * (np.abs(A) @ np.abs(B)) + 2.0 ** -24 * np.abs(R) + 1e-30
+    assert np.all(np.abs(C.cpu().double().numpy() - R) <= bound)
+    with pytest.raises(ValueError):
+        dg.gemm(At.t()[::2, ::2], Bt.t()[::2, :], torch.zeros(65, 70, device=dev))
