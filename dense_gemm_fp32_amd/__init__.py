@@ -12,7 +12,7 @@ _LAYOUT_NAMES = tuple("gemm_%s_%s" % (t, l) for t in ("f32", "f16", "f16f32") fo
 _BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
                   "gemm_f16_colmajor",
                   "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe",
-                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma", "gemm", "GemmError",
+                  "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split", "gemm_set_tail_split", "gemm_probe_mfma", "gemm", "GemmError",
                   "LIB_PATH",
                   "EXPORTS", "LAYOUT_NAMES") + _LAYOUT_NAMES
 

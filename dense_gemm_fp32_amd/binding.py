@@ -44,13 +44,16 @@ _lib.gemm_set_tile_config.argtypes = [_I]
 _lib.gemm_set_tile_config.restype = _I
 _lib.gemm_set_split.argtypes = [_I]
 _lib.gemm_set_split.restype = _I
+_lib.gemm_set_tail_split.argtypes = [_I]
+_lib.gemm_set_tail_split.restype = _I
 _lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
                                  ctypes.POINTER(ctypes.c_double), _P]
 _lib.gemm_probe_mfma.restype = _I
 
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
            "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
-           "gemm_set_tile_config", "gemm_set_split", "gemm_probe_mfma") + LAYOUT_NAMES
+           "gemm_set_tile_config", "gemm_set_split", "gemm_set_tail_split",
+           "gemm_probe_mfma") + LAYOUT_NAMES
 
 
 class GemmError(RuntimeError):
@@ -171,6 +174,12 @@ def gemm_probe_mfma(dtype, iters, operands, out, stream=None):
                               out.numel() * out.element_size(), ctypes.byref(flops),
                               _stream(stream))
     return rc, flops.value
+
+
+def gemm_set_tail_split(mode):
+    """fp32: 0 = split the last partly filled round of tiles by size
+    (default), 1 = never, 2..64 = force that many K chunks for it."""
+    return _lib.gemm_set_tail_split(int(mode))
 
 
 def gemm_set_split(mode):

@@ -18,6 +18,7 @@ namespace {
 std::atomic<int> g_load_mode{0};
 std::atomic<int> g_tile_config{0};
 std::atomic<int> g_split_mode{0};
+std::atomic<int> g_tail_mode{0};
 
 // Shared argument checks.  ta / tb: A is stored transposed (K x M, so its
 // rows hold M elements) / B is (N x K, rows of K); otherwise A is M x K and B
@@ -96,6 +97,10 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.splits = 1;
   c.k_chunk = 0;
   c.split_stride = 0;
+  c.tile_base = 0;
+  c.tile_count = 0;
+  c.c_tiles = false;
+  c.tail_mode = g_tail_mode.load(std::memory_order_relaxed);
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -290,6 +295,7 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
         dgemm::Plan p = dtype ? dgemm::plan_f16(c) : dgemm::plan_f32(c);
         char split[48] = "";
         if (p.splits > 1) snprintf(split, sizeof split, " split-K %d", p.splits);
+        else if (p.tail > 1) snprintf(split, sizeof split, " last round split-K %d", p.tail);
         snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s",
                  p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",
                  p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split,
@@ -327,6 +333,11 @@ int gemm_set_load_mode(int mode) {
 int gemm_set_split(int mode) {
   if (mode < 0 || mode > 64) return -1;
   return g_split_mode.exchange(mode);
+}
+
+int gemm_set_tail_split(int mode) {
+  if (mode < 0 || mode > 64) return -1;
+  return g_tail_mode.exchange(mode);
 }
 
 int gemm_set_tile_config(int config) {

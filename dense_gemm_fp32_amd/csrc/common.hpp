@@ -42,6 +42,13 @@ struct GemmParams {
   long long split_stride;  // elements between the slabs of consecutive splits
   // Bit 0: every row of A starts 16-byte aligned (vector loads); bit 1: of B.
   int vec_ab;
+  // A launch may cover part of the tile order: tiles [tile_base, tile_base +
+  // tile_count) of the grouped order (tile_count 0: all of them).  With
+  // c_tiles set, a split-K pass writes each (split, tile) result as a dense
+  // BM x BN fp32 block at C + (split*tile_count + local tile)*BM*BN instead
+  // of into an M x N slab.
+  int tile_base, tile_count;
+  int c_tiles;
 };
 
 // Restrict the kernel arguments to split `s` of a split-K launch: K range
@@ -56,6 +63,19 @@ __device__ __forceinline__ void select_split(GemmParams &p, int s) {
   p.A = static_cast<const TIn *>(p.A) + (TA ? (size_t)kb * (size_t)p.lda : (size_t)kb);
   p.B = static_cast<const TIn *>(p.B) + (TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb);
   p.C = static_cast<TOut *>(p.C) + (size_t)s * (size_t)p.split_stride;
+}
+
+// Tile (tm, tn) at position b of the grouped order (see tile_of_block).
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int &tm,
+                                            int &tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = b / per_group;
+  const int first_m = g * group_m;
+  const int rows_left = tiles_m - first_m;
+  const int gm = rows_left < group_m ? rows_left : group_m;
+  const int in = b - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
 }
 
 // Map a linear workgroup id to a C tile (tm, tn).
@@ -73,24 +93,29 @@ __device__ __forceinline__ void select_split(GemmParams &p, int s) {
 // per K chunk, after one another: the renumbered id gives the split (b / T for
 // T tiles) and the tile within it, so an XCD's range covers tiles of the same
 // K chunk, which share A and B panels.
+//
+// A launch over part of the order (tile_base, tiles) numbers its workgroups
+// the same way over that part.
+// `tiles`: tiles per split in this launch (they start at position tile_base
+// of the grouped order); `local` receives the tile's index among them.
 __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
-                                              int group_m, int &tm, int &tn, int &split) {
+                                              int group_m, int tiles, int tile_base, int &tm,
+                                              int &tn, int &split, int &local) {
   const int xcd = bid % kXcds;
-  const int local = bid / kXcds;
+  const int lid = bid / kXcds;
   const int q = nblocks / kXcds;
   const int r = nblocks % kXcds;
-  int b = xcd * q + (xcd < r ? xcd : r) + local;
-  const int tiles = tiles_m * tiles_n;
+  int b = xcd * q + (xcd < r ? xcd : r) + lid;
   split = b / tiles;
-  b -= split * tiles;
-  const int per_group = group_m * tiles_n;
-  const int g = b / per_group;
-  const int first_m = g * group_m;
-  const int rows_left = tiles_m - first_m;
-  const int gm = rows_left < group_m ? rows_left : group_m;
-  const int in = b - g * per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
+  local = b - split * tiles;
+  tile_coords(tile_base + local, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int group_m, int &tm, int &tn, int &split) {
+  int local;
+  tile_of_block(bid, nblocks, tiles_m, tiles_n, group_m, tiles_m * tiles_n, 0, tm, tn, split,
+                local);
 }
 
 // fp32 -> fp16 with round-to-nearest-even (v_cvt_f16_f32 under the default

@@ -783,6 +783,7 @@ static Plan make_plan(const Call &c, const char *name) {
   const long long tn = (c.N + T::BN - 1) / T::BN;
   pl.blocks = tm * tn;
   pl.splits = 1;
+  pl.tail = 1;
   return pl;
 }
 
@@ -807,6 +808,9 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
   p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  p.tile_base = 0;
+  p.tile_count = 0;
+  p.c_tiles = 0;
   hipLaunchKernelGGL((hgemm_mfma<T, TA, TB, VC, OUT32>), dim3((unsigned)(pl.blocks * c.splits)),
                      dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();

@@ -746,8 +746,10 @@ template <class T, bool TA, bool TB, bool VC>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   typedef FLayout<T, TA, TB> L;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
-  int tm, tn, split;
-  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
+  int tm, tn, split, local;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m,
+                p.tile_count > 0 ? p.tile_count : p.tiles_m * p.tiles_n, p.tile_base, tm, tn, split,
+                local);
   select_split<float, float, TA, TB>(p, split);
   const int m0 = tm * T::BM;
   const int n0 = tn * T::BN;
@@ -775,6 +777,17 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
 
+  if (p.c_tiles) {
+    // Split-K pass over a run of tiles: this (split, tile)'s raw sums fill a
+    // dense BM x BN block of the workspace (rows and columns past the matrix
+    // included; the reduction ignores them).  alpha = 1, beta = 0 here.
+    GemmParams q = p;
+    q.C = static_cast<float *>(p.C) + ((size_t)split * (size_t)p.tile_count + (size_t)local) *
+                                          (size_t)(T::BM * T::BN);
+    q.ldc = T::BN;
+    epilogue32<T, true, false>(q, wm0, wn0, acc);
+    return;
+  }
   const bool edge = n_edge || m_edge;
   if (edge) epilogue32<T, VC, true>(p, m0 + wm0, n0 + wn0, acc);
   else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
@@ -812,8 +825,9 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.vec_c = vc ? T::FN : 1;
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
-  pl.blocks = tm * tn;
+  pl.blocks = c.tile_count > 0 ? c.tile_count : tm * tn;
   pl.splits = 1;
+  pl.tail = 1;
   return pl;
 }
 
@@ -838,6 +852,9 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
   p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  p.tile_base = c.tile_base;
+  p.tile_count = c.tile_count;
+  p.c_tiles = c.c_tiles ? 1 : 0;
   hipLaunchKernelGGL((sgemm_mfma<T, TA, TB, VC>), dim3((unsigned)(pl.blocks * c.splits)),
                      dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
@@ -910,6 +927,7 @@ struct F32Choice {
   F32Cfg cfg;
   int splits;   // wanted K chunks (1 = none); clamp_splits has the last word
   double time;  // estimated seconds
+  int tail;     // K chunks of the last round's tiles (1 = the round runs whole)
 };
 
 // Estimated time of a choice: the product at `score` of the fp32 peak, plus,
@@ -934,8 +952,47 @@ static void try_splits(const Call &c, F32Cfg cfg, double eff, int per_cu, int km
     const int used = (c.K + kc - 1) / kc;
     const double e = cfg == F32Cfg::kTiny ? tiny_eff(kc) : eff;
     const double t = est_time(c, score_of<T>(c, e, per_cu, used), used);
-    if (t < best.time * 0.98) best = F32Choice{cfg, used, t};
+    if (t < best.time * 0.98) best = F32Choice{cfg, used, t, 1};
   }
+}
+
+// The last round.  T tiles fill floor(T/CUs) whole rounds (whole tiles per
+// CU, the busy share's unit); the r = T mod CUs tiles left over would keep r
+// CUs busy for a whole tile's time while the others idle.  Run instead as a
+// split-K pass of S chunks of kc k over the CUs, they cost each CU
+// ceil(r*S/CUs) workgroups of (kc + k0)/K of a tile's time, k0 being a
+// workgroup's prologue and epilogue in k units (measured: ~700 for the large
+// tile, which runs alone on its CU, ~200 for the medium one, whose
+// co-resident workgroups hide most of it), plus a second launch and the
+// reduction of r*S dense fp32 tile blocks.  The medium tile needs two whole
+// rounds first (with one tile per CU its rounds run below the measured
+// efficiency).  The best split is taken when it beats the choice so far by 1%
+// (measured over the 93 sizes of the square sweep, the model's picks gain up
+// to 13% and lose nowhere more than run-to-run variation).
+template <class T>
+static void try_tail(const Call &c, F32Cfg cfg, double eff, int per_cu, int min_rounds, double k0,
+                     F32Choice &best) {
+  const long long tiles = tiles_of<T>(c);
+  const long long full = tiles / kCUs * kCUs;
+  const int rest = (int)(tiles - full);
+  if (full < (long long)min_rounds * kCUs || rest == 0 || rest * 2 > kCUs) return;
+  const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
+  const double whole = (double)tiles / kCUs;   // tiles per CU on average
+  const double simd = simd_share<T>(full, per_cu);
+  F32Choice pick{cfg, 1, 0.0, 1};
+  for (int S = 2; S <= 16; ++S) {
+    const int kc = chunk_of<T>(c, S);
+    if (kc < 128) break;
+    const int used = (c.K + kc - 1) / kc;
+    const long long wgs = (long long)rest * used;
+    const double tail = (double)((wgs + kCUs - 1) / kCUs) * ((double)kc + k0) / (double)c.K;
+    const double busy = whole / ((double)(full / kCUs) + tail);
+    const double extra = (double)wgs * T::BM * T::BN * 4.0 * 2.0 +
+                         (double)rest * T::BM * T::BN * 4.0 * (c.beta != 0.0f ? 2.0 : 1.0);
+    const double t = flops / (eff * busy * simd * 157.3e12) + 8e-6 + extra / 6e12;
+    if (pick.tail == 1 || t < pick.time) pick = F32Choice{cfg, 1, t, used};
+  }
+  if (pick.tail > 1 && pick.time < best.time * 0.99) best = pick;
 }
 
 // Otherwise score = measured throughput at full occupancy (fraction of the
@@ -948,11 +1005,12 @@ static void try_splits(const Call &c, F32Cfg cfg, double eff, int per_cu, int km
 // those whose tiles already fill the CUs stay unsplit).
 static F32Choice choose_f32(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
-  if (c.tile_config == 1) return F32Choice{F32Cfg::kBig, forced, 0.0};
-  if (c.tile_config == 2) return F32Choice{F32Cfg::kMid, forced, 0.0};
-  if (c.tile_config == 3) return F32Choice{F32Cfg::kSmall, forced, 0.0};
-  if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0};
-  if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0};
+  const int tail = c.tail_mode >= 2 && forced == 1 ? c.tail_mode : 1;
+  if (c.tile_config == 1) return F32Choice{F32Cfg::kBig, forced, 0.0, tail};
+  if (c.tile_config == 2) return F32Choice{F32Cfg::kMid, forced, 0.0, tail};
+  if (c.tile_config == 3) return F32Choice{F32Cfg::kSmall, forced, 0.0, tail};
+  if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
+  if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
   const double small = score_of<F32Small>(c, 0.57, 3, 1);
@@ -961,14 +1019,14 @@ static F32Choice choose_f32(const Call &c) {
   if (tiles_of<F32Tiny>(c) <= kCUs) {
     // Problems too small to give every CU even a 32x32 tile are
     // latency-bound: the most workgroups and the shortest prologue win.
-    best = F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1)};
+    best = F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1), 1};
   } else if (big >= mid && big >= small && big >= tiny) {
-    best = F32Choice{F32Cfg::kBig, 1, est_time(c, big, 1)};
+    best = F32Choice{F32Cfg::kBig, 1, est_time(c, big, 1), 1};
   } else if (mid >= small && mid >= tiny) {
-    best = F32Choice{F32Cfg::kMid, 1, est_time(c, mid, 1)};
+    best = F32Choice{F32Cfg::kMid, 1, est_time(c, mid, 1), 1};
   } else {
-    best = small >= tiny ? F32Choice{F32Cfg::kSmall, 1, est_time(c, small, 1)}
-                         : F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1)};
+    best = small >= tiny ? F32Choice{F32Cfg::kSmall, 1, est_time(c, small, 1), 1}
+                         : F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1), 1};
   }
   if (c.split_mode == 0 && c.K >= 1024 && c.K >= (c.M > c.N ? c.M : c.N)) {
     // The large tile runs one workgroup per CU, so nothing overlaps its
@@ -980,6 +1038,12 @@ static F32Choice choose_f32(const Call &c) {
   } else if (c.split_mode >= 2) {
     best.splits = forced;
   }
+  if (c.split_mode == 0 && c.tail_mode == 0) {
+    try_tail<F32Big>(c, F32Cfg::kBig, 0.92, 1, 1, 700.0, best);
+    try_tail<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 2, 200.0, best);
+  } else if (c.tail_mode >= 2 && best.splits == 1) {
+    best.tail = c.tail_mode;
+  }
   // Spread loads pay while a CU holds one workgroup; with several resident
   // the others hide the load bursts and issuing them together is cheaper.
   if (best.cfg == F32Cfg::kMid && tiles_of<F32Mid>(c) * best.splits > kCUs) best.cfg = F32Cfg::kMidB;
@@ -990,8 +1054,71 @@ static F32Choice choose_f32(const Call &c) {
 // of every K chunk write raw fp32 sums to a pooled workspace, then one pass
 // sums the chunks in order and applies alpha and beta.  If the workspace
 // cannot be had the call runs unsplit.
+// The last round's tiles as a split-K pass (try_tail): the whole rounds run
+// as usual, then the r leftover tiles' K chunks write dense fp32 tile blocks
+// to a pooled workspace and a reduction combines them into C.  Returns false
+// (nothing launched) when the split does not apply or the workspace cannot
+// be had; the caller then runs the call whole.
 template <class T>
-static hipError_t launch_cfg(const Call &c, int want) {
+static bool launch_tail(const Call &c, int want, hipError_t *err) {
+  const long long tiles = tiles_of<T>(c);
+  const long long full = tiles / kCUs * kCUs;
+  const int rest = (int)(tiles - full);
+  if (want < 2 || full == 0 || rest == 0 || tiles > 0x7fffffffLL) return false;
+  Call tc = c;
+  tc.tile_base = (int)full;
+  tc.tile_count = rest;
+  int kc = 0;
+  const size_t block = (size_t)T::BM * T::BN;
+  const int S = clamp_splits(tc, want, T::BK, rest, &kc, (long long)rest * (long long)block);
+  if (S <= 1) return false;
+  void *ws = nullptr;
+  if (workspace_alloc(c.stream, (size_t)S * (size_t)rest * block * sizeof(float), &ws) != hipSuccess)
+    return false;
+  Call dc = c;
+  dc.tile_base = 0;
+  dc.tile_count = (int)full;
+  hipError_t e = dispatch<T>(dc);
+  if (e == hipSuccess) {
+    tc.C = ws;
+    tc.ldc = T::BN;
+    tc.alpha = 1.0f;
+    tc.beta = 0.0f;
+    tc.splits = S;
+    tc.k_chunk = kc;
+    tc.split_stride = 0;
+    tc.c_tiles = true;
+    e = dispatch<T>(tc);
+  }
+  if (e == hipSuccess) {
+    TileReduce r;
+    r.W = static_cast<const float *>(ws);
+    r.S = S;
+    r.tiles = rest;
+    r.tile_base = (int)full;
+    r.BM = T::BM;
+    r.BN = T::BN;
+    r.tiles_m = (c.M + T::BM - 1) / T::BM;
+    r.tiles_n = (c.N + T::BN - 1) / T::BN;
+    r.group_m = T::GROUP_M;
+    r.M = c.M;
+    r.N = c.N;
+    r.alpha = c.alpha;
+    r.beta = c.beta;
+    r.C = static_cast<float *>(c.C);
+    r.ldc = c.ldc;
+    r.force_scalar = c.force_scalar;
+    e = launch_tile_reduce(r, c.stream);
+  }
+  const hipError_t f = workspace_free(c.stream, ws);
+  *err = e != hipSuccess ? e : f;
+  return true;
+}
+
+template <class T>
+static hipError_t launch_cfg(const Call &c, int want, int tail = 1) {
+  hipError_t te;
+  if (tail >= 2 && launch_tail<T>(c, tail, &te)) return te;
   int kc = 0;
   const int S = clamp_splits(c, want, T::BK, tiles_of<T>(c), &kc);
   if (S <= 1) return dispatch<T>(c);
@@ -1030,9 +1157,24 @@ static hipError_t launch_cfg(const Call &c, int want) {
 }
 
 template <class T>
-static Plan plan_cfg(const Call &c, const char *name, int want) {
+static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
   Plan pl = make_plan<T>(c, name);
   int kc = 0;
+  pl.tail = 1;
+  if (tail >= 2) {
+    const long long tiles = tiles_of<T>(c), full = tiles / kCUs * kCUs;
+    const int rest = (int)(tiles - full);
+    Call tc = c;
+    tc.tile_base = (int)full;
+    tc.tile_count = rest;
+    if (full > 0 && rest > 0)
+      pl.tail = clamp_splits(tc, tail, T::BK, rest, &kc,
+                             (long long)rest * (long long)(T::BM * T::BN));
+    if (pl.tail > 1) {
+      pl.splits = 1;
+      return pl;
+    }
+  }
   pl.splits = clamp_splits(c, want, T::BK, pl.blocks, &kc);
   return pl;
 }
@@ -1040,22 +1182,22 @@ static Plan plan_cfg(const Call &c, const char *name, int want) {
 Plan plan_f32(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
-    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits);
-    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits);
-    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits);
-    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits);
-    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits);
+    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits, ch.tail);
+    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits, ch.tail);
+    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
+    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits, ch.tail);
+    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits, ch.tail);
   }
 }
 
 hipError_t launch_f32(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
-    case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits);
-    case F32Cfg::kMid: return launch_cfg<F32Mid>(c, ch.splits);
-    case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits);
-    case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits);
-    default: return launch_cfg<F32Tiny>(c, ch.splits);
+    case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits, ch.tail);
+    case F32Cfg::kMid: return launch_cfg<F32Mid>(c, ch.splits, ch.tail);
+    case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits, ch.tail);
+    case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits, ch.tail);
+    default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }
 

@@ -26,6 +26,12 @@ struct Call {
   int splits;
   int k_chunk;
   long long split_stride;
+  // Set by the launcher for a launch over part of the tile order (else 0, 0,
+  // false): tiles [tile_base, tile_base + tile_count) of the grouped order;
+  // c_tiles: the split-K pass writes dense per-(split, tile) blocks.
+  int tile_base, tile_count;
+  bool c_tiles;
+  int tail_mode;         // 0 = split the last round's tiles by size, 1 = never, >= 2 = that many (diagnostic)
   int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
                          // 5 = medium with the loads of a step issued together
   hipStream_t stream;
@@ -39,7 +45,25 @@ struct Plan {
   int vec_a, vec_b, vec_c;   // elements per global access (1 = scalar)
   long long blocks;          // tiles
   int splits;                // K chunks (1 = no split)
+  int tail;                  // K chunks of the last round's tiles (1 = none)
 };
+
+// The reduction pass of a split-K run of tiles: for each of `tiles` tiles
+// (positions tile_base.. of the grouped order over a tiles_m x tiles_n grid
+// of BM x BN tiles), C := alpha * sum_s W[s][tile] + beta * C on the part of
+// the tile inside the M x N matrix; W[s][tile] is a dense BM x BN fp32 block
+// at W + (s*tiles + tile)*BM*BN.  fp32 C.
+struct TileReduce {
+  const float *W;
+  int S, tiles, tile_base;
+  int BM, BN, tiles_m, tiles_n, group_m;
+  int M, N;
+  float alpha, beta;
+  float *C;
+  int ldc;
+  bool force_scalar;
+};
+hipError_t launch_tile_reduce(const TileReduce &r, hipStream_t s);
 
 // The reduction pass of a split-K call: C := alpha * sum_s W_s + beta * C over
 // an M x N matrix, the S slabs of W (fp32, row pitch ldw, `stride` floats
@@ -63,8 +87,10 @@ hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s);
 // Split count for a problem with `tiles` tiles of K step `bk`, given the
 // call's split mode and the heuristic's choice `want` (1 = no split): clamped
 // so every split has at least one K step, the grid stays within range and the
-// workspace under its cap.  Also returns the chunk length.
-int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk);
+// workspace under its cap (ws_elems_per_split floats per split; 0: an M x N
+// slab).  Also returns the chunk length.
+int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk,
+                 long long ws_elems_per_split = 0);
 
 Plan plan_f32(const Call &c);
 Plan plan_f16(const Call &c);

@@ -151,12 +151,78 @@ hipError_t reduce_launch(const SplitReduce &r, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One thread per 4 adjacent columns of a tile row: sum the S dense blocks in
+// order s = 0..S-1, then alpha*sum + beta*C on the elements inside the
+// matrix.  Blocks are BM x BN with BN a multiple of 4, so the 16-byte loads
+// stay inside each block.
+template <bool VEC_C, bool READ_C>
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_tiles(TileReduce r) {
+  const int groups = r.BN / 4;
+  const long long per_tile = (long long)r.BM * groups;
+  const long long total = (long long)r.tiles * per_tile;
+  const size_t block = (size_t)r.BM * (size_t)r.BN;
+  for (long long t = (long long)blockIdx.x * kReduceThreads + threadIdx.x; t < total;
+       t += (long long)gridDim.x * kReduceThreads) {
+    const int lt = (int)(t / per_tile);
+    const int rem = (int)(t - (long long)lt * per_tile);
+    const int i = rem / groups;
+    const int j = 4 * (rem - i * groups);
+    int tm, tn;
+    tile_coords(r.tile_base + lt, r.tiles_m, r.tiles_n, r.group_m, tm, tn);
+    const int row = tm * r.BM + i, col = tn * r.BN + j;
+    if (row >= r.M || col >= r.N) continue;
+    const float *w = r.W + (size_t)lt * block + (size_t)i * r.BN + j;
+    f32x4 sum = *reinterpret_cast<const f32x4 *>(w);
+    for (int s = 1; s < r.S; ++s)
+      sum += *reinterpret_cast<const f32x4 *>(w + (size_t)s * (size_t)r.tiles * block);
+    float *c = r.C + (size_t)row * (size_t)r.ldc + col;
+    if (VEC_C && col + 3 < r.N) {
+      f32x4 o;
+      if (READ_C) {
+        const f32x4 cv = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(r.beta, cv[e], r.alpha * sum[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = r.alpha * sum[e];
+      }
+      *reinterpret_cast<f32x4 *>(c) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= r.N) continue;
+        float o = r.alpha * sum[e];
+        if (READ_C) o = __builtin_fmaf(r.beta, c[e], o);
+        c[e] = o;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_reduce(const TileReduce &r, hipStream_t s) {
+  const long long total = (long long)r.tiles * r.BM * (r.BN / 4);
+  long long blocks = (total + kReduceThreads - 1) / kReduceThreads;
+  if (blocks > kReduceMaxBlocks) blocks = kReduceMaxBlocks;
+  if (blocks < 1) blocks = 1;
+  const bool vec = !r.force_scalar && (r.ldc % 4) == 0 && aligned_to(r.C, 16);
+  const dim3 g((unsigned)blocks), b(kReduceThreads);
+  if (r.beta != 0.0f) {
+    if (vec) hipLaunchKernelGGL((splitk_reduce_tiles<true, true>), g, b, 0, s, r);
+    else hipLaunchKernelGGL((splitk_reduce_tiles<false, true>), g, b, 0, s, r);
+  } else {
+    if (vec) hipLaunchKernelGGL((splitk_reduce_tiles<true, false>), g, b, 0, s, r);
+    else hipLaunchKernelGGL((splitk_reduce_tiles<false, false>), g, b, 0, s, r);
+  }
+  return hipGetLastError();
+}
 
 // Largest workspace a split-K call takes; beyond it the call runs unsplit.
 constexpr long long kWorkspaceCap = 1LL << 30;
 
-int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk) {
+int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk,
+                 long long ws_elems_per_split) {
   *k_chunk = 0;
   int S = c.split_mode == 1 ? 1 : (c.split_mode >= 2 ? c.split_mode : want);
   const int steps = (c.K + bk - 1) / bk;
@@ -167,7 +233,8 @@ int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk)
   if (S < 2) return 1;
   if (tiles * (long long)S > 0x7fffffffLL) return 1;
   const long long ldw = ((long long)c.N + 3) / 4 * 4;
-  if ((long long)S * (long long)c.M * ldw * (long long)sizeof(float) > kWorkspaceCap) return 1;
+  const long long per = ws_elems_per_split > 0 ? ws_elems_per_split : (long long)c.M * ldw;
+  if ((long long)S * per * (long long)sizeof(float) > kWorkspaceCap) return 1;
   *k_chunk = kc;
   return S;
 }

@@ -32,7 +32,11 @@
  *   - Split K: when a problem's tile grid would leave CUs idle, a call may
  *     divide K into S chunks, multiply each chunk into its own fp32 slab of a
  *     workspace, and then form alpha * (slab_0 + ... + slab_{S-1}) + beta * C
- *     in one more pass (same bound; one rounding to the output type).
+ *     in one more pass (same bound; one rounding to the output type).  An
+ *     fp32 call whose tiles fill some whole rounds of the CUs and leave a
+ *     small remainder may do this for the remainder's tiles only (dense
+ *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
+ *     the whole rounds.
  *   - Accuracy: |C_gpu - C_exact| <= 4*K*u*(|alpha|*(|A||B|)_ij + |beta|*|C_ij|)
  *     plus one rounding to the output type, u = 2^-24 (fp32 accumulation).
  *
@@ -268,6 +272,17 @@ int gemm_set_tile_config(int config);
  * value.
  */
 int gemm_set_split(int mode);
+
+/*
+ * Diagnostic switch for tests (fp32 calls): 0 = decide by problem size
+ * whether the last, partly filled round of tiles runs as a split-K pass (the
+ * default; see "Split K" above); 1 = never; 2..64 = split that round's tiles
+ * into that many K chunks whenever the call has more tiles than CUs, is not
+ * split as a whole, and the leftover tiles are at most half the CUs.
+ * Process-wide, like gemm_set_load_mode.  Returns the previous setting, or -1
+ * for an unknown value.
+ */
+int gemm_set_tail_split(int mode);
 
 /*
  * Matrix-core ceiling probe: a measurement aid, not a GEMM.  It bounds what

@@ -200,7 +200,8 @@ def test_tile_table_choice_and_override():
     assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
     assert "split" not in name("f16", 1536)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
-    assert "split-K 2" in name("f32", 5120) and "split" not in name("f32", 8192)
+    # the last round of 5120^3 (1600 tiles: 6 rounds + 64) runs split
+    assert "last round split-K 4" in name("f32", 5120) and "split" not in name("f32", 8192)
     assert "256x128x32" in name("f32", 8192)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
     assert "128x128x32" in name("f16", 2048) and "64x128x32" in name("f16", 512)
@@ -287,3 +288,30 @@ def test_layout_argument_checks(dt, case):
     assert fn(M, N, K, 0.0, FAKE, lda, FAKE, ldb, 1.0, FAKE, ldc, None) == expected
     if expected in (-6, -8):
         assert "stored transposed" in dg.gemm_status_string(expected)
+
+
+def test_tail_split_in_descriptions():
+    """The plan names the split of the last round when the model takes it,
+    and the diagnostic switch turns it off or forces it."""
+    import dense_gemm_fp32_amd as dg
+    n = 4608
+    args = (n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
+    rc, text = dg.gemm_describe("f32", *args)
+    assert rc == 0 and "last round split-K" in text, text
+    prev = dg.gemm_set_tail_split(1)
+    try:
+        rc, text = dg.gemm_describe("f32", *args)
+        assert "last round" not in text, text
+        dg.gemm_set_tail_split(3)
+        rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE,
+                                    4096)
+        assert "last round" not in text, text        # 512 tiles: whole rounds only
+        rc, text = dg.gemm_describe("f32", 4200, 2000, 256, 1.0, FAKE, 256, FAKE, 2000, 0.0, FAKE,
+                                    2000)
+        assert "last round split-K 3" in text, text
+    finally:
+        dg.gemm_set_tail_split(prev)
+    assert dg.gemm_set_tail_split(65) == -1 and dg.gemm_set_tail_split(-1) == -1
+    # the square 4096 workload stays whole: 512 tiles fill two rounds
+    rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
+    assert "split" not in text, text

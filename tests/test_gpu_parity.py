@@ -829,3 +829,73 @@ def test_tensor_wrapper_takes_transposed_views():
     assert np.all(np.abs(C.cpu().double().numpy() - R) <= bound)
     with pytest.raises(ValueError):
         dg.gemm(At.t()[::2, ::2], Bt.t()[::2, :], torch.zeros(65, 70, device=dev))
+
+
+# ---------------------------------------------------------------- split of the last round (fp32)
+
+@contextmanager
+def tail_split(mode):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_tail_split(mode)
+    try:
+        yield
+    finally:
+        dg.gemm_set_tail_split(prev)
+
+
+# (tile config, M, N, K): more tiles than CUs, so whole rounds run first and
+# the leftover tiles (the last ones of the grouped order) run split.
+TAIL_CASES = [
+    (1, 4200, 2000, 256),     # 256x128: 17 x 16 = 272 tiles -> 256 + 16
+    (2, 2200, 1900, 300),     # 128x128: 18 x 15 = 270 tiles -> 256 + 14
+    (3, 1100, 1000, 200),     # 64x64:   18 x 16 = 288 tiles -> 256 + 32
+    (4, 600, 600, 700),       # 32x32:   19 x 19 = 361 tiles -> 256 + 105
+]
+
+
+@pytest.mark.parametrize("S", [2, 5])
+@pytest.mark.parametrize("case", TAIL_CASES, ids=["big", "mid", "small", "tiny"])
+def test_tail_split_matches_oracle(case, S):
+    """The last round's tiles as an S-way split-K pass writing dense tile
+    blocks, then the tile reduction (alpha, beta, edges), after the whole
+    rounds: every element against the oracle, pads and guard untouched, and
+    the same bits on a second call."""
+    cfg, M, N, K = case
+    from gemm_harness import check_layout, layout_case, run_layout
+    for idx, (layout, beta) in enumerate([("nn", 0.5), ("tt", 0.0)]):
+        ta, tb = layout[0] == "t", layout[1] == "t"
+        lda, ldb, ldc = (M if ta else K), (K if tb else N), N + 4
+        Abuf, Bbuf, Cbuf, A, B, C = layout_case("f32", M, N, K, ta, tb, lda, ldb, ldc, 600 + idx)
+        with tile_config(cfg), tail_split(S):
+            if layout == "nn":
+                rc, out = run("f32", M, N, K, 1.25, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc,
+                              tag="tail S=%d cfg%d" % (S, cfg))
+                rc2, out2 = run("f32", M, N, K, 1.25, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc,
+                                tag="tail again")
+                assert rc2 == 0 and np.array_equal(bits(out, "f32"), bits(out2, "f32"))
+            else:
+                rc, out = run_layout("f32", layout, M, N, K, 1.25, Abuf, lda, Bbuf, ldb, beta, Cbuf,
+                                     ldc, "tail S=%d cfg%d" % (S, cfg))
+        assert rc == 0
+        check_layout("f32", M, N, K, 1.25, A, B, beta, C, Cbuf, ldc, out,
+                     "tail S=%d cfg%d %s" % (S, cfg, layout))
+
+
+def test_tail_split_chosen_by_size():
+    """A size whose last round the model splits (4608^3 on the 128x128
+    tile) matches the oracle on sampled rows that include the last tile
+    rows (where the leftover tiles of the grouped order lie)."""
+    import dense_gemm_fp32_amd as dg
+    n = 4608
+    rc, plan = dg.gemm_describe("f32", n, n, n, 1.0, 0x10000, n, 0x10000, n, 1.0, 0x10000, n)
+    assert rc == 0 and "last round split-K" in plan, plan
+    from gemm_harness import layout_case
+    Abuf, Bbuf, Cbuf, A, B, C = layout_case("f32", n, n, n, False, False, n, n, n, 700)
+    rc, out = run("f32", n, n, n, 1.0, Abuf, n, Bbuf, n, 1.0, Cbuf, n, tag="tail by size")
+    assert rc == 0
+    rows = np.unique(np.concatenate([wl.sample_rows(n, 24, 3), np.arange(n - 40, n)]))
+    R, G = oracle.gemm(len(rows), n, n, 1.0, np.ascontiguousarray(A[rows]).reshape(-1), n,
+                       B.reshape(-1), n, 1.0, np.ascontiguousarray(C[rows]).reshape(-1), n, "f32")
+    tol = oracle.tolerance(G, np.abs(C[rows].astype(np.float64)), 1.0, 1.0, n, R, oracle.out_type("f32"))
+    ok, worst, where = oracle.compare(np.ascontiguousarray(wl.view(out, n, n, n)[rows]), R, tol)
+    assert ok, "4608^3 last-round split: worst %.3g at %s" % (worst, where)
