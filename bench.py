@@ -33,6 +33,10 @@ Also reported on the same line:
     holds under matrix-core load, and each GEMM's fraction of it;
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same workload (a subset of output rows).
+
+    python bench.py --table    one JSON row per workload of the pages'
+                               measurements, GPU next to the whole-product oracle
+    python bench.py --sweep    the fp32 square sweep 1024..12800
 """
 import argparse
 import hashlib
@@ -226,6 +230,10 @@ def parse_args():
                     help="length of each measured power window")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--table", action="store_true",
+                    help="one JSON row per workload (fp32 256^3; fp32 512..4096 powers of two; fp16 "
+                         "4096^3; the ragged fp32 and fp16 workloads): GPU replay protocol next to "
+                         "the CPU oracle on the whole product, plus the oracle on one thread at 256^3")
     ap.add_argument("--sweep", action="store_true",
                     help="fp32 size sweep M=N=K=1024..12800 step 128, beta=1, replay protocol "
                          "with cache flush; one JSON row per size")
@@ -258,6 +266,9 @@ def main():
         return
     if args.sweep:
         run_sweep(args, torch, dev, stream)
+        return
+    if args.table:
+        run_table(torch, dev, stream)
         return
 
     def upload(w):
@@ -466,6 +477,75 @@ def run_sweep(args, torch, dev, stream):
                           "pct_of_peak": round(100 * 2.0 * n ** 3 / (mean * 1e-3) / 1e12 / PEAK_F32, 2),
                           "plan": plan}), flush=True)
         del A, B, C
+
+
+def run_table(torch, dev, stream):
+    """Every workload of the pages' measurements on the GPU and on the CPU
+    oracle, one JSON row each.  GPU: the SGEMM summary's replay protocol
+    (floor(1000*exp((1024-n)/3100)) replays with n = round(cbrt(MNK)), a
+    512 MiB flush before each outside the events, mean of the second half).
+    Oracle: the whole product once, timed on all the host cores it uses.
+    Last row: the oracle on one thread at 256^3 (a child process with
+    OMP_NUM_THREADS=1)."""
+    import subprocess
+    import dense_gemm_fp32_amd as dg
+    import oracle
+    import workloads as wl
+    fns = {"f32": dg.gemm_f32, "f16": dg.gemm_f16, "f16f32": dg.gemm_f16f32}
+    peaks = {"f32": PEAK_F32, "f16": PEAK_F16, "f16f32": PEAK_F16}
+    works = [wl.F32_256] + [wl.square(n) for n in (512, 1024, 2048, 4096)] + \
+            [wl.F16_4096, wl.RAGGED_F32, wl.RAGGED_F16]
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    threads = oracle.threads()
+    for w in works:
+        A, B, C = wl.make(w)
+        dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+        fn = fns[w.dtype]
+        n = round((w.M * w.N * w.K) ** (1.0 / 3.0))
+        reps = replay_count(n)
+        rc = fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream)
+        if rc != 0:
+            raise RuntimeError("%s returned %d" % (fn.__name__, rc))
+        times = []
+        for _ in range(reps):
+            flush.zero_()
+            s_ev.record(stream)
+            fn(w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta, dC, w.ldc, stream)
+            e_ev.record(stream)
+            e_ev.synchronize()
+            times.append(s_ev.elapsed_time(e_ev))
+        last = times[len(times) - len(times) // 2:]
+        mean = sum(last) / len(last)
+        rc, plan = dg.gemm_describe(w.dtype, w.M, w.N, w.K, w.alpha, dA, w.lda, dB, w.ldb, w.beta,
+                                    dC, w.ldc)
+        del dA, dB, dC
+        t0 = time.perf_counter()
+        oracle.gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta,
+                    C if w.beta != 0 else None, w.ldc, w.dtype)
+        cpu_s = time.perf_counter() - t0
+        print(json.dumps({
+            "workload": w.name, "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
+            "lda": w.lda, "ldb": w.ldb, "ldc": w.ldc, "alpha": w.alpha, "beta": w.beta,
+            "replays": reps, "averaged": len(last), "gpu_mean_ms": round(mean, 5),
+            "gpu_median_ms": round(sorted(last)[len(last) // 2], 5),
+            "gpu_min_ms": round(min(times), 5),
+            "gpu_tflops": round(w.flops / (mean * 1e-3) / 1e12, 3),
+            "pct_of_peak": round(100.0 * w.flops / (mean * 1e-3) / 1e12 / peaks[w.dtype], 2),
+            "oracle_s": round(cpu_s, 3), "oracle_gflops": round(w.flops / cpu_s / 1e9, 2),
+            "oracle_threads": threads, "gpu_over_oracle": round(cpu_s * 1e3 / mean, 1),
+            "plan": plan}), flush=True)
+    code = ("import sys, time; sys.path.insert(0, %r); import oracle, workloads as wl; "
+            "w = wl.F32_256; A, B, C = wl.make(w); t = time.perf_counter(); "
+            "oracle.gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, None, w.ldc, 'f32'); "
+            "print(time.perf_counter() - t, oracle.threads())" % ROOT)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         check=True).stdout.split()
+    sec, nthr = float(out[0]), int(out[1])
+    print(json.dumps({"workload": "f32_256 oracle on one thread", "oracle_s": round(sec, 4),
+                      "oracle_gflops": round(wl.F32_256.flops / sec / 1e9, 3),
+                      "oracle_threads": nthr}), flush=True)
 
 
 def run_copy_calibration(torch, dev):
