@@ -899,3 +899,62 @@ def test_tail_split_chosen_by_size():
     tol = oracle.tolerance(G, np.abs(C[rows].astype(np.float64)), 1.0, 1.0, n, R, oracle.out_type("f32"))
     ok, worst, where = oracle.compare(np.ascontiguousarray(wl.view(out, n, n, n)[rows]), R, tol)
     assert ok, "4608^3 last-round split: worst %.3g at %s" % (worst, where)
+
+
+def test_concurrent_streams_and_threads_share_the_workspace_pool():
+    """Split-K calls on two streams, issued from two host threads at once,
+    each take their own workspace blocks from the library's pool (requests
+    of different sizes, so the pool grows while the other stream holds a
+    block): every result equals the same call run alone, bit for bit (the
+    chunks are summed in a fixed order)."""
+    import threading
+    import torch
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import note
+    note("concurrent streams and threads: split K 8 and 5 by size, last-round split 3")
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(21)
+    cases = [(512, 520, 4096), (1000, 700, 3000), (4200, 2000, 256)]
+    data = []
+    for M, N, K in cases:
+        A = (torch.rand(M, K, generator=g) * 2 - 1).to(dev)
+        B = (torch.rand(K, N, generator=g) * 2 - 1).to(dev)
+        data.append((M, N, K, A, B))
+    # by size: 128x128 split-K 8, split-K 5; forced: the last round split 3
+    with tail_split(3):
+        for M, N, K, A, B in data:
+            rc, plan = dg.gemm_describe("f32", M, N, K, 1.0, A, K, B, N, 0.0, A, N)
+            assert "split-K" in plan, plan
+        ref = []
+        for M, N, K, A, B in data:
+            C = torch.zeros(M, N, device=dev)
+            assert dg.gemm_f32(M, N, K, 1.0, A, K, B, N, 0.0, C, N, None) == 0
+            torch.cuda.synchronize()
+            ref.append(C.clone())
+        streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+        outs = [[torch.full((M, N), float("nan"), device=dev) for (M, N, K, A, B) in data]
+                for _ in streams]
+        torch.cuda.synchronize()
+        errors = []
+
+        def worker(t):
+            try:
+                for rep in range(6):
+                    for i, (M, N, K, A, B) in enumerate(data[::(1 if t == 0 else -1)]):
+                        j = i if t == 0 else len(data) - 1 - i
+                        rc = dg.gemm_f32(M, N, K, 1.0, A, K, B, N, 0.0, outs[t][j], N, streams[t])
+                        if rc != 0:
+                            errors.append(rc)
+            except Exception as e:          # reported below, on the main thread
+                errors.append(repr(e))
+
+        threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        for t in range(2):
+            for j in range(len(data)):
+                assert torch.equal(outs[t][j], ref[j]), (t, cases[j])
