@@ -903,9 +903,9 @@ static void try_splits16(const Call &c, F16Cfg cfg, double eff, int per_cu, F16C
 // the fastest estimate (est_time16) wins.
 static F16Choice choose_f16(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
-  if (c.tile_config == 1) return F16Choice{F16Cfg::kBig, forced, 0.0};
+  if (c.tile_config == 1 || c.tile_config == 6) return F16Choice{F16Cfg::kBig, forced, 0.0};
   if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
-  if (c.tile_config >= 3) return F16Choice{F16Cfg::kSmall, forced, 0.0};
+  if (c.tile_config == 3 || c.tile_config == 4) return F16Choice{F16Cfg::kSmall, forced, 0.0};
   F16Choice best;
   if (tiles_of<F16Big>(c) >= kCUs / 2)
     best = F16Choice{F16Cfg::kBig, 1, est_time16(c, score16<F16Big>(c, 0.47, 1, 1), 1)};

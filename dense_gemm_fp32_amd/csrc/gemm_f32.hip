@@ -575,7 +575,7 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
   constexpr int NL = T::LOADS;
   constexpr int NREAD = L::NREAD;          // LDS reads per k group
   constexpr int RPS = (NREAD + 3) / 4;     // reads placed after each k slot
-  static_assert(2 * RPS <= 8, "reads per k slot");
+  static_assert(2 * RPS <= 16, "reads per k slot");
   const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr32<T> da;
   direct_setup32<T, L>(p, m0, n0, da);
@@ -635,7 +635,7 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
           const int rg = last ? 0 : g + 1;
           // Reads in frag_read32's order (read_item32).
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
+          for (int q = 0; q < 16; ++q) {
             const int r = first + q;
             if (q < cnt && r < NREAD) read_item32<T, L>(r, rs, fa, rg, nxt);
           }
@@ -799,6 +799,7 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 // L2 group rows), largest first.  A call takes the configuration with the
 // best estimated throughput for its tile count (the size-based kernel choice
 // of the SGEMM summary's results section, retuned for 256 CUs).
+typedef S32Tile<256, 256, 32, 2, 4, 2, 8> F32Huge;       // 8 waves, 128 KB LDS, 1 WG/CU
 typedef S32Tile<256, 128, 32, 4, 2, 3, 8, true> F32Big;  // 8 waves, 144 KB LDS, 1 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8, true> F32Mid;  // 4 waves,  48 KB LDS, 3 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issued together
@@ -882,7 +883,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kBig, kMid, kMidB, kSmall, kTiny };
+enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
@@ -998,7 +999,11 @@ static void try_tail(const Call &c, F32Cfg cfg, double eff, int per_cu, int min_
 // Otherwise score = measured throughput at full occupancy (fraction of the
 // fp32 peak at 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57,
 // and tiny_eff for the 32x32 tile) x the two shares above; the largest score
-// wins.  When K is at least max(M, N) and 1024, K splits of every
+// wins.  The 256x256 tile (two 64 KB slots, no room for a third, so its loads
+// are issued together) measures 1-1.4% ahead of 256x128 when its tiles fill
+// whole rounds exactly -- 4096^3, 8192^3, 12288^3 -- and behind it elsewhere
+// on the sweep (edge tiles waste more of it, and without spread loads it
+// falls back at large K); it is taken only in that case.  When K is at least max(M, N) and 1024, K splits of every
 // configuration are estimated too (est_time; measured
 // winners: 1536^3, 2560^3, 3072^3 and deep-K shapes such as 1024 x 1024 x
 // 8192 take 3-8 chunks of the 128x128 tile; square problems up to 1024 and
@@ -1011,6 +1016,10 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 3) return F32Choice{F32Cfg::kSmall, forced, 0.0, tail};
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
+  if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
+  const bool exact = c.M % F32Huge::BM == 0 && c.N % F32Huge::BN == 0 &&
+                     tiles_of<F32Huge>(c) % kCUs == 0;
+  const double huge = exact ? score_of<F32Huge>(c, 0.93, 1, 1) : 0.0;
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
   const double small = score_of<F32Small>(c, 0.57, 3, 1);
@@ -1020,6 +1029,8 @@ static F32Choice choose_f32(const Call &c) {
     // Problems too small to give every CU even a 32x32 tile are
     // latency-bound: the most workgroups and the shortest prologue win.
     best = F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1), 1};
+  } else if (huge >= big && huge >= mid && huge >= small && huge >= tiny) {
+    best = F32Choice{F32Cfg::kHuge, 1, est_time(c, huge, 1), 1};
   } else if (big >= mid && big >= small && big >= tiny) {
     best = F32Choice{F32Cfg::kBig, 1, est_time(c, big, 1), 1};
   } else if (mid >= small && mid >= tiny) {
@@ -1182,6 +1193,7 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
 Plan plan_f32(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
+    case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots", ch.splits, ch.tail);
     case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
@@ -1193,6 +1205,7 @@ Plan plan_f32(const Call &c) {
 hipError_t launch_f32(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
+    case F32Cfg::kHuge: return launch_cfg<F32Huge>(c, ch.splits, ch.tail);
     case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits, ch.tail);
     case F32Cfg::kMid: return launch_cfg<F32Mid>(c, ch.splits, ch.tail);
     case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits, ch.tail);

@@ -33,7 +33,8 @@ struct Call {
   bool c_tiles;
   int tail_mode;         // 0 = split the last round's tiles by size, 1 = never, >= 2 = that many (diagnostic)
   int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
-                         // 5 = medium with the loads of a step issued together
+                         // 5 = medium with the loads of a step issued together,
+                         // 6 = fp32 256x256 (fp16: its large tile)
   hipStream_t stream;
 };
 

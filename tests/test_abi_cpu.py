@@ -192,7 +192,7 @@ def test_tile_table_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
-    assert "256x128x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
+    assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
     assert "32x32x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
     assert "32x32x32" in name("f32", 64) and "split" not in name("f32", 1024)
     # K split where the grid leaves CUs idle and K is long enough
@@ -202,7 +202,7 @@ def test_tile_table_choice_and_override():
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
     # the last round of 5120^3 (1600 tiles: 6 rounds + 64) runs split
     assert "last round split-K 4" in name("f32", 5120) and "split" not in name("f32", 8192)
-    assert "256x128x32" in name("f32", 8192)
+    assert "256x256x32" in name("f32", 8192) and "256x128x32" in name("f32", 6400)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
     assert "128x128x32" in name("f16", 2048) and "64x128x32" in name("f16", 512)
     prev = dg.gemm_set_tile_config(1)
@@ -210,6 +210,8 @@ def test_tile_table_choice_and_override():
         assert "256x128x32" in name("f32", 256) and "256x256x64" in name("f16", 256)
         dg.gemm_set_tile_config(3)
         assert "64x64x32" in name("f32", 4096)
+        dg.gemm_set_tile_config(6)
+        assert "256x256x32" in name("f32", 256) and "256x256x64" in name("f16", 256)
         dg.gemm_set_tile_config(4)
         assert "32x32x32" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
     finally:

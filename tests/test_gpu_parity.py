@@ -395,7 +395,8 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5], ids=["large", "medium", "small", "tiny", "medium-bunched"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6],
+                         ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -447,7 +448,7 @@ from hypothesis import HealthCheck, given, settings, strategies as st
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
        beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 5]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6]),
        seed=st.integers(0, 2 ** 31 - 1))
 def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed):
     """Random small shapes (every tail residue of every tile size is
@@ -548,7 +549,7 @@ def test_split_k_deterministic_and_paths_agree(dtype):
     assert np.array_equal(bits(o1, dtype), bits(o2, dtype))
     assert np.array_equal(bits(o1, dtype), bits(o3, dtype))
     check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o1, "split det")
-    for cfg in (1, 2, 3, 4):
+    for cfg in (1, 2, 3, 4, 6):
         with split_mode(3), tile_config(cfg):
             rc, o = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split cfg%d" % cfg)
         assert rc == 0
@@ -762,7 +763,7 @@ def test_layouts_match_oracle(dtype, layout):
         _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_layouts_every_tile(dtype, layout, cfg):
@@ -850,11 +851,12 @@ TAIL_CASES = [
     (2, 2200, 1900, 300),     # 128x128: 18 x 15 = 270 tiles -> 256 + 14
     (3, 1100, 1000, 200),     # 64x64:   18 x 16 = 288 tiles -> 256 + 32
     (4, 600, 600, 700),       # 32x32:   19 x 19 = 361 tiles -> 256 + 105
+    (6, 4200, 4200, 256),     # 256x256: 17 x 17 = 289 tiles -> 256 + 33
 ]
 
 
 @pytest.mark.parametrize("S", [2, 5])
-@pytest.mark.parametrize("case", TAIL_CASES, ids=["big", "mid", "small", "tiny"])
+@pytest.mark.parametrize("case", TAIL_CASES, ids=["big", "mid", "small", "tiny", "huge"])
 def test_tail_split_matches_oracle(case, S):
     """The last round's tiles as an S-way split-K pass writing dense tile
     blocks, then the tile reduction (alpha, beta, edges), after the whole
