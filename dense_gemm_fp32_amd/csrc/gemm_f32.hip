@@ -563,15 +563,17 @@ __device__ __forceinline__ Fill make_fill(const GemmParams &p, const KSteps &ks,
 // a few, evenly) follows each of the next NS k slots: slots NS-2 and NS-1 of
 // step kt and slots 0 .. NS-3 of step kt+1.  A step's last load is thus issued
 // just before the barrier of the step that follows the one that started it,
-// and is needed STAGES-2 barriers later.
+// and is needed STAGES-2 barriers later.  With two slots a load is needed at
+// that very barrier, so the loads are spread over the first NS/2 gaps only:
+// the last one then has half a step (thousands of MFMA cycles) to land.
 template <class T, class L>
 __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, int n0, char *lds,
                                                   uint32_t lds_u32, int wm0, int wn0,
                                                   f32x16 (&acc)[T::FM][T::FN]) {
-  static_assert(T::STAGES >= 3, "a load needs a step of lead");
-  static_assert(T::STAGES - 2 <= 3, "vmcnt steps");
+  static_assert(T::STAGES >= 2 && T::STAGES - 2 <= 3, "vmcnt steps");
   static_assert(T::KG % 2 == 0, "the last k group reads the next step's group 0 into fr[0]");
   constexpr int NS = 4 * T::KG;            // k slots per step
+  constexpr int GAPS = T::STAGES >= 3 ? NS : NS / 2;   // gaps the loads are spread over
   constexpr int NL = T::LOADS;
   constexpr int NREAD = L::NREAD;          // LDS reads per k group
   constexpr int RPS = (NREAD + 3) / 4;     // reads placed after each k slot
@@ -654,7 +656,7 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
         const int gap = kslot >= NS - 2 ? kslot - (NS - 2) : kslot + 2;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-          if ((j * NS) / NL == gap && fill.live) direct_one32<T>(da, j, fill.ra, fill.rb, fill.slot_addr, wave);
+          if ((j * GAPS) / NL == gap && fill.live) direct_one32<T>(da, j, fill.ra, fill.rb, fill.slot_addr, wave);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 // L2 group rows), largest first.  A call takes the configuration with the
 // best estimated throughput for its tile count (the size-based kernel choice
 // of the SGEMM summary's results section, retuned for 256 CUs).
-typedef S32Tile<256, 256, 32, 2, 4, 2, 8> F32Huge;       // 8 waves, 128 KB LDS, 1 WG/CU
+typedef S32Tile<256, 256, 32, 2, 4, 2, 8, true> F32Huge; // 8 waves, 128 KB LDS, 1 WG/CU
 typedef S32Tile<256, 128, 32, 4, 2, 3, 8, true> F32Big;  // 8 waves, 144 KB LDS, 1 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8, true> F32Mid;  // 4 waves,  48 KB LDS, 3 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issued together
@@ -999,11 +1001,13 @@ static void try_tail(const Call &c, F32Cfg cfg, double eff, int per_cu, int min_
 // Otherwise score = measured throughput at full occupancy (fraction of the
 // fp32 peak at 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57,
 // and tiny_eff for the 32x32 tile) x the two shares above; the largest score
-// wins.  The 256x256 tile (two 64 KB slots, no room for a third, so its loads
-// are issued together) measures 1-1.4% ahead of 256x128 when its tiles fill
-// whole rounds exactly -- 4096^3, 8192^3, 12288^3 -- and behind it elsewhere
-// on the sweep (edge tiles waste more of it, and without spread loads it
-// falls back at large K); it is taken only in that case.  When K is at least max(M, N) and 1024, K splits of every
+// wins.  Last, an unsplit 256x128 choice gives way to the 256x256 tile
+// (unsplit, or with its own last-round split) when that is estimated no
+// slower at efficiency 0.95: measured over the square sweep (interleaved
+// A/B), it runs 2-3.5% ahead wherever it replaces an unsplit 256x128 call
+// (4096^3 149.5 vs 144.4, 8192^3 151.2 vs 146.7), but falls 2-8% behind
+// where the 256x128 or 128x128 tile has a last-round or whole split that
+// evens out its rounds, so it is offered only in place of the former.  When K is at least max(M, N) and 1024, K splits of every
 // configuration are estimated too (est_time; measured
 // winners: 1536^3, 2560^3, 3072^3 and deep-K shapes such as 1024 x 1024 x
 // 8192 take 3-8 chunks of the 128x128 tile; square problems up to 1024 and
@@ -1017,9 +1021,6 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
-  const bool exact = c.M % F32Huge::BM == 0 && c.N % F32Huge::BN == 0 &&
-                     tiles_of<F32Huge>(c) % kCUs == 0;
-  const double huge = exact ? score_of<F32Huge>(c, 0.93, 1, 1) : 0.0;
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
   const double small = score_of<F32Small>(c, 0.57, 3, 1);
@@ -1029,8 +1030,6 @@ static F32Choice choose_f32(const Call &c) {
     // Problems too small to give every CU even a 32x32 tile are
     // latency-bound: the most workgroups and the shortest prologue win.
     best = F32Choice{F32Cfg::kTiny, 1, est_time(c, tiny, 1), 1};
-  } else if (huge >= big && huge >= mid && huge >= small && huge >= tiny) {
-    best = F32Choice{F32Cfg::kHuge, 1, est_time(c, huge, 1), 1};
   } else if (big >= mid && big >= small && big >= tiny) {
     best = F32Choice{F32Cfg::kBig, 1, est_time(c, big, 1), 1};
   } else if (mid >= small && mid >= tiny) {
@@ -1054,6 +1053,12 @@ static F32Choice choose_f32(const Call &c) {
     try_tail<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 2, 200.0, best);
   } else if (c.tail_mode >= 2 && best.splits == 1) {
     best.tail = c.tail_mode;
+  }
+  if (c.split_mode == 0 && c.tail_mode == 0 && best.cfg == F32Cfg::kBig && best.splits == 1 &&
+      best.tail == 1) {
+    F32Choice h{F32Cfg::kHuge, 1, est_time(c, score_of<F32Huge>(c, 0.95, 1, 1), 1), 1};
+    try_tail<F32Huge>(c, F32Cfg::kHuge, 0.95, 1, 1, 700.0, h);
+    if (h.time <= best.time) best = h;
   }
   // Spread loads pay while a CU holds one workgroup; with several resident
   // the others hide the load bursts and issuing them together is cheaper.
@@ -1193,7 +1198,7 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
 Plan plan_f32(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
-    case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots", ch.splits, ch.tail);
+    case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
