@@ -960,3 +960,20 @@ def test_concurrent_streams_and_threads_share_the_workspace_pool():
         for t in range(2):
             for j in range(len(data)):
                 assert torch.equal(outs[t][j], ref[j]), (t, cases[j])
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(dtype=st.sampled_from(DTYPES), layout=st.sampled_from(LAYOUTS),
+       M=st.integers(1, 300), N=st.integers(1, 300), K=st.integers(1, 300),
+       pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
+       beta=st.sampled_from([0.0, 1.0, -1.5]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 6]),
+       split=st.sampled_from([0, 1, 3]),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, split, seed):
+    """Random small shapes with transposed operands: random row padding
+    (aligned and unaligned), beta, forced tile configurations and splits."""
+    with tile_config(cfg), split_mode(split):
+        _layout_run_check(dtype, layout, M, N, K, pads, seed % 100000, beta=beta,
+                          label="hyp cfg%d split%d" % (cfg, split))
