@@ -899,11 +899,16 @@ static double busy_share(long long tiles) {
 
 // Share of a busy CU's four SIMDs that hold a wave: the workgroups resident
 // on it at once (at most `per_cu`, the LDS limit) times the waves of each.
+// A multi-wave tile built to share its CU (per_cu > 1) runs below its
+// measured efficiency when it is alone there: nothing else hides its load
+// waits (the 128x128 tile at 1792^3..2048^3 with one workgroup per CU ran
+// 5-7% behind the same tile split twice, two per CU).
 template <class T>
 static double simd_share(long long tiles, int per_cu) {
   long long resident = (tiles + kCUs - 1) / kCUs;
   if (resident > per_cu) resident = per_cu;
   const double waves = (double)(resident * T::NWAVES);
+  if (per_cu > 1 && T::NWAVES >= 4 && resident == 1) return 0.88;
   return waves >= 4.0 ? 1.0 : waves / 4.0;
 }
 
@@ -935,7 +940,8 @@ struct F32Choice {
 
 // Estimated time of a choice: the product at `score` of the fp32 peak, plus,
 // when K is split S ways, the extra pass: a few microseconds to launch and S
-// fp32 slabs of M x N written and read back at ~6 TB/s (the writes overlap the product).
+// fp32 slabs of M x N written and read back at ~6 TB/s (the writes overlap the
+// product).
 static double est_time(const Call &c, double score, int splits) {
   const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
   double t = flops / (score * 157.3e12);
@@ -1042,7 +1048,7 @@ static F32Choice choose_f32(const Call &c) {
     // The large tile runs one workgroup per CU, so nothing overlaps its
     // prologue and epilogue: it needs longer chunks than the others.
     try_splits<F32Big>(c, F32Cfg::kBig, 0.92, 1, 1024, best);
-    try_splits<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 384, best);
+    try_splits<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 256, best);
     try_splits<F32Small>(c, F32Cfg::kSmall, 0.57, 3, 1024, best);
     try_splits<F32Tiny>(c, F32Cfg::kTiny, 0.63, 6, 1024, best);
   } else if (c.split_mode >= 2) {

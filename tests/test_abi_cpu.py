@@ -193,8 +193,10 @@ def test_tile_table_choice_and_override():
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
     assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
-    assert "32x32x32" in name("f32", 1024) and "32x32x32" in name("f32", 256)
-    assert "32x32x32" in name("f32", 64) and "split" not in name("f32", 1024)
+    # 1024^3: four K chunks of the 128x128 tile beat 1024 one-wave 32x32 tiles
+    assert "128x128x16" in name("f32", 1024) and "split-K 4" in name("f32", 1024)
+    assert "32x32x32" in name("f32", 256) and "32x32x32" in name("f32", 64)
+    assert "split" not in name("f32", 256) and "split" not in name("f32", 768)
     # K split where the grid leaves CUs idle and K is long enough
     assert "128x128x16" in name("f32", 1536) and "split-K 3" in name("f32", 1536)
     assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
