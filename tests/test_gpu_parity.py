@@ -977,3 +977,48 @@ def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, sp
     with tile_config(cfg), split_mode(split):
         _layout_run_check(dtype, layout, M, N, K, pads, seed % 100000, beta=beta,
                           label="hyp cfg%d split%d" % (cfg, split))
+
+
+def test_calls_replay_from_a_captured_graph():
+    """Library calls captured into a HIP graph (torch.cuda.CUDAGraph on a
+    side stream) -- unsplit fp32 and fp16, a whole split K, a last-round
+    split, whose workspace becomes an allocation node of the graph -- replay
+    the eager results bit for bit, several times, with eager GEMMs and
+    synchronisations between the replays."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import note
+    note("graph capture: unsplit f32/f16, split K 4, last-round split 3")
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(9)
+    cases = [("f32", 1000, 700, 3000, 1, 1), ("f16", 600, 520, 1000, 1, 1),
+             ("f32", 1000, 700, 3000, 4, 1), ("f32", 4200, 2000, 256, 1, 3)]
+    for dtype, M, N, K, split, tail in cases:
+        t = torch.float32 if dtype == "f32" else torch.float16
+        fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_f16
+        A = (torch.rand(M, K, generator=g) * 2 - 1).to(t).to(dev)
+        B = (torch.rand(K, N, generator=g) * 2 - 1).to(t).to(dev)
+        C0 = (torch.rand(M, N, generator=g) * 2 - 1).to(t).to(dev)
+        with split_mode(split), tail_split(tail):
+            ref = C0.clone()
+            assert fn(M, N, K, 1.25, A, K, B, N, 0.5, ref, N, None) == 0
+            torch.cuda.synchronize()
+            C = C0.clone()
+            s = torch.cuda.Stream(device=dev)
+            graph = torch.cuda.CUDAGraph()
+            s.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(s):
+                graph.capture_begin()
+                rc = fn(M, N, K, 1.25, A, K, B, N, 0.5, C, N, s)
+                graph.capture_end()
+            torch.cuda.synchronize()
+            assert rc == 0
+            for rep in range(3):
+                C.copy_(C0)
+                other = torch.zeros(M, N, dtype=t, device=dev)
+                assert fn(M, N, K, 1.0, A, K, B, N, 0.0, other, N, None) == 0   # eager work between
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(C, ref), (dtype, M, N, K, split, tail, rep)
+            del graph
