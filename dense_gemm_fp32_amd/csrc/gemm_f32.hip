@@ -15,11 +15,14 @@
 // wait overlaps them; by then every wave has read all of step kt, so step
 // kt's slot can take step kt+STAGES.  The multi-wave tiles spread that step's
 // loads over the following k slots, one between each group of MFMAs
-// (mainloop_spread32): issued all at once they fill the load queue, and the
-// wave that blocks on a full queue also stops issuing MFMAs.  The one-wave
-// tiles, which share a CU with other workgroups, issue them together
-// (mainloop_direct32).  Each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile
-// held as FM x FN blocks of 32x32 accumulators.
+// (mainloop_spread32; with two slots over the first half of the next step):
+// issued all at once they fill the load queue, and the wave that blocks on a
+// full queue also stops issuing MFMAs.  The one-wave tiles, which share a CU
+// with other workgroups, issue them together (mainloop_direct32).  Each wave
+// owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as FM x FN blocks of 32x32
+// accumulators.  A launch may cover part of the tile order, and its split-K
+// pass may write dense per-tile blocks (the last-round split; see
+// launch_tail).
 //
 // Operand layout.  For v_mfma_f32_32x32x2_f32 lane l supplies A(row l%32,
 // k-slot l/32) and B(k-slot l/32, col l%32) and receives C(row
