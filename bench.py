@@ -61,13 +61,38 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 from dense_gemm_fp32_amd.model import replay_count  # noqa: E402
 
 
+def _code_only(text):
+    """C++ source without comments or whitespace (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            if not text[i].isspace():
+                out.append(text[i])
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and layout excluded), so
+    that a committed counter summary stays valid across comment edits."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_fp32_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
