@@ -79,10 +79,15 @@ def check_m0_only_in_asm(src):
 def build(verbose=False):
     """Compile all sources and link libgemm.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    for src in M0_ASM_SOURCES:
-        check_m0_only_in_asm(src)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    # The m0 checks and the object compiles are independent hipcc runs: run
+    # them side by side (the two kernel sources dominate the build time).
+    workers = min(os.cpu_count() or 4, len(SOURCES) + len(M0_ASM_SOURCES), 16)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        checks = [ex.submit(check_m0_only_in_asm, src) for src in M0_ASM_SOURCES]
+        compiles = [ex.submit(_compile, src, verbose) for src in SOURCES]
+        for f in checks:
+            f.result()
+        objs = [f.result() for f in compiles]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
