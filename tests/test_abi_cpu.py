@@ -183,9 +183,11 @@ def test_only_inline_asm_touches_m0():
     """The fp16 kernel sets m0 in inline assembly; no compiler-generated
     instruction of that translation unit may use m0 (checked on the gfx950
     assembly of the current source)."""
+    import concurrent.futures
     from dense_gemm_fp32_amd import build as b
-    for src in b.M0_ASM_SOURCES:
-        b.check_m0_only_in_asm(src)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(b.M0_ASM_SOURCES)) as ex:
+        for f in [ex.submit(b.check_m0_only_in_asm, src) for src in b.M0_ASM_SOURCES]:
+            f.result()
 
 
 def test_tile_table_choice_and_override():
