@@ -72,6 +72,11 @@ struct S32Tile {
   static constexpr int GROUP_M = GROUP_M_;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * kWave;
+  // Epilogue: load a block's 16 rows of C before storing any of them.  It
+  // costs registers, which the multi-wave tiles that share their CU (loads
+  // issued together) need for their occupancy; their neighbours hide the
+  // epilogue's memory latency instead.
+  static constexpr bool C_BATCH = SPREAD || NWAVES == 1;
   static constexpr int WTM = BM / WAVES_M;              // wave tile rows
   static constexpr int WTN = BN / WAVES_N;              // wave tile columns
   static constexpr int FM = WTM / 32;                   // 32x32 blocks per wave (rows)
@@ -708,6 +713,18 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
   const bool cols_ok = !CHECK || col + T::FN - 1 < p.N;
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi) {
+    // With C_BATCH the block's 16 rows of C are all loaded before the first
+    // store: a load placed after a store to the same array cannot be moved
+    // above it, so interleaved they wait out one memory latency per row.
+    CVec cin[16];
+    if (T::C_BATCH && VEC_C && cols_ok && beta != 0.0f) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + 32 * bi + 8 * (r / 4) + 4 * lh + (r % 4);
+        if (!CHECK || row < p.M)
+          cin[r] = *reinterpret_cast<const CVec *>(C + (size_t)row * (size_t)p.ldc + col);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = r0 + 32 * bi + 8 * (r / 4) + 4 * lh + (r % 4);
@@ -719,7 +736,7 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
       if (VEC_C && cols_ok) {
         CVec o;
         if (beta != 0.0f) {
-          CVec cv = *reinterpret_cast<const CVec *>(dst);
+          const CVec cv = T::C_BATCH ? cin[r] : *reinterpret_cast<const CVec *>(dst);
           if constexpr (T::FN == 1) o = __builtin_fmaf(beta, cv, v[0]);
           else {
 #pragma unroll
