@@ -1024,6 +1024,48 @@ static void try_tail(const Call &c, F32Cfg cfg, double eff, int per_cu, int min_
   if (pick.tail > 1 && pick.time < best.time * 0.99) best = pick;
 }
 
+// Calls with an operand that cannot take 16-byte loads (leading dimension or
+// base not a multiple of 4 floats) run the register-staged, element-wise load
+// path, whose workgroups wait on their loads much longer than the direct
+// path's, so the estimate above does not hold for them.  Measured on seven
+// such shapes (interleaved, every tile and split): the 128x128 tile alone on
+// a CU, or two or three sharing it, each cost about 0.106, 0.175 and 0.221
+// us per k of work, plus a fixed ~110 k (alone) or ~44 k (shared) for the
+// prologue and epilogue; the other tiles ran behind it.  The chosen K split
+// S (1..8, chunks of at least 128 k) minimises the busiest CU's time, its
+// workgroups taken in groups of three, plus the split's second pass
+// (S fp32 slabs written and read, C read and written, at ~5 TB/s).  Against
+// the direct-path estimate: 1000x3000x517 +15%, 2000x2000x1000 +15%,
+// 3000^3 +10%, 1500^3 +10%, 1000^3 +41%, 517x3000x1000 +89%.  Grids of three
+// or more 128x128 tiles per CU keep the direct-path choice: there the large
+// tiles, staged, run ahead (4096^3 126 against 110 TFLOP/s, 8000^3 118
+// against 111).
+// (The element-wise load switch for tests does not count: it changes how the
+// data moves, never the tile or the K split, so results stay bitwise equal.)
+static bool staged_call(const Call &c) {
+  return !vec_ok(c.A, c.lda, 4, 4) || !vec_ok(c.B, c.ldb, 4, 4);
+}
+
+static F32Choice choose_staged(const Call &c) {
+  static const double us_per_k[4] = {0.0, 0.106e-6, 0.175e-6, 0.221e-6};
+  const long long tiles = tiles_of<F32Mid>(c);
+  const double mn_bytes = (double)c.M * (double)c.N * 4.0;
+  F32Choice best{F32Cfg::kMid, 1, 0.0, 1};
+  for (int S = 1; S <= 8; ++S) {
+    const int kc = S == 1 ? c.K : chunk_of<F32Mid>(c, S);
+    if (S > 1 && kc < 128) break;
+    const int used = S == 1 ? 1 : (c.K + kc - 1) / kc;
+    const long long n = (tiles * used + kCUs - 1) / kCUs;   // busiest CU's workgroups
+    const double k0 = n == 1 ? 110.0 : 44.0;
+    double t = ((double)kc + k0) * ((double)(n / 3) * us_per_k[3] + us_per_k[n % 3]);
+    t += used > 1 ? 4e-6 + (2.0 * used + 2.0) * mn_bytes / 5e12
+                  : (c.beta != 0.0f ? 2.0 : 1.0) * mn_bytes / 5e12;
+    if (S == 1 || t < best.time) best = F32Choice{F32Cfg::kMid, used, t, 1};
+  }
+  if (tiles * best.splits > kCUs) best.cfg = F32Cfg::kMidB;
+  return best;
+}
+
 // Otherwise score = measured throughput at full occupancy (fraction of the
 // fp32 peak at 4096^3, same-process interleaved timing: 0.92, 0.91, 0.57,
 // and tiny_eff for the 32x32 tile) x the two shares above; the largest score
@@ -1047,6 +1089,9 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
+  if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
+      tiles_of<F32Mid>(c) < 3LL * kCUs)
+    return choose_staged(c);
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
   const double small = score_of<F32Small>(c, 0.57, 3, 1);

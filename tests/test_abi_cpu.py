@@ -223,12 +223,36 @@ def test_tile_table_choice_and_override():
     assert dg.gemm_set_tile_config(9) == -1
 
 
+def test_staged_calls_split_the_medium_tile():
+    """Unaligned operands (element-wise loads): grids under three 128x128
+    tiles per CU take that tile with the K split of least estimated time;
+    larger grids keep the direct-path choice."""
+    import dense_gemm_fp32_amd as dg
+    def d(M, N, K):
+        return dg.gemm_describe("f32", M, N, K, 1.5, FAKE, K + 13, FAKE, N + 5, -0.75, FAKE, N + 3)[1]
+    for (M, N, K), S in [((1000, 3000, 517), 4), ((2000, 2000, 1000), 3), ((3000, 3000, 3000), 4),
+                         ((1000, 1000, 4000), 8), ((517, 3000, 1000), 4)]:
+        t = d(M, N, K)
+        assert "128x128x16" in t and ("split-K %d" % S) in t and "scalar1" in t, (M, N, K, t)
+    assert "256x256x32" in d(4096, 4096, 4096) and "split" not in d(4096, 4096, 4096)
+    assert "32x32x32" in d(300, 300, 300)      # fewer 32x32 tiles than CUs: latency-bound
+    # a misaligned base alone makes the call staged too
+    t = dg.gemm_describe("f32", 1000, 3000, 512, 1.0, FAKE + 4, 512, FAKE, 3000, 0.0, FAKE, 3000)[1]
+    assert "A:scalar1" in t and "split-K" in t
+    # forced tile or split settings still win
+    prev = dg.gemm_set_split(1)
+    try:
+        assert "split" not in d(1000, 3000, 517)
+    finally:
+        dg.gemm_set_split(prev)
+
+
 def test_split_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def d(dt, M, N, K):
         return dg.gemm_describe(dt, M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
     assert "split-K 8" in d("f16", 1024, 1024, 8192) and "split-K 4" in d("f32", 512, 512, 8192)
-    assert "split" not in d("f32", 1000, 3000, 517)
+    assert "split" not in d("f32", 1000, 3000, 512)
     prev = dg.gemm_set_split(1)
     try:
         assert "split" not in d("f16", 1024, 1024, 8192)
