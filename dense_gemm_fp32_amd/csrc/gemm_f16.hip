@@ -901,11 +901,33 @@ static void try_splits16(const Call &c, F16Cfg cfg, double eff, int per_cu, F16C
 // the tiles' throughput at two waves per SIMD as a fraction of the fp16 peak
 // (0.47, 0.47, 0.42); split candidates' chunks are at least 1024 deep and
 // the fastest estimate (est_time16) wins.
+// Calls with an operand that cannot take 16-byte loads run the element-wise
+// staged loads, and their workgroups need company on the CU to hide them.
+// Measured (interleaved, every tile and split of 1-4) on six such shapes with
+// fewer than 1.5 medium tiles per CU, the best was always the 128x128 tile
+// with the smallest K split reaching 1.5 workgroups per CU (at most 4, chunks
+// of at least 128 k): 1000x3000x517 86.6 against 83.7 TFLOP/s for the
+// direct-path choice, 2000x2000x1000 165 / 152, 1500^3 119 / 67,
+// 517x3000x1000 91 / 54, 1000x1000x4000 unchanged.  (The element-wise load
+// test switch does not count: it never changes the tile or the split.)
+static bool staged_call16(const Call &c) {
+  return !vec_ok(c.A, c.lda, 8) || !vec_ok(c.B, c.ldb, 8);
+}
+
 static F16Choice choose_f16(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
   if (c.tile_config == 1 || c.tile_config == 6) return F16Choice{F16Cfg::kBig, forced, 0.0};
   if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
   if (c.tile_config == 3 || c.tile_config == 4) return F16Choice{F16Cfg::kSmall, forced, 0.0};
+  const long long mid_tiles = tiles_of<F16Mid>(c);
+  if (c.split_mode == 0 && staged_call16(c) && 2 * mid_tiles < 3LL * kCUs &&
+      tiles_of<F16Small>(c) >= kCUs / 2) {
+    int S = 1;
+    while (S < 4 && 2 * mid_tiles * S < 3LL * kCUs &&
+           ((c.K + S) / (S + 1) + F16Mid::BK - 1) / F16Mid::BK * F16Mid::BK >= 128)
+      ++S;
+    return F16Choice{F16Cfg::kMid, S, 0.0};
+  }
   F16Choice best;
   if (tiles_of<F16Big>(c) >= kCUs / 2)
     best = F16Choice{F16Cfg::kBig, 1, est_time16(c, score16<F16Big>(c, 0.47, 1, 1), 1)};

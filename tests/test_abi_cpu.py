@@ -224,9 +224,10 @@ def test_tile_table_choice_and_override():
 
 
 def test_staged_calls_split_the_medium_tile():
-    """Unaligned operands (element-wise loads): grids under three 128x128
-    tiles per CU take that tile with the K split of least estimated time;
-    larger grids keep the direct-path choice."""
+    """Unaligned operands (element-wise loads): fp32 grids under three
+    128x128 tiles per CU take that tile with the K split of least estimated
+    time, fp16 grids under 1.5 take it with the smallest split reaching 1.5
+    workgroups per CU; larger grids keep the direct-path choice."""
     import dense_gemm_fp32_amd as dg
     def d(M, N, K):
         return dg.gemm_describe("f32", M, N, K, 1.5, FAKE, K + 13, FAKE, N + 5, -0.75, FAKE, N + 3)[1]
@@ -239,10 +240,19 @@ def test_staged_calls_split_the_medium_tile():
     # a misaligned base alone makes the call staged too
     t = dg.gemm_describe("f32", 1000, 3000, 512, 1.0, FAKE + 4, 512, FAKE, 3000, 0.0, FAKE, 3000)[1]
     assert "A:scalar1" in t and "split-K" in t
+    # fp16: the 128x128 tile with the smallest split reaching 1.5 workgroups per CU
+    def h(M, N, K):
+        return dg.gemm_describe("f16", M, N, K, 1.5, FAKE, K + 13, FAKE, N + 5, -0.75, FAKE, N + 3)[1]
+    for (M, N, K), S in [((1000, 3000, 517), 2), ((2000, 2000, 1000), 2), ((1500, 1500, 1500), 3),
+                         ((517, 3000, 1000), 4), ((1000, 1000, 4000), 4)]:
+        t = h(M, N, K)
+        assert "128x128x32" in t and ("split-K %d" % S) in t and "scalar1" in t, (M, N, K, t)
+    assert "256x256x64" in h(3000, 3000, 3000) and "split" not in h(3000, 3000, 3000)
+    assert "64x128x32" in h(100, 100, 100)
     # forced tile or split settings still win
     prev = dg.gemm_set_split(1)
     try:
-        assert "split" not in d(1000, 3000, 517)
+        assert "split" not in d(1000, 3000, 517) and "split" not in h(1000, 3000, 517)
     finally:
         dg.gemm_set_split(prev)
 
