@@ -1116,6 +1116,14 @@ static F32Choice choose_f32(const Call &c) {
     try_splits<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 256, best);
     try_splits<F32Small>(c, F32Cfg::kSmall, 0.57, 3, 1024, best);
     try_splits<F32Tiny>(c, F32Cfg::kTiny, 0.63, 6, 1024, best);
+  } else if (c.split_mode == 0 && c.K >= 512 && c.K < (c.M > c.N ? c.M : c.N) &&
+             tiles_of<F32Mid>(c) < kCUs) {
+    // Wide, short problems whose 128x128 tiles leave CUs idle: that tile in
+    // chunks of at least 512 k beats the small tiles' many workgroups
+    // (interleaved: 517x3000x1000 +13%, 256x4096x2048 +7%, 256x8192x1024
+    // +33%, 128x16384x4096 +65%); with shorter chunks it fell behind
+    // (384x3000x600 in chunks of 304: -21%).
+    try_splits<F32Mid>(c, F32Cfg::kMid, 0.91, 3, 512, best);
   } else if (c.split_mode >= 2) {
     best.splits = forced;
   }

@@ -257,6 +257,20 @@ def test_staged_calls_split_the_medium_tile():
         dg.gemm_set_split(prev)
 
 
+def test_wide_short_problems_split_the_medium_tile():
+    """Aligned problems with K below max(M, N) whose 128x128 tiles leave CUs
+    idle split that tile in chunks of at least 512 k; shorter chunks do not
+    pay, and square problems keep their own rule."""
+    import dense_gemm_fp32_amd as dg
+    def d(M, N, K):
+        return dg.gemm_describe("f32", M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
+    assert "128x128x16" in d(517, 3000, 1000) and "split-K 2" in d(517, 3000, 1000)
+    assert "split-K 4" in d(128, 16384, 4096) and "split-K 2" in d(256, 8192, 1024)
+    assert "split" not in d(384, 3000, 600)          # two chunks would be 304 deep
+    assert "split" not in d(1000, 8000, 700)         # 504 tiles: CUs already busy
+    assert "32x32x32" in d(1000, 1000, 1000) and "split" not in d(1000, 1000, 1000)
+
+
 def test_split_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def d(dt, M, N, K):
