@@ -524,6 +524,39 @@ def test_split_k_ragged_workload(w):
           w.name + " split4")
 
 
+# Shapes that the size-based choice itself splits through its rules for wide,
+# short problems and for unaligned (element-wise loaded) operands:
+# (dtype, M, N, K, pad of lda / ldb / ldc, expected split in the plan).
+CHOSEN_SPLIT_CASES = [
+    ("f32", 517, 3000, 1000, (0, 0, 0), "split-K 2"),      # wide, short, aligned
+    ("f32", 128, 16384, 4096, (0, 0, 0), "split-K 4"),
+    ("f32", 517, 3000, 1000, (13, 5, 3), "split-K 4"),     # unaligned
+    ("f32", 2000, 2000, 1000, (13, 5, 3), "split-K 3"),
+    ("f16", 1500, 1500, 1500, (13, 5, 3), "split-K 3"),
+    ("f16", 517, 3000, 1000, (13, 5, 3), "split-K 4"),
+    ("f16f32", 1000, 3000, 517, (13, 5, 3), "split-K 2"),
+]
+
+
+@pytest.mark.parametrize("case", CHOSEN_SPLIT_CASES, ids=lambda c: "%s_%dx%dx%d_pad%d" % (c[0], *c[1:4], c[4][0]))
+def test_splits_chosen_by_rule_match_oracle(case):
+    """The plan takes the expected split by itself (no test switch), with NaN
+    pads and a C-pad sentinel, and matches the oracle element by element."""
+    import dense_gemm_fp32_amd as dg
+    dtype, M, N, K, (pa, pb, pc), want = case
+    lda, ldb, ldc = K + pa, N + pb, N + pc
+    rng = np.random.default_rng(M + 7 * N + 13 * K + pa)
+    A = wl.pad(rng.standard_normal((M, K)).astype(_t(dtype)), lda, np.nan)
+    B = wl.pad(rng.standard_normal((K, N)).astype(_t(dtype)), ldb, np.nan)
+    C = wl.pad(rng.standard_normal((M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
+    base = 1 << 20
+    plan = dg.gemm_describe(dtype, M, N, K, 1.5, base, lda, base, ldb, -0.75, base, ldc)[1]
+    assert want in plan and "last round" not in plan, plan
+    rc, out = run(dtype, M, N, K, 1.5, A, lda, B, ldb, -0.75, C, ldc, "chosen " + want)
+    assert rc == 0
+    check(dtype, M, N, K, 1.5, A, lda, B, ldb, -0.75, C, ldc, out, "chosen %s %s" % (dtype, want))
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_split_k_deterministic_and_paths_agree(dtype):
     """A split call gives the same bits twice, with element-wise loads forced
