@@ -264,7 +264,8 @@ def parse_args():
                          "with cache flush; one JSON row per size")
     ap.add_argument("--sweep-sizes", default=None,
                     help="comma-separated sizes for --sweep (default 1024..12800 step 128)")
-    ap.add_argument("--only", choices=["f32", "f16", "f16f32", "valu", "copy"], default=None,
+    ap.add_argument("--only", choices=["f32", "f16", "f16f32", "valu", "copy", "ragged_f32",
+                                       "ragged_f16"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
                          "device copy of known size to calibrate HBM counters")
     return ap.parse_args()
@@ -380,6 +381,17 @@ def main():
         res, _ = measure(dg.gemm_f16f32, wl.F16F32_4096, PEAK_F16, "f16f32", args.steps,
                          args.warmup, False)
         print(json.dumps({"only": "f16f32", **res}), flush=True)
+        return
+    if args.only in ("ragged_f32", "ragged_f16"):
+        # the unaligned 1000 x 3000 x 517 workload (element-wise loads, split K
+        # by the library's own choice); a call's time includes its reduction
+        w = wl.RAGGED_F32 if args.only == "ragged_f32" else wl.RAGGED_F16
+        fn = dg.gemm_f32 if args.only == "ragged_f32" else dg.gemm_f16
+        res, _ = measure(fn, w, PEAK_F32 if args.only == "ragged_f32" else PEAK_F16, args.only,
+                         args.steps, args.warmup, False)
+        res["plan"] = dg.gemm_describe(w.dtype, w.M, w.N, w.K, w.alpha, 1 << 20, w.lda, 1 << 20,
+                                       w.ldb, w.beta, 1 << 20, w.ldc)[1]
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
     w32 = wl.F32_4096
     main_res, host32 = measure(dg.gemm_f32, w32, PEAK_F32, "f32", args.steps, args.warmup,
