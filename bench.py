@@ -224,7 +224,7 @@ def mfma_ceiling(torch, dev, stream, dg, wl, dtype, peak, seconds):
     iters = max(1, int(iters * 20.0 / max(ms, 1e-3)))
     timed(iters, 5)                       # bring the clock to its loaded level
     fl, ms = timed(iters, 10)
-    res = {"instruction": "v_mfma_f32_32x32x16_f16" if dtype == 1 else "v_mfma_f32_32x32x2_f32",
+    res = {"instruction": "v_mfma_f32_16x16x32_f16" if dtype == 1 else "v_mfma_f32_32x32x2_f32",
            "iters": iters, "ms_per_launch": round(ms, 4),
            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
            "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / peak, 4)}

@@ -1,5 +1,6 @@
 // gemm_f16.hip -- fp16-in / fp16-out GEMM with fp32 accumulation on the
-// gfx950 matrix cores (v_mfma_f32_32x32x16_f16).
+// gfx950 matrix cores (v_mfma_f32_16x16x32_f16 for the large tile,
+// v_mfma_f32_32x32x16_f16 for the others).
 //
 // C := alpha*A*B + beta*C with A, B, C in binary16.  Products of halves are
 // exact in fp32 and are accumulated in fp32; alpha*acc + beta*C is formed in
@@ -26,15 +27,21 @@
 //     k], row r's logical chunk c at chunk c ^ swz(r), which spreads 8
 //     consecutive rows over distinct bank groups for the 128-bit reads.
 //   * index-major (B as stored, K x N; A stored transposed, K x M): [BK rows]
-//     [EXT], k-row kr's chunk c at c ^ 4*(kr%4), so the four k-rows read
-//     together by a transpose read use distinct banks.
+//     [EXT], k-row kr's chunk c at c ^ (4*(kr%4) + 2*((kr/8)%2)), so the k-rows
+//     read together by a transpose-read pass use distinct banks (four rows
+//     for 32x32 blocks, four rows plus the same four 8 rows on for 16x16).
 // The swizzle is applied on the global side: lane L of a direct load writes
 // LDS bytes 16L..16L+15 of its 1 KB, so it fetches the global chunk that
 // belongs there.
 //
 // Operands.  v_mfma_f32_32x32x16_f16: lane l supplies A(row l%32, k 8h..8h+7)
-// and B(k 8h..8h+7, col l%32) for h = l/32 (any k order shared by A and B gives
-// the same sum).  From a k-major region: one ds_read_b128 of the lane's row.
+// and B(k 8h..8h+7, col l%32) for h = l/32; v_mfma_f32_16x16x32_f16 likewise
+// with index l%16 and h = l/16 (any k order shared by A and B gives the same
+// sum).  With random operands the part holds a higher clock under the 16x16
+// form at the same work per clock, so the large tile uses it; its fragments
+// cover twice the k, so A is re-read block row by block row into the
+// registers just released instead of double-buffered (the whole tile then
+// fits 256 VGPRs).  From a k-major region: one ds_read_b128 of the lane's row.
 // From an index-major region: two ds_read_b64_tr_b16, each returning 4
 // consecutive k of the lane's index from a 4 (k) x 16 (index) block that 16
 // lanes address (within each 16-lane group, lane i receives element i%4 of the
@@ -43,7 +50,7 @@
 // points flip either.
 //
 // Epilogue.  Accumulators leave the MFMA layout (one column per lane) through
-// a per-wave LDS staging area, 32 rows at a time; each lane then owns 4
+// a per-wave LDS staging area, 32 rows at a time (stage_rows); each lane then owns 4
 // adjacent columns of a row, reads C there when beta != 0 (8-byte accesses),
 // forms alpha*acc + beta*C in fp32, rounds to half and stores 8 bytes, so 32
 // lanes write 256 contiguous bytes of a row (the coalesced, LDS-staged
@@ -61,6 +68,8 @@
 // dimension) or whose offsets would reach 2^31 elements (32-bit load
 // offsets), uses the register-staged path instead: masked loads (0 outside
 // the matrix; pad elements are never read) written to the same LDS layout.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -69,8 +78,11 @@ namespace dgemm {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int GROUP_M_,
+          int MF_ = 32>
 struct H16Tile {
+  static constexpr int MF = MF_;                       // MFMA block edge: 32x32x16 or 16x16x32
+  static constexpr int KM = 512 / MF;                  // k per MFMA
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
@@ -79,9 +91,12 @@ struct H16Tile {
   static constexpr int NT = NWAVES * kWave;
   static constexpr int WTM = BM / WAVES_M;
   static constexpr int WTN = BN / WAVES_N;
-  static constexpr int FM = WTM / 32;
-  static constexpr int FN = WTN / 32;
-  static constexpr int SUB = BK / 16;                   // MFMA k sub-steps per K step
+  static constexpr int FM = WTM / MF;
+  static constexpr int FN = WTN / MF;
+  static constexpr int NG = WTM / 32;                   // 32-row epilogue groups per wave
+  static constexpr int SUB = BK / KM;                   // MFMA k sub-steps per K step
+  typedef typename std::conditional<MF == 32, f32x16, f32x4>::type Acc;
+  static constexpr int ACC_N = MF == 32 ? 16 : 4;
   static constexpr int A_BYTES = BM * BK * 2;           // a slot's A region
   static constexpr int B_BYTES = BK * BN * 2;           // ... and B region
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -94,7 +109,7 @@ struct H16Tile {
   static constexpr int EP_BYTES = 32 * EP_STRIDE * 4;   // per wave
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(BM % (WAVES_M * 32) == 0 && BN % (WAVES_N * 32) == 0, "wave tiling");
-  static_assert(BK % 32 == 0 && SUB % 2 == 0, "BK multiple of 32");
+  static_assert(BK % 32 == 0 && (SUB % 2 == 0 || MF == 16), "BK multiple of 32");
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KB load granules");
   static_assert(QA % NWAVES == 0 && QB % NWAVES == 0, "loads split over waves");
   static_assert(WTM % 64 == 0 && WTN % 64 == 0, "wave origins multiples of 64");
@@ -137,7 +152,7 @@ struct HRegion {
 
   __device__ static __forceinline__ int swz(int row) {
     if constexpr (KMAJ) return (row / RPW) % CH;
-    else if constexpr (ROW >= 256) return 4 * (row & 3);
+    else if constexpr (ROW >= 256) return 4 * (row & 3) + 2 * ((row >> 3) & 1);
     else return 4 * ((row >> 1) & 1);
   }
 
@@ -360,38 +375,49 @@ struct FragAddr {
 // a 4 (k) x 16 (index) block that 16 lanes address: 16-lane group g reads k
 // rows 8*(g/2) + i/4 (+4 for the second read) at indices
 // w0 + 32*b + 16*(g%2) + 4*(i%4) .. +3 (i = lane % 16).
-template <class R, int SUB, int NB>
+template <int MF, class R, int SUB, int NB>
 __device__ __forceinline__ void op_setup(int w0, OpAddr<R, SUB, NB> &f) {
   const int lane = threadIdx.x % kWave;
   if constexpr (R::K_MAJOR) {
-    const int row = w0 + lane % 32, lh = lane / 32;
+    // lane l: index l % MF, k group l / MF (8 k each) of the sub-step
+    constexpr int G = 64 / MF;
+    const int row = w0 + lane % MF, lh = lane / MF;
     const int sw = R::swz(row);
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) f.o[s] = row * R::ROW + 16 * ((2 * s + lh) ^ sw);
-  } else {
+    for (int s = 0; s < SUB; ++s) f.o[s] = row * R::ROW + 16 * ((G * s + lh) ^ sw);
+  } else if constexpr (MF == 32) {
     const int g = lane / 16, i = lane % 16;
     const int kr = 8 * (g / 2) + i / 4;
     const int t = 2 * (g % 2) + (i % 4) / 2;
     const int sw = R::swz(kr);
 #pragma unroll
     for (int b = 0; b < NB; ++b) f.o[b] = kr * R::ROW + 16 * ((w0 / 8 + 4 * b + t) ^ sw) + 8 * (i % 2);
+  } else {
+    // 16-lane group g reads k rows 8g + i/4 (+4 for the second read) at
+    // indices w0 + 16b + 4*(i%4) .. +3: lane i then holds k 8g..8g+7 of index i
+    const int g = lane / 16, i = lane % 16;
+    const int kr = 8 * g + i / 4;
+    const int t = (i % 4) / 2;
+    const int sw = R::swz(kr);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) f.o[b] = kr * R::ROW + 16 * ((w0 / 8 + 2 * b + t) ^ sw) + 8 * (i % 2);
   }
 }
 
 template <class T, class L>
 __device__ __forceinline__ void frag_setup(int wm0, int wn0, FragAddr<T, L> &f) {
-  op_setup(wm0, f.a);
-  op_setup(wn0, f.b);
+  op_setup<T::MF>(wm0, f.a);
+  op_setup<T::MF>(wn0, f.b);
 }
 
 // Fragment of block b at k sub-step s from an operand region.
-template <class R, int SUB, int NB>
+template <int MF, class R, int SUB, int NB>
 __device__ __forceinline__ f16x8 op_read(const char *region, const OpAddr<R, SUB, NB> &f, int s,
                                          int b) {
   if constexpr (R::K_MAJOR) {
-    return *reinterpret_cast<const f16x8 *>(region + f.o[s] + 32 * b * R::ROW);
+    return *reinterpret_cast<const f16x8 *>(region + f.o[s] + MF * b * R::ROW);
   } else {
-    const char *base = region + f.o[b] + 16 * s * R::ROW;
+    const char *base = region + f.o[b] + (512 / MF) * s * R::ROW;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 4 * R::ROW));
     return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -403,22 +429,27 @@ __device__ __forceinline__ f16x8 op_read(const char *region, const OpAddr<R, SUB
 template <class T, class L>
 __device__ __forceinline__ void frag_read(const char *slot, const FragAddr<T, L> &f, int s,
                                           Frag<T> &fr) {
-  fr.a[0] = op_read(slot, f.a, s, 0);
+  fr.a[0] = op_read<T::MF>(slot, f.a, s, 0);
 #pragma unroll
-  for (int bj = 0; bj < T::FN; ++bj) fr.b[bj] = op_read(slot + T::A_BYTES, f.b, s, bj);
+  for (int bj = 0; bj < T::FN; ++bj) fr.b[bj] = op_read<T::MF>(slot + T::A_BYTES, f.b, s, bj);
 #pragma unroll
-  for (int bi = 1; bi < T::FM; ++bi) fr.a[bi] = op_read(slot, f.a, s, bi);
+  for (int bi = 1; bi < T::FM; ++bi) fr.a[bi] = op_read<T::MF>(slot, f.a, s, bi);
 }
 
 // MFMAs for block rows [BI0, BI1) of one sub-step.
 template <class T, int BI0, int BI1>
-__device__ __forceinline__ void mfma_rows(const Frag<T> &fr, f32x16 (&acc)[T::FM][T::FN]) {
+__device__ __forceinline__ void mfma_rows(const Frag<T> &fr, typename T::Acc (&acc)[T::FM][T::FN]) {
 #pragma unroll
   for (int bi = BI0; bi < BI1; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < T::FN; ++bj)
-      acc[bi][bj] =
-          __builtin_amdgcn_mfma_f32_32x32x16_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+    for (int bj = 0; bj < T::FN; ++bj) {
+      if constexpr (T::MF == 32)
+        acc[bi][bj] =
+            __builtin_amdgcn_mfma_f32_32x32x16_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+      else
+        acc[bi][bj] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+    }
 }
 
 // Scheduling pattern for a region holding NM MFMAs and NR LDS reads: the
@@ -443,15 +474,39 @@ __device__ __forceinline__ void interleave_mfma_reads() {
   interleave_slot<0, NM, NR, TAIL>();
 }
 
+// Write 32-row group g of a wave's accumulators (rows 32g .. 32g+31 of its
+// tile, all its columns) into the wave's staging area, row-major.
+template <class T>
+__device__ __forceinline__ void stage_rows(float *stage, const typename T::Acc (&acc)[T::FM][T::FN],
+                                           int g, int lane) {
+  if constexpr (T::MF == 32) {
+    const int li = lane % 32, lh = lane / 32;
+#pragma unroll
+    for (int bj = 0; bj < T::FN; ++bj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[g][bj][r];
+  } else {
+    // 16x16 block: lane l holds rows 4*(l/16) .. +3 of column l % 16
+    const int lc = lane % 16, lq = lane / 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int bj = 0; bj < T::FN; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          stage[(16 * h + 4 * lq + r) * T::EP_STRIDE + 16 * bj + lc] = acc[2 * g + h][bj][r];
+  }
+}
+
 // ---------------------------------------------------------------- epilogue
 
 template <class T, bool VEC_C, bool CHECK>
 __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, char *lds,
-                                         const f32x16 (&acc)[T::FM][T::FN]) {
+                                         const typename T::Acc (&acc)[T::FM][T::FN]) {
   uint16_t *C = static_cast<uint16_t *>(p.C);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32, lh = lane / 32;
   float *stage = reinterpret_cast<float *>(lds + wave * T::EP_BYTES);
   const float alpha = p.alpha, beta = p.beta;
   constexpr int LPR = T::WTN / 4;                 // lanes per staged row
@@ -463,10 +518,10 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
   // Every C value this lane combines (vector path, beta != 0) is loaded
   // before the first is used, so the latencies of the loads overlap instead
   // of adding up block row by block row.
-  u32x2 cpre[T::FM][PASSES];
+  u32x2 cpre[T::NG][PASSES];
   if (VEC_C && beta != 0.0f) {
 #pragma unroll
-    for (int bi = 0; bi < T::FM; ++bi)
+    for (int bi = 0; bi < T::NG; ++bi)
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
@@ -476,12 +531,8 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
       }
   }
 #pragma unroll
-  for (int bi = 0; bi < T::FM; ++bi) {
-#pragma unroll
-    for (int bj = 0; bj < T::FN; ++bj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[bi][bj][r];
+  for (int bi = 0; bi < T::NG; ++bi) {
+    stage_rows<T>(stage, acc, bi, lane);
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       const int rl = pass * ROWS_PER_PASS + lane / LPR;
@@ -525,11 +576,10 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
 // without holding every row's C in registers at once.
 template <class T, bool VEC_C, bool CHECK>
 __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int c0, char *lds,
-                                               const f32x16 (&acc)[T::FM][T::FN]) {
+                                               const typename T::Acc (&acc)[T::FM][T::FN]) {
   float *C = static_cast<float *>(p.C);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int li = lane % 32, lh = lane / 32;
   float *stage = reinterpret_cast<float *>(lds + wave * T::EP_BYTES);
   const float alpha = p.alpha, beta = p.beta;
   constexpr int LPR = T::WTN / 4;
@@ -539,7 +589,7 @@ __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int 
   const int col = c0 + cl;
   const bool cols_ok = !CHECK || col + 3 < p.N;
 #pragma unroll
-  for (int bi = 0; bi < T::FM; ++bi) {
+  for (int bi = 0; bi < T::NG; ++bi) {
     f32x4 cpre[PASSES];
     if (VEC_C && beta != 0.0f) {
 #pragma unroll
@@ -550,11 +600,7 @@ __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int 
           cpre[pass] = *reinterpret_cast<const f32x4 *>(C + (size_t)row * (size_t)p.ldc + col);
       }
     }
-#pragma unroll
-    for (int bj = 0; bj < T::FN; ++bj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stage[(8 * (r / 4) + 4 * lh + (r % 4)) * T::EP_STRIDE + 32 * bj + li] = acc[bi][bj][r];
+    stage_rows<T>(stage, acc, bi, lane);
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       const int rl = pass * ROWS_PER_PASS + lane / LPR;
@@ -588,13 +634,13 @@ __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int 
 // ---------------------------------------------------------------- main loops
 
 template <class T>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
+__device__ __forceinline__ void zero_acc(typename T::Acc (&acc)[T::FM][T::FN]) {
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi)
 #pragma unroll
     for (int bj = 0; bj < T::FN; ++bj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+      for (int r = 0; r < T::ACC_N; ++r) acc[bi][bj][r] = 0.0f;
 }
 
 // All sub-steps of one K step from LDS slot `slot`.  On entry fr[0] holds
@@ -605,10 +651,65 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
 // K step is read from `next_slot` into fr[0] between the remaining MFMAs.  On
 // the last K step this reads a stale slot whose values are never used:
 // keeping the reads unconditional keeps the LDS wait counts exact.
+// 16x16x32 blocks: a sub-step's fragments are twice the registers of the
+// 32x32x16 ones, too many to double-buffer.  A is read row block by row block
+// into the registers the row's MFMAs just released; only B is double-buffered.
+template <class T, class L, class Next>
+__device__ __forceinline__ void kstep_rolling(const char *slot, const char *next_slot,
+                                              const FragAddr<T, L> &fa, Frag<T> &fr,
+                                              typename T::Acc (&acc)[T::FM][T::FN], Next next) {
+  constexpr int HALF = T::FM / 2;
+#pragma unroll
+  for (int s = 0; s < T::SUB; ++s) {
+    f16x8 bn[T::FN];
+    if (s + 1 < T::SUB) {
+#pragma unroll
+      for (int bj = 0; bj < T::FN; ++bj) bn[bj] = op_read<T::MF>(slot + T::A_BYTES, fa.b, s + 1, bj);
+#pragma unroll
+      for (int bi = 0; bi < T::FM; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < T::FN; ++bj)
+          acc[bi][bj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+        fr.a[bi] = op_read<T::MF>(slot, fa.a, s + 1, bi);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < HALF; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < T::FN; ++bj)
+          acc[bi][bj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      next();
+#pragma unroll
+      for (int bj = 0; bj < T::FN; ++bj) bn[bj] = op_read<T::MF>(next_slot + T::A_BYTES, fa.b, 0, bj);
+#pragma unroll
+      for (int bi = 0; bi < HALF; ++bi) fr.a[bi] = op_read<T::MF>(next_slot, fa.a, 0, bi);
+#pragma unroll
+      for (int bi = HALF; bi < T::FM; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < T::FN; ++bj)
+          acc[bi][bj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(fr.a[bi], fr.b[bj], acc[bi][bj], 0, 0, 0);
+        fr.a[bi] = op_read<T::MF>(next_slot, fa.a, 0, bi);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int bj = 0; bj < T::FN; ++bj) fr.b[bj] = bn[bj];
+  }
+}
+
 template <class T, class L, class Next>
 __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
                                       const FragAddr<T, L> &fa, Frag<T> (&fr)[2],
-                                      f32x16 (&acc)[T::FM][T::FN], Next next) {
+                                      typename T::Acc (&acc)[T::FM][T::FN], Next next) {
+  if constexpr (T::MF == 16) {
+    kstep_rolling<T, L>(slot, next_slot, fa, fr[0], acc, next);
+    return;
+  }
   constexpr int NREAD = L::NREAD;     // LDS instructions per sub-step
   constexpr int HALF = T::FM / 2;
 #pragma unroll
@@ -634,7 +735,7 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
 template <class T, class L>
 __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int n0, char *lds,
                                                 uint32_t lds_u32, int wm0, int wn0,
-                                                f32x16 (&acc)[T::FM][T::FN]) {
+                                                typename T::Acc (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   DirectAddr<T> da;
   direct_setup<T, L>(p, m0, n0, da);
@@ -690,7 +791,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
 template <class T, class L>
 __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int n0, char *lds,
                                                 int wm0, int wn0, bool va, bool vb,
-                                                f32x16 (&acc)[T::FM][T::FN]) {
+                                                typename T::Acc (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   FragAddr<T, L> fa;
   frag_setup<T, L>(wm0, wn0, fa);
@@ -727,7 +828,7 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   const int wave = threadIdx.x / kWave;
   const int wm0 = (wave / T::WAVES_N) * T::WTM;
   const int wn0 = (wave % T::WAVES_N) * T::WTN;
-  f32x16 acc[T::FM][T::FN];
+  typename T::Acc acc[T::FM][T::FN];
   zero_acc<T>(acc);
 
   const bool m_edge = m0 + T::BM > p.M;
@@ -755,7 +856,7 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 // Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
 // L2 group rows), largest first; a call takes the largest tile that still
 // gives at least half of the CUs a workgroup.
-typedef H16Tile<256, 256, 64, 2, 4, 2, 4> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU
+typedef H16Tile<256, 256, 64, 2, 4, 2, 4, 16> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU, 16x16x32
 typedef H16Tile<128, 128, 32, 2, 2, 4, 8> F16Mid;     // 4 waves,  64 KB LDS, 2 WG/CU
 typedef H16Tile<64, 128, 32, 1, 2, 4, 8> F16Small;    // 2 waves,  48 KB LDS, 3 WG/CU
 
@@ -826,9 +927,15 @@ static hipError_t dispatch_out(const Call &c, const Plan &pl) {
     case 3: return launch_variant<T, false, true, true, OUT32>(c, pl);
     case 4: return launch_variant<T, true, false, false, OUT32>(c, pl);
     case 5: return launch_variant<T, true, false, true, OUT32>(c, pl);
-    case 6: return launch_variant<T, true, true, false, OUT32>(c, pl);
-    default: return launch_variant<T, true, true, true, OUT32>(c, pl);
+    default: break;
   }
+  // Both operands stored transposed: with 16x16x32 blocks that kernel needs
+  // more than 256 VGPRs (it spills), so it keeps the 32x32x16 blocks.
+  typedef typename std::conditional<
+      T::MF == 16,
+      H16Tile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::STAGES, T::GROUP_M, 32>, T>::type TT;
+  if (key == 6) return launch_variant<TT, true, true, false, OUT32>(c, pl);
+  return launch_variant<TT, true, true, true, OUT32>(c, pl);
 }
 
 template <class T>
@@ -1002,8 +1109,8 @@ Plan plan_f16(const Call &c) {
   const F16Choice ch = choose_f16(c);
   switch (ch.cfg) {
     case F16Cfg::kBig:
-      return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
-                                         : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots", ch.splits);
+      return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots out f32"
+                                         : "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots", ch.splits);
     case F16Cfg::kMid:
       return plan_cfg<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
                                          : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots", ch.splits);

@@ -119,7 +119,8 @@ int gemm_f32(int M, int N, int K, float alpha,
 /*
  * fp16 GEMM with fp32 accumulation: A, B, C hold binary16 bit patterns;
  * products are exact in fp32 and accumulated in fp32 on the matrix cores
- * (v_mfma_f32_32x32x16_f16); alpha*acc + beta*C is formed in fp32 (C widened
+ * (v_mfma_f32_16x16x32_f16 on the large tile, v_mfma_f32_32x32x16_f16 on the
+ * smaller ones); alpha*acc + beta*C is formed in fp32 (C widened
  * exactly) and rounded once to binary16, round-to-nearest-even, overflowing
  * to +-infinity.  Arguments as for gemm_f32; alpha and beta are binary32.
  */
@@ -132,7 +133,7 @@ int gemm_f16(int M, int N, int K, float alpha,
 /*
  * fp16 inputs, fp32 C and result: A and B hold binary16 values (as for
  * gemm_f16), C holds binary32.  Products are accumulated in fp32 on the
- * matrix cores (v_mfma_f32_32x32x16_f16); alpha*acc + beta*C is formed in fp32
+ * matrix cores (as for gemm_f16); alpha*acc + beta*C is formed in fp32
  * and stored as binary32 (no rounding to half).  Arguments and return values
  * as for gemm_f32, with ldc counting floats.  The degenerate paths (alpha == 0
  * or K == 0) scale the fp32 C as gemm_f32 does.
@@ -293,17 +294,18 @@ int gemm_set_tail_split(int mode);
  * any GEMM kernel can reach on this part at the clock the part sustains
  * under matrix-core load (the power-aware comparison of the SGEMM summary's
  * discussion of tuning and power): one launch of 512 workgroups x 8 waves,
- * each wave running `iters` rounds of 8 independent MFMAs on operand
- * registers loaded once (dtype 1: v_mfma_f32_32x32x16_f16, fp16 operands;
- * dtype 0: v_mfma_f32_32x32x2_f32, fp32 operands), with no memory traffic
- * inside the loop.
+ * each wave running `iters` rounds of independent MFMAs over a 128 x 64
+ * wave tile on operand registers loaded once (dtype 1: 32 of
+ * v_mfma_f32_16x16x32_f16, fp16 operands; dtype 0: 8 of
+ * v_mfma_f32_32x32x2_f32, fp32 operands: the large GEMM tiles' instructions),
+ * with no memory traffic inside the loop.
  *   operands: DEVICE buffer of at least 65536 bytes holding fp16 (dtype 1)
  *             or fp32 (dtype 0) values; give it the distribution of the GEMM
  *             inputs being compared, since the MFMA power depends on the bits.
  *   out:      DEVICE buffer of at least 1 MiB; receives one float per thread
  *             (the sum of its accumulators), so that no MFMA is dead.
  *   flops:    HOST pointer; receives the launch's flop count
- *             (waves x iters x 8 x 2*32*32*k).
+ *             (waves x iters x 2*128*64*k, k = 32 for fp16, 2 for fp32).
  * Enqueues one kernel on `stream` and returns 0, a positive hipError_t if the
  * launch fails, or -101 .. -107 for an invalid argument 1 .. 7 (checked in
  * order, before any HIP call).

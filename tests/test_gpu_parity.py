@@ -727,7 +727,8 @@ def test_valu_4096_sampled():
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_mfma_probe_runs_and_counts(dtype):
     """The matrix-core ceiling probe: its flop count follows its definition
-    (512 workgroups x 8 waves x iters x 8 MFMAs of 2*32*32*k flops) and every
+    (512 workgroups x 8 waves x iters x a 128 x 64 wave tile over k, 2*128*64*k
+    flops, k = 32 for fp16 and 2 for fp32) and every
     thread's accumulator sum equals iters times the sum after one round (the
     rounds repeat the same products; small integer operands keep every sum
     exact)."""
@@ -747,8 +748,8 @@ def test_mfma_probe_runs_and_counts(dtype):
     rc, f3 = dg.gemm_probe_mfma(dtype, 3, ops, out3)
     assert rc == 0, dg.gemm_status_string(rc)
     torch.cuda.synchronize(dev)
-    k = 16 if dtype == 1 else 2
-    assert f1 == 512 * 8 * 1 * 8 * 2 * 32 * 32 * k and f3 == 3 * f1
+    k = 32 if dtype == 1 else 2
+    assert f1 == 512 * 8 * 1 * 2 * 128 * 64 * k and f3 == 3 * f1
     a1, a3 = out1.cpu().double(), out3.cpu().double()
     assert torch.isfinite(a1).all() and torch.isfinite(a3).all()
     assert torch.equal(a3, 3 * a1)
