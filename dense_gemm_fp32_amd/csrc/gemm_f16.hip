@@ -651,9 +651,12 @@ __device__ __forceinline__ void zero_acc(typename T::Acc (&acc)[T::FM][T::FN]) {
 // K step is read from `next_slot` into fr[0] between the remaining MFMAs.  On
 // the last K step this reads a stale slot whose values are never used:
 // keeping the reads unconditional keeps the LDS wait counts exact.
-// 16x16x32 blocks: a sub-step's fragments are twice the registers of the
-// 32x32x16 ones, too many to double-buffer.  A is read row block by row block
-// into the registers the row's MFMAs just released; only B is double-buffered.
+//
+// kstep_rolling is that schedule for 16x16x32 blocks, whose sub-step
+// fragments take twice the registers of the 32x32x16 ones, too many to
+// double-buffer: on entry fr holds sub-step 0; A is read block row by block
+// row into the registers the row's MFMAs just released, and only B has a
+// second buffer (bn).  kstep picks the schedule by the tile's block shape.
 template <class T, class L, class Next>
 __device__ __forceinline__ void kstep_rolling(const char *slot, const char *next_slot,
                                               const FragAddr<T, L> &fa, Frag<T> &fr,
@@ -707,26 +710,26 @@ __device__ __forceinline__ void kstep(const char *slot, const char *next_slot,
                                       const FragAddr<T, L> &fa, Frag<T> (&fr)[2],
                                       typename T::Acc (&acc)[T::FM][T::FN], Next next) {
   if constexpr (T::MF == 16) {
-    kstep_rolling<T, L>(slot, next_slot, fa, fr[0], acc, next);
-    return;
-  }
-  constexpr int NREAD = L::NREAD;     // LDS instructions per sub-step
-  constexpr int HALF = T::FM / 2;
+    kstep_rolling<T, L>(slot, next_slot, fa, fr[0], acc, next);   // fr[1] is not used
+  } else {
+    constexpr int NREAD = L::NREAD;     // LDS instructions per sub-step
+    constexpr int HALF = T::FM / 2;
 #pragma unroll
-  for (int s = 0; s < T::SUB; ++s) {
-    if (s + 1 < T::SUB) {
-      frag_read<T, L>(slot, fa, s + 1, fr[(s + 1) & 1]);
-      mfma_rows<T, 0, T::FM>(fr[s & 1], acc);
-      interleave_mfma_reads<T::FM * T::FN, NREAD, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      mfma_rows<T, 0, HALF>(fr[s & 1], acc);
-      __builtin_amdgcn_sched_barrier(0);
-      next();
-      frag_read<T, L>(next_slot, fa, 0, fr[0]);
-      mfma_rows<T, HALF, T::FM>(fr[s & 1], acc);
-      interleave_mfma_reads<(T::FM - HALF) * T::FN, NREAD, 2>();
-      __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < T::SUB; ++s) {
+      if (s + 1 < T::SUB) {
+        frag_read<T, L>(slot, fa, s + 1, fr[(s + 1) & 1]);
+        mfma_rows<T, 0, T::FM>(fr[s & 1], acc);
+        interleave_mfma_reads<T::FM * T::FN, NREAD, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        mfma_rows<T, 0, HALF>(fr[s & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        next();
+        frag_read<T, L>(next_slot, fa, 0, fr[0]);
+        mfma_rows<T, HALF, T::FM>(fr[s & 1], acc);
+        interleave_mfma_reads<(T::FM - HALF) * T::FN, NREAD, 2>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
