@@ -1112,6 +1112,10 @@ Plan plan_f16(const Call &c) {
   const F16Choice ch = choose_f16(c);
   switch (ch.cfg) {
     case F16Cfg::kBig:
+      if (c.ta && c.tb)   // both operands transposed: 32x32x16 blocks (see dispatch_out)
+        return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
+                                           : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots",
+                                ch.splits);
       return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots out f32"
                                          : "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots", ch.splits);
     case F16Cfg::kMid:
