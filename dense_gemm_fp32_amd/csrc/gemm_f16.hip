@@ -860,6 +860,7 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 // L2 group rows), largest first; a call takes the largest tile that still
 // gives at least half of the CUs a workgroup.
 typedef H16Tile<256, 256, 64, 2, 4, 2, 4, 16> F16Big;     // 8 waves, 128 KB LDS, 1 WG/CU, 16x16x32
+typedef H16Tile<256, 256, 64, 2, 4, 2, 4, 32> F16Big32;   // the same tile on 32x32x16 blocks
 typedef H16Tile<128, 128, 32, 2, 2, 4, 8> F16Mid;     // 4 waves,  64 KB LDS, 2 WG/CU
 typedef H16Tile<64, 128, 32, 1, 2, 4, 8> F16Small;    // 2 waves,  48 KB LDS, 3 WG/CU
 
@@ -953,7 +954,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F16Cfg { kBig, kMid, kSmall };
+enum class F16Cfg { kBig, kBig32, kMid, kSmall };
 
 // Share of the CUs kept busy by `tiles` workgroups (whole tiles per CU) and
 // share of the two-waves-per-SIMD occupancy a busy CU reaches with its
@@ -1026,7 +1027,8 @@ static bool staged_call16(const Call &c) {
 
 static F16Choice choose_f16(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
-  if (c.tile_config == 1 || c.tile_config == 6) return F16Choice{F16Cfg::kBig, forced, 0.0};
+  if (c.tile_config == 1) return F16Choice{F16Cfg::kBig, forced, 0.0};
+  if (c.tile_config == 6) return F16Choice{F16Cfg::kBig32, forced, 0.0};
   if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
   if (c.tile_config == 3 || c.tile_config == 4) return F16Choice{F16Cfg::kSmall, forced, 0.0};
   const long long mid_tiles = tiles_of<F16Mid>(c);
@@ -1052,6 +1054,14 @@ static F16Choice choose_f16(const Call &c) {
   } else if (c.split_mode >= 2) {
     best.splits = forced;
   }
+  // The large tile's two block shapes.  16x16x32 blocks let the part hold a
+  // higher clock where it is power-bound, but do a little less work per clock
+  // (A re-read per block row): they win when the workgroups fill every CU and
+  // the clock drops (interleaved, sustained: 4096^3 +3.5-6%, 5120^3 +2.7%,
+  // 8192^3 +2.7%) and lose where part of the chip idles and the clock stays
+  // near its maximum (3072^3, 144 tiles at 2.38 GHz: -7.5%).
+  if (best.cfg == F16Cfg::kBig && tiles_of<F16Big>(c) * best.splits < kCUs)
+    best.cfg = F16Cfg::kBig32;
   return best;
 }
 
@@ -1118,6 +1128,10 @@ Plan plan_f16(const Call &c) {
                                 ch.splits);
       return plan_cfg<F16Big>(c, c.out32 ? "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots out f32"
                                          : "f16 mfma16x16x32 tile 256x256x64 8 waves 2 slots", ch.splits);
+    case F16Cfg::kBig32:
+      return plan_cfg<F16Big32>(c, c.out32 ? "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots out f32"
+                                           : "f16 mfma32x32x16 tile 256x256x64 8 waves 2 slots",
+                                ch.splits);
     case F16Cfg::kMid:
       return plan_cfg<F16Mid>(c, c.out32 ? "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots out f32"
                                          : "f16 mfma32x32x16 tile 128x128x32 4 waves 4 slots", ch.splits);
@@ -1131,6 +1145,7 @@ hipError_t launch_f16(const Call &c) {
   const F16Choice ch = choose_f16(c);
   switch (ch.cfg) {
     case F16Cfg::kBig: return launch_cfg<F16Big>(c, ch.splits);
+    case F16Cfg::kBig32: return launch_cfg<F16Big32>(c, ch.splits);
     case F16Cfg::kMid: return launch_cfg<F16Mid>(c, ch.splits);
     default: return launch_cfg<F16Small>(c, ch.splits);
   }

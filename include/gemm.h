@@ -262,8 +262,9 @@ int gemm_set_load_mode(int mode);
  * problem size (the default); 1, 2, 3, 4 = force the large, medium, small or
  * (fp32 only; fp16 uses its small one) tiny configuration; 5 = the medium
  * configuration with each K step's loads issued together rather than spread
- * (fp32 only; fp16 uses its medium one); 6 = the fp32 256 x 256 tile (fp16
- * uses its large one, which is 256 x 256 already).  Process-wide,
+ * (fp32 only; fp16 uses its medium one); 6 = the fp32 256 x 256 tile, and
+ * for fp16 the large tile on 32x32x16 blocks (1 forces it on 16x16x32
+ * blocks; the size-based choice takes either).  Process-wide,
  * like gemm_set_load_mode.  Returns the previous setting, or -1 for an
  * unknown value.
  */

@@ -208,6 +208,10 @@ def test_tile_table_choice_and_override():
     assert "last round split-K 4" in name("f32", 5120) and "split" not in name("f32", 8192)
     assert "256x256x32" in name("f32", 8192) and "256x128x32" in name("f32", 6400)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
+    # the large fp16 tile: 16x16x32 blocks when its workgroups fill the CUs,
+    # 32x32x16 blocks when part of the chip idles (the clock then stays high)
+    assert "mfma16x16x32" in name("f16", 4096) and "mfma32x32x16" in name("f16", 3072)
+    assert "mfma16x16x32" in name("f16", 8192) and "mfma16x16x32" in name("f16", 5120)
     assert "128x128x32" in name("f16", 2048) and "64x128x32" in name("f16", 512)
     prev = dg.gemm_set_tile_config(1)
     try:
