@@ -1,7 +1,12 @@
 """Mutation check of the oracle's pins: plant one plausible mistake at a time
-in a copy of oracle.c (a transposed or mis-strided operand, a dropped term, a
-wrong sign, an off-by-one loop, a wrong binary16 bias or rounding rule), build
-it on the CPU, and require the pin suite to fail against it."""
+in a copy of the oracle and require the pin suite to fail against it.
+
+  * oracle.c (a transposed or mis-strided operand, a dropped term, a wrong
+    sign, an off-by-one loop, a wrong binary16 bias or rounding rule): the
+    copy is built on the CPU and loaded in place of liboracle.so;
+  * the Python side, oracle/__init__.py (the acceptance bound, the
+    element-wise comparison, the whole-matrix checksum and Freivalds' check):
+    the copy is imported as the `oracle` package before the pins run."""
 import os
 import subprocess
 import sys
@@ -85,3 +90,82 @@ def test_unmutated_copy_passes(tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout[-3000:]
+
+
+# Mistakes planted in oracle/__init__.py: (name, text, replacement, occurrence).
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = [
+    # tolerance(): the bound every parity test accepts against
+    ("tol_f32_uses_f16_unit", "u_out, eta = U32, ETA32", "u_out, eta = U16, ETA32", 1),
+    ("tol_f16_uses_f32_unit", "u_out, eta = U16, ETA16", "u_out, eta = U32, ETA16", 1),
+    ("tol_f16_eta_of_f32", "u_out, eta = U16, ETA16", "u_out, eta = U16, ETA32", 1),
+    ("tol_beta_C_dropped", "mag = abs(float(alpha)) * G + abs(float(beta)) * Cabs",
+     "mag = abs(float(alpha)) * G", 1),
+    ("tol_alpha_not_abs", "mag = abs(float(alpha)) * G", "mag = float(alpha) * G", 1),
+    ("tol_factor_4_to_1", "4.0 * max(int(K), 1)", "1.0 * max(int(K), 1)", 1),
+    ("tol_K_not_max1", "4.0 * max(int(K), 1)", "4.0 * int(K)", 1),
+    ("tol_no_out_rounding_factor", "(1.0 + u_out) * 4.0", "4.0", 1),
+    ("tol_no_R_term", "+ u_out * np.abs(R) + eta", "+ eta", 1),
+    ("tol_no_eta", "+ u_out * np.abs(R) + eta", "+ u_out * np.abs(R)", 1),
+    # compare(): the element-wise verdict
+    ("cmp_strict_less", "return bool(worst <= 1.0)", "return bool(worst < 1.0)", 1),
+    ("cmp_nan_only_R", "both_nan = np.isnan(g) & np.isnan(R)", "both_nan = np.isnan(R)", 1),
+    ("cmp_nan_only_gpu", "both_nan = np.isnan(g) & np.isnan(R)", "both_nan = np.isnan(g)", 1),
+    ("cmp_signed_error", "err = np.abs(g - R)", "err = g - R", 1),
+    ("cmp_any_inf_passes", "ratio = np.where(inf_r & (g == R), 0.0, ratio)",
+     "ratio = np.where(inf_r, 0.0, ratio)", 1),
+    # checksum(): the whole-matrix sum and its magnitude
+    ("sum_beta_mag_dropped", "mag += abs(float(beta)) * float(np.abs(C2).sum())", "mag += 0.0", 1),
+    ("sum_alpha_mag_signed", "np.abs(A2).sum(axis=0) @ np.abs(B2).sum(axis=1)",
+     "A2.sum(axis=0) @ np.abs(B2).sum(axis=1)", 1),
+    ("sum_beta_term_sign", "exp += float(beta) * float(C2.sum())",
+     "exp -= float(beta) * float(C2.sum())", 1),
+    ("sum_B_colsum", "rb = B2.sum(axis=1)", "rb = B2.sum(axis=0)[:B2.shape[0]]", 1),
+    # freivalds(): the product check
+    ("frv_beta_mag_dropped", "mag += abs(float(beta)) * (np.abs(C2) @ np.abs(x))", "mag += 0.0", 1),
+    ("frv_x_not_abs", "(np.abs(B2) @ np.abs(x))", "(np.abs(B2) @ x)", 1),
+    ("frv_beta_dropped", "y += float(beta) * (C2 @ x)", "y += 0.0", 1),
+    ("frv_B_transposed", "y += float(alpha) * (A2 @ (B2 @ x))",
+     "y += float(alpha) * (A2 @ (B2.T[:B2.shape[0]] @ x[:B2.shape[0]]))", 1),
+    # _view2(): the padded-buffer view used by both whole-matrix checks
+    ("view_ignores_ld", "strides=(ld * a.itemsize, a.itemsize)",
+     "strides=(cols * a.itemsize, a.itemsize)", 1),
+]
+
+_RUN_WITH_PACKAGE = (
+    "import sys; sys.path.insert(0, sys.argv[1]); import oracle; "
+    "assert oracle.__file__.startswith(sys.argv[1]), oracle.__file__; "
+    "import pytest; sys.exit(pytest.main(sys.argv[2:]))")
+
+
+def _run_pins_with_package(pkg_root):
+    from oracle.build import LIB, build_oracle
+    if not os.path.exists(LIB):
+        build_oracle()
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=LIB, OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, "-c", _RUN_WITH_PACKAGE, str(pkg_root), "-x", "-q",
+                           "-p", "no:cacheprovider", "-k", "not ragged and not match_full",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+
+
+def _package_copy(tmp_path, text):
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(text)
+    for name in ("build.py", "oracle.c"):
+        (pkg / name).write_text(open(os.path.join(ROOT, "oracle", name)).read())
+    return tmp_path
+
+
+@pytest.mark.parametrize("name,old,new,occ", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_planted_python_mistake(tmp_path, name, old, new, occ):
+    text = open(PY_SRC).read()
+    r = _run_pins_with_package(_package_copy(tmp_path, _mutate(text, old, new, occ)))
+    assert r.returncode != 0, "mutant %s survived the pins:\n%s" % (name, r.stdout[-2000:])
+
+
+def test_unmutated_python_copy_passes(tmp_path):
+    """Control: the same procedure on an unmodified copy of the package passes."""
+    r = _run_pins_with_package(_package_copy(tmp_path, open(PY_SRC).read()))
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-2000:]

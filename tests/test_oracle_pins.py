@@ -6,6 +6,7 @@ transposed operand in the oracle fails at least one of them (the mutation
 tests in test_oracle_mutants.py check exactly that)."""
 from fractions import Fraction
 import itertools
+import os
 
 import numpy as np
 import pytest
@@ -411,3 +412,100 @@ def test_compare_nan_and_inf_handling():
     assert not oracle.compare(np.array([np.nan, np.nan, np.inf], np.float32), R, tol)[0]
     assert not oracle.compare(np.array([1.0, 0.0, np.inf], np.float32), R, tol)[0]
     assert not oracle.compare(np.array([1.0, np.nan, -np.inf], np.float32), R, tol)[0]
+
+
+# ---------------------------------------------------------------- tolerance, by hand
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _exact_term(t):
+    """'c*2^e', '2^e' or a decimal number, as an exact Fraction."""
+    t = t.strip()
+    coef, _, powr = t.rpartition("*") if "^" in t else ("", "", t)
+    if "^" in powr:
+        base, e = powr.split("^")
+        assert base == "2", t
+        v = Fraction(2) ** int(e)
+        return v * (Fraction(coef) if coef else 1)
+    return Fraction(powr)
+
+
+def _exact_sum(expr):
+    return sum((_exact_term(t) for t in expr.split("+")), Fraction(0))
+
+
+def _tolerance_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "tolerance.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("|")
+            out, K, alpha, beta, G, Cabs, R = lhs.split()
+            rows.append((out, int(K), *(float(_exact_term(x)) for x in (alpha, beta, G, Cabs, R)),
+                         _exact_sum(rhs)))
+    return rows
+
+
+def test_tolerance_matches_hand_computed_values():
+    """The bound at hand-worked points (tests/golden/tolerance.txt): K = 0,
+    beta*C alone, a subnormal-range R, large |R|, a negative alpha, fp32 and
+    fp16 outputs.  A wrong u_out, a dropped |beta||C|, eta or (1 + u_out)
+    term, 4K in place of K, or K in place of max(K, 1) each miss one row."""
+    rows = _tolerance_rows()
+    assert len(rows) >= 9
+    for out, K, alpha, beta, G, Cabs, R, expect in rows:
+        got = oracle.tolerance(np.array([G]), np.array([Cabs]), alpha, beta, K, np.array([R]), out)
+        got = Fraction(float(got[0]))
+        assert abs(got - expect) <= expect * Fraction(1, 2 ** 50), (out, K, alpha, beta, G, Cabs, R,
+                                                                   float(got), float(expect))
+
+
+def test_compare_boundary_sign_and_shape():
+    """An error exactly equal to the bound passes, one just above fails, in
+    either direction; the worst ratio and its position are reported."""
+    R = np.array([[1.0, 2.0], [3.0, 4.0]])
+    tol = np.full((2, 2), 2.0 ** -20)
+    at = R + np.array([[0.0, 2.0 ** -20], [0.0, -2.0 ** -20]])
+    ok, worst, idx = oracle.compare(at, R, tol)
+    assert ok and worst == 1.0 and idx in ((0, 1), (1, 1))
+    over = R.copy()
+    over[1, 0] -= 2.0 ** -19        # below R by twice the bound
+    ok, worst, idx = oracle.compare(over, R, tol)
+    assert not ok and worst == 2.0 and idx == (1, 0)
+    over = R.copy()
+    over[0, 0] += 2.0 ** -19
+    assert not oracle.compare(over, R, tol)[0]
+    assert oracle.compare(np.zeros((0, 3)), np.zeros((0, 3)), np.zeros((0, 3)))[0]
+
+
+# A 2 x 2 by 2 x 3 product worked out by hand for the whole-matrix checks:
+#   A = [[1, -2], [3, 4]], B = [[1, -1, 2], [0, 3, -1]], C = [[1, -1, 0], [2, 0, 1]],
+#   alpha = 2, beta = -3.  AB = [[1, -7, 4], [3, 9, 2]] (sum 12), sum C = 3:
+#   checksum = 2*12 - 3*3 = 15;  magnitude = 2 * (colsum|A| . rowsum|B|)
+#   + 3 * sum|C| = 2 * ([4, 6] . [4, 4]) + 3 * 5 = 80 + 15 = 95.
+#   x = [1, -1, 1]: ABx = [12, -4], Cx = [2, 3], y = 2*ABx - 3*Cx = [18, -17];
+#   |B||x| = [4, 4], |A|[4, 4] = [12, 28], |C||x| = [2, 3]:
+#   magnitude = 2*[12, 28] + 3*[2, 3] = [30, 65].
+_HA = np.array([[1, -2], [3, 4]], np.float32)
+_HB = np.array([[1, -1, 2], [0, 3, -1]], np.float32)
+_HC = np.array([[1, -1, 0], [2, 0, 1]], np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "f16f32"])
+def test_checksum_and_freivalds_hand_computed(dtype):
+    tin, tc = (_NP[x] for x in wl.operand_types(dtype))
+    A = _buf(_HA.astype(tin), 3)
+    B = _buf(_HB.astype(tin), 5)
+    C = _buf(_HC.astype(tc), 4)
+    exp, mag = oracle.checksum(2, 3, 2, 2.0, A, 3, B, 5, -3.0, C, 4, dtype)
+    assert (exp, mag) == (15.0, 95.0)
+    y, ymag = oracle.freivalds(2, 3, 2, 2.0, A, 3, B, 5, -3.0, C, 4, np.array([1.0, -1.0, 1.0]),
+                               dtype)
+    np.testing.assert_array_equal(y, [18.0, -17.0])
+    np.testing.assert_array_equal(ymag, [30.0, 65.0])
+    # beta = 0: C is neither summed nor counted (its buffer may be absent)
+    exp, mag = oracle.checksum(2, 3, 2, 2.0, A, 3, B, 5, 0.0, None, 4, dtype)
+    assert (exp, mag) == (24.0, 80.0)
