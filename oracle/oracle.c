@@ -141,21 +141,48 @@ static void row_f32(int N, int K, const float *Arow, const float *B, long ldb,
     }
 }
 
-static void row_f16(int N, int K, const uint16_t *Arow, const uint16_t *B, long ldb,
-                    double *s, double *g, double *bdec)
+/* The same row for operands already decoded to double: A's row (K values)
+ * and B dense K x N.  Decoding is exact, so the sums equal those of the
+ * binary16 values themselves. */
+static void row_f64(int N, int K, const double *Arow, const double *B,
+                    double *s, double *g)
 {
     for (int j = 0; j < N; ++j) { s[j] = 0.0; g[j] = 0.0; }
     for (int k = 0; k < K; ++k) {
-        double a = oracle_half_to_double(Arow[k]);
+        double a = Arow[k];
         double aa = fabs(a);
-        const uint16_t *Bk = B + (size_t)k * (size_t)ldb;
-        for (int j = 0; j < N; ++j)
-            bdec[j] = oracle_half_to_double(Bk[j]);
+        const double *Bk = B + (size_t)k * (size_t)N;
         for (int j = 0; j < N; ++j) {
-            s[j] += a * bdec[j];
-            g[j] += aa * fabs(bdec[j]);
+            s[j] += a * Bk[j];
+            g[j] += aa * fabs(Bk[j]);
         }
     }
+}
+
+/* A rows x cols binary16 matrix (leading dimension ld) decoded once into a
+ * dense double array, so that each value is converted once per call rather
+ * than once per output row.  NULL on allocation failure. */
+static double *decode_dense(int rows, int cols, const uint16_t *X, long ld)
+{
+    double *d = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) *
+                                 (size_t)(cols > 0 ? cols : 1));
+    if (!d)
+        return NULL;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            d[(size_t)r * (size_t)cols + c] = oracle_half_to_double(X[(size_t)r * (size_t)ld + c]);
+    return d;
+}
+
+/* One output row of a binary16 product: A's row decoded into adec, then the
+ * double row above against the decoded B. */
+static void row_f16(int N, int K, const uint16_t *Arow, const double *Bdec,
+                    double *s, double *g, double *adec)
+{
+    for (int k = 0; k < K; ++k)
+        adec[k] = oracle_half_to_double(Arow[k]);
+    row_f64(N, K, adec, Bdec, s, g);
 }
 
 /* R := alpha*A*B + beta*C and G := |A||B| for fp32 inputs.
@@ -206,20 +233,27 @@ int oracle_gemm_f16(int M, int N, int K, double alpha,
 {
     int use_ab = (alpha != 0.0) && (K > 0);
     int err = 0;
+    double *bdec = NULL;
+    if (use_ab && M > 0) {
+        bdec = decode_dense(K, N, B, ldb);
+        if (!bdec)
+            return -1;
+    }
 #pragma omp parallel
     {
         size_t n1 = (size_t)(N > 0 ? N : 1);
-        double *s = (double *)malloc(sizeof(double) * n1 * 3);
+        size_t k1 = (size_t)(K > 0 ? K : 1);
+        double *s = (double *)malloc(sizeof(double) * (n1 * 2 + k1));
         if (!s) {
 #pragma omp atomic write
             err = -1;
         } else {
             double *g = s + n1;
-            double *bdec = s + 2 * n1;
+            double *adec = s + 2 * n1;
 #pragma omp for schedule(static)
             for (int i = 0; i < M; ++i) {
                 if (use_ab) {
-                    row_f16(N, K, A + (size_t)i * (size_t)lda, B, ldb, s, g, bdec);
+                    row_f16(N, K, A + (size_t)i * (size_t)lda, bdec, s, g, adec);
                 } else {
                     for (int j = 0; j < N; ++j) { s[j] = 0.0; g[j] = 0.0; }
                 }
@@ -234,6 +268,7 @@ int oracle_gemm_f16(int M, int N, int K, double alpha,
             free(s);
         }
     }
+    free(bdec);
     return err;
 }
 
@@ -249,20 +284,27 @@ int oracle_gemm_f16f32(int M, int N, int K, double alpha,
 {
     int use_ab = (alpha != 0.0) && (K > 0);
     int err = 0;
+    double *bdec = NULL;
+    if (use_ab && M > 0) {
+        bdec = decode_dense(K, N, B, ldb);
+        if (!bdec)
+            return -1;
+    }
 #pragma omp parallel
     {
         size_t n1 = (size_t)(N > 0 ? N : 1);
-        double *s = (double *)malloc(sizeof(double) * n1 * 3);
+        size_t k1 = (size_t)(K > 0 ? K : 1);
+        double *s = (double *)malloc(sizeof(double) * (n1 * 2 + k1));
         if (!s) {
 #pragma omp atomic write
             err = -1;
         } else {
             double *g = s + n1;
-            double *bdec = s + 2 * n1;
+            double *adec = s + 2 * n1;
 #pragma omp for schedule(static)
             for (int i = 0; i < M; ++i) {
                 if (use_ab) {
-                    row_f16(N, K, A + (size_t)i * (size_t)lda, B, ldb, s, g, bdec);
+                    row_f16(N, K, A + (size_t)i * (size_t)lda, bdec, s, g, adec);
                 } else {
                     for (int j = 0; j < N; ++j) { s[j] = 0.0; g[j] = 0.0; }
                 }
@@ -277,6 +319,7 @@ int oracle_gemm_f16f32(int M, int N, int K, double alpha,
             free(s);
         }
     }
+    free(bdec);
     return err;
 }
 

@@ -142,11 +142,13 @@ def bits(x, dtype):
     return np.asarray(x).view(np.uint16 if dtype == "f16" else np.uint32)
 
 
-def check_sampled(dtype, w, A, B, C, out, nrows=48, seed=0):
-    """Full-size parity on sampled rows (oracle on those rows only), the
-    whole-matrix checksum and Freivalds' product check."""
+def check_sampled(dtype, w, A, B, C, out, nrows=48, seed=0, extra_rows=()):
+    """Full-size parity on sampled rows (oracle on those rows only; seeded
+    random rows plus `extra_rows`), the whole-matrix checksum and Freivalds'
+    product check."""
     M, N, K = w.M, w.N, w.K
-    rows = wl.sample_rows(M, nrows, seed)
+    rows = np.union1d(wl.sample_rows(M, nrows, seed),
+                      np.array([r for r in extra_rows if 0 <= r < M], np.int64))
     t = _np_t(dtype)
     Av = wl.view(np.asarray(A), M, K, w.lda)[rows]
     Cv_full = wl.view(np.asarray(C), M, N, w.ldc)

@@ -55,28 +55,40 @@ def test_ragged_padded_unaligned(w):
     _w_run_check(w)
 
 
-def test_f32_4096_sampled():
-    w = wl.F32_4096
-    A, B, C = wl.make(w)
-    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+def _plan(w):
+    import dense_gemm_fp32_amd as dg
+    rc, text = dg.gemm_describe(w.dtype, w.M, w.N, w.K, w.alpha, 4096, w.lda, 4096, w.ldb, w.beta,
+                                4096, w.ldc)
     assert rc == 0
-    check_sampled(w.dtype, w, A, B, C, out)
+    return text
 
 
-def test_f16_4096_beta_half_sampled():
-    w = wl.F16_4096
+@pytest.mark.parametrize("w", [wl.F32_4096, wl.F16_4096, wl.F16F32_4096], ids=lambda w: w.name)
+def test_headline_4096_every_element(w):
+    """The 4096^3 workloads (fp32 with beta = 0; fp16 and fp16-in/fp32-out
+    with beta = 0.5), in the configuration the benchmark times, compared with
+    the full oracle element by element: all 16.7 million outputs."""
+    plan = _plan(w)
+    assert "256x256" in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
+@pytest.mark.parametrize("n", [1792, 2944, 3584])
+def test_f32_sweep_mid_sizes_sampled(n):
+    """Sweep sizes whose chosen plans split K: 1792^3 (every tile split),
+    2944^3 and 3584^3 (the last, partly filled round of tiles split), with
+    beta = 1, on sampled rows that include one row of each of the last eight
+    tile rows (where the split leftover tiles lie), the checksum and
+    Freivalds' check."""
+    w = wl.sweep(n)
+    plan = _plan(w)
+    assert "split-K" in plan, plan
     A, B, C = wl.make(w)
-    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                  "%s (%s)" % (w.name, plan))
     assert rc == 0
-    check_sampled(w.dtype, w, A, B, C, out)
-
-
-def test_f16f32_4096_beta_half_sampled():
-    w = wl.F16F32_4096
-    A, B, C = wl.make(w)
-    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, w.name)
-    assert rc == 0
-    check_sampled(w.dtype, w, A, B, C, out)
+    check_sampled(w.dtype, w, A, B, C, out, nrows=24, seed=n,
+                  extra_rows=[n - 1 - 128 * i - 37 for i in range(8)])
 
 
 def test_f32_sweep_endpoints_sampled():
@@ -820,16 +832,22 @@ def test_layouts_split_k(dtype, layout):
         _layout_run_check(dtype, layout, 129, 77, 515, (3, 1, 2), 401, label="split3 ragged")
 
 
+@pytest.mark.parametrize("cfg", [1, 6])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_layouts_large_sampled(dtype, layout):
-    """2048^3 with transposed operands on the large tiles (direct loads),
-    checked on sampled rows against the oracle."""
+def test_layouts_large_sampled(dtype, layout, cfg):
+    """2048^3 with transposed operands on each large tile, forced: fp32 256x128
+    (cfg 1) and 256x256 (cfg 6); fp16 256x256 on 16x16x32 blocks (cfg 1; with
+    both operands transposed that tile keeps 32x32x16 blocks) and on 32x32x16
+    blocks (cfg 6).  32 k-steps of the direct-load pipeline; sampled rows
+    against the oracle."""
     from gemm_harness import layout_case, run_layout
     n = 2048
     ta, tb = layout[0] == "t", layout[1] == "t"
     Abuf, Bbuf, Cbuf, A, B, C = layout_case(dtype, n, n, n, ta, tb, n, n, n, 500)
-    rc, out = run_layout(dtype, layout, n, n, n, 1.0, Abuf, n, Bbuf, n, 0.5, Cbuf, n, "large")
+    with tile_config(cfg):
+        rc, out = run_layout(dtype, layout, n, n, n, 1.0, Abuf, n, Bbuf, n, 0.5, Cbuf, n,
+                             "large cfg%d" % cfg)
     assert rc == 0
     rows = wl.sample_rows(n, 32, 7)
     R, G = oracle.gemm(len(rows), n, n, 1.0, np.ascontiguousarray(A[rows]).reshape(-1), n,
@@ -838,7 +856,7 @@ def test_layouts_large_sampled(dtype, layout):
                            oracle.out_type(dtype))
     got = wl.view(out, n, n, n)[rows]
     ok, worst, where = oracle.compare(np.ascontiguousarray(got), R, tol)
-    assert ok, "%s %s 2048^3 sampled: worst %.3g at %s" % (dtype, layout, worst, where)
+    assert ok, "%s %s cfg %d 2048^3 sampled: worst %.3g at %s" % (dtype, layout, cfg, worst, where)
 
 
 def test_tensor_wrapper_takes_transposed_views():

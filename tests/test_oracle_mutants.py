@@ -41,6 +41,11 @@ MUTANTS = [
     ("f16_ties_away", "(rem == 0.5 && fmod(fl, 2.0) != 0.0)", "(rem == 0.5)", 1),
     ("f16_truncate", "if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0))", "if (0)", 1),
     ("f16_no_overflow_check", "if (v > 65504.0)", "if (v > 65504.0 && 0)", 1),
+    ("f16_decode_ignores_ld", "X[(size_t)r * (size_t)ld + c]", "X[(size_t)r * (size_t)cols + c]", 1),
+    ("f16_decoded_B_stride", "const double *Bk = B + (size_t)k * (size_t)N;",
+     "const double *Bk = B + (size_t)k * (size_t)K;", 1),
+    ("f16_A_row_not_decoded_per_row", "adec[k] = oracle_half_to_double(Arow[k]);",
+     "adec[k] = oracle_half_to_double(Arow[0]);", 1),
     ("f16_elems_A_stride", "double a = oracle_half_to_double(A[i * (size_t)lda + k]);",
      "double a = oracle_half_to_double(A[i * (size_t)K + k]);", 1),
     ("mixed_beta_dropped", "r += beta * (double)C[(size_t)i * (size_t)ldc + j];", "r += 0.0;", 2),
