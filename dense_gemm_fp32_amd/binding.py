@@ -46,14 +46,16 @@ _lib.gemm_set_split.argtypes = [_I]
 _lib.gemm_set_split.restype = _I
 _lib.gemm_set_tail_split.argtypes = [_I]
 _lib.gemm_set_tail_split.restype = _I
+_lib.gemm_set_workspace_limit.argtypes = [ctypes.c_longlong]
+_lib.gemm_set_workspace_limit.restype = ctypes.c_longlong
 _lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
                                  ctypes.POINTER(ctypes.c_double), _P]
 _lib.gemm_probe_mfma.restype = _I
 
-EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_colmajor",
-           "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
-           "gemm_set_tile_config", "gemm_set_split", "gemm_set_tail_split",
-           "gemm_probe_mfma") + LAYOUT_NAMES
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu",
+           "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string",
+           "gemm_describe", "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split",
+           "gemm_set_tail_split", "gemm_set_workspace_limit", "gemm_probe_mfma") + LAYOUT_NAMES
 
 
 class GemmError(RuntimeError):
@@ -180,6 +182,13 @@ def gemm_set_tail_split(mode):
     """fp32: 0 = split the last partly filled round of tiles by size
     (default), 1 = never, 2..64 = force that many K chunks for it."""
     return _lib.gemm_set_tail_split(int(mode))
+
+
+def gemm_set_workspace_limit(nbytes):
+    """Cap on one call's split-K workspace from the pool: -1 = none
+    (default), 0 = never split, n = splits needing more than n bytes run
+    unsplit.  Returns the previous setting."""
+    return _lib.gemm_set_workspace_limit(int(nbytes))
 
 
 def gemm_set_split(mode):

@@ -19,6 +19,7 @@ std::atomic<int> g_load_mode{0};
 std::atomic<int> g_tile_config{0};
 std::atomic<int> g_split_mode{0};
 std::atomic<int> g_tail_mode{0};
+std::atomic<long long> g_ws_limit{-1};
 
 // Shared argument checks.  ta / tb: A is stored transposed (K x M, so its
 // rows hold M elements) / B is (N x K, rows of K); otherwise A is M x K and B
@@ -101,6 +102,9 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.tile_count = 0;
   c.c_tiles = false;
   c.tail_mode = g_tail_mode.load(std::memory_order_relaxed);
+  c.ws_limit = g_ws_limit.load(std::memory_order_relaxed);
+  c.ws_fixed = nullptr;
+  c.ws_fixed_bytes = 0;
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -296,9 +300,11 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
         char split[48] = "";
         if (p.splits > 1) snprintf(split, sizeof split, " split-K %d", p.splits);
         else if (p.tail > 1) snprintf(split, sizeof split, " last round split-K %d", p.tail);
-        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s",
+        char ws[48] = "";
+        if (p.ws_bytes > 0) snprintf(ws, sizeof ws, " workspace %zu bytes", p.ws_bytes);
+        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s%s",
                  p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",
-                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split,
+                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split, ws,
                  beta == 0.0f ? " beta0 (C not read)" : "");
         break;
       }
@@ -343,6 +349,11 @@ int gemm_set_tail_split(int mode) {
 int gemm_set_tile_config(int config) {
   if (config < 0 || config > 6) return -1;
   return g_tile_config.exchange(config);
+}
+
+long long gemm_set_workspace_limit(long long bytes) {
+  if (bytes < -1) return -2;
+  return g_ws_limit.exchange(bytes);
 }
 
 }  // extern "C"

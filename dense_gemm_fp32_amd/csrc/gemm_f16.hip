@@ -889,6 +889,7 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.blocks = tm * tn;
   pl.splits = 1;
   pl.tail = 1;
+  pl.ws_bytes = 0;
   return pl;
 }
 
@@ -1078,8 +1079,7 @@ static hipError_t launch_cfg(const Call &c, int want) {
   const int ldw = (c.N + 3) / 4 * 4;
   const long long stride = (long long)c.M * ldw;
   void *ws = nullptr;
-  if (workspace_alloc(c.stream, (size_t)S * (size_t)stride * sizeof(float), &ws) != hipSuccess)
-    return dispatch<T>(c);
+  if (workspace_alloc(c, split_ws_bytes(S, c.M, c.N), &ws) != hipSuccess) return dispatch<T>(c);
   Call pc = c;
   pc.C = ws;
   pc.ldc = ldw;
@@ -1106,7 +1106,7 @@ static hipError_t launch_cfg(const Call &c, int want) {
     r.force_scalar = c.force_scalar;
     e = launch_splitk_reduce(r, c.stream);
   }
-  const hipError_t f = workspace_free(c.stream, ws);
+  const hipError_t f = workspace_free(c, ws);
   return e != hipSuccess ? e : f;
 }
 
@@ -1115,6 +1115,7 @@ static Plan plan_cfg(const Call &c, const char *name, int want) {
   Plan pl = make_plan<T>(c, name);
   int kc = 0;
   pl.splits = clamp_splits(c, want, T::BK, pl.blocks, &kc);
+  pl.ws_bytes = pl.splits > 1 ? split_ws_bytes(pl.splits, c.M, c.N) : 0;
   return pl;
 }
 

@@ -851,6 +851,7 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.blocks = c.tile_count > 0 ? c.tile_count : tm * tn;
   pl.splits = 1;
   pl.tail = 1;
+  pl.ws_bytes = 0;
   return pl;
 }
 
@@ -1168,8 +1169,7 @@ static bool launch_tail(const Call &c, int want, hipError_t *err) {
   const int S = clamp_splits(tc, want, T::BK, rest, &kc, (long long)rest * (long long)block);
   if (S <= 1) return false;
   void *ws = nullptr;
-  if (workspace_alloc(c.stream, (size_t)S * (size_t)rest * block * sizeof(float), &ws) != hipSuccess)
-    return false;
+  if (workspace_alloc(c, tail_ws_bytes(S, rest, T::BM, T::BN), &ws) != hipSuccess) return false;
   Call dc = c;
   dc.tile_base = 0;
   dc.tile_count = (int)full;
@@ -1205,7 +1205,7 @@ static bool launch_tail(const Call &c, int want, hipError_t *err) {
     r.force_scalar = c.force_scalar;
     e = launch_tile_reduce(r, c.stream);
   }
-  const hipError_t f = workspace_free(c.stream, ws);
+  const hipError_t f = workspace_free(c, ws);
   *err = e != hipSuccess ? e : f;
   return true;
 }
@@ -1220,8 +1220,7 @@ static hipError_t launch_cfg(const Call &c, int want, int tail = 1) {
   const int ldw = (c.N + 3) / 4 * 4;
   const long long stride = (long long)c.M * ldw;
   void *ws = nullptr;
-  if (workspace_alloc(c.stream, (size_t)S * (size_t)stride * sizeof(float), &ws) != hipSuccess)
-    return dispatch<T>(c);
+  if (workspace_alloc(c, split_ws_bytes(S, c.M, c.N), &ws) != hipSuccess) return dispatch<T>(c);
   Call pc = c;
   pc.C = ws;
   pc.ldc = ldw;
@@ -1247,7 +1246,7 @@ static hipError_t launch_cfg(const Call &c, int want, int tail = 1) {
     r.force_scalar = c.force_scalar;
     e = launch_splitk_reduce(r, c.stream);
   }
-  const hipError_t f = workspace_free(c.stream, ws);
+  const hipError_t f = workspace_free(c, ws);
   return e != hipSuccess ? e : f;
 }
 
@@ -1267,10 +1266,12 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
                              (long long)rest * (long long)(T::BM * T::BN));
     if (pl.tail > 1) {
       pl.splits = 1;
+      pl.ws_bytes = tail_ws_bytes(pl.tail, rest, T::BM, T::BN);
       return pl;
     }
   }
   pl.splits = clamp_splits(c, want, T::BK, pl.blocks, &kc);
+  pl.ws_bytes = pl.splits > 1 ? split_ws_bytes(pl.splits, c.M, c.N) : 0;
   return pl;
 }
 

@@ -35,6 +35,13 @@ struct Call {
   int tile_config;       // diagnostic: 0 = by size, 1/2/3/4 = large/medium/small/tiny,
                          // 5 = medium with the loads of a step issued together,
                          // 6 = fp32 256x256 (fp16: its large tile)
+  // Split-K workspace source: the library's per-device pool (ws_fixed ==
+  // nullptr), requests above ws_limit bytes failing (-1: no limit), or a
+  // fixed device region of ws_fixed_bytes bytes that is never allocated or
+  // freed (the entry point that allocates nothing).
+  long long ws_limit;
+  void *ws_fixed;
+  size_t ws_fixed_bytes;
   hipStream_t stream;
 };
 
@@ -47,6 +54,7 @@ struct Plan {
   long long blocks;          // tiles
   int splits;                // K chunks (1 = no split)
   int tail;                  // K chunks of the last round's tiles (1 = none)
+  size_t ws_bytes;           // split-K workspace the call takes (0 = none)
 };
 
 // The reduction pass of a split-K run of tiles: for each of `tiles` tiles
@@ -80,9 +88,24 @@ struct SplitReduce {
   bool force_scalar;
 };
 
-// Workspace from the library's per-device memory pool, ordered on stream s.
-hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr);
-hipError_t workspace_free(hipStream_t s, void *ptr);
+// Split-K workspace of `bytes` bytes for call c, ordered on c.stream: from
+// c's fixed region when it has one (no allocation; fails if too small), else
+// from the library's per-device memory pool (fails above c.ws_limit).  A
+// launcher that cannot get its workspace runs the call unsplit.
+hipError_t workspace_alloc(const Call &c, size_t bytes, void **ptr);
+hipError_t workspace_free(const Call &c, void *ptr);
+
+// Bytes of a whole split-K workspace (S slabs of M x ceil(N/4)*4 floats) and
+// of a last-round split (S dense BM x BN fp32 blocks per leftover tile).
+inline size_t split_ws_bytes(int S, int M, int N) {
+  return (size_t)S * (size_t)M * (size_t)((N + 3) / 4 * 4) * sizeof(float);
+}
+inline size_t tail_ws_bytes(int S, int tiles, int BM, int BN) {
+  return (size_t)S * (size_t)tiles * (size_t)BM * (size_t)BN * sizeof(float);
+}
+
+// Device a stream belongs to (NULL stream: the current device); -1 on error.
+int stream_device(hipStream_t s);
 hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s);
 
 // Split count for a problem with `tiles` tiles of K step `bk`, given the

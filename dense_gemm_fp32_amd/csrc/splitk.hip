@@ -18,8 +18,12 @@
 // with stream-ordered allocation on the call's stream: it is taken before
 // the GEMM pass and given back after the reduction, in stream order, so
 // concurrent calls on different streams never share it and nothing is
-// synchronised.  Freed blocks stay in the pool for later calls, and every
-// request is made at the largest size used so far (see workspace_alloc).
+// synchronised.  Freed blocks stay in the pool for later calls up to a release
+// threshold (kPoolKeep), beyond which the runtime returns the memory at the
+// next synchronisation; every request is made at the largest size used so far
+// (see workspace_alloc).  A caller may cap the workspace of a call
+// (gemm_set_workspace_limit); a call that cannot get its workspace runs
+// unsplit.
 #include <mutex>
 
 #include "common.hpp"
@@ -30,6 +34,9 @@ namespace dgemm {
 namespace {
 
 constexpr int kMaxDevices = 64;
+// Freed workspace the pool keeps for later calls; memory beyond it goes back
+// to the runtime at the next synchronisation.
+constexpr uint64_t kPoolKeep = (uint64_t)256 << 20;
 std::mutex g_pool_mu;
 hipMemPool_t g_pool[kMaxDevices];
 bool g_pool_made[kMaxDevices];
@@ -45,20 +52,13 @@ hipError_t pool_for(int dev, hipMemPool_t *out) {
     props.location.id = dev;
     hipError_t e = hipMemPoolCreate(&g_pool[dev], &props);
     if (e != hipSuccess) return e;
-    uint64_t keep = UINT64_MAX;   // keep freed blocks for the next call
+    uint64_t keep = kPoolKeep;
     e = hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
     if (e != hipSuccess) return e;
     g_pool_made[dev] = true;
   }
   *out = g_pool[dev];
   return hipSuccess;
-}
-
-int stream_device(hipStream_t s) {
-  int dev = -1;
-  if (s != nullptr && hipStreamGetDevice(s, &dev) == hipSuccess) return dev;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  return dev;
 }
 
 constexpr int kReduceThreads = 256;
@@ -239,15 +239,28 @@ int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk,
   return S;
 }
 
-// Every request asks for the largest size requested so far on the device
-// (in 2 MiB steps), so a freed block always fits the next request: measured,
-// a request larger than the blocks the pool holds costs ~30 us more than one
-// it can serve from a freed block, and the pool does not reuse a block
-// across different sizes.  The pool thus holds at most a few blocks of the
-// largest workspace in use (bounded by the 1 GiB cap per call).
-hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr) {
+int stream_device(hipStream_t s) {
+  int dev = -1;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) == hipSuccess) return dev;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return dev;
+}
+
+// Pool requests ask for the largest size requested so far on the device (in
+// 2 MiB steps), so a freed block always fits the next request: measured, a
+// request larger than the blocks the pool holds costs ~30 us more than one it
+// can serve from a freed block, and the pool does not reuse a block across
+// different sizes.  A call with a fixed region uses it when it is large
+// enough and never touches the pool.
+hipError_t workspace_alloc(const Call &c, size_t bytes, void **ptr) {
   *ptr = nullptr;
-  const int dev = stream_device(s);
+  if (c.ws_fixed != nullptr) {
+    if (bytes > c.ws_fixed_bytes) return hipErrorOutOfMemory;
+    *ptr = c.ws_fixed;
+    return hipSuccess;
+  }
+  if (c.ws_limit >= 0 && (long long)bytes > c.ws_limit) return hipErrorOutOfMemory;
+  const int dev = stream_device(c.stream);
   hipMemPool_t pool;
   hipError_t e = pool_for(dev, &pool);
   if (e != hipSuccess) return e;
@@ -258,7 +271,7 @@ hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr) {
     if (bytes > g_high_water[dev]) g_high_water[dev] = bytes;
     bytes = g_high_water[dev];
   }
-  e = hipMallocFromPoolAsync(ptr, bytes, pool, s);
+  e = hipMallocFromPoolAsync(ptr, bytes, pool, c.stream);
   if (e != hipSuccess) {
     *ptr = nullptr;
     (void)hipGetLastError();   // a failed allocation is not the caller's error
@@ -266,8 +279,9 @@ hipError_t workspace_alloc(hipStream_t s, size_t bytes, void **ptr) {
   return e;
 }
 
-hipError_t workspace_free(hipStream_t s, void *ptr) {
-  return ptr ? hipFreeAsync(ptr, s) : hipSuccess;
+hipError_t workspace_free(const Call &c, void *ptr) {
+  if (ptr == nullptr || c.ws_fixed != nullptr) return hipSuccess;
+  return hipFreeAsync(ptr, c.stream);
 }
 
 hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s) {

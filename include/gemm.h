@@ -44,14 +44,18 @@
  *   - A, B and C are DEVICE pointers owned by the caller.  The library keeps
  *     no pointer to them after it returns and never allocates or frees the
  *     caller's memory.
- *   - A split-K call needs S*M*ceil(N/4)*16 bytes of workspace (at most
- *     1 GiB; larger splits are not taken) and takes it from a memory pool the
- *     library creates per device, with stream-ordered allocation on the
- *     call's stream, returning it to the pool, in stream order, after its
- *     last kernel.  Requests are made at the largest size used so far on the
- *     device (2 MiB steps) so that freed blocks are reused; they stay in the
- *     pool until the process ends.  If the workspace cannot be had the call
- *     runs without splitting.
+ *   - A split-K call needs S*M*ceil(N/4)*16 bytes of workspace (a last-round
+ *     split S*tiles*BM*BN*4 bytes; at most 1 GiB, larger splits are not
+ *     taken) and takes it from a memory pool the library creates per device,
+ *     with stream-ordered allocation on the call's stream, returning it to
+ *     the pool, in stream order, after its last kernel.  Requests are made at
+ *     the largest size used so far on the device (2 MiB steps) so that freed
+ *     blocks are reused; the pool keeps up to 256 MiB of freed blocks and
+ *     hands the rest back to the runtime at the next synchronisation.
+ *     gemm_set_workspace_limit caps the workspace of a call.  If the workspace
+ *     cannot be had the call runs without splitting (same bound; the
+ *     summation order is then that of an unsplit call).  gemm_describe
+ *     reports the workspace a call would take.
  *   - C must not overlap A or B.
  *   - The pad elements of each row (columns K..lda-1 of A, N..ldb-1 of B,
  *     N..ldc-1 of C) are never read or written.
@@ -289,6 +293,15 @@ int gemm_set_split(int mode);
  * for an unknown value.
  */
 int gemm_set_tail_split(int mode);
+
+/*
+ * Cap on the split-K workspace one call may take from the library's pool, in
+ * bytes: -1 = no cap (the default), 0 = never use workspace (every call runs
+ * unsplit), n > 0 = calls whose split needs more than n bytes run unsplit.
+ * Process-wide, like gemm_set_load_mode.
+ * Returns the previous setting, or -2 for a value below -1.
+ */
+long long gemm_set_workspace_limit(long long bytes);
 
 /*
  * Matrix-core ceiling probe: a measurement aid, not a GEMM.  It bounds what

@@ -373,3 +373,26 @@ def test_tail_split_in_descriptions():
     # the square 4096 workload stays whole: 512 tiles fill two rounds
     rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
     assert "split" not in text, text
+
+
+def test_describe_reports_split_workspace():
+    """The workspace a split call takes, worked out by hand: 1792^3 splits the
+    128 x 128 tiles 5 ways into M x N fp32 slabs, 5 * 1792 * 1792 * 4 bytes;
+    2944^3 (23 x 23 = 529 tiles of 128 x 128, 2 whole rounds of 256 and 17
+    left over) splits the 17 leftover tiles 15 ways into dense tile blocks,
+    15 * 17 * 128 * 128 * 4 bytes.  An unsplit call takes none."""
+    import dense_gemm_fp32_amd as dg
+    cases = [(1792, "split-K 5", 64225280), (2944, "last round split-K 15", 16711680)]
+    for n, split, nbytes in cases:
+        rc, text = dg.gemm_describe("f32", n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
+        assert rc == 0 and split in text and ("workspace %d bytes" % nbytes) in text, text
+    rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
+    assert rc == 0 and "workspace" not in text, text
+
+
+def test_workspace_limit_switch():
+    import dense_gemm_fp32_amd as dg
+    assert dg.gemm_set_workspace_limit(0) == -1
+    assert dg.gemm_set_workspace_limit(1 << 20) == 0
+    assert dg.gemm_set_workspace_limit(-5) == -2
+    assert dg.gemm_set_workspace_limit(-1) == 1 << 20

@@ -1074,3 +1074,48 @@ def test_calls_replay_from_a_captured_graph():
                 torch.cuda.synchronize()
                 assert torch.equal(C, ref), (dtype, M, N, K, split, tail, rep)
             del graph
+
+
+@contextmanager
+def workspace_limit(nbytes):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_workspace_limit(nbytes)
+    try:
+        yield
+    finally:
+        dg.gemm_set_workspace_limit(prev)
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 1792, 1792, 1792), ("f32", 2944, 2944, 2944),
+                                         ("f16", 512, 512, 8192), ("f16f32", 512, 512, 8192)])
+def test_workspace_refused_runs_unsplit(dtype, M, N, K):
+    """With the workspace limit at 0 every split request fails: the call runs
+    unsplit (the fallback the header promises), bitwise equal to the same call
+    with splitting switched off, and within the bound of the oracle.  Then a
+    limit just below the call's workspace does the same, and a limit at it lets
+    the call split again (bitwise equal to the default)."""
+    import dense_gemm_fp32_amd as dg
+    w = wl.Workload("wslimit_%s_%d" % (dtype, M), dtype, M, N, K, K, N, N, 1.0, 0.5, "uniform",
+                    "uniform", (31, 32, 33))
+    rc, plan = dg.gemm_describe(dtype, M, N, K, 1.0, 4096, K, 4096, N, 0.5, 4096, N)
+    assert rc == 0 and "workspace" in plan, plan
+    nbytes = int(plan.split("workspace ")[1].split()[0])
+    A, B, C = wl.make(w)
+    with workspace_limit(0):
+        rc, out0 = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "limit 0 (%s)" % plan)
+    assert rc == 0
+    with workspace_limit(nbytes - 1):
+        rc, out1 = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "limit below")
+    assert rc == 0
+    with split_mode(1), tail_split(1):
+        rc, ref = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "unsplit")
+    assert rc == 0
+    assert np.array_equal(bits(out0, dtype), bits(ref, dtype))
+    assert np.array_equal(bits(out1, dtype), bits(ref, dtype))
+    check(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, out0, "workspace refused")
+    with workspace_limit(nbytes):
+        rc, out2 = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "limit at")
+    assert rc == 0
+    rc, dflt = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "default")
+    assert rc == 0
+    assert np.array_equal(bits(out2, dtype), bits(dflt, dtype))
