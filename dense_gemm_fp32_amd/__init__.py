@@ -9,12 +9,12 @@ without the library; using the GEMM entry points without a built library
 raises ImportError.
 """
 _LAYOUT_NAMES = tuple("gemm_%s_%s" % (t, l) for t in ("f32", "f16", "f16f32") for l in ("nt", "tn", "tt"))
-_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu",
+_BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_noalloc",
                   "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor",
                   "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
                   "gemm_set_tile_config", "gemm_set_split", "gemm_set_tail_split",
                   "gemm_set_workspace_limit", "gemm_probe_mfma", "gemm", "GemmError",
-                  "LIB_PATH", "EXPORTS", "LAYOUT_NAMES") + _LAYOUT_NAMES
+                  "GEMM_ERR_SCRATCH_LIMIT", "LIB_PATH", "EXPORTS", "LAYOUT_NAMES") + _LAYOUT_NAMES
 
 __all__ = list(_BINDING_NAMES)
 

@@ -31,7 +31,7 @@ _lib.gemm_f16f32.argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
 _lib.gemm_f16f32.restype = _I
 LAYOUT_NAMES = tuple("gemm_%s_%s" % (t, l) for t in ("f32", "f16", "f16f32") for l in ("nt", "tn", "tt"))
 for _n in ("gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor",
-           "gemm_f32_valu") + LAYOUT_NAMES:
+           "gemm_f32_valu", "gemm_f32_noalloc") + LAYOUT_NAMES:
     getattr(_lib, _n).argtypes = [_I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
     getattr(_lib, _n).restype = _I
 _lib.gemm_status_string.argtypes = [_I]
@@ -52,10 +52,11 @@ _lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_
                                  ctypes.POINTER(ctypes.c_double), _P]
 _lib.gemm_probe_mfma.restype = _I
 
-EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu",
+EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_noalloc",
            "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string",
            "gemm_describe", "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split",
            "gemm_set_tail_split", "gemm_set_workspace_limit", "gemm_probe_mfma") + LAYOUT_NAMES
+GEMM_ERR_SCRATCH_LIMIT = -200
 
 
 class GemmError(RuntimeError):
@@ -106,6 +107,14 @@ def gemm_f32_valu(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
     include/gemm.h)."""
     return _lib.gemm_f32_valu(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                               _stream(stream))
+
+
+def gemm_f32_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """gemm_f32 with its split-K workspace in the library's fixed scratch
+    region: no allocation (see include/gemm.h); GEMM_ERR_SCRATCH_LIMIT when
+    the call would need more workspace than the region holds."""
+    return _lib.gemm_f32_noalloc(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C),
+                                 ldc, _stream(stream))
 
 
 def gemm_f32_colmajor(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):

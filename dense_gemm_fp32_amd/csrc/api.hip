@@ -201,6 +201,39 @@ int gemm_f16f32_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int l
   return run_gemm(2, true, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
+// gemm_f32 for callers that cannot allocate: the same checks, plan and
+// kernels, with the split-K workspace taken from the library's fixed scratch
+// region instead of its memory pool.  A call whose plan needs more workspace
+// than the region holds is refused before anything is enqueued.
+int gemm_f32_noalloc(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                     int ldb, float beta, float *C, int ldc, void *stream) {
+  const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (rc != 0) return rc;
+  hipError_t e = hipSuccess;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (route(M, N, K, alpha, beta)) {
+    case Route::kNothing:
+      return GEMM_SUCCESS;
+    case Route::kScale:
+      e = dgemm::launch_scale_f32(M, N, beta, C, ldc, s);
+      break;
+    case Route::kGemm: {
+      dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+      const dgemm::Plan p = dgemm::plan_f32(c);
+      if (p.ws_bytes > dgemm::kScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
+      if (p.ws_bytes > 0) {
+        const int dev = dgemm::stream_device(s);
+        e = dgemm::scratch_region(dev, &c.ws_fixed);
+        if (e != hipSuccess) return (int)e;
+        c.ws_fixed_bytes = dgemm::kScratchBytes;
+      }
+      e = dgemm::launch_f32(c);
+      break;
+    }
+  }
+  return e == hipSuccess ? GEMM_SUCCESS : (int)e;
+}
+
 int gemm_f32_valu(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                   int ldb, float beta, float *C, int ldc, void *stream) {
   const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
@@ -261,6 +294,7 @@ const char *gemm_status_string(int status) {
     case -8: return "invalid argument 8: ldb < max(1, row length of B as stored: N, or K when B is stored transposed or column-major)";
     case -10: return "invalid argument 10: C is NULL";
     case -11: return "invalid argument 11: ldc < max(1, N) (row-major) or max(1, M) (column-major)";
+    case GEMM_ERR_SCRATCH_LIMIT: return "gemm_f32_noalloc: the call's split-K workspace would exceed the library's fixed scratch region (64 MiB); nothing was enqueued";
     case -101: return "invalid probe argument 1: dtype is not 0 (fp32) or 1 (fp16)";
     case -102: return "invalid probe argument 2: iters < 1";
     case -103: return "invalid probe argument 3: operands is NULL";

@@ -104,6 +104,11 @@ inline size_t tail_ws_bytes(int S, int tiles, int BM, int BN) {
   return (size_t)S * (size_t)tiles * (size_t)BM * (size_t)BN * sizeof(float);
 }
 
+// The fixed scratch region of the entry point that allocates nothing: a
+// file-scope device array of kScratchBytes bytes, its address on device
+// `dev` looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_region(int dev, void **ptr);
 // Device a stream belongs to (NULL stream: the current device); -1 on error.
 int stream_device(hipStream_t s);
 hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s);

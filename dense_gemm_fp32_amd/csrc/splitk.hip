@@ -24,6 +24,9 @@
 // (see workspace_alloc).  A caller may cap the workspace of a call
 // (gemm_set_workspace_limit); a call that cannot get its workspace runs
 // unsplit.
+//
+// The entry point that allocates nothing takes its workspace from `scratch`,
+// a file-scope device array of fixed size, instead of the pool.
 #include <mutex>
 
 #include "common.hpp"
@@ -60,6 +63,14 @@ hipError_t pool_for(int dev, hipMemPool_t *out) {
   *out = g_pool[dev];
   return hipSuccess;
 }
+
+// The no-allocation entry point's workspace: one copy per device, alive until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device memory: its device address comes from hipGetSymbolAddress,
+// looked up once per device (with that device current) and kept.
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
 
 constexpr int kReduceThreads = 256;
 constexpr unsigned kReduceMaxBlocks = 8192;
@@ -244,6 +255,27 @@ int stream_device(hipStream_t s) {
   if (s != nullptr && hipStreamGetDevice(s, &dev) == hipSuccess) return dev;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   return dev;
+}
+
+hipError_t scratch_region(int dev, void **ptr) {
+  *ptr = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (r != hipSuccess) return r;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // Pool requests ask for the largest size requested so far on the device (in

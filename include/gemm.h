@@ -56,6 +56,9 @@
  *     cannot be had the call runs without splitting (same bound; the
  *     summation order is then that of an unsplit call).  gemm_describe
  *     reports the workspace a call would take.
+ *   - gemm_f32_noalloc is gemm_f32 without any allocation: its workspace is a
+ *     fixed 64 MiB region of device memory owned by the library (one per
+ *     device, held until the process ends).
  *   - C must not overlap A or B.
  *   - The pad elements of each row (columns K..lda-1 of A, N..ldb-1 of B,
  *     N..ldc-1 of C) are never read or written.
@@ -87,6 +90,9 @@
  *                     Argument checks make no HIP call, so they work without
  *                     a GPU.
  *   > 0               a hipError_t from the kernel launch.
+ *   GEMM_ERR_SCRATCH_LIMIT (gemm_f32_noalloc only) the call would need more
+ *                     split-K workspace than the fixed scratch region holds;
+ *                     nothing was enqueued.
  */
 #ifndef DENSE_GEMM_GEMM_H
 #define DENSE_GEMM_GEMM_H
@@ -102,6 +108,7 @@ extern "C" {
 typedef uint16_t gemm_half_t;
 
 #define GEMM_SUCCESS 0
+#define GEMM_ERR_SCRATCH_LIMIT (-200)
 
 /*
  * fp32 GEMM: A, B, C hold binary32 values; products are accumulated in fp32
@@ -147,6 +154,30 @@ int gemm_f16f32(int M, int N, int K, float alpha,
                 const gemm_half_t *B, int ldb,
                 float beta, float *C, int ldc,
                 void *stream);
+
+/*
+ * gemm_f32 for callers that cannot allocate device memory: code under HIP
+ * graph capture that must not add allocation nodes, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, semantics, plan, kernels
+ * and results (bit for bit) as gemm_f32; the caller still passes A, B and C.
+ * The only difference is where a split-K call's workspace comes from: a
+ * file-scope device array of 64 MiB inside the library (one copy per device,
+ * held until the process ends) instead of the memory pool, so the call makes
+ * no hipMalloc, hipFree or pool allocation.  A call whose plan would need
+ * more workspace than that returns GEMM_ERR_SCRATCH_LIMIT before enqueuing
+ * anything (gemm_describe reports the workspace a call would take).  Nothing
+ * in the region needs to start at zero: every split pass writes the values
+ * its reduction reads.  All calls on one device share the region, which keeps
+ * the last call's contents: calls that may overlap on one device (different
+ * streams without ordering between them) race on it, so order them (one
+ * stream, or events).  The first call on a device looks up the region's
+ * address there (hipGetSymbolAddress).
+ */
+int gemm_f32_noalloc(int M, int N, int K, float alpha,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float beta, float *C, int ldc,
+                     void *stream);
 
 /*
  * fp32 GEMM on the vector ALUs instead of the matrix cores: the SIMT design of
@@ -298,7 +329,7 @@ int gemm_set_tail_split(int mode);
  * Cap on the split-K workspace one call may take from the library's pool, in
  * bytes: -1 = no cap (the default), 0 = never use workspace (every call runs
  * unsplit), n > 0 = calls whose split needs more than n bytes run unsplit.
- * Process-wide, like gemm_set_load_mode.
+ * Process-wide, like gemm_set_load_mode; gemm_f32_noalloc ignores it.
  * Returns the previous setting, or -2 for a value below -1.
  */
 long long gemm_set_workspace_limit(long long bytes);

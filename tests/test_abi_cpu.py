@@ -69,7 +69,8 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu",
+                                "gemm_f32_noalloc"])
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_argument_checks_and_quick_returns(fn, case):
     import dense_gemm_fp32_amd as dg
@@ -77,7 +78,7 @@ def test_argument_checks_and_quick_returns(fn, case):
     assert getattr(dg, fn)(*args, None) == expected
     # gemm_describe applies the same checks
     rc, text = dg.gemm_describe({"gemm_f32": "f32", "gemm_f16": "f16", "gemm_f16f32": "f16f32",
-                                 "gemm_f32_valu": "f32"}[fn], *args)
+                                 "gemm_f32_valu": "f32", "gemm_f32_noalloc": "f32"}[fn], *args)
     assert rc == expected
     if expected < 0:
         assert text.startswith("invalid")
@@ -388,6 +389,23 @@ def test_describe_reports_split_workspace():
         assert rc == 0 and split in text and ("workspace %d bytes" % nbytes) in text, text
     rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
     assert rc == 0 and "workspace" not in text, text
+
+
+def test_noalloc_refuses_workspace_beyond_the_scratch_region():
+    """3000 x 3000 x 30000 splits K 8 ways into 288,000,000 bytes of slabs,
+    more than the 64 MiB scratch region: gemm_f32_noalloc refuses before any
+    HIP call (so this runs without a GPU; the pointers are never touched),
+    while its argument checks come first."""
+    import dense_gemm_fp32_amd as dg
+    rc, text = dg.gemm_describe("f32", 3000, 3000, 30000, 1.0, FAKE, 30000, FAKE, 3000, 0.0, FAKE,
+                                3000)
+    assert "workspace 288000000 bytes" in text, text
+    assert dg.gemm_f32_noalloc(3000, 3000, 30000, 1.0, FAKE, 30000, FAKE, 3000, 0.0, FAKE, 3000,
+                               None) == dg.GEMM_ERR_SCRATCH_LIMIT
+    assert dg.gemm_f32_noalloc(3000, 3000, 30000, 1.0, FAKE, 29999, FAKE, 3000, 0.0, FAKE, 3000,
+                               None) == -6
+    msg = dg.gemm_status_string(dg.GEMM_ERR_SCRATCH_LIMIT)
+    assert "scratch" in msg and "nothing was enqueued" in msg
 
 
 def test_workspace_limit_switch():

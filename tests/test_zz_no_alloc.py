@@ -1,0 +1,90 @@
+"""gemm_f32_noalloc, the entry point for callers that cannot allocate, against
+gemm_f32 on the same inputs: same plan, same kernels, so the results must be
+the same bits, and both within the accuracy bound of the oracle.  The calls
+come in a row on one device, so the library's fixed scratch region is reused
+with the previous call's contents still in it; the second call is smaller
+than the first."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gemm_harness import bits, check, check_sampled, note, run
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(w):
+    import dense_gemm_fp32_amd as dg
+    rc, text = dg.gemm_describe("f32", w.M, w.N, w.K, w.alpha, 4096, w.lda, 4096, w.ldb, w.beta,
+                                4096, w.ldc)
+    assert rc == 0
+    return text
+
+
+def _both(w):
+    """Outputs of gemm_f32_noalloc and gemm_f32 on fresh copies of w's inputs."""
+    A, B, C = wl.make(w)
+    plan = _plan(w)
+    rc, out_na = run("f32", w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                     "%s noalloc (%s)" % (w.name, plan), entry="gemm_f32_noalloc")
+    assert rc == 0
+    rc, out_ref = run("f32", w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                      "%s gemm_f32" % w.name)
+    assert rc == 0
+    return plan, (A, B, C), out_na, out_ref
+
+
+def test_noalloc_matches_gemm_f32_on_calls_in_a_row():
+    # 1) 1792^3, beta = 1: K split 5 ways into M x N slabs, 64,225,280 bytes
+    #    of the 64 MiB region.
+    w1 = wl.sweep(1792)
+    plan, (A, B, C), out_na, out_ref = _both(w1)
+    assert "split-K 5" in plan and "workspace 64225280 bytes" in plan, plan
+    assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
+    check_sampled("f32", w1, A, B, C, out_na, nrows=16, seed=3)
+
+    # 2) smaller: the ragged 1000 x 3000 x 517 workload (unaligned lda, all
+    #    three tails), K split 4 ways, 48,000,000 bytes; the region still holds
+    #    the first call's slabs beyond that.
+    w2 = wl.RAGGED_F32
+    plan, (A, B, C), out_na, out_ref = _both(w2)
+    assert "split-K 4" in plan and "workspace 48000000 bytes" in plan, plan
+    assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
+    check("f32", w2.M, w2.N, w2.K, w2.alpha, A, w2.lda, B, w2.ldb, w2.beta, C, w2.ldc, out_na,
+          "ragged noalloc")
+
+    # 3) the last-round split: 2944^3, 17 leftover tiles in 15 K chunks,
+    #    16,711,680 bytes of dense tile blocks.
+    w3 = wl.sweep(2944)
+    plan, (A, B, C), out_na, out_ref = _both(w3)
+    assert "last round split-K 15" in plan, plan
+    assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
+    check_sampled("f32", w3, A, B, C, out_na, nrows=16, seed=5,
+                  extra_rows=[2944 - 1 - 128 * i - 37 for i in range(8)])
+
+    # 4) a call that does not split uses no workspace at all.
+    w4 = wl.square(384, seeds=(8, 9, 10))
+    plan, (A, B, C), out_na, out_ref = _both(w4)
+    assert "workspace" not in plan, plan
+    assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
+    check("f32", w4.M, w4.N, w4.K, w4.alpha, A, w4.lda, B, w4.ldb, w4.beta, C, w4.ldc, out_na,
+          "384 noalloc")
+
+
+def test_noalloc_refuses_a_call_beyond_the_region_and_touches_nothing():
+    """3000 x 3000 x 30000 would split into 288,000,000 bytes of slabs: refused
+    with GEMM_ERR_SCRATCH_LIMIT before anything is enqueued, C unchanged."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    note("noalloc refusal 3000x3000x30000")
+    dev = torch.device("cuda:0")
+    # full-size buffers, so that even a launch could not reach past them
+    A = torch.zeros(3000 * 30000, device=dev)
+    B = torch.zeros(30000 * 3000, device=dev)
+    C = torch.full((3000 * 3000,), 7.0, device=dev)
+    rc = dg.gemm_f32_noalloc(3000, 3000, 30000, 1.0, A, 30000, B, 3000, 0.0, C, 3000,
+                             torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    assert rc == dg.GEMM_ERR_SCRATCH_LIMIT
+    assert bool((C == 7.0).all())
