@@ -19,7 +19,9 @@
 // landed (so its first fragments are read while the last MFMAs of kt run),
 // and every wave has read all of step kt's fragments, so step kt's slot is
 // refilled at once with step kt+STAGES.  A load thus has STAGES-1 steps of
-// compute to arrive, and two slots are enough to run the pipeline.
+// compute to arrive, and two slots are enough to run the pipeline.  On the
+// eight-wave large tile, half the waves issue all of a step's loads (see
+// kSplitLoaders).
 //
 // LDS layout (per slot, no padding, 16-byte chunks XOR-swizzled by row).
 // Each operand keeps its stored orientation (HRegion):
@@ -117,7 +119,7 @@ struct H16Tile {
   static_assert(STAGES >= 2, "the pipeline needs two or more slots");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(NWAVES * EP_BYTES <= LDS_BYTES, "epilogue staging fits in the pipeline LDS");
-  static_assert(3 * LOADS <= 63, "vmcnt range");
+  static_assert(6 * LOADS <= 63, "vmcnt range");
 };
 
 // Operand regions.  A slot holds an A region (BM indices m by BK k) and a B
@@ -193,9 +195,18 @@ struct HLayout {
 // taking this path.
 template <class T>
 struct DirectAddr {
-  uint32_t a[T::QA_W];
-  uint32_t b[T::QB_W];
+  uint32_t a[2 * T::QA_W];
+  uint32_t b[2 * T::QB_W];
 };
+// Eight-wave 16x16x32 tile: waves 4-7 issue every direct load of a step
+// (their own chunks and those of wave - 4) and waves 0-3 none.  A step's 64
+// loads take the texture unit longer than a wave's turn at the matrix pipe,
+// and a wave whose next load finds the unit's queue full cannot issue its
+// MFMAs either; with the loads on one wave per SIMD, the other wave of each
+// SIMD never waits at a load (measured: 4096^3 +2%, 8192^3 +2%, bit-identical
+// results).
+template <class T>
+constexpr bool kSplitLoaders = T::MF == 16 && T::NWAVES == 8;
 
 // Offset of the chunk at tile-relative (idx, kk).  Indices past the edge:
 // k-major rows are clamped to the last row (they only feed rows or columns of
@@ -234,17 +245,23 @@ __device__ __forceinline__ void direct_setup(const GemmParams &p, int m0, int n0
                                              DirectAddr<T> &d) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  constexpr int REP = kSplitLoaders<T> ? 2 : 1;
 #pragma unroll
-  for (int j = 0; j < T::QA_W; ++j) {
-    int idx, kk;
-    L::RA::chunk(wave * T::QA_W + j, lane, idx, kk);
-    d.a[j] = direct_offset<typename L::RA>(idx, kk, m0, p.M, p.lda);
-  }
+  for (int r = 0; r < REP; ++r) {
+    const int w = kSplitLoaders<T> ? (r == 0 ? wave - 4 : wave) : wave;
+    const int wc = w < 0 ? 0 : w;
 #pragma unroll
-  for (int j = 0; j < T::QB_W; ++j) {
-    int idx, kk;
-    L::RB::chunk(wave * T::QB_W + j, lane, idx, kk);
-    d.b[j] = direct_offset<typename L::RB>(idx, kk, n0, p.N, p.ldb);
+    for (int j = 0; j < T::QA_W; ++j) {
+      int idx, kk;
+      L::RA::chunk(wc * T::QA_W + j, lane, idx, kk);
+      d.a[r * T::QA_W + j] = direct_offset<typename L::RA>(idx, kk, m0, p.M, p.lda);
+    }
+#pragma unroll
+    for (int j = 0; j < T::QB_W; ++j) {
+      int idx, kk;
+      L::RB::chunk(wc * T::QB_W + j, lane, idx, kk);
+      d.b[r * T::QB_W + j] = direct_offset<typename L::RB>(idx, kk, n0, p.N, p.ldb);
+    }
   }
 }
 
@@ -254,12 +271,27 @@ __device__ __forceinline__ void direct_issue(const GemmParams &p, const DirectAd
   const int wave = wave_id();
   const BufRsrc ra = buffer_rsrc(tile_base<typename L::RA>(p.A, m0, k0, p.lda));
   const BufRsrc rb = buffer_rsrc(tile_base<typename L::RB>(p.B, n0, k0, p.ldb));
+  if constexpr (kSplitLoaders<T>) {
+    if (wave < 4) return;
 #pragma unroll
-  for (int j = 0; j < T::QA_W; ++j)
-    buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+    for (int r = 0; r < 2; ++r) {
+      const int w = r == 0 ? wave - 4 : wave;
 #pragma unroll
-  for (int j = 0; j < T::QB_W; ++j)
-    buffer_load16(d.b[j], rb, slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+      for (int j = 0; j < T::QA_W; ++j)
+        buffer_load16(d.a[r * T::QA_W + j], ra, slot_addr + (uint32_t)((w * T::QA_W + j) * 1024));
+#pragma unroll
+      for (int j = 0; j < T::QB_W; ++j)
+        buffer_load16(d.b[r * T::QB_W + j], rb,
+                      slot_addr + (uint32_t)(T::A_BYTES + (w * T::QB_W + j) * 1024));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::QA_W; ++j)
+      buffer_load16(d.a[j], ra, slot_addr + (uint32_t)((wave * T::QA_W + j) * 1024));
+#pragma unroll
+    for (int j = 0; j < T::QB_W; ++j)
+      buffer_load16(d.b[j], rb, slot_addr + (uint32_t)(T::A_BYTES + (wave * T::QB_W + j) * 1024));
+  }
 }
 
 // ---------------------------------------------------------------- register-staged loads
@@ -763,7 +795,8 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
     }
   }
   // Publish step 0; the loads of steps 1.. may stay in flight.
-  wait_direct<T::LOADS>(issued - 1);
+  constexpr int WL = kSplitLoaders<T> ? 2 * T::LOADS : T::LOADS;
+  wait_direct<WL>(issued - 1);
   lds_barrier();
 
   Frag<T> fr[2];
@@ -777,7 +810,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
       // Step kt+1 must have landed (steps issued after it may stay in
       // flight), and this wave's reads of step kt must be complete.  After
       // the last step nothing is in flight and this is a full wait.
-      wait_direct<T::LOADS>((issued - 1) - (kt + 1));
+      wait_direct<WL>((issued - 1) - (kt + 1));
       lds_barrier();
       // Every wave has read all of step kt: its slot takes step kt+STAGES.
       const int nx = kt + T::STAGES;
