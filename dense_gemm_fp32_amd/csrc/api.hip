@@ -337,8 +337,9 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
         char ws[48] = "";
         if (p.ws_bytes > 0) snprintf(ws, sizeof ws, " workspace %zu bytes", p.ws_bytes);
         snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s%s",
-                 p.name, p.vec_a > 1 ? "vec" : "scalar", p.vec_a, p.vec_b > 1 ? "vec" : "scalar",
-                 p.vec_b, p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split, ws,
+                 p.name, p.vec_a > 2 ? "vec" : (p.vec_a == 2 ? "pair" : "scalar"), p.vec_a,
+                 p.vec_b > 2 ? "vec" : (p.vec_b == 2 ? "pair" : "scalar"), p.vec_b,
+                 p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split, ws,
                  beta == 0.0f ? " beta0 (C not read)" : "");
         break;
       }

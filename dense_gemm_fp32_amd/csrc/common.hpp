@@ -41,6 +41,8 @@ struct GemmParams {
   int k_chunk;
   long long split_stride;  // elements between the slabs of consecutive splits
   // Bit 0: every row of A starts 16-byte aligned (vector loads); bit 1: of B.
+  // Bit 2: every row of A starts aligned to two elements (the register-staged
+  // path loads element pairs: 8 bytes of fp32, 4 of fp16); bit 3: of B.
   int vec_ab;
   // A launch may cover part of the tile order: tiles [tile_base, tile_base +
   // tile_count) of the grouped order (tile_count 0: all of them).  With
@@ -213,6 +215,22 @@ struct KSteps {
     return tail ? (kt == 0 ? nfull * bk : (kt - 1) * bk) : kt * bk;
   }
 };
+
+// Load width of an operand on the register-staged path, from GemmParams::vec_ab:
+// 2 = 16-byte vectors, 1 = element pairs, 0 = single elements.
+__device__ __forceinline__ int vec_width_a(int vec_ab) {
+  return (vec_ab & 1) ? 2 : ((vec_ab & 4) ? 1 : 0);
+}
+__device__ __forceinline__ int vec_width_b(int vec_ab) {
+  return (vec_ab & 2) ? 2 : ((vec_ab & 8) ? 1 : 0);
+}
+
+// vec_ab from the per-operand widths a plan chose (elements per access; the
+// full vector width `vec` means 16 bytes).
+inline int vec_bits(int vec_a, int vec_b, int vec) {
+  return (vec_a == vec ? 1 : 0) | (vec_b == vec ? 2 : 0) | (vec_a == 2 ? 4 : 0) |
+         (vec_b == 2 ? 8 : 0);
+}
 
 __device__ __forceinline__ KSteps make_steps(int K, int BK) {
   KSteps s;

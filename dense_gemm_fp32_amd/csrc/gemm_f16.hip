@@ -305,6 +305,20 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *src) {
   return v;
 }
 
+// Eight halves from a 4-byte aligned address as four 4-byte loads (rows whose
+// leading dimension is even but not a multiple of 8).
+__device__ __forceinline__ u32x4 load8_pairs(const uint16_t *src) {
+  const uint32_t *w = reinterpret_cast<const uint32_t *>(src);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// A whole in-range chunk at width w (2 = 16 bytes, 1 = pairs, 0 = elements).
+__device__ __forceinline__ u32x4 load8_width(const uint16_t *src, int w) {
+  if (w == 2) return load8<true>(src);
+  if (w == 1) return load8_pairs(src);
+  return load8<false>(src);
+}
+
 template <class Ok>
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t *src, Ok ok) {
   u32x4 v;
@@ -324,21 +338,22 @@ struct RegTile {
 };
 
 // One chunk of an operand (tile origin idx0, k0) through registers, with 0
-// for every element outside the matrix (index >= ext, k >= K).  `vec`: the
-// operand's rows start 16-byte aligned, so a whole chunk is one load.
+// for every element outside the matrix (index >= ext, k >= K).  `w`: the
+// operand's load width (its rows start 16-byte aligned: a whole chunk is one
+// load; 4-byte aligned: four; otherwise element by element).
 template <class R>
 __device__ __forceinline__ u32x4 staged_chunk(const void *X, int ld, int idx0, int ext, int k0,
-                                              int K, int idx, int kk, bool vec) {
+                                              int K, int idx, int kk, int w) {
   const int g = idx0 + idx, gk = k0 + kk;
   if constexpr (R::K_MAJOR) {
     const uint16_t *src = static_cast<const uint16_t *>(X) + (size_t)g * (size_t)ld + gk;
     const bool ok = g < ext;
-    if (ok && gk + 7 < K) return vec ? load8<true>(src) : load8<false>(src);
+    if (ok && gk + 7 < K) return load8_width(src, w);
     return load8_masked(src, [&](int e) { return ok && gk + e < K; });
   } else {
     const uint16_t *src = static_cast<const uint16_t *>(X) + (size_t)gk * (size_t)ld + g;
     const bool ok = gk < K;
-    if (ok && g + 7 < ext) return vec ? load8<true>(src) : load8<false>(src);
+    if (ok && g + 7 < ext) return load8_width(src, w);
     return load8_masked(src, [&](int e) { return ok && g + e < ext; });
   }
 }
@@ -346,8 +361,8 @@ __device__ __forceinline__ u32x4 staged_chunk(const void *X, int ld, int idx0, i
 // The chunks a direct load would fetch, through registers, with 0 for every
 // element outside the matrix (rows >= M, columns >= N, k >= K).
 template <class T, class L>
-__device__ __forceinline__ void reg_load(const GemmParams &p, int m0, int n0, int k0, bool va,
-                                         bool vb, RegTile<T> &t) {
+__device__ __forceinline__ void reg_load(const GemmParams &p, int m0, int n0, int k0, int va,
+                                         int vb, RegTile<T> &t) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
@@ -781,7 +796,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
   // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile<T> t;
-    reg_load<T, L>(p, m0, n0, ks.k0(0), true, true, t);
+    reg_load<T, L>(p, m0, n0, ks.k0(0), 2, 2, t);
     reg_store<T>(t, lds);
   } else {
     direct_issue<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
@@ -826,7 +841,7 @@ __device__ __forceinline__ void mainloop_direct(const GemmParams &p, int m0, int
 // edges of index-major operands).
 template <class T, class L>
 __device__ __forceinline__ void mainloop_staged(const GemmParams &p, int m0, int n0, char *lds,
-                                                int wm0, int wn0, bool va, bool vb,
+                                                int wm0, int wn0, int va, int vb,
                                                 typename T::Acc (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   FragAddr<T, L> fa;
@@ -869,8 +884,8 @@ __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
 
   const bool m_edge = m0 + T::BM > p.M;
   const bool n_edge = n0 + T::BN > p.N;
-  const bool va = (p.vec_ab & 1) != 0, vb = (p.vec_ab & 2) != 0;
-  const bool direct = va && vb && direct_ok<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
+  const int va = vec_width_a(p.vec_ab), vb = vec_width_b(p.vec_ab);
+  const bool direct = va == 2 && vb == 2 && direct_ok<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
                       direct_ok<typename L::RB, T::BK>(n_edge, p.N, p.ldb);
   if (direct) mainloop_direct<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
   else mainloop_staged<T, L>(p, m0, n0, lds, wm0, wn0, va, vb, acc);
@@ -911,11 +926,15 @@ static Plan make_plan(const Call &c, const char *name) {
   pl.threads = T::NT;
   const bool va = !c.force_scalar && vec_ok(c.A, c.lda, 8);
   const bool vb = !c.force_scalar && vec_ok(c.B, c.ldb, 8);
+  // element pairs (4 bytes) when a leading dimension is even but 16-byte
+  // loads are out
+  const bool pa = !va && !c.force_scalar && vec_ok(c.A, c.lda, 2);
+  const bool pb = !vb && !c.force_scalar && vec_ok(c.B, c.ldb, 2);
   // C: 4 adjacent elements per access (8 bytes of fp16 or 16 of fp32).
   const bool vc = !c.force_scalar && (c.ldc % 4) == 0 &&
                   aligned_to(c.C, (uintptr_t)(c.out32 ? 16 : 8));
-  pl.vec_a = va ? 8 : 1;
-  pl.vec_b = vb ? 8 : 1;
+  pl.vec_a = va ? 8 : (pa ? 2 : 1);
+  pl.vec_b = vb ? 8 : (pb ? 2 : 1);
   pl.vec_c = vc ? 4 : 1;
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
@@ -946,7 +965,7 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.splits = c.splits;
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
-  p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  p.vec_ab = vec_bits(pl.vec_a, pl.vec_b, 8);
   p.tile_base = 0;
   p.tile_count = 0;
   p.c_tiles = 0;

@@ -270,6 +270,22 @@ __device__ __forceinline__ f32x4 load4(const float *src) {
   return v;
 }
 
+// Four floats from an 8-byte aligned address as two 8-byte loads (rows whose
+// leading dimension is even but not a multiple of 4: the SGEMM summary's
+// memory-layout section ties 64-bit accesses to an even leading dimension).
+__device__ __forceinline__ f32x4 load4_pairs(const float *src) {
+  const f32x2 lo = *reinterpret_cast<const f32x2 *>(src);
+  const f32x2 hi = *reinterpret_cast<const f32x2 *>(src + 2);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// A whole in-range chunk at width w (2 = 16 bytes, 1 = pairs, 0 = elements).
+__device__ __forceinline__ f32x4 load4_width(const float *src, int w) {
+  if (w == 2) return load4<true>(src);
+  if (w == 1) return load4_pairs(src);
+  return load4<false>(src);
+}
+
 template <class T>
 struct RegTile32 {
   f32x4 a[T::QA_W];
@@ -277,23 +293,24 @@ struct RegTile32 {
 };
 
 // One chunk of an operand (tile origin idx0, k0) through registers, with 0
-// for every element outside the matrix (index >= ext, k >= K).  `vec`: the
-// operand's rows start 16-byte aligned, so a whole chunk is one load.
+// for every element outside the matrix (index >= ext, k >= K).  `w`: the
+// operand's load width (its rows start 16-byte aligned: a whole chunk is one
+// load; 8-byte aligned: two; otherwise element by element).
 template <class R>
 __device__ __forceinline__ f32x4 staged_chunk32(const void *X, int ld, int idx0, int ext, int k0,
-                                                int K, int idx, int kk, bool vec) {
+                                                int K, int idx, int kk, int w) {
   const int g = idx0 + idx, gk = k0 + kk;
   f32x4 v;
   if constexpr (R::K_MAJOR) {
     const float *src = static_cast<const float *>(X) + (size_t)g * (size_t)ld + gk;
     const bool ok = g < ext;
-    if (ok && gk + 3 < K) return vec ? load4<true>(src) : load4<false>(src);
+    if (ok && gk + 3 < K) return load4_width(src, w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (ok && gk + e < K) ? src[e] : 0.0f;
   } else {
     const float *src = static_cast<const float *>(X) + (size_t)gk * (size_t)ld + g;
     const bool ok = gk < K;
-    if (ok && g + 3 < ext) return vec ? load4<true>(src) : load4<false>(src);
+    if (ok && g + 3 < ext) return load4_width(src, w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (ok && g + e < ext) ? src[e] : 0.0f;
   }
@@ -303,8 +320,8 @@ __device__ __forceinline__ f32x4 staged_chunk32(const void *X, int ld, int idx0,
 // The chunks the direct loads would fetch, through registers, with 0 for every
 // element outside the matrix (rows >= M, columns >= N, k >= K).
 template <class T, class L>
-__device__ __forceinline__ void reg_load32(const GemmParams &p, int m0, int n0, int k0, bool va,
-                                           bool vb, RegTile32<T> &t) {
+__device__ __forceinline__ void reg_load32(const GemmParams &p, int m0, int n0, int k0, int va,
+                                           int vb, RegTile32<T> &t) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
 #pragma unroll
@@ -493,7 +510,7 @@ __device__ __forceinline__ void mainloop_direct32(const GemmParams &p, int m0, i
   // step), then direct loads of steps 1 .. STAGES-1.
   if (ks.tail) {
     RegTile32<T> t;
-    reg_load32<T, L>(p, m0, n0, ks.k0(0), true, true, t);
+    reg_load32<T, L>(p, m0, n0, ks.k0(0), 2, 2, t);
     reg_store32<T>(t, lds);
   } else {
     direct_issue32<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
@@ -595,7 +612,7 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
 
   if (ks.tail) {
     RegTile32<T> t;
-    reg_load32<T, L>(p, m0, n0, ks.k0(0), true, true, t);
+    reg_load32<T, L>(p, m0, n0, ks.k0(0), 2, 2, t);
     reg_store32<T>(t, lds);
   } else {
     direct_issue32<T, L>(p, da, m0, n0, ks.k0(0), lds_u32);
@@ -673,7 +690,7 @@ __device__ __forceinline__ void mainloop_spread32(const GemmParams &p, int m0, i
 
 template <class T, class L>
 __device__ __forceinline__ void mainloop_staged32(const GemmParams &p, int m0, int n0, char *lds,
-                                                  int wm0, int wn0, bool va, bool vb,
+                                                  int wm0, int wn0, int va, int vb,
                                                   f32x16 (&acc)[T::FM][T::FN]) {
   const KSteps ks = make_steps(p.K, T::BK);
   FragAddr32<T, L> fa;
@@ -788,8 +805,8 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 
   const bool m_edge = m0 + T::BM > p.M;
   const bool n_edge = n0 + T::BN > p.N;
-  const bool va = (p.vec_ab & 1) != 0, vb = (p.vec_ab & 2) != 0;
-  const bool direct = va && vb && direct_ok32<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
+  const int va = vec_width_a(p.vec_ab), vb = vec_width_b(p.vec_ab);
+  const bool direct = va == 2 && vb == 2 && direct_ok32<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
                       direct_ok32<typename L::RB, T::BK>(n_edge, p.N, p.ldb);
   if (direct) {
     if constexpr (T::SPREAD) mainloop_spread32<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
@@ -843,8 +860,10 @@ static Plan make_plan(const Call &c, const char *name) {
   const bool va = !c.force_scalar && vec_ok(c.A, c.lda, 4, 4);
   const bool vb = !c.force_scalar && vec_ok(c.B, c.ldb, 4, 4);
   const bool vc = !c.force_scalar && T::FN > 1 && vec_ok(c.C, c.ldc, T::FN, 4);
-  pl.vec_a = va ? 4 : 1;
-  pl.vec_b = vb ? 4 : 1;
+  // element pairs (8 bytes) when a leading dimension is even but 16-byte
+  // loads are out
+  pl.vec_a = va ? 4 : (!c.force_scalar && vec_ok(c.A, c.lda, 2, 4) ? 2 : 1);
+  pl.vec_b = vb ? 4 : (!c.force_scalar && vec_ok(c.B, c.ldb, 2, 4) ? 2 : 1);
   pl.vec_c = vc ? T::FN : 1;
   const long long tm = (c.M + T::BM - 1) / T::BM;
   const long long tn = (c.N + T::BN - 1) / T::BN;
@@ -875,7 +894,7 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.splits = c.splits;
   p.k_chunk = c.k_chunk;
   p.split_stride = c.split_stride;
-  p.vec_ab = (pl.vec_a > 1 ? 1 : 0) | (pl.vec_b > 1 ? 2 : 0);
+  p.vec_ab = vec_bits(pl.vec_a, pl.vec_b, 4);
   p.tile_base = c.tile_base;
   p.tile_count = c.tile_count;
   p.c_tiles = c.c_tiles ? 1 : 0;

@@ -122,11 +122,22 @@ def test_describe_picks_vector_or_scalar_loads():
     import dense_gemm_fp32_amd as dg
     rc, t = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
     assert rc == 0 and "A:vec4" in t and "B:vec4" in t and "C:vec" in t and "beta0" in t
-    # ragged, unaligned leading dimensions (K+13, N+5, N+3): element-wise everywhere
+    # ragged, unaligned leading dimensions (K+13, N+5, N+3): lda = 530 is even,
+    # so A takes element pairs (8 bytes of fp32, 4 of fp16; the SGEMM summary's
+    # layout section: 64-bit accesses need an even leading dimension); the odd
+    # ldb and ldc leave B and C element-wise
     rc, t = dg.gemm_describe("f32", 1000, 3000, 517, 1.5, FAKE, 530, FAKE, 3005, -0.75, FAKE, 3003)
-    assert rc == 0 and "A:scalar1" in t and "B:scalar1" in t and "C:scalar1" in t
+    assert rc == 0 and "A:pair2" in t and "B:scalar1" in t and "C:scalar1" in t
     rc, t = dg.gemm_describe("f16", 1000, 3000, 517, 1.5, FAKE, 530, FAKE, 3005, -0.75, FAKE, 3003)
-    assert rc == 0 and "A:scalar1" in t and "B:scalar1" in t and "C:scalar1" in t
+    assert rc == 0 and "A:pair2" in t and "B:scalar1" in t and "C:scalar1" in t
+    # odd lda, even ldb: the other way round; a base aligned to one element only
+    # keeps single elements even with an even leading dimension
+    rc, t = dg.gemm_describe("f16", 1000, 3000, 517, 1.5, FAKE, 531, FAKE, 3006, -0.75, FAKE, 3003)
+    assert "A:scalar1" in t and "B:pair2" in t
+    rc, t = dg.gemm_describe("f32", 1000, 3000, 517, 1.5, FAKE + 4, 530, FAKE, 3005, -0.75, FAKE, 3003)
+    assert "A:scalar1" in t
+    rc, t = dg.gemm_describe("f16", 1000, 3000, 517, 1.5, FAKE + 2, 530, FAKE, 3005, -0.75, FAKE, 3003)
+    assert "A:scalar1" in t
     rc, t = dg.gemm_describe("f16", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.5, FAKE, 4096)
     assert rc == 0 and "A:vec8" in t and "B:vec8" in t and "beta0" not in t
     # misaligned base pointer: scalar for that operand only
