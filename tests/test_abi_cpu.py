@@ -388,13 +388,13 @@ def test_tail_split_in_descriptions():
 
 
 def test_describe_reports_split_workspace():
-    """The workspace a split call takes, worked out by hand: 1792^3 splits the
-    128 x 128 tiles 5 ways into M x N fp32 slabs, 5 * 1792 * 1792 * 4 bytes;
+    """The workspace a split call takes, worked out by hand: 2304^3 splits the
+    128 x 128 tiles 3 ways into M x N fp32 slabs, 3 * 2304 * 2304 * 4 bytes;
     2944^3 (23 x 23 = 529 tiles of 128 x 128, 2 whole rounds of 256 and 17
     left over) splits the 17 leftover tiles 15 ways into dense tile blocks,
     15 * 17 * 128 * 128 * 4 bytes.  An unsplit call takes none."""
     import dense_gemm_fp32_amd as dg
-    cases = [(1792, "split-K 5", 64225280), (2944, "last round split-K 15", 16711680)]
+    cases = [(2304, "split-K 3", 63700992), (2944, "last round split-K 15", 16711680)]
     for n, split, nbytes in cases:
         rc, text = dg.gemm_describe("f32", n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
         assert rc == 0 and split in text and ("workspace %d bytes" % nbytes) in text, text

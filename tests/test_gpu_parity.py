@@ -73,9 +73,9 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n", [1792, 2944, 3584])
+@pytest.mark.parametrize("n", [2304, 2944, 3584])
 def test_f32_sweep_mid_sizes_sampled(n):
-    """Sweep sizes whose chosen plans split K: 1792^3 (every tile split),
+    """Sweep sizes whose chosen plans split K: 2304^3 (every tile split),
     2944^3 and 3584^3 (the last, partly filled round of tiles split), with
     beta = 1, on sampled rows that include one row of each of the last eight
     tile rows (where the split leftover tiles lie), the checksum and
@@ -1086,7 +1086,7 @@ def workspace_limit(nbytes):
         dg.gemm_set_workspace_limit(prev)
 
 
-@pytest.mark.parametrize("dtype,M,N,K", [("f32", 1792, 1792, 1792), ("f32", 2944, 2944, 2944),
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 2304, 2304, 2304), ("f32", 2944, 2944, 2944),
                                          ("f16", 512, 512, 8192), ("f16f32", 512, 512, 8192)])
 def test_workspace_refused_runs_unsplit(dtype, M, N, K):
     """With the workspace limit at 0 every split request fails: the call runs

@@ -36,11 +36,11 @@ def _both(w):
 
 
 def test_noalloc_matches_gemm_f32_on_calls_in_a_row():
-    # 1) 1792^3, beta = 1: K split 5 ways into M x N slabs, 64,225,280 bytes
+    # 1) 2304^3, beta = 1: K split 3 ways into M x N slabs, 63,700,992 bytes
     #    of the 64 MiB region.
-    w1 = wl.sweep(1792)
+    w1 = wl.sweep(2304)
     plan, (A, B, C), out_na, out_ref = _both(w1)
-    assert "split-K 5" in plan and "workspace 64225280 bytes" in plan, plan
+    assert "split-K 3" in plan and "workspace 63700992 bytes" in plan, plan
     assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
     check_sampled("f32", w1, A, B, C, out_na, nrows=16, seed=3)
 
