@@ -11,7 +11,10 @@ import os
 import torch  # noqa: F401  (loads torch's HIP runtime first, so libgemm.so binds to the same one)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgemm.so")
+# DENSE_GEMM_FP32_AMD_LIB selects another build of the same library (the
+# LDS-poison debug build of build.py); by default the release build next to
+# this file.
+LIB_PATH = os.environ.get("DENSE_GEMM_FP32_AMD_LIB") or os.path.join(HERE, "libgemm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgemm.so is not built (%s); run `python -m dense_gemm_fp32_amd.build`"

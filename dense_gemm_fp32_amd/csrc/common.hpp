@@ -194,6 +194,22 @@ __device__ __forceinline__ uint32_t lds_address(const char *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
+// Debug builds (DGEMM_LDS_POISON): fill a kernel's shared memory with
+// 0x7FC07FC0, a NaN both as one binary32 value and as two binary16 values,
+// before the kernel uses it, so that any read of LDS that the pipeline never
+// wrote (a wrong offset, swizzle or staging row) turns the result into NaN
+// and fails the parity tests.  Release builds compile this away.
+__device__ __forceinline__ void lds_poison(void *lds, int bytes) {
+#ifdef DGEMM_LDS_POISON
+  uint32_t *w = static_cast<uint32_t *>(lds);
+  for (int i = (int)threadIdx.x; i < bytes / 4; i += (int)blockDim.x) w[i] = 0x7FC07FC0u;
+  __syncthreads();
+#else
+  (void)lds;
+  (void)bytes;
+#endif
+}
+
 // Wave index as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));

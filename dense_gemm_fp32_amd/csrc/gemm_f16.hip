@@ -871,6 +871,7 @@ template <class T, bool TA, bool TB, bool VC, bool OUT32>
 __global__ __launch_bounds__(T::NT) void hgemm_mfma(GemmParams p) {
   typedef HLayout<T, TA, TB> L;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  lds_poison(lds, T::LDS_BYTES);
   int tm, tn, split;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
   select_split<uint16_t, float, TA, TB>(p, split);   // split-K passes always write fp32 slabs

@@ -785,6 +785,7 @@ template <class T, bool TA, bool TB, bool VC>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   typedef FLayout<T, TA, TB> L;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  lds_poison(lds, T::LDS_BYTES);
   int tm, tn, split, local;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m,
                 p.tile_count > 0 ? p.tile_count : p.tiles_m * p.tiles_n, p.tile_base, tm, tn, split,

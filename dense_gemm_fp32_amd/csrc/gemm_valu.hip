@@ -90,6 +90,8 @@ template <bool VEC_AB, bool VEC_C>
 __global__ __launch_bounds__(VT) __attribute__((amdgpu_waves_per_eu(4))) void sgemm_valu(GemmParams p) {
   __shared__ __attribute__((aligned(16))) float As[2][VBK * ROWA];
   __shared__ __attribute__((aligned(16))) float Bs[2][VBK * ROWB];
+  lds_poison(As, sizeof(As));
+  lds_poison(Bs, sizeof(Bs));
   int tm, tn, split;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn, split);
   const int m0 = tm * VBM, n0 = tn * VBN;

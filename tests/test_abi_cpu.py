@@ -202,6 +202,55 @@ def test_only_inline_asm_touches_m0():
             f.result()
 
 
+def test_library_override_loads_the_named_build(tmp_path):
+    """DENSE_GEMM_FP32_AMD_LIB makes the binding load that file (the
+    LDS-poison debug build runs the GPU suite this way) and only that file;
+    a path that does not exist fails loudly."""
+    import sys
+    from dense_gemm_fp32_amd.build import LIB
+    alt = tmp_path / "libgemm_copy.so"
+    alt.write_bytes(open(LIB, "rb").read())
+    code = ("import dense_gemm_fp32_amd as dg; dg.gemm_status_string(0); "
+            "m = open('/proc/self/maps').read(); "
+            "print(dg.LIB_PATH in m, %r in m)" % LIB)
+    env = dict(os.environ, DENSE_GEMM_FP32_AMD_LIB=str(alt))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split() == ["True", "False"], r.stdout
+    env["DENSE_GEMM_FP32_AMD_LIB"] = str(tmp_path / "missing.so")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0 and "ImportError" in r.stderr
+
+
+def test_spill_check_reads_kernel_descriptors():
+    """The build's spill check finds every kernel descriptor in gfx950
+    assembly and refuses a GEMM kernel with a scratch segment (a synthetic
+    descriptor as negative control; the real sources pass in
+    test_only_inline_asm_touches_m0, which runs the same check)."""
+    from dense_gemm_fp32_amd import build as b
+    text = "\n".join([
+        ".amdhsa_kernel _ZN5dgemm10hgemm_mfmaIXEEvNS_10GemmParamsE",
+        "  .amdhsa_private_segment_fixed_size 0",
+        ".end_amdhsa_kernel",
+        ".amdhsa_kernel _ZN5dgemm10sgemm_mfmaIXEEvNS_10GemmParamsE",
+        "  .amdhsa_private_segment_fixed_size 48",
+        ".end_amdhsa_kernel",
+        ".amdhsa_kernel _ZN5dgemm14scale_f32_kernelEv",
+        "  .amdhsa_private_segment_fixed_size 16",
+        ".end_amdhsa_kernel"])
+    sizes = b.scratch_sizes(text)
+    assert sizes == {"_ZN5dgemm10hgemm_mfmaIXEEvNS_10GemmParamsE": 0,
+                     "_ZN5dgemm10sgemm_mfmaIXEEvNS_10GemmParamsE": 48,
+                     "_ZN5dgemm14scale_f32_kernelEv": 16}
+    with pytest.raises(RuntimeError, match="sgemm_mfma"):
+        b.check_no_spills(text, "synthetic")
+    b.check_no_spills(text.replace("fixed_size 48", "fixed_size 0"), "synthetic")
+    with pytest.raises(RuntimeError, match="no kernel descriptors"):
+        b.check_no_spills("", "empty")
+
+
 def test_tile_table_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def name(dt, n):
