@@ -136,6 +136,69 @@ def smi_handle(torch, dev):
     return amdsmi, handles[0]
 
 
+def clock_sample(smi, h):
+    """Mean of the per-XCD graphics clocks in MHz from the SMU's metrics
+    table (refreshed every few milliseconds, so meaningful only after tens of
+    milliseconds of steady load); None without amdsmi."""
+    if h is None:
+        return None
+    try:
+        m = smi.amdsmi_get_gpu_metrics_info(h)
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int) and c < 0xFFFF]
+        return round(sum(clks) / len(clks), 1) if clks else None
+    except Exception:
+        return None
+
+
+def smu_snapshot(smi, h):
+    """The SMU's cumulative counters: energy (J) with its timestamp (s), and
+    the residency accumulators of package-power (PPT) and socket-thermal
+    throttling with their common denominator; None without amdsmi."""
+    if h is None:
+        return None
+    try:
+        e = smi.amdsmi_get_energy_count(h)
+        m = smi.amdsmi_get_gpu_metrics_info(h)
+        return {"j": e["energy_accumulator"] * e["counter_resolution"] * 1e-6,
+                "t": e["timestamp"] * 1e-9, "acc": m.get("accumulation_counter"),
+                "ppt": m.get("ppt_residency_acc"), "thm": m.get("socket_thm_residency_acc")}
+    except Exception:
+        return None
+
+
+def smu_between(a, b):
+    """Average socket power and throttle residencies between two snapshots
+    (the energy counter refreshes about once a second: short intervals read
+    as None)."""
+    out = {"avg_socket_power_w": None, "ppt_throttle_residency": None,
+           "thermal_throttle_residency": None}
+    if not a or not b:
+        return out
+    if b["t"] > a["t"] and b["j"] > a["j"]:
+        out["avg_socket_power_w"] = round((b["j"] - a["j"]) / (b["t"] - a["t"]), 1)
+    try:
+        dacc = b["acc"] - a["acc"]
+        if dacc > 0:
+            out["ppt_throttle_residency"] = round((b["ppt"] - a["ppt"]) / dacc, 4)
+            out["thermal_throttle_residency"] = round((b["thm"] - a["thm"]) / dacc, 4)
+    except Exception:
+        pass
+    return out
+
+
+def launch_stats(launch_ms, flops):
+    """How the per-launch times of a timed window move: first and last
+    launch, median, and the mean of the first and of the last quarter."""
+    n = len(launch_ms)
+    q = max(1, n // 4)
+    first_q = sum(launch_ms[:q]) / q
+    last_q = sum(launch_ms[-q:]) / q
+    return {"median_launch_ms": round(sorted(launch_ms)[n // 2], 5),
+            "first_launch_ms": round(launch_ms[0], 5), "last_launch_ms": round(launch_ms[-1], 5),
+            "first_quarter_tflops": round(flops / (first_q * 1e-3) / 1e12, 2),
+            "last_quarter_tflops": round(flops / (last_q * 1e-3) / 1e12, 2)}
+
+
 def power_window(torch, dev, call, flops, peak, seconds, warm=1.5):
     """Back-to-back calls for `warm` + `seconds` seconds.  Power is the SMU
     energy accumulator's increase over its own timestamps between two reads
@@ -170,9 +233,11 @@ def power_window(torch, dev, call, flops, peak, seconds, warm=1.5):
     try:
         run_for(warm)
         e0, ts0 = energy()
+        snap0 = smu_snapshot(smi, h)
         samples = []
         calls, wall = run_for(seconds, samples)
         e1, ts1 = energy()
+        snap1 = smu_snapshot(smi, h)
     except Exception:
         return None
     if ts1 <= ts0:
@@ -191,6 +256,9 @@ def power_window(torch, dev, call, flops, peak, seconds, warm=1.5):
            "clock_adjusted_peak": round(peak * clk / NOMINAL_SCLK_MHZ, 1) if clk else None}
     if clk:
         res["frac_of_clock_adjusted_peak"] = round(flops / per_call_s / 1e12 / res["clock_adjusted_peak"], 4)
+    thr = smu_between(snap0, snap1)
+    res["ppt_throttle_residency"] = thr["ppt_throttle_residency"]
+    res["thermal_throttle_residency"] = thr["thermal_throttle_residency"]
     return res
 
 
@@ -264,6 +332,14 @@ def parse_args():
                          "with cache flush; one JSON row per size")
     ap.add_argument("--sweep-sizes", default=None,
                     help="comma-separated sizes for --sweep (default 1024..12800 step 128)")
+    ap.add_argument("--sweep-clock-seconds", type=float, default=0.25,
+                    help="back-to-back load per sweep size before its clock is sampled")
+    ap.add_argument("--sweep-oracle", action="store_true",
+                    help="after --sweep, time the CPU oracle on the same sizes, ascending")
+    ap.add_argument("--sweep-oracle-cap", type=float, default=600.0,
+                    help="largest predicted oracle time of one sweep size, seconds")
+    ap.add_argument("--sweep-oracle-total", type=float, default=300.0,
+                    help="largest total time of the oracle sweep leg, seconds")
     ap.add_argument("--only", choices=["f32", "f16", "f16f32", "valu", "copy", "ragged_f32",
                                        "ragged_f16"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
@@ -354,6 +430,7 @@ def main():
                          "traffic": traffic,
                          "avg_launch_ms": round(avg_launch, 5),
                          "algorithmic_flops_per_launch": w.flops},
+            "timed_window": launch_stats(launch_ms, w.flops),
         }
         if p4:
             res["p4_protocol"] = p4_protocol(fn, w, dA, dB, dC)
@@ -391,6 +468,21 @@ def main():
                          args.steps, args.warmup, False)
         res["plan"] = dg.gemm_describe(w.dtype, w.M, w.N, w.K, w.alpha, 1 << 20, w.lda, 1 << 20,
                                        w.ldb, w.beta, 1 << 20, w.ldc)[1]
+        if args.only == "ragged_f16":
+            # 192 flop per compulsory byte against the machine's 314.6 for fp16:
+            # the floor is HBM (16.1 MB at 8 TB/s, 2.0 us)
+            nbytes = ragged_bytes(w)
+            avg_s = res["roofline"]["avg_launch_ms"] * 1e-3
+            res["roofline"] = {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1),
+                               "peak": PEAK_HBM, "unit": "GB/s",
+                               "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM, 4),
+                               "traffic": None, "avg_launch_ms": res["roofline"]["avg_launch_ms"],
+                               "algorithmic_bytes_per_launch": nbytes,
+                               "floor_us": round(nbytes / (PEAK_HBM * 1e9) * 1e6, 2)}
+        else:
+            # 96 flop per compulsory byte against 19.7 for fp32: the floor is
+            # the matrix cores (3.102e9 flop at 157.3 TFLOP/s, 19.7 us)
+            res["roofline"]["floor_us"] = round(w.flops / (PEAK_F32 * 1e12) * 1e6, 2)
         print(json.dumps({"only": args.only, **res}), flush=True)
         return
     w32 = wl.F32_4096
@@ -475,6 +567,14 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def ragged_bytes(w):
+    """Compulsory HBM bytes of a GEMM: A and B read once, C written (and read
+    first when beta != 0)."""
+    s_in = 4 if w.dtype == "f32" else 2
+    s_out = 2 if w.dtype == "f16" else 4
+    return s_in * (w.M * w.K + w.K * w.N) + s_out * w.M * w.N * (2 if w.beta != 0 else 1)
+
+
 def run_sweep(args, torch, dev, stream):
     """The square fp32 sweep of the SGEMM summary's benchmarking section:
     M = N = K = n, A, B, C ~ U[-1, 1], alpha = beta = 1, floor(1000 *
@@ -491,6 +591,7 @@ def run_sweep(args, torch, dev, stream):
            for seed in w.seeds]
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    smi, smi_h = smi_handle(torch, dev)
     for n in sizes:
         A, B, C = (x[:n, :n].contiguous() for x in big)
         reps = replay_count(n)
@@ -498,22 +599,74 @@ def run_sweep(args, torch, dev, stream):
         if rc != 0:
             raise RuntimeError("gemm_f32 returned %d" % rc)
         times = []
-        for _ in range(reps):
+        snap0 = smu_snapshot(smi, smi_h)
+        for r in range(reps):
             flush.zero_()
             s_ev.record(stream)
             dg.gemm_f32(n, n, n, 1.0, A, n, B, n, 1.0, C, n, stream)
             e_ev.record(stream)
             e_ev.synchronize()
             times.append(s_ev.elapsed_time(e_ev))
+        snap1 = smu_snapshot(smi, smi_h)
         last = times[len(times) - len(times) // 2:]
         mean = sum(last) / len(last)
         rc, plan = dg.gemm_describe("f32", n, n, n, 1.0, A, n, B, n, 1.0, C, n)
+        # the clock this size holds under steady load: back-to-back calls for
+        # a quarter of a second (no flushes), sampled at the end
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.sweep_clock_seconds:
+            for _ in range(4):
+                dg.gemm_f32(n, n, n, 1.0, A, n, B, n, 1.0, C, n, stream)
+            torch.cuda.synchronize(dev)
+        clk = clock_sample(smi, smi_h)
         print(json.dumps({"n": n, "replays": reps, "averaged": len(last),
                           "mean_ms": round(mean, 5), "min_ms": round(min(times), 5),
                           "tflops": round(2.0 * n ** 3 / (mean * 1e-3) / 1e12, 2),
                           "pct_of_peak": round(100 * 2.0 * n ** 3 / (mean * 1e-3) / 1e12 / PEAK_F32, 2),
+                          "replay_loop": smu_between(snap0, snap1),
+                          "steady_gfxclk_mhz": clk,
                           "plan": plan}), flush=True)
         del A, B, C
+    if args.sweep_oracle:
+        run_sweep_oracle(args, sizes)
+
+
+def run_sweep_oracle(args, sizes):
+    """The CPU oracle on the sweep's sizes, ascending, on the same leading
+    n x n blocks of the seeded 12800 x 12800 inputs, all host cores: a size
+    runs while its predicted time (the previous size's time x (n/n_prev)^3)
+    stays under --sweep-oracle-cap seconds and the leg's total under
+    --sweep-oracle-total seconds; the rows after that say why they did not
+    run."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    nmax = max(sizes)
+    w = wl.sweep(nmax)
+    big = [wl.draw(nmax, nmax, "uniform", seed, "f32") for seed in w.seeds]
+    threads = oracle.threads()
+    total, prev = 0.0, None
+    stop = None
+    for n in sorted(sizes):
+        if stop is None and prev is not None:
+            pred = prev[1] * (n / prev[0]) ** 3
+            if pred > args.sweep_oracle_cap:
+                stop = "oracle did not finish within cap (predicted %.0f s > %.0f s)" % (
+                    pred, args.sweep_oracle_cap)
+            elif total + pred > args.sweep_oracle_total:
+                stop = "not run: the leg's total budget of %.0f s" % args.sweep_oracle_total
+        if stop is not None:
+            print(json.dumps({"n": n, "oracle": stop}), flush=True)
+            continue
+        A, B, C = (np.ascontiguousarray(x[:n, :n]).reshape(-1) for x in big)
+        t0 = time.perf_counter()
+        oracle.gemm(n, n, n, 1.0, A, n, B, n, 1.0, C, n, "f32")
+        sec = time.perf_counter() - t0
+        total += sec
+        prev = (n, sec)
+        print(json.dumps({"n": n, "oracle_s": round(sec, 3),
+                          "oracle_gflops": round(2.0 * n ** 3 / sec / 1e9, 2),
+                          "oracle_threads": threads}), flush=True)
 
 
 def run_table(torch, dev, stream):
