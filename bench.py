@@ -345,6 +345,9 @@ def parse_args():
                     help="largest predicted oracle time of one sweep size, seconds")
     ap.add_argument("--sweep-oracle-total", type=float, default=300.0,
                     help="largest total time of the oracle sweep leg, seconds")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write profiles/hbm_traffic.json from the rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE runs under DIR (no GPU needed)")
     ap.add_argument("--only", choices=["f32", "f16", "f16f32", "valu", "copy", "ragged_f32",
                                        "ragged_f16"], default=None,
                     help="run only one kernel (profiling runs); 'copy' runs a plain "
@@ -354,6 +357,9 @@ def parse_args():
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -482,7 +488,7 @@ def main():
         if args.only == "ragged_f16":
             # 192 flop per compulsory byte against the machine's 314.6 for fp16:
             # the floor is HBM (16.1 MB at 8 TB/s, 2.0 us)
-            nbytes = ragged_bytes(w)
+            nbytes = compulsory_bytes(w)
             avg_s = res["roofline"]["avg_launch_ms"] * 1e-3
             res["roofline"] = {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1),
                                "peak": PEAK_HBM, "unit": "GB/s",
@@ -579,7 +585,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def ragged_bytes(w):
+def compulsory_bytes(w):
     """Compulsory HBM bytes of a GEMM: A and B read once, C written (and read
     first when beta != 0)."""
     s_in = 4 if w.dtype == "f32" else 2
@@ -748,6 +754,59 @@ def run_table(torch, dev, stream):
     print(json.dumps({"workload": "f32_256 oracle on one thread", "oracle_s": round(sec, 4),
                       "oracle_gflops": round(wl.F32_256.flops / sec / 1e9, 3),
                       "oracle_threads": nthr}), flush=True)
+
+
+TRAFFIC_KERNELS = {"f32": "sgemm_mfma", "f16": "hgemm_mfma", "copy": "copyBuffer"}
+
+
+def pmc_average(csv_path, kernel_substr, counter):
+    """Average per dispatch of `counter` over the dispatches of the kernel
+    whose name contains `kernel_substr`, from a rocprofv3 counter CSV;
+    returns (average, dispatches, full kernel name)."""
+    import csv
+    vals, name = {}, None
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+    if not vals:
+        raise ValueError("no %s samples of %s in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals.values()) / len(vals), len(vals), name
+
+
+def write_traffic(src_dir):
+    """profiles/hbm_traffic.json from the FETCH_SIZE and WRITE_SIZE runs in
+    src_dir (subdirectories pmc_<k>_<COUNTER>/p_counter_collection.csv for
+    k = f32, f16 and copy, one counter per run).  Both counters are scaled by
+    what they read for the plain 1 GiB copy (1 GiB read, 1 GiB written)."""
+    import glob
+
+    def avg(k, counter):
+        paths = glob.glob(os.path.join(src_dir, "pmc_%s_%s" % (k, counter), "*counter_collection.csv"))
+        if not paths:
+            raise FileNotFoundError("no %s run for %s under %s" % (counter, k, src_dir))
+        return pmc_average(paths[0], TRAFFIC_KERNELS[k], counter)
+
+    copy_bytes = 1 << 30
+    cf, _, cname = avg("copy", "FETCH_SIZE")
+    cw, _, _ = avg("copy", "WRITE_SIZE")
+    ff, wf = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    import workloads as wl
+    out = {"source_hash": kernel_source_hash(),
+           "copy_calibration": {"kernel": cname, "bytes": copy_bytes, "fetch_kib": round(cf, 2),
+                                "write_kib": round(cw, 2), "fetch_factor": round(ff, 4),
+                                "write_factor": round(wf, 4)},
+           "kernels": {}}
+    for k, w in (("f32", wl.F32_4096), ("f16", wl.F16_4096)):
+        fk, n, kname = avg(k, "FETCH_SIZE")
+        wk, _, _ = avg(k, "WRITE_SIZE")
+        out["kernels"][k] = {"kernel": kname, "fetch_kib": round(fk, 2), "write_kib": round(wk, 2),
+                             "hbm_bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf)),
+                             "algorithmic_bytes": compulsory_bytes(w), "dispatches": n}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def run_copy_calibration(torch, dev):
