@@ -49,6 +49,8 @@ _lib.gemm_set_split.argtypes = [_I]
 _lib.gemm_set_split.restype = _I
 _lib.gemm_set_tail_split.argtypes = [_I]
 _lib.gemm_set_tail_split.restype = _I
+_lib.gemm_set_pack.argtypes = [_I]
+_lib.gemm_set_pack.restype = _I
 _lib.gemm_set_workspace_limit.argtypes = [ctypes.c_longlong]
 _lib.gemm_set_workspace_limit.restype = ctypes.c_longlong
 _lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
@@ -58,7 +60,7 @@ _lib.gemm_probe_mfma.restype = _I
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_noalloc",
            "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string",
            "gemm_describe", "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split",
-           "gemm_set_tail_split", "gemm_set_workspace_limit", "gemm_probe_mfma") + LAYOUT_NAMES
+           "gemm_set_tail_split", "gemm_set_pack", "gemm_set_workspace_limit", "gemm_probe_mfma") + LAYOUT_NAMES
 GEMM_ERR_SCRATCH_LIMIT = -200
 
 
@@ -194,6 +196,14 @@ def gemm_set_tail_split(mode):
     """fp32: 0 = split the last partly filled round of tiles by size
     (default), 1 = never, 2..64 = force that many K chunks for it."""
     return _lib.gemm_set_tail_split(int(mode))
+
+
+def gemm_set_pack(mode):
+    """0 = copy operands whose rows do not allow 16-byte loads to 16-byte rows
+    when the call does at least 5e9 (fp32) / 1.5e10 (fp16) flops (default);
+    1 = never; 2 = whenever their rows do not allow 16-byte loads.  Returns
+    the previous mode, or -1."""
+    return _lib.gemm_set_pack(int(mode))
 
 
 def gemm_set_workspace_limit(nbytes):

@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 POISON_LIB = os.path.join(HERE, "libgemm_lds_poison.so")
 POISON_BUILD_DIR = os.path.join(HERE, "_build_lds_poison")
 SOURCES = ["api.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_valu.hip", "scale.hip", "splitk.hip",
-           "probe.hip"]
+           "pack.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

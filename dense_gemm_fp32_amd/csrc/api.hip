@@ -20,6 +20,7 @@ std::atomic<int> g_tile_config{0};
 std::atomic<int> g_split_mode{0};
 std::atomic<int> g_tail_mode{0};
 std::atomic<long long> g_ws_limit{-1};
+std::atomic<int> g_pack_mode{0};
 
 // Shared argument checks.  ta / tb: A is stored transposed (K x M, so its
 // rows hold M elements) / B is (N x K, rows of K); otherwise A is M x K and B
@@ -105,6 +106,7 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.ws_limit = g_ws_limit.load(std::memory_order_relaxed);
   c.ws_fixed = nullptr;
   c.ws_fixed_bytes = 0;
+  c.pack_mode = g_pack_mode.load(std::memory_order_relaxed);
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -202,8 +204,8 @@ int gemm_f16f32_tt(int M, int N, int K, float alpha, const gemm_half_t *A, int l
 }
 
 // gemm_f32 for callers that cannot allocate: the same checks, plan and
-// kernels, with the split-K workspace taken from the library's fixed scratch
-// region instead of its memory pool.  A call whose plan needs more workspace
+// kernels, with the workspace (operand copies, split K) taken from the
+// library's fixed scratch region instead of its memory pool.  A call whose plan needs more workspace
 // than the region holds is refused before anything is enqueued.
 int gemm_f32_noalloc(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                      int ldb, float beta, float *C, int ldc, void *stream) {
@@ -219,14 +221,14 @@ int gemm_f32_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
       break;
     case Route::kGemm: {
       dgemm::Call c = make_call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+      // The plan sees the region's size (copies of unaligned operands are
+      // made only where they fit in it beside the split-K workspace); the
+      // refusal comes before any HIP call.
+      c.ws_fixed_bytes = dgemm::kScratchBytes;
       const dgemm::Plan p = dgemm::plan_f32(c);
       if (p.ws_bytes > dgemm::kScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
-      if (p.ws_bytes > 0) {
-        const int dev = dgemm::stream_device(s);
-        e = dgemm::scratch_region(dev, &c.ws_fixed);
-        if (e != hipSuccess) return (int)e;
-        c.ws_fixed_bytes = dgemm::kScratchBytes;
-      }
+      e = dgemm::scratch_region(dgemm::stream_device(s), &c.ws_fixed);
+      if (e != hipSuccess) return (int)e;
       e = dgemm::launch_f32(c);
       break;
     }
@@ -294,7 +296,7 @@ const char *gemm_status_string(int status) {
     case -8: return "invalid argument 8: ldb < max(1, row length of B as stored: N, or K when B is stored transposed or column-major)";
     case -10: return "invalid argument 10: C is NULL";
     case -11: return "invalid argument 11: ldc < max(1, N) (row-major) or max(1, M) (column-major)";
-    case GEMM_ERR_SCRATCH_LIMIT: return "gemm_f32_noalloc: the call's split-K workspace would exceed the library's fixed scratch region (64 MiB); nothing was enqueued";
+    case GEMM_ERR_SCRATCH_LIMIT: return "gemm_f32_noalloc: the call's workspace (split K) would exceed the library's fixed scratch region (64 MiB); nothing was enqueued";
     case -101: return "invalid probe argument 1: dtype is not 0 (fp32) or 1 (fp16)";
     case -102: return "invalid probe argument 2: iters < 1";
     case -103: return "invalid probe argument 3: operands is NULL";
@@ -336,10 +338,12 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
         else if (p.tail > 1) snprintf(split, sizeof split, " last round split-K %d", p.tail);
         char ws[48] = "";
         if (p.ws_bytes > 0) snprintf(ws, sizeof ws, " workspace %zu bytes", p.ws_bytes);
-        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d blocks %lld threads %d%s%s%s",
+        const char *packed = p.packed_a ? (p.packed_b ? " copies A B" : " copies A")
+                                        : (p.packed_b ? " copies B" : "");
+        snprintf(text, sizeof text, "%s loads A:%s%d B:%s%d C:%s%d%s blocks %lld threads %d%s%s%s",
                  p.name, p.vec_a > 2 ? "vec" : (p.vec_a == 2 ? "pair" : "scalar"), p.vec_a,
                  p.vec_b > 2 ? "vec" : (p.vec_b == 2 ? "pair" : "scalar"), p.vec_b,
-                 p.vec_c > 1 ? "vec" : "scalar", p.vec_c, p.blocks, p.threads, split, ws,
+                 p.vec_c > 1 ? "vec" : "scalar", p.vec_c, packed, p.blocks, p.threads, split, ws,
                  beta == 0.0f ? " beta0 (C not read)" : "");
         break;
       }
@@ -384,6 +388,11 @@ int gemm_set_tail_split(int mode) {
 int gemm_set_tile_config(int config) {
   if (config < 0 || config > 6) return -1;
   return g_tile_config.exchange(config);
+}
+
+int gemm_set_pack(int mode) {
+  if (mode < 0 || mode > 2) return -1;
+  return g_pack_mode.exchange(mode);
 }
 
 long long gemm_set_workspace_limit(long long bytes) {

@@ -562,23 +562,41 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
   const int cl = 4 * (lane % LPR);
   const int col = c0 + cl;
   const bool cols_ok = !CHECK || col + 3 < p.N;
-  // Every C value this lane combines (vector path, beta != 0) is loaded
-  // before the first is used, so the latencies of the loads overlap instead
-  // of adding up block row by block row.
-  u32x2 cpre[T::NG][PASSES];
+  // C values are loaded ahead of their use, so the latencies of the loads
+  // overlap instead of adding up pass by pass (a store to C keeps a later
+  // load of C from moving above it).  Vector C: every value this lane
+  // combines, before the first block row is staged (8-byte loads; the lanes
+  // past an edge tile's last full group of 4 columns load theirs when they
+  // store).  Element-wise C: one block row at a time, masked at the matrix
+  // edge, which is what the registers of the largest tile allow; values are
+  // packed two halves per word.
+  u32x2 cpre[VEC_C ? T::NG : 1][PASSES];
   if (VEC_C && beta != 0.0f) {
 #pragma unroll
     for (int bi = 0; bi < T::NG; ++bi)
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
-        cpre[bi][pass] = u32x2{0u, 0u};
+        cpre[VEC_C ? bi : 0][pass] = u32x2{0u, 0u};
         if (!CHECK || (row < p.M && cols_ok))
-          cpre[bi][pass] = *reinterpret_cast<const u32x2 *>(C + (size_t)row * (size_t)p.ldc + col);
+          cpre[VEC_C ? bi : 0][pass] =
+              *reinterpret_cast<const u32x2 *>(C + (size_t)row * (size_t)p.ldc + col);
       }
   }
 #pragma unroll
   for (int bi = 0; bi < T::NG; ++bi) {
+    if (!VEC_C && beta != 0.0f) {
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
+        const uint16_t *src = C + (size_t)row * (size_t)p.ldc + col;
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = (!CHECK || (row < p.M && col + e < p.N)) ? (uint32_t)src[e] : 0u;
+        cpre[0][pass] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      }
+    }
     stage_rows<T>(stage, acc, bi, lane);
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -590,7 +608,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
       if (VEC_C && cols_ok) {
         float o[4];
         if (beta != 0.0f) {
-          const u32x2 w = cpre[bi][pass];
+          const u32x2 w = cpre[VEC_C ? bi : 0][pass];
           o[0] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] & 0xffff)), alpha * v[0]);
           o[1] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[0] >> 16)), alpha * v[1]);
           o[2] = __builtin_fmaf(beta, f16_bits_to_f32((uint16_t)(w[1] & 0xffff)), alpha * v[2]);
@@ -599,16 +617,21 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
         }
-        u32x2 w;
-        w[0] = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
-        w[1] = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
-        *reinterpret_cast<u32x2 *>(dst) = w;
+        u32x2 ow;
+        ow[0] = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
+        ow[1] = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
+        *reinterpret_cast<u32x2 *>(dst) = ow;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (CHECK && col + e >= p.N) continue;
           float o = alpha * v[e];
-          if (beta != 0.0f) o = __builtin_fmaf(beta, f16_bits_to_f32(dst[e]), o);
+          if (beta != 0.0f) {
+            const u32x2 w = cpre[0][pass];
+            const uint16_t ce =
+                VEC_C ? dst[e] : (uint16_t)((e < 2 ? w[0] : w[1]) >> (16 * (e & 1)));
+            o = __builtin_fmaf(beta, f16_bits_to_f32(ce), o);
+          }
           dst[e] = f32_to_f16_bits(o);
         }
       }
@@ -618,7 +641,8 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int r0, int c0, ch
 
 // The same epilogue for an fp32 C and result: alpha*acc + beta*C in fp32,
 // written as 16-byte stores (4 adjacent floats per lane, 512 contiguous
-// bytes per 32 lanes).  C is loaded one block row at a time, before that
+// bytes per 32 lanes).  C is loaded one block row at a time (16-byte loads,
+// or element by element, masked, where C does not allow them), before that
 // row's accumulators are staged, so the load latency overlaps the staging
 // without holding every row's C in registers at once.
 template <class T, bool VEC_C, bool CHECK>
@@ -638,13 +662,19 @@ __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int 
 #pragma unroll
   for (int bi = 0; bi < T::NG; ++bi) {
     f32x4 cpre[PASSES];
-    if (VEC_C && beta != 0.0f) {
+    if (beta != 0.0f) {
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int row = r0 + 32 * bi + pass * ROWS_PER_PASS + lane / LPR;
+        const float *src = C + (size_t)row * (size_t)p.ldc + col;
         cpre[pass] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (!CHECK || (row < p.M && cols_ok))
-          cpre[pass] = *reinterpret_cast<const f32x4 *>(C + (size_t)row * (size_t)p.ldc + col);
+        if (VEC_C) {
+          if (!CHECK || (row < p.M && cols_ok)) cpre[pass] = *reinterpret_cast<const f32x4 *>(src);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!CHECK || (row < p.M && col + e < p.N)) cpre[pass][e] = src[e];
+        }
       }
     }
     stage_rows<T>(stage, acc, bi, lane);
@@ -670,7 +700,7 @@ __device__ __forceinline__ void epilogue_out32(const GemmParams &p, int r0, int 
         for (int e = 0; e < 4; ++e) {
           if (CHECK && col + e >= p.N) continue;
           float o = alpha * v[e];
-          if (beta != 0.0f) o = __builtin_fmaf(beta, dst[e], o);
+          if (beta != 0.0f) o = __builtin_fmaf(beta, VEC_C ? dst[e] : cpre[pass][e], o);
           dst[e] = o;
         }
       }
@@ -1172,7 +1202,7 @@ static Plan plan_cfg(const Call &c, const char *name, int want) {
   return pl;
 }
 
-Plan plan_f16(const Call &c) {
+static Plan plan_f16_as_is(const Call &c) {
   const F16Choice ch = choose_f16(c);
   switch (ch.cfg) {
     case F16Cfg::kBig:
@@ -1195,7 +1225,7 @@ Plan plan_f16(const Call &c) {
   }
 }
 
-hipError_t launch_f16(const Call &c) {
+static hipError_t launch_f16_as_is(const Call &c) {
   const F16Choice ch = choose_f16(c);
   switch (ch.cfg) {
     case F16Cfg::kBig: return launch_cfg<F16Big>(c, ch.splits);
@@ -1204,5 +1234,11 @@ hipError_t launch_f16(const Call &c) {
     default: return launch_cfg<F16Small>(c, ch.splits);
   }
 }
+
+// Operands whose rows do not allow 16-byte loads may first be copied to ones
+// that do (pack.hip); the tile and split are then chosen for the copies.
+Plan plan_f16(const Call &c) { return plan_packed(c, 2, plan_f16_as_is); }
+
+hipError_t launch_f16(const Call &c) { return run_packed(c, 2, plan_f16_as_is, launch_f16_as_is); }
 
 }  // namespace dgemm

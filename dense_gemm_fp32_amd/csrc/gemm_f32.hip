@@ -730,9 +730,46 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
   const bool cols_ok = !CHECK || col + T::FN - 1 < p.N;
 #pragma unroll
   for (int bi = 0; bi < T::FM; ++bi) {
+    if constexpr (!VEC_C) {
+      // Element-wise C (unaligned ldc or base): the C values of G rows are
+      // loaded, masked, before the first of them is stored, so the rows wait
+      // out one memory latency per group instead of one per row (a store to
+      // C keeps a later load of C from moving above it).  G = 16 (the whole
+      // block) where the tile's registers allow it, else 4.
+      constexpr int G = T::C_BATCH ? 16 : 4;
+#pragma unroll
+      for (int g0 = 0; g0 < 16; g0 += G) {
+        float cs[G][T::FN];
+        if (beta != 0.0f) {
+#pragma unroll
+          for (int r = 0; r < G; ++r) {
+            const int row = r0 + 32 * bi + 8 * ((g0 + r) / 4) + 4 * lh + ((g0 + r) % 4);
+            const float *src = C + (size_t)row * (size_t)p.ldc + col;
+#pragma unroll
+            for (int bj = 0; bj < T::FN; ++bj)
+              cs[r][bj] = (!CHECK || (row < p.M && col + bj < p.N)) ? src[bj] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+          const int row = r0 + 32 * bi + 8 * ((g0 + r) / 4) + 4 * lh + ((g0 + r) % 4);
+          if (CHECK && row >= p.M) continue;
+          float *dst = C + (size_t)row * (size_t)p.ldc + col;
+#pragma unroll
+          for (int bj = 0; bj < T::FN; ++bj) {
+            if (CHECK && col + bj >= p.N) continue;
+            const float v = alpha * acc[bi][bj][g0 + r];
+            dst[bj] = beta != 0.0f ? __builtin_fmaf(beta, cs[r][bj], v) : v;
+          }
+        }
+      }
+      continue;
+    }
     // With C_BATCH the block's 16 rows of C are all loaded before the first
     // store: a load placed after a store to the same array cannot be moved
     // above it, so interleaved they wait out one memory latency per row.
+    // (The lanes past an edge tile's last full column group load theirs
+    // element by element as they store.)
     CVec cin[16];
     if (T::C_BATCH && VEC_C && cols_ok && beta != 0.0f) {
 #pragma unroll
@@ -1307,7 +1344,7 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
   return pl;
 }
 
-Plan plan_f32(const Call &c) {
+static Plan plan_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
     case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots spread loads", ch.splits, ch.tail);
@@ -1319,7 +1356,7 @@ Plan plan_f32(const Call &c) {
   }
 }
 
-hipError_t launch_f32(const Call &c) {
+static hipError_t launch_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
   switch (ch.cfg) {
     case F32Cfg::kHuge: return launch_cfg<F32Huge>(c, ch.splits, ch.tail);
@@ -1330,5 +1367,11 @@ hipError_t launch_f32(const Call &c) {
     default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }
+
+// Operands whose rows do not allow 16-byte loads may first be copied to ones
+// that do (pack.hip); the tile and split are then chosen for the copies.
+Plan plan_f32(const Call &c) { return plan_packed(c, 4, plan_f32_as_is); }
+
+hipError_t launch_f32(const Call &c) { return run_packed(c, 4, plan_f32_as_is, launch_f32_as_is); }
 
 }  // namespace dgemm

@@ -42,6 +42,10 @@ struct Call {
   long long ws_limit;
   void *ws_fixed;
   size_t ws_fixed_bytes;
+  // Copies of A and B with 16-byte rows (pack.hip): 0 = when an operand's rows
+  // do not allow 16-byte loads and the call is large enough, 1 = never,
+  // 2 = whenever an operand's rows do not allow them (diagnostic).
+  int pack_mode;
   hipStream_t stream;
 };
 
@@ -54,7 +58,9 @@ struct Plan {
   long long blocks;          // tiles
   int splits;                // K chunks (1 = no split)
   int tail;                  // K chunks of the last round's tiles (1 = none)
-  size_t ws_bytes;           // split-K workspace the call takes (0 = none)
+  size_t ws_bytes;           // workspace the call takes: copies of A and B, split K (0 = none)
+  bool packed_a = false;     // the GEMM runs on a 16-byte-row copy of A ...
+  bool packed_b = false;     // ... of B
 };
 
 // The reduction pass of a split-K run of tiles: for each of `tiles` tiles
@@ -120,6 +126,27 @@ hipError_t launch_splitk_reduce(const SplitReduce &r, hipStream_t s);
 // slab).  Also returns the chunk length.
 int clamp_splits(const Call &c, int want, int bk, long long tiles, int *k_chunk,
                  long long ws_elems_per_split = 0);
+
+// Copies of A and B whose rows allow 16-byte loads (pack.hip).  pack_choice:
+// which operands of call c (elements of eb bytes: 4 or 2) are copied and the
+// workspace that takes, including the split-K workspace of the GEMM on the
+// copies (planned by `plan`); nothing is copied when both operands already
+// allow 16-byte loads, under the test switches, for small calls, or when the
+// total exceeds the workspace the call may take.  plan_packed / run_packed:
+// the plan and the launch of call c with those copies (the copy kernel, then
+// `launch` on the copies, on c's stream, from one workspace allocation; the
+// call runs on the original operands when that allocation fails).
+struct PackChoice {
+  bool a = false, b = false;
+  int lda = 0, ldb = 0;            // leading dimensions of the copies
+  size_t a_bytes = 0, b_bytes = 0;
+  size_t inner_ws = 0;             // split-K workspace of the GEMM on the copies
+  size_t bytes = 0;                // the whole workspace
+};
+PackChoice pack_choice(const Call &c, int eb, Plan (*plan)(const Call &));
+Plan plan_packed(const Call &c, int eb, Plan (*plan)(const Call &));
+hipError_t run_packed(const Call &c, int eb, Plan (*plan)(const Call &),
+                      hipError_t (*launch)(const Call &));
 
 Plan plan_f32(const Call &c);
 Plan plan_f16(const Call &c);

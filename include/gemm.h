@@ -37,6 +37,15 @@
  *     small remainder may do this for the remainder's tiles only (dense
  *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
  *     the whole rounds.
+ *   - Operand copies: when the rows of A or B do not allow 16-byte loads (ld
+ *     not a multiple of 4 floats / 8 halves, or a base not 16-byte aligned)
+ *     and the call does at least 5e9 flops (fp32) or 1.5e10 (fp16 inputs),
+ *     that operand is first copied, bit for bit, into workspace rows padded
+ *     to 16 bytes, and the GEMM runs on the copy (the SGEMM summary's
+ *     memory-layout section: its 128-bit loads need ld % 4 == 0).  Same products, same bound; the tile and
+ *     split are chosen for the copy.  Smaller calls, and calls whose
+ *     workspace cannot be had, load such operands in pairs or element by
+ *     element instead.
  *   - Accuracy: |C_gpu - C_exact| <= 4*K*u*(|alpha|*(|A||B|)_ij + |beta|*|C_ij|)
  *     plus one rounding to the output type, u = 2^-24 (fp32 accumulation).
  *
@@ -52,10 +61,12 @@
  *     the largest size used so far on the device (2 MiB steps) so that freed
  *     blocks are reused; the pool keeps up to 256 MiB of freed blocks and
  *     hands the rest back to the runtime at the next synchronisation.
- *     gemm_set_workspace_limit caps the workspace of a call.  If the workspace
- *     cannot be had the call runs without splitting (same bound; the
- *     summation order is then that of an unsplit call).  gemm_describe
- *     reports the workspace a call would take.
+ *     Operand copies (above) take rows*ceil(cols/v)*16 bytes each (v = 4
+ *     floats or 8 halves per 16 bytes) from the same allocation as the
+ *     split.  gemm_set_workspace_limit caps the workspace of a call.  If the
+ *     workspace cannot be had the call runs without copies or splitting (same
+ *     bound; the summation order is then that of an unsplit call).
+ *     gemm_describe reports the workspace a call would take.
  *   - gemm_f32_noalloc is gemm_f32 without any allocation: its workspace is a
  *     fixed 64 MiB region of device memory owned by the library (one per
  *     device, held until the process ends).
@@ -91,7 +102,8 @@
  *                     a GPU.
  *   > 0               a hipError_t from the kernel launch.
  *   GEMM_ERR_SCRATCH_LIMIT (gemm_f32_noalloc only) the call would need more
- *                     split-K workspace than the fixed scratch region holds;
+ *                     split-K workspace than the fixed scratch region holds
+ *                     (operand copies are made only where they fit);
  *                     nothing was enqueued.
  */
 #ifndef DENSE_GEMM_GEMM_H
@@ -326,9 +338,22 @@ int gemm_set_split(int mode);
 int gemm_set_tail_split(int mode);
 
 /*
- * Cap on the split-K workspace one call may take from the library's pool, in
- * bytes: -1 = no cap (the default), 0 = never use workspace (every call runs
- * unsplit), n > 0 = calls whose split needs more than n bytes run unsplit.
+ * Diagnostic switch for tests: 0 = copy A or B to 16-byte rows when their
+ * rows do not allow 16-byte loads and the call is large enough (the default;
+ * see "Operand copies" above); 1 = never copy; 2 = copy whenever
+ * their rows do not allow 16-byte loads, whatever the size.  Copies are made
+ * only where the workspace fits (gemm_set_workspace_limit) and never under
+ * gemm_set_load_mode(1).  Process-wide, like gemm_set_load_mode.  Returns the
+ * previous setting, or -1 for an unknown value.
+ */
+int gemm_set_pack(int mode);
+
+/*
+ * Cap on the workspace one call may take from the library's pool (operand
+ * copies and split K), in bytes: -1 = no cap (the default), 0 = never use
+ * workspace (every call runs unsplit, without copies), n > 0 = calls whose
+ * copies and split need more than n bytes run without them (copies are
+ * dropped first, then the split).
  * Process-wide, like gemm_set_load_mode; gemm_f32_noalloc ignores it.
  * Returns the previous setting, or -2 for a value below -1.
  */

@@ -289,11 +289,20 @@ def test_tile_table_choice_and_override():
 
 
 def test_staged_calls_split_the_medium_tile():
-    """Unaligned operands (element-wise loads): fp32 grids under three
-    128x128 tiles per CU take that tile with the K split of least estimated
-    time, fp16 grids under 1.5 take it with the smallest split reaching 1.5
-    workgroups per CU; larger grids keep the direct-path choice."""
+    """Unaligned operands (element-wise loads, operand copies switched off):
+    fp32 grids under three 128x128 tiles per CU take that tile with the K
+    split of least estimated time, fp16 grids under 1.5 take it with the
+    smallest split reaching 1.5 workgroups per CU; larger grids keep the
+    direct-path choice."""
     import dense_gemm_fp32_amd as dg
+    prev_pack = dg.gemm_set_pack(1)
+    try:
+        _staged_choices(dg)
+    finally:
+        dg.gemm_set_pack(prev_pack)
+
+
+def _staged_choices(dg):
     def d(M, N, K):
         return dg.gemm_describe("f32", M, N, K, 1.5, FAKE, K + 13, FAKE, N + 5, -0.75, FAKE, N + 3)[1]
     for (M, N, K), S in [((1000, 3000, 517), 4), ((2000, 2000, 1000), 3), ((3000, 3000, 3000), 4),
@@ -474,3 +483,70 @@ def test_workspace_limit_switch():
     assert dg.gemm_set_workspace_limit(1 << 20) == 0
     assert dg.gemm_set_workspace_limit(-5) == -2
     assert dg.gemm_set_workspace_limit(-1) == 1 << 20
+
+
+def test_operand_copies_by_size_and_switches():
+    """Operands whose rows do not allow 16-byte loads are copied to 16-byte
+    rows above the size rule (5e9 flops fp32, 1.5e10 fp16), never under
+    gemm_set_pack(1) or the element-wise load switch, always under
+    gemm_set_pack(2); the copies' bytes are part of the reported workspace
+    and a workspace limit below them drops the copies."""
+    import dense_gemm_fp32_amd as dg
+
+    def d(dtype, M, N, K, lda, ldb, ldc, a=FAKE, b=FAKE):
+        rc, t = dg.gemm_describe(dtype, M, N, K, 1.0, a, lda, b, ldb, 0.5, FAKE, ldc)
+        assert rc == 0
+        return t
+
+    def ws(t):
+        return int(t.split("workspace ")[1].split()[0]) if "workspace" in t else 0
+
+    # fp32 2048^3, every ld 2049: two copies of 2048 x 2048 floats (rows of
+    # 2048 already fill whole 16-byte chunks), and the GEMM on them is unsplit
+    t = d("f32", 2048, 2048, 2048, 2049, 2049, 2049)
+    assert "copies A B" in t and "A:vec4 B:vec4" in t and ws(t) == 2 * 2048 * 2048 * 4, t
+    # one unaligned operand: only it is copied; 1001 columns pad to 1004
+    t = d("f32", 2000, 2000, 1001, 1001, 2000, 2000)
+    assert "copies A" in t and "copies A B" not in t and ws(t) >= 2000 * 1004 * 4, t
+    t = d("f32", 2000, 2000, 1000, 1000, 2001, 2000)
+    assert "copies B" in t, t
+    # a base off a 16-byte boundary alone is enough
+    assert "copies A" in d("f32", 2048, 2048, 2048, 2048, 2048, 2048, a=FAKE + 4)
+    # below the rule: the ragged workload (3.1e9 flops) and fp16 1536^3 are not copied
+    assert "copies" not in d("f32", 1000, 3000, 517, 530, 3005, 3003)
+    assert "copies" not in d("f16", 1536, 1536, 1536, 1537, 1537, 1537)
+    assert "copies A B" in d("f16", 2048, 2048, 2048, 2049, 2049, 2049)
+    # aligned operands are never copied
+    assert "copies" not in d("f32", 4096, 4096, 4096, 4096, 4096, 4097)
+    # the switches
+    prev = dg.gemm_set_pack(1)
+    try:
+        assert prev == 0
+        assert "copies" not in d("f32", 2048, 2048, 2048, 2049, 2049, 2049)
+        assert dg.gemm_set_pack(2) == 1
+        t = d("f32", 300, 200, 100, 101, 201, 200)
+        # A: 300 rows of K = 100 floats, B: 100 rows of N = 200 (both already
+        # whole 16-byte chunks), each copy rounded up to 256 bytes
+        assert "copies A B" in t and ws(t) == (300 * 100 * 4 + 255) // 256 * 256 + \
+            (100 * 200 * 4 + 255) // 256 * 256, t
+        t = d("f16", 300, 200, 100, 101, 201, 200)
+        # fp16: 100 halves pad to 104, 200 to 200
+        assert "copies A B" in t and ws(t) == (300 * 104 * 2 + 255) // 256 * 256 + \
+            (100 * 200 * 2 + 255) // 256 * 256, t
+        load = dg.gemm_set_load_mode(1)
+        try:
+            assert "copies" not in d("f32", 300, 200, 100, 101, 201, 200)
+        finally:
+            dg.gemm_set_load_mode(load)
+    finally:
+        dg.gemm_set_pack(prev)
+    assert dg.gemm_set_pack(3) == -1 and dg.gemm_set_pack(-1) == -1
+    # a workspace limit below the copies drops them (and the split, if any)
+    need = ws(d("f32", 2048, 2048, 2048, 2049, 2049, 2049))
+    prev = dg.gemm_set_workspace_limit(need - 1)
+    try:
+        assert "copies" not in d("f32", 2048, 2048, 2048, 2049, 2049, 2049)
+        dg.gemm_set_workspace_limit(need)
+        assert "copies A B" in d("f32", 2048, 2048, 2048, 2049, 2049, 2049)
+    finally:
+        dg.gemm_set_workspace_limit(prev)

@@ -10,7 +10,7 @@ import pytest
 import oracle
 import workloads as wl
 from gemm_harness import (bits, check, check_sampled, colmajor_buf, colmajor_view, exact_expected,
-                          np_in, np_out, run, run_colmajor)
+                          note, np_in, np_out, run, run_colmajor)
 
 pytestmark = pytest.mark.gpu
 
@@ -552,8 +552,10 @@ CHOSEN_SPLIT_CASES = [
 
 @pytest.mark.parametrize("case", CHOSEN_SPLIT_CASES, ids=lambda c: "%s_%dx%dx%d_pad%d" % (c[0], *c[1:4], c[4][0]))
 def test_splits_chosen_by_rule_match_oracle(case):
-    """The plan takes the expected split by itself (no test switch), with NaN
-    pads and a C-pad sentinel, and matches the oracle element by element."""
+    """The plan takes the expected split by itself (no tile or split switch;
+    operand copies off, so unaligned operands keep their staged loads), with
+    NaN pads and a C-pad sentinel, and matches the oracle element by
+    element."""
     import dense_gemm_fp32_amd as dg
     dtype, M, N, K, (pa, pb, pc), want = case
     lda, ldb, ldc = K + pa, N + pb, N + pc
@@ -562,9 +564,10 @@ def test_splits_chosen_by_rule_match_oracle(case):
     B = wl.pad(rng.standard_normal((K, N)).astype(_t(dtype)), ldb, np.nan)
     C = wl.pad(rng.standard_normal((M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
     base = 1 << 20
-    plan = dg.gemm_describe(dtype, M, N, K, 1.5, base, lda, base, ldb, -0.75, base, ldc)[1]
-    assert want in plan and "last round" not in plan, plan
-    rc, out = run(dtype, M, N, K, 1.5, A, lda, B, ldb, -0.75, C, ldc, "chosen " + want)
+    with pack_mode(1):
+        plan = dg.gemm_describe(dtype, M, N, K, 1.5, base, lda, base, ldb, -0.75, base, ldc)[1]
+        assert want in plan and "last round" not in plan, plan
+        rc, out = run(dtype, M, N, K, 1.5, A, lda, B, ldb, -0.75, C, ldc, "chosen " + want)
     assert rc == 0
     check(dtype, M, N, K, 1.5, A, lda, B, ldb, -0.75, C, ldc, out, "chosen %s %s" % (dtype, want))
 
@@ -1119,3 +1122,144 @@ def test_workspace_refused_runs_unsplit(dtype, M, N, K):
     rc, dflt = run(dtype, M, N, K, 1.0, A, K, B, N, 0.5, C, N, "default")
     assert rc == 0
     assert np.array_equal(bits(out2, dtype), bits(dflt, dtype))
+
+
+# ---------------------------------------------------------------- operand copies
+
+@contextmanager
+def pack_mode(mode):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_pack(mode)
+    assert prev in (0, 1, 2)
+    try:
+        yield
+    finally:
+        dg.gemm_set_pack(prev)
+
+
+def _layout_outputs(dtype, layout, M, N, K, pads, seed, alpha, beta, label):
+    """Stored operands (NaN pads) of a call in `layout` ("nn" = gemm_<dtype>)
+    and the call's output; returns (A, B, C, Cbuf, ldc, out)."""
+    from gemm_harness import layout_case, run_layout
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    lda = (M if ta else K) + pads[0]
+    ldb = (K if tb else N) + pads[1]
+    ldc = N + pads[2]
+    Abuf, Bbuf, Cbuf, A, B, C = layout_case(dtype, M, N, K, ta, tb, lda, ldb, ldc, seed)
+    if layout == "nn":
+        rc, out = run(dtype, M, N, K, alpha, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc, label)
+    else:
+        rc, out = run_layout(dtype, layout, M, N, K, alpha, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc,
+                             label)
+    assert rc == 0, rc
+    return A, B, C, Cbuf, ldc, out
+
+
+# (M, N, K, pad_a, pad_b, pad_c): odd pads leave the rows of that operand
+# without 16-byte alignment, so it is copied when copies are forced.
+COPY_SHAPES = [
+    (1000, 3000, 517, 13, 5, 3),       # the ragged workload's sizes: A and B copied
+    (301, 203, 97, 1, 3, 0),           # tails in M, N and K
+    (256, 512, 384, 1, 0, 0),          # only A copied
+    (256, 512, 384, 0, 1, 8),          # only B copied
+    (7, 130, 45, 1, 0, 2),
+]
+
+
+@pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_operand_copies_match_oracle_and_staged_path(dtype, layout):
+    """Copies forced (gemm_set_pack(2)) against copies off (1), under the same
+    forced tile and split: the copy is bit-exact and the kernels sum the same
+    products in the same order, so the outputs are the same bits; both within
+    the oracle's bound, NaN pads never read (the copy reads only the matrix
+    and writes zeros into its own pads)."""
+    from gemm_harness import check_layout
+    for idx, (M, N, K, *pads) in enumerate(COPY_SHAPES):
+        beta = [-0.75, 0.0, 1.0, 0.5, 0.25][idx]
+        outs = []
+        for mode in (2, 1):
+            with pack_mode(mode), tile_config(2), split_mode(1):
+                A, B, C, Cbuf, ldc, out = _layout_outputs(dtype, layout, M, N, K, pads, 700 + idx,
+                                                          1.5, beta, "pack%d" % mode)
+            check_layout(dtype, M, N, K, 1.5, A, B, beta, C, Cbuf, ldc, out,
+                         "pack %d %s" % (mode, (M, N, K)))
+            outs.append(out)
+        assert np.array_equal(bits(outs[0], dtype), bits(outs[1], dtype)), (dtype, layout, M, N, K)
+        # and with the tile and split the rule picks for the copies
+        with pack_mode(2):
+            A, B, C, Cbuf, ldc, out = _layout_outputs(dtype, layout, M, N, K, pads, 700 + idx, 1.5,
+                                                      beta, "pack2 by size")
+        check_layout(dtype, M, N, K, 1.5, A, B, beta, C, Cbuf, ldc, out, "pack 2 by size")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_operand_copy_of_a_misaligned_base(dtype):
+    """Leading dimensions that allow 16-byte rows, but A and B start one
+    element past a 16-byte boundary: the rows are copied (forced) to an
+    aligned buffer; bitwise equal to the staged path under the same tile and
+    split, and within the oracle's bound."""
+    import torch
+    import dense_gemm_fp32_amd as dg
+    M, N, K = 384, 320, 256
+    rng = np.random.default_rng(91)
+    t = _t(dtype)
+    A = rng.uniform(-1, 1, (M, K)).astype(t)
+    B = rng.uniform(-1, 1, (K, N)).astype(t)
+    C = rng.uniform(-1, 1, (M, N)).astype(_tc(dtype))
+    dev = torch.device("cuda:0")
+    fn = {"f32": dg.gemm_f32, "f16": dg.gemm_f16, "f16f32": dg.gemm_f16f32}[dtype]
+    outs = []
+    for mode in (2, 1):
+        note("misaligned base, copies mode %d, %s %dx%dx%d" % (mode, dtype, M, N, K))
+        # one leading element, so the matrices start 4 (fp32) or 2 (fp16) bytes in
+        dA = torch.from_numpy(np.concatenate([np.zeros(1, t), A.reshape(-1)])).to(dev)
+        dB = torch.from_numpy(np.concatenate([np.zeros(1, t), B.reshape(-1)])).to(dev)
+        dC = torch.from_numpy(C.reshape(-1).copy()).to(dev)
+        with pack_mode(mode), tile_config(2), split_mode(1):
+            rc, plan = dg.gemm_describe(dtype, M, N, K, 1.0, dA[1:], K, dB[1:], N, 0.5, dC, N)
+            assert rc == 0 and (("copies A B" in plan) == (mode == 2)), plan
+            rc = fn(M, N, K, 1.0, dA[1:], K, dB[1:], N, 0.5, dC, N,
+                    torch.cuda.current_stream(dev))
+        torch.cuda.synchronize(dev)
+        assert rc == 0
+        outs.append(dC.cpu().numpy())
+    assert np.array_equal(bits(outs[0], dtype), bits(outs[1], dtype))
+    check(dtype, M, N, K, 1.0, A.reshape(-1), K, B.reshape(-1), N, 0.5, C.reshape(-1), N, outs[0],
+          "misaligned base copied")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "f16f32"])
+def test_operand_copies_chosen_by_size_sampled(dtype):
+    """2048^3 with every leading dimension 2049: above the size rule, so A and
+    B are copied and the GEMM runs the direct-load kernels on the copies;
+    sampled rows against the oracle, plus the last tile row and column."""
+    import dense_gemm_fp32_amd as dg
+    n = 2048
+    w = wl.Workload("copies_%s_%d" % (dtype, n), dtype, n, n, n, n + 1, n + 1, n + 1, 1.0, 0.5,
+                    "uniform", "uniform", (61, 62, 63))
+    rc, plan = dg.gemm_describe(dtype, n, n, n, 1.0, 4096, n + 1, 4096, n + 1, 0.5, 4096, n + 1)
+    assert rc == 0 and "copies A B" in plan, plan
+    A, B, C = wl.make(w)
+    rc, out = run(dtype, n, n, n, 1.0, A, n + 1, B, n + 1, 0.5, C, n + 1, "copies by size (%s)" % plan)
+    assert rc == 0
+    check_sampled(dtype, w, A, B, C, out, nrows=24, seed=11, extra_rows=[n - 1, n - 129])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_operand_copies_refused_fall_back(dtype):
+    """With no workspace to be had (limit 0) a call above the size rule runs
+    on its original operands, unsplit: bitwise equal to copies and splitting
+    switched off, within the oracle's bound."""
+    n = 2048
+    w = wl.Workload("copies_refused_%s" % dtype, dtype, n, n, n, n + 1, n + 1, n + 1, 1.0, 0.5,
+                    "uniform", "uniform", (64, 65, 66))
+    A, B, C = wl.make(w)
+    with workspace_limit(0):
+        rc, out0 = run(dtype, n, n, n, 1.0, A, n + 1, B, n + 1, 0.5, C, n + 1, "copies refused")
+    assert rc == 0
+    with pack_mode(1), split_mode(1), tail_split(1):
+        rc, ref = run(dtype, n, n, n, 1.0, A, n + 1, B, n + 1, 0.5, C, n + 1, "no copies, unsplit")
+    assert rc == 0
+    assert np.array_equal(bits(out0, dtype), bits(ref, dtype))
+    check_sampled(dtype, w, A, B, C, out0, nrows=12, seed=12)

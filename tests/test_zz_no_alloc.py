@@ -63,12 +63,23 @@ def test_noalloc_matches_gemm_f32_on_calls_in_a_row():
     check_sampled("f32", w3, A, B, C, out_na, nrows=16, seed=5,
                   extra_rows=[2944 - 1 - 128 * i - 37 for i in range(8)])
 
-    # 4) a call that does not split uses no workspace at all.
-    w4 = wl.square(384, seeds=(8, 9, 10))
+    # 4) unaligned leading dimensions above the size rule for operand copies:
+    #    2048^3 with every ld = 2049.  A and B are copied into the region (two
+    #    2048 x 2048 fp32 copies, 33,554,432 bytes) and the GEMM runs on the
+    #    copies, unsplit.
+    w4 = wl.Workload("noalloc_copies_2048", "f32", 2048, 2048, 2048, 2049, 2049, 2049, 1.0, 0.5,
+                     "uniform", "uniform", (12, 13, 14))
     plan, (A, B, C), out_na, out_ref = _both(w4)
+    assert "copies A B" in plan and "workspace 33554432 bytes" in plan, plan
+    assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
+    check_sampled("f32", w4, A, B, C, out_na, nrows=12, seed=6, extra_rows=[2047])
+
+    # 5) a call that does not split uses no workspace at all.
+    w5 = wl.square(384, seeds=(8, 9, 10))
+    plan, (A, B, C), out_na, out_ref = _both(w5)
     assert "workspace" not in plan, plan
     assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
-    check("f32", w4.M, w4.N, w4.K, w4.alpha, A, w4.lda, B, w4.ldb, w4.beta, C, w4.ldc, out_na,
+    check("f32", w5.M, w5.N, w5.K, w5.alpha, A, w5.lda, B, w5.ldb, w5.beta, C, w5.ldc, out_na,
           "384 noalloc")
 
 
