@@ -550,3 +550,63 @@ def test_operand_copies_by_size_and_switches():
         assert "copies A B" in d("f32", 2048, 2048, 2048, 2049, 2049, 2049)
     finally:
         dg.gemm_set_workspace_limit(prev)
+
+
+def _profile_rows(name):
+    """Data rows of the markdown table in profiles/<name> (lists of cells):
+    the lines after the table's header and separator."""
+    rows, seen_sep = [], False
+    with open(os.path.join(ROOT, "profiles", name)) as f:
+        for line in f:
+            if not line.startswith("|"):
+                continue
+            if line.startswith("|---"):
+                seen_sep = True
+                continue
+            if seen_sep:
+                rows.append([c.strip() for c in line.strip().strip("|").split("|")])
+    return rows
+
+
+def _short_plan(plan, sweep):
+    """The tile column the sweep and workload tables print for a plan."""
+    body = plan.split(" tile ", 1)[1]
+    if sweep:
+        short = body.split(" loads A:")[0]
+        if "split-K" in plan:
+            short += " " + ("last round " if "last round" in plan else "") + \
+                "split-K " + plan.split("split-K ")[1].split()[0]
+        return short
+    short = body.split(" blocks ")[0]
+    if "split-K" in plan:
+        short += " split-K " + plan.split("split-K ")[1].split()[0]
+    return short
+
+
+def test_plans_match_the_committed_sweep_and_table():
+    """Each size of the committed fp32 sweep and each workload of the
+    committed table was measured with a plan (tile, loads, split) that the
+    library still chooses for it: a change to the tile or split rules that
+    moves any of them must come with new measurements."""
+    import dense_gemm_fp32_amd as dg
+    import workloads as wl
+    sweep = _profile_rows("sweep_f32_1024_12800.md")
+    assert len(sweep) == len(wl.sweep_sizes()), len(sweep)
+    for cells in sweep:
+        n = int(cells[0])
+        rc, plan = dg.gemm_describe("f32", n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
+        assert rc == 0
+        assert _short_plan(plan, True) == cells[-1], (n, plan, cells[-1])
+    table = {c[0]: c for c in _profile_rows("workloads_table.md")}
+    by_name = {w.name: w for w in wl.ALL}
+    checked = 0
+    for name, cells in table.items():
+        w = by_name.get(name)
+        if w is None:
+            continue
+        rc, plan = dg.gemm_describe(w.dtype, w.M, w.N, w.K, w.alpha, FAKE, w.lda, FAKE, w.ldb,
+                                    w.beta, FAKE, w.ldc)
+        assert rc == 0
+        assert _short_plan(plan, False) == cells[-1], (name, plan, cells[-1])
+        checked += 1
+    assert checked >= 7, sorted(table)
