@@ -160,7 +160,9 @@ def gemm_set_load_mode(mode):
 
 def gemm_set_tile_config(config):
     """0 = tile configuration by problem size (default); 1/2/3/4 = force the
-    large/medium/small/tiny configuration (fp16 maps 4 to small)."""
+    large/medium/small/tiny configuration (fp16 maps 4 to small); 5 = fp32
+    medium with loads issued together; 6 = fp32 256x256 (fp16 large on
+    32x32x16 blocks); 7 = fp32 64x64 with four waves (fp16 small)."""
     return _lib.gemm_set_tile_config(int(config))
 
 
@@ -200,9 +202,9 @@ def gemm_set_tail_split(mode):
 
 def gemm_set_pack(mode):
     """0 = copy operands whose rows do not allow 16-byte loads to 16-byte rows
-    when the call does at least 5e9 (fp32) / 1.5e10 (fp16) flops (default);
-    1 = never; 2 = whenever their rows do not allow 16-byte loads.  Returns
-    the previous mode, or -1."""
+    in fp32 calls of at least 5e9 flops, or 1.5e9 with N % 4 == 0 (default);
+    1 = never; 2 = whenever their rows do not allow 16-byte loads (fp16
+    too).  Returns the previous mode, or -1."""
     return _lib.gemm_set_pack(int(mode))
 
 

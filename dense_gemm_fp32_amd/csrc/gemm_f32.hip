@@ -881,6 +881,7 @@ typedef S32Tile<256, 128, 32, 4, 2, 3, 8, true> F32Big;  // 8 waves, 144 KB LDS,
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8, true> F32Mid;  // 4 waves,  48 KB LDS, 3 WG/CU
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issued together
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
+typedef S32Tile<64, 64, 32, 2, 2, 3, 8> F32Quad;      // 4 waves of 32x32, 48 KB LDS, 3 WG/CU
 typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
@@ -963,7 +964,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny };
+enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
@@ -1159,9 +1160,27 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
+  if (c.tile_config == 7) return F32Choice{F32Cfg::kQuad, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
       tiles_of<F32Mid>(c) < 3LL * kCUs)
     return choose_staged(c);
+  // Grids of one to three 64x64 tiles per CU (all resident at once) whose K
+  // is not deep: the 64x64 tile of four 32x32 waves, unsplit.  Each CU then
+  // holds four to twelve waves with no split pass, where the 128x128 tile
+  // needs a K split (and its reduction) to fill the CUs and the 32x32 tile
+  // runs a single wave per workgroup.  Measured (interleaved, beta 1 and 0)
+  // against the choice before it: 1024^3 56 -> 78 TFLOP/s, 1280^3 80 -> 85,
+  // 1408^3 88 -> 103, 1536^3 90 -> 93, 1664^3 105 -> 110,
+  // 2048x1024x1024 83 -> 103, 1536x1024x1024 65 -> 78, 2048x512x2048
+  // 79-84 -> 86, 1000^3 and 4096x256x1024 +1-3%; 1152^3 71 -> 68 is the one
+  // loss.  Deeper K (1024x1024x4096) keeps the 128x128 tile in 8 chunks
+  // (106 against 93), and 1792^3 (3.1 tiles per CU) the unsplit 128x128 tile.
+  if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
+    const long long q = tiles_of<F32Quad>(c);
+    const long long mx = c.M > c.N ? c.M : c.N;
+    if (q >= kCUs && q <= 3LL * kCUs && (long long)c.K <= 2 * mx)
+      return F32Choice{F32Cfg::kQuad, 1, 0.0, 1};
+  }
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
   const double small = score_of<F32Small>(c, 0.57, 3, 1);
@@ -1352,6 +1371,7 @@ static Plan plan_f32_as_is(const Call &c) {
     case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
     case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits, ch.tail);
+    case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots", ch.splits, ch.tail);
     default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits, ch.tail);
   }
 }
@@ -1364,6 +1384,7 @@ static hipError_t launch_f32_as_is(const Call &c) {
     case F32Cfg::kMid: return launch_cfg<F32Mid>(c, ch.splits, ch.tail);
     case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits, ch.tail);
     case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits, ch.tail);
+    case F32Cfg::kQuad: return launch_cfg<F32Quad>(c, ch.splits, ch.tail);
     default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }

@@ -128,20 +128,28 @@ long long ws_available(const Call &c) {
   return kPoolCallCap;
 }
 
-// The rule: copy when the call does at least kPackMinFlops32 (fp32) or
-// kPackMinFlops16 (fp16) flops.  Measured interleaved, with and without the
-// copies, on square sizes with ld = n + 1 and on skewed shapes: the copy costs
-// a launch of about 9 us for a few MB (latency-bound) plus the operands' bytes
-// at memory speed; above the thresholds the GEMM on the copies won every time
-// (fp32 2048^3 +15%, 4096^3 +11-16%, 8192^3 +16%, 2000x2000x1000 +20%,
-// 1000x1000x4000 +16%; fp16 2048^3 +10-23%, 8192^3 +12-22%,
-// 1000x1000x4000 +23-33%, 2000x2000x1000 +11-15%).  Below them the register-
-// staged path, whose tile and split were chosen for it, was as fast or faster
-// on several shapes (fp16 1536^3 -2-4%, 3000x517x1000 -55%; fp32
-// 3000x517x1000 -25%, 256^3 -12-18%), and fp16's large tile loses little to
-// staged loads (4096^3 with every ld = 4097: -8% to +1%).
-constexpr double kPackMinFlops32 = 5.0e9;
-constexpr double kPackMinFlops16 = 1.5e10;
+// The rule (fp32): copy when the call does at least kPackMinFlops flops, or
+// at least kPackMinFlopsEvenN with N a multiple of 4 (then the copied call's
+// last tile column still takes the direct loads; with a ragged N that column
+// runs the masked staged path, and a grid of one round waits for it).
+// Measured interleaved, copies forced on and off: the copy costs a launch of
+// about 9 us for a few MB (latency-bound) plus the operands' bytes at memory
+// speed; 2048^3 with every ld = 2049 +14-18%, 4096^3 +11-16%, 8192^3 +16%,
+// 2000x2000x1000 +17-20%, 1000x1000x4000 +12-16%, 1536^3 +3-9%, the ragged
+// 1000x3000x517 workload +21-29% (its copies take the four-wave 64x64 tile),
+// 517x3000x1000 +4-12%, 1024^3 +5-7%, 1000^3 +3%; 1280^3 -4%; below the
+// rule 768^3 -3%, 256^3 -11%, and 3000x517x1000 (N = 517) -20%.
+// fp16 copies are made only when forced: the same measurements gave +10-23%
+// on one box and -1 to -20% on another for the same shapes (2048^3, 4096^3,
+// 8192^3 with ld = n + 1), so no size rule held.
+constexpr double kPackMinFlops = 5.0e9;
+constexpr double kPackMinFlopsEvenN = 1.5e9;
+
+bool pack_by_size(const Call &c, int eb) {
+  if (eb != 4) return false;
+  const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
+  return flops >= kPackMinFlops || (flops >= kPackMinFlopsEvenN && c.N % 4 == 0);
+}
 
 }  // namespace
 
@@ -150,8 +158,7 @@ PackChoice pack_choice(const Call &c, int eb, Plan (*plan)(const Call &)) {
   if (c.force_scalar || c.pack_mode == 1) return pk;
   const bool ua = !rows_aligned(c.A, c.lda, eb), ub = !rows_aligned(c.B, c.ldb, eb);
   if (!ua && !ub) return pk;
-  const double flops = 2.0 * (double)c.M * (double)c.N * (double)c.K;
-  if (c.pack_mode != 2 && flops < (eb == 4 ? kPackMinFlops32 : kPackMinFlops16)) return pk;
+  if (c.pack_mode != 2 && !pack_by_size(c, eb)) return pk;
   int ra, ca, rb, cb;
   stored_a(c, &ra, &ca);
   stored_b(c, &rb, &cb);

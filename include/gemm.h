@@ -37,15 +37,16 @@
  *     small remainder may do this for the remainder's tiles only (dense
  *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
  *     the whole rounds.
- *   - Operand copies: when the rows of A or B do not allow 16-byte loads (ld
- *     not a multiple of 4 floats / 8 halves, or a base not 16-byte aligned)
- *     and the call does at least 5e9 flops (fp32) or 1.5e10 (fp16 inputs),
- *     that operand is first copied, bit for bit, into workspace rows padded
- *     to 16 bytes, and the GEMM runs on the copy (the SGEMM summary's
- *     memory-layout section: its 128-bit loads need ld % 4 == 0).  Same products, same bound; the tile and
- *     split are chosen for the copy.  Smaller calls, and calls whose
- *     workspace cannot be had, load such operands in pairs or element by
- *     element instead.
+ *   - Operand copies (fp32): when the rows of A or B do not allow 16-byte
+ *     loads (ld not a multiple of 4, or a base not 16-byte aligned) and the
+ *     call does at least 5e9 flops, or 1.5e9 with N a multiple of 4, that
+ *     operand is first copied, bit for bit, into workspace rows padded to 16
+ *     bytes, and the GEMM runs on the copy (the SGEMM summary's
+ *     memory-layout section: its 128-bit loads need ld % 4 == 0).  Same
+ *     products, same bound; the tile and split are chosen for the copy.
+ *     Smaller calls, fp16 calls (unless forced, gemm_set_pack) and calls
+ *     whose workspace cannot be had load such operands in pairs or element
+ *     by element instead.
  *   - Accuracy: |C_gpu - C_exact| <= 4*K*u*(|alpha|*(|A||B|)_ij + |beta|*|C_ij|)
  *     plus one rounding to the output type, u = 2^-24 (fp32 accumulation).
  *
@@ -311,7 +312,8 @@ int gemm_set_load_mode(int mode);
  * configuration with each K step's loads issued together rather than spread
  * (fp32 only; fp16 uses its medium one); 6 = the fp32 256 x 256 tile, and
  * for fp16 the large tile on 32x32x16 blocks (1 forces it on 16x16x32
- * blocks; the size-based choice takes either).  Process-wide,
+ * blocks; the size-based choice takes either); 7 = the fp32 64 x 64 tile of
+ * four 32 x 32 waves (fp16 uses its small one).  Process-wide,
  * like gemm_set_load_mode.  Returns the previous setting, or -1 for an
  * unknown value.
  */
@@ -339,9 +341,9 @@ int gemm_set_tail_split(int mode);
 
 /*
  * Diagnostic switch for tests: 0 = copy A or B to 16-byte rows when their
- * rows do not allow 16-byte loads and the call is large enough (the default;
- * see "Operand copies" above); 1 = never copy; 2 = copy whenever
- * their rows do not allow 16-byte loads, whatever the size.  Copies are made
+ * rows do not allow 16-byte loads and the fp32 call is large enough (the
+ * default; see "Operand copies" above); 1 = never copy; 2 = copy whenever
+ * their rows do not allow 16-byte loads, whatever the size and type.  Copies are made
  * only where the workspace fits (gemm_set_workspace_limit) and never under
  * gemm_set_load_mode(1).  Process-wide, like gemm_set_load_mode.  Returns the
  * previous setting, or -1 for an unknown value.

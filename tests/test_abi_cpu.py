@@ -119,7 +119,18 @@ def test_status_strings():
 
 
 def test_describe_picks_vector_or_scalar_loads():
+    """Load widths per operand from its leading dimension and base (operand
+    copies switched off: they would replace an unaligned fp32 operand by an
+    aligned copy)."""
     import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_pack(1)
+    try:
+        _load_widths(dg)
+    finally:
+        dg.gemm_set_pack(prev)
+
+
+def _load_widths(dg):
     rc, t = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
     assert rc == 0 and "A:vec4" in t and "B:vec4" in t and "C:vec" in t and "beta0" in t
     # ragged, unaligned leading dimensions (K+13, N+5, N+3): lda = 530 is even,
@@ -256,12 +267,16 @@ def test_tile_table_choice_and_override():
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
     assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
-    # 1024^3: four K chunks of the 128x128 tile beat 1024 one-wave 32x32 tiles
-    assert "128x128x16" in name("f32", 1024) and "split-K 4" in name("f32", 1024)
+    # one to three 64x64 tiles per CU: that tile with four 32x32 waves, unsplit
+    for n in (1024, 1280, 1536, 1664):
+        assert "64x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
+    assert "64x64x32 4 waves" not in name("f32", 1792) and "64x64x32 4 waves" not in name("f32", 768)
     assert "32x32x32" in name("f32", 256) and "32x32x32" in name("f32", 64)
     assert "split" not in name("f32", 256) and "split" not in name("f32", 768)
     # K split where the grid leaves CUs idle and K is long enough
-    assert "128x128x16" in name("f32", 1536) and "split-K 3" in name("f32", 1536)
+    t = dg.gemm_describe("f32", 1024, 1024, 4096, 1.0, FAKE, 4096, FAKE, 1024, 0.0, FAKE, 1024)[1]
+    assert "128x128x16" in t and "split-K 8" in t, t
+    assert "128x128x16" in name("f32", 2304) and "split-K 3" in name("f32", 2304)
     assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
     assert "split" not in name("f16", 1536)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
@@ -283,9 +298,11 @@ def test_tile_table_choice_and_override():
         assert "256x256x32" in name("f32", 256) and "256x256x64" in name("f16", 256)
         dg.gemm_set_tile_config(4)
         assert "32x32x32" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
+        dg.gemm_set_tile_config(7)
+        assert "64x64x32 4 waves" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
     finally:
         dg.gemm_set_tile_config(prev)
-    assert dg.gemm_set_tile_config(9) == -1
+    assert dg.gemm_set_tile_config(9) == -1 and dg.gemm_set_tile_config(8) == -1
 
 
 def test_staged_calls_split_the_medium_tile():
@@ -331,18 +348,23 @@ def _staged_choices(dg):
         dg.gemm_set_split(prev)
 
 
-def test_wide_short_problems_split_the_medium_tile():
-    """Aligned problems with K below max(M, N) whose 128x128 tiles leave CUs
-    idle split that tile in chunks of at least 512 k; shorter chunks do not
-    pay, and square problems keep their own rule."""
+def test_wide_short_problems_take_the_four_wave_64x64_tile():
+    """Aligned problems whose 64x64 tiles give every CU one to three of them
+    (and whose K is not deeper than twice max(M, N)) take that tile with four
+    32x32 waves, unsplit; beyond three per CU, or with fewer tiles than CUs,
+    the other rules decide (wide, short problems whose 128x128 tiles leave CUs
+    idle then split that tile in chunks of at least 512 k)."""
     import dense_gemm_fp32_amd as dg
     def d(M, N, K):
         return dg.gemm_describe("f32", M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
-    assert "128x128x16" in d(517, 3000, 1000) and "split-K 2" in d(517, 3000, 1000)
-    assert "split-K 4" in d(128, 16384, 4096) and "split-K 2" in d(256, 8192, 1024)
-    assert "split" not in d(384, 3000, 600)          # two chunks would be 304 deep
-    assert "split" not in d(1000, 8000, 700)         # 504 tiles: CUs already busy
-    assert "32x32x32" in d(1000, 1000, 1000) and "split" not in d(1000, 1000, 1000)
+    for shape in [(517, 3000, 1000), (256, 8192, 1024), (128, 16384, 4096), (384, 3000, 600),
+                  (256, 4096, 2048), (1000, 3000, 520), (1000, 1000, 1000)]:
+        t = d(*shape)
+        assert "64x64x32 4 waves" in t and "split" not in t, (shape, t)
+    assert "64x64x32 4 waves" not in d(1000, 8000, 700)    # 2000 tiles: over three per CU
+    assert "64x64x32 4 waves" not in d(1024, 1024, 4096)   # deep K: the 128x128 tile in chunks
+    t = d(2048, 384, 2048)                                 # 192 tiles: fewer than the CUs
+    assert "128x128x16" in t and "split-K" in t, t
 
 
 def test_split_choice_and_override():
@@ -487,10 +509,11 @@ def test_workspace_limit_switch():
 
 def test_operand_copies_by_size_and_switches():
     """Operands whose rows do not allow 16-byte loads are copied to 16-byte
-    rows above the size rule (5e9 flops fp32, 1.5e10 fp16), never under
-    gemm_set_pack(1) or the element-wise load switch, always under
-    gemm_set_pack(2); the copies' bytes are part of the reported workspace
-    and a workspace limit below them drops the copies."""
+    rows in fp32 calls above the size rule (5e9 flops, or 1.5e9 with N a
+    multiple of 4), never in fp16 calls by size, never under gemm_set_pack(1)
+    or the element-wise load switch, always under gemm_set_pack(2); the
+    copies' bytes are part of the reported workspace and a workspace limit
+    below them drops the copies."""
     import dense_gemm_fp32_amd as dg
 
     def d(dtype, M, N, K, lda, ldb, ldc, a=FAKE, b=FAKE):
@@ -512,10 +535,16 @@ def test_operand_copies_by_size_and_switches():
     assert "copies B" in t, t
     # a base off a 16-byte boundary alone is enough
     assert "copies A" in d("f32", 2048, 2048, 2048, 2048, 2048, 2048, a=FAKE + 4)
-    # below the rule: the ragged workload (3.1e9 flops) and fp16 1536^3 are not copied
-    assert "copies" not in d("f32", 1000, 3000, 517, 530, 3005, 3003)
-    assert "copies" not in d("f16", 1536, 1536, 1536, 1537, 1537, 1537)
-    assert "copies A B" in d("f16", 2048, 2048, 2048, 2049, 2049, 2049)
+    # the ragged workload (3.1e9 flops, N = 3000): copied, and the copies take
+    # the four-wave 64x64 tile
+    t = d("f32", 1000, 3000, 517, 530, 3005, 3003)
+    assert "copies A B" in t and "64x64x32 4 waves" in t, t
+    # the same size with a ragged N, and smaller calls: not copied
+    assert "copies" not in d("f32", 3000, 517, 1000, 1001, 519, 519)
+    assert "copies" not in d("f32", 768, 768, 768, 769, 769, 769)
+    # fp16: not by size
+    assert "copies" not in d("f16", 4096, 4096, 4096, 4097, 4097, 4097)
+    assert "copies" not in d("f16", 1000, 3000, 517, 530, 3005, 3003)
     # aligned operands are never copied
     assert "copies" not in d("f32", 4096, 4096, 4096, 4096, 4096, 4097)
     # the switches

@@ -73,6 +73,16 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
+@pytest.mark.parametrize("n", [1152, 1408, 1664])
+def test_f32_sweep_four_wave_tile_full_oracle(n):
+    """Sweep sizes (beta = 1) whose plan is the 64x64 tile of four 32x32
+    waves, one to three tiles per CU, every element against the oracle."""
+    w = wl.sweep(n)
+    plan = _plan(w)
+    assert "64x64x32 4 waves" in plan and "split" not in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
 @pytest.mark.parametrize("n", [2304, 2944, 3584])
 def test_f32_sweep_mid_sizes_sampled(n):
     """Sweep sizes whose chosen plans split K: 2304^3 (every tile split),
@@ -407,8 +417,9 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6],
-                         ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7],
+                         ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256",
+                              "f32-64x64-four-waves"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -540,8 +551,8 @@ def test_split_k_ragged_workload(w):
 # short problems and for unaligned (element-wise loaded) operands:
 # (dtype, M, N, K, pad of lda / ldb / ldc, expected split in the plan).
 CHOSEN_SPLIT_CASES = [
-    ("f32", 517, 3000, 1000, (0, 0, 0), "split-K 2"),      # wide, short, aligned
-    ("f32", 128, 16384, 4096, (0, 0, 0), "split-K 4"),
+    ("f32", 2048, 384, 2048, (0, 0, 0), "split-K 5"),      # fewer 64x64 tiles than CUs, aligned
+    ("f32", 1024, 1024, 4096, (0, 0, 0), "split-K 8"),     # deep K
     ("f32", 517, 3000, 1000, (13, 5, 3), "split-K 4"),     # unaligned
     ("f32", 2000, 2000, 1000, (13, 5, 3), "split-K 3"),
     ("f16", 1500, 1500, 1500, (13, 5, 3), "split-K 3"),
@@ -604,7 +615,7 @@ def test_split_k_deterministic_and_paths_agree(dtype):
         check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o, "split 3 cfg %d" % cfg)
 
 
-@pytest.mark.parametrize("dtype,M,N,K", [("f32", 1536, 1536, 1536), ("f16", 1024, 1024, 8192),
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 2304, 2304, 2304), ("f16", 1024, 1024, 8192),
                                           ("f16f32", 512, 512, 8192), ("f32", 512, 512, 8192)])
 def test_split_k_chosen_by_size_sampled(dtype, M, N, K):
     """Shapes whose tile grid leaves CUs idle take split K by themselves;
@@ -812,7 +823,7 @@ def test_layouts_match_oracle(dtype, layout):
         _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_layouts_every_tile(dtype, layout, cfg):
@@ -1231,9 +1242,18 @@ def test_operand_copy_of_a_misaligned_base(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "f16f32"])
 def test_operand_copies_chosen_by_size_sampled(dtype):
-    """2048^3 with every leading dimension 2049: above the size rule, so A and
-    B are copied and the GEMM runs the direct-load kernels on the copies;
-    sampled rows against the oracle, plus the last tile row and column."""
+    """2048^3 with every leading dimension 2049: above the fp32 size rule, so
+    A and B are copied and the GEMM runs the direct-load kernels on the
+    copies (fp16 copies forced: no size rule copies them); sampled rows
+    against the oracle, plus the last tile row and column."""
+    if dtype == "f32":
+        _copies_2048(dtype)
+    else:
+        with pack_mode(2):
+            _copies_2048(dtype)
+
+
+def _copies_2048(dtype):
     import dense_gemm_fp32_amd as dg
     n = 2048
     w = wl.Workload("copies_%s_%d" % (dtype, n), dtype, n, n, n, n + 1, n + 1, n + 1, 1.0, 0.5,
@@ -1248,14 +1268,15 @@ def test_operand_copies_chosen_by_size_sampled(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_operand_copies_refused_fall_back(dtype):
-    """With no workspace to be had (limit 0) a call above the size rule runs
-    on its original operands, unsplit: bitwise equal to copies and splitting
-    switched off, within the oracle's bound."""
+    """With no workspace to be had (limit 0) a call that would copy its
+    operands (fp32 above the size rule; fp16 with copies forced) runs on its
+    original operands, unsplit: bitwise equal to copies and splitting switched
+    off, within the oracle's bound."""
     n = 2048
     w = wl.Workload("copies_refused_%s" % dtype, dtype, n, n, n, n + 1, n + 1, n + 1, 1.0, 0.5,
                     "uniform", "uniform", (64, 65, 66))
     A, B, C = wl.make(w)
-    with workspace_limit(0):
+    with workspace_limit(0), pack_mode(0 if dtype == "f32" else 2):
         rc, out0 = run(dtype, n, n, n, 1.0, A, n + 1, B, n + 1, 0.5, C, n + 1, "copies refused")
     assert rc == 0
     with pack_mode(1), split_mode(1), tail_split(1):

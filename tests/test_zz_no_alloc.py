@@ -44,12 +44,13 @@ def test_noalloc_matches_gemm_f32_on_calls_in_a_row():
     assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
     check_sampled("f32", w1, A, B, C, out_na, nrows=16, seed=3)
 
-    # 2) smaller: the ragged 1000 x 3000 x 517 workload (unaligned lda, all
-    #    three tails), K split 4 ways, 48,000,000 bytes; the region still holds
-    #    the first call's slabs beyond that.
+    # 2) smaller: the ragged 1000 x 3000 x 517 workload (unaligned lda and
+    #    ldb, all three tails): A and B copied to 16-byte rows in the region
+    #    (1000 x 520 and 517 x 3000 floats, 8,284,160 bytes), unsplit; the
+    #    region still holds the first call's slabs beyond that.
     w2 = wl.RAGGED_F32
     plan, (A, B, C), out_na, out_ref = _both(w2)
-    assert "split-K 4" in plan and "workspace 48000000 bytes" in plan, plan
+    assert "copies A B" in plan and "workspace 8284160 bytes" in plan, plan
     assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
     check("f32", w2.M, w2.N, w2.K, w2.alpha, A, w2.lda, B, w2.ldb, w2.beta, C, w2.ldc, out_na,
           "ragged noalloc")
