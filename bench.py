@@ -477,8 +477,10 @@ def main():
         print(json.dumps({"only": "f16f32", **res}), flush=True)
         return
     if args.only in ("ragged_f32", "ragged_f16"):
-        # the unaligned 1000 x 3000 x 517 workload (element-wise loads, split K
-        # by the library's own choice); a call's time includes its reduction
+        # the unaligned 1000 x 3000 x 517 workload under the library's own plan
+        # (fp32: A and B copied to 16-byte rows, then the four-wave 64x64 tile;
+        # fp16: element-wise and pair loads, K split 2 ways); a call's time
+        # includes its copy kernel or its reduction
         w = wl.RAGGED_F32 if args.only == "ragged_f32" else wl.RAGGED_F16
         fn = dg.gemm_f32 if args.only == "ragged_f32" else dg.gemm_f16
         res, _ = measure(fn, w, PEAK_F32 if args.only == "ragged_f32" else PEAK_F16, args.only,
