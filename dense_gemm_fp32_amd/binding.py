@@ -162,7 +162,8 @@ def gemm_set_tile_config(config):
     """0 = tile configuration by problem size (default); 1/2/3/4 = force the
     large/medium/small/tiny configuration (fp16 maps 4 to small); 5 = fp32
     medium with loads issued together; 6 = fp32 256x256 (fp16 large on
-    32x32x16 blocks); 7 = fp32 64x64 with four waves (fp16 small)."""
+    32x32x16 blocks); 7 = fp32 64x64 with four waves (fp16 small); 8 = fp32
+    128x64 with four waves (fp16 medium)."""
     return _lib.gemm_set_tile_config(int(config))
 
 

@@ -1116,6 +1116,7 @@ static F16Choice choose_f16(const Call &c) {
   if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
   if (c.tile_config == 3 || c.tile_config == 4 || c.tile_config == 7)
     return F16Choice{F16Cfg::kSmall, forced, 0.0};
+  if (c.tile_config == 8) return F16Choice{F16Cfg::kMid, forced, 0.0};
   const long long mid_tiles = tiles_of<F16Mid>(c);
   if (c.split_mode == 0 && staged_call16(c) && 2 * mid_tiles < 3LL * kCUs &&
       tiles_of<F16Small>(c) >= kCUs / 2) {

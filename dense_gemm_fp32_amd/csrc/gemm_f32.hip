@@ -882,6 +882,7 @@ typedef S32Tile<128, 128, 16, 2, 2, 3, 8, true> F32Mid;  // 4 waves,  48 KB LDS,
 typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issued together
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
 typedef S32Tile<64, 64, 32, 2, 2, 3, 8> F32Quad;      // 4 waves of 32x32, 48 KB LDS, 3 WG/CU
+typedef S32Tile<128, 64, 32, 2, 2, 3, 8> F32Half;     // 4 waves of 64x32, 72 KB LDS, 2 WG/CU
 typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
@@ -964,7 +965,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad };
+enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad, kHalf };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
@@ -1161,6 +1162,7 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
   if (c.tile_config == 7) return F32Choice{F32Cfg::kQuad, forced, 0.0, tail};
+  if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
       tiles_of<F32Mid>(c) < 3LL * kCUs)
     return choose_staged(c);
@@ -1175,11 +1177,19 @@ static F32Choice choose_f32(const Call &c) {
   // 79-84 -> 86, 1000^3 and 4096x256x1024 +1-3%; 1152^3 71 -> 68 is the one
   // loss.  Deeper K (1024x1024x4096) keeps the 128x128 tile in 8 chunks
   // (106 against 93), and 1792^3 (3.1 tiles per CU) the unsplit 128x128 tile.
+  // Past three of those per CU, grids of 1.5 to 2 128x64 tiles per CU (both
+  // resident at once) take that tile, four 64x32 waves, unsplit: measured
+  // against the 128x128 tile chosen before (beta 1 and 0), 1792^3 90-97 ->
+  // 99-100 TFLOP/s, 1920^3 110 -> 114-116, 2048^3 124-125 -> 130-131,
+  // 1800x1900x2000 95-97 -> 101-104, 1024x4096x1024 116-119 -> 120-124,
+  // 4096x1024x2048 +3-4%, 2048x2048x512 +5%, 2560x1280x1280 +2%.
   if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
-    const long long q = tiles_of<F32Quad>(c);
+    const long long q = tiles_of<F32Quad>(c), h = tiles_of<F32Half>(c);
     const long long mx = c.M > c.N ? c.M : c.N;
-    if (q >= kCUs && q <= 3LL * kCUs && (long long)c.K <= 2 * mx)
-      return F32Choice{F32Cfg::kQuad, 1, 0.0, 1};
+    if ((long long)c.K <= 2 * mx) {
+      if (q >= kCUs && q <= 3LL * kCUs) return F32Choice{F32Cfg::kQuad, 1, 0.0, 1};
+      if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
+    }
   }
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
   const double mid = score_of<F32Mid>(c, 0.91, 3, 1);
@@ -1372,6 +1382,7 @@ static Plan plan_f32_as_is(const Call &c) {
     case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
     case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits, ch.tail);
     case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots", ch.splits, ch.tail);
+    case F32Cfg::kHalf: return plan_cfg<F32Half>(c, "f32 mfma32x32x2 tile 128x64x32 4 waves 3 slots", ch.splits, ch.tail);
     default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits, ch.tail);
   }
 }
@@ -1385,6 +1396,7 @@ static hipError_t launch_f32_as_is(const Call &c) {
     case F32Cfg::kMidB: return launch_cfg<F32MidB>(c, ch.splits, ch.tail);
     case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits, ch.tail);
     case F32Cfg::kQuad: return launch_cfg<F32Quad>(c, ch.splits, ch.tail);
+    case F32Cfg::kHalf: return launch_cfg<F32Half>(c, ch.splits, ch.tail);
     default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }

@@ -266,7 +266,10 @@ def test_tile_table_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
-    assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2048)
+    assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2304)
+    # 1.5 to 2 128x64 tiles per CU (past three 64x64 ones): the four-wave 128x64 tile
+    for n in (1792, 1920, 2048):
+        assert "128x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
     # one to three 64x64 tiles per CU: that tile with four 32x32 waves, unsplit
     for n in (1024, 1280, 1536, 1664):
         assert "64x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
@@ -300,9 +303,11 @@ def test_tile_table_choice_and_override():
         assert "32x32x32" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
         dg.gemm_set_tile_config(7)
         assert "64x64x32 4 waves" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
+        dg.gemm_set_tile_config(8)
+        assert "128x64x32 4 waves" in name("f32", 4096) and "128x128x32" in name("f16", 4096)
     finally:
         dg.gemm_set_tile_config(prev)
-    assert dg.gemm_set_tile_config(9) == -1 and dg.gemm_set_tile_config(8) == -1
+    assert dg.gemm_set_tile_config(9) == -1 and dg.gemm_set_tile_config(-1) == -1
 
 
 def test_staged_calls_split_the_medium_tile():

@@ -73,13 +73,16 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n", [1152, 1408, 1664])
-def test_f32_sweep_four_wave_tile_full_oracle(n):
-    """Sweep sizes (beta = 1) whose plan is the 64x64 tile of four 32x32
-    waves, one to three tiles per CU, every element against the oracle."""
+@pytest.mark.parametrize("n,tile", [(1152, "64x64x32 4 waves"), (1408, "64x64x32 4 waves"),
+                                    (1664, "64x64x32 4 waves"), (1792, "128x64x32 4 waves"),
+                                    (1920, "128x64x32 4 waves")])
+def test_f32_sweep_four_wave_tile_full_oracle(n, tile):
+    """Sweep sizes (beta = 1) whose plan is a four-wave tile, unsplit: the
+    64x64 tile of 32x32 waves (one to three tiles per CU) or the 128x64 tile
+    of 64x32 waves (1.5 to 2 per CU), every element against the oracle."""
     w = wl.sweep(n)
     plan = _plan(w)
-    assert "64x64x32 4 waves" in plan and "split" not in plan, plan
+    assert tile in plan and "split" not in plan, plan
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
@@ -417,9 +420,9 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7],
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8],
                          ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256",
-                              "f32-64x64-four-waves"])
+                              "f32-64x64-four-waves", "f32-128x64-four-waves"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -823,7 +826,7 @@ def test_layouts_match_oracle(dtype, layout):
         _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7, 8])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_layouts_every_tile(dtype, layout, cfg):
