@@ -26,73 +26,88 @@ namespace dgemm {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr unsigned kPackMaxBlocks = 2048;
+constexpr unsigned kPackMaxBlocks = 8192;
 constexpr size_t kPackAlign = 256;     // workspace sub-buffers start on 256-byte boundaries
 // Largest workspace a call takes from the pool (the split-K cap in splitk.hip).
 constexpr long long kPoolCallCap = 1LL << 30;
 
-// One stored matrix to copy: rows x cols elements at src (row pitch ld_src
-// elements) into dst (row pitch ld_dst elements, a multiple of 16 bytes);
-// n = rows * ld_dst elements written.
+// One stored matrix to copy: `rows` rows of row_bytes bytes (cols elements)
+// at src, row pitch src_pitch bytes, into dst, whose rows are cpr 16-byte
+// chunks; n = rows * cpr chunks written.
 struct PackJob {
-  const void *src;
-  void *dst;
-  long long ld_src;
-  unsigned ld_dst;
-  int cols;
+  const char *src;
+  char *dst;
+  long long src_pitch;
+  long long row_bytes;
+  unsigned cpr;
   long long n;
 };
 
-// Consecutive threads on consecutive elements of a row, so that every wave
-// reads and writes one contiguous run of each matrix; elements past a row's
-// last column are written as zeros.  Each thread takes kPackIlp elements a
-// grid apart and issues all their loads before any store (a store could
-// otherwise alias the next load and hold it back a full memory latency).
-// Jobs j0 and j1 (A and B) share the launch: elements [0, j0.n) of the
-// combined range are j0's.  WIDE: a job holds 2^32 elements or more (64-bit
-// index arithmetic).
-constexpr int kPackIlp = 8;
-
-template <typename E, bool WIDE>
-__device__ __forceinline__ const E *pack_source(const PackJob &j, long long u) {
-  long long row;
-  int col;
-  if constexpr (WIDE) {
-    row = u / j.ld_dst;
-    col = (int)(u - row * j.ld_dst);
-  } else {
-    const unsigned uu = (unsigned)u;
-    row = uu / j.ld_dst;
-    col = (int)(uu - (unsigned)row * j.ld_dst);
-  }
-  return col < j.cols ? static_cast<const E *>(j.src) + row * j.ld_src + col : nullptr;
-}
-
-template <typename E, bool WIDE>
+// One 16-byte chunk of a destination row per thread.  The chunk's source
+// bytes start anywhere on an element boundary, so they are read as the one or
+// two aligned 16-byte granules that hold them and shifted into place: two
+// 16-byte loads instead of four (fp32) or eight (fp16) element loads, and one
+// 16-byte store.  The first granule holds the chunk's first byte; the second
+// is read only when the chunk needs bytes from it that lie inside the row.
+// A granule that holds any byte of the matrix lies in the same page as that
+// byte, so no read can touch a page the matrix does not; bytes read from
+// outside the row are never used.  Bytes past the row's last column are
+// written as zeros.  Consecutive threads take consecutive chunks, so every
+// wave reads and writes contiguous runs.  Jobs j0 and j1 (A and B) share the
+// launch: chunks [0, j0.n) of the combined range are j0's.  WIDE: a job holds
+// 2^32 chunks or more (64-bit index arithmetic).
+template <bool WIDE>
 __global__ __launch_bounds__(kPackThreads) void pack_rows(PackJob j0, PackJob j1) {
   const long long total = j0.n + j1.n;
-  const long long step = (long long)gridDim.x * kPackThreads;
-  for (long long t0 = (long long)blockIdx.x * kPackThreads + threadIdx.x; t0 < total;
-       t0 += step * kPackIlp) {
-    E v[kPackIlp];
-#pragma unroll
-    for (int i = 0; i < kPackIlp; ++i) {
-      const long long t = t0 + i * step;
-      v[i] = E(0);
-      if (t < total) {
-        const bool second = t >= j0.n;
-        const E *s = pack_source<E, WIDE>(second ? j1 : j0, second ? t - j0.n : t);
-        if (s != nullptr) v[i] = *s;
-      }
+  for (long long t = (long long)blockIdx.x * kPackThreads + threadIdx.x; t < total;
+       t += (long long)gridDim.x * kPackThreads) {
+    // the job's fields by value (a reference to one of the two arguments
+    // would put them in scratch memory)
+    const bool second = t >= j0.n;
+    const long long u = second ? t - j0.n : t;
+    const char *src = second ? j1.src : j0.src;
+    char *dst = second ? j1.dst : j0.dst;
+    const long long pitch = second ? j1.src_pitch : j0.src_pitch;
+    const long long row_bytes = second ? j1.row_bytes : j0.row_bytes;
+    const unsigned cpr = second ? j1.cpr : j0.cpr;
+    long long row, chunk;
+    if constexpr (WIDE) {
+      row = u / cpr;
+      chunk = u - row * cpr;
+    } else {
+      const unsigned uu = (unsigned)u;
+      row = uu / cpr;
+      chunk = uu - (unsigned)row * cpr;
     }
+    const long long off = chunk * 16;
+    const long long valid = row_bytes - off;        // bytes of the chunk inside the row, >= 1
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src + row * pitch + off);
+    const uintptr_t g = a & ~(uintptr_t)15;
+    const int s = (int)(a & 15);
+    typedef const __attribute__((address_space(1))) u32x4 GlobalVec;   // global, not flat, loads
+    const u32x4 lo = *reinterpret_cast<GlobalVec *>(g);
+    u32x4 hi = u32x4{0u, 0u, 0u, 0u};
+    if (s != 0 && (long long)(g + 16 - a) < valid) hi = *reinterpret_cast<GlobalVec *>(g + 16);
+    // The chunk is bytes s .. s+15 of the 32 bytes lo, hi: first shift by
+    // whole dwords (s / 4, two select stages on its bits, so that no
+    // per-lane index into registers is needed), then by s % 4 bytes.
+    const bool q1 = (s & 4) != 0, q2 = (s & 8) != 0;
+    const uint32_t d0 = lo[0], d1 = lo[1], d2 = lo[2], d3 = lo[3];
+    const uint32_t d4 = hi[0], d5 = hi[1], d6 = hi[2], d7 = hi[3];
+    // e[k] = d[k + (q1 ? 1 : 0)], then f[k] = e[k + (q2 ? 2 : 0)], k = 0..4
+    const uint32_t e0 = q1 ? d1 : d0, e1 = q1 ? d2 : d1, e2 = q1 ? d3 : d2, e3 = q1 ? d4 : d3;
+    const uint32_t e4 = q1 ? d5 : d4, e5 = q1 ? d6 : d5, e6 = q1 ? d7 : d6;
+    const uint32_t f[5] = {q2 ? e2 : e0, q2 ? e3 : e1, q2 ? e4 : e2, q2 ? e5 : e3, q2 ? e6 : e4};
+    const int r = s & 3;
+    u32x4 w;
 #pragma unroll
-    for (int i = 0; i < kPackIlp; ++i) {
-      const long long t = t0 + i * step;
-      if (t < total) {
-        const bool second = t >= j0.n;
-        static_cast<E *>(second ? j1.dst : j0.dst)[second ? t - j0.n : t] = v[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = r == 0 ? f[i] : __builtin_amdgcn_alignbyte(f[i + 1], f[i], (uint32_t)r);
+      if (4 * i >= valid) v = 0u;
+      else if (4 * i + 4 > valid) v &= 0xffffu;     // fp16: one half of this dword is in the row
+      w[i] = v;
     }
+    *reinterpret_cast<u32x4 *>(dst + u * 16) = w;
   }
 }
 
@@ -224,7 +239,9 @@ hipError_t run_packed(const Call &c, int eb, Plan (*plan)(const Call &),
   if (pk.a) {
     int rows, cols;
     stored_a(c, &rows, &cols);
-    ja = PackJob{c.A, base, c.lda, (unsigned)pk.lda, cols, (long long)rows * pk.lda};
+    const unsigned cpr = (unsigned)((long long)pk.lda * eb / 16);
+    ja = PackJob{static_cast<const char *>(c.A), base, (long long)c.lda * eb, (long long)cols * eb,
+                 cpr, (long long)rows * cpr};
     in.A = base;
     in.lda = pk.lda;
   }
@@ -232,7 +249,9 @@ hipError_t run_packed(const Call &c, int eb, Plan (*plan)(const Call &),
     int rows, cols;
     stored_b(c, &rows, &cols);
     char *dst = base + pk.a_bytes;
-    jb = PackJob{c.B, dst, c.ldb, (unsigned)pk.ldb, cols, (long long)rows * pk.ldb};
+    const unsigned cpr = (unsigned)((long long)pk.ldb * eb / 16);
+    jb = PackJob{static_cast<const char *>(c.B), dst, (long long)c.ldb * eb, (long long)cols * eb,
+                 cpr, (long long)rows * cpr};
     in.B = dst;
     in.ldb = pk.ldb;
   }
@@ -240,18 +259,14 @@ hipError_t run_packed(const Call &c, int eb, Plan (*plan)(const Call &),
   in.ws_fixed = base + pk.a_bytes + pk.b_bytes;
   in.ws_fixed_bytes = pk.bytes - pk.a_bytes - pk.b_bytes;
   const long long total = ja.n + jb.n;
-  long long blocks = (total + kPackThreads * kPackIlp - 1) / (kPackThreads * kPackIlp);
+  long long blocks = (total + kPackThreads - 1) / kPackThreads;
   if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
   if (blocks < 1) blocks = 1;
-  const bool wide = ja.n >= (1LL << 32) || jb.n >= (1LL << 32);
   const dim3 g((unsigned)blocks), b(kPackThreads);
-  if (eb == 4) {
-    if (wide) hipLaunchKernelGGL((pack_rows<uint32_t, true>), g, b, 0, c.stream, ja, jb);
-    else hipLaunchKernelGGL((pack_rows<uint32_t, false>), g, b, 0, c.stream, ja, jb);
-  } else {
-    if (wide) hipLaunchKernelGGL((pack_rows<uint16_t, true>), g, b, 0, c.stream, ja, jb);
-    else hipLaunchKernelGGL((pack_rows<uint16_t, false>), g, b, 0, c.stream, ja, jb);
-  }
+  if (ja.n >= (1LL << 32) || jb.n >= (1LL << 32))
+    hipLaunchKernelGGL(pack_rows<true>, g, b, 0, c.stream, ja, jb);
+  else
+    hipLaunchKernelGGL(pack_rows<false>, g, b, 0, c.stream, ja, jb);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = launch(in);
   const hipError_t f = workspace_free(c, ws);
