@@ -1142,11 +1142,13 @@ static F16Choice choose_f16(const Call &c) {
   }
   // The large tile's two block shapes.  16x16x32 blocks let the part hold a
   // higher clock where it is power-bound, but do a little less work per clock
-  // (A re-read per block row): they win when the workgroups fill every CU and
-  // the clock drops (interleaved, sustained: 4096^3 +3.5-6%, 5120^3 +2.7%,
-  // 8192^3 +2.7%) and lose where part of the chip idles and the clock stays
-  // near its maximum (3072^3, 144 tiles at 2.38 GHz: -7.5%).
-  if (best.cfg == F16Cfg::kBig && tiles_of<F16Big>(c) * best.splits < kCUs)
+  // (A re-read per block row): they win when the workgroups fill at least
+  // three quarters of the CUs and the clock drops (interleaved, sustained:
+  // 4096^3 +3.5-6%, 5120^3 +2.7%, 8192^3 +2.7%; 196 tiles, 3456^3 and
+  // 3584^3: +4%, 225 tiles, 3712^3 and 3840^3: +5%, 3584x3584x8192 +5%) and
+  // lose where more of the chip idles and the clock stays near its maximum
+  // (144 tiles, 3072^3: -2 to -7.5%; 128 and 160 tiles: -1 to -4%; 169: even).
+  if (best.cfg == F16Cfg::kBig && 4 * tiles_of<F16Big>(c) * best.splits < 3LL * kCUs)
     best.cfg = F16Cfg::kBig32;
   return best;
 }

@@ -86,6 +86,23 @@ def test_f32_sweep_four_wave_tile_full_oracle(n, tile):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
+@pytest.mark.parametrize("n,blocks", [(3200, "mfma32x32x16"), (3584, "mfma16x16x32")])
+def test_f16_large_tile_block_shape_by_size_sampled(n, blocks):
+    """fp16 sizes whose 256x256 tiles fill less than every CU: 32x32x16
+    blocks below three quarters of the CUs (3200^3, 169 tiles), 16x16x32 from
+    there (3584^3, 196 tiles); sampled rows against the oracle, with rows of
+    the last tile row."""
+    w = wl.Workload("f16_%d_beta0.5" % n, "f16", n, n, n, n, n, n, 1.0, 0.5, "uniform", "uniform",
+                    (3, 4, 5))
+    plan = _plan(w)
+    assert "256x256x64" in plan and blocks in plan, plan
+    A, B, C = wl.make(w)
+    rc, out = run(w.dtype, w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                  "%s (%s)" % (w.name, plan))
+    assert rc == 0
+    check_sampled(w.dtype, w, A, B, C, out, nrows=16, seed=n, extra_rows=[n - 1, n - 200])
+
+
 @pytest.mark.parametrize("n", [2304, 2944, 3584])
 def test_f32_sweep_mid_sizes_sampled(n):
     """Sweep sizes whose chosen plans split K: 2304^3 (every tile split),
