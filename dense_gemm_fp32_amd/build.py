@@ -103,15 +103,83 @@ def check_no_spills(asm_text, src):
         raise RuntimeError("GEMM kernels in %s spill to scratch memory:\n%s" % (src, "\n".join(bad)))
 
 
+# Register budget per lane of each GEMM tile: a SIMD's 512 registers per lane
+# (architected and accumulation) are shared by the waves it holds, so a tile
+# meant to put W waves on each SIMD (its workgroups per CU, as its LDS allows,
+# times its waves, over 4 SIMDs) may use at most 512 / W of them, in granules
+# of 8.  One more register and fewer of its workgroups fit on a CU.
+# (symbol fragment of the tile's template arguments, workgroups per CU, waves)
+TILE_OCCUPANCY = (
+    ("S32TileILi256ELi256ELi32E", 1, 8),
+    ("S32TileILi256ELi128ELi32E", 1, 8),
+    # the 128x128 tile with spread loads runs only on grids of at most one
+    # workgroup per CU; with the loads issued together, three share a CU
+    ("S32TileILi128ELi128ELi16ELi2ELi2ELi3ELi8ELb1E", 1, 4),
+    ("S32TileILi128ELi128ELi16ELi2ELi2ELi3ELi8ELb0E", 3, 4),
+    ("S32TileILi128ELi64ELi32E", 2, 4),
+    ("S32TileILi64ELi64ELi32ELi2ELi2E", 3, 4),
+    ("S32TileILi64ELi64ELi32ELi1ELi1E", 3, 1),
+    ("S32TileILi32ELi32ELi32E", 6, 1),
+    ("H16TileILi256ELi256ELi64E", 1, 8),
+    ("H16TileILi128ELi128ELi32E", 2, 4),
+    ("H16TileILi64ELi128ELi32E", 3, 2),
+)
+
+
+def register_budget(wgs_per_cu, waves):
+    per_simd = max(1, -(-wgs_per_cu * waves // 4))
+    return 512 // per_simd // 8 * 8
+
+
+def register_counts(asm_text):
+    """{kernel symbol: registers per lane (.amdhsa_next_free_vgpr)}."""
+    counts = {}
+    current = None
+    for line in asm_text.splitlines():
+        t = line.strip()
+        m = re.match(r"^\.amdhsa_kernel\s+(\S+)", t)
+        if m:
+            current = m.group(1)
+            continue
+        m = re.match(r"^\.amdhsa_next_free_vgpr\s+(\d+)", t)
+        if m and current is not None:
+            counts[current] = int(m.group(1))
+        if t.startswith(".end_amdhsa_kernel"):
+            current = None
+    return counts
+
+
+def check_register_budget(asm_text, src):
+    """Raise RuntimeError if a GEMM kernel in `src`'s assembly uses more
+    registers than its tile's occupancy allows (TILE_OCCUPANCY), or if a GEMM
+    kernel's tile has no entry there."""
+    bad = []
+    for kernel, regs in register_counts(asm_text).items():
+        if not any(n in kernel for n in NO_SPILL_KERNELS) or "sgemm_valu" in kernel:
+            continue
+        entry = [e for e in TILE_OCCUPANCY if e[0] in kernel]
+        if not entry:
+            bad.append("%s: no occupancy entry for its tile" % kernel)
+            continue
+        budget = register_budget(entry[0][1], entry[0][2])
+        if regs > budget:
+            bad.append("%s: %d registers, budget %d (%d workgroups of %d waves per CU)"
+                       % (kernel, regs, budget, entry[0][1], entry[0][2]))
+    if bad:
+        raise RuntimeError("GEMM kernels in %s exceed their register budget:\n%s"
+                           % (src, "\n".join(bad)))
+
+
 def check_m0_only_in_asm(src):
     """Compile `src` to gfx950 assembly and verify that every instruction
     mentioning m0 lies inside an inline-asm block, and that no GEMM kernel
-    spills.  Raises RuntimeError."""
+    spills or exceeds its register budget.  Raises RuntimeError."""
     cmd = [HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc -S failed on %s:\n%s" % (src, r.stderr))
     check_no_spills(r.stdout, src)
+    check_register_budget(r.stdout, src)
     inside = False
     bad = []
     for n, line in enumerate(r.stdout.splitlines(), 1):

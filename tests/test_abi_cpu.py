@@ -262,6 +262,27 @@ def test_spill_check_reads_kernel_descriptors():
         b.check_no_spills("", "empty")
 
 
+def test_register_budget_check_reads_kernel_descriptors():
+    """The build's register check compares each GEMM kernel's registers per
+    lane with the budget of its tile's occupancy (512 registers per SIMD lane
+    over the waves a SIMD is meant to hold) and refuses one over budget or
+    with no occupancy entry (synthetic descriptors; the real sources pass in
+    test_only_inline_asm_touches_m0, which runs the same check)."""
+    from dense_gemm_fp32_amd import build as b
+    assert b.register_budget(3, 4) == 168 and b.register_budget(1, 8) == 256
+    assert b.register_budget(2, 4) == 256 and b.register_budget(1, 4) == 512
+    mid = "_ZN5dgemm10sgemm_mfmaINS_7S32TileILi128ELi128ELi16ELi2ELi2ELi3ELi8ELb0EEELb0ELb0ELb1EEEvNS_10GemmParamsE"
+    text = "\n".join([".amdhsa_kernel " + mid, "  .amdhsa_next_free_vgpr 168", ".end_amdhsa_kernel",
+                      ".amdhsa_kernel _ZN5dgemm14scale_f32_kernelEv", "  .amdhsa_next_free_vgpr 400",
+                      ".end_amdhsa_kernel"])
+    assert b.register_counts(text) == {mid: 168, "_ZN5dgemm14scale_f32_kernelEv": 400}
+    b.check_register_budget(text, "synthetic")          # at the budget; other kernels ignored
+    with pytest.raises(RuntimeError, match="budget 168"):
+        b.check_register_budget(text.replace("vgpr 168", "vgpr 176"), "synthetic")
+    with pytest.raises(RuntimeError, match="no occupancy entry"):
+        b.check_register_budget(text.replace("ILi128ELi128ELi16E", "ILi96ELi96ELi16E"), "synthetic")
+
+
 def test_tile_table_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def name(dt, n):
