@@ -491,23 +491,27 @@ from hypothesis import HealthCheck, given, settings, strategies as st
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
        beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6, 7, 8]),
+       pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
-def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, seed):
+def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, pack, seed):
     """Random small shapes (every tail residue of every tile size is
     reachable), random row padding (aligned and unaligned leading
-    dimensions), alpha/beta and forced tile configurations."""
+    dimensions), alpha/beta, forced tile configurations, and operand copies
+    by size (none at these sizes) or forced."""
     t = _t(dtype)
     rng = np.random.default_rng(seed)
     lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
     A = wl.pad(rng.uniform(-1, 1, (M, K)).astype(t), lda, np.nan)
     B = wl.pad(rng.uniform(-1, 1, (K, N)).astype(t), ldb, np.nan)
     C = wl.pad(rng.uniform(-1, 1, (M, N)).astype(_tc(dtype)), ldc, wl.C_PAD_SENTINEL)
-    with tile_config(cfg):
-        rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, "hyp cfg%d" % cfg)
+    with tile_config(cfg), pack_mode(pack):
+        rc, out = run(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      "hyp cfg%d pack%d" % (cfg, pack))
     assert rc == 0
     check(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out,
-          "random %s M=%d N=%d K=%d ld=%d,%d,%d cfg=%d" % (dtype, M, N, K, lda, ldb, ldc, cfg))
+          "random %s M=%d N=%d K=%d ld=%d,%d,%d cfg=%d pack=%d" % (dtype, M, N, K, lda, ldb, ldc,
+                                                                 cfg, pack))
 
 
 # ---------------------------------------------------------------- split K
@@ -1054,13 +1058,15 @@ def test_concurrent_streams_and_threads_share_the_workspace_pool():
        M=st.integers(1, 300), N=st.integers(1, 300), K=st.integers(1, 300),
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        beta=st.sampled_from([0.0, 1.0, -1.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 6]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8]),
        split=st.sampled_from([0, 1, 3]),
+       pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
-def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, split, seed):
+def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, split, pack, seed):
     """Random small shapes with transposed operands: random row padding
-    (aligned and unaligned), beta, forced tile configurations and splits."""
-    with tile_config(cfg), split_mode(split):
+    (aligned and unaligned), beta, forced tile configurations and splits,
+    and operand copies by size or forced."""
+    with tile_config(cfg), split_mode(split), pack_mode(pack):
         _layout_run_check(dtype, layout, M, N, K, pads, seed % 100000, beta=beta,
                           label="hyp cfg%d split%d" % (cfg, split))
 
