@@ -1074,26 +1074,32 @@ def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, sp
 def test_calls_replay_from_a_captured_graph():
     """Library calls captured into a HIP graph (torch.cuda.CUDAGraph on a
     side stream) -- unsplit fp32 and fp16, a whole split K, a last-round
-    split, whose workspace becomes an allocation node of the graph -- replay
-    the eager results bit for bit, several times, with eager GEMMs and
+    split, and a call whose unaligned operands are copied to 16-byte rows,
+    whose workspace becomes an allocation node of the graph -- replay the
+    eager results bit for bit, several times, with eager GEMMs and
     synchronisations between the replays."""
     import torch
     import dense_gemm_fp32_amd as dg
     from gemm_harness import note
-    note("graph capture: unsplit f32/f16, split K 4, last-round split 3")
+    note("graph capture: unsplit f32/f16, split K 4, last-round split 3, operand copies")
     dev = torch.device("cuda:0")
     g = torch.Generator().manual_seed(9)
-    cases = [("f32", 1000, 700, 3000, 1, 1), ("f16", 600, 520, 1000, 1, 1),
-             ("f32", 1000, 700, 3000, 4, 1), ("f32", 4200, 2000, 256, 1, 3)]
-    for dtype, M, N, K, split, tail in cases:
+    # (dtype, M, N, K, split mode, tail mode, row pad of A and B)
+    cases = [("f32", 1000, 700, 3000, 1, 1, 0), ("f16", 600, 520, 1000, 1, 1, 0),
+             ("f32", 1000, 700, 3000, 4, 1, 0), ("f32", 4200, 2000, 256, 1, 3, 0),
+             ("f32", 2048, 2048, 2048, 0, 0, 1)]
+    for dtype, M, N, K, split, tail, pad in cases:
         t = torch.float32 if dtype == "f32" else torch.float16
         fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_f16
-        A = (torch.rand(M, K, generator=g) * 2 - 1).to(t).to(dev)
-        B = (torch.rand(K, N, generator=g) * 2 - 1).to(t).to(dev)
+        lda, ldb = K + pad, N + pad
+        A = (torch.rand(M, lda, generator=g) * 2 - 1).to(t).to(dev)
+        B = (torch.rand(K, ldb, generator=g) * 2 - 1).to(t).to(dev)
         C0 = (torch.rand(M, N, generator=g) * 2 - 1).to(t).to(dev)
+        plan = dg.gemm_describe(dtype, M, N, K, 1.25, A, lda, B, ldb, 0.5, C0, N)[1]
+        assert ("copies A B" in plan) == (pad > 0), plan
         with split_mode(split), tail_split(tail):
             ref = C0.clone()
-            assert fn(M, N, K, 1.25, A, K, B, N, 0.5, ref, N, None) == 0
+            assert fn(M, N, K, 1.25, A, lda, B, ldb, 0.5, ref, N, None) == 0
             torch.cuda.synchronize()
             C = C0.clone()
             s = torch.cuda.Stream(device=dev)
@@ -1101,18 +1107,18 @@ def test_calls_replay_from_a_captured_graph():
             s.wait_stream(torch.cuda.current_stream(dev))
             with torch.cuda.stream(s):
                 graph.capture_begin()
-                rc = fn(M, N, K, 1.25, A, K, B, N, 0.5, C, N, s)
+                rc = fn(M, N, K, 1.25, A, lda, B, ldb, 0.5, C, N, s)
                 graph.capture_end()
             torch.cuda.synchronize()
             assert rc == 0
             for rep in range(3):
                 C.copy_(C0)
                 other = torch.zeros(M, N, dtype=t, device=dev)
-                assert fn(M, N, K, 1.0, A, K, B, N, 0.0, other, N, None) == 0   # eager work between
+                assert fn(M, N, K, 1.0, A, lda, B, ldb, 0.0, other, N, None) == 0   # eager work between
                 torch.cuda.synchronize()
                 graph.replay()
                 torch.cuda.synchronize()
-                assert torch.equal(C, ref), (dtype, M, N, K, split, tail, rep)
+                assert torch.equal(C, ref), (dtype, M, N, K, split, tail, pad, rep)
             del graph
 
 
