@@ -80,8 +80,9 @@
  *     enqueues work on it and returns; it does not synchronise.  The caller
  *     keeps A, B and C alive until that work has completed.
  *   - Calls may be captured into a HIP graph on a capturing stream (no
- *     memset is enqueued; a split call's workspace becomes the graph's
- *     allocation node); replays repeat the captured arguments and choice.
+ *     memset is enqueued; the workspace of a split or operand-copying call
+ *     becomes the graph's allocation node); replays repeat the captured
+ *     arguments and choice.
  *   - The library keeps no per-call state, so calls are thread-safe and
  *     reentrant; the only process-wide state is the workspace pools and the
  *     diagnostic switches at the end of this header (default off).
