@@ -13,7 +13,7 @@ _BINDING_NAMES = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_
                   "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor",
                   "gemm_status_string", "gemm_describe", "gemm_set_load_mode",
                   "gemm_set_tile_config", "gemm_set_split", "gemm_set_tail_split",
-                  "gemm_set_pack", "gemm_set_workspace_limit", "gemm_probe_mfma", "gemm", "GemmError",
+                  "gemm_set_pack", "gemm_set_stream_k", "gemm_set_workspace_limit", "gemm_probe_mfma", "gemm", "GemmError",
                   "GEMM_ERR_SCRATCH_LIMIT", "LIB_PATH", "EXPORTS", "LAYOUT_NAMES") + _LAYOUT_NAMES
 
 __all__ = list(_BINDING_NAMES)

@@ -51,6 +51,8 @@ _lib.gemm_set_tail_split.argtypes = [_I]
 _lib.gemm_set_tail_split.restype = _I
 _lib.gemm_set_pack.argtypes = [_I]
 _lib.gemm_set_pack.restype = _I
+_lib.gemm_set_stream_k.argtypes = [_I]
+_lib.gemm_set_stream_k.restype = _I
 _lib.gemm_set_workspace_limit.argtypes = [ctypes.c_longlong]
 _lib.gemm_set_workspace_limit.restype = ctypes.c_longlong
 _lib.gemm_probe_mfma.argtypes = [_I, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
@@ -60,7 +62,8 @@ _lib.gemm_probe_mfma.restype = _I
 EXPORTS = ("gemm_f32", "gemm_f16", "gemm_f16f32", "gemm_f32_valu", "gemm_f32_noalloc",
            "gemm_f32_colmajor", "gemm_f16_colmajor", "gemm_f16f32_colmajor", "gemm_status_string",
            "gemm_describe", "gemm_set_load_mode", "gemm_set_tile_config", "gemm_set_split",
-           "gemm_set_tail_split", "gemm_set_pack", "gemm_set_workspace_limit", "gemm_probe_mfma") + LAYOUT_NAMES
+           "gemm_set_tail_split", "gemm_set_pack", "gemm_set_stream_k", "gemm_set_workspace_limit",
+           "gemm_probe_mfma") + LAYOUT_NAMES
 GEMM_ERR_SCRATCH_LIMIT = -200
 
 
@@ -207,6 +210,14 @@ def gemm_set_pack(mode):
     1 = never; 2 = whenever their rows do not allow 16-byte loads (fp16
     too).  Returns the previous mode, or -1."""
     return _lib.gemm_set_pack(int(mode))
+
+
+def gemm_set_stream_k(mode):
+    """fp32 calls on the 64x64 tile: 0 = Stream-K by size (default),
+    1 = never, 2..4 = every tile's K steps over 1..3 workgroups per CU,
+    5..6 = whole rounds first, the rest over 1..2 more workgroups per CU.
+    Returns the previous mode, or -1."""
+    return _lib.gemm_set_stream_k(int(mode))
 
 
 def gemm_set_workspace_limit(nbytes):

@@ -71,7 +71,7 @@ def check_spills_only(src):
 # Kernels whose registers hold the accumulator tiles: a spill to scratch
 # memory would put every MFMA's operands behind memory traffic, so the build
 # refuses one.
-NO_SPILL_KERNELS = ("hgemm_mfma", "sgemm_mfma", "sgemm_valu")
+NO_SPILL_KERNELS = ("hgemm_mfma", "sgemm_mfma", "sgemm_streamk", "sgemm_valu")
 
 
 def scratch_sizes(asm_text):

@@ -21,6 +21,7 @@ std::atomic<int> g_split_mode{0};
 std::atomic<int> g_tail_mode{0};
 std::atomic<long long> g_ws_limit{-1};
 std::atomic<int> g_pack_mode{0};
+std::atomic<int> g_streamk_mode{0};
 
 // Shared argument checks.  ta / tb: A is stored transposed (K x M, so its
 // rows hold M elements) / B is (N x K, rows of K); otherwise A is M x K and B
@@ -107,6 +108,7 @@ dgemm::Call make_call(int M, int N, int K, float alpha, const void *A, int lda, 
   c.ws_fixed = nullptr;
   c.ws_fixed_bytes = 0;
   c.pack_mode = g_pack_mode.load(std::memory_order_relaxed);
+  c.streamk_mode = g_streamk_mode.load(std::memory_order_relaxed);
   c.stream = static_cast<hipStream_t>(stream);
   return c;
 }
@@ -334,7 +336,10 @@ int gemm_describe(int dtype, int M, int N, int K, float alpha, const void *A, in
                                   nullptr, dtype == 2);
         dgemm::Plan p = dtype ? dgemm::plan_f16(c) : dgemm::plan_f32(c);
         char split[48] = "";
-        if (p.splits > 1) snprintf(split, sizeof split, " split-K %d", p.splits);
+        if (p.streamk && p.sk_whole > 0)
+          snprintf(split, sizeof split, " stream-K after %lld whole tiles", p.sk_whole);
+        else if (p.streamk) snprintf(split, sizeof split, " stream-K");
+        else if (p.splits > 1) snprintf(split, sizeof split, " split-K %d", p.splits);
         else if (p.tail > 1) snprintf(split, sizeof split, " last round split-K %d", p.tail);
         char ws[48] = "";
         if (p.ws_bytes > 0) snprintf(ws, sizeof ws, " workspace %zu bytes", p.ws_bytes);
@@ -393,6 +398,11 @@ int gemm_set_tile_config(int config) {
 int gemm_set_pack(int mode) {
   if (mode < 0 || mode > 2) return -1;
   return g_pack_mode.exchange(mode);
+}
+
+int gemm_set_stream_k(int mode) {
+  if (mode < 0 || mode > 6) return -1;
+  return g_streamk_mode.exchange(mode);
 }
 
 long long gemm_set_workspace_limit(long long bytes) {

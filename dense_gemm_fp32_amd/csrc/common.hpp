@@ -53,6 +53,17 @@ struct GemmParams {
   int c_tiles;
 };
 
+// A Stream-K launch: the first `dp` workgroups each compute one of tiles
+// 0 .. dp-1 whole; the K steps of the other tiles (dp .. tiles-1, `steps`
+// each) are dealt out in runs of `iters` steps to the remaining workgroups.
+// W holds two BM x BN fp32 blocks per such workgroup for the parts of tiles
+// it covers.
+struct StreamKRun {
+  int tiles, steps, dp;
+  long long iters;
+  float *W;
+};
+
 // Restrict the kernel arguments to split `s` of a split-K launch: K range
 // [s*k_chunk, min(K, (s+1)*k_chunk)) and that split's output slab.  TA / TB:
 // A is stored K x M / B is stored N x K (k runs along the rows).
@@ -100,14 +111,20 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 // the same way over that part.
 // `tiles`: tiles per split in this launch (they start at position tile_base
 // of the grouped order); `local` receives the tile's index among them.
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
-                                              int group_m, int tiles, int tile_base, int &tm,
-                                              int &tn, int &split, int &local) {
+// Position of workgroup `bid` in an order where every XCD owns one
+// contiguous range (step 1 below).
+__device__ __forceinline__ int xcd_order(int bid, int nblocks) {
   const int xcd = bid % kXcds;
   const int lid = bid / kXcds;
   const int q = nblocks / kXcds;
   const int r = nblocks % kXcds;
-  int b = xcd * q + (xcd < r ? xcd : r) + lid;
+  return xcd * q + (xcd < r ? xcd : r) + lid;
+}
+
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int group_m, int tiles, int tile_base, int &tm,
+                                              int &tn, int &split, int &local) {
+  int b = xcd_order(bid, nblocks);
   split = b / tiles;
   local = b - split * tiles;
   tile_coords(tile_base + local, tiles_m, tiles_n, group_m, tm, tn);

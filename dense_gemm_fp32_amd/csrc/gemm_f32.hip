@@ -817,6 +817,35 @@ __device__ __forceinline__ void epilogue32(const GemmParams &p, int r0, int c0,
   }
 }
 
+// The product of one C tile (origin m0, n0) over p's K range (p.A and p.B
+// point at its first k) into acc: direct loads where the tile and its
+// operands allow them, else the register-staged path.  Returns with every
+// load complete.
+template <class T, bool TA, bool TB>
+__device__ __forceinline__ void tile_product(const GemmParams &p, int m0, int n0, char *lds,
+                                             int wm0, int wn0, f32x16 (&acc)[T::FM][T::FN]) {
+  typedef FLayout<T, TA, TB> L;
+#pragma unroll
+  for (int bi = 0; bi < T::FM; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < T::FN; ++bj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+
+  const bool m_edge = m0 + T::BM > p.M;
+  const bool n_edge = n0 + T::BN > p.N;
+  const int va = vec_width_a(p.vec_ab), vb = vec_width_b(p.vec_ab);
+  const bool direct = va == 2 && vb == 2 && direct_ok32<typename L::RA, T::BK>(m_edge, p.M, p.lda) &&
+                      direct_ok32<typename L::RB, T::BK>(n_edge, p.N, p.ldb);
+  if (direct) {
+    if constexpr (T::SPREAD) mainloop_spread32<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+    else mainloop_direct32<T, L>(p, m0, n0, lds, lds_address(lds), wm0, wn0, acc);
+  } else {
+    mainloop_staged32<T, L>(p, m0, n0, lds, wm0, wn0, va, vb, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+}
+
 // TA / TB: A is stored transposed (K x M, lda >= M) / B is (N x K, ldb >= K).
 template <class T, bool TA, bool TB, bool VC>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
@@ -870,6 +899,81 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
   else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
 }
 
+// Stream-K (the SGEMM summary's results section names it as the next step
+// beyond fixed tiles), optionally behind whole tiles.  Workgroups with
+// blockIdx.x < sk.dp each compute one of tiles 0 .. dp-1 whole, in the
+// XCD-aware order of sgemm_mfma.  The K steps of the remaining tiles, tile
+// after tile in the grouped order, are dealt out in equal runs of sk.iters to
+// the other workgroups, so that every CU ends up with the same work whatever
+// the tile count; dp is a whole number of rounds of one tile per CU, and the
+// hardware hands out workgroups in blockIdx order, so each CU holds the same
+// mix of whole-tile and Stream-K workgroups.  A run crosses tile boundaries;
+// a tile it covers whole is written to C as usual, and a part of a tile (its
+// first or last segment) is written as raw fp32 sums to the workgroup's
+// workspace slot: 2g for its first segment, 2g + 1 for its last, g the
+// workgroup's position among the Stream-K workgroups in XCD-remapped order.
+// The fix-up pass (launch_streamk_fixup) then sums each shared tile's slots
+// in workgroup order -- ascending K -- and applies alpha and beta, so results
+// do not depend on which workgroup finishes first.
+template <class T, bool TA, bool TB, bool VC>
+__global__ __launch_bounds__(T::NT) void sgemm_streamk(GemmParams p, StreamKRun sk) {
+  __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  lds_poison(lds, T::LDS_BYTES);
+  const int wave = wave_id();
+  const int wm0 = (wave / T::WAVES_N) * T::WTM;
+  const int wn0 = (wave % T::WAVES_N) * T::WTN;
+  const int bid = blockIdx.x;
+  if (bid < sk.dp) {
+    int tm, tn;
+    tile_coords(xcd_order(bid, sk.dp), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    f32x16 acc[T::FM][T::FN];
+    tile_product<T, TA, TB>(p, m0, n0, lds, wm0, wn0, acc);
+    const bool edge = n0 + T::BN > p.N || m0 + T::BM > p.M;
+    if (edge) epilogue32<T, VC, true>(p, m0 + wm0, n0 + wn0, acc);
+    else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
+    return;
+  }
+  const int g = xcd_order(bid - sk.dp, (int)gridDim.x - sk.dp);
+  const long long it_all = (long long)(sk.tiles - sk.dp) * sk.steps;
+  long long it = (long long)g * sk.iters;
+  const long long it1 = it + sk.iters < it_all ? it + sk.iters : it_all;
+  bool first = true;
+  while (it < it1) {
+    const int local = (int)(it / sk.steps);
+    const int kb = (int)(it - (long long)local * sk.steps);
+    const long long room = it1 - it;
+    const int ke = room < (long long)(sk.steps - kb) ? kb + (int)room : sk.steps;
+    int tm, tn;
+    tile_coords(sk.dp + local, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    // This segment's K range: steps kb .. ke-1 of T::BK (the last may be short).
+    const int k_lo = kb * T::BK;
+    const int k_hi = (long long)ke * T::BK < (long long)p.K ? ke * T::BK : p.K;
+    GemmParams q = p;
+    q.K = k_hi - k_lo;
+    q.A = static_cast<const float *>(p.A) + (TA ? (size_t)k_lo * (size_t)p.lda : (size_t)k_lo);
+    q.B = static_cast<const float *>(p.B) + (TB ? (size_t)k_lo : (size_t)k_lo * (size_t)p.ldb);
+    if (!first) __syncthreads();   // every wave is done with the previous segment's LDS
+    f32x16 acc[T::FM][T::FN];
+    tile_product<T, TA, TB>(q, m0, n0, lds, wm0, wn0, acc);
+    if (kb == 0 && ke == sk.steps) {
+      const bool edge = n0 + T::BN > p.N || m0 + T::BM > p.M;
+      if (edge) epilogue32<T, VC, true>(p, m0 + wm0, n0 + wn0, acc);
+      else epilogue32<T, VC, false>(p, m0 + wm0, n0 + wn0, acc);
+    } else {
+      GemmParams w = p;
+      w.C = sk.W + (size_t)(2 * g + (first ? 0 : 1)) * (size_t)(T::BM * T::BN);
+      w.ldc = T::BN;
+      w.alpha = 1.0f;
+      w.beta = 0.0f;
+      epilogue32<T, true, false>(w, wm0, wn0, acc);
+    }
+    first = false;
+    it += ke - kb;
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 // Tile configurations (BM, BN, BK, waves along M, waves along N, LDS slots,
@@ -914,8 +1018,8 @@ static Plan make_plan(const Call &c, const char *name) {
   return pl;
 }
 
-template <class T, bool TA, bool TB, bool VC>
-static hipError_t launch_variant(const Call &c, const Plan &pl) {
+template <class T>
+static GemmParams make_params(const Call &c, const Plan &pl) {
   GemmParams p;
   p.A = c.A;
   p.B = c.B;
@@ -938,9 +1042,42 @@ static hipError_t launch_variant(const Call &c, const Plan &pl) {
   p.tile_base = c.tile_base;
   p.tile_count = c.tile_count;
   p.c_tiles = c.c_tiles ? 1 : 0;
+  return p;
+}
+
+template <class T, bool TA, bool TB, bool VC>
+static hipError_t launch_variant(const Call &c, const Plan &pl) {
+  const GemmParams p = make_params<T>(c, pl);
   hipLaunchKernelGGL((sgemm_mfma<T, TA, TB, VC>), dim3((unsigned)(pl.blocks * c.splits)),
                      dim3(T::NT), 0, c.stream, p);
   return hipGetLastError();
+}
+
+// A Stream-K launch of configuration T over `blocks` workgroups (see
+// sgemm_streamk), followed by nothing: the caller runs the fix-up.
+template <class T, bool TA, bool TB, bool VC>
+static hipError_t launch_streamk_variant(const Call &c, const Plan &pl, const StreamKRun &sk,
+                                         long long blocks) {
+  const GemmParams p = make_params<T>(c, pl);
+  hipLaunchKernelGGL((sgemm_streamk<T, TA, TB, VC>), dim3((unsigned)blocks), dim3(T::NT), 0,
+                     c.stream, p, sk);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t dispatch_streamk(const Call &c, const StreamKRun &sk, long long blocks) {
+  const Plan pl = make_plan<T>(c, "");
+  const int key = (c.ta ? 4 : 0) | (c.tb ? 2 : 0) | (pl.vec_c > 1 ? 1 : 0);
+  switch (key) {
+    case 0: return launch_streamk_variant<T, false, false, false>(c, pl, sk, blocks);
+    case 1: return launch_streamk_variant<T, false, false, true>(c, pl, sk, blocks);
+    case 2: return launch_streamk_variant<T, false, true, false>(c, pl, sk, blocks);
+    case 3: return launch_streamk_variant<T, false, true, true>(c, pl, sk, blocks);
+    case 4: return launch_streamk_variant<T, true, false, false>(c, pl, sk, blocks);
+    case 5: return launch_streamk_variant<T, true, false, true>(c, pl, sk, blocks);
+    case 6: return launch_streamk_variant<T, true, true, false>(c, pl, sk, blocks);
+    default: return launch_streamk_variant<T, true, true, true>(c, pl, sk, blocks);
+  }
 }
 
 template <class T>
@@ -1016,6 +1153,7 @@ struct F32Choice {
   int splits;   // wanted K chunks (1 = none); clamp_splits has the last word
   double time;  // estimated seconds
   int tail;     // K chunks of the last round's tiles (1 = the round runs whole)
+  int sk = 0;   // Stream-K mode (streamk_geometry; 0 = none)
 };
 
 // Estimated time of a choice: the product at `score` of the fp32 peak, plus,
@@ -1152,6 +1290,32 @@ static F32Choice choose_staged(const Call &c) {
 // winners: 1536^3, 2560^3, 3072^3 and deep-K shapes such as 1024 x 1024 x
 // 8192 take 3-8 chunks of the 128x128 tile; square problems up to 1024 and
 // those whose tiles already fill the CUs stay unsplit).
+// Stream-K mode (streamk_geometry) for a call that takes the four-wave 64x64
+// tile whole (0: the plain launch).  By size: the whole rounds of one tile
+// per CU as whole tiles and the r leftover tiles' K steps dealt out to one
+// more workgroup per CU (mode 5), when r is at most 30% of the CUs past one
+// round or 50% past two.  The plain launch gives r CUs one tile more than
+// the others; the leftover's K steps spread over every CU instead, and the
+// Stream-K workgroups run beside the whole tiles (three of these workgroups
+// fit on a CU).  Measured (interleaved, beta 1, TFLOP/s, plain -> this):
+// 1088^3 58.3 -> 61.6, 1152^3 67.9 -> 70.3, 1472^3 85.4 -> 95.0, 1536^3
+// 93.6 -> 103.6, 1600^3 101.7 -> 106.3, 2048x1152x1024 88.4 -> 91.4,
+// 1152x2048x1536 93.4 -> 103.9; with larger leftovers it lost (1216^3 and
+// 1664^3 +-1%, 1280^3 -2%, 1408^3 -8%, 1728^3 -5%), and so did dealing out
+// every tile's K steps with no whole tiles first (1408^3 -15%, 1664^3 -8%,
+// 1536^3 +4%: most tiles were then shared, and their partial sums went
+// through memory).
+static int streamk_of(const Call &c) {
+  if (c.streamk_mode >= 2) return c.streamk_mode;
+  if (c.streamk_mode == 1) return 0;
+  const long long tiles = tiles_of<F32Quad>(c);
+  if (tiles < kCUs || tiles > 3LL * kCUs) return 0;
+  const long long r = tiles % kCUs;
+  if (r == 0) return 0;
+  const bool small_rest = tiles < 2LL * kCUs ? 10 * r <= 3LL * kCUs : 2 * r <= kCUs;
+  return small_rest ? 5 : 0;
+}
+
 static F32Choice choose_f32(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
   const int tail = c.tail_mode >= 2 && forced == 1 ? c.tail_mode : 1;
@@ -1161,7 +1325,8 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
   if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
-  if (c.tile_config == 7) return F32Choice{F32Cfg::kQuad, forced, 0.0, tail};
+  if (c.tile_config == 7)
+    return F32Choice{F32Cfg::kQuad, forced, 0.0, tail, forced == 1 && tail == 1 ? streamk_of(c) : 0};
   if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
       tiles_of<F32Mid>(c) < 3LL * kCUs)
@@ -1187,7 +1352,7 @@ static F32Choice choose_f32(const Call &c) {
     const long long q = tiles_of<F32Quad>(c), h = tiles_of<F32Half>(c);
     const long long mx = c.M > c.N ? c.M : c.N;
     if ((long long)c.K <= 2 * mx) {
-      if (q >= kCUs && q <= 3LL * kCUs) return F32Choice{F32Cfg::kQuad, 1, 0.0, 1};
+      if (q >= kCUs && q <= 3LL * kCUs) return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, streamk_of(c)};
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
     }
   }
@@ -1308,6 +1473,83 @@ static bool launch_tail(const Call &c, int want, hipError_t *err) {
   return true;
 }
 
+// Stream-K geometry of configuration T.  mode 2..4: every tile's K steps
+// dealt out to (mode - 1) workgroups per CU; mode 5, 6: the whole rounds of
+// one tile per CU as whole tiles, the leftover tiles' K steps dealt out to
+// (mode - 4) more workgroups per CU.  Every Stream-K workgroup runs `iters`
+// consecutive K steps of its tiles' combined sequence (the last one fewer);
+// `blocks` workgroups in all.  False when nothing is left to deal out or the
+// grid would not fit the kernel's int arithmetic.
+template <class T>
+static bool streamk_geometry(const Call &c, int mode, StreamKRun &sk, long long &blocks) {
+  const long long tiles = tiles_of<T>(c);
+  const long long steps = (c.K + T::BK - 1) / T::BK;
+  if (tiles < 1 || tiles > 0x7fffffffLL || steps < 1 || tiles * steps > (1LL << 40)) return false;
+  const bool hybrid = mode >= 5;
+  const long long dp = hybrid ? tiles / kCUs * kCUs : 0;
+  const long long total = (tiles - dp) * steps;
+  if (total < 1) return false;
+  const long long want = (long long)(hybrid ? mode - 4 : mode - 1) * kCUs;
+  sk.tiles = (int)tiles;
+  sk.steps = (int)steps;
+  sk.dp = (int)dp;
+  sk.iters = (total + want - 1) / want;
+  sk.W = nullptr;
+  blocks = dp + (total + sk.iters - 1) / sk.iters;
+  return blocks <= 0x7fffffffLL;
+}
+
+// Two fp32 tile blocks per Stream-K workgroup.
+static size_t streamk_ws_bytes(const StreamKRun &sk, long long blocks, int bm, int bn) {
+  return (size_t)(blocks - sk.dp) * 2 * (size_t)bm * (size_t)bn * sizeof(float);
+}
+
+// streamk_geometry, also false when the call's workspace cannot hold the
+// partial blocks (the call then runs the plain launch).
+template <class T>
+static bool streamk_fits(const Call &c, int mode, StreamKRun &sk, long long &blocks) {
+  return streamk_geometry<T>(c, mode, sk, blocks) &&
+         (long long)streamk_ws_bytes(sk, blocks, T::BM, T::BN) <= ws_available(c);
+}
+
+// Run configuration T as Stream-K (sgemm_streamk, then launch_streamk_fixup
+// for the tiles several workgroups share).  Returns false (nothing launched)
+// when the geometry does not apply or the workspace cannot be had.
+template <class T>
+static bool launch_streamk(const Call &c, int mode, hipError_t *err) {
+  StreamKRun sk;
+  long long blocks = 0;
+  if (!streamk_fits<T>(c, mode, sk, blocks)) return false;
+  void *ws = nullptr;
+  if (workspace_alloc(c, streamk_ws_bytes(sk, blocks, T::BM, T::BN), &ws) != hipSuccess) return false;
+  sk.W = static_cast<float *>(ws);
+  hipError_t e = dispatch_streamk<T>(c, sk, blocks);
+  if (e == hipSuccess) {
+    StreamKFixup f;
+    f.W = sk.W;
+    f.tiles = sk.tiles;
+    f.tile_base = sk.dp;
+    f.steps = sk.steps;
+    f.iters = sk.iters;
+    f.BM = T::BM;
+    f.BN = T::BN;
+    f.tiles_m = (c.M + T::BM - 1) / T::BM;
+    f.tiles_n = (c.N + T::BN - 1) / T::BN;
+    f.group_m = T::GROUP_M;
+    f.M = c.M;
+    f.N = c.N;
+    f.alpha = c.alpha;
+    f.beta = c.beta;
+    f.C = static_cast<float *>(c.C);
+    f.ldc = c.ldc;
+    f.force_scalar = c.force_scalar;
+    e = launch_streamk_fixup(f, c.stream);
+  }
+  const hipError_t fe = workspace_free(c, ws);
+  *err = e != hipSuccess ? e : fe;
+  return true;
+}
+
 template <class T>
 static hipError_t launch_cfg(const Call &c, int want, int tail = 1) {
   hipError_t te;
@@ -1375,6 +1617,18 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
 
 static Plan plan_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
+  if (ch.cfg == F32Cfg::kQuad && ch.sk > 0) {
+    Plan pl = make_plan<F32Quad>(c, "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots");
+    StreamKRun sk;
+    long long blocks = 0;
+    if (streamk_fits<F32Quad>(c, ch.sk, sk, blocks)) {
+      pl.streamk = true;
+      pl.sk_whole = sk.dp;
+      pl.blocks = blocks;
+      pl.ws_bytes = streamk_ws_bytes(sk, blocks, F32Quad::BM, F32Quad::BN);
+      return pl;
+    }
+  }
   switch (ch.cfg) {
     case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots spread loads", ch.splits, ch.tail);
     case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits, ch.tail);
@@ -1389,6 +1643,8 @@ static Plan plan_f32_as_is(const Call &c) {
 
 static hipError_t launch_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
+  hipError_t se;
+  if (ch.cfg == F32Cfg::kQuad && ch.sk > 0 && launch_streamk<F32Quad>(c, ch.sk, &se)) return se;
   switch (ch.cfg) {
     case F32Cfg::kHuge: return launch_cfg<F32Huge>(c, ch.splits, ch.tail);
     case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits, ch.tail);

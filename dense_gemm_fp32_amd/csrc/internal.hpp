@@ -48,6 +48,9 @@ struct Call {
   // do not allow 16-byte loads and the call is large enough, 1 = never,
   // 2 = whenever an operand's rows do not allow them (diagnostic).
   int pack_mode;
+  // Stream-K for the four-wave 64x64 fp32 tile: 0 = by size, 1 = never,
+  // 2..6 = whenever that tile is taken, in that mode (see streamk_geometry).
+  int streamk_mode;
   hipStream_t stream;
 };
 
@@ -63,6 +66,8 @@ struct Plan {
   size_t ws_bytes;           // workspace the call takes: copies of A and B, split K (0 = none)
   bool packed_a = false;     // the GEMM runs on a 16-byte-row copy of A ...
   bool packed_b = false;     // ... of B
+  bool streamk = false;      // Stream-K over `blocks` workgroups, then a fix-up pass ...
+  long long sk_whole = 0;    // ... the first sk_whole of them computing whole tiles
 };
 
 // The reduction pass of a split-K run of tiles: for each of `tiles` tiles
@@ -81,6 +86,26 @@ struct TileReduce {
   bool force_scalar;
 };
 hipError_t launch_tile_reduce(const TileReduce &r, hipStream_t s);
+
+// The fix-up pass of a Stream-K launch: tiles tile_base .. tiles-1 of
+// `steps` K steps each, dealt out in runs of `iters` steps per Stream-K
+// workgroup; for every tile that more than one workgroup covered, C :=
+// alpha * (sum of its workgroups' partial blocks, in workgroup order) +
+// beta * C on the part of the tile inside the matrix.  Stream-K workgroup
+// g's partial blocks are W[2g] (its first segment) and W[2g + 1] (its last),
+// dense BM x BN fp32 each.  fp32 C.
+struct StreamKFixup {
+  const float *W;
+  int tiles, tile_base, steps;
+  long long iters;
+  int BM, BN, tiles_m, tiles_n, group_m;
+  int M, N;
+  float alpha, beta;
+  float *C;
+  int ldc;
+  bool force_scalar;
+};
+hipError_t launch_streamk_fixup(const StreamKFixup &f, hipStream_t s);
 
 // The reduction pass of a split-K call: C := alpha * sum_s W_s + beta * C over
 // an M x N matrix, the S slabs of W (fp32, row pitch ldw, `stride` floats
@@ -146,6 +171,10 @@ struct PackChoice {
   size_t bytes = 0;                // the whole workspace
 };
 PackChoice pack_choice(const Call &c, int eb, Plan (*plan)(const Call &));
+
+// Workspace a call may take: its fixed region, else its limit, else the
+// pool's per-call cap.
+long long ws_available(const Call &c);
 Plan plan_packed(const Call &c, int eb, Plan (*plan)(const Call &));
 hipError_t run_packed(const Call &c, int eb, Plan (*plan)(const Call &),
                       hipError_t (*launch)(const Call &));

@@ -135,14 +135,6 @@ size_t copy_bytes(int rows, int cols, int eb) {
   return round_up((size_t)rows * (size_t)padded_ld(cols, eb) * (size_t)eb, kPackAlign);
 }
 
-// Workspace a call may take: its fixed region, else its limit, else the
-// pool's per-call cap.
-long long ws_available(const Call &c) {
-  if (c.ws_fixed != nullptr || c.ws_fixed_bytes > 0) return (long long)c.ws_fixed_bytes;
-  if (c.ws_limit >= 0) return c.ws_limit < kPoolCallCap ? c.ws_limit : kPoolCallCap;
-  return kPoolCallCap;
-}
-
 // The rule (fp32): copy when the call does at least kPackMinFlops flops, or
 // at least kPackMinFlopsEvenN with N a multiple of 4 (then the copied call's
 // last tile column still takes the direct loads; with a ragged N that column
@@ -167,6 +159,12 @@ bool pack_by_size(const Call &c, int eb) {
 }
 
 }  // namespace
+
+long long ws_available(const Call &c) {
+  if (c.ws_fixed != nullptr || c.ws_fixed_bytes > 0) return (long long)c.ws_fixed_bytes;
+  if (c.ws_limit >= 0) return c.ws_limit < kPoolCallCap ? c.ws_limit : kPoolCallCap;
+  return kPoolCallCap;
+}
 
 PackChoice pack_choice(const Call &c, int eb, Plan (*plan)(const Call &)) {
   PackChoice pk;

@@ -210,7 +210,80 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_tiles(TileReduce
   }
 }
 
+// One thread per 4 adjacent columns of a tile row, over every tile; tiles
+// that one workgroup covered whole were written by the GEMM and are skipped.
+template <bool VEC_C, bool READ_C>
+__global__ __launch_bounds__(kReduceThreads) void streamk_fixup(StreamKFixup f) {
+  const int groups = f.BN / 4;
+  const long long per_tile = (long long)f.BM * groups;
+  const long long total = (long long)(f.tiles - f.tile_base) * per_tile;
+  const size_t block = (size_t)f.BM * (size_t)f.BN;
+  for (long long t = (long long)blockIdx.x * kReduceThreads + threadIdx.x; t < total;
+       t += (long long)gridDim.x * kReduceThreads) {
+    const int local = (int)(t / per_tile);
+    const long long first_it = (long long)local * f.steps;
+    const long long g0 = first_it / f.iters;
+    const long long g1 = (first_it + f.steps - 1) / f.iters;
+    if (g0 == g1) continue;
+    const int rem = (int)(t - (long long)local * per_tile);
+    const int i = rem / groups;
+    const int j = 4 * (rem - i * groups);
+    int tm, tn;
+    tile_coords(f.tile_base + local, f.tiles_m, f.tiles_n, f.group_m, tm, tn);
+    const int row = tm * f.BM + i, col = tn * f.BN + j;
+    if (row >= f.M || col >= f.N) continue;
+    // workgroup g holds this tile in its last segment if the tile starts
+    // after g's run does, else in its first
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (long long g = g0; g <= g1; ++g) {
+      const long long slot = 2 * g + (first_it > g * f.iters ? 1 : 0);
+      sum += *reinterpret_cast<const f32x4 *>(f.W + (size_t)slot * block + (size_t)i * f.BN + j);
+    }
+    float *c = f.C + (size_t)row * (size_t)f.ldc + col;
+    if (VEC_C && col + 3 < f.N) {
+      f32x4 o;
+      if (READ_C) {
+        const f32x4 cv = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(f.beta, cv[e], f.alpha * sum[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f.alpha * sum[e];
+      }
+      *reinterpret_cast<f32x4 *>(c) = o;
+    } else {
+      float cv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cv[e] = (READ_C && col + e < f.N) ? c[e] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= f.N) continue;
+        float o = f.alpha * sum[e];
+        if (READ_C) o = __builtin_fmaf(f.beta, cv[e], o);
+        c[e] = o;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_streamk_fixup(const StreamKFixup &f, hipStream_t s) {
+  const long long total = (long long)(f.tiles - f.tile_base) * f.BM * (f.BN / 4);
+  long long blocks = (total + kReduceThreads - 1) / kReduceThreads;
+  if (blocks > kReduceMaxBlocks) blocks = kReduceMaxBlocks;
+  if (blocks < 1) blocks = 1;
+  const bool vec = !f.force_scalar && (f.ldc % 4) == 0 && aligned_to(f.C, 16);
+  const dim3 g((unsigned)blocks), b(kReduceThreads);
+  if (f.beta != 0.0f) {
+    if (vec) hipLaunchKernelGGL((streamk_fixup<true, true>), g, b, 0, s, f);
+    else hipLaunchKernelGGL((streamk_fixup<false, true>), g, b, 0, s, f);
+  } else {
+    if (vec) hipLaunchKernelGGL((streamk_fixup<true, false>), g, b, 0, s, f);
+    else hipLaunchKernelGGL((streamk_fixup<false, false>), g, b, 0, s, f);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_reduce(const TileReduce &r, hipStream_t s) {
   const long long total = (long long)r.tiles * r.BM * (r.BN / 4);

@@ -37,6 +37,14 @@
  *     small remainder may do this for the remainder's tiles only (dense
  *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
  *     the whole rounds.
+ *   - Stream-K (fp32, the 64x64 tile): when a call's 64x64 tiles fill one
+ *     or two whole rounds of the CUs and leave a small remainder, the whole
+ *     rounds' tiles run whole while the remainder's K steps are dealt out
+ *     evenly, in runs that may span tiles, to one more workgroup per CU in
+ *     the same launch (the "Stream-K" decomposition that the SGEMM summary's
+ *     results section names).  A tile so shared is summed from its parts'
+ *     fp32 partial sums, in K order, by a second pass that also applies
+ *     alpha and beta (2 * CUs * 64 * 64 * 4 bytes of workspace).
  *   - Operand copies (fp32): when the rows of A or B do not allow 16-byte
  *     loads (ld not a multiple of 4, or a base not 16-byte aligned) and the
  *     call does at least 5e9 flops, or 1.5e9 with N a multiple of 4, that
@@ -55,8 +63,8 @@
  *     no pointer to them after it returns and never allocates or frees the
  *     caller's memory.
  *   - A split-K call needs S*M*ceil(N/4)*16 bytes of workspace (a last-round
- *     split S*tiles*BM*BN*4 bytes; at most 1 GiB, larger splits are not
- *     taken) and takes it from a memory pool the library creates per device,
+ *     split S*tiles*BM*BN*4 bytes, a Stream-K call 2*64*64*4 bytes per
+ *     Stream-K workgroup; at most 1 GiB, larger splits are not taken) and takes it from a memory pool the library creates per device,
  *     with stream-ordered allocation on the call's stream, returning it to
  *     the pool, in stream order, after its last kernel.  Requests are made at
  *     the largest size used so far on the device (2 MiB steps) so that freed
@@ -351,6 +359,18 @@ int gemm_set_tail_split(int mode);
  * previous setting, or -1 for an unknown value.
  */
 int gemm_set_pack(int mode);
+
+/*
+ * Diagnostic switch for tests (fp32 calls that take the 64x64 tile whole):
+ * 0 = decide by problem size whether they run Stream-K (the default; see
+ * "Stream-K" above); 1 = never; 2, 3, 4 = always, every tile's K steps dealt
+ * out to 1, 2 or 3 workgroups per CU; 5, 6 = always, the whole rounds of one
+ * tile per CU first and the other tiles' K steps dealt out to 1 or 2 more
+ * workgroups per CU (5 is the by-size choice).  Calls whose workspace cannot
+ * be had run the plain launch.  Process-wide, like gemm_set_load_mode.
+ * Returns the previous setting, or -1 for an unknown value.
+ */
+int gemm_set_stream_k(int mode);
 
 /*
  * Cap on the workspace one call may take from the library's pool (operand

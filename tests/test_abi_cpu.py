@@ -533,6 +533,74 @@ def test_workspace_limit_switch():
     assert dg.gemm_set_workspace_limit(-1) == 1 << 20
 
 
+def test_stream_k_by_size_and_switches():
+    """Calls on the four-wave 64x64 tile whose last round is small -- at most
+    30% of the CUs past one round of tiles, 50% past two -- run Stream-K
+    behind the whole rounds, with two 64x64 fp32 blocks of workspace per
+    Stream-K workgroup (one per CU); other sizes, other tiles and calls whose
+    workspace cannot hold the blocks run the plain launch.  The switch forces
+    each decomposition, and refuses unknown modes."""
+    import dense_gemm_fp32_amd as dg
+
+    def d(M, N, K, lda=None, ldb=None, ldc=None):
+        rc, t = dg.gemm_describe("f32", M, N, K, 1.0, FAKE, lda or K, FAKE, ldb or N, 0.5, FAKE,
+                                 ldc or N)
+        assert rc == 0
+        return t
+
+    def ws(t):
+        return int(t.split("workspace ")[1].split()[0]) if "workspace" in t else 0
+
+    block = 2 * 64 * 64 * 4
+    # 1152^3: 324 tiles, 256 whole and 68 left (27% of the CUs); the 68
+    # tiles' 36 K steps each, 2448 in all, in runs of 10 over 245 workgroups
+    t = d(1152, 1152, 1152)
+    assert "64x64x32 4 waves" in t and "stream-K after 256 whole tiles" in t, t
+    assert "blocks 501 " in t and ws(t) == 245 * block, t
+    # 1536^3: 576 tiles, 512 whole and 64 left over 256 workgroups
+    t = d(1536, 1536, 1536)
+    assert "stream-K after 512 whole tiles" in t and "blocks 768 " in t and ws(t) == 256 * block, t
+    for n in (1088, 1472, 1600):
+        assert "stream-K after" in d(n, n, n), n
+    assert "stream-K after 512 whole tiles" in d(2048, 1152, 1024)
+    # larger leftovers (1216^3: 105 tiles, 1664^3: 164), a whole number of
+    # rounds (1024^3), and other tiles: the plain launch
+    for n in (1024, 1216, 1280, 1408, 1664, 2048, 4096):
+        assert "stream-K" not in d(n, n, n), n
+    # copies and Stream-K share one workspace
+    t = d(1536, 1536, 1536, 1537, 1537, 1537)
+    assert "copies A B" in t and "stream-K after 512" in t and ws(t) == 2 * 1536 * 1536 * 4 + 256 * block, t
+    # a workspace limit below the blocks drops Stream-K
+    prev = dg.gemm_set_workspace_limit(256 * block - 1)
+    try:
+        assert "stream-K" not in d(1536, 1536, 1536)
+        dg.gemm_set_workspace_limit(256 * block)
+        assert "stream-K after 512" in d(1536, 1536, 1536)
+    finally:
+        dg.gemm_set_workspace_limit(prev)
+    # the switch
+    prev = dg.gemm_set_stream_k(1)
+    try:
+        assert prev == 0
+        assert "stream-K" not in d(1536, 1536, 1536)
+        # every tile's K steps: 400 tiles x 40 steps over 256 workgroups
+        assert dg.gemm_set_stream_k(2) == 1
+        t = d(1280, 1280, 1280)
+        assert "stream-K" in t and "whole tiles" not in t and "blocks 254 " in t, t
+        # ... and with one round whole first (1024^3 has nothing left: plain)
+        dg.gemm_set_stream_k(5)
+        assert "stream-K after 256 whole tiles" in d(1280, 1280, 1280)
+        assert "stream-K" not in d(1024, 1024, 1024)
+        dg.gemm_set_stream_k(6)
+        t = d(1280, 1280, 1280)
+        assert "stream-K after 256 whole tiles" in t and ws(t) == (int(t.split("blocks ")[1].split()[0]) - 256) * block, t
+        # only calls on the 64x64 tile
+        assert "stream-K" not in d(4096, 4096, 4096)
+    finally:
+        dg.gemm_set_stream_k(prev)
+    assert dg.gemm_set_stream_k(7) == -1 and dg.gemm_set_stream_k(-1) == -1
+
+
 def test_operand_copies_by_size_and_switches():
     """Operands whose rows do not allow 16-byte loads are copied to 16-byte
     rows in fp32 calls above the size rule (5e9 flops, or 1.5e9 with N a

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gemm_harness import (bits, check, check_sampled, colmajor_buf, colmajor_view, exact_expected,
+from gemm_harness import (assert_pads_unchanged, bits, check, check_sampled, colmajor_buf,
+                          colmajor_view, exact_expected,
                           note, np_in, np_out, run, run_colmajor)
 
 pytestmark = pytest.mark.gpu
@@ -73,16 +74,25 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n,tile", [(1152, "64x64x32 4 waves"), (1408, "64x64x32 4 waves"),
-                                    (1664, "64x64x32 4 waves"), (1792, "128x64x32 4 waves"),
-                                    (1920, "128x64x32 4 waves")])
-def test_f32_sweep_four_wave_tile_full_oracle(n, tile):
-    """Sweep sizes (beta = 1) whose plan is a four-wave tile, unsplit: the
+@pytest.mark.parametrize("n,tile,whole", [(1152, "64x64x32 4 waves", 256),
+                                          (1408, "64x64x32 4 waves", 0),
+                                          (1536, "64x64x32 4 waves", 512),
+                                          (1664, "64x64x32 4 waves", 0),
+                                          (1792, "128x64x32 4 waves", 0),
+                                          (1920, "128x64x32 4 waves", 0)])
+def test_f32_sweep_four_wave_tile_full_oracle(n, tile, whole):
+    """Sweep sizes (beta = 1) whose plan is a four-wave tile, K unsplit: the
     64x64 tile of 32x32 waves (one to three tiles per CU) or the 128x64 tile
-    of 64x32 waves (1.5 to 2 per CU), every element against the oracle."""
+    of 64x32 waves (1.5 to 2 per CU), every element against the oracle.
+    1152^3 (324 tiles) and 1536^3 (576) leave a small last round, whose K
+    steps run Stream-K behind 256 and 512 whole tiles."""
     w = wl.sweep(n)
     plan = _plan(w)
     assert tile in plan and "split" not in plan, plan
+    if whole:
+        assert "stream-K after %d whole tiles" % whole in plan, plan
+    else:
+        assert "stream-K" not in plan, plan
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
@@ -1074,20 +1084,20 @@ def test_random_layouts_match_oracle(dtype, layout, M, N, K, pads, beta, cfg, sp
 def test_calls_replay_from_a_captured_graph():
     """Library calls captured into a HIP graph (torch.cuda.CUDAGraph on a
     side stream) -- unsplit fp32 and fp16, a whole split K, a last-round
-    split, and a call whose unaligned operands are copied to 16-byte rows,
-    whose workspace becomes an allocation node of the graph -- replay the
-    eager results bit for bit, several times, with eager GEMMs and
+    split, a Stream-K call, and a call whose unaligned operands are copied to
+    16-byte rows, whose workspace becomes an allocation node of the graph --
+    replay the eager results bit for bit, several times, with eager GEMMs and
     synchronisations between the replays."""
     import torch
     import dense_gemm_fp32_amd as dg
     from gemm_harness import note
-    note("graph capture: unsplit f32/f16, split K 4, last-round split 3, operand copies")
+    note("graph capture: unsplit f32/f16, split K 4, last-round split 3, stream-K, operand copies")
     dev = torch.device("cuda:0")
     g = torch.Generator().manual_seed(9)
     # (dtype, M, N, K, split mode, tail mode, row pad of A and B)
     cases = [("f32", 1000, 700, 3000, 1, 1, 0), ("f16", 600, 520, 1000, 1, 1, 0),
              ("f32", 1000, 700, 3000, 4, 1, 0), ("f32", 4200, 2000, 256, 1, 3, 0),
-             ("f32", 2048, 2048, 2048, 0, 0, 1)]
+             ("f32", 1536, 1536, 1536, 0, 0, 0), ("f32", 2048, 2048, 2048, 0, 0, 1)]
     for dtype, M, N, K, split, tail, pad in cases:
         t = torch.float32 if dtype == "f32" else torch.float16
         fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_f16
@@ -1097,6 +1107,7 @@ def test_calls_replay_from_a_captured_graph():
         C0 = (torch.rand(M, N, generator=g) * 2 - 1).to(t).to(dev)
         plan = dg.gemm_describe(dtype, M, N, K, 1.25, A, lda, B, ldb, 0.5, C0, N)[1]
         assert ("copies A B" in plan) == (pad > 0), plan
+        assert ("stream-K" in plan) == (M == 1536), plan
         with split_mode(split), tail_split(tail):
             ref = C0.clone()
             assert fn(M, N, K, 1.25, A, lda, B, ldb, 0.5, ref, N, None) == 0
@@ -1316,3 +1327,158 @@ def test_operand_copies_refused_fall_back(dtype):
     assert rc == 0
     assert np.array_equal(bits(out0, dtype), bits(ref, dtype))
     check_sampled(dtype, w, A, B, C, out0, nrows=12, seed=12)
+
+
+# ---------------------------------------------------------------- Stream-K
+
+@contextmanager
+def stream_k(mode):
+    import dense_gemm_fp32_amd as dg
+    prev = dg.gemm_set_stream_k(mode)
+    assert 0 <= prev <= 6
+    try:
+        yield
+    finally:
+        dg.gemm_set_stream_k(prev)
+
+
+# (M, N, K, pad_a, pad_b, pad_c, beta) on the 64x64 tile, every Stream-K mode
+STREAMK_CASES = [
+    (1100, 1200, 1300, 0, 0, 0, 0.5),   # 342 tiles; tails in M, N and K
+    (1152, 1152, 1152, 0, 0, 3, 1.0),   # C rows not 16-byte aligned: element-wise fix-up
+    (700, 1900, 333, 0, 0, 0, 0.0),     # beta 0 over a NaN C; K rows without 16-byte loads
+    (1090, 1500, 64, 4, 0, 0, -0.75),   # two K steps: runs shorter than a tile, many shared tiles
+]
+
+
+@pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
+def test_stream_k_every_mode_matches_oracle(layout):
+    """Every Stream-K decomposition of the 64x64 tile (every tile's K steps
+    over 1, 2 or 3 workgroups per CU; whole rounds first, the rest over 1 or
+    2 more per CU) and the plain launch, in each layout, against the oracle
+    element by element: shared tiles summed from their parts, tiles a run
+    covers whole written directly, ragged edges, alpha and beta applied once,
+    C pads untouched, and with beta = 0 a C full of NaN never read.  A second
+    call of each mode gives the same bits (the fix-up sums parts in K order)."""
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import layout_case, run_layout
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    for idx, (M, N, K, pa, pb, pc, beta) in enumerate(STREAMK_CASES):
+        lda = (M if ta else K) + pa
+        ldb = (K if tb else N) + pb
+        ldc = N + pc
+        Abuf, Bbuf, Cbuf, A, B, C = layout_case("f32", M, N, K, ta, tb, lda, ldb, ldc, 900 + idx)
+        if beta == 0.0:
+            Cbuf = wl.pad(np.full((M, N), np.nan, np.float32), ldc, wl.C_PAD_SENTINEL)
+        R, G = oracle.gemm(M, N, K, 1.5, A.reshape(-1), K, B.reshape(-1), N, beta,
+                           np.ascontiguousarray(C).reshape(-1) if beta != 0 else None, N, "f32")
+        Cv = C.astype(np.float64) if beta != 0 else 0.0
+        tol = oracle.tolerance(G, np.abs(Cv), 1.5, beta, K, R, oracle.out_type("f32"))
+        for mode in (1, 2, 3, 4, 5, 6):
+            label = "stream-K mode %d %s %dx%dx%d" % (mode, layout, M, N, K)
+            with stream_k(mode), tile_config(7):
+                # (gemm_describe takes the untransposed layout; the forced
+                # mode decides Stream-K whatever the layout)
+                rc, plan = dg.gemm_describe("f32", M, N, K, 1.5, 4096, K + pa, 4096, N + pb, beta,
+                                            4096, ldc)
+                assert rc == 0 and ("stream-K" in plan) == (mode >= 2), plan
+                outs = []
+                for rep in range(2):
+                    if layout == "nn":
+                        rc, out = run("f32", M, N, K, 1.5, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc,
+                                      label)
+                    else:
+                        rc, out = run_layout("f32", layout, M, N, K, 1.5, Abuf, lda, Bbuf, ldb,
+                                             beta, Cbuf, ldc, label)
+                    assert rc == 0, rc
+                    outs.append(out)
+            assert np.array_equal(bits(outs[0], "f32"), bits(outs[1], "f32")), label
+            gpu = wl.view(outs[0], M, N, ldc)
+            ok, worst, where = oracle.compare(gpu, R, tol)
+            assert ok, "%s (%s): worst |err|/tol %.3g at %s" % (label, plan, worst, where)
+            assert_pads_unchanged(outs[0], Cbuf, M, N, ldc, "f32")
+
+
+def test_stream_k_element_wise_loads_same_bits():
+    """Stream-K with the element-wise load switch (register-staged loads, an
+    element-wise fix-up) gives the bits of the 16-byte-load run: the same
+    products are summed in the same order, whichever way the data moves."""
+    import dense_gemm_fp32_amd as dg
+    M, N, K = 1536, 1536, 1100
+    w = wl.Workload("streamk_loads", "f32", M, N, K, K, N, N, 1.0, 0.25, "uniform", "uniform",
+                    (71, 72, 73))
+    A, B, C = wl.make(w)
+    outs = []
+    for scalar in (False, True):
+        prev = dg.gemm_set_load_mode(1 if scalar else 0)
+        try:
+            with stream_k(5):
+                rc, plan = dg.gemm_describe("f32", M, N, K, 1.0, 4096, K, 4096, N, 0.25, 4096, N)
+                assert "stream-K after 512 whole tiles" in plan, plan
+                rc, out = run("f32", M, N, K, 1.0, A, K, B, N, 0.25, C, N,
+                              "stream-K loads %s" % ("element-wise" if scalar else "16-byte"))
+        finally:
+            dg.gemm_set_load_mode(prev)
+        assert rc == 0
+        outs.append(out)
+    assert np.array_equal(bits(outs[0], "f32"), bits(outs[1], "f32"))
+    check_sampled("f32", w, A, B, C, outs[0], nrows=16, seed=13, extra_rows=[M - 1, M - 64])
+
+
+def test_stream_k_refused_falls_back():
+    """With the workspace capped below the partial blocks' 8 MiB, a call the
+    rule would run Stream-K runs the plain launch: the bits of Stream-K
+    switched off."""
+    import dense_gemm_fp32_amd as dg
+    n = 1536
+    w = wl.sweep(n)
+    A, B, C = wl.make(w)
+    with workspace_limit(1 << 20):
+        rc, plan = dg.gemm_describe("f32", n, n, n, w.alpha, 4096, n, 4096, n, w.beta, 4096, n)
+        assert rc == 0 and "stream-K" not in plan, plan
+        rc, out0 = run("f32", n, n, n, w.alpha, A, n, B, n, w.beta, C, n, "stream-K refused")
+    assert rc == 0
+    with stream_k(1):
+        rc, ref = run("f32", n, n, n, w.alpha, A, n, B, n, w.beta, C, n, "stream-K off")
+    assert rc == 0
+    assert np.array_equal(bits(out0, "f32"), bits(ref, "f32"))
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(layout=st.sampled_from(["nn"] + LAYOUTS),
+       M=st.integers(1, 400), N=st.integers(1, 400), K=st.integers(1, 400),
+       pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
+       beta=st.sampled_from([0.0, 1.0, -1.5]),
+       mode=st.sampled_from([2, 3, 4]),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_random_stream_k_match_oracle(layout, M, N, K, pads, beta, mode, seed):
+    """Random small shapes on the 64x64 tile with every tile's K steps dealt
+    out Stream-K over 1 to 3 workgroups per CU: runs of one K step up to
+    several tiles, every tail residue, aligned and unaligned rows, each
+    layout."""
+    _stream_k_case(layout, M, N, K, pads, beta, mode, seed)
+
+
+@settings(max_examples=12, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(layout=st.sampled_from(["nn"] + LAYOUTS),
+       M=st.integers(1025, 1400), N=st.integers(1025, 1400), K=st.integers(1, 200),
+       pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
+       beta=st.sampled_from([0.0, 1.0, -1.5]),
+       mode=st.sampled_from([5, 6]),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_random_stream_k_behind_whole_tiles_match_oracle(layout, M, N, K, pads, beta, mode, seed):
+    """Random shapes of 257 to 484 64x64 tiles, short K, with one round of
+    whole tiles and the leftover tiles' K steps dealt out to one or two more
+    workgroups per CU, each layout, against the oracle."""
+    _stream_k_case(layout, M, N, K, pads, beta, mode, seed)
+
+
+def _stream_k_case(layout, M, N, K, pads, beta, mode, seed):
+    from gemm_harness import check_layout
+    label = "hyp stream-K mode %d %s %s" % (mode, layout, (M, N, K))
+    with tile_config(7), stream_k(mode):
+        A, B, C, Cbuf, ldc, out = _layout_outputs("f32", layout, M, N, K, pads, seed % 100000, 1.5,
+                                                  beta, label)
+    check_layout("f32", M, N, K, 1.5, A, B, beta, C, Cbuf, ldc, out, label)
