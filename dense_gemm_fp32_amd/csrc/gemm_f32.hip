@@ -1291,29 +1291,30 @@ static F32Choice choose_staged(const Call &c) {
 // 8192 take 3-8 chunks of the 128x128 tile; square problems up to 1024 and
 // those whose tiles already fill the CUs stay unsplit).
 // Stream-K mode (streamk_geometry) for a call that takes the four-wave 64x64
-// tile whole (0: the plain launch).  By size: the whole rounds of one tile
-// per CU as whole tiles and the r leftover tiles' K steps dealt out to one
-// more workgroup per CU (mode 5), when r is at most 30% of the CUs past one
-// round or 50% past two.  The plain launch gives r CUs one tile more than
-// the others; the leftover's K steps spread over every CU instead, and the
-// Stream-K workgroups run beside the whole tiles (three of these workgroups
-// fit on a CU).  Measured (interleaved, beta 1, TFLOP/s, plain -> this):
-// 1088^3 58.3 -> 61.6, 1152^3 67.9 -> 70.3, 1472^3 85.4 -> 95.0, 1536^3
-// 93.6 -> 103.6, 1600^3 101.7 -> 106.3, 2048x1152x1024 88.4 -> 91.4,
-// 1152x2048x1536 93.4 -> 103.9; with larger leftovers it lost (1216^3 and
-// 1664^3 +-1%, 1280^3 -2%, 1408^3 -8%, 1728^3 -5%), and so did dealing out
-// every tile's K steps with no whole tiles first (1408^3 -15%, 1664^3 -8%,
-// 1536^3 +4%: most tiles were then shared, and their partial sums went
-// through memory).
+// tile whole (0: the plain launch).  By size: past two whole rounds of one
+// tile per CU, with r leftover tiles, at most half the CUs, the whole rounds
+// run as whole tiles and the leftover tiles' K steps are dealt out to one
+// more workgroup per CU (mode 5).  The plain launch gives r CUs one tile
+// more than the others; the leftover's K steps spread over every CU
+// instead, and the Stream-K workgroups run beside the whole tiles (three of
+// these workgroups fit on a CU).  Measured, plain -> Stream-K, TFLOP/s, beta
+// 1, interleaved; first back to back, then with a 512 MiB cache flush before
+// each call: 1472^3 85.4 -> 95.0 and 80.9 -> 88.9, 1536^3 93.6 -> 103.6 and
+// 88.8 -> 96.6, 1600^3 101.7 -> 106.3 and 96.1 -> 98.4, 2048x1152x1024
+// 88.4 -> 91.4 and 82.2 -> 83.9, 1152x2048x1536 93.4 -> 103.9.  Past one
+// round only it gained back to back (1088^3 58.3 -> 61.6, 1152^3 67.9 ->
+// 70.3) but not after a flush (57.3 -> 56.2, 63.4 -> 63.1), so those stay
+// plain; with larger leftovers it lost (1664^3 and 1216^3 +-1%, 1280^3 -2%,
+// 1408^3 -8%, 1728^3 -5%), and so did dealing out every tile's K steps with
+// no whole tiles first (1408^3 -15%, 1664^3 -8%, 1536^3 +4%: most tiles
+// were then shared, and their partial sums went through memory).
 static int streamk_of(const Call &c) {
   if (c.streamk_mode >= 2) return c.streamk_mode;
   if (c.streamk_mode == 1) return 0;
   const long long tiles = tiles_of<F32Quad>(c);
-  if (tiles < kCUs || tiles > 3LL * kCUs) return 0;
+  if (tiles <= 2LL * kCUs || tiles > 3LL * kCUs) return 0;
   const long long r = tiles % kCUs;
-  if (r == 0) return 0;
-  const bool small_rest = tiles < 2LL * kCUs ? 10 * r <= 3LL * kCUs : 2 * r <= kCUs;
-  return small_rest ? 5 : 0;
+  return r > 0 && 2 * r <= kCUs ? 5 : 0;
 }
 
 static F32Choice choose_f32(const Call &c) {

@@ -37,8 +37,8 @@
  *     small remainder may do this for the remainder's tiles only (dense
  *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
  *     the whole rounds.
- *   - Stream-K (fp32, the 64x64 tile): when a call's 64x64 tiles fill one
- *     or two whole rounds of the CUs and leave a small remainder, the whole
+ *   - Stream-K (fp32, the 64x64 tile): when a call's 64x64 tiles fill two
+ *     whole rounds of the CUs and leave at most half a round more, the whole
  *     rounds' tiles run whole while the remainder's K steps are dealt out
  *     evenly, in runs that may span tiles, to one more workgroup per CU in
  *     the same launch (the "Stream-K" decomposition that the SGEMM summary's

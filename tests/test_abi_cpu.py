@@ -534,12 +534,12 @@ def test_workspace_limit_switch():
 
 
 def test_stream_k_by_size_and_switches():
-    """Calls on the four-wave 64x64 tile whose last round is small -- at most
-    30% of the CUs past one round of tiles, 50% past two -- run Stream-K
-    behind the whole rounds, with two 64x64 fp32 blocks of workspace per
-    Stream-K workgroup (one per CU); other sizes, other tiles and calls whose
-    workspace cannot hold the blocks run the plain launch.  The switch forces
-    each decomposition, and refuses unknown modes."""
+    """Calls on the four-wave 64x64 tile with two whole rounds of tiles and
+    at most half a round more run Stream-K behind the whole rounds, with two
+    64x64 fp32 blocks of workspace per Stream-K workgroup (one per CU); other
+    sizes, other tiles and calls whose workspace cannot hold the blocks run
+    the plain launch.  The switch forces each decomposition, and refuses
+    unknown modes."""
     import dense_gemm_fp32_amd as dg
 
     def d(M, N, K, lda=None, ldb=None, ldc=None):
@@ -552,20 +552,19 @@ def test_stream_k_by_size_and_switches():
         return int(t.split("workspace ")[1].split()[0]) if "workspace" in t else 0
 
     block = 2 * 64 * 64 * 4
-    # 1152^3: 324 tiles, 256 whole and 68 left (27% of the CUs); the 68
-    # tiles' 36 K steps each, 2448 in all, in runs of 10 over 245 workgroups
-    t = d(1152, 1152, 1152)
-    assert "64x64x32 4 waves" in t and "stream-K after 256 whole tiles" in t, t
-    assert "blocks 501 " in t and ws(t) == 245 * block, t
     # 1536^3: 576 tiles, 512 whole and 64 left over 256 workgroups
     t = d(1536, 1536, 1536)
-    assert "stream-K after 512 whole tiles" in t and "blocks 768 " in t and ws(t) == 256 * block, t
-    for n in (1088, 1472, 1600):
-        assert "stream-K after" in d(n, n, n), n
+    assert "64x64x32 4 waves" in t and "stream-K after 512 whole tiles" in t, t
+    assert "blocks 768 " in t and ws(t) == 256 * block, t
+    # 1472^3: 529 tiles, 17 left; their 46 K steps each, 782 in all, in runs
+    # of 4 over 196 workgroups
+    t = d(1472, 1472, 1472)
+    assert "stream-K after 512 whole tiles" in t and "blocks 708 " in t and ws(t) == 196 * block, t
+    assert "stream-K after 512 whole tiles" in d(1600, 1600, 1600)
     assert "stream-K after 512 whole tiles" in d(2048, 1152, 1024)
-    # larger leftovers (1216^3: 105 tiles, 1664^3: 164), a whole number of
-    # rounds (1024^3), and other tiles: the plain launch
-    for n in (1024, 1216, 1280, 1408, 1664, 2048, 4096):
+    # one round and a small leftover (1088^3, 1152^3), larger leftovers
+    # (1664^3: 164 tiles), whole rounds (1024^3), other tiles: plain
+    for n in (1024, 1088, 1152, 1216, 1280, 1408, 1664, 2048, 4096):
         assert "stream-K" not in d(n, n, n), n
     # copies and Stream-K share one workspace
     t = d(1536, 1536, 1536, 1537, 1537, 1537)
@@ -696,6 +695,8 @@ def _short_plan(plan, sweep):
     body = plan.split(" tile ", 1)[1]
     if sweep:
         short = body.split(" loads A:")[0]
+        if "stream-K" in plan:
+            short += " stream-K" + plan.split("stream-K")[1].split(" workspace")[0]
         if "split-K" in plan:
             short += " " + ("last round " if "last round" in plan else "") + \
                 "split-K " + plan.split("split-K ")[1].split()[0]

@@ -74,7 +74,7 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n,tile,whole", [(1152, "64x64x32 4 waves", 256),
+@pytest.mark.parametrize("n,tile,whole", [(1152, "64x64x32 4 waves", 0),
                                           (1408, "64x64x32 4 waves", 0),
                                           (1536, "64x64x32 4 waves", 512),
                                           (1664, "64x64x32 4 waves", 0),
@@ -84,8 +84,8 @@ def test_f32_sweep_four_wave_tile_full_oracle(n, tile, whole):
     """Sweep sizes (beta = 1) whose plan is a four-wave tile, K unsplit: the
     64x64 tile of 32x32 waves (one to three tiles per CU) or the 128x64 tile
     of 64x32 waves (1.5 to 2 per CU), every element against the oracle.
-    1152^3 (324 tiles) and 1536^3 (576) leave a small last round, whose K
-    steps run Stream-K behind 256 and 512 whole tiles."""
+    1536^3 (576 tiles) leaves a small third round, whose K steps run
+    Stream-K behind 512 whole tiles."""
     w = wl.sweep(n)
     plan = _plan(w)
     assert tile in plan and "split" not in plan, plan
