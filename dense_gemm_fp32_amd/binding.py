@@ -213,10 +213,11 @@ def gemm_set_pack(mode):
 
 
 def gemm_set_stream_k(mode):
-    """fp32 calls on the 64x64 tile: 0 = Stream-K by size (default),
-    1 = never, 2..4 = every tile's K steps over 1..3 workgroups per CU,
-    5..6 = whole rounds first, the rest over 1..2 more workgroups per CU.
-    Returns the previous mode, or -1."""
+    """fp32: 0 = Stream-K by size (default), 1 = never; with the 64x64
+    four-wave tile or a forced tile configuration (1, 5, 6, 7): 2..4 = every
+    tile's K steps over 1..3 workgroups per CU, 5..6 = whole rounds first,
+    the rest over 1..2 more workgroups per CU.  Returns the previous mode,
+    or -1."""
     return _lib.gemm_set_stream_k(int(mode))
 
 

@@ -907,11 +907,14 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma(GemmParams p) {
 // the other workgroups, so that every CU ends up with the same work whatever
 // the tile count; dp is a whole number of rounds of one tile per CU, and the
 // hardware hands out workgroups in blockIdx order, so each CU holds the same
-// mix of whole-tile and Stream-K workgroups.  A run crosses tile boundaries;
-// a tile it covers whole is written to C as usual, and a part of a tile (its
-// first or last segment) is written as raw fp32 sums to the workgroup's
-// workspace slot: 2g for its first segment, 2g + 1 for its last, g the
-// workgroup's position among the Stream-K workgroups in XCD-remapped order.
+// mix of whole-tile and Stream-K workgroups.  A run is at most one tile's K
+// steps long, so it touches one tile or crosses into a second (two
+// segments, written out rather than looped: a loop kept the load addresses
+// of one segment live through the next, past the larger tiles' register
+// budgets); a segment covering its tile whole is written to C as usual, and
+// a part of a tile is written as raw fp32 sums to the workgroup's workspace
+// slot: 2g for its first segment, 2g + 1 for its second, g the workgroup's
+// position among the Stream-K workgroups in XCD-remapped order.
 // The fix-up pass (launch_streamk_fixup) then sums each shared tile's slots
 // in workgroup order -- ascending K -- and applies alpha and beta, so results
 // do not depend on which workgroup finishes first.
@@ -938,8 +941,7 @@ __global__ __launch_bounds__(T::NT) void sgemm_streamk(GemmParams p, StreamKRun 
   const long long it_all = (long long)(sk.tiles - sk.dp) * sk.steps;
   long long it = (long long)g * sk.iters;
   const long long it1 = it + sk.iters < it_all ? it + sk.iters : it_all;
-  bool first = true;
-  while (it < it1) {
+  auto segment = [&](bool first) {
     const int local = (int)(it / sk.steps);
     const int kb = (int)(it - (long long)local * sk.steps);
     const long long room = it1 - it;
@@ -947,14 +949,12 @@ __global__ __launch_bounds__(T::NT) void sgemm_streamk(GemmParams p, StreamKRun 
     int tm, tn;
     tile_coords(sk.dp + local, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
-    // This segment's K range: steps kb .. ke-1 of T::BK (the last may be short).
     const int k_lo = kb * T::BK;
     const int k_hi = (long long)ke * T::BK < (long long)p.K ? ke * T::BK : p.K;
     GemmParams q = p;
     q.K = k_hi - k_lo;
     q.A = static_cast<const float *>(p.A) + (TA ? (size_t)k_lo * (size_t)p.lda : (size_t)k_lo);
     q.B = static_cast<const float *>(p.B) + (TB ? (size_t)k_lo : (size_t)k_lo * (size_t)p.ldb);
-    if (!first) __syncthreads();   // every wave is done with the previous segment's LDS
     f32x16 acc[T::FM][T::FN];
     tile_product<T, TA, TB>(q, m0, n0, lds, wm0, wn0, acc);
     if (kb == 0 && ke == sk.steps) {
@@ -969,8 +969,12 @@ __global__ __launch_bounds__(T::NT) void sgemm_streamk(GemmParams p, StreamKRun 
       w.beta = 0.0f;
       epilogue32<T, true, false>(w, wm0, wn0, acc);
     }
-    first = false;
     it += ke - kb;
+  };
+  segment(true);
+  if (it < it1) {
+    __syncthreads();
+    segment(false);
   }
 }
 
@@ -1317,15 +1321,97 @@ static int streamk_of(const Call &c) {
   return r > 0 && 2 * r <= kCUs ? 5 : 0;
 }
 
+// Stream-K behind whole rounds (mode 5) in place of the model's choice
+// `best`, for calls with 1024 <= K <= 2 max(M, N) and rows that take 16-byte
+// loads (deeper K keeps the model's K splits, which were not measured
+// against it).  The r leftover tiles' K steps go to one more workgroup per
+// CU in the same launch, so every CU ends with the same work.  Measured
+// (interleaved, a 512 MiB flush before each call, beta 1, TFLOP/s, on two
+// boxes, one of which held its package power limit most of the time):
+// - the 128x128 tile with Stream-K, whatever was chosen, for 2 to 7 rounds
+//   of its tiles and r from a quarter to seven eighths of the CUs: 3328^3
+//   (256x128 tile split 3) 127.0 -> 135.4, 3840^3 (256x256 tile) 128.1 ->
+//   139.4, 4352^3 (128x128 tile) 131.0 -> 141.7, 4864^3 (256x128 tile) 134.7
+//   -> 142.1, 5248^3 136.5 -> 144.5 (a K split there too: 3200^3 131.1 ->
+//   132.7); both boxes gained.  Past about seven
+//   rounds the runs are long enough for the power-limited box to clock the
+//   128x128 tile ~5% below the larger tiles (2.20-2.25 against 2.33-2.38
+//   GHz), so
+// - from 7 to 16 rounds it replaces only the 128x128 tile itself (plain or
+//   with the last round split): 6016^3 139.4 -> 145.0, 7040^3 142.4 ->
+//   145.3, 7296^3 141.2 -> 144.7; with a leftover of a few tiles the last
+//   round's split did as well or better (2944^3 128.6 against 126.8,
+//   4608^3 141.8 against 139.5), with a nearly full last round the plain
+//   launch is balanced already (4992^3 -0.8%, 5760^3 -0.3%), and past 16
+//   rounds the imbalance is small (9344^3 145.0 against 144.5);
+// - the 256x128 and 256x256 tiles, plain or with the last round split, take
+//   Stream-K on the same tile whenever a round is left partly filled: over
+//   35 sweep sizes from 3328^3 to 12672^3 none lost more than 0.2%, 4864^3
+//   134.7 -> 139.7, 5632^3 139.8 -> 144.5, 6400^3 140.5 -> 142.1, 10752^3
+//   146.2 -> 147.6, the last-round splits' sizes +0.2% on average;
+// - ahead of all of these, the 256x256 tile (Stream-K when a round is left
+//   partly filled) wherever it has at least one round of tiles and at least
+//   97% of its tiles' area lies inside the matrix: in place of the 128x128
+//   tile, 6144^3 147.2 -> 148.9, 8448^3 144.6 -> 149.8, 9472^3 144.1 ->
+//   150.4, 11008^3 145.1 -> 151.2, 12800^3 145.7 -> 150.5 (n a multiple of
+//   256: no tile area lost), 9344^3 142.5 -> 146.2, 12416^3 144.2 -> 148.3
+//   (half-empty last tiles, 97-98% of the area inside); at 96-96.5%
+//   (6528^3 .. 7296^3) it lost 0.3-1.6% and is not taken.  Both boxes hold
+//   this tile's clock highest.  The model's efficiencies, measured at
+//   4096^3 in short runs, count neither the area of half-empty edge tiles
+//   nor the lower clock of the smaller tiles over long runs.
+template <class T>
+static bool streamk_fits(const Call &c, int mode, StreamKRun &sk, long long &blocks);
+
+// The choice with Stream-K mode 5 on configuration T, if its partial blocks
+// fit the call's workspace; else `best` (which may split the last round in
+// less workspace).
+template <class T>
+static F32Choice streamk_if_fits(const Call &c, F32Cfg cfg, const F32Choice &best) {
+  StreamKRun sk;
+  long long blocks = 0;
+  return streamk_fits<T>(c, 5, sk, blocks) ? F32Choice{cfg, 1, best.time, 1, 5} : best;
+}
+
+static F32Choice streamk_instead(const Call &c, const F32Choice &best) {
+  const long long mx = c.M > c.N ? c.M : c.N;
+  if (c.split_mode != 0 || c.tail_mode != 0 || c.streamk_mode != 0 || c.K < 1024 ||
+      (long long)c.K > 2 * mx || staged_call(c))
+    return best;
+  // The 256x256 tile, with Stream-K when its last round is partly filled,
+  // wherever it has a round of tiles and at least 97% of its tiles' area
+  // lies inside the matrix.
+  const long long th = tiles_of<F32Huge>(c);
+  const double useful = (double)c.M * (double)c.N / ((double)th * F32Huge::BM * F32Huge::BN);
+  if (th >= kCUs && useful >= 0.97) {
+    if (th % kCUs == 0) return F32Choice{F32Cfg::kHuge, 1, best.time, 1, 0};
+    return streamk_if_fits<F32Huge>(c, F32Cfg::kHuge, best);
+  }
+  const long long tm = tiles_of<F32MidB>(c);
+  const long long r = tm % kCUs;
+  const bool whole_k = best.splits == 1;   // unsplit, or only the last round split
+  const bool mid = whole_k && (best.cfg == F32Cfg::kMid || best.cfg == F32Cfg::kMidB);
+  if (tm >= 2LL * kCUs && 4 * r >= kCUs && 8 * r <= 7LL * kCUs &&
+      (tm <= 7LL * kCUs || (mid && tm <= 16LL * kCUs)))
+    return streamk_if_fits<F32MidB>(c, F32Cfg::kMidB, best);
+  if (!whole_k) return best;
+  if (best.cfg == F32Cfg::kHuge && tiles_of<F32Huge>(c) >= kCUs && tiles_of<F32Huge>(c) % kCUs != 0)
+    return streamk_if_fits<F32Huge>(c, F32Cfg::kHuge, best);
+  if (best.cfg == F32Cfg::kBig && tiles_of<F32Big>(c) >= kCUs && tiles_of<F32Big>(c) % kCUs != 0)
+    return streamk_if_fits<F32Big>(c, F32Cfg::kBig, best);
+  return best;
+}
+
 static F32Choice choose_f32(const Call &c) {
   const int forced = c.split_mode >= 2 ? c.split_mode : 1;
   const int tail = c.tail_mode >= 2 && forced == 1 ? c.tail_mode : 1;
-  if (c.tile_config == 1) return F32Choice{F32Cfg::kBig, forced, 0.0, tail};
+  const int fsk = forced == 1 && tail == 1 && c.streamk_mode >= 2 ? c.streamk_mode : 0;
+  if (c.tile_config == 1) return F32Choice{F32Cfg::kBig, forced, 0.0, tail, fsk};
   if (c.tile_config == 2) return F32Choice{F32Cfg::kMid, forced, 0.0, tail};
   if (c.tile_config == 3) return F32Choice{F32Cfg::kSmall, forced, 0.0, tail};
   if (c.tile_config == 4) return F32Choice{F32Cfg::kTiny, forced, 0.0, tail};
-  if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail};
-  if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail};
+  if (c.tile_config == 5) return F32Choice{F32Cfg::kMidB, forced, 0.0, tail, fsk};
+  if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail, fsk};
   if (c.tile_config == 7)
     return F32Choice{F32Cfg::kQuad, forced, 0.0, tail, forced == 1 && tail == 1 ? streamk_of(c) : 0};
   if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
@@ -1407,7 +1493,7 @@ static F32Choice choose_f32(const Call &c) {
   // Spread loads pay while a CU holds one workgroup; with several resident
   // the others hide the load bursts and issuing them together is cheaper.
   if (best.cfg == F32Cfg::kMid && tiles_of<F32Mid>(c) * best.splits > kCUs) best.cfg = F32Cfg::kMidB;
-  return best;
+  return streamk_instead(c, best);
 }
 
 // Run configuration T, splitting K when the split count says so: the tiles
@@ -1478,8 +1564,9 @@ static bool launch_tail(const Call &c, int want, hipError_t *err) {
 // dealt out to (mode - 1) workgroups per CU; mode 5, 6: the whole rounds of
 // one tile per CU as whole tiles, the leftover tiles' K steps dealt out to
 // (mode - 4) more workgroups per CU.  Every Stream-K workgroup runs `iters`
-// consecutive K steps of its tiles' combined sequence (the last one fewer);
-// `blocks` workgroups in all.  False when nothing is left to deal out or the
+// consecutive K steps of its tiles' combined sequence (the last one fewer),
+// at most one tile's steps (more workgroups than asked for when the share
+// would be longer); `blocks` workgroups in all.  False when nothing is left to deal out or the
 // grid would not fit the kernel's int arithmetic.
 template <class T>
 static bool streamk_geometry(const Call &c, int mode, StreamKRun &sk, long long &blocks) {
@@ -1495,6 +1582,7 @@ static bool streamk_geometry(const Call &c, int mode, StreamKRun &sk, long long 
   sk.steps = (int)steps;
   sk.dp = (int)dp;
   sk.iters = (total + want - 1) / want;
+  if (sk.iters > steps) sk.iters = steps;   // a run touches at most two tiles
   sk.W = nullptr;
   blocks = dp + (total + sk.iters - 1) / sk.iters;
   return blocks <= 0x7fffffffLL;
@@ -1616,36 +1704,70 @@ static Plan plan_cfg(const Call &c, const char *name, int want, int tail) {
   return pl;
 }
 
+// Plan of a Stream-K call of configuration T (false: it does not apply).
+template <class T>
+static bool plan_streamk(const Call &c, const char *name, int mode, Plan &pl) {
+  StreamKRun sk;
+  long long blocks = 0;
+  if (!streamk_fits<T>(c, mode, sk, blocks)) return false;
+  pl = make_plan<T>(c, name);
+  pl.streamk = true;
+  pl.sk_whole = sk.dp;
+  pl.blocks = blocks;
+  pl.ws_bytes = streamk_ws_bytes(sk, blocks, T::BM, T::BN);
+  return true;
+}
+
+static const char *f32_name(F32Cfg cfg) {
+  switch (cfg) {
+    case F32Cfg::kHuge: return "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots spread loads";
+    case F32Cfg::kBig: return "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads";
+    case F32Cfg::kMid: return "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads";
+    case F32Cfg::kMidB: return "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots";
+    case F32Cfg::kSmall: return "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots";
+    case F32Cfg::kQuad: return "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots";
+    case F32Cfg::kHalf: return "f32 mfma32x32x2 tile 128x64x32 4 waves 3 slots";
+    default: return "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots";
+  }
+}
+
 static Plan plan_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
-  if (ch.cfg == F32Cfg::kQuad && ch.sk > 0) {
-    Plan pl = make_plan<F32Quad>(c, "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots");
-    StreamKRun sk;
-    long long blocks = 0;
-    if (streamk_fits<F32Quad>(c, ch.sk, sk, blocks)) {
-      pl.streamk = true;
-      pl.sk_whole = sk.dp;
-      pl.blocks = blocks;
-      pl.ws_bytes = streamk_ws_bytes(sk, blocks, F32Quad::BM, F32Quad::BN);
-      return pl;
+  const char *name = f32_name(ch.cfg);
+  Plan pl;
+  if (ch.sk > 0) {
+    switch (ch.cfg) {
+      case F32Cfg::kHuge: if (plan_streamk<F32Huge>(c, name, ch.sk, pl)) return pl; break;
+      case F32Cfg::kBig: if (plan_streamk<F32Big>(c, name, ch.sk, pl)) return pl; break;
+      case F32Cfg::kMidB: if (plan_streamk<F32MidB>(c, name, ch.sk, pl)) return pl; break;
+      case F32Cfg::kQuad: if (plan_streamk<F32Quad>(c, name, ch.sk, pl)) return pl; break;
+      default: break;
     }
   }
   switch (ch.cfg) {
-    case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, "f32 mfma32x32x2 tile 256x256x32 8 waves 2 slots spread loads", ch.splits, ch.tail);
-    case F32Cfg::kBig: return plan_cfg<F32Big>(c, "f32 mfma32x32x2 tile 256x128x32 8 waves 3 slots spread loads", ch.splits, ch.tail);
-    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots spread loads", ch.splits, ch.tail);
-    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, "f32 mfma32x32x2 tile 128x128x16 4 waves 3 slots", ch.splits, ch.tail);
-    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots", ch.splits, ch.tail);
-    case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots", ch.splits, ch.tail);
-    case F32Cfg::kHalf: return plan_cfg<F32Half>(c, "f32 mfma32x32x2 tile 128x64x32 4 waves 3 slots", ch.splits, ch.tail);
-    default: return plan_cfg<F32Tiny>(c, "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots", ch.splits, ch.tail);
+    case F32Cfg::kHuge: return plan_cfg<F32Huge>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kBig: return plan_cfg<F32Big>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kMid: return plan_cfg<F32Mid>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kMidB: return plan_cfg<F32MidB>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kSmall: return plan_cfg<F32Small>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kHalf: return plan_cfg<F32Half>(c, name, ch.splits, ch.tail);
+    default: return plan_cfg<F32Tiny>(c, name, ch.splits, ch.tail);
   }
 }
 
 static hipError_t launch_f32_as_is(const Call &c) {
   const F32Choice ch = choose_f32(c);
   hipError_t se;
-  if (ch.cfg == F32Cfg::kQuad && ch.sk > 0 && launch_streamk<F32Quad>(c, ch.sk, &se)) return se;
+  if (ch.sk > 0) {
+    switch (ch.cfg) {
+      case F32Cfg::kHuge: if (launch_streamk<F32Huge>(c, ch.sk, &se)) return se; break;
+      case F32Cfg::kBig: if (launch_streamk<F32Big>(c, ch.sk, &se)) return se; break;
+      case F32Cfg::kMidB: if (launch_streamk<F32MidB>(c, ch.sk, &se)) return se; break;
+      case F32Cfg::kQuad: if (launch_streamk<F32Quad>(c, ch.sk, &se)) return se; break;
+      default: break;
+    }
+  }
   switch (ch.cfg) {
     case F32Cfg::kHuge: return launch_cfg<F32Huge>(c, ch.splits, ch.tail);
     case F32Cfg::kBig: return launch_cfg<F32Big>(c, ch.splits, ch.tail);

@@ -48,8 +48,9 @@ struct Call {
   // do not allow 16-byte loads and the call is large enough, 1 = never,
   // 2 = whenever an operand's rows do not allow them (diagnostic).
   int pack_mode;
-  // Stream-K for the four-wave 64x64 fp32 tile: 0 = by size, 1 = never,
-  // 2..6 = whenever that tile is taken, in that mode (see streamk_geometry).
+  // Stream-K (fp32): 0 = by size, 1 = never, 2..6 = in that mode (see
+  // streamk_geometry) whenever the four-wave 64x64 tile or a forced tile
+  // configuration (1, 5, 6, 7) is taken.
   int streamk_mode;
   hipStream_t stream;
 };

@@ -355,7 +355,11 @@ hipError_t scratch_region(int dev, void **ptr) {
 // 2 MiB steps), so a freed block always fits the next request: measured, a
 // request larger than the blocks the pool holds costs ~30 us more than one it
 // can serve from a freed block, and the pool does not reuse a block across
-// different sizes.  A call with a fixed region uses it when it is large
+// different sizes.  That size rises only up to what the pool keeps: a block
+// larger than kPoolKeep goes back to the runtime at the next
+// synchronisation, so raising every later request to it would make each
+// such request a fresh allocation of that size.  Larger requests are made at
+// their own size.  A call with a fixed region uses it when it is large
 // enough and never touches the pool.
 hipError_t workspace_alloc(const Call &c, size_t bytes, void **ptr) {
   *ptr = nullptr;
@@ -373,8 +377,10 @@ hipError_t workspace_alloc(const Call &c, size_t bytes, void **ptr) {
   bytes = (bytes + kStep - 1) / kStep * kStep;
   {
     std::lock_guard<std::mutex> lock(g_pool_mu);
-    if (bytes > g_high_water[dev]) g_high_water[dev] = bytes;
-    bytes = g_high_water[dev];
+    if (bytes <= kPoolKeep) {
+      if (bytes > g_high_water[dev]) g_high_water[dev] = bytes;
+      bytes = g_high_water[dev];
+    }
   }
   e = hipMallocFromPoolAsync(ptr, bytes, pool, c.stream);
   if (e != hipSuccess) {

@@ -37,14 +37,20 @@
  *     small remainder may do this for the remainder's tiles only (dense
  *     per-tile blocks of the workspace, S * tiles * BM * BN floats), after
  *     the whole rounds.
- *   - Stream-K (fp32, the 64x64 tile): when a call's 64x64 tiles fill two
- *     whole rounds of the CUs and leave at most half a round more, the whole
- *     rounds' tiles run whole while the remainder's K steps are dealt out
- *     evenly, in runs that may span tiles, to one more workgroup per CU in
- *     the same launch (the "Stream-K" decomposition that the SGEMM summary's
- *     results section names).  A tile so shared is summed from its parts'
- *     fp32 partial sums, in K order, by a second pass that also applies
- *     alpha and beta (2 * CUs * 64 * 64 * 4 bytes of workspace).
+ *   - Stream-K (fp32): when the tiles a call takes leave the last round of
+ *     the CUs partly filled -- 64x64 tiles past two whole rounds with at most
+ *     half a round more; 256x256 tiles wherever there is a round of them and
+ *     97% of their area lies inside the matrix; 128x128 tiles over 2 to 7
+ *     rounds (up to 16 where the size rules pick that tile anyway) with a
+ *     quarter to seven eighths of a round more; the 256x128 tile whenever it
+ *     is picked; for the larger tiles 1024 <= K <= 2 max(M, N) --
+ *     the whole rounds' tiles run whole while the remainder's K steps are
+ *     dealt out evenly, in runs that may span two tiles, to one more
+ *     workgroup per CU in the same launch (the "Stream-K" decomposition that
+ *     the SGEMM summary's results section names).  A tile so shared is
+ *     summed from its parts' fp32 partial sums, in K order, by a second pass
+ *     that also applies alpha and beta (two fp32 tile blocks of workspace per
+ *     Stream-K workgroup: 8, 32, 64 or 128 MiB by tile).
  *   - Operand copies (fp32): when the rows of A or B do not allow 16-byte
  *     loads (ld not a multiple of 4, or a base not 16-byte aligned) and the
  *     call does at least 5e9 flops, or 1.5e9 with N a multiple of 4, that
@@ -67,9 +73,10 @@
  *     Stream-K workgroup; at most 1 GiB, larger splits are not taken) and takes it from a memory pool the library creates per device,
  *     with stream-ordered allocation on the call's stream, returning it to
  *     the pool, in stream order, after its last kernel.  Requests are made at
- *     the largest size used so far on the device (2 MiB steps) so that freed
- *     blocks are reused; the pool keeps up to 256 MiB of freed blocks and
- *     hands the rest back to the runtime at the next synchronisation.
+ *     the largest size used so far on the device up to 256 MiB (2 MiB
+ *     steps), so that freed blocks are reused, and larger ones at their own
+ *     size; the pool keeps up to 256 MiB of freed blocks and hands the rest
+ *     back to the runtime at the next synchronisation.
  *     Operand copies (above) take rows*ceil(cols/v)*16 bytes each (v = 4
  *     floats or 8 halves per 16 bytes) from the same allocation as the
  *     split.  gemm_set_workspace_limit caps the workspace of a call.  If the
@@ -361,13 +368,15 @@ int gemm_set_tail_split(int mode);
 int gemm_set_pack(int mode);
 
 /*
- * Diagnostic switch for tests (fp32 calls that take the 64x64 tile whole):
- * 0 = decide by problem size whether they run Stream-K (the default; see
- * "Stream-K" above); 1 = never; 2, 3, 4 = always, every tile's K steps dealt
- * out to 1, 2 or 3 workgroups per CU; 5, 6 = always, the whole rounds of one
- * tile per CU first and the other tiles' K steps dealt out to 1 or 2 more
- * workgroups per CU (5 is the by-size choice).  Calls whose workspace cannot
- * be had run the plain launch.  Process-wide, like gemm_set_load_mode.
+ * Diagnostic switch for tests (fp32): 0 = decide by problem size whether a
+ * call runs Stream-K (the default; see "Stream-K" above); 1 = never; with
+ * the 64x64 four-wave tile taken whole, or a tile forced by
+ * gemm_set_tile_config (1, 5, 6 or 7), 2, 3, 4 = always, every tile's K
+ * steps dealt out to 1, 2 or 3 workgroups per CU (in runs of at most one
+ * tile's steps: more workgroups where the share would be longer); 5, 6 =
+ * always, the whole rounds of one tile per CU first and the other tiles' K
+ * steps dealt out to 1 or 2 more workgroups per CU (5 is the by-size
+ * choice).  Calls whose workspace cannot be had run the plain launch.  Process-wide, like gemm_set_load_mode.
  * Returns the previous setting, or -1 for an unknown value.
  */
 int gemm_set_stream_k(int mode);

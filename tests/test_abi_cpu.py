@@ -303,10 +303,13 @@ def test_tile_table_choice_and_override():
     assert "128x128x16" in name("f32", 2304) and "split-K 3" in name("f32", 2304)
     assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
     assert "split" not in name("f16", 1536)
-    assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 5120)
-    # the last round of 5120^3 (1600 tiles: 6 rounds + 64) runs split
-    assert "last round split-K 4" in name("f32", 5120) and "split" not in name("f32", 8192)
-    assert "256x256x32" in name("f32", 8192) and "256x128x32" in name("f32", 6400)
+    assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 4480)
+    # the last round of 2944^3 (529 tiles: 2 rounds + 17) runs split; 5120^3
+    # takes the 256x256 tile (400 tiles) with Stream-K after its first round
+    # (test_stream_k_by_size_and_switches)
+    assert "last round split-K 15" in name("f32", 2944) and "split" not in name("f32", 8192)
+    assert "256x256x32" in name("f32", 5120) and "stream-K after 256 whole tiles" in name("f32", 5120)
+    assert "256x256x32" in name("f32", 8192) and "256x128x32" in name("f32", 7808)
     assert "256x256x64" in name("f16", 4096) and "256x256x64" in name("f16", 3072)
     # the large fp16 tile: 16x16x32 blocks when its workgroups fill the CUs,
     # 32x32x16 blocks when part of the chip idles (the clock then stays high)
@@ -470,7 +473,7 @@ def test_tail_split_in_descriptions():
     """The plan names the split of the last round when the model takes it,
     and the diagnostic switch turns it off or forces it."""
     import dense_gemm_fp32_amd as dg
-    n = 4608
+    n = 5504
     args = (n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
     rc, text = dg.gemm_describe("f32", *args)
     assert rc == 0 and "last round split-K" in text, text
@@ -534,12 +537,15 @@ def test_workspace_limit_switch():
 
 
 def test_stream_k_by_size_and_switches():
-    """Calls on the four-wave 64x64 tile with two whole rounds of tiles and
-    at most half a round more run Stream-K behind the whole rounds, with two
-    64x64 fp32 blocks of workspace per Stream-K workgroup (one per CU); other
-    sizes, other tiles and calls whose workspace cannot hold the blocks run
-    the plain launch.  The switch forces each decomposition, and refuses
-    unknown modes."""
+    """Stream-K behind the whole rounds, with two fp32 tile blocks of
+    workspace per Stream-K workgroup (one per CU): the four-wave 64x64 tile
+    with two whole rounds and at most half a round more; the 128x128 tile
+    with two to seven rounds and a leftover of a quarter to seven eighths of
+    a round, in place of any choice, and up to sixteen rounds in place of
+    that tile; the 256x128 and 256x256 tiles with a round partly filled, in
+    place of themselves.  Other sizes, deep K, and calls whose workspace
+    cannot hold the blocks run without it.  The switch forces each
+    decomposition, and refuses unknown modes."""
     import dense_gemm_fp32_amd as dg
 
     def d(M, N, K, lda=None, ldb=None, ldc=None):
@@ -577,15 +583,81 @@ def test_stream_k_by_size_and_switches():
         assert "stream-K after 512" in d(1536, 1536, 1536)
     finally:
         dg.gemm_set_workspace_limit(prev)
+    # the 128x128 tile: two to sixteen rounds of its tiles, a leftover of a
+    # quarter to seven eighths of the CUs, K >= 1024.  3840^3: 900 tiles, 768
+    # whole, 132 left, in runs of 124 of their 240 K steps over 256 workgroups
+    t = d(3840, 3840, 3840)
+    assert "128x128x16 4 waves 3 slots loads" in t and "stream-K after 768 whole tiles" in t, t
+    assert "blocks 1024 " in t and ws(t) == 256 * 2 * 128 * 128 * 4, t
+    # ... in place of a K split (3328^3, the 256x128 tile split 3) or the
+    # larger tiles (3840^3) up to seven rounds of 128x128 tiles; from seven
+    # to sixteen only in place of the 128x128 tile itself (6016^3)
+    for n in (3072, 3328, 3840, 5248, 6016, 7040):
+        assert "128x128x16" in d(n, n, n) and "stream-K after" in d(n, n, n), n
+    # the 256x256 tile, wherever it has a round of tiles and at least 97% of
+    # their area lies inside the matrix: 6400^3 (625 tiles, 512 whole),
+    # 9344^3 (36.5 tiles a side: 97.3%), 4352^3; not at 7296^3 (28.5 a
+    # side: 96.5%) nor under one round (3840^3: 225 tiles); plain with whole
+    # rounds (8192^3, 12288^3)
+    # (6400^3: the 113 leftover tiles' 200 K steps each, 22600 in all, in
+    # runs of 89 over 254 workgroups)
+    t = d(6400, 6400, 6400)
+    assert "256x256x32" in t and "stream-K after 512 whole tiles" in t and "blocks 766 " in t, t
+    assert ws(t) == 254 * 2 * 256 * 256 * 4, t
+    for n in (4352, 9344, 10752, 12800):
+        assert "256x256x32" in d(n, n, n) and "stream-K after" in d(n, n, n), n
+    assert "256x256x32" not in d(7296, 7296, 7296) and "256x256x32" not in d(3840, 3840, 3840)
+    for n in (8192, 12288):
+        assert "256x256x32" in d(n, n, n) and "stream-K" not in d(n, n, n), n
+    # the 256x128 tile, plain or with the last round split, takes Stream-K on
+    # the same tile when a round is partly filled (7808^3: 30.5 256x256
+    # tiles a side would be 96.7% inside)
+    t = d(7808, 7808, 7808)
+    assert "256x128x32" in t and "stream-K after 1792 whole tiles" in t, t
+    assert ws(t) == 255 * 2 * 256 * 128 * 4, t
+    # where the workspace cannot hold the partial blocks, the model's own
+    # choice: 7808^3's last round split, 6400^3 whole on the 256x128 tile
+    prev = dg.gemm_set_workspace_limit(60 << 20)
+    try:
+        t = d(7808, 7808, 7808)
+        assert "256x128x32" in t and "last round split-K" in t and "stream-K" not in t, t
+        t = d(6400, 6400, 6400)
+        assert "256x128x32" in t and "split" not in t and "stream-K" not in t, t
+    finally:
+        dg.gemm_set_workspace_limit(prev)
+    # 128x128 tiles with a leftover under a quarter (2944^3: 17 tiles) or
+    # over seven eighths (4992^3: 241), whole rounds of 256x256 tiles
+    # (4096^3), K under 1024, rows without 16-byte loads: no Stream-K
+    for n in (2944, 4096, 4992):
+        assert "stream-K" not in d(n, n, n), n
+    assert "stream-K" not in d(3840, 3840, 1000)
+    # deep K keeps the model's K split
+    t = d(3000, 3000, 30000)
+    assert "stream-K" not in t and "split-K" in t, t
+    assert "stream-K after 512" in d(3000, 3000, 6000)
+    # unaligned rows: copied (and then Stream-K on the copies), or, with
+    # copies off, the register-staged path's own rule
+    t = d(3840, 3840, 3840, 3841, 3841, 3840)
+    assert "copies A B" in t and "stream-K after 768" in t, t
+    pack = dg.gemm_set_pack(1)
+    try:
+        assert "stream-K" not in d(3840, 3840, 3840, 3841, 3841, 3840)
+    finally:
+        dg.gemm_set_pack(pack)
     # the switch
     prev = dg.gemm_set_stream_k(1)
     try:
         assert prev == 0
         assert "stream-K" not in d(1536, 1536, 1536)
-        # every tile's K steps: 400 tiles x 40 steps over 256 workgroups
-        assert dg.gemm_set_stream_k(2) == 1
+        assert "stream-K" not in d(3840, 3840, 3840)
+        # every tile's K steps: 400 tiles x 40 steps, in runs of 32 over 500
+        # workgroups (two per CU asked for) ...
+        assert dg.gemm_set_stream_k(3) == 1
         t = d(1280, 1280, 1280)
-        assert "stream-K" in t and "whole tiles" not in t and "blocks 254 " in t, t
+        assert "stream-K" in t and "whole tiles" not in t and "blocks 500 " in t, t
+        # ... and with one per CU asked for, runs capped at one tile's steps
+        dg.gemm_set_stream_k(2)
+        assert "blocks 400 " in d(1280, 1280, 1280)
         # ... and with one round whole first (1024^3 has nothing left: plain)
         dg.gemm_set_stream_k(5)
         assert "stream-K after 256 whole tiles" in d(1280, 1280, 1280)

@@ -984,11 +984,12 @@ def test_tail_split_matches_oracle(case, S):
 
 
 def test_tail_split_chosen_by_size():
-    """A size whose last round the model splits (4608^3 on the 128x128
-    tile) matches the oracle on sampled rows that include the last tile
-    rows (where the leftover tiles of the grouped order lie)."""
+    """A size whose last round the model splits (5504^3 on the 128x128
+    tile: 1849 tiles, 7 rounds and 57 left) matches the oracle on sampled
+    rows that include the last tile rows (where the leftover tiles of the
+    grouped order lie)."""
     import dense_gemm_fp32_amd as dg
-    n = 4608
+    n = 5504
     rc, plan = dg.gemm_describe("f32", n, n, n, 1.0, 0x10000, n, 0x10000, n, 1.0, 0x10000, n)
     assert rc == 0 and "last round split-K" in plan, plan
     from gemm_harness import layout_case
@@ -1000,7 +1001,7 @@ def test_tail_split_chosen_by_size():
                        B.reshape(-1), n, 1.0, np.ascontiguousarray(C[rows]).reshape(-1), n, "f32")
     tol = oracle.tolerance(G, np.abs(C[rows].astype(np.float64)), 1.0, 1.0, n, R, oracle.out_type("f32"))
     ok, worst, where = oracle.compare(np.ascontiguousarray(wl.view(out, n, n, n)[rows]), R, tol)
-    assert ok, "4608^3 last-round split: worst %.3g at %s" % (worst, where)
+    assert ok, "5504^3 last-round split: worst %.3g at %s" % (worst, where)
 
 
 def test_concurrent_streams_and_threads_share_the_workspace_pool():
@@ -1397,6 +1398,80 @@ def test_stream_k_every_mode_matches_oracle(layout):
             ok, worst, where = oracle.compare(gpu, R, tol)
             assert ok, "%s (%s): worst |err|/tol %.3g at %s" % (label, plan, worst, where)
             assert_pads_unchanged(outs[0], Cbuf, M, N, ldc, "f32")
+
+
+# tile configuration -> (M, N, K, pad_a, pad_b, pad_c, beta) cases: one grid
+# over a round of that tile's tiles (whole tiles first in modes 5, 6), one
+# under it
+STREAMK_TILE_CASES = {
+    6: [(4300, 4400, 333, 0, 0, 0, 0.5), (900, 1300, 515, 0, 0, 1, 0.0)],   # 256x256
+    1: [(4300, 2200, 700, 0, 4, 0, -0.75), (1500, 700, 260, 0, 0, 0, 1.0)],  # 256x128
+    5: [(2200, 2200, 1000, 0, 0, 3, 0.0), (900, 1300, 515, 4, 0, 0, 0.5)],   # 128x128
+}
+
+
+@pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
+@pytest.mark.parametrize("cfg", [6, 1, 5], ids=["256x256", "256x128", "128x128"])
+def test_stream_k_large_tiles_every_mode_matches_oracle(cfg, layout):
+    """Stream-K on the 256x256, 256x128 and 128x128 tiles, in every mode
+    and layout, against the oracle element by element: runs of one K step up
+    to a whole tile, partial K steps, ragged edges, C rows not 16-byte
+    aligned, beta = 0 over a NaN C, pads untouched."""
+    import dense_gemm_fp32_amd as dg
+    from gemm_harness import layout_case, run_layout
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    for idx, (M, N, K, pa, pb, pc, beta) in enumerate(STREAMK_TILE_CASES[cfg]):
+        lda = (M if ta else K) + pa
+        ldb = (K if tb else N) + pb
+        ldc = N + pc
+        Abuf, Bbuf, Cbuf, A, B, C = layout_case("f32", M, N, K, ta, tb, lda, ldb, ldc,
+                                                 950 + 10 * cfg + idx)
+        if beta == 0.0:
+            Cbuf = wl.pad(np.full((M, N), np.nan, np.float32), ldc, wl.C_PAD_SENTINEL)
+        R, G = oracle.gemm(M, N, K, 1.25, A.reshape(-1), K, B.reshape(-1), N, beta,
+                           np.ascontiguousarray(C).reshape(-1) if beta != 0 else None, N, "f32")
+        Cv = C.astype(np.float64) if beta != 0 else 0.0
+        tol = oracle.tolerance(G, np.abs(Cv), 1.25, beta, K, R, oracle.out_type("f32"))
+        for mode in (2, 3, 4, 5, 6):
+            label = "stream-K cfg %d mode %d %s %dx%dx%d" % (cfg, mode, layout, M, N, K)
+            with stream_k(mode), tile_config(cfg):
+                rc, plan = dg.gemm_describe("f32", M, N, K, 1.25, 4096, K + pa, 4096, N + pb, beta,
+                                            4096, ldc)
+                assert rc == 0 and "stream-K" in plan, plan
+                if layout == "nn":
+                    rc, out = run("f32", M, N, K, 1.25, Abuf, lda, Bbuf, ldb, beta, Cbuf, ldc, label)
+                else:
+                    rc, out = run_layout("f32", layout, M, N, K, 1.25, Abuf, lda, Bbuf, ldb, beta,
+                                         Cbuf, ldc, label)
+            assert rc == 0, rc
+            ok, worst, where = oracle.compare(wl.view(out, M, N, ldc), R, tol)
+            assert ok, "%s (%s): worst |err|/tol %.3g at %s" % (label, plan, worst, where)
+            assert_pads_unchanged(out, Cbuf, M, N, ldc, "f32")
+
+
+def test_stream_k_128x128_chosen_by_size_full_oracle():
+    """3840^3 (beta = 1), where the size rule runs 768 128x128 tiles whole and
+    the last 132 tiles' K steps Stream-K, against the full oracle."""
+    w = wl.sweep(3840)
+    plan = _plan(w)
+    assert "128x128x16" in plan and "stream-K after 768 whole tiles" in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
+@pytest.mark.parametrize("shape,tile,whole", [((5632, 5632, 5632), "256x256x32", 256),
+                                              ((5120, 3200, 2048), "256x128x32", 256)])
+def test_stream_k_large_tiles_chosen_by_size_full_oracle(shape, tile, whole):
+    """Calls (beta = 1) whose 256x256 (5632^3: 484 tiles) or 256x128 (5120 x
+    3200 x 2048: 500 tiles) tiles leave a round partly filled: the whole
+    rounds run whole and the leftover tiles' K steps Stream-K on the same
+    tile; every element against the oracle."""
+    M, N, K = shape
+    w = wl.sweep(M) if M == N == K else wl.Workload(
+        "streamk_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform", "uniform",
+        (81, 82, 83))
+    plan = _plan(w)
+    assert tile in plan and "stream-K after %d whole tiles" % whole in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
 def test_stream_k_element_wise_loads_same_bits():
