@@ -1493,6 +1493,28 @@ static F32Choice choose_f32(const Call &c) {
   // Spread loads pay while a CU holds one workgroup; with several resident
   // the others hide the load bursts and issuing them together is cheaper.
   if (best.cfg == F32Cfg::kMid && tiles_of<F32Mid>(c) * best.splits > kCUs) best.cfg = F32Cfg::kMidB;
+  // Grids of 170 to 255 64x64 tiles (two thirds of a round to just under
+  // one) with K <= 1.5 max(M, N): the 64x64 tile of four 32x32 waves,
+  // unsplit, in place of the 32x32 tile when that tile would put a fourth
+  // workgroup on some CUs, and in place of a K split when K <= 1536.
+  // Measured (interleaved, a 512 MiB flush before each call, beta 1,
+  // TFLOP/s, the choice before -> this): 896^3 (the 32x32 tile, 784 of
+  // them) 39.9 -> 51.0, 928^3 42.9 -> 52.4, 960^3 46.2 -> 59.1, 600 x 1600 x
+  // 800 45.0 -> 56.9, 800x1200x1000 44.8 -> 57.9, 1024x768x1024 (the 128x128
+  // tile split 4) 41.4 -> 51.6, 1000x700x1200 (split 4) 38.4 -> 45.4, 960 x
+  // 1024 x 1400 (split 4) 55.6 -> 67.6, 1500x500x1500 (split 5) 49.9 ->
+  // 51.7.  With at most three 32x32 tiles per CU that tile stays ahead
+  // (864^3 48.8 against 44.7, 832^3 45.2 against 43.2), and so does the K
+  // split for longer K (2048x384x2048 67.9 against 60.4, 768x1024x2048 67.4
+  // against 60.8, 896x896x3000 81.4 against 65.2).
+  if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
+    const long long q = tiles_of<F32Quad>(c);
+    const long long mx = c.M > c.N ? c.M : c.N;
+    if (q >= 170 && q < kCUs && 2LL * c.K <= 3 * mx &&
+        ((best.cfg == F32Cfg::kTiny && tiles_of<F32Tiny>(c) > 3LL * kCUs) ||
+         (best.splits > 1 && c.K <= 1536)))
+      return F32Choice{F32Cfg::kQuad, 1, best.time, 1};
+  }
   return streamk_instead(c, best);
 }
 

@@ -392,8 +392,36 @@ def test_wide_short_problems_take_the_four_wave_64x64_tile():
         assert "64x64x32 4 waves" in t and "split" not in t, (shape, t)
     assert "64x64x32 4 waves" not in d(1000, 8000, 700)    # 2000 tiles: over three per CU
     assert "64x64x32 4 waves" not in d(1024, 1024, 4096)   # deep K: the 128x128 tile in chunks
-    t = d(2048, 384, 2048)                                 # 192 tiles: fewer than the CUs
+    t = d(2048, 384, 2048)                                 # 192 tiles, K 2048: the split stays
     assert "128x128x16" in t and "split-K" in t, t
+
+
+def test_grids_under_one_round_take_the_four_wave_64x64_tile():
+    """Grids of 170 to 255 64x64 tiles with K <= 1.5 max(M, N) take that tile
+    with four 32x32 waves, unsplit, where the model would put a fourth 32x32
+    workgroup on some CUs or split K at K <= 1536; with at most three 32x32
+    tiles per CU, fewer 64x64 tiles, or longer K the model's choice stands."""
+    import dense_gemm_fp32_amd as dg
+    def d(M, N, K):
+        return dg.gemm_describe("f32", M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
+    for shape in [(896, 896, 896), (928, 928, 928), (960, 960, 960), (600, 1600, 800),
+                  (800, 1200, 1000), (1024, 768, 1024), (1000, 700, 1200), (960, 1024, 1400)]:
+        t = d(*shape)
+        assert "64x64x32 4 waves" in t and "split" not in t, (shape, t)
+    # 864^3: 729 32x32 tiles, at most three per CU; 832^3: 169 64x64 tiles
+    for n in (864, 832, 768):
+        assert "32x32x32" in d(n, n, n), n
+    # longer K keeps the K split
+    for shape in [(2048, 384, 2048), (768, 1024, 2048), (896, 896, 3000)]:
+        t = d(*shape)
+        assert "128x128x16" in t and "split-K" in t, (shape, t)
+    # the switches that force a split or disable the last-round split leave
+    # the model's choice
+    prev = dg.gemm_set_tail_split(1)
+    try:
+        assert "32x32x32" in d(896, 896, 896)
+    finally:
+        dg.gemm_set_tail_split(prev)
 
 
 def test_split_choice_and_override():
