@@ -166,7 +166,8 @@ def gemm_set_tile_config(config):
     large/medium/small/tiny configuration (fp16 maps 4 to small); 5 = fp32
     medium with loads issued together; 6 = fp32 256x256 (fp16 large on
     32x32x16 blocks); 7 = fp32 64x64 with four waves (fp16 small); 8 = fp32
-    128x64 with four waves (fp16 medium)."""
+    128x64 with four waves (fp16 medium); 9 = fp32 64x64 with four waves in
+    64-k steps (fp16 small)."""
     return _lib.gemm_set_tile_config(int(config))
 
 

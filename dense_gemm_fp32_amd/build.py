@@ -117,6 +117,7 @@ TILE_OCCUPANCY = (
     ("S32TileILi128ELi128ELi16ELi2ELi2ELi3ELi8ELb1E", 1, 4),
     ("S32TileILi128ELi128ELi16ELi2ELi2ELi3ELi8ELb0E", 3, 4),
     ("S32TileILi128ELi64ELi32E", 2, 4),
+    ("S32TileILi64ELi64ELi64ELi2ELi2ELi2E", 2, 4),
     ("S32TileILi64ELi64ELi32ELi2ELi2E", 3, 4),
     ("S32TileILi64ELi64ELi32ELi1ELi1E", 3, 1),
     ("S32TileILi32ELi32ELi32E", 6, 1),

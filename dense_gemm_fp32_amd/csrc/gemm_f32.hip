@@ -991,6 +991,7 @@ typedef S32Tile<128, 128, 16, 2, 2, 3, 8> F32MidB;       // the same, loads issu
 typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 WG/CU
 typedef S32Tile<64, 64, 32, 2, 2, 3, 8> F32Quad;      // 4 waves of 32x32, 48 KB LDS, 3 WG/CU
 typedef S32Tile<128, 64, 32, 2, 2, 3, 8> F32Half;     // 4 waves of 64x32, 72 KB LDS, 2 WG/CU
+typedef S32Tile<64, 64, 64, 2, 2, 2, 8> F32QuadK;   // the same in 64-k steps, 64 KB LDS, 2 WG/CU
 typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
@@ -1106,7 +1107,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad, kHalf };
+enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad, kHalf, kQuadK };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
@@ -1415,6 +1416,7 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 7)
     return F32Choice{F32Cfg::kQuad, forced, 0.0, tail, forced == 1 && tail == 1 ? streamk_of(c) : 0};
   if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
+  if (c.tile_config == 9) return F32Choice{F32Cfg::kQuadK, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
       tiles_of<F32Mid>(c) < 3LL * kCUs)
     return choose_staged(c);
@@ -1435,11 +1437,23 @@ static F32Choice choose_f32(const Call &c) {
   // 99-100 TFLOP/s, 1920^3 110 -> 114-116, 2048^3 124-125 -> 130-131,
   // 1800x1900x2000 95-97 -> 101-104, 1024x4096x1024 116-119 -> 120-124,
   // 4096x1024x2048 +3-4%, 2048x2048x512 +5%, 2560x1280x1280 +2%.
+  // Up to two 64x64 tiles per CU the tile runs in 64-k steps through two LDS
+  // slots (64 KB, so two of its workgroups share a CU): half the steps, and
+  // half the barriers, per tile.  Measured (interleaved, a 512 MiB flush
+  // before each call, beta 1, TFLOP/s, 32-k steps in three slots -> this):
+  // 1024^3 68.0 -> 73.9, 1000^3 59.9 -> 64.0, 1024x1024x2048 80.2 -> 89.3,
+  // 1152^3 63.9 -> 65.8, 1280^3 80.2 -> 82.1, 1408^3 97.5 -> 100.7, 896^3
+  // 51.0 -> 55.3; past two per CU the third workgroup no longer fits and
+  // three 32-k slots stay ahead (1664^3 104.9 against 98.8), as did 64-k
+  // steps in three slots (one workgroup per CU: 1024^3 71.5, 1408^3 81.7).
   if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
     const long long q = tiles_of<F32Quad>(c), h = tiles_of<F32Half>(c);
     const long long mx = c.M > c.N ? c.M : c.N;
     if ((long long)c.K <= 2 * mx) {
-      if (q >= kCUs && q <= 3LL * kCUs) return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, streamk_of(c)};
+      if (q >= kCUs && q <= 3LL * kCUs) {
+        const int sk = streamk_of(c);
+        return F32Choice{sk == 0 && q <= 2LL * kCUs ? F32Cfg::kQuadK : F32Cfg::kQuad, 1, 0.0, 1, sk};
+      }
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
     }
   }
@@ -1513,7 +1527,7 @@ static F32Choice choose_f32(const Call &c) {
     if (q >= 170 && q < kCUs && 2LL * c.K <= 3 * mx &&
         ((best.cfg == F32Cfg::kTiny && tiles_of<F32Tiny>(c) > 3LL * kCUs) ||
          (best.splits > 1 && c.K <= 1536)))
-      return F32Choice{F32Cfg::kQuad, 1, best.time, 1};
+      return F32Choice{F32Cfg::kQuadK, 1, best.time, 1};
   }
   return streamk_instead(c, best);
 }
@@ -1749,6 +1763,7 @@ static const char *f32_name(F32Cfg cfg) {
     case F32Cfg::kSmall: return "f32 mfma32x32x2 tile 64x64x32 1 wave 3 slots";
     case F32Cfg::kQuad: return "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots";
     case F32Cfg::kHalf: return "f32 mfma32x32x2 tile 128x64x32 4 waves 3 slots";
+    case F32Cfg::kQuadK: return "f32 mfma32x32x2 tile 64x64x64 4 waves 2 slots";
     default: return "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots";
   }
 }
@@ -1774,6 +1789,7 @@ static Plan plan_f32_as_is(const Call &c) {
     case F32Cfg::kSmall: return plan_cfg<F32Small>(c, name, ch.splits, ch.tail);
     case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, name, ch.splits, ch.tail);
     case F32Cfg::kHalf: return plan_cfg<F32Half>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kQuadK: return plan_cfg<F32QuadK>(c, name, ch.splits, ch.tail);
     default: return plan_cfg<F32Tiny>(c, name, ch.splits, ch.tail);
   }
 }
@@ -1798,6 +1814,7 @@ static hipError_t launch_f32_as_is(const Call &c) {
     case F32Cfg::kSmall: return launch_cfg<F32Small>(c, ch.splits, ch.tail);
     case F32Cfg::kQuad: return launch_cfg<F32Quad>(c, ch.splits, ch.tail);
     case F32Cfg::kHalf: return launch_cfg<F32Half>(c, ch.splits, ch.tail);
+    case F32Cfg::kQuadK: return launch_cfg<F32QuadK>(c, ch.splits, ch.tail);
     default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }

@@ -291,10 +291,14 @@ def test_tile_table_choice_and_override():
     # 1.5 to 2 128x64 tiles per CU (past three 64x64 ones): the four-wave 128x64 tile
     for n in (1792, 1920, 2048):
         assert "128x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
-    # one to three 64x64 tiles per CU: that tile with four 32x32 waves, unsplit
-    for n in (1024, 1280, 1536, 1664):
-        assert "64x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
-    assert "64x64x32 4 waves" not in name("f32", 1792) and "64x64x32 4 waves" not in name("f32", 768)
+    # one to three 64x64 tiles per CU: that tile with four 32x32 waves,
+    # unsplit; up to two per CU in 64-k steps through two slots
+    for n in (1024, 1280):
+        assert "64x64x64 4 waves 2 slots" in name("f32", n) and "split" not in name("f32", n), n
+    for n in (1536, 1664):
+        assert "64x64x32 4 waves 3 slots" in name("f32", n) and "split" not in name("f32", n), n
+    for n in (1792, 768):
+        assert "64x64x32 4 waves" not in name("f32", n) and "64x64x64" not in name("f32", n), n
     assert "32x32x32" in name("f32", 256) and "32x32x32" in name("f32", 64)
     assert "split" not in name("f32", 256) and "split" not in name("f32", 768)
     # K split where the grid leaves CUs idle and K is long enough
@@ -329,9 +333,11 @@ def test_tile_table_choice_and_override():
         assert "64x64x32 4 waves" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
         dg.gemm_set_tile_config(8)
         assert "128x64x32 4 waves" in name("f32", 4096) and "128x128x32" in name("f16", 4096)
+        dg.gemm_set_tile_config(9)
+        assert "64x64x64 4 waves 2 slots" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
     finally:
         dg.gemm_set_tile_config(prev)
-    assert dg.gemm_set_tile_config(9) == -1 and dg.gemm_set_tile_config(-1) == -1
+    assert dg.gemm_set_tile_config(10) == -1 and dg.gemm_set_tile_config(-1) == -1
 
 
 def test_staged_calls_split_the_medium_tile():
@@ -389,9 +395,12 @@ def test_wide_short_problems_take_the_four_wave_64x64_tile():
     for shape in [(517, 3000, 1000), (256, 8192, 1024), (128, 16384, 4096), (384, 3000, 600),
                   (256, 4096, 2048), (1000, 3000, 520), (1000, 1000, 1000)]:
         t = d(*shape)
-        assert "64x64x32 4 waves" in t and "split" not in t, (shape, t)
-    assert "64x64x32 4 waves" not in d(1000, 8000, 700)    # 2000 tiles: over three per CU
-    assert "64x64x32 4 waves" not in d(1024, 1024, 4096)   # deep K: the 128x128 tile in chunks
+        q = ((shape[0] + 63) // 64) * ((shape[1] + 63) // 64)
+        # up to two tiles per CU in 64-k steps (two slots), else 32-k steps
+        tile = "64x64x64 4 waves 2 slots" if q <= 512 else "64x64x32 4 waves 3 slots"
+        assert tile in t and "split" not in t, (shape, t)
+    assert "64x64x" not in d(1000, 8000, 700)              # 2000 tiles: over three per CU
+    assert "64x64x" not in d(1024, 1024, 4096)             # deep K: the 128x128 tile in chunks
     t = d(2048, 384, 2048)                                 # 192 tiles, K 2048: the split stays
     assert "128x128x16" in t and "split-K" in t, t
 
@@ -407,7 +416,7 @@ def test_grids_under_one_round_take_the_four_wave_64x64_tile():
     for shape in [(896, 896, 896), (928, 928, 928), (960, 960, 960), (600, 1600, 800),
                   (800, 1200, 1000), (1024, 768, 1024), (1000, 700, 1200), (960, 1024, 1400)]:
         t = d(*shape)
-        assert "64x64x32 4 waves" in t and "split" not in t, (shape, t)
+        assert "64x64x64 4 waves 2 slots" in t and "split" not in t, (shape, t)
     # 864^3: 729 32x32 tiles, at most three per CU; 832^3: 169 64x64 tiles
     for n in (864, 832, 768):
         assert "32x32x32" in d(n, n, n), n

@@ -74,16 +74,17 @@ def test_headline_4096_every_element(w):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n,tile,whole", [(1152, "64x64x32 4 waves", 0),
-                                          (1408, "64x64x32 4 waves", 0),
+@pytest.mark.parametrize("n,tile,whole", [(1152, "64x64x64 4 waves 2 slots", 0),
+                                          (1408, "64x64x64 4 waves 2 slots", 0),
                                           (1536, "64x64x32 4 waves", 512),
                                           (1664, "64x64x32 4 waves", 0),
                                           (1792, "128x64x32 4 waves", 0),
                                           (1920, "128x64x32 4 waves", 0)])
 def test_f32_sweep_four_wave_tile_full_oracle(n, tile, whole):
     """Sweep sizes (beta = 1) whose plan is a four-wave tile, K unsplit: the
-    64x64 tile of 32x32 waves (one to three tiles per CU) or the 128x64 tile
-    of 64x32 waves (1.5 to 2 per CU), every element against the oracle.
+    64x64 tile of 32x32 waves (one to three tiles per CU; up to two per CU
+    in 64-k steps) or the 128x64 tile of 64x32 waves (1.5 to 2 per CU),
+    every element against the oracle.
     1536^3 (576 tiles) leaves a small third round, whose K steps run
     Stream-K behind 512 whole tiles."""
     w = wl.sweep(n)
@@ -123,7 +124,7 @@ def test_f32_under_one_round_four_wave_tile_full_oracle(shape):
     w = wl.Workload("quad_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform",
                     "uniform", (91, 92, 93))
     plan = _plan(w)
-    assert "64x64x32 4 waves" in plan and "split" not in plan, plan
+    assert "64x64x64 4 waves 2 slots" in plan and "split" not in plan, plan
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
@@ -461,9 +462,10 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8],
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9],
                          ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256",
-                              "f32-64x64-four-waves", "f32-128x64-four-waves"])
+                              "f32-64x64-four-waves", "f32-128x64-four-waves",
+                              "f32-64x64-four-waves-k64"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -515,7 +517,7 @@ from hypothesis import HealthCheck, given, settings, strategies as st
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
        beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6, 7, 8]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6, 7, 8, 9]),
        pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
 def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, pack, seed):
@@ -656,7 +658,7 @@ def test_split_k_deterministic_and_paths_agree(dtype):
     assert np.array_equal(bits(o1, dtype), bits(o2, dtype))
     assert np.array_equal(bits(o1, dtype), bits(o3, dtype))
     check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o1, "split det")
-    for cfg in (1, 2, 3, 4, 6):
+    for cfg in (1, 2, 3, 4, 6, 9):
         with split_mode(3), tile_config(cfg):
             rc, o = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split cfg%d" % cfg)
         assert rc == 0
@@ -871,7 +873,7 @@ def test_layouts_match_oracle(dtype, layout):
         _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7, 8])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7, 8, 9])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_layouts_every_tile(dtype, layout, cfg):
@@ -1083,7 +1085,7 @@ def test_concurrent_streams_and_threads_share_the_workspace_pool():
        M=st.integers(1, 300), N=st.integers(1, 300), K=st.integers(1, 300),
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        beta=st.sampled_from([0.0, 1.0, -1.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8, 9]),
        split=st.sampled_from([0, 1, 3]),
        pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
