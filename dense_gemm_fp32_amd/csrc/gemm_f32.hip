@@ -1521,6 +1521,16 @@ static F32Choice choose_f32(const Call &c) {
   // (864^3 48.8 against 44.7, 832^3 45.2 against 43.2), and so does the K
   // split for longer K (2048x384x2048 67.9 against 60.4, 768x1024x2048 67.4
   // against 60.8, 896x896x3000 81.4 against 65.2).
+  // Under one round of 64x64 tiles, the same tile (64-k steps) also replaces
+  // an unsplit larger tile that leaves over half the CUs idle, with K <=
+  // max(M, N).  Measured (interleaved, flush before each call, TFLOP/s, the
+  // choice before -> this): 512x1024x256 (the 128x128 tile, 32 of them)
+  // 10.8 -> 20.1, 200x3000x300 9.5 -> 21.2, 64x8192x512 (the 256x128 tile,
+  // 64 of them) 7.6 -> 28.4.  In place of the 32x32 tile at up to three of
+  // those per CU it won and lost by a few percent (512^3 16.2 -> 17.3, 768^3
+  // 39.2 -> 43.2, but 320^3 5.2 -> 4.8, 448^3 11.6 -> 11.1, 800^3 41.6 ->
+  // 38.3), so that tile stays there; deep-K splits stay too (512x512x2048
+  // 29.2 against 23.4).
   if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
     const long long q = tiles_of<F32Quad>(c);
     const long long mx = c.M > c.N ? c.M : c.N;
@@ -1528,6 +1538,14 @@ static F32Choice choose_f32(const Call &c) {
         ((best.cfg == F32Cfg::kTiny && tiles_of<F32Tiny>(c) > 3LL * kCUs) ||
          (best.splits > 1 && c.K <= 1536)))
       return F32Choice{F32Cfg::kQuadK, 1, best.time, 1};
+    if (q < kCUs && best.splits == 1 && best.tail == 1) {
+      long long tb = 0;
+      if (best.cfg == F32Cfg::kMid || best.cfg == F32Cfg::kMidB) tb = tiles_of<F32Mid>(c);
+      else if (best.cfg == F32Cfg::kBig) tb = tiles_of<F32Big>(c);
+      else if (best.cfg == F32Cfg::kHuge) tb = tiles_of<F32Huge>(c);
+      if (tb > 0 && 2 * tb < kCUs && q > tb && (long long)c.K <= mx)
+        return F32Choice{F32Cfg::kQuadK, 1, best.time, 1};
+    }
   }
   return streamk_instead(c, best);
 }

@@ -408,8 +408,10 @@ def test_wide_short_problems_take_the_four_wave_64x64_tile():
 def test_grids_under_one_round_take_the_four_wave_64x64_tile():
     """Grids of 170 to 255 64x64 tiles with K <= 1.5 max(M, N) take that tile
     with four 32x32 waves, unsplit, where the model would put a fourth 32x32
-    workgroup on some CUs or split K at K <= 1536; with at most three 32x32
-    tiles per CU, fewer 64x64 tiles, or longer K the model's choice stands."""
+    workgroup on some CUs or split K at K <= 1536; grids under one round of
+    them, with K <= max(M, N), take it in place of an unsplit larger tile
+    that leaves over half the CUs idle; with at most three 32x32 tiles per
+    CU or longer K the model's choice stands."""
     import dense_gemm_fp32_amd as dg
     def d(M, N, K):
         return dg.gemm_describe("f32", M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)[1]
@@ -424,11 +426,22 @@ def test_grids_under_one_round_take_the_four_wave_64x64_tile():
     for shape in [(2048, 384, 2048), (768, 1024, 2048), (896, 896, 3000)]:
         t = d(*shape)
         assert "128x128x16" in t and "split-K" in t, (shape, t)
+    # an unsplit larger tile that would leave over half the CUs idle, K <=
+    # max(M, N): 512x1024x256 (32 128x128 tiles), 64x8192x512 (64 256x128
+    # tiles), 128x8192x256, 2048x512x256, 200x3000x300
+    for shape in [(512, 1024, 256), (64, 8192, 512), (128, 8192, 256), (2048, 512, 256),
+                  (200, 3000, 300)]:
+        t = d(*shape)
+        assert "64x64x64 4 waves 2 slots" in t and "split" not in t, (shape, t)
+    # small squares keep the 32x32 tile
+    for n in (256, 512, 768):
+        assert "32x32x32" in d(n, n, n), n
     # the switches that force a split or disable the last-round split leave
     # the model's choice
     prev = dg.gemm_set_tail_split(1)
     try:
         assert "32x32x32" in d(896, 896, 896)
+        assert "128x128x16" in d(512, 1024, 256)
     finally:
         dg.gemm_set_tail_split(prev)
 

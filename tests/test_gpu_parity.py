@@ -114,12 +114,14 @@ def test_f16_large_tile_block_shape_by_size_sampled(n, blocks):
     check_sampled(w.dtype, w, A, B, C, out, nrows=16, seed=n, extra_rows=[n - 1, n - 200])
 
 
-@pytest.mark.parametrize("shape", [(896, 896, 896), (1024, 768, 1024), (600, 1600, 800)])
+@pytest.mark.parametrize("shape", [(896, 896, 896), (1024, 768, 1024), (600, 1600, 800),
+                                   (512, 1024, 256), (64, 8192, 512)])
 def test_f32_under_one_round_four_wave_tile_full_oracle(shape):
-    """Grids of 170 to 255 64x64 tiles where the size rule takes that tile
-    with four waves, unsplit, in place of the 32x32 tile (896^3, 600 x 1600
-    x 800) or of a K split (1024 x 768 x 1024): every element against the
-    oracle (beta = 1)."""
+    """Grids under one round of 64x64 tiles where the size rule takes that
+    tile with four waves, unsplit, in place of the 32x32 tile (896^3, 600 x
+    1600 x 800), of a K split (1024 x 768 x 1024) or of a larger tile that
+    would leave most CUs idle (512 x 1024 x 256, 64 x 8192 x 512): every
+    element against the oracle (beta = 1)."""
     M, N, K = shape
     w = wl.Workload("quad_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform",
                     "uniform", (91, 92, 93))
