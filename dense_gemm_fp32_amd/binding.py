@@ -167,7 +167,8 @@ def gemm_set_tile_config(config):
     medium with loads issued together; 6 = fp32 256x256 (fp16 large on
     32x32x16 blocks); 7 = fp32 64x64 with four waves (fp16 small); 8 = fp32
     128x64 with four waves (fp16 medium); 9 = fp32 64x64 with four waves in
-    64-k steps (fp16 small)."""
+    64-k steps (fp16 small); 10 = fp32 32x32, one wave, 64-k steps (fp16
+    small)."""
     return _lib.gemm_set_tile_config(int(config))
 
 

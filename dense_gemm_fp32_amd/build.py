@@ -120,6 +120,7 @@ TILE_OCCUPANCY = (
     ("S32TileILi64ELi64ELi64ELi2ELi2ELi2E", 2, 4),
     ("S32TileILi64ELi64ELi32ELi2ELi2E", 3, 4),
     ("S32TileILi64ELi64ELi32ELi1ELi1E", 3, 1),
+    ("S32TileILi32ELi32ELi64E", 5, 1),
     ("S32TileILi32ELi32ELi32E", 6, 1),
     ("H16TileILi256ELi256ELi64E", 1, 8),
     ("H16TileILi128ELi128ELi32E", 2, 4),

@@ -391,7 +391,7 @@ int gemm_set_tail_split(int mode) {
 }
 
 int gemm_set_tile_config(int config) {
-  if (config < 0 || config > 9) return -1;
+  if (config < 0 || config > 10) return -1;
   return g_tile_config.exchange(config);
 }
 

@@ -1114,7 +1114,7 @@ static F16Choice choose_f16(const Call &c) {
   if (c.tile_config == 1) return F16Choice{F16Cfg::kBig, forced, 0.0};
   if (c.tile_config == 6) return F16Choice{F16Cfg::kBig32, forced, 0.0};
   if (c.tile_config == 2 || c.tile_config == 5) return F16Choice{F16Cfg::kMid, forced, 0.0};
-  if (c.tile_config == 3 || c.tile_config == 4 || c.tile_config == 7 || c.tile_config == 9)
+  if (c.tile_config == 3 || c.tile_config == 4 || c.tile_config == 7 || c.tile_config >= 9)
     return F16Choice{F16Cfg::kSmall, forced, 0.0};
   if (c.tile_config == 8) return F16Choice{F16Cfg::kMid, forced, 0.0};
   const long long mid_tiles = tiles_of<F16Mid>(c);

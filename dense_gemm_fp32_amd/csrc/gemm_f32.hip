@@ -992,6 +992,7 @@ typedef S32Tile<64, 64, 32, 1, 1, 3, 8> F32Small;     // 1 wave,   48 KB LDS, 3 
 typedef S32Tile<64, 64, 32, 2, 2, 3, 8> F32Quad;      // 4 waves of 32x32, 48 KB LDS, 3 WG/CU
 typedef S32Tile<128, 64, 32, 2, 2, 3, 8> F32Half;     // 4 waves of 64x32, 72 KB LDS, 2 WG/CU
 typedef S32Tile<64, 64, 64, 2, 2, 2, 8> F32QuadK;   // the same in 64-k steps, 64 KB LDS, 2 WG/CU
+typedef S32Tile<32, 32, 64, 1, 1, 2, 8> F32TinyK;   // 1 wave, 64-k steps, 32 KB LDS, 5 WG/CU
 typedef S32Tile<32, 32, 32, 1, 1, 3, 8> F32Tiny;      // 1 wave,   24 KB LDS, 6 WG/CU
 
 static bool vec_ok(const void *p, int ld, int elems, int bytes_per_elem) {
@@ -1107,7 +1108,7 @@ static long long tiles_of(const Call &c) {
   return (long long)((c.M + T::BM - 1) / T::BM) * (long long)((c.N + T::BN - 1) / T::BN);
 }
 
-enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad, kHalf, kQuadK };
+enum class F32Cfg { kHuge, kBig, kMid, kMidB, kSmall, kTiny, kQuad, kHalf, kQuadK, kTinyK };
 
 // Share of the machine a configuration keeps busy: with T tiles spread over
 // the CUs, the busiest CU holds ceil(T/CUs) of them while the average is
@@ -1417,6 +1418,7 @@ static F32Choice choose_f32(const Call &c) {
     return F32Choice{F32Cfg::kQuad, forced, 0.0, tail, forced == 1 && tail == 1 ? streamk_of(c) : 0};
   if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
   if (c.tile_config == 9) return F32Choice{F32Cfg::kQuadK, forced, 0.0, tail};
+  if (c.tile_config == 10) return F32Choice{F32Cfg::kTinyK, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
       tiles_of<F32Mid>(c) < 3LL * kCUs)
     return choose_staged(c);
@@ -1531,6 +1533,18 @@ static F32Choice choose_f32(const Call &c) {
   // 39.2 -> 43.2, but 320^3 5.2 -> 4.8, 448^3 11.6 -> 11.1, 800^3 41.6 ->
   // 38.3), so that tile stays there; deep-K splits stay too (512x512x2048
   // 29.2 against 23.4).
+  // The 32x32 tile in 64-k steps through two slots (32 KB, five workgroups
+  // per CU) where the model takes that tile with at most 2.25 of them per
+  // CU: half the steps, so half the waits and load-issue points.  Measured
+  // (interleaved, flush before each call, TFLOP/s, 32-k steps -> this):
+  // 512^3 15.8 -> 17.1, 640^3 25.7 -> 27.7, 768^3 37.8 -> 40.5, 384^3 8.1
+  // -> 8.6, 256^3 3.0 -> 3.1, 1000x200x1000 13.1 -> 13.9, 256x2048x512 30.2
+  // -> 32.2, 300x700x900 13.2 -> 13.7; with more tiles per CU the 32-k form
+  // stayed ahead (800^3 41.4 against 40.4, 864^3 48.5 against 47.8,
+  // 100x5000x400 21.4 against 20.6).
+  if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c) && best.cfg == F32Cfg::kTiny &&
+      best.splits == 1 && best.tail == 1 && 4 * tiles_of<F32Tiny>(c) <= 9LL * kCUs)
+    best.cfg = F32Cfg::kTinyK;
   if (c.split_mode == 0 && c.tail_mode == 0 && !staged_call(c)) {
     const long long q = tiles_of<F32Quad>(c);
     const long long mx = c.M > c.N ? c.M : c.N;
@@ -1782,6 +1796,7 @@ static const char *f32_name(F32Cfg cfg) {
     case F32Cfg::kQuad: return "f32 mfma32x32x2 tile 64x64x32 4 waves 3 slots";
     case F32Cfg::kHalf: return "f32 mfma32x32x2 tile 128x64x32 4 waves 3 slots";
     case F32Cfg::kQuadK: return "f32 mfma32x32x2 tile 64x64x64 4 waves 2 slots";
+    case F32Cfg::kTinyK: return "f32 mfma32x32x2 tile 32x32x64 1 wave 2 slots";
     default: return "f32 mfma32x32x2 tile 32x32x32 1 wave 3 slots";
   }
 }
@@ -1808,6 +1823,7 @@ static Plan plan_f32_as_is(const Call &c) {
     case F32Cfg::kQuad: return plan_cfg<F32Quad>(c, name, ch.splits, ch.tail);
     case F32Cfg::kHalf: return plan_cfg<F32Half>(c, name, ch.splits, ch.tail);
     case F32Cfg::kQuadK: return plan_cfg<F32QuadK>(c, name, ch.splits, ch.tail);
+    case F32Cfg::kTinyK: return plan_cfg<F32TinyK>(c, name, ch.splits, ch.tail);
     default: return plan_cfg<F32Tiny>(c, name, ch.splits, ch.tail);
   }
 }
@@ -1833,6 +1849,7 @@ static hipError_t launch_f32_as_is(const Call &c) {
     case F32Cfg::kQuad: return launch_cfg<F32Quad>(c, ch.splits, ch.tail);
     case F32Cfg::kHalf: return launch_cfg<F32Half>(c, ch.splits, ch.tail);
     case F32Cfg::kQuadK: return launch_cfg<F32QuadK>(c, ch.splits, ch.tail);
+    case F32Cfg::kTinyK: return launch_cfg<F32TinyK>(c, ch.splits, ch.tail);
     default: return launch_cfg<F32Tiny>(c, ch.splits, ch.tail);
   }
 }

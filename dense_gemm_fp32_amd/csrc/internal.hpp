@@ -37,7 +37,8 @@ struct Call {
                          // 6 = fp32 256x256 (fp16: its large tile),
                          // 7 = fp32 64x64 with four waves (fp16: its small tile),
                          // 8 = fp32 128x64 with four waves (fp16: its medium tile),
-                         // 9 = fp32 64x64 four waves, 64-k steps (fp16: its small tile)
+                         // 9 = fp32 64x64 four waves, 64-k steps (fp16: its small tile),
+                         // 10 = fp32 32x32 one wave, 64-k steps (fp16: its small tile)
   // Split-K workspace source: the library's per-device pool (ws_fixed ==
   // nullptr), requests above ws_limit bytes failing (-1: no limit), or a
   // fixed device region of ws_fixed_bytes bytes that is never allocated or

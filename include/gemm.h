@@ -331,7 +331,8 @@ int gemm_set_load_mode(int mode);
  * blocks; the size-based choice takes either); 7 = the fp32 64 x 64 tile of
  * four 32 x 32 waves (fp16 uses its small one); 8 = the fp32 128 x 64 tile of
  * four 64 x 32 waves (fp16 uses its medium one); 9 = the fp32 64 x 64 tile of
- * four waves in 64-k steps through two LDS slots (fp16 uses its small one).
+ * four waves in 64-k steps through two LDS slots, 10 = the fp32 32 x 32 tile
+ * of one wave in 64-k steps (fp16 uses its small one for both).
  * Process-wide,
  * like gemm_set_load_mode.  Returns the previous setting, or -1 for an
  * unknown value.

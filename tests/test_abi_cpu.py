@@ -299,7 +299,9 @@ def test_tile_table_choice_and_override():
         assert "64x64x32 4 waves 3 slots" in name("f32", n) and "split" not in name("f32", n), n
     for n in (1792, 768):
         assert "64x64x32 4 waves" not in name("f32", n) and "64x64x64" not in name("f32", n), n
-    assert "32x32x32" in name("f32", 256) and "32x32x32" in name("f32", 64)
+    # the 32x32 tile, in 64-k steps up to 2.25 of them per CU
+    assert "32x32x64 1 wave 2 slots" in name("f32", 256) and "32x32x64" in name("f32", 64)
+    assert "32x32x32 1 wave 3 slots" in name("f32", 864)
     assert "split" not in name("f32", 256) and "split" not in name("f32", 768)
     # K split where the grid leaves CUs idle and K is long enough
     t = dg.gemm_describe("f32", 1024, 1024, 4096, 1.0, FAKE, 4096, FAKE, 1024, 0.0, FAKE, 1024)[1]
@@ -335,9 +337,11 @@ def test_tile_table_choice_and_override():
         assert "128x64x32 4 waves" in name("f32", 4096) and "128x128x32" in name("f16", 4096)
         dg.gemm_set_tile_config(9)
         assert "64x64x64 4 waves 2 slots" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
+        dg.gemm_set_tile_config(10)
+        assert "32x32x64 1 wave 2 slots" in name("f32", 4096) and "64x128x32" in name("f16", 4096)
     finally:
         dg.gemm_set_tile_config(prev)
-    assert dg.gemm_set_tile_config(10) == -1 and dg.gemm_set_tile_config(-1) == -1
+    assert dg.gemm_set_tile_config(11) == -1 and dg.gemm_set_tile_config(-1) == -1
 
 
 def test_staged_calls_split_the_medium_tile():
@@ -362,7 +366,7 @@ def _staged_choices(dg):
         t = d(M, N, K)
         assert "128x128x16" in t and ("split-K %d" % S) in t and "scalar1" in t, (M, N, K, t)
     assert "256x256x32" in d(4096, 4096, 4096) and "split" not in d(4096, 4096, 4096)
-    assert "32x32x32" in d(300, 300, 300)      # fewer 32x32 tiles than CUs: latency-bound
+    assert "32x32x" in d(300, 300, 300)        # fewer 32x32 tiles than CUs: latency-bound
     # a misaligned base alone makes the call staged too
     t = dg.gemm_describe("f32", 1000, 3000, 512, 1.0, FAKE + 4, 512, FAKE, 3000, 0.0, FAKE, 3000)[1]
     assert "A:scalar1" in t and "split-K" in t
@@ -419,9 +423,11 @@ def test_grids_under_one_round_take_the_four_wave_64x64_tile():
                   (800, 1200, 1000), (1024, 768, 1024), (1000, 700, 1200), (960, 1024, 1400)]:
         t = d(*shape)
         assert "64x64x64 4 waves 2 slots" in t and "split" not in t, (shape, t)
-    # 864^3: 729 32x32 tiles, at most three per CU; 832^3: 169 64x64 tiles
-    for n in (864, 832, 768):
-        assert "32x32x32" in d(n, n, n), n
+    # 864^3: 729 32x32 tiles, at most three per CU; 832^3: 169 64x64 tiles;
+    # 768^3: 576 32x32 tiles, which run in 64-k steps
+    for n in (864, 832):
+        assert "32x32x32 1 wave 3 slots" in d(n, n, n), n
+    assert "32x32x64 1 wave 2 slots" in d(768, 768, 768)
     # longer K keeps the K split
     for shape in [(2048, 384, 2048), (768, 1024, 2048), (896, 896, 3000)]:
         t = d(*shape)
@@ -433,9 +439,9 @@ def test_grids_under_one_round_take_the_four_wave_64x64_tile():
                   (200, 3000, 300)]:
         t = d(*shape)
         assert "64x64x64 4 waves 2 slots" in t and "split" not in t, (shape, t)
-    # small squares keep the 32x32 tile
+    # small squares keep the 32x32 tile (in 64-k steps: at most 2.25 per CU)
     for n in (256, 512, 768):
-        assert "32x32x32" in d(n, n, n), n
+        assert "32x32x64 1 wave 2 slots" in d(n, n, n), n
     # the switches that force a split or disable the last-round split leave
     # the model's choice
     prev = dg.gemm_set_tail_split(1)

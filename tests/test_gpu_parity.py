@@ -464,10 +464,10 @@ TABLE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9],
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10],
                          ids=["large", "medium", "small", "tiny", "medium-bunched", "f32-256x256",
                               "f32-64x64-four-waves", "f32-128x64-four-waves",
-                              "f32-64x64-four-waves-k64"])
+                              "f32-64x64-four-waves-k64", "f32-32x32-k64"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_tile_configuration_matches_oracle(dtype, cfg):
     t = _t(dtype)
@@ -519,7 +519,7 @@ from hypothesis import HealthCheck, given, settings, strategies as st
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        alpha=st.sampled_from([1.0, -0.5, 2.0, 0.25]),
        beta=st.sampled_from([0.0, 1.0, -1.5, 0.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6, 7, 8, 9]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]),
        pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
 def test_random_shapes_match_oracle(dtype, M, N, K, pads, alpha, beta, cfg, pack, seed):
@@ -660,7 +660,7 @@ def test_split_k_deterministic_and_paths_agree(dtype):
     assert np.array_equal(bits(o1, dtype), bits(o2, dtype))
     assert np.array_equal(bits(o1, dtype), bits(o3, dtype))
     check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o1, "split det")
-    for cfg in (1, 2, 3, 4, 6, 9):
+    for cfg in (1, 2, 3, 4, 6, 9, 10):
         with split_mode(3), tile_config(cfg):
             rc, o = run(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, "split cfg%d" % cfg)
         assert rc == 0
@@ -875,7 +875,7 @@ def test_layouts_match_oracle(dtype, layout):
         _layout_run_check(dtype, layout, M, N, K, pads, 100 + idx, beta=beta, label="layout")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7, 8, 9])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6, 7, 8, 9, 10])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_layouts_every_tile(dtype, layout, cfg):
@@ -1087,7 +1087,7 @@ def test_concurrent_streams_and_threads_share_the_workspace_pool():
        M=st.integers(1, 300), N=st.integers(1, 300), K=st.integers(1, 300),
        pads=st.tuples(st.integers(0, 9), st.integers(0, 9), st.integers(0, 9)),
        beta=st.sampled_from([0.0, 1.0, -1.5]),
-       cfg=st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8, 9]),
+       cfg=st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8, 9, 10]),
        split=st.sampled_from([0, 1, 3]),
        pack=st.sampled_from([0, 2]),
        seed=st.integers(0, 2 ** 31 - 1))
