@@ -1456,6 +1456,21 @@ static F32Choice choose_f32(const Call &c) {
         const int sk = streamk_of(c);
         return F32Choice{sk == 0 && q <= 2LL * kCUs ? F32Cfg::kQuadK : F32Cfg::kQuad, 1, 0.0, 1, sk};
       }
+      // Three whole rounds and at most a third of a round more: the same tile
+      // with Stream-K behind the whole rounds (the leftover's K steps over one
+      // more workgroup per CU), in place of the 128x64 tile.  Measured
+      // (interleaved, flush before each call, TFLOP/s, 128x64 -> this):
+      // 1760^3 (784 tiles) 88.7 -> 100.0, 1792^3 94.7 -> 105.1, 2048 x 1600 x
+      // 1800 (800) 93.7 -> 103.9, 1700x1900x1500 (810) 89.2 -> 96.5, 1856^3
+      // (841) 99.5 -> 104.7, 1792x1920x1792 (840) 100.7 -> 104.5; from half a
+      // round more it lost (1920^3, 900 tiles, 108.6 against 101.6; 1984^3
+      // 114.1 against 98.4).
+      StreamKRun skr;
+      long long skb = 0;
+      const int sk3 = c.streamk_mode >= 2 ? c.streamk_mode : 5;
+      if (q > 3LL * kCUs && 3 * (q - 3LL * kCUs) <= kCUs && c.streamk_mode != 1 &&
+          streamk_fits<F32Quad>(c, sk3, skr, skb))
+        return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, sk3};
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
     }
   }

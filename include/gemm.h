@@ -39,7 +39,8 @@
  *     the whole rounds.
  *   - Stream-K (fp32): when the tiles a call takes leave the last round of
  *     the CUs partly filled -- 64x64 tiles past two whole rounds with at most
- *     half a round more; 256x256 tiles wherever there is a round of them and
+ *     half a round more, or past three with at most a third of a round more
+ *     (K <= 2 max(M, N)); 256x256 tiles wherever there is a round of them and
  *     97% of their area lies inside the matrix; 128x128 tiles over 2 to 7
  *     rounds (up to 16 where the size rules pick that tile anyway) with a
  *     quarter to seven eighths of a round more; the 256x128 tile whenever it

@@ -288,16 +288,17 @@ def test_tile_table_choice_and_override():
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
     assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2304)
-    # 1.5 to 2 128x64 tiles per CU (past three 64x64 ones): the four-wave 128x64 tile
-    for n in (1792, 1920, 2048):
+    # past three and a third 64x64 tiles per CU, up to two 128x64 ones: the
+    # four-wave 128x64 tile
+    for n in (1888, 1920, 2048):
         assert "128x64x32 4 waves" in name("f32", n) and "split" not in name("f32", n), n
     # one to three 64x64 tiles per CU: that tile with four 32x32 waves,
     # unsplit; up to two per CU in 64-k steps through two slots
     for n in (1024, 1280):
         assert "64x64x64 4 waves 2 slots" in name("f32", n) and "split" not in name("f32", n), n
-    for n in (1536, 1664):
+    for n in (1536, 1664, 1792):
         assert "64x64x32 4 waves 3 slots" in name("f32", n) and "split" not in name("f32", n), n
-    for n in (1792, 768):
+    for n in (1888, 768):
         assert "64x64x32 4 waves" not in name("f32", n) and "64x64x64" not in name("f32", n), n
     # the 32x32 tile, in 64-k steps up to 2.25 of them per CU
     assert "32x32x64 1 wave 2 slots" in name("f32", 256) and "32x32x64" in name("f32", 64)
@@ -595,7 +596,8 @@ def test_workspace_limit_switch():
 def test_stream_k_by_size_and_switches():
     """Stream-K behind the whole rounds, with two fp32 tile blocks of
     workspace per Stream-K workgroup (one per CU): the four-wave 64x64 tile
-    with two whole rounds and at most half a round more; the 128x128 tile
+    with two whole rounds and at most half a round more, or three and at
+    most a third of a round more; the 128x128 tile
     with two to seven rounds and a leftover of a quarter to seven eighths of
     a round, in place of any choice, and up to sixteen rounds in place of
     that tile; the 256x128 and 256x256 tiles with a round partly filled, in
@@ -628,6 +630,20 @@ def test_stream_k_by_size_and_switches():
     # (1664^3: 164 tiles), whole rounds (1024^3), other tiles: plain
     for n in (1024, 1088, 1152, 1216, 1280, 1408, 1664, 2048, 4096):
         assert "stream-K" not in d(n, n, n), n
+    # past three whole rounds by at most a third of a round: 1792^3 (784
+    # tiles), 1856^3 (841), 2048x1600x1800 (800); from 1888^3 (900) the
+    # 128x64 tile, plain
+    for s in ((1760, 1760, 1760), (1792, 1792, 1792), (1856, 1856, 1856), (2048, 1600, 1800)):
+        t = d(*s)
+        assert "64x64x32 4 waves" in t and "stream-K after 768 whole tiles" in t, (s, t)
+    # 1792^3: 16 tiles left, their 56 K steps each in runs of 4 over 224
+    # workgroups
+    t = d(1792, 1792, 1792)
+    assert "blocks 992 " in t and ws(t) == 224 * block, t
+    for n in (1888, 1920, 1984):
+        assert "128x64x32 4 waves" in d(n, n, n) and "stream-K" not in d(n, n, n), n
+    # deep K (K > 2 max(M, N)) stays off it
+    assert "stream-K" not in d(1792, 1792, 3600)
     # copies and Stream-K share one workspace
     t = d(1536, 1536, 1536, 1537, 1537, 1537)
     assert "copies A B" in t and "stream-K after 512" in t and ws(t) == 2 * 1536 * 1536 * 4 + 256 * block, t

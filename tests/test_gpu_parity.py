@@ -78,15 +78,15 @@ def test_headline_4096_every_element(w):
                                           (1408, "64x64x64 4 waves 2 slots", 0),
                                           (1536, "64x64x32 4 waves", 512),
                                           (1664, "64x64x32 4 waves", 0),
-                                          (1792, "128x64x32 4 waves", 0),
+                                          (1792, "64x64x32 4 waves", 768),
                                           (1920, "128x64x32 4 waves", 0)])
 def test_f32_sweep_four_wave_tile_full_oracle(n, tile, whole):
     """Sweep sizes (beta = 1) whose plan is a four-wave tile, K unsplit: the
-    64x64 tile of 32x32 waves (one to three tiles per CU; up to two per CU
-    in 64-k steps) or the 128x64 tile of 64x32 waves (1.5 to 2 per CU),
-    every element against the oracle.
-    1536^3 (576 tiles) leaves a small third round, whose K steps run
-    Stream-K behind 512 whole tiles."""
+    64x64 tile of 32x32 waves (one to three and a third tiles per CU; up to
+    two per CU in 64-k steps) or the 128x64 tile of 64x32 waves (past that,
+    up to 2 per CU), every element against the oracle.
+    1536^3 (576 tiles) and 1792^3 (784) leave a small last round, whose K
+    steps run Stream-K behind the whole ones."""
     w = wl.sweep(n)
     plan = _plan(w)
     assert tile in plan and "split" not in plan, plan
@@ -1473,6 +1473,21 @@ def test_stream_k_128x128_chosen_by_size_full_oracle():
     w = wl.sweep(3840)
     plan = _plan(w)
     assert "128x128x16" in plan and "stream-K after 768 whole tiles" in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
+@pytest.mark.parametrize("shape", [(1856, 1856, 1856), (2048, 1600, 1800), (1700, 1900, 1500)])
+def test_stream_k_four_wave_tile_past_three_rounds_full_oracle(shape):
+    """Calls (beta = 1) with three whole rounds of four-wave 64x64 tiles and at
+    most a third of a round more (1856^3: 841 tiles; 2048 x 1600 x 1800: 800;
+    1700 x 1900 x 1500: 810, ragged in M and N): the whole rounds run whole and
+    the leftover tiles' K steps Stream-K; every element against the oracle."""
+    M, N, K = shape
+    w = wl.sweep(M) if M == N == K else wl.Workload(
+        "streamk_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform", "uniform",
+        (91, 92, 93))
+    plan = _plan(w)
+    assert "64x64x32 4 waves" in plan and "stream-K after 768 whole tiles" in plan, plan
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
