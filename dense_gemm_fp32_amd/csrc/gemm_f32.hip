@@ -1416,7 +1416,7 @@ static F32Choice choose_f32(const Call &c) {
   if (c.tile_config == 6) return F32Choice{F32Cfg::kHuge, forced, 0.0, tail, fsk};
   if (c.tile_config == 7)
     return F32Choice{F32Cfg::kQuad, forced, 0.0, tail, forced == 1 && tail == 1 ? streamk_of(c) : 0};
-  if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail};
+  if (c.tile_config == 8) return F32Choice{F32Cfg::kHalf, forced, 0.0, tail, fsk};
   if (c.tile_config == 9) return F32Choice{F32Cfg::kQuadK, forced, 0.0, tail};
   if (c.tile_config == 10) return F32Choice{F32Cfg::kTinyK, forced, 0.0, tail};
   if (c.split_mode == 0 && c.tail_mode == 0 && staged_call(c) && tiles_of<F32Tiny>(c) > kCUs &&
@@ -1472,6 +1472,21 @@ static F32Choice choose_f32(const Call &c) {
           streamk_fits<F32Quad>(c, sk3, skr, skb))
         return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, sk3};
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
+      // Two to three and a half rounds of 128x64 tiles, a round partly
+      // filled, both sides and K at least 1024: that tile with Stream-K
+      // behind the whole rounds, in place of any other choice.  Measured
+      // (interleaved, flush before each call, beta 1, TFLOP/s, the choice
+      // before -> this): 2176^3 (578 tiles; 128x128 split 4) 104.9 -> 119.1,
+      // 2304^3 (648; split 3) 114.0 -> 119.8, 2432^3 (722) 118.1 -> 119.7,
+      // 2560^3 (800) 116.7 -> 121.6, 2688^3 (882; 256x128) 119.3 -> 125.9,
+      // 2048x2304x2048 (576; 32x32) 93.6 -> 120.6, 2560x2048x2560 118.6 ->
+      // 123.1, 2176x2176x1536 (256x128) 75.4 -> 112.3, 1536x3072x2048
+      // (32x32) 93.7 -> 120.8.  The tile alone, without Stream-K, lost at
+      // most of these (2176^3 94.7, 2560^3 103.8).
+      const long long mn = c.M < c.N ? c.M : c.N;
+      if (h > 2LL * kCUs && 2 * h <= 7LL * kCUs && h % kCUs != 0 && c.K >= 1024 && mn >= 1024 &&
+          c.streamk_mode != 1 && streamk_fits<F32Half>(c, sk3, skr, skb))
+        return F32Choice{F32Cfg::kHalf, 1, 0.0, 1, sk3};
     }
   }
   const double big = score_of<F32Big>(c, 0.92, 1, 1);
@@ -1826,6 +1841,7 @@ static Plan plan_f32_as_is(const Call &c) {
       case F32Cfg::kBig: if (plan_streamk<F32Big>(c, name, ch.sk, pl)) return pl; break;
       case F32Cfg::kMidB: if (plan_streamk<F32MidB>(c, name, ch.sk, pl)) return pl; break;
       case F32Cfg::kQuad: if (plan_streamk<F32Quad>(c, name, ch.sk, pl)) return pl; break;
+      case F32Cfg::kHalf: if (plan_streamk<F32Half>(c, name, ch.sk, pl)) return pl; break;
       default: break;
     }
   }
@@ -1852,6 +1868,7 @@ static hipError_t launch_f32_as_is(const Call &c) {
       case F32Cfg::kBig: if (launch_streamk<F32Big>(c, ch.sk, &se)) return se; break;
       case F32Cfg::kMidB: if (launch_streamk<F32MidB>(c, ch.sk, &se)) return se; break;
       case F32Cfg::kQuad: if (launch_streamk<F32Quad>(c, ch.sk, &se)) return se; break;
+      case F32Cfg::kHalf: if (launch_streamk<F32Half>(c, ch.sk, &se)) return se; break;
       default: break;
     }
   }

@@ -40,7 +40,8 @@
  *   - Stream-K (fp32): when the tiles a call takes leave the last round of
  *     the CUs partly filled -- 64x64 tiles past two whole rounds with at most
  *     half a round more, or past three with at most a third of a round more
- *     (K <= 2 max(M, N)); 256x256 tiles wherever there is a round of them and
+ *     (K <= 2 max(M, N)); 128x64 tiles over two to three and a half rounds
+ *     (M, N, K >= 1024); 256x256 tiles wherever there is a round of them and
  *     97% of their area lies inside the matrix; 128x128 tiles over 2 to 7
  *     rounds (up to 16 where the size rules pick that tile anyway) with a
  *     quarter to seven eighths of a round more; the 256x128 tile whenever it
@@ -51,7 +52,7 @@
  *     the SGEMM summary's results section names).  A tile so shared is
  *     summed from its parts' fp32 partial sums, in K order, by a second pass
  *     that also applies alpha and beta (two fp32 tile blocks of workspace per
- *     Stream-K workgroup: 8, 32, 64 or 128 MiB by tile).
+ *     Stream-K workgroup: 8, 16, 32, 64 or 128 MiB by tile).
  *   - Operand copies (fp32): when the rows of A or B do not allow 16-byte
  *     loads (ld not a multiple of 4, or a base not 16-byte aligned) and the
  *     call does at least 5e9 flops, or 1.5e9 with N a multiple of 4, that

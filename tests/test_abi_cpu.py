@@ -287,7 +287,7 @@ def test_tile_table_choice_and_override():
     import dense_gemm_fp32_amd as dg
     def name(dt, n):
         return dg.gemm_describe(dt, n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)[1]
-    assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 2304)
+    assert "256x256x32" in name("f32", 4096) and "128x128x16" in name("f32", 3072)
     # past three and a third 64x64 tiles per CU, up to two 128x64 ones: the
     # four-wave 128x64 tile
     for n in (1888, 1920, 2048):
@@ -307,7 +307,8 @@ def test_tile_table_choice_and_override():
     # K split where the grid leaves CUs idle and K is long enough
     t = dg.gemm_describe("f32", 1024, 1024, 4096, 1.0, FAKE, 4096, FAKE, 1024, 0.0, FAKE, 1024)[1]
     assert "128x128x16" in t and "split-K 8" in t, t
-    assert "128x128x16" in name("f32", 2304) and "split-K 3" in name("f32", 2304)
+    t = dg.gemm_describe("f32", 2304, 2304, 5000, 1.0, FAKE, 5000, FAKE, 2304, 0.0, FAKE, 2304)[1]
+    assert "256x128x32" in t and "split-K 3" in t, t
     assert "split" not in name("f32", 4096) and "split" not in name("f16", 4096)
     assert "split" not in name("f16", 1536)
     assert "128x128x16" in name("f32", 3072) and "128x128x16" in name("f32", 4480)
@@ -554,15 +555,17 @@ def test_tail_split_in_descriptions():
 
 
 def test_describe_reports_split_workspace():
-    """The workspace a split call takes, worked out by hand: 2304^3 splits the
-    128 x 128 tiles 3 ways into M x N fp32 slabs, 3 * 2304 * 2304 * 4 bytes;
+    """The workspace a split call takes, worked out by hand: 2304 x 2304 x 5000
+    splits the 256 x 128 tiles 3 ways into M x N fp32 slabs, 3 * 2304 * 2304 *
+    4 bytes;
     2944^3 (23 x 23 = 529 tiles of 128 x 128, 2 whole rounds of 256 and 17
     left over) splits the 17 leftover tiles 15 ways into dense tile blocks,
     15 * 17 * 128 * 128 * 4 bytes.  An unsplit call takes none."""
     import dense_gemm_fp32_amd as dg
-    cases = [(2304, "split-K 3", 63700992), (2944, "last round split-K 15", 16711680)]
-    for n, split, nbytes in cases:
-        rc, text = dg.gemm_describe("f32", n, n, n, 1.0, FAKE, n, FAKE, n, 1.0, FAKE, n)
+    cases = [((2304, 2304, 5000), "split-K 3", 63700992),
+             ((2944, 2944, 2944), "last round split-K 15", 16711680)]
+    for (m, n, k), split, nbytes in cases:
+        rc, text = dg.gemm_describe("f32", m, n, k, 1.0, FAKE, k, FAKE, n, 1.0, FAKE, n)
         assert rc == 0 and split in text and ("workspace %d bytes" % nbytes) in text, text
     rc, text = dg.gemm_describe("f32", 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
     assert rc == 0 and "workspace" not in text, text
@@ -597,7 +600,8 @@ def test_stream_k_by_size_and_switches():
     """Stream-K behind the whole rounds, with two fp32 tile blocks of
     workspace per Stream-K workgroup (one per CU): the four-wave 64x64 tile
     with two whole rounds and at most half a round more, or three and at
-    most a third of a round more; the 128x128 tile
+    most a third of a round more; the 128x64 tile with two to three and a
+    half rounds; the 128x128 tile
     with two to seven rounds and a leftover of a quarter to seven eighths of
     a round, in place of any choice, and up to sixteen rounds in place of
     that tile; the 256x128 and 256x256 tiles with a round partly filled, in
@@ -644,6 +648,23 @@ def test_stream_k_by_size_and_switches():
         assert "128x64x32 4 waves" in d(n, n, n) and "stream-K" not in d(n, n, n), n
     # deep K (K > 2 max(M, N)) stays off it
     assert "stream-K" not in d(1792, 1792, 3600)
+    # the 128x64 tile: two to three and a half rounds of its tiles, a round
+    # partly filled, M, N and K at least 1024.  2176^3: 578 tiles, 512 whole,
+    # 66 left; their 68 K steps each, 4488 in all, in runs of 18 over 250
+    # workgroups, two 128x64 blocks each
+    t = d(2176, 2176, 2176)
+    assert "128x64x32 4 waves" in t and "stream-K after 512 whole tiles" in t, t
+    assert "blocks 762 " in t and ws(t) == 250 * 2 * 128 * 64 * 4, t
+    for s in ((2304, 2304, 2304), (2432, 2432, 2432), (2048, 2304, 2048), (1536, 3072, 2048),
+              (2176, 2176, 1536)):
+        assert "128x64x32 4 waves" in d(*s) and "stream-K after 512 whole tiles" in d(*s), s
+    for n in (2560, 2688):
+        assert "128x64x32 4 waves" in d(n, n, n) and "stream-K after 768 whole tiles" in d(n, n, n), n
+    # not past three and a half rounds (2816^3: 968 tiles), at whole rounds
+    # (2048 x 3072 x 2048: 768), with K or a side below 1024, or deep K
+    for s in ((2816, 2816, 2816), (2048, 3072, 2048), (2176, 2176, 512), (1000, 4000, 2000),
+              (2304, 2304, 5000)):
+        assert not ("128x64x32" in d(*s) and "stream-K" in d(*s)), (s, d(*s))
     # copies and Stream-K share one workspace
     t = d(1536, 1536, 1536, 1537, 1537, 1537)
     assert "copies A B" in t and "stream-K after 512" in t and ws(t) == 2 * 1536 * 1536 * 4 + 256 * block, t

@@ -130,10 +130,10 @@ def test_f32_under_one_round_four_wave_tile_full_oracle(shape):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
-@pytest.mark.parametrize("n", [2304, 2944, 3584])
+@pytest.mark.parametrize("n", [2944, 3584])
 def test_f32_sweep_mid_sizes_sampled(n):
-    """Sweep sizes whose chosen plans split K: 2304^3 (every tile split),
-    2944^3 and 3584^3 (the last, partly filled round of tiles split), with
+    """Sweep sizes whose chosen plans split K: 2944^3 and 3584^3 (the last,
+    partly filled round of tiles split), with
     beta = 1, on sampled rows that include one row of each of the last eight
     tile rows (where the split leftover tiles lie), the checksum and
     Freivalds' check."""
@@ -667,7 +667,7 @@ def test_split_k_deterministic_and_paths_agree(dtype):
         check(dtype, M, N, K, 0.5, A, K, B, N, 2.0, C, N, o, "split 3 cfg %d" % cfg)
 
 
-@pytest.mark.parametrize("dtype,M,N,K", [("f32", 2304, 2304, 2304), ("f16", 1024, 1024, 8192),
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 2304, 2304, 5000), ("f16", 1024, 1024, 8192),
                                           ("f16f32", 512, 512, 8192), ("f32", 512, 512, 8192)])
 def test_split_k_chosen_by_size_sampled(dtype, M, N, K):
     """Shapes whose tile grid leaves CUs idle take split K by themselves;
@@ -1425,13 +1425,14 @@ STREAMK_TILE_CASES = {
     6: [(4300, 4400, 333, 0, 0, 0, 0.5), (900, 1300, 515, 0, 0, 1, 0.0)],   # 256x256
     1: [(4300, 2200, 700, 0, 4, 0, -0.75), (1500, 700, 260, 0, 0, 0, 1.0)],  # 256x128
     5: [(2200, 2200, 1000, 0, 0, 3, 0.0), (900, 1300, 515, 4, 0, 0, 0.5)],   # 128x128
+    8: [(2200, 2250, 1100, 0, 4, 1, 0.5), (700, 1500, 515, 0, 0, 0, 0.0)],   # 128x64
 }
 
 
 @pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
-@pytest.mark.parametrize("cfg", [6, 1, 5], ids=["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("cfg", [6, 1, 5, 8], ids=["256x256", "256x128", "128x128", "128x64"])
 def test_stream_k_large_tiles_every_mode_matches_oracle(cfg, layout):
-    """Stream-K on the 256x256, 256x128 and 128x128 tiles, in every mode
+    """Stream-K on the 256x256, 256x128, 128x128 and 128x64 tiles, in every mode
     and layout, against the oracle element by element: runs of one K step up
     to a whole tile, partial K steps, ragged edges, C rows not 16-byte
     aligned, beta = 0 over a NaN C, pads untouched."""
@@ -1473,6 +1474,23 @@ def test_stream_k_128x128_chosen_by_size_full_oracle():
     w = wl.sweep(3840)
     plan = _plan(w)
     assert "128x128x16" in plan and "stream-K after 768 whole tiles" in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
+@pytest.mark.parametrize("shape", [(2176, 2176, 2176), (2560, 2560, 2560), (2688, 2688, 2688),
+                                   (2048, 2304, 2048), (2200, 2300, 1500)])
+def test_stream_k_128x64_tile_chosen_by_size_full_oracle(shape):
+    """Calls (beta = 1) with two to three and a half rounds of 128x64 tiles,
+    the last partly filled (2176^3: 578 tiles; 2560^3: 800; 2688^3: 882;
+    2048 x 2304 x 2048: 576; 2200 x 2300 x 1500: 648, ragged in M and N):
+    the whole rounds run whole and the leftover tiles' K steps Stream-K on
+    the same tile; every element against the oracle."""
+    M, N, K = shape
+    w = wl.sweep(M) if M == N == K else wl.Workload(
+        "streamk_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform", "uniform",
+        (94, 95, 96))
+    plan = _plan(w)
+    assert "128x64x32 4 waves" in plan and "stream-K after" in plan, plan
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 

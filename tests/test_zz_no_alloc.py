@@ -36,9 +36,10 @@ def _both(w):
 
 
 def test_noalloc_matches_gemm_f32_on_calls_in_a_row():
-    # 1) 2304^3, beta = 1: K split 3 ways into M x N slabs, 63,700,992 bytes
-    #    of the 64 MiB region.
-    w1 = wl.sweep(2304)
+    # 1) 2304 x 2304 x 5000, beta = 1: K split 3 ways into M x N slabs,
+    #    63,700,992 bytes of the 64 MiB region.
+    w1 = wl.Workload("noalloc_2304x2304x5000", "f32", 2304, 2304, 5000, 5000, 2304, 2304, 1.0, 1.0,
+                     "uniform", "uniform", (5, 6, 7))
     plan, (A, B, C), out_na, out_ref = _both(w1)
     assert "split-K 3" in plan and "workspace 63700992 bytes" in plan, plan
     assert np.array_equal(bits(out_na, "f32"), bits(out_ref, "f32"))
