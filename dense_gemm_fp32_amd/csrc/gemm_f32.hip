@@ -1473,7 +1473,7 @@ static F32Choice choose_f32(const Call &c) {
         return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, sk3};
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
       // Two to three and a half rounds of 128x64 tiles, a round partly
-      // filled, both sides and K at least 1024: that tile with Stream-K
+      // filled, both sides and K at least 640: that tile with Stream-K
       // behind the whole rounds, in place of any other choice.  Measured
       // (interleaved, flush before each call, beta 1, TFLOP/s, the choice
       // before -> this): 2176^3 (578 tiles; 128x128 split 4) 104.9 -> 119.1,
@@ -1481,10 +1481,14 @@ static F32Choice choose_f32(const Call &c) {
       // 2560^3 (800) 116.7 -> 121.6, 2688^3 (882; 256x128) 119.3 -> 125.9,
       // 2048x2304x2048 (576; 32x32) 93.6 -> 120.6, 2560x2048x2560 118.6 ->
       // 123.1, 2176x2176x1536 (256x128) 75.4 -> 112.3, 1536x3072x2048
-      // (32x32) 93.7 -> 120.8.  The tile alone, without Stream-K, lost at
-      // most of these (2176^3 94.7, 2560^3 103.8).
+      // (32x32) 93.7 -> 120.8; narrow and short calls as well: 768 x 6144 x
+      // 2048 (32x32) 93.2 -> 120.3, 640x8192x1536 (256x128) 82.9 -> 113.7,
+      // 896x5120x3000 91.4 -> 121.3, 2176x2176x768 68.5 -> 90.6,
+      // 3072x1536x640 65.2 -> 86.0.  At K = 512 it lost (2560x2560x512 84.6
+      // against 79.7).  The tile alone, without Stream-K, lost at most of
+      // these (2176^3 94.7, 2560^3 103.8).
       const long long mn = c.M < c.N ? c.M : c.N;
-      if (h > 2LL * kCUs && 2 * h <= 7LL * kCUs && h % kCUs != 0 && c.K >= 1024 && mn >= 1024 &&
+      if (h > 2LL * kCUs && 2 * h <= 7LL * kCUs && h % kCUs != 0 && c.K >= 640 && mn >= 640 &&
           c.streamk_mode != 1 && streamk_fits<F32Half>(c, sk3, skr, skb))
         return F32Choice{F32Cfg::kHalf, 1, 0.0, 1, sk3};
     }

@@ -41,7 +41,7 @@
  *     the CUs partly filled -- 64x64 tiles past two whole rounds with at most
  *     half a round more, or past three with at most a third of a round more
  *     (K <= 2 max(M, N)); 128x64 tiles over two to three and a half rounds
- *     (M, N, K >= 1024); 256x256 tiles wherever there is a round of them and
+ *     (M, N, K >= 640); 256x256 tiles wherever there is a round of them and
  *     97% of their area lies inside the matrix; 128x128 tiles over 2 to 7
  *     rounds (up to 16 where the size rules pick that tile anyway) with a
  *     quarter to seven eighths of a round more; the 256x128 tile whenever it

@@ -601,7 +601,7 @@ def test_stream_k_by_size_and_switches():
     workspace per Stream-K workgroup (one per CU): the four-wave 64x64 tile
     with two whole rounds and at most half a round more, or three and at
     most a third of a round more; the 128x64 tile with two to three and a
-    half rounds; the 128x128 tile
+    half rounds (M, N, K >= 640); the 128x128 tile
     with two to seven rounds and a leftover of a quarter to seven eighths of
     a round, in place of any choice, and up to sixteen rounds in place of
     that tile; the 256x128 and 256x256 tiles with a round partly filled, in
@@ -649,21 +649,22 @@ def test_stream_k_by_size_and_switches():
     # deep K (K > 2 max(M, N)) stays off it
     assert "stream-K" not in d(1792, 1792, 3600)
     # the 128x64 tile: two to three and a half rounds of its tiles, a round
-    # partly filled, M, N and K at least 1024.  2176^3: 578 tiles, 512 whole,
+    # partly filled, M, N and K at least 640.  2176^3: 578 tiles, 512 whole,
     # 66 left; their 68 K steps each, 4488 in all, in runs of 18 over 250
     # workgroups, two 128x64 blocks each
     t = d(2176, 2176, 2176)
     assert "128x64x32 4 waves" in t and "stream-K after 512 whole tiles" in t, t
     assert "blocks 762 " in t and ws(t) == 250 * 2 * 128 * 64 * 4, t
     for s in ((2304, 2304, 2304), (2432, 2432, 2432), (2048, 2304, 2048), (1536, 3072, 2048),
-              (2176, 2176, 1536)):
+              (2176, 2176, 1536), (768, 6144, 2048), (6144, 768, 2048), (640, 8192, 1536),
+              (2176, 2176, 768), (3072, 1536, 640)):
         assert "128x64x32 4 waves" in d(*s) and "stream-K after 512 whole tiles" in d(*s), s
     for n in (2560, 2688):
         assert "128x64x32 4 waves" in d(n, n, n) and "stream-K after 768 whole tiles" in d(n, n, n), n
     # not past three and a half rounds (2816^3: 968 tiles), at whole rounds
-    # (2048 x 3072 x 2048: 768), with K or a side below 1024, or deep K
+    # (2048 x 3072 x 2048: 768), with K or a side below 640, or deep K
     for s in ((2816, 2816, 2816), (2048, 3072, 2048), (2176, 2176, 512), (1000, 4000, 2000),
-              (2304, 2304, 5000)):
+              (2304, 2304, 5000), (2560, 2560, 512), (600, 8192, 2048), (2176, 2176, 600)):
         assert not ("128x64x32" in d(*s) and "stream-K" in d(*s)), (s, d(*s))
     # copies and Stream-K share one workspace
     t = d(1536, 1536, 1536, 1537, 1537, 1537)

@@ -1478,11 +1478,13 @@ def test_stream_k_128x128_chosen_by_size_full_oracle():
 
 
 @pytest.mark.parametrize("shape", [(2176, 2176, 2176), (2560, 2560, 2560), (2688, 2688, 2688),
-                                   (2048, 2304, 2048), (2200, 2300, 1500)])
+                                   (2048, 2304, 2048), (2200, 2300, 1500), (768, 6144, 2048),
+                                   (900, 5000, 700)])
 def test_stream_k_128x64_tile_chosen_by_size_full_oracle(shape):
     """Calls (beta = 1) with two to three and a half rounds of 128x64 tiles,
     the last partly filled (2176^3: 578 tiles; 2560^3: 800; 2688^3: 882;
-    2048 x 2304 x 2048: 576; 2200 x 2300 x 1500: 648, ragged in M and N):
+    2048 x 2304 x 2048: 576; 2200 x 2300 x 1500: 648, ragged in M and N;
+    768 x 6144 x 2048: 576, narrow; 900 x 5000 x 700: 632, ragged and short):
     the whole rounds run whole and the leftover tiles' K steps Stream-K on
     the same tile; every element against the oracle."""
     M, N, K = shape
