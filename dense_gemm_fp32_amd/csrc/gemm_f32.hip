@@ -1472,6 +1472,15 @@ static F32Choice choose_f32(const Call &c) {
           streamk_fits<F32Quad>(c, sk3, skr, skb))
         return F32Choice{F32Cfg::kQuad, 1, 0.0, 1, sk3};
       if (2 * h >= 3LL * kCUs && h <= 2LL * kCUs) return F32Choice{F32Cfg::kHalf, 1, 0.0, 1};
+      // Exactly two full rounds of the 64x64 tile at three resident
+      // workgroups per CU (six tiles on every CU), 1024 <= K <= max(M, N):
+      // that tile, plain, where the larger tiles leave a round partly filled.
+      // Measured (interleaved, flush before each call, beta 1, TFLOP/s, the
+      // 256x128 tile chosen before -> this): 1536x4096x1536 99.0 -> 124.0,
+      // 1024x6144x1024 94.4 -> 116.6, 4096x1536x2048 102.1 -> 127.6 (the
+      // 128x64 tile ran 120.0, 112.5, 123.6 there).
+      if (q == 6LL * kCUs && c.K >= 1024 && c.K <= mx)
+        return F32Choice{F32Cfg::kQuad, 1, 0.0, 1};
       // Two to three and a half rounds of 128x64 tiles, a round partly
       // filled, both sides and K at least 640: that tile with Stream-K
       // behind the whole rounds, in place of any other choice.  Measured

@@ -648,6 +648,12 @@ def test_stream_k_by_size_and_switches():
         assert "128x64x32 4 waves" in d(n, n, n) and "stream-K" not in d(n, n, n), n
     # deep K (K > 2 max(M, N)) stays off it
     assert "stream-K" not in d(1792, 1792, 3600)
+    # exactly 1536 64x64 tiles (six per CU), K >= 1024: that tile, plain
+    for s in ((1536, 4096, 1536), (1024, 6144, 1024), (4096, 1536, 2048), (2048, 3072, 2048)):
+        t = d(*s)
+        assert "64x64x32 4 waves 3 slots" in t and "stream-K" not in t and "split" not in t, (s, t)
+    assert "64x64x32" not in d(1536, 4096, 512) and "64x64x32" not in d(2048, 4096, 1024)
+    assert "64x64x32" not in d(3072, 2048, 4000)
     # the 128x64 tile: two to three and a half rounds of its tiles, a round
     # partly filled, M, N and K at least 640.  2176^3: 578 tiles, 512 whole,
     # 66 left; their 68 K steps each, 4488 in all, in runs of 18 over 250

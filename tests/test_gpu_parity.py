@@ -1496,6 +1496,20 @@ def test_stream_k_128x64_tile_chosen_by_size_full_oracle(shape):
     _w_run_check(w, "%s (%s)" % (w.name, plan))
 
 
+@pytest.mark.parametrize("shape", [(1536, 4096, 1536), (4096, 1536, 2048), (1000, 6144, 1100)])
+def test_f32_six_four_wave_tiles_per_cu_full_oracle(shape):
+    """Calls (beta = 1) with exactly 1536 64x64 tiles, six on every CU at
+    three resident workgroups (1000 x 6144 x 1100 ragged in M and K): the
+    four-wave 64x64 tile, plain; every element against the oracle."""
+    M, N, K = shape
+    w = wl.Workload("six_per_cu_%dx%dx%d" % shape, "f32", M, N, K, K, N, N, 1.0, 1.0, "uniform",
+                    "uniform", (97, 98, 99))
+    plan = _plan(w)
+    assert "64x64x32 4 waves 3 slots" in plan and "stream-K" not in plan, plan
+    assert "split" not in plan, plan
+    _w_run_check(w, "%s (%s)" % (w.name, plan))
+
+
 @pytest.mark.parametrize("shape", [(1856, 1856, 1856), (2048, 1600, 1800), (1700, 1900, 1500)])
 def test_stream_k_four_wave_tile_past_three_rounds_full_oracle(shape):
     """Calls (beta = 1) with three whole rounds of four-wave 64x64 tiles and at
